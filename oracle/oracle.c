@@ -1,0 +1,213 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for SANATAN p=1/p=2 attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file: only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+ * shares no code, header, table or constant with the GPU library.
+ *
+ * Every quantity is IEEE binary64 with the C library's cos/sin/tanh/pow; built without
+ * fast-math and with FMA contraction off, so what is written is what is computed.
+ *
+ * Sources (the pages are cited by title and section):
+ *   [N]  "SANATAN: root-label gated angular kernel, exact recurrence and revised
+ *        evidence" -- reading notes on the SANATAN v2 paper (page 1).
+ *   [F]  The author's forum post restating the method (page 2).
+ *
+ * Definitions used (one head, d content dims, d_v value dims, positions t = pos0 + i):
+ *   theta(u)   = pi * u / (1 + |u|)                         [N] §2.2, angle map phi(u)
+ *   r(u)       = tanh(gamma * (cos(theta+omega_a) - sin(theta+omega_a)))
+ *                 -- from the UNROTATED angle                [N] §2.2, root equation; [F]
+ *   lambda_a   = base^(-a/d), a = 0..d-1                     (fixed geometric ladder; the
+ *                 notes' §2.2 rotation equation uses a learned per-dim frequency -- this
+ *                 ladder is the reading taken, first frequency 1 rad/token)
+ *   theta_rot  = theta + t * lambda_a                        [N] §2.2, rotation equation
+ *   kappa(t,s) = sum_a (1 + r_q r_k)(1 + cos(theta_q - theta_k + (t-s) lambda_a))
+ *                                                            [N] overview kappa equation
+ *   w(t,s)     = (kappa / c)^p, s <= t                       [N] §2.6 power normalisation
+ *   o_t        = sum_s w v_s / (sum_s w + eps)               [N] §2.6
+ *   Phi_a      = [1, cos th_rot, sin th_rot, r, r cos th_rot, r sin th_rot]
+ *                                                            [N] §2.3 six-channel block; [F]
+ *                stored channel-major: feature row c*d + a.
+ *   S_t = S_{t-1} + Phi(k_t) v_t^T, z_t = z_{t-1} + Phi(k_t),
+ *   o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c*eps)          [N] §2.7 recurrence and the
+ *                                                            normalising-constant paragraph
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_PI 3.14159265358979323846
+
+/* Angle map: [N] §2.2, phi(u) = pi u / (1 + |u|). */
+static double sanatan_angle(double u) { return ORACLE_PI * u / (1.0 + fabs(u)); }
+
+/* Soft root label from the unrotated angle: [N] §2.2 root equation. */
+static double sanatan_root(double theta, double omega, double gamma) {
+  return tanh(gamma * (cos(theta + omega) - sin(theta + omega)));
+}
+
+/* Rotation frequency of content dim a: base^(-a/d). */
+static double sanatan_freq(int a, int d, double base) { return pow(base, -(double)a / (double)d); }
+
+/* Exported so that tests can check angle/root/frequency at special points. */
+double oracle_angle(double u) { return sanatan_angle(u); }
+double oracle_root(double u, double omega, double gamma) { return sanatan_root(sanatan_angle(u), omega, gamma); }
+double oracle_freq(int a, int d, double base) { return sanatan_freq(a, d, base); }
+
+/*
+ * Feature map of T vectors u[T][d] at positions pos0..pos0+T-1 -> phi[T][6d], channel-major
+ * (row c*d + a; c = 0..5 for 1, cos, sin, r, r cos, r sin).  [N] §2.3, six-channel block.
+ */
+void oracle_features(const double* u, int T, int d, int64_t pos0, const double* omega, double gamma,
+                     double lambda_base, double* phi) {
+  for (int i = 0; i < T; i++) {
+    const double t = (double)(pos0 + i);
+    double* row = phi + (size_t)i * 6 * d;
+    for (int a = 0; a < d; a++) {
+      const double th = sanatan_angle(u[(size_t)i * d + a]);
+      const double r = sanatan_root(th, omega[a], gamma);
+      const double th_rot = th + t * sanatan_freq(a, d, lambda_base);
+      const double c = cos(th_rot), s = sin(th_rot);
+      row[0 * d + a] = 1.0;
+      row[1 * d + a] = c;
+      row[2 * d + a] = s;
+      row[3 * d + a] = r;
+      row[4 * d + a] = r * c;
+      row[5 * d + a] = r * s;
+    }
+  }
+}
+
+/*
+ * kappa between query q[d] at position t and key k[d] at position s, written as the
+ * sum of gate times angular similarity with the cosine of the rotated-angle
+ * difference -- NOT through the feature map.  [N] overview equation; §2.2 notes that
+ * the rotation enters only as (t - s) lambda.
+ */
+double oracle_kappa(const double* q, const double* k, int d, int64_t t, int64_t s, const double* omega,
+                    double gamma, double lambda_base) {
+  double acc = 0.0;
+  for (int a = 0; a < d; a++) {
+    const double thq = sanatan_angle(q[a]), thk = sanatan_angle(k[a]);
+    const double rq = sanatan_root(thq, omega[a], gamma), rk = sanatan_root(thk, omega[a], gamma);
+    const double dth = thq - thk + (double)(t - s) * sanatan_freq(a, d, lambda_base);
+    acc += (1.0 + rq * rk) * (1.0 + cos(dth));
+  }
+  return acc;
+}
+
+/*
+ * Normalised causal power attention, direct quadratic form, one head.
+ *   q,k [T][d], v [T][dv], positions pos0+i.  Output rows: all T rows when rows == NULL
+ *   (out [T][dv]), else only rows[0..n_rows) (out [n_rows][dv]).
+ * Weight w(t,s) = (kappa(t,s)/c)^p for s <= t, o_t = sum w v / (sum w + eps).
+ * [N] §2.6 normalised power attention; mask inclusive s <= t as in §2.7.
+ * The per-token angles and roots are tabulated first (they are per-token quantities of
+ * the definition); kappa itself is summed with the cosine of a difference per pair.
+ */
+void oracle_attention_direct(const double* q, const double* k, const double* v, int T, int d, int dv,
+                             int64_t pos0, const double* omega, double gamma, double lambda_base, double c,
+                             double eps, int p, const int* rows, int n_rows, double* out) {
+  (void)pos0; /* only t - s enters */
+  double* thq = (double*)malloc(sizeof(double) * (size_t)T * d);
+  double* thk = (double*)malloc(sizeof(double) * (size_t)T * d);
+  double* rq = (double*)malloc(sizeof(double) * (size_t)T * d);
+  double* rk = (double*)malloc(sizeof(double) * (size_t)T * d);
+  double* lam = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int a = 0; a < d; a++) lam[a] = sanatan_freq(a, d, lambda_base);
+  for (size_t i = 0; i < (size_t)T * d; i++) {
+    const int a = (int)(i % (size_t)d);
+    thq[i] = sanatan_angle(q[i]);
+    thk[i] = sanatan_angle(k[i]);
+    rq[i] = sanatan_root(thq[i], omega[a], gamma);
+    rk[i] = sanatan_root(thk[i], omega[a], gamma);
+  }
+  const int n_out = rows ? n_rows : T;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int j = 0; j < n_out; j++) {
+    const int t = rows ? rows[j] : j;
+    double* o = out + (size_t)j * dv;
+    double* num = (double*)calloc((size_t)dv, sizeof(double));
+    double den = 0.0;
+    for (int s = 0; s <= t; s++) {
+      double kap = 0.0;
+      for (int a = 0; a < d; a++) {
+        const double dth = thq[(size_t)t * d + a] - thk[(size_t)s * d + a] + (double)(t - s) * lam[a];
+        kap += (1.0 + rq[(size_t)t * d + a] * rk[(size_t)s * d + a]) * (1.0 + cos(dth));
+      }
+      double w = kap / c;
+      double wp = 1.0;
+      for (int e = 0; e < p; e++) wp *= w;
+      den += wp;
+      for (int n = 0; n < dv; n++) num[n] += wp * v[(size_t)s * dv + n];
+    }
+    for (int n = 0; n < dv; n++) o[n] = num[n] / (den + eps);
+    free(num);
+  }
+  free(thq);
+  free(thk);
+  free(rq);
+  free(rk);
+  free(lam);
+}
+
+/*
+ * p = 1 constant-state recurrence, one head, token by token.  [N] §2.7:
+ *   S_t = S_{t-1} + Phi(k_t) v_t^T ; z_t = z_{t-1} + Phi(k_t)   (write, then read)
+ *   o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c*eps)
+ * S [6d][dv] and z [6d] hold the initial state on entry and the final state on exit.
+ * out [T][dv] may be NULL (state only).
+ */
+void oracle_recurrent(const double* q, const double* k, const double* v, int T, int d, int dv, int64_t pos0,
+                      const double* omega, double gamma, double lambda_base, double c, double eps, double* S,
+                      double* z, double* out) {
+  const int D = 6 * d;
+  double* fq = (double*)malloc(sizeof(double) * (size_t)D);
+  double* fk = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int i = 0; i < T; i++) {
+    oracle_features(k + (size_t)i * d, 1, d, pos0 + i, omega, gamma, lambda_base, fk);
+    for (int f = 0; f < D; f++) {
+      z[f] += fk[f];
+      for (int n = 0; n < dv; n++) S[(size_t)f * dv + n] += fk[f] * v[(size_t)i * dv + n];
+    }
+    if (!out) continue;
+    oracle_features(q + (size_t)i * d, 1, d, pos0 + i, omega, gamma, lambda_base, fq);
+    double den = 0.0;
+    for (int f = 0; f < D; f++) den += fq[f] * z[f];
+    for (int n = 0; n < dv; n++) {
+      double num = 0.0;
+      for (int f = 0; f < D; f++) num += fq[f] * S[(size_t)f * dv + n];
+      out[(size_t)i * dv + n] = num / (den + c * eps);
+    }
+  }
+  free(fq);
+  free(fk);
+}
+
+/*
+ * Many independent heads of the recurrence, one OpenMP task per head.
+ *   q,k [NH][T][d], v [NH][T][dv]; omega rows: head j uses omega[(j % n_param_heads)*d ..].
+ *   S [NH][6d][dv], z [NH][6d] in/out; out [NH][T][dv] or NULL.
+ */
+void oracle_recurrent_heads(const double* q, const double* k, const double* v, int NH, int T, int d, int dv,
+                            int64_t pos0, const double* omega, int n_param_heads, double gamma,
+                            double lambda_base, double c, double eps, double* S, double* z, double* out) {
+  const size_t D = (size_t)6 * d;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int j = 0; j < NH; j++) {
+    oracle_recurrent(q + (size_t)j * T * d, k + (size_t)j * T * d, v + (size_t)j * T * dv, T, d, dv, pos0,
+                     omega + (size_t)(j % n_param_heads) * d, gamma, lambda_base, c, eps, S + (size_t)j * D * dv,
+                     z + (size_t)j * D, out ? out + (size_t)j * T * dv : NULL);
+  }
+}
+
+/* Number of threads OpenMP will use (reported next to oracle timings). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

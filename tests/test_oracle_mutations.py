@@ -1,0 +1,62 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a TEMPORARY COPY of oracle/oracle.c (a dropped term,
+a wrong sign or index, a transposed operand, a wrong mask or epsilon), rebuilds that copy and
+runs the pin suite against it: every planted mistake must make at least one pin fail.  The
+real oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTS = [
+  ("angle formula", "ORACLE_PI * u / (1.0 + fabs(u))", "ORACLE_PI * u / (1.0 + u * u)"),
+  ("root sign", "cos(theta + omega) - sin(theta + omega)", "cos(theta + omega) + sin(theta + omega)"),
+  ("root from rotated angle", "const double r = sanatan_root(th, omega[a], gamma);\n      const double th_rot = th + t * sanatan_freq(a, d, lambda_base);",
+     "const double th_rot = th + t * sanatan_freq(a, d, lambda_base);\n      const double r = sanatan_root(th_rot, omega[a], gamma);"),
+  ("feature rotation sign", "th + t * sanatan_freq", "th - t * sanatan_freq"),
+  ("kappa (t-s) sign", "(double)(t - s) * sanatan_freq(a, d, lambda_base)", "(double)(s - t) * sanatan_freq(a, d, lambda_base)"),
+  ("direct rotation sign", "+ (double)(t - s) * lam[a]", "- (double)(t - s) * lam[a]"),
+  ("direct mask strict", "for (int s = 0; s <= t; s++)", "for (int s = 0; s < t; s++)"),
+  ("direct eps scaled", "o[n] = num[n] / (den + eps)", "o[n] = num[n] / (den + c * eps)"),
+  ("recurrent eps unscaled", "num / (den + c * eps)", "num / (den + eps)"),
+  ("freq index", "-(double)a / (double)d", "-(double)(a + 1) / (double)d"),
+  ("power off by one", "for (int e = 0; e < p; e++)", "for (int e = 0; e <= p; e++)"),
+  ("channel 4 wrong", "row[4 * d + a] = r * c;", "row[4 * d + a] = r * s;"),
+  ("gate dropped", "acc += (1.0 + rq * rk) * (1.0 + cos(dth));", "acc += (1.0 + cos(dth));"),
+  ("direct gate dropped", "kap += (1.0 + rq[(size_t)t * d + a] * rk[(size_t)s * d + a]) * (1.0 + cos(dth));", "kap += 2.0 * (1.0 + cos(dth));"),
+  ("recurrent read before write", None, None),
+  ("S transposed", "S[(size_t)f * dv + n] += fk[f]", "S[(size_t)n * 6 * d + f] += fk[f]"),
+  ("direct weight not normalised by c", "double w = kap / c;", "double w = kap;"),
+]
+
+READ_BEFORE_WRITE = (
+    "    oracle_features(k + (size_t)i * d, 1, d, pos0 + i, omega, gamma, lambda_base, fk);\n"
+    "    for (int f = 0; f < D; f++) {\n      z[f] += fk[f];",
+    "    oracle_features(k + (size_t)i * d, 1, d, pos0 + i, omega, gamma, lambda_base, fk);\n"
+    "    if (i > 0) oracle_features(k + (size_t)(i-1) * d, 1, d, pos0 + i - 1, omega, gamma, lambda_base, fk);\n"
+    "    for (int f = 0; f < D; f++) {\n      z[f] += fk[f];",
+)
+
+
+@pytest.mark.parametrize("name,old,new", MUTS, ids=[m[0] for m in MUTS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    if name == "recurrent read before write":
+        old, new = READ_BEFORE_WRITE
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert old in src, "mutation anchor not found: " + name
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "*.tmp*", "__pycache__"))
+    (tmp_path / "tests" / "golden").mkdir(parents=True)
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copy(os.path.join(ROOT, "tests", "golden", "pages_values.json"), tmp_path / "tests" / "golden")
+    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "planted mistake '%s' passed every pin:\n%s" % (name, r.stdout[-2000:])
