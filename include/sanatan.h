@@ -1,0 +1,138 @@
+/*
+ * sanatan.h -- C ABI of libsanatan.so: SANATAN root-parity gated angular attention on gfx950.
+ *
+ * Method (cited by page title and section):
+ *   [N] "SANATAN: root-label gated angular kernel, exact recurrence and revised evidence"
+ *       (reading notes on the SANATAN v2 paper), §2.2 angle map / root label / rotation,
+ *       §2.3 six-channel feature map, §2.6 normalised power attention, §2.7 exact recurrence.
+ *   [F] The author's forum post restating the feature map and the p=1 recurrence.
+ *
+ * Per head, with content dim d, value dim d_v, positions t = pos0 + i:
+ *   theta = pi u / (1 + |u|)                                    [N] §2.2
+ *   r     = tanh(gamma (cos(theta + omega_a) - sin(theta + omega_a)))   (unrotated angle)
+ *   theta_rot = theta + t lambda_a,  lambda_a = lambda_base^(-a/d), a = 0..d-1
+ *   Phi   = [1, cos theta_rot, sin theta_rot, r, r cos theta_rot, r sin theta_rot]  [N] §2.3
+ *   kappa(t,s) = <Phi(q_t), Phi(k_s)> = sum_a (1 + r_q r_k)(1 + cos dtheta_rot)
+ *   p-th power attention: w = (kappa/c)^p, o_t = sum_{s<=t} w v_s / (sum_{s<=t} w + eps)  [N] §2.6
+ *   p = 1 recurrence: S_t = S_{t-1} + Phi(k_t) v_t^T, z_t = z_{t-1} + Phi(k_t),
+ *                     o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c eps)                     [N] §2.7
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE memory owned by the caller; contiguous row-major, last dim fastest.
+ *   - Feature vectors and state rows use channel-major order: feature row c*d + a, channel
+ *     c = 0..5 for (1, cos, sin, r, r cos, r sin).  (The notes concatenate per-dim blocks;
+ *     kappa is invariant to the permutation.)
+ *   - The library never allocates device memory inside a call and keeps no state between calls
+ *     beyond cached device properties.  Calls are asynchronous on `stream`; errors are returned as
+ *     status codes, never thrown.  Arguments are validated on the host BEFORE any launch; on a
+ *     non-OK status nothing has been launched, except SANATAN_ERR_HIP, which reports a launch
+ *     failure (hipGetLastError) after the fact.
+ *   - Only d = d_v = 64 is implemented; other values return SANATAN_ERR_UNSUPPORTED.
+ *   - Calls that share output or state buffers on overlapping streams race; order them on one stream.
+ *   - NaN/Inf inputs propagate; they are not checked.
+ */
+#ifndef SANATAN_H
+#define SANATAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SANATAN_OK = 0,
+  SANATAN_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, unknown enum, bad parameter value */
+  SANATAN_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (d or d_v != 64, chunk not supported) */
+  SANATAN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the matching *_workspace_bytes() */
+  SANATAN_ERR_HIP = 4          /* a kernel launch failed */
+} sanatan_status;
+
+typedef enum { SANATAN_F32 = 0, SANATAN_BF16 = 1 } sanatan_dtype;
+
+/* Method parameters. The struct itself is host memory, read during the call only. */
+typedef struct {
+  int d;               /* content dims per head; must be 64 */
+  int d_v;             /* value dims per head; must be 64 */
+  float gamma;         /* root sharpness gamma (>= 0) */
+  float c;             /* score normaliser c (> 0); the notes use 4d */
+  float eps;           /* normalised epsilon (>= 0); denominators are sum(kappa) + c*eps */
+  double lambda_base;  /* rotation ladder base (> 0): lambda_a = lambda_base^(-a/d) */
+  const float* omega;  /* DEVICE [n_param_heads][d] fp32 root anchors omega (learned per head in [N]) */
+  int n_param_heads;   /* head h (or head-state i) uses omega row h % n_param_heads; >= 1 */
+} sanatan_params;
+
+/* Bytes of one head's fp32 recurrent state: S [6d][d_v] plus z [6d].  [N] §4.5 memory equation. */
+size_t sanatan_state_bytes(int d, int d_v);
+
+/*
+ * sanatan_featurize -- the feature map Phi of every vector of u.  [N] §2.2-§2.3.
+ *   u    : [B][H][T][d], element type in_t (F32 or BF16).
+ *   pos0 : position of u[..][..][0]; token i sits at pos0 + i (any int64 with |pos| < 2^53).
+ *   phi  : [B][H][T][6d], element type out_t; row c*d + a as above.
+ * Head h uses omega row h % n_param_heads.  Returns INVALID_ARG for NULL pointers or
+ * B, H, T <= 0; UNSUPPORTED for d != 64.
+ */
+sanatan_status sanatan_featurize(const void* u, sanatan_dtype in_t, int B, int H, int T, int64_t pos0,
+                                 const sanatan_params* params, void* phi, sanatan_dtype out_t,
+                                 hipStream_t stream);
+
+/* Workspace bytes sanatan_prefill_chunked needs for these sizes (0 on invalid sizes). */
+size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const sanatan_params* params);
+
+/*
+ * sanatan_prefill_chunked -- normalised causal p=1 attention over whole sequences, computed as
+ * the exact chunked regrouping of the recurrence of [N] §2.7: within a chunk the masked product
+ * mask(Phi(Q) Phi(K)^T) V, across chunks the readout Phi(Q) S; S += Phi(K)^T V after each chunk.
+ *   q, k  : [B][H][T][d],  v : [B][H][T][d_v], element type t (F32 or BF16).
+ *   chunk : chunk length in tokens; one of 16, 32, 64, 128 (128 with BF16 only).
+ *   pos0  : position of token 0.
+ *   S, z  : both NULL -> start from the zero state and do not return a final state;
+ *           both non-NULL -> fp32 S [B][H][6d][d_v], z [B][H][6d] hold the initial state on entry
+ *           and the state after the last token on exit (in place).  One NULL -> INVALID_ARG.
+ *   out   : [B][H][T][d_v], element type t; o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c eps).
+ *   ws    : device workspace of at least sanatan_prefill_workspace_bytes() bytes, else WORKSPACE.
+ * Accumulation is fp32; with BF16 inputs the products run on bf16 MFMA with fp32 accumulation.
+ */
+sanatan_status sanatan_prefill_chunked(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                       int H, int T, int chunk, int64_t pos0, const sanatan_params* params,
+                                       float* S, float* z, void* out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/*
+ * sanatan_decode_step -- one token of the p=1 constant-state recurrence for N independent
+ * head-states (e.g. batch x layers x heads).  [N] §2.7: write the token into the state, then read.
+ *   q, k : [N][d] fp32;  v : [N][d_v] fp32;  pos : position of this token (shared by all N).
+ *   S    : [N][6d][d_v] fp32, z : [N][6d] fp32, updated in place.
+ *   out  : [N][d_v] fp32.
+ * Head-state i uses omega row i % n_param_heads.  Streams each state once (read + write).
+ */
+sanatan_status sanatan_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                   const sanatan_params* params, float* S, float* z, float* out,
+                                   hipStream_t stream);
+
+/* Workspace bytes sanatan_quadratic_ref_p2 needs (0 on invalid sizes). */
+size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params);
+
+/*
+ * sanatan_quadratic_ref_p2 -- normalised causal power attention in its masked quadratic
+ * (training) form, no recurrence: w = (kappa/c)^p, o_t = sum_{s<=t} w v_s / (sum w + eps).
+ * [N] §2.6; p = 2 is the sharpened kernel trained first in [N] §4.1, p = 1 the deployed one.
+ *   q, k : [B][H][T][d], v, out : [B][H][T][d_v], element type t; p : 1 or 2 (else INVALID_ARG).
+ *   ws   : at least sanatan_quadratic_workspace_bytes() bytes (holds Phi(K) in element type t).
+ */
+sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                        int H, int T, int p, int64_t pos0, const sanatan_params* params,
+                                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static human-readable name of a status code. */
+const char* sanatan_status_string(sanatan_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANATAN_H */

@@ -1,0 +1,231 @@
+"""Thin ctypes binding of libsanatan.so -- SANATAN root-parity gated attention on MI355X (gfx950).
+
+Every function here has the name of the C entry point it wraps and only marshals arguments:
+checks that tensors are contiguous CUDA/HIP tensors of the expected dtype, allocates outputs and
+workspaces with torch when the caller passes none, and forwards raw pointers plus the current
+stream.  All arithmetic runs in the library's kernels.  If the library has not been built this
+module raises instead of falling back to anything else.
+
+Build the library with ``python -m root_parity_gated_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsanatan.so")
+
+SANATAN_OK, SANATAN_ERR_INVALID_ARG, SANATAN_ERR_UNSUPPORTED, SANATAN_ERR_WORKSPACE, SANATAN_ERR_HIP = range(5)
+SANATAN_F32, SANATAN_BF16 = 0, 1
+D = 64
+DV = 64
+
+
+class SanatanError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sanatan_status_string(status)} (status {status})")
+
+
+class sanatan_params(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int),
+        ("d_v", ctypes.c_int),
+        ("gamma", ctypes.c_float),
+        ("c", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("lambda_base", ctypes.c_double),
+        ("omega", ctypes.c_void_p),
+        ("n_param_heads", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m root_parity_gated_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        pp = ctypes.POINTER(sanatan_params)
+        L.sanatan_state_bytes.restype = sz
+        L.sanatan_state_bytes.argtypes = [i32, i32]
+        L.sanatan_status_string.restype = ctypes.c_char_p
+        L.sanatan_status_string.argtypes = [i32]
+        L.sanatan_featurize.restype = i32
+        L.sanatan_featurize.argtypes = [vp, i32, i32, i32, i32, i64, pp, vp, i32, vp]
+        L.sanatan_prefill_workspace_bytes.restype = sz
+        L.sanatan_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
+        L.sanatan_prefill_chunked.restype = i32
+        L.sanatan_prefill_chunked.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp, sz, vp]
+        L.sanatan_decode_step.restype = i32
+        L.sanatan_decode_step.argtypes = [vp, vp, vp, i32, i64, pp, vp, vp, vp, vp]
+        L.sanatan_quadratic_workspace_bytes.restype = sz
+        L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
+        L.sanatan_quadratic_ref_p2.restype = i32
+        L.sanatan_quadratic_ref_p2.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+EXPORTED = [
+    "sanatan_state_bytes", "sanatan_status_string", "sanatan_featurize", "sanatan_prefill_workspace_bytes",
+    "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_quadratic_workspace_bytes",
+    "sanatan_quadratic_ref_p2",
+]
+
+
+@dataclass
+class Params:
+    """Method parameters; `omega` is a device fp32 tensor [n_param_heads, d]."""
+    omega: object
+    gamma: float = 4.0
+    c: float | None = None
+    eps: float = 1e-6
+    lambda_base: float = 10000.0
+    d: int = D
+    d_v: int = DV
+
+    def struct(self) -> sanatan_params:
+        om = self.omega
+        if om is None:
+            ptr, nph = None, 1
+        else:
+            _check_tensor(om, "omega", dtypes=("float32",))
+            ptr, nph = om.data_ptr(), int(om.shape[0]) if om.dim() == 2 else 1
+        c = float(4 * self.d) if self.c is None else float(self.c)
+        return sanatan_params(int(self.d), int(self.d_v), float(self.gamma), c, float(self.eps),
+                              float(self.lambda_base), ptr, nph)
+
+
+def sanatan_status_string(status: int) -> str:
+    return lib().sanatan_status_string(int(status)).decode()
+
+
+def sanatan_state_bytes(d: int = D, d_v: int = DV) -> int:
+    return int(lib().sanatan_state_bytes(int(d), int(d_v)))
+
+
+def _check(status: int, where: str):
+    if status != SANATAN_OK:
+        raise SanatanError(status, where)
+
+
+def _check_tensor(t, name, dtypes=("float32", "bfloat16")):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    return SANATAN_BF16 if t.dtype == torch.bfloat16 else SANATAN_F32
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def sanatan_featurize(u, pos0: int, params: Params, out_dtype=None, out=None):
+    """Phi of u [B,H,T,64] at positions pos0.. -> [B,H,T,384] (channel-major feature rows)."""
+    import torch
+
+    _check_tensor(u, "u")
+    B, H, T, d = u.shape
+    out_dtype = u.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, T, 6 * d), dtype=out_dtype, device=u.device)
+    _check_tensor(out, "phi")
+    p = params.struct()
+    _check(lib().sanatan_featurize(_ptr(u), _dtype_code(u), B, H, T, int(pos0), ctypes.byref(p), _ptr(out),
+                                   _dtype_code(out), _stream()), "sanatan_featurize")
+    return out
+
+
+def sanatan_prefill_workspace_bytes(B: int, H: int, T: int, chunk: int, params: Params | None = None) -> int:
+    p = params.struct() if params is not None else None
+    return int(lib().sanatan_prefill_workspace_bytes(B, H, T, chunk, ctypes.byref(p) if p is not None else None))
+
+
+def sanatan_prefill_chunked(q, k, v, chunk: int, params: Params, pos0: int = 0, S=None, z=None, out=None, ws=None):
+    """Chunked causal p=1 attention; S, z (fp32, in/out) optional.  Returns out [B,H,T,64]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name)
+    B, H, T, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, T, v.shape[-1]), dtype=q.dtype, device=q.device)
+    _check_tensor(out, "out")
+    for name, t in (("S", S), ("z", z)):
+        if t is not None:
+            _check_tensor(t, name, dtypes=("float32",))
+    p = params.struct()
+    need = int(lib().sanatan_prefill_workspace_bytes(B, H, T, chunk, ctypes.byref(p)))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().sanatan_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(chunk), int(pos0),
+                                         ctypes.byref(p), _ptr(S), _ptr(z), _ptr(out), _ptr(ws), ws.numel(),
+                                         _stream()), "sanatan_prefill_chunked")
+    return out
+
+
+def sanatan_decode_step(q, k, v, pos: int, params: Params, S, z, out=None):
+    """One token for N head-states: q,k [N,64], v [N,64] fp32; S [N,384,64], z [N,384] in/out."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("S", S), ("z", z)):
+        _check_tensor(t, name, dtypes=("float32",))
+    N = q.shape[0]
+    if out is None:
+        out = torch.empty((N, v.shape[-1]), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", dtypes=("float32",))
+    p = params.struct()
+    _check(lib().sanatan_decode_step(_ptr(q), _ptr(k), _ptr(v), N, int(pos), ctypes.byref(p), _ptr(S), _ptr(z),
+                                     _ptr(out), _stream()), "sanatan_decode_step")
+    return out
+
+
+def sanatan_quadratic_workspace_bytes(B: int, H: int, T: int, dtype_code: int, params: Params | None = None) -> int:
+    p = params.struct() if params is not None else None
+    return int(lib().sanatan_quadratic_workspace_bytes(B, H, T, dtype_code, ctypes.byref(p) if p is not None else None))
+
+
+def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, ws=None):
+    """Masked quadratic normalised power attention (p = 1 or 2).  Returns out [B,H,T,64]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name)
+    B, H, T, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, T, v.shape[-1]), dtype=q.dtype, device=q.device)
+    _check_tensor(out, "out")
+    p = params.struct()
+    need = int(lib().sanatan_quadratic_workspace_bytes(B, H, T, _dtype_code(q), ctypes.byref(p)))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().sanatan_quadratic_ref_p2(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(p_exp), int(pos0),
+                                          ctypes.byref(p), _ptr(out), _ptr(ws), ws.numel(), _stream()),
+           "sanatan_quadratic_ref_p2")
+    return out

@@ -1,0 +1,123 @@
+// api.hip -- the C ABI of libsanatan.so: argument validation on the host, then launches.
+// Every check happens before the first launch, so a non-OK status (other than
+// SANATAN_ERR_HIP) means nothing was enqueued.
+#include <math.h>
+
+#include "launchers.h"
+#include "sanatan.h"
+#include "sanatan_device.h"
+
+using namespace sanatan;
+
+namespace {
+
+sanatan_status check_params(const sanatan_params* p) {
+  if (!p || !p->omega) return SANATAN_ERR_INVALID_ARG;
+  if (p->n_param_heads < 1) return SANATAN_ERR_INVALID_ARG;
+  if (!(p->gamma >= 0.0f) || !isfinite(p->gamma)) return SANATAN_ERR_INVALID_ARG;
+  if (!(p->c > 0.0f) || !isfinite(p->c)) return SANATAN_ERR_INVALID_ARG;
+  if (!(p->eps >= 0.0f) || !isfinite(p->eps)) return SANATAN_ERR_INVALID_ARG;
+  if (!(p->lambda_base > 0.0) || !isfinite(p->lambda_base)) return SANATAN_ERR_INVALID_ARG;
+  if (p->d <= 0 || p->d_v <= 0) return SANATAN_ERR_INVALID_ARG;
+  if (p->d != kD || p->d_v != kDV) return SANATAN_ERR_UNSUPPORTED;
+  return SANATAN_OK;
+}
+
+bool dtype_ok(sanatan_dtype t) { return t == SANATAN_F32 || t == SANATAN_BF16; }
+
+MethodConsts consts(const sanatan_params* p) {
+  MethodConsts mc;
+  mc.omega = p->omega;
+  mc.nph = p->n_param_heads;
+  mc.kr = (float)(2.0 * 1.4142135623730950488 * (double)p->gamma * 1.4426950408889634074);
+  mc.log2_base = log2(p->lambda_base);
+  mc.ceps = (float)((double)p->c * (double)p->eps);
+  mc.inv_c = (float)(1.0 / (double)p->c);
+  mc.eps = p->eps;
+  return mc;
+}
+
+// Sizes whose element counts must stay addressable with the kernels' index arithmetic.
+bool sizes_ok(int B, int H, int T) {
+  if (B <= 0 || H <= 0 || T <= 0) return false;
+  const long long tokens = (long long)B * H * T;
+  return tokens * kF < (1LL << 40);
+}
+
+sanatan_status hip_status(hipError_t e) { return e == hipSuccess ? SANATAN_OK : SANATAN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sanatan_state_bytes(int d, int d_v) {
+  if (d <= 0 || d_v <= 0) return 0;
+  return ((size_t)6 * d * d_v + (size_t)6 * d) * sizeof(float);
+}
+
+const char* sanatan_status_string(sanatan_status status) {
+  switch (status) {
+    case SANATAN_OK: return "ok";
+    case SANATAN_ERR_INVALID_ARG: return "invalid argument";
+    case SANATAN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SANATAN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SANATAN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+sanatan_status sanatan_featurize(const void* u, sanatan_dtype in_t, int B, int H, int T, int64_t pos0,
+                                 const sanatan_params* params, void* phi, sanatan_dtype out_t, hipStream_t stream) {
+  if (!u || !phi || !dtype_ok(in_t) || !dtype_ok(out_t) || !sizes_ok(B, H, T)) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  return hip_status(launch_featurize(u, in_t, B, H, T, pos0, consts(params), phi, out_t, stream));
+}
+
+size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const sanatan_params* params) {
+  (void)params;
+  PrefillPlan plan;
+  if (!sizes_ok(B, H, T) || chunk <= 0 || !prefill_plan(B, H, T, chunk, &plan)) return 0;
+  return plan.total_bytes;
+}
+
+sanatan_status sanatan_prefill_chunked(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
+                                       int T, int chunk, int64_t pos0, const sanatan_params* params, float* S,
+                                       float* z, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || chunk <= 0) return SANATAN_ERR_INVALID_ARG;
+  if ((S == nullptr) != (z == nullptr)) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (chunk % 16 != 0 || !prefill_chunk_supported(chunk, t)) return SANATAN_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!prefill_plan(B, H, T, chunk, &plan)) return SANATAN_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < plan.total_bytes) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_prefill(q, k, v, t, B, H, T, pos0, consts(params), S, z, out, ws, plan, stream));
+}
+
+sanatan_status sanatan_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                   const sanatan_params* params, float* S, float* z, float* out, hipStream_t stream) {
+  if (!q || !k || !v || !S || !z || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  return hip_status(launch_decode_step(q, k, v, N, pos, consts(params), S, z, out, stream));
+}
+
+size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params) {
+  (void)params;
+  if (!sizes_ok(B, H, T) || !dtype_ok(t)) return 0;
+  return quadratic_ws_bytes(B, H, T, t);
+}
+
+sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
+                                        int T, int p, int64_t pos0, const sanatan_params* params, void* out, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || (p != 1 && p != 2))
+    return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (!ws || ws_bytes < quadratic_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, pos0, consts(params), out, ws, stream));
+}
+
+}  // extern "C"

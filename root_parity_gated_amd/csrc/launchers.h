@@ -1,0 +1,55 @@
+// launchers.h -- host-side interface between the C ABI (api.hip) and the kernel files.
+// All sizes have been validated by the caller; launchers only compute grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sanatan.h"
+
+namespace sanatan {
+
+// Method constants prepared once per call on the host.
+struct MethodConsts {
+  const float* omega;   // device [nph][64]
+  int nph;              // omega rows
+  float kr;             // 2 sqrt2 gamma log2(e)
+  double log2_base;     // log2(lambda_base)
+  float ceps;           // c * eps (raw-unit epsilon)
+  float inv_c;          // 1 / c
+  float eps;            // normalised epsilon
+};
+
+// rho[t][a] = frac((pos0 + t) lambda_a / 2pi), t < T (fp32 table, fp64 reduction)
+hipError_t launch_phase_table(float* rho, int T, int64_t pos0, double log2_base, hipStream_t stream);
+
+hipError_t launch_featurize(const void* u, sanatan_dtype in_t, int B, int H, int T, int64_t pos0,
+                            const MethodConsts& mc, void* phi, sanatan_dtype out_t, hipStream_t stream);
+
+hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
+                              const MethodConsts& mc, float* S, float* z, float* out, hipStream_t stream);
+
+// Prefill plan: the flattened (sequence, chunk) list split into G equal ranges (one workgroup
+// each) and the workspace layout (phase table, then boundary-state slots).
+struct PrefillPlan {
+  int chunk;            // tokens per chunk
+  int ncs;              // chunks per sequence
+  int G;                // workgroups
+  long long total;      // B*H*ncs chunks
+  int multi;            // some sequence spans several ranges (pass 1 + scan needed)
+  size_t rho_bytes;     // phase table [T][64] fp32
+  size_t state_bytes;   // (B*H + G - 1) boundary states of kStateFloats fp32
+  size_t total_bytes;
+};
+bool prefill_plan(int B, int H, int T, int chunk, PrefillPlan* plan);
+bool prefill_chunk_supported(int chunk, sanatan_dtype t);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                          int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,
+                          const PrefillPlan& plan, hipStream_t stream);
+
+size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t);
+hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                            int p, int64_t pos0, const MethodConsts& mc, void* out, void* ws, hipStream_t stream);
+
+}  // namespace sanatan

@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function declared in
+include/sanatan.h, and rejects bad arguments with the documented status codes before any launch.
+Pointers passed here are never dereferenced on the host (validation fails first)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import root_parity_gated_amd as rpg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sanatan.h")
+FAKE = ctypes.c_void_p(0x1000)  # non-null, never dereferenced by the validation paths exercised here
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_values.json")))
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sanatan_\w+)\s*\(", src)))
+
+
+def params(**kw):
+    p = dict(d=64, d_v=64, gamma=4.0, c=256.0, eps=1e-6, lambda_base=10000.0, omega=0x2000, n_param_heads=1)
+    p.update(kw)
+    return rpg.sanatan_params(p["d"], p["d_v"], p["gamma"], p["c"], p["eps"], p["lambda_base"], p["omega"],
+                              p["n_param_heads"])
+
+
+@pytest.fixture(scope="module")
+def L():
+    return rpg.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(rpg.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_state_bytes_matches_pages(L):
+    assert L.sanatan_state_bytes(64, 64) == GOLD["state_bytes_per_head_d64"]["value"]
+    assert 144 * L.sanatan_state_bytes(64, 64) == GOLD["state_bytes_12layers_12heads_d64"]["value"]
+    assert L.sanatan_state_bytes(0, 64) == 0
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.sanatan_status_string(s)
+    assert b"unknown" in L.sanatan_status_string(99)
+
+
+def _prefill(L, p, q=FAKE, t=rpg.SANATAN_BF16, B=1, H=1, T=128, chunk=64, S=None, z=None, ws=FAKE, ws_bytes=1 << 40):
+    return L.sanatan_prefill_chunked(q, FAKE, FAKE, t, B, H, T, chunk, 0, ctypes.byref(p), S, z, FAKE, ws, ws_bytes,
+                                     None)
+
+
+def test_prefill_validation(L):
+    p = params()
+    assert _prefill(L, p, q=None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert _prefill(L, p, T=0) == rpg.SANATAN_ERR_INVALID_ARG
+    assert _prefill(L, p, B=-1) == rpg.SANATAN_ERR_INVALID_ARG
+    assert _prefill(L, p, chunk=0) == rpg.SANATAN_ERR_INVALID_ARG
+    assert _prefill(L, p, t=7) == rpg.SANATAN_ERR_INVALID_ARG
+    assert _prefill(L, p, S=FAKE, z=None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert _prefill(L, p, chunk=48) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert _prefill(L, p, chunk=24) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert _prefill(L, p, chunk=128, t=rpg.SANATAN_F32) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert _prefill(L, params(d=32)) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert _prefill(L, params(d_v=128)) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert _prefill(L, p, ws=None) == rpg.SANATAN_ERR_WORKSPACE
+    assert _prefill(L, p, ws_bytes=16) == rpg.SANATAN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("bad", [dict(omega=0), dict(n_param_heads=0), dict(gamma=-1.0), dict(gamma=float("nan")),
+                                 dict(c=0.0), dict(c=float("inf")), dict(eps=-1e-3), dict(lambda_base=0.0),
+                                 dict(d=0)])
+def test_param_validation(L, bad):
+    assert _prefill(L, params(**bad)) == rpg.SANATAN_ERR_INVALID_ARG
+
+
+def test_featurize_decode_quadratic_validation(L):
+    p = params()
+    assert L.sanatan_featurize(None, 0, 1, 1, 8, 0, ctypes.byref(p), FAKE, 0, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_featurize(FAKE, 0, 1, 1, 0, 0, ctypes.byref(p), FAKE, 0, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_featurize(FAKE, 0, 1, 1, 8, 0, ctypes.byref(params(d=16)), FAKE, 0,
+                               None) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert L.sanatan_decode_step(FAKE, FAKE, FAKE, 0, 0, ctypes.byref(p), FAKE, FAKE, FAKE,
+                                 None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_decode_step(FAKE, FAKE, FAKE, 4, 0, ctypes.byref(p), None, FAKE, FAKE,
+                                 None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_decode_step(FAKE, FAKE, FAKE, 4, 0, None, FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    for pe in (0, 3):
+        assert L.sanatan_quadratic_ref_p2(FAKE, FAKE, FAKE, 1, 1, 1, 64, pe, 0, ctypes.byref(p), FAKE, FAKE, 1 << 40,
+                                          None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_quadratic_ref_p2(FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, 0, ctypes.byref(p), FAKE, FAKE, 10,
+                                      None) == rpg.SANATAN_ERR_WORKSPACE
+
+
+def test_workspace_sizes(L):
+    p = params()
+    assert L.sanatan_prefill_workspace_bytes(0, 1, 64, 64, ctypes.byref(p)) == 0
+    assert L.sanatan_prefill_workspace_bytes(1, 1, 64, 0, ctypes.byref(p)) == 0
+    assert L.sanatan_quadratic_workspace_bytes(1, 1, 0, 1, ctypes.byref(p)) == 0
+    # quadratic: Phi(K) in the element type, [B,H,T,384]
+    assert L.sanatan_quadratic_workspace_bytes(4, 12, 4096, rpg.SANATAN_BF16, ctypes.byref(p)) == 4 * 12 * 4096 * 384 * 2
+    assert L.sanatan_quadratic_workspace_bytes(1, 1, 256, rpg.SANATAN_F32, ctypes.byref(p)) == 256 * 384 * 4
+    # prefill: phase table [T][64] fp32 (256-byte aligned) + one boundary state per (sequence + range - 1)
+    ws = L.sanatan_prefill_workspace_bytes(8, 12, 2048, 64, ctypes.byref(p))
+    state = L.sanatan_state_bytes(64, 64)
+    rho = 2048 * 64 * 4
+    G = (ws - rho) // state - 96 + 1
+    assert (ws - rho) % state == 0 and 1 <= G <= 3072

@@ -1,0 +1,208 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerance: max over rows of ||o - o_ref||_inf / max(||o_ref||_inf, 1e-12) <= 1e-4 for fp32 inputs and
+<= 2e-2 for bf16 inputs (fp32 accumulation).  The oracle always sees exactly the values the GPU sees
+(bf16 inputs are generated bf16-exact).  Inputs come from sanatan_inputs (seeded N(0,1), omega ~ U(-pi,pi)).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import sanatan_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import root_parity_gated_amd as rpg
+
+    rpg.lib()  # fail loudly if the library is missing
+    return torch
+
+
+def dev(torch, x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def params(torch, omega, **kw):
+    import root_parity_gated_amd as rpg
+
+    return rpg.Params(omega=torch.from_numpy(np.ascontiguousarray(omega, dtype=np.float32)).cuda(), **kw)
+
+
+def row_rel_err(got, want):
+    got = np.asarray(got, np.float64).reshape(-1, want.shape[-1])
+    want = np.asarray(want, np.float64).reshape(-1, want.shape[-1])
+    num = np.abs(got - want).max(1)
+    den = np.maximum(np.abs(want).max(1), 1e-12)
+    return float((num / den).max())
+
+
+def oracle_heads(q, k, v, omega, pos0=0, eps=1e-6, S=None, z=None):
+    """Recurrent fp64 oracle over [B,H,T,*] inputs; omega [H,d]. Returns out, S, z with [B,H,...] shapes."""
+    B, H, T, d = q.shape
+    om = np.tile(omega, (B, 1))
+    out, S2, z2 = oracle.recurrent_heads(q.reshape(B * H, T, d), k.reshape(B * H, T, d),
+                                         v.reshape(B * H, T, -1), om, pos0=pos0, eps=eps,
+                                         S=None if S is None else S.reshape(B * H, *S.shape[2:]),
+                                         z=None if z is None else z.reshape(B * H, -1))
+    return out.reshape(B, H, T, -1), S2.reshape(B, H, *S2.shape[1:]), z2.reshape(B, H, -1)
+
+
+# ----------------------------------------------------------------------------------- featurize
+@pytest.mark.parametrize("dtype,pos0", [("f32", 0), ("f32", 1_000_003), ("bf16", 17)])
+def test_featurize_matches_oracle(torch_dev, dtype, pos0):
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    q, k, v, om = si.attention_inputs(7, 2, 3, 50, dtype)
+    u = q * 2.5
+    u = si.bf16_round(u) if dtype == "bf16" else u
+    phi = rpg.sanatan_featurize(dev(torch, u, dtype), pos0, params(torch, om), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = host(phi)
+    # fp32 bound: the revolution-domain arguments carry ~2^-24 rev of rounding (3.7e-7 rad) plus the
+    # hardware sin/cos error (1.2e-7); the root label amplifies its argument error by at most
+    # gamma*sqrt(2) (= 5.7 at gamma = 4), so |r - r_ref| <~ 3e-6 and the r*cos, r*sin channels add ~1e-6.
+    tol = 2.0 ** -24 * 2 * np.pi * 4.0 * np.sqrt(2) * 2 + 2e-6
+    for b in range(2):
+        for h in range(3):
+            want = oracle.features(u[b, h], pos0, om[h])
+            assert np.abs(got[b, h] - want).max() < tol, (b, h)
+    phib = rpg.sanatan_featurize(dev(torch, u, dtype), pos0, params(torch, om), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.abs(host(phib) - got).max() <= 2.0 ** -8
+
+
+# ----------------------------------------------------------------------------------- decode
+def test_decode_steps_match_recurrence(torch_dev):
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    N, steps = 144, 40
+    om, _, (sq, sk, sv) = si.decode_inputs_numpy(3, N, 1, steps)
+    p = params(torch, om)
+    S = torch.zeros((N, 384, 64), device="cuda")
+    z = torch.zeros((N, 384), device="cuda")
+    outs = []
+    for i in range(steps):
+        outs.append(rpg.sanatan_decode_step(dev(torch, sq[i], "f32"), dev(torch, sk[i], "f32"),
+                                            dev(torch, sv[i], "f32"), 100 + i, p, S, z).clone())
+    torch.cuda.synchronize()
+    got = np.stack([host(o) for o in outs], 1)  # [N, steps, 64]
+    want, Sw, zw = oracle.recurrent_heads(sq.transpose(1, 0, 2), sk.transpose(1, 0, 2), sv.transpose(1, 0, 2), om,
+                                          pos0=100)
+    assert row_rel_err(got, want) <= TOL["f32"]
+    assert np.abs(host(S) - Sw).max() <= 1e-4 * max(1.0, np.abs(Sw).max())
+    assert np.abs(host(z) - zw).max() <= 1e-4 * max(1.0, np.abs(zw).max())
+
+
+# ----------------------------------------------------------------------------------- prefill
+@pytest.mark.parametrize("dtype,chunk", [("f32", 16), ("f32", 32), ("f32", 64), ("bf16", 16), ("bf16", 32),
+                                         ("bf16", 64), ("bf16", 128)])
+def test_prefill_tiny_all_chunks(torch_dev, dtype, chunk):
+    """Tiny workload (B1 H1 T256, d=64) in chunked form vs the direct and recurrent oracles."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    w = si.TINY
+    q, k, v, om = si.attention_inputs(w.seed, 1, 1, 256, dtype)
+    out = rpg.sanatan_prefill_chunked(dev(torch, q, dtype), dev(torch, k, dtype), dev(torch, v, dtype), chunk,
+                                      params(torch, om))
+    torch.cuda.synchronize()
+    direct = oracle.attention_direct(q[0, 0], k[0, 0], v[0, 0], om[0])
+    assert row_rel_err(host(out)[0, 0], direct) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,chunk,B,H,T", [("f32", 64, 2, 3, 200), ("bf16", 64, 2, 3, 200),
+                                               ("bf16", 16, 4, 8, 496), ("bf16", 128, 1, 2, 333),
+                                               ("f32", 32, 3, 2, 77)])
+def test_prefill_ragged_multi_piece_with_state(torch_dev, dtype, chunk, B, H, T):
+    """Ragged tails, ranges that cross sequence boundaries, a given initial state and the final state."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    q, k, v, om = si.attention_inputs(11 + T, B, H, T + 40, dtype)
+    # initial state: the recurrence over 40 earlier tokens (built by the oracle on the CPU side and by the
+    # GPU prefill on the GPU side -- each side from the same tokens)
+    pre = slice(0, 40)
+    _, S0, z0 = oracle_heads(q[:, :, pre], k[:, :, pre], v[:, :, pre], om)
+    Sg = torch.zeros((B, H, 384, 64), device="cuda")
+    zg = torch.zeros((B, H, 384), device="cuda")
+    rpg.sanatan_prefill_chunked(dev(torch, q[:, :, pre], dtype), dev(torch, k[:, :, pre], dtype),
+                                dev(torch, v[:, :, pre], dtype), chunk, params(torch, om), S=Sg, z=zg)
+    main = slice(40, 40 + T)
+    out = rpg.sanatan_prefill_chunked(dev(torch, q[:, :, main], dtype), dev(torch, k[:, :, main], dtype),
+                                      dev(torch, v[:, :, main], dtype), chunk, params(torch, om), pos0=40, S=Sg, z=zg)
+    torch.cuda.synchronize()
+    want, Sw, zw = oracle_heads(q[:, :, main], k[:, :, main], v[:, :, main], om, pos0=40, S=S0, z=z0)
+    assert row_rel_err(host(out), want) <= TOL[dtype]
+    tol_s = 1e-4 if dtype == "f32" else 2e-2
+    assert np.abs(host(Sg) - Sw).max() <= tol_s * np.abs(Sw).max()
+    assert np.abs(host(zg) - zw).max() <= tol_s * np.abs(zw).max()
+
+
+def test_prefill_single_workgroup_and_determinism(torch_dev, monkeypatch):
+    """One workgroup walking every sequence (SANATAN_PREFILL_WGS=1) gives the same result up to
+    rounding, and repeated runs are bitwise identical."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    q, k, v, om = si.attention_inputs(5, 2, 2, 160, "bf16")
+    args = [dev(torch, x, "bf16") for x in (q, k, v)]
+    a = rpg.sanatan_prefill_chunked(*args, 32, params(torch, om)).clone()
+    b = rpg.sanatan_prefill_chunked(*args, 32, params(torch, om)).clone()
+    monkeypatch.setenv("SANATAN_PREFILL_WGS", "1")
+    c = rpg.sanatan_prefill_chunked(*args, 32, params(torch, om)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    want, _, _ = oracle_heads(q, k, v, om)
+    assert row_rel_err(host(c), want) <= TOL["bf16"]
+    assert row_rel_err(host(a), want) <= TOL["bf16"]
+
+
+def test_prefill_position_shift(torch_dev):
+    """Shifting every position by 10^6 leaves the output unchanged (only t - s enters kappa)."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    q, k, v, om = si.attention_inputs(9, 1, 2, 128, "f32")
+    args = [dev(torch, x, "f32") for x in (q, k, v)]
+    a = rpg.sanatan_prefill_chunked(*args, 64, params(torch, om), pos0=0)
+    b = rpg.sanatan_prefill_chunked(*args, 64, params(torch, om), pos0=1_000_000)
+    torch.cuda.synchronize()
+    want, _, _ = oracle_heads(q, k, v, om)
+    assert row_rel_err(host(b), want) <= TOL["f32"]
+    assert row_rel_err(host(a), host(b)) <= 1e-4
+
+
+# ----------------------------------------------------------------------------------- quadratic
+@pytest.mark.parametrize("dtype,p,B,H,T", [("f32", 1, 1, 1, 256), ("f32", 2, 1, 1, 256), ("bf16", 2, 1, 2, 300),
+                                           ("bf16", 1, 2, 1, 190)])
+def test_quadratic_matches_direct(torch_dev, dtype, p, B, H, T):
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    q, k, v, om = si.attention_inputs(21 + p, B, H, T, dtype)
+    out = rpg.sanatan_quadratic_ref_p2(dev(torch, q, dtype), dev(torch, k, dtype), dev(torch, v, dtype), p,
+                                       params(torch, om), pos0=5)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        for h in range(H):
+            want = oracle.attention_direct(q[b, h], k[b, h], v[b, h], om[h], pos0=5, p=p)
+            assert row_rel_err(got[b, h], want) <= TOL[dtype], (b, h)
