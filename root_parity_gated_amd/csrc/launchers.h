@@ -37,8 +37,9 @@ struct PrefillPlan {
   int ncs;              // chunks per sequence
   int G;                // workgroups
   long long total;      // B*H*ncs chunks
-  int multi;            // some sequence spans several ranges (pass 1 + scan needed)
-  size_t rho_bytes;     // phase table [T][64] fp32
+  int multi;            // some sequence spans several ranges (pass 1 needed)
+  int scanned;          // so many pieces per sequence that a separate scan kernel runs
+  size_t rho_bytes;     // position-phase table [T][64] fp32 (256-byte aligned)
   size_t state_bytes;   // (B*H + G - 1) boundary states of kStateFloats fp32
   size_t total_bytes;
 };

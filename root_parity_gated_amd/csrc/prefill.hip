@@ -1,386 +1,329 @@
-// prefill.hip -- chunked causal p = 1 SANATAN attention on bf16 / fp32 MFMA.
+// prefill.hip -- chunked causal p = 1 SANATAN attention on gfx950 MFMA: host plan, dispatch,
+// the boundary scan, and the 4-wave kernel (fp32 inputs, and 128-token chunks).  The 8-wave bf16
+// kernel for chunks up to 64 tokens is in prefill8.hip.
 //
 // Exact regrouping of the recurrence of the SANATAN reading notes §2.7 (sum over s <= t of
-// kappa(t,s) v_s, kappa = <Phi(q_t), Phi(k_s)>, §2.3): for a chunk of C tokens with the state
-// (S, z) of everything before it,
-//     num_t = sum_{s in chunk, s <= t} A_ts v_s + Phi(q_t)^T S,   A = Phi(Q) Phi(K)^T,
-//     den_t = sum_{s in chunk, s <= t} A_ts     + Phi(q_t)^T z,   o_t = num_t / (den_t + c eps),
-// then S += Phi(K)^T V, z += Phi(K)^T 1.  The denominator rides along as a 65th value column
-// (V' = [V | 1], state S' = [S | z]), padded to a fifth 16-wide MFMA tile.
+// kappa(t,s) v_s with kappa = <Phi(q_t), Phi(k_s)>, §2.3).  For a chunk with the state (S, z) of
+// all earlier tokens:
+//     num_t = sum_{s in chunk, s <= t} A_ts v_s + Phi(q_t)^T S,       A = Phi(Q) Phi(K)^T
+//     den_t = sum_{s in chunk, s <= t} A_ts     + Phi(q_t)^T z,       o_t = num_t / (den_t + c eps)
+// then S += Phi(K)^T V and z += Phi(K)^T 1.
 //
 // Work split (MI355X-first):
-//   * G = #CUs workgroups (4 waves each, one resident per CU) split the flattened (sequence,
-//     chunk) list into equal contiguous ranges, so every CU runs the same number of chunks in
-//     one round.  A range covering part of a sequence is a "piece": pass 1 computes each
-//     non-final piece's state increment, a scan turns them into exclusive prefixes per sequence,
-//     pass 3 runs each piece's chunks in order starting from its prefix.  The update is purely
-//     additive (the notes stress there is no decay or forgetting), so piece summaries compose
-//     by addition.
-//   * Wave w owns content dims 16w..16w+15, i.e. 96 of the 384 features (6 channels x 16 dims).
-//     Each lane featurizes 4 dims of one token per 16-row block, straight into MFMA operand
-//     registers -- Phi never goes to HBM or LDS except one transposed copy of Phi(K) for the
-//     state update.  The wave's 96 x 80 slice of S' lives in MFMA accumulators for the whole
-//     segment.  Every product is split over waves along the feature axis, so the four waves'
-//     partial (num, den) are summed through LDS in a fixed order (deterministic) before the
-//     division.
-//   * 16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16, or 8 x v_mfma_f32_16x16x4_f32 for fp32 inputs)
-//     with token and feature K-slot permutations chosen so that an accumulator tile is directly
-//     the next product's operand: A^T tiles feed the A.V product and S' tiles feed the readout
-//     without any data movement.
+//   * G = #CUs workgroups (one resident per CU) split the flattened (sequence, chunk) list into
+//     equal contiguous ranges.  A range's part of one sequence is a "piece": pass 1 computes each
+//     non-final piece's state increment, the scan (fused into pass 3 when a sequence has few pieces)
+//     gives each piece its exclusive prefix, pass 3 runs the chunks.  The update is purely
+//     additive (no decay, as the notes stress), so pieces compose by addition.
+//   * Features are split across waves by content dims (see prefill_common.h).  Lanes featurize
+//     straight into the K-slots of the 32x32x16 MFMA; Phi never leaves the CU.  Phi(K) is kept
+//     token-major in LDS for the intra product and read through the gfx950 transposing LDS load
+//     (ds_read_b64_tr_b16) as the token-consecutive operand of the state update; V likewise.
+//   * Accumulator tiles are directly the next product's operands: A^T tiles (rows s, cols t) are the
+//     B operand of num^T = V^T A^T, and S tiles (rows f, cols v) the A operand of the readout
+//     num^T += S^T Phi(Q)^T.  The state slice stays in accumulators for a whole piece; z lives in LDS.
+//     The denominator is computed on VALU (row sums of the masked A^T tiles with v_dot2, and
+//     Phi(q) . z), far cheaper than a 32-column MFMA tile for one column.
+//   * Partial (num, den) over feature groups are added through LDS in a fixed order (bitwise
+//     deterministic) before the division.
 #include <stdlib.h>
 
-#include "launchers.h"
-#include "sanatan_device.h"
+#include "prefill_common.h"
 
 namespace sanatan {
 
-// Work partition: the B*H sequences are cut into chunks of C tokens and the flattened
-// (sequence, chunk) list is split into G equal contiguous ranges, one per workgroup.  A range
-// that crosses sequence boundaries is processed as several "pieces" (one per sequence touched).
-// Piece (bh, g) owns boundary-state slot bh + g; slots are disjoint and increasing in (bh, g).
-struct PrefillArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* out;
-  const float* omega;
-  float* S;          // user state [BH][6d][dv] or null
-  float* z;          // user state [BH][6d] or null
-  float* ws_state;   // [BH + G - 1][kStateFloats] boundary states (pieces' exclusive prefixes)
-  const float* rho;  // [T][64] position phases
-  long long total;   // BH * ncs chunks
-  int G;             // workgroups in the partition
-  int ncs;           // chunks per sequence
-  int nph, H, T;
-  int multi;         // 1 if some sequence spans more than one piece (pass 1 + scan ran)
-  float kr, ceps;
+template <typename T, int CH>
+struct Geom4 {
+  static constexpr int TB = (CH + 31) / 32;   // 32-token blocks per chunk
+  static constexpr int CT = 32 * TB;          // tile tokens
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int VP = 64 + 16 / ES;     // Vs pitch (elements): +16 B keeps alignment, skews banks
+  static constexpr int KP = 96 + 16 / ES;     // KS pitch
+  static constexpr int RP = 68;               // red pitch (floats): 64 values, den at 64
+  static constexpr size_t vs_bytes = (size_t)CT * VP * ES;
+  static constexpr size_t ks_bytes = (size_t)4 * CT * KP * ES;
+  static constexpr size_t red_bytes = (size_t)4 * 32 * RP * 4;
+  static constexpr size_t z_bytes = 4 * 96 * 4;
+  static constexpr size_t stage_bytes = (size_t)(kF * kDV + kF) * 4;
+  static constexpr size_t body(bool state_only) { return vs_bytes + ks_bytes + (state_only ? 0 : red_bytes); }
+  static constexpr size_t lds(bool state_only) {
+    return (body(state_only) > stage_bytes ? body(state_only) : stage_bytes) + z_bytes;
+  }
 };
 
-__device__ __forceinline__ long long range_lo(long long g, const PrefillArgs& a) { return g * a.total / a.G; }
-
-template <typename T, int NB>
-struct PrefillGeom {
-  static constexpr int C = NB * 16;                    // chunk tokens
-  static constexpr int CP = ((C + 31) / 32) * 32;      // padded to whole 32-token K-steps
-  static constexpr int NM = CP / 32;                   // token K-steps per chunk
-  static constexpr int PITCH = CP + 16 / (int)sizeof(T);  // LDS row pitch (elements); the pad breaks bank aliasing
-  static constexpr int QG = NB < 2 ? NB : 2;  // query row-blocks per group (bounds live registers)
-  static constexpr size_t vt_bytes = (size_t)kDV * PITCH * sizeof(T);
-  static constexpr size_t kt_bytes = (size_t)4 * 96 * PITCH * sizeof(T);
-  static constexpr size_t red_bytes = (size_t)4 * QG * 16 * 65 * sizeof(float);
-  static constexpr size_t lds_bytes(bool state_only) { return vt_bytes + kt_bytes + (state_only ? 0 : red_bytes); }
-};
-
-// Add a state slot ([6d][dv] then z[6d]) into the wave's accumulator slice.
-__device__ __forceinline__ void add_state(f32x4 (&Sacc)[6][5], const float* __restrict__ s,
-                                          const float* __restrict__ zz, int a0, int r) {
-#pragma unroll
-  for (int c = 0; c < 6; c++) {
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) Sacc[c][nt][i] += s[(size_t)(c * kD + a0 + i) * kDV + 16 * nt + r];
-    if (r == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) Sacc[c][4][i] += zz[c * kD + a0 + i];
-    }
-  }
-}
-
-__device__ __forceinline__ void store_state(const f32x4 (&Sacc)[6][5], float* __restrict__ s,
-                                            float* __restrict__ zz, int a0, int r) {
-#pragma unroll
-  for (int c = 0; c < 6; c++) {
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) s[(size_t)(c * kD + a0 + i) * kDV + 16 * nt + r] = Sacc[c][nt][i];
-    if (r == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) zz[c * kD + a0 + i] = Sacc[c][4][i];
-    }
-  }
-}
-
-// Featurize 4 dims of one token (validity-masked) into the three operand fragments
-// (channels {0,1}, {2,3}, {4,5}); optionally also return the six channel values.
-template <typename T>
-__device__ __forceinline__ void featurize_frag(const float (&u)[4], const float (&rh)[4], const float (&om4)[4],
-                                               float kr, bool valid, typename FragT<T>::type (&F)[3],
-                                               float (&ch)[6][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    float cr, sr, rr;
-    featurize1(u[i], rh[i], om4[i], kr, cr, sr, rr);
-    ch[0][i] = valid ? 1.0f : 0.0f;
-    ch[1][i] = valid ? cr : 0.0f;
-    ch[2][i] = valid ? sr : 0.0f;
-    ch[3][i] = valid ? rr : 0.0f;
-    ch[4][i] = ch[3][i] * ch[1][i];
-    ch[5][i] = ch[3][i] * ch[2][i];
-  }
-  F[0] = pack8<T>(ch[0], ch[1]);
-  F[1] = pack8<T>(ch[2], ch[3]);
-  F[2] = pack8<T>(ch[4], ch[5]);
-}
-
-// Operand fragment of a transposed [row][token] LDS buffer: row `row`, token K-step m, lane quarter qd.
-// Slots 0..3: tokens 32m + 4qd + i; slots 4..7: tokens 32m + 16 + 4qd + i.
-template <typename T>
-__device__ __forceinline__ typename FragT<T>::type lds_tok_frag(const T* __restrict__ buf, int pitch, int row, int m,
-                                                                int qd) {
-  typename FragT<T>::type f;
-  const T* p = buf + row * pitch + 32 * m + 4 * qd;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    f[i] = p[i];
-    f[4 + i] = p[16 + i];
-  }
-  return f;
-}
-
-template <typename T, int NB, bool STATE_ONLY>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillArgs args) {
-  using G = PrefillGeom<T, NB>;
+template <typename T, int CH, bool STATE_ONLY>
+__global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args) {
+  using G = Geom4<T, CH>;
   using Frag = typename FragT<T>::type;
-  constexpr int C = G::C, CP = G::CP, NM = G::NM, PITCH = G::PITCH, QG = G::QG;
+  constexpr int TB = G::TB, CT = G::CT, VP = G::VP, KP = G::KP, RP = G::RP;
+  constexpr size_t LDS = G::lds(STATE_ONLY);
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  T* Vt = reinterpret_cast<T*>(smem);                         // [64][PITCH]   V^T of the chunk
-  T* KT = reinterpret_cast<T*>(smem + G::vt_bytes);           // [4][96][PITCH] Phi(K)^T per wave
-  float* red = reinterpret_cast<float*>(smem + G::vt_bytes + G::kt_bytes);  // [4][QG*16][65]
+  T* Vs = reinterpret_cast<T*>(smem);                                       // [CT][VP] V
+  T* KS = reinterpret_cast<T*>(smem + G::vs_bytes);                         // [4][CT][KP] Phi(K)
+  float* red = reinterpret_cast<float*>(smem + G::vs_bytes + G::ks_bytes);  // [4][32][RP]
+  float* stage = reinterpret_cast<float*>(smem);                            // state staging (aliases)
+  float* Zb = reinterpret_cast<float*>(smem + LDS - G::z_bytes);            // [4][96] z
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, qd = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
   const int g = blockIdx.x;
   const int Tn = args.T;
-  const int a0 = 16 * w + 4 * qd;  // this lane's 4 content dims
-  const float kr = args.kr;
-
-  T* KTw = KT + w * 96 * PITCH;
-  if (CP > C) {  // padding token columns of Phi(K)^T stay zero for the whole kernel
-    for (int idx = l; idx < 96 * (CP - C); idx += 64) KTw[(idx / (CP - C)) * PITCH + C + idx % (CP - C)] = (T)0.0f;
-  }
-  Frag ONES;  // B operand of the denominator column: column 0 of the fifth tile is all ones
-#pragma unroll
-  for (int i = 0; i < 8; i++) ONES[i] = (T)(r == 0 ? 1.0f : 0.0f);
+  T* KSw = KS + w * CT * KP;
+  float* Zw = Zb + w * 96;
+  const int dbase = 16 * w + 4 * h;  // this lane's dims: dbase + {0..3, 8..11}
 
   const long long hi = range_lo(g + 1, args);
   for (long long c = range_lo(g, args); c < hi;) {
     const int bh = (int)(c / args.ncs);
-    const long long seq_end = (long long)(bh + 1) * args.ncs;
+    const long long seq_c0 = (long long)bh * args.ncs;
+    const long long seq_end = seq_c0 + args.ncs;
     const long long pend = hi < seq_end ? hi : seq_end;
     const bool last_piece = (pend == seq_end);
-    const int t_begin = (int)(c - (long long)bh * args.ncs) * C;
-    const int t_end = min(Tn, (int)(pend - (long long)bh * args.ncs) * C);
+    const int t_begin = (int)(c - seq_c0) * CH;
+    const int t_end = min(Tn, (int)(pend - seq_c0) * CH);
     c = pend;
     if (STATE_ONLY && last_piece) continue;
-    const int h = bh % args.H;
+    const int hh = bh % args.H;
     const T* __restrict__ qp = static_cast<const T*>(args.q) + (size_t)bh * Tn * kD;
     const T* __restrict__ kp = static_cast<const T*>(args.k) + (size_t)bh * Tn * kD;
     const T* __restrict__ vp = static_cast<const T*>(args.v) + (size_t)bh * Tn * kDV;
     T* __restrict__ op = static_cast<T*>(args.out) + (size_t)bh * Tn * kDV;
     float* slot = args.ws_state + (size_t)(bh + g) * kStateFloats;
 
-    float om4[4];
+    float om4[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) om4[i] = anchor_rev(args.omega[(size_t)(h % args.nph) * kD + a0 + i]);
+    for (int i = 0; i < 8; i++)
+      om4[i] = anchor_rev(args.omega[(size_t)(hh % args.nph) * kD + dbase + (i & 3) + 8 * (i >> 2)]);
 
-    f32x4 Sacc[6][5];
+    // ---- initial state of the piece
+    f32x16 Sacc[2][3];
 #pragma unroll
-    for (int cc = 0; cc < 6; cc++)
+    for (int vt = 0; vt < 2; vt++)
 #pragma unroll
-      for (int nt = 0; nt < 5; nt++) Sacc[cc][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ft = 0; ft < 3; ft++) zero16(Sacc[vt][ft]);
+    for (int m = l; m < 96; m += 64) Zw[m] = 0.0f;
     if (!STATE_ONLY) {
-      if (args.multi) add_state(Sacc, slot, slot + kF * kDV, a0, r);
-      else if (args.S) add_state(Sacc, args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF, a0, r);
-    }
-
-    for (int t0 = t_begin; t0 < t_end; t0 += C) {
-      const int nvalid = min(C, t_end - t0);
-
-      // (a) V chunk -> LDS, transposed to [value col][token]; tokens >= nvalid are zero.
-      {
-        constexpr int E = 16 / (int)sizeof(T);
-        constexpr int TPT = kDV / E;
-        constexpr int TOKS = 256 / TPT;
-        const int n0 = (tid % TPT) * E;
-        for (int s = tid / TPT; s < CP; s += TOKS) {
-          T vals[E];
-          if (s < nvalid) {
-            const uint4 raw = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + s) * kDV + n0);
-            const T* rv = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-            for (int j = 0; j < E; j++) vals[j] = rv[j];
-          } else {
-#pragma unroll
-            for (int j = 0; j < E; j++) vals[j] = (T)0.0f;
+      auto add_slot = [&](const float* s, const float* zz) {
+        __syncthreads();
+        stage_in<256>(stage, s, zz);
+        __syncthreads();
+        stage_add_tile(Sacc[0], stage, w, 0, l);
+        stage_add_tile(Sacc[1], stage, w, 1, l);
+        for (int m = l; m < 96; m += 64) Zw[m] += stage[kStageS + w * 96 + m];
+      };
+      if (args.multi && args.scanned) {
+        add_slot(slot, slot + kF * kDV);
+      } else {
+        if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
+        if (args.multi) {  // few pieces per sequence: add the earlier pieces' increments here
+          const int gf = range_of_chunk(seq_c0, args);
+          for (int gg = gf; gg < g; gg++) {
+            const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
+            add_slot(sj, sj + kF * kDV);
           }
-#pragma unroll
-          for (int j = 0; j < E; j++) Vt[(n0 + j) * PITCH + s] = vals[j];
         }
       }
+      __syncthreads();  // the staging area is reused by the tiles
+    }
 
-      // (b) Phi(K): operand fragments in registers + transposed copy in this wave's LDS slice.
-      Frag KF[NB][3];
+    for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+      const int nvalid = min(CH, t_end - t0);
+
+      // (a) V tile -> LDS (token-major), zero beyond nvalid (loads clamped in bounds).
+      {
+        constexpr int EPL = 16 / G::ES;
+        constexpr int PER_TOK = kDV / EPL;
 #pragma unroll
-      for (int rb = 0; rb < NB; rb++) {
-        const int sl = 16 * rb + r;
-        const bool valid = sl < nvalid;
-        float u[4] = {0.f, 0.f, 0.f, 0.f}, rh[4] = {0.f, 0.f, 0.f, 0.f};
-        if (valid) {
-          load4(kp + (size_t)(t0 + sl) * kD + a0, u);
-          load4(args.rho + (size_t)(t0 + sl) * kD + a0, rh);
+        for (int idx = tid; idx < CT * PER_TOK; idx += 256) {
+          const int s = idx / PER_TOK, col = (idx % PER_TOK) * EPL;
+          const int sc = min(s, nvalid - 1);
+          uint4 raw = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + sc) * kDV + col);
+          if (s >= nvalid) raw = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(Vs + s * VP + col) = raw;
         }
-        float ch[6][4];
-        featurize_frag<T>(u, rh, om4, kr, valid, KF[rb], ch);
+      }
+      // (b) Phi(K) of the chunk -> this wave's token-major LDS tile (zero rows beyond nvalid)
 #pragma unroll
-        for (int c = 0; c < 6; c++)
+      for (int sb = 0; sb < TB; sb++) {
+        const int sl = 32 * sb + n32;
+        const int sc = t0 + min(sl, nvalid - 1);
+        float u[8], rh[8];
+        load8(kp + (size_t)sc * kD + dbase, u);
+        load8(args.rho + (size_t)sc * kD + dbase, rh);
+        float ch[6][8];
+        featurize8(u, rh, om4, args.kr, ch);
+        const float keep = sl < nvalid ? 1.0f : 0.0f;
 #pragma unroll
-          for (int i = 0; i < 4; i++) KTw[(c * 16 + 4 * qd + i) * PITCH + sl] = (T)ch[c][i];
+        for (int cc = 0; cc < 6; cc++) {
+          T* p = KSw + sl * KP + 16 * cc + 4 * h;
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            p[i] = (T)(ch[cc][i] * keep);
+            p[8 + i] = (T)(ch[cc][4 + i] * keep);
+          }
+        }
       }
       __syncthreads();
 
       if (!STATE_ONLY) {
+        // readout operands S^T (rows v, K = features) from the state before this chunk
+        Frag SA[2][6];
 #pragma unroll
-        for (int qg = 0; qg < NB; qg += QG) {
-          // Phi(Q) for query row-blocks g .. g+QG-1
-          Frag QF[QG][3];
+        for (int vt = 0; vt < 2; vt++)
 #pragma unroll
-          for (int tbl = 0; tbl < QG; tbl++) {
-            const int tl = 16 * (qg + tbl) + r;
-            const bool valid = (qg + tbl < NB) && tl < nvalid;
-            float u[4] = {0.f, 0.f, 0.f, 0.f}, rh[4] = {0.f, 0.f, 0.f, 0.f};
-            if (valid) {
-              load4(qp + (size_t)(t0 + tl) * kD + a0, u);
-              load4(args.rho + (size_t)(t0 + tl) * kD + a0, rh);
-            }
-            float ch[6][4];
-            featurize_frag<T>(u, rh, om4, kr, valid, QF[tbl], ch);
+          for (int cc = 0; cc < 6; cc++) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) x[i] = Sacc[vt][cc >> 1][8 * (cc & 1) + i];
+            SA[vt][cc] = pack8f<T>(x);
           }
-          f32x4 num[QG][5];
 #pragma unroll
-          for (int tbl = 0; tbl < QG; tbl++)
+        for (int tb = 0; tb < TB; tb++) {
+          // Phi(Q) of query block tb, and the readout part of the denominator, Phi(q) . z
+          const int tl = 32 * tb + n32;
+          const int tc = t0 + min(tl, nvalid - 1);
+          float u[8], rh[8];
+          load8(qp + (size_t)tc * kD + dbase, u);
+          load8(args.rho + (size_t)tc * kD + dbase, rh);
+          float ch[6][8];
+          featurize8(u, rh, om4, args.kr, ch);
+          Frag QF[6];
+          float den = 0.0f;
 #pragma unroll
-            for (int nt = 0; nt < 5; nt++) num[tbl][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+          for (int cc = 0; cc < 6; cc++) {
+            QF[cc] = pack8f<T>(ch[cc]);
+            const float4 za = *reinterpret_cast<const float4*>(Zw + 16 * cc + 4 * h);
+            const float4 zb = *reinterpret_cast<const float4*>(Zw + 16 * cc + 8 + 4 * h);
+            den = fmaf(ch[cc][0], za.x, den);
+            den = fmaf(ch[cc][1], za.y, den);
+            den = fmaf(ch[cc][2], za.z, den);
+            den = fmaf(ch[cc][3], za.w, den);
+            den = fmaf(ch[cc][4], zb.x, den);
+            den = fmaf(ch[cc][5], zb.y, den);
+            den = fmaf(ch[cc][6], zb.z, den);
+            den = fmaf(ch[cc][7], zb.w, den);
+          }
+          f32x16 numT[2];
+          zero16(numT[0]);
+          zero16(numT[1]);
           // intra-chunk: A^T tiles (rows s, cols t) over this wave's 96 features, masked s <= t,
-          // then straight into the A.V' product as the A operand.
+          // straight into num^T = V^T A^T as the B operand
 #pragma unroll
-          for (int tbl = 0; tbl < QG; tbl++) {
-            const int tb = qg + tbl;
-            if (tb >= NB) continue;
+          for (int sb = 0; sb <= tb; sb++) {
+            f32x16 at;
+            zero16(at);
 #pragma unroll
-            for (int m = 0; 2 * m <= tb; m++) {
-              const int sb0 = 2 * m, sb1 = 2 * m + 1;
-              f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+            for (int cc = 0; cc < 6; cc++) mma32(at, lds_rowfrag<T>(KSw, KP, 32 * sb + n32, cc, h), QF[cc]);
+            float lo[8], hi2[8];
 #pragma unroll
-              for (int j = 0; j < 3; j++) mma(d0, KF[sb0][j], QF[tbl][j]);
-              if (sb1 <= tb) {
+            for (int i = 0; i < 16; i++) {
+              const int sl = 8 * (i >> 2) + 4 * h + (i & 3);
+              const float a = (sb == tb && sl > n32) ? 0.0f : at[i];
+              if (i < 8) lo[i] = a;
+              else hi2[i - 8] = a;
+            }
+            const Frag P0 = pack8f<T>(lo), P1 = pack8f<T>(hi2);
+            den = frag_sum(P1, frag_sum(P0, den));  // row sum of the values the A.V product sees
 #pragma unroll
-                for (int j = 0; j < 3; j++) mma(d1, KF[sb1][j], QF[tbl][j]);
-              }
-              if (sb0 == tb) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) d0[i] = (4 * qd + i > r) ? 0.0f : d0[i];
-              }
-              if (sb1 == tb) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) d1[i] = (4 * qd + i > r) ? 0.0f : d1[i];
-              }
-              const Frag P = pack8v<T>(d0, d1);
-#pragma unroll
-              for (int nt = 0; nt < 4; nt++) mma(num[tbl][nt], P, lds_tok_frag<T>(Vt, PITCH, 16 * nt + r, m, qd));
-              mma(num[tbl][4], P, ONES);
+            for (int vt = 0; vt < 2; vt++) {
+              mma32(numT[vt], lds_tokfrag(Vs, VP, 32 * sb, 32 * vt, l), P0);
+              mma32(numT[vt], lds_tokfrag(Vs, VP, 32 * sb + 16, 32 * vt, l), P1);
             }
           }
-          // inter-chunk readout with the state before this chunk: num += Phi(Q) S'
+          // inter-chunk readout: num^T += S^T Phi(Q)^T
 #pragma unroll
-          for (int j = 0; j < 3; j++) {
+          for (int cc = 0; cc < 6; cc++)
 #pragma unroll
-            for (int nt = 0; nt < 5; nt++) {
-              const Frag SB = pack8v<T>(Sacc[2 * j][nt], Sacc[2 * j + 1][nt]);
+            for (int vt = 0; vt < 2; vt++) mma32(numT[vt], SA[vt][cc], QF[cc]);
+          den += __shfl_xor(den, 32);
+          // this wave's partial (num, den) -> LDS: row t, 64 value columns, den at column 64
+          float* rw = red + w * 32 * RP + n32 * RP;
 #pragma unroll
-              for (int tbl = 0; tbl < QG; tbl++)
-                if (qg + tbl < NB) mma(num[tbl][nt], QF[tbl][j], SB);
-            }
-          }
-          // cross-wave sum of the partial (num, den) in a fixed order, then divide and store.
-          float* redw = red + (size_t)w * QG * 16 * 65;
+          for (int vt = 0; vt < 2; vt++)
 #pragma unroll
-          for (int tbl = 0; tbl < QG; tbl++) {
-#pragma unroll
-            for (int nt = 0; nt < 4; nt++)
-#pragma unroll
-              for (int i = 0; i < 4; i++) redw[(16 * tbl + 4 * qd + i) * 65 + 16 * nt + r] = num[tbl][nt][i];
-            if (r == 0) {
-#pragma unroll
-              for (int i = 0; i < 4; i++) redw[(16 * tbl + 4 * qd + i) * 65 + 64] = num[tbl][4][i];
-            }
-          }
+            for (int j = 0; j < 4; j++)
+              *reinterpret_cast<float4*>(rw + 32 * vt + 8 * j + 4 * h) =
+                  make_float4(numT[vt][4 * j], numT[vt][4 * j + 1], numT[vt][4 * j + 2], numT[vt][4 * j + 3]);
+          if (h == 0) rw[64] = den;
           __syncthreads();
           {
-            constexpr int ROWS = QG * 16;
-            constexpr int CPT = ROWS * kDV / 256;
-            constexpr int TPR = kDV / CPT;
-            const int row = tid / TPR;
-            const int c0 = (tid % TPR) * CPT;
-            const int tl = 16 * qg + row;
-            if (tl < nvalid) {
-              constexpr int WS = QG * 16 * 65;
-              const float den = ((red[row * 65 + 64] + red[WS + row * 65 + 64]) + red[2 * WS + row * 65 + 64]) +
-                                red[3 * WS + row * 65 + 64];
-              const float inv = 1.0f / (den + args.ceps);
-              T o[CPT];
+            const int row = tid >> 3, v0 = 8 * (tid & 7);
+            const int t_out = 32 * tb + row;
+            if (t_out < nvalid) {
+              constexpr int WS = 32 * RP;
+              const float dsum = ((red[row * RP + 64] + red[WS + row * RP + 64]) + red[2 * WS + row * RP + 64]) +
+                                 red[3 * WS + row * RP + 64];
+              const float inv = 1.0f / (dsum + args.ceps);
+              T o[8];
 #pragma unroll
-              for (int cc = 0; cc < CPT; cc++) {
-                const int idx = row * 65 + c0 + cc;
-                const float s = ((red[idx] + red[WS + idx]) + red[2 * WS + idx]) + red[3 * WS + idx];
-                o[cc] = from_f32<T>(s * inv);
+              for (int hv = 0; hv < 2; hv++) {
+                const float4 a0 = *reinterpret_cast<const float4*>(red + row * RP + v0 + 4 * hv);
+                const float4 a1 = *reinterpret_cast<const float4*>(red + WS + row * RP + v0 + 4 * hv);
+                const float4 a2 = *reinterpret_cast<const float4*>(red + 2 * WS + row * RP + v0 + 4 * hv);
+                const float4 a3 = *reinterpret_cast<const float4*>(red + 3 * WS + row * RP + v0 + 4 * hv);
+                o[4 * hv + 0] = from_f32<T>((((a0.x + a1.x) + a2.x) + a3.x) * inv);
+                o[4 * hv + 1] = from_f32<T>((((a0.y + a1.y) + a2.y) + a3.y) * inv);
+                o[4 * hv + 2] = from_f32<T>((((a0.z + a1.z) + a2.z) + a3.z) * inv);
+                o[4 * hv + 3] = from_f32<T>((((a0.w + a1.w) + a2.w) + a3.w) * inv);
               }
-              T* dst = op + (size_t)(t0 + tl) * kDV + c0;
+              uint4* dst = reinterpret_cast<uint4*>(op + (size_t)(t0 + t_out) * kDV + v0);
+              const uint4* src = reinterpret_cast<const uint4*>(o);
 #pragma unroll
-              for (int cc = 0; cc < CPT; cc++) dst[cc] = o[cc];
+              for (int i = 0; i < (int)sizeof(o) / 16; i++) dst[i] = src[i];
             }
           }
           __syncthreads();
         }
       }
 
-      // state update S' += Phi(K)^T V' (this wave's 96 feature rows), after this chunk's readout.
+      // (c) state update S += Phi(K)^T V (this wave's 96 feature rows) and z += Phi(K)^T 1
+      float zadd[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 6; c++) {
+      for (int ft = 0; ft < 3; ft++) {
 #pragma unroll
-        for (int m = 0; m < NM; m++) {
-          const Frag A = lds_tok_frag<T>(KTw, PITCH, c * 16 + r, m, qd);
+        for (int ks = 0; ks < 2 * TB; ks++) {
+          const Frag A = lds_tokfrag(KSw, KP, 16 * ks, 32 * ft, l);
+          zadd[ft] = frag_sum(A, zadd[ft]);
 #pragma unroll
-          for (int nt = 0; nt < 4; nt++) mma(Sacc[c][nt], A, lds_tok_frag<T>(Vt, PITCH, 16 * nt + r, m, qd));
-          mma(Sacc[c][4], A, ONES);
+          for (int vt = 0; vt < 2; vt++) mma32(Sacc[vt][ft], A, lds_tokfrag(Vs, VP, 16 * ks, 32 * vt, l));
         }
+      }
+#pragma unroll
+      for (int ft = 0; ft < 3; ft++) zadd[ft] += __shfl_xor(zadd[ft], 32);
+      if (h == 0) {
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) Zw[32 * ft + n32] += zadd[ft];
       }
       __syncthreads();
     }
 
-    if (STATE_ONLY) {
-      store_state(Sacc, slot, slot + kF * kDV, a0, r);
-    } else if (last_piece && args.S) {
-      store_state(Sacc, args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF, a0, r);
+    float* dst_s = STATE_ONLY ? slot : (last_piece && args.S ? args.S + (size_t)bh * kF * kDV : nullptr);
+    float* dst_z = STATE_ONLY ? slot + kF * kDV : (last_piece && args.S ? args.z + (size_t)bh * kF : nullptr);
+    if (dst_s) {
+      __syncthreads();
+      stage_put_tile(Sacc[0], stage, w, 0, l);
+      stage_put_tile(Sacc[1], stage, w, 1, l);
+      for (int m = l; m < 96; m += 64) stage[kStageS + w * 96 + m] = Zw[m];
+      __syncthreads();
+      stage_out<256>(stage, dst_s, dst_z);
     }
-  }  // pieces
+    __syncthreads();  // Zw and the staging area are reused by the next piece
+  }
 }
 
-// Exclusive prefix over the pieces of each sequence, in place: slot(bh, g) <- S0 + sum of the
-// increments of the earlier pieces of sequence bh.  One thread per (sequence, state element).
+// Exclusive prefix over the pieces of each sequence, in place: slot(bh, g) <- S0 + increments of the
+// earlier pieces of sequence bh.  One thread per (sequence, state element).
 __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs args, int BH) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
   if (e >= kStateFloats || bh >= BH) return;
   const long long c0 = (long long)bh * args.ncs, c1 = c0 + args.ncs - 1;
-  const int gf = (int)(((c0 + 1) * args.G - 1) / args.total);
-  const int gl = (int)(((c1 + 1) * args.G - 1) / args.total);
+  const int gf = range_of_chunk(c0, args);
+  const int gl = range_of_chunk(c1, args);
   float run = 0.0f;
   if (args.S) run = (e < kF * kDV) ? args.S[(size_t)bh * kF * kDV + e] : args.z[(size_t)bh * kF + (e - kF * kDV)];
-  for (int g = gf; g <= gl; g++) {
-    float* p = args.ws_state + (size_t)(bh + g) * kStateFloats + e;
-    const float d = (g < gl) ? *p : 0.0f;
+  for (int gg = gf; gg <= gl; gg++) {
+    float* p = args.ws_state + (size_t)(bh + gg) * kStateFloats + e;
+    const float d = (gg < gl) ? *p : 0.0f;
     *p = run;
     run += d;
   }
@@ -396,7 +339,8 @@ static int device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       cus = n;
     else
       cus = 256;
@@ -404,12 +348,15 @@ static int device_cus() {
   return cus;
 }
 
+// Pieces per sequence above which the separate scan kernel is cheaper than letting each pass-3
+// workgroup add up its predecessors' increments.
+static constexpr int kFusedScanMaxPieces = 4;
+
 bool prefill_plan(int B, int H, int T, int chunk, PrefillPlan* plan) {
   if (B <= 0 || H <= 0 || T <= 0 || chunk <= 0) return false;
   const long long BH = (long long)B * H;
   const long long ncs = (T + chunk - 1) / chunk;
   const long long total = BH * ncs;
-  // One resident workgroup per CU: G = #CUs equal ranges fill the chip in one round.
   long long G = device_cus();
   const char* env = getenv("SANATAN_PREFILL_WGS");
   if (env && atoll(env) > 0) G = atoll(env);
@@ -421,35 +368,45 @@ bool prefill_plan(int B, int H, int T, int chunk, PrefillPlan* plan) {
   plan->rho_bytes = (((size_t)T * kD * sizeof(float)) + 255) & ~(size_t)255;
   plan->state_bytes = (size_t)(BH + G - 1) * kStateFloats * sizeof(float);
   plan->total_bytes = plan->rho_bytes + plan->state_bytes;
-  // Does any sequence span more than one range?  (then pass 1 and the scan are needed)
-  plan->multi = 0;
-  for (long long bh = 0; bh < BH && !plan->multi; bh++) {
+  int max_pieces = 1;
+  for (long long bh = 0; bh < BH; bh++) {
     const long long c0 = bh * ncs, c1 = c0 + ncs - 1;
-    if (((c0 + 1) * G - 1) / total != ((c1 + 1) * G - 1) / total) plan->multi = 1;
+    const int np = (int)(((c1 + 1) * G - 1) / total - ((c0 + 1) * G - 1) / total) + 1;
+    if (np > max_pieces) max_pieces = np;
   }
+  plan->multi = max_pieces > 1;
+  plan->scanned = max_pieces > kFusedScanMaxPieces;
   return true;
 }
 
-template <typename T, int NB>
-static hipError_t launch_prefill_t(const PrefillArgs& a, int BH, hipStream_t stream) {
-  using G = PrefillGeom<T, NB>;
+template <typename T, int CH>
+static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t stream) {
+  using G = Geom4<T, CH>;
+  static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
   if (a.multi) {
-    const size_t lds1 = G::lds_bytes(true);
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_kernel<T, NB, true>,
+    const size_t lds1 = G::lds(true);
+    hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_kernel<T, NB, true>), dim3(a.G), dim3(256), lds1, stream, a);
+    hipLaunchKernelGGL((prefill4_kernel<T, CH, true>), dim3(a.G), dim3(256), lds1, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (a.scanned) {
+      hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
-  const size_t lds3 = G::lds_bytes(false);
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_kernel<T, NB, false>,
+  const size_t lds3 = G::lds(false);
+  hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_kernel<T, NB, false>), dim3(a.G), dim3(256), lds3, stream, a);
+  hipLaunchKernelGGL((prefill4_kernel<T, CH, false>), dim3(a.G), dim3(256), lds3, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);
   return hipGetLastError();
 }
 
@@ -457,29 +414,32 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
                           int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,
                           const PrefillPlan& plan, hipStream_t stream) {
   float* rho = static_cast<float*>(ws);
-  float* ws_state = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.rho_bytes);
   hipError_t e = launch_phase_table(rho, T, pos0, mc.log2_base, stream);
   if (e != hipSuccess) return e;
   PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
-  a.omega = mc.omega; a.S = S; a.z = z; a.ws_state = ws_state; a.rho = rho;
-  a.total = plan.total; a.G = plan.G; a.ncs = plan.ncs; a.multi = plan.multi;
-  a.nph = mc.nph; a.H = H; a.T = T;
+  a.omega = mc.omega; a.S = S; a.z = z;
+  a.ws_state = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.rho_bytes);
+  a.rho = rho;
+  a.total = plan.total;
+  a.G = plan.G; a.ncs = plan.ncs; a.nph = mc.nph; a.H = H; a.T = T;
+  a.multi = plan.multi; a.scanned = plan.scanned;
   a.kr = mc.kr; a.ceps = mc.ceps;
   const int BH = B * H;
-  const int nb = plan.chunk / 16;
   if (t == SANATAN_BF16) {
-    switch (nb) {
-      case 1: return launch_prefill_t<__bf16, 1>(a, BH, stream);
-      case 2: return launch_prefill_t<__bf16, 2>(a, BH, stream);
-      case 4: return launch_prefill_t<__bf16, 4>(a, BH, stream);
-      case 8: return launch_prefill_t<__bf16, 8>(a, BH, stream);
+    const char* env = getenv("SANATAN_PREFILL_4WAVE");
+    const bool four = env && atoi(env) > 0;
+    switch (plan.chunk) {
+      case 16: return four ? launch_prefill4_t<__bf16, 16>(a, BH, stream) : launch_prefill8(a, 16, BH, stream);
+      case 32: return four ? launch_prefill4_t<__bf16, 32>(a, BH, stream) : launch_prefill8(a, 32, BH, stream);
+      case 64: return four ? launch_prefill4_t<__bf16, 64>(a, BH, stream) : launch_prefill8(a, 64, BH, stream);
+      case 128: return launch_prefill4_t<__bf16, 128>(a, BH, stream);
     }
   } else {
-    switch (nb) {
-      case 1: return launch_prefill_t<float, 1>(a, BH, stream);
-      case 2: return launch_prefill_t<float, 2>(a, BH, stream);
-      case 4: return launch_prefill_t<float, 4>(a, BH, stream);
+    switch (plan.chunk) {
+      case 16: return launch_prefill4_t<float, 16>(a, BH, stream);
+      case 32: return launch_prefill4_t<float, 32>(a, BH, stream);
+      case 64: return launch_prefill4_t<float, 64>(a, BH, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -1,0 +1,211 @@
+// prefill_common.h -- pieces shared by the chunked-prefill kernels (4-wave and 8-wave variants).
+//
+// Feature ownership used by every variant: feature group g (0..3) = content dims 16g..16g+15,
+// i.e. 96 features (6 channels x 16 dims); wave feature index m = 16 c + dim.  Within a group the
+// state rows are tiled as 3 "f-tiles" of 32 features (ft = m / 32).  In a 32x32 accumulator tile
+// lane (n32 = l % 32, h = l / 32) holds rows 8 j + 4 h + i4 (j < 4, i4 < 4; register 4 j + i4) of
+// column n32 -- so K-step c (16 features) of an MFMA operand is channel c, and lane (row, h) holds
+// dims {4h..4h+3, 8+4h..11+4h} of it.
+#pragma once
+
+#include "launchers.h"
+#include "sanatan_device.h"
+
+namespace sanatan {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+}
+__device__ __forceinline__ void zero16(f32x16& a) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) a[i] = 0.0f;
+}
+
+// Work partition (see prefill_plan): the flattened (sequence, chunk) list split into G ranges, one per
+// workgroup.  Piece (bh, g) owns boundary-state slot bh + g (disjoint and increasing in (bh, g)).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const float* omega;
+  float* S;          // user state [BH][6d][dv] or null
+  float* z;          // user state [BH][6d] or null
+  float* ws_state;   // [BH + G - 1][kStateFloats]
+  const float* rho;  // [T][64] position phases in revolutions
+  long long total;   // BH * ncs chunks
+  int G, ncs, nph, H, T;
+  int multi;         // some sequence spans several pieces: pass 1 ran
+  int scanned;       // the scan kernel ran: each slot holds its piece's prefix (else pass 3 sums slots)
+  float kr, ceps;
+};
+
+__device__ __forceinline__ long long range_lo(long long g, const PrefillArgs& a) { return g * a.total / a.G; }
+__device__ __forceinline__ int range_of_chunk(long long c, const PrefillArgs& a) {
+  return (int)(((c + 1) * a.G - 1) / a.total);
+}
+
+hipError_t launch_prefill8(const PrefillArgs& a, int chunk, int BH, hipStream_t stream);
+hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream);
+
+template <typename T> __device__ __forceinline__ typename FragT<T>::type pack8f(const float (&x)[8]) {
+  typename FragT<T>::type f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) f[i] = (T)x[i];
+  return f;
+}
+
+// Token-consecutive operand from a token-major LDS tile [token][pitch]: lane (row = l % 32, h)
+// gets column col0 + (l % 32) at tokens tok0 + 8*(i/4) + 4h + (i % 4), i = 0..7.
+// bf16: two transposing loads; each 16-lane block addresses 4 tokens x 4 column groups, and lane j
+// of the block receives column j of those 4 tokens.  Whole-vector bit casts only: per-element casts
+// of the loaded halves were miscompiled into duplicated words.
+__device__ __forceinline__ bf16x8 lds_tokfrag(const __bf16* buf, int pitch, int tok0, int col0, int l) {
+  const int b = l >> 4, L = l & 15;
+  const int tok = tok0 + 4 * (b >> 1) + (L >> 2);
+  const int col = col0 + 16 * (b & 1) + 4 * (L & 3);
+  const u32x2 lo =
+      __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + tok * pitch + col)));
+  const u32x2 hi = __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + (tok + 8) * pitch + col)));
+  const u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ f32x8 lds_tokfrag(const float* buf, int pitch, int tok0, int col0, int l) {
+  const int col = col0 + (l & 31), tb = tok0 + 4 * (l >> 5);
+  f32x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[i] = buf[(tb + i) * pitch + col];
+    f[4 + i] = buf[(tb + 8 + i) * pitch + col];
+  }
+  return f;
+}
+
+// Row operand (channel c = K-step, 8 dims of one token) from a token-major feature tile [token][pitch]
+// whose columns are wave features 16c + dim.
+template <typename T>
+__device__ __forceinline__ typename FragT<T>::type lds_rowfrag(const T* ks, int pitch, int s, int c, int h) {
+  typename FragT<T>::type f;
+  const T* p = ks + s * pitch + 16 * c + 4 * h;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[i] = p[i];
+    f[4 + i] = p[8 + i];
+  }
+  return f;
+}
+
+// This lane's 8 values (dims dbase + {0..3, 8..11}) of one row.
+__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 8);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void load8(const __bf16* p, float (&o)[8]) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p), b = *reinterpret_cast<const bf16x4*>(p + 8);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    o[i] = (float)a[i];
+    o[4 + i] = (float)b[i];
+  }
+}
+
+// Featurize this lane's 8 dims of one token given the position phases rho (revolutions):
+// ch[c][i] = channel c (1, cos, sin, r, r cos, r sin) of dim i.
+__device__ __forceinline__ void featurize8(const float (&u)[8], const float (&rho)[8], const float (&om4)[8], float kr,
+                                           float (&ch)[6][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float cr, sr, rr;
+    featurize1(u[i], rho[i], om4[i], kr, cr, sr, rr);
+    ch[0][i] = 1.0f;
+    ch[1][i] = cr;
+    ch[2][i] = sr;
+    ch[3][i] = rr;
+    ch[4][i] = rr * cr;
+    ch[5][i] = rr * sr;
+  }
+}
+
+// Sum of the 8 bf16 values of a fragment (v_dot2 with ones).  Pairs are taken with shufflevector:
+// extracting words from a bit-cast of the bf16 vector was miscompiled into reusing the first word.
+__device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const f32x8& f, float acc) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc += f[i];
+  return acc;
+}
+
+// ------------------------------------------------------------------ state staging through LDS
+// State I/O goes through LDS so global traffic stays coalesced and each lane moves its accumulator
+// slice with constant LDS offsets.  Staging layout (floats): S at [g][vt][ft][i][lane] (lane fastest,
+// i = accumulator register), then z at [g][96] (wave feature m).
+constexpr int kStageS = 4 * 2 * 3 * 16 * 64;  // = 6d * d_v
+
+__device__ __forceinline__ int stage_index(int row, int col) {
+  const int c = row >> 6, a = row & 63, g = a >> 4, dim = a & 15;
+  const int m = 16 * c + dim, ft = m >> 5, mm = m & 31;
+  const int j = mm >> 3, h = (mm >> 2) & 1, i4 = mm & 3;
+  const int vt = col >> 5, n32 = col & 31;
+  return (((g * 2 + vt) * 3 + ft) * 16 + 4 * j + i4) * 64 + 32 * h + n32;
+}
+
+// global state (ABI layout: S [6d][d_v] then z [6d]) <-> staging; NT threads cooperate.
+template <int NT>
+__device__ __forceinline__ void stage_in(float* st, const float* __restrict__ s, const float* __restrict__ zz) {
+  for (int e4 = threadIdx.x; e4 < kF * kDV / 4; e4 += NT) {
+    const float4 v = reinterpret_cast<const float4*>(s)[e4];
+    const int row = (4 * e4) / kDV, col = (4 * e4) % kDV;
+    *reinterpret_cast<float4*>(st + stage_index(row, col)) = v;  // 4 columns = 4 consecutive lanes
+  }
+  for (int r = threadIdx.x; r < kF; r += NT) {
+    const int c = r >> 6, a = r & 63;
+    st[kStageS + (a >> 4) * 96 + 16 * c + (a & 15)] = zz[r];
+  }
+}
+template <int NT>
+__device__ __forceinline__ void stage_out(const float* st, float* __restrict__ s, float* __restrict__ zz) {
+  for (int e4 = threadIdx.x; e4 < kF * kDV / 4; e4 += NT) {
+    const int row = (4 * e4) / kDV, col = (4 * e4) % kDV;
+    reinterpret_cast<float4*>(s)[e4] = *reinterpret_cast<const float4*>(st + stage_index(row, col));
+  }
+  for (int r = threadIdx.x; r < kF; r += NT) {
+    const int c = r >> 6, a = r & 63;
+    zz[r] = st[kStageS + (a >> 4) * 96 + 16 * c + (a & 15)];
+  }
+}
+// One value tile (vt) of group g: staging -> accumulators (added) / accumulators -> staging.
+__device__ __forceinline__ void stage_add_tile(f32x16 (&acc)[3], const float* st, int g, int vt, int l) {
+  const float* p = st + (g * 2 + vt) * (3 * 16 * 64) + l;
+#pragma unroll
+  for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[ft][i] += p[(ft * 16 + i) * 64];
+}
+__device__ __forceinline__ void stage_put_tile(const f32x16 (&acc)[3], float* st, int g, int vt, int l) {
+  float* p = st + (g * 2 + vt) * (3 * 16 * 64) + l;
+#pragma unroll
+  for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) p[(ft * 16 + i) * 64] = acc[ft][i];
+}
+
+}  // namespace sanatan
