@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -52,6 +53,12 @@ def quadratic_flops(B, H, T):
     return B * H * pairs * 2 * (F + DV)
 
 
+PREFILL_SOURCES = ("api.hip", "featurize.hip", "prefill.hip", "prefill_grp.hip", "prefill_common.h", "launchers.h",
+                   "sanatan_device.h")
+PREFILL_KERNELS = ("phase_table_kernel", "prefill_grp_kernel", "prefill_scan_kernel", "prefill4_kernel")
+CAL_BYTES = 256 << 20       # plain device copy used to calibrate the memory counters
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -70,6 +77,53 @@ def traffic_from_profiles(kernel_key, src_hash):
     if not rec or rec.get("source_hash") != src_hash:
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, key):
+    """Per-call HBM bytes of the prefill from two rocprofv3 --pmc runs of `bench.py --calibrate-copy`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled so that the calibration copy of
+    CAL_BYTES reads / writes exactly CAL_BYTES.  Writes profiles/traffic.json[key]."""
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
+        cal = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not cal:
+            raise SystemExit(f"no calibration copy found in {d}")
+        scale = CAL_BYTES / (max(cal) * 1024.0)
+        per_kernel = {}
+        for r in rows:
+            kn = r["Kernel_Name"]
+            hit = next((k for k in PREFILL_KERNELS if k in kn), None)
+            if hit is None:
+                continue
+            m = re.search(r"(\w+_kernel(<[^>]*>)?)", kn)
+            label = m.group(1) if m else kn
+            per_kernel.setdefault(label, []).append(float(r["Counter_Value"]) * 1024.0 * scale)
+        calls = len(per_kernel.get("phase_table_kernel", [])) or max(len(v) for v in per_kernel.values())
+        out[name] = {"scale": scale, "calibration_kib": max(cal),
+                     "per_kernel_bytes_avg": {k: sum(v) / len(v) for k, v in per_kernel.items()},
+                     "bytes_per_call": sum(sum(v) for v in per_kernel.values()) / calls}
+    rec = {"source_hash": source_hash(*PREFILL_SOURCES),
+           "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_call"] + out["WRITE_SIZE"]["bytes_per_call"],
+           "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        allrec = json.load(open(path))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[key] = rec
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1))
 
 
 def log(msg):
@@ -216,7 +270,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain %d MiB device copy first (reference kernel for memory counters)" % (CAL_BYTES >> 20))
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic:
+        traffic_summary(args.traffic[0], args.traffic[1], "prefill_b8h12_t2048")
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(pass --gpus 1).", file=sys.stderr)
@@ -231,6 +292,13 @@ def main():
     import sanatan_inputs as si
 
     rpg.lib()  # raises if the HIP library is not built
+    if args.calibrate_copy:
+        src_buf = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+        dst_buf = torch.empty_like(src_buf)
+        for _ in range(3):
+            dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
     w = si.PREFILL
     log(f"prefill {w.name}: {args.warmup} warmup + {args.steps} timed steps")
     ms, per = bench_prefill_like(torch, rpg, si, w, args.steps, args.warmup)
@@ -240,7 +308,7 @@ def main():
     fl = prefill_flops(w.B, w.H, w.T, w.chunk)
     fl_dense = prefill_flops(w.B, w.H, w.T, w.chunk, causal=False)
     achieved = fl / (call_ms * 1e-3) / 1e12
-    src = source_hash("prefill.hip", "featurize.hip", "sanatan_device.h")
+    src = source_hash(*PREFILL_SOURCES)
     result = {
         "metric": "prefill tokens/s (12h x d64, T=2K, p=1)",
         "value": tokens / (ms * 1e-3),
@@ -260,7 +328,8 @@ def main():
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": traffic_from_profiles("prefill_b8h12_t2048", src),
-            "kernel": "sanatan_prefill_chunked (phase table, pass 1, scan, pass 3 launches)",
+            "kernel": "sanatan_prefill_chunked: phase table + pass 1 (state increments) + pass 3 (outputs), "
+                      "timed as one launch sequence",
             "flops_per_launch": fl, "flops_dense_tile": fl_dense,
             "hbm_bytes_algorithmic": prefill_bytes(w.B, w.H, w.T),
             "hbm_frac_algorithmic": prefill_bytes(w.B, w.H, w.T) / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -9,18 +9,20 @@
 
 namespace sanatan {
 
+// rho[t][a] = phase of position pos0 + t; a block covers 16 positions, each thread one dim and 4 of them.
 __global__ __launch_bounds__(256) void phase_table_kernel(float* __restrict__ rho, int T, int64_t pos0,
                                                           double log2_base) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)T * kD) return;
-  const int a = (int)(idx % kD);
-  const int64_t t = idx / kD;
-  rho[idx] = phase_rev(pos0 + t, a, log2_base);
+  const int a = threadIdx.x & 63;
+  const double step = phase_step(a, log2_base);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int64_t t = (int64_t)blockIdx.x * 16 + 4 * j + (threadIdx.x >> 6);
+    if (t < T) rho[t * kD + a] = phase_at(pos0 + t, step);
+  }
 }
 
 hipError_t launch_phase_table(float* rho, int T, int64_t pos0, double log2_base, hipStream_t stream) {
-  const int64_t n = (int64_t)T * kD;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  const unsigned blocks = (unsigned)((T + 15) / 16);
   hipLaunchKernelGGL(phase_table_kernel, dim3(blocks), dim3(256), 0, stream, rho, T, pos0, log2_base);
   return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 // prefill.hip -- chunked causal p = 1 SANATAN attention on gfx950 MFMA: host plan, dispatch,
-// the boundary scan, and the 4-wave kernel (fp32 inputs, and 128-token chunks).  The 8-wave bf16
-// kernel for chunks up to 64 tokens is in prefill8.hip.
+// the boundary scan, and the 4-wave kernel (fp32 inputs, and 128-token chunks).  The bf16 kernel
+// for chunks up to 64 tokens (one wave per feature group) is in prefill_grp.hip.
 //
 // Exact regrouping of the recurrence of the SANATAN reading notes §2.7 (sum over s <= t of
 // kappa(t,s) v_s with kappa = <Phi(q_t), Phi(k_s)>, §2.3).  For a chunk with the state (S, z) of
@@ -427,12 +427,10 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
   a.kr = mc.kr; a.ceps = mc.ceps;
   const int BH = B * H;
   if (t == SANATAN_BF16) {
-    const char* env = getenv("SANATAN_PREFILL_4WAVE");
-    const bool four = env && atoi(env) > 0;
     switch (plan.chunk) {
-      case 16: return four ? launch_prefill4_t<__bf16, 16>(a, BH, stream) : launch_prefill8(a, 16, BH, stream);
-      case 32: return four ? launch_prefill4_t<__bf16, 32>(a, BH, stream) : launch_prefill8(a, 32, BH, stream);
-      case 64: return four ? launch_prefill4_t<__bf16, 64>(a, BH, stream) : launch_prefill8(a, 64, BH, stream);
+      case 16:
+      case 32:
+      case 64: return launch_prefill_grp(a, plan.chunk, BH, stream);
       case 128: return launch_prefill4_t<__bf16, 128>(a, BH, stream);
     }
   } else {

@@ -1,4 +1,4 @@
-// prefill_common.h -- pieces shared by the chunked-prefill kernels (4-wave and 8-wave variants).
+// prefill_common.h -- pieces shared by the chunked-prefill kernels (prefill.hip, prefill_grp.hip).
 //
 // Feature ownership used by every variant: feature group g (0..3) = content dims 16g..16g+15,
 // i.e. 96 features (6 channels x 16 dims); wave feature index m = 16 c + dim.  Within a group the
@@ -19,6 +19,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> one word of two bf16 (round to nearest even), low half = a.
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 
 __device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
@@ -56,7 +63,7 @@ __device__ __forceinline__ int range_of_chunk(long long c, const PrefillArgs& a)
   return (int)(((c + 1) * a.G - 1) / a.total);
 }
 
-hipError_t launch_prefill8(const PrefillArgs& a, int chunk, int BH, hipStream_t stream);
+hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream);
 hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream);
 
 template <typename T> __device__ __forceinline__ typename FragT<T>::type pack8f(const float (&x)[8]) {

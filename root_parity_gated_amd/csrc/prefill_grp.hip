@@ -1,0 +1,559 @@
+// prefill_grp.hip -- bf16 chunked causal p = 1 prefill, one wave per feature group.
+//
+// Mathematics: the chunked regrouping of the recurrence of the SANATAN reading notes §2.7 (intra-chunk
+// masked Phi(Q) Phi(K)^T V, inter-chunk readout Phi(Q) S and Phi(Q) . z, state update S += Phi(K)^T V,
+// z += Phi(K)^T 1), with the work partition of prefill.hip (pieces of the flattened chunk list, pass 1 =
+// increments of non-final pieces, pass 3 = outputs).
+//
+// Layout.  A workgroup is 4 waves, one per SIMD; wave g owns feature group g = content dims 16g..16g+15,
+// i.e. the 96 features (channel c, dim) of those dims, and the 96 x 64 slice of S for them (6 accumulator
+// tiles of 32 x 32 fp32, 96 AGPR/VGPR per lane).  Lane (n32 = l % 32, h = l / 32) featurizes token n32 of
+// each 32-token block, dims 16g + 8h .. 16g + 8h + 7: exactly the 8 K-slots it supplies to the MFMA
+// operands of Phi(Q) and Phi(K) (K-step = channel), so the intra-chunk product and the readout take
+// their feature operands straight from registers.  Only Phi(K) is written to LDS (wave-private, for the
+// transposed read of the state update), with V (also wave-private).  The one cross-wave exchange is
+// the reduction of the four groups' partial numerators and denominators before the normalisation.
+//
+// Accumulator row order.  In a 32-row accumulator tile, lane half h holds rows {4h..4h+3, 8+4h..11+4h}
+// of each 16-row block, while it featurized dims 8h..8h+7; the state rows are therefore ordered
+// with bits 2 and 3 of the dim swapped (swz16), and the transposed LDS read of Phi(K) for the update
+// uses the same swap, so readout K-slots and state rows line up.
+//
+// Channel 0 of Phi is the constant 1: in the intra-chunk product its 16 features contribute exactly
+// 16 to every entry, which initialises the accumulator instead of an MFMA.
+#include "prefill_common.h"
+
+namespace sanatan {
+namespace {
+
+__device__ __forceinline__ int swz16(int d) { return (d & 3) | ((d >> 1) & 4) | ((d << 1) & 8); }
+
+constexpr unsigned kOnes2 = 0x3F803F80u;  // two bf16 ones
+
+template <int CH>
+struct GeomG {
+  static constexpr int TB = (CH + 31) / 32;  // 32-token blocks per chunk
+  static constexpr int CT = 32 * TB;         // tile tokens
+  static constexpr int KP = 104;             // Phi(K) tile pitch (bf16): 96 features + 8
+  static constexpr int VP = 72;              // V tile pitch (bf16)
+  static constexpr int RP = 68;              // reduction pitch (floats): 64 values, denominator at 64
+  static constexpr int ks_bytes = CT * KP * 2;   // one wave's Phi(K) tile
+  static constexpr int vs_bytes = CT * VP * 2;   // one V tile
+  static constexpr int red_bytes = TB * 4 * 32 * RP * 4;
+  static constexpr int stage_bytes = kStateFloats * 4;
+  // pass 3: [Phi(K) x 4 waves][V x 2 (shared, double-buffered)][reduction]; pass 1: [Phi(K) x 4][V x 4 (private)]
+  static constexpr int vs_off = 4 * ks_bytes;
+  static constexpr int red_off = vs_off + 2 * vs_bytes;
+  static constexpr int body(bool state_only) { return state_only ? vs_off + 4 * vs_bytes : red_off + red_bytes; }
+  static constexpr int main_bytes(bool state_only) {
+    return body(state_only) > stage_bytes ? body(state_only) : stage_bytes;
+  }
+  static constexpr int lds(bool state_only) { return main_bytes(state_only) + 4 * 96 * 4; }
+};
+
+// Staging layout of the state (floats): wave g's tile (ft, vt) occupies 16 x 64 consecutive floats in
+// accumulator order [register][lane]; z follows at kStageS, [g][16 c + dim].
+__device__ __forceinline__ int gstage_index(int row, int col) {
+  const int c = row >> 6, a = row & 63, g = a >> 4, d = a & 15;
+  const int r = 16 * (c & 1) + swz16(d), ft = c >> 1;
+  const int reg = 4 * (r >> 3) + (r & 3), hh = (r >> 2) & 1;
+  const int vt = col >> 5, n32 = col & 31;
+  return (((g * 3 + ft) * 2 + vt) * 16 + reg) * 64 + 32 * hh + n32;
+}
+__device__ __forceinline__ void gstage_in(float* st, const float* __restrict__ s, const float* __restrict__ zz) {
+  for (int e4 = threadIdx.x; e4 < kF * kDV / 4; e4 += 256) {
+    const float4 v = reinterpret_cast<const float4*>(s)[e4];
+    const int row = (4 * e4) / kDV, col = (4 * e4) % kDV;
+    *reinterpret_cast<float4*>(st + gstage_index(row, col)) = v;
+  }
+  for (int r = threadIdx.x; r < kF; r += 256) {
+    const int c = r >> 6, a = r & 63;
+    st[kStageS + (a >> 4) * 96 + 16 * c + (a & 15)] = zz[r];
+  }
+}
+__device__ __forceinline__ void gstage_out(const float* st, float* __restrict__ s, float* __restrict__ zz) {
+  for (int e4 = threadIdx.x; e4 < kF * kDV / 4; e4 += 256) {
+    const int row = (4 * e4) / kDV, col = (4 * e4) % kDV;
+    reinterpret_cast<float4*>(s)[e4] = *reinterpret_cast<const float4*>(st + gstage_index(row, col));
+  }
+  for (int r = threadIdx.x; r < kF; r += 256) {
+    const int c = r >> 6, a = r & 63;
+    zz[r] = st[kStageS + (a >> 4) * 96 + 16 * c + (a & 15)];
+  }
+}
+
+// Transposed (token-consecutive) read of the Phi(K) tile for the state update: like lds_tokfrag, but
+// lane row r of the 32-row tile receives column col0 + 16 (r / 16) + swz16(r % 16).
+__device__ __forceinline__ bf16x8 lds_tokfrag_swz(const __bf16* buf, int pitch, int tok0, int col0, int l) {
+  const int b = l >> 4, L = l & 15;
+  const int tok = tok0 + 4 * (b >> 1) + (L >> 2);
+  const int g4 = L & 3, sg = ((g4 & 1) << 1) | (g4 >> 1);
+  const int col = col0 + 16 * (b & 1) + 4 * sg;
+  const u32x2 lo =
+      __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + tok * pitch + col)));
+  const u32x2 hi = __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + (tok + 8) * pitch + col)));
+  const u32x4 r = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Featurize 8 consecutive dims of one token: channels 1..5 as MFMA operand fragments (slot i = dim i),
+// and the fp32 cos, sin, r.
+__device__ __forceinline__ void feat8(const bf16x8& u, const float4& rh0, const float4& rh1, const float (&om4)[8],
+                                      float kr, bf16x8 (&F)[5], float (&cr)[8], float (&sr)[8], float (&rr)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float rho = i < 4 ? rh0[i] : rh1[i - 4];
+    featurize1((float)u[i], rho, om4[i], kr, cr[i], sr[i], rr[i]);
+  }
+  u32x4 w[5];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int a = 2 * j, b = 2 * j + 1;
+    w[0][j] = pack_bf16x2(cr[a], cr[b]);
+    w[1][j] = pack_bf16x2(sr[a], sr[b]);
+    w[2][j] = pack_bf16x2(rr[a], rr[b]);
+    w[3][j] = pack_bf16x2(rr[a] * cr[a], rr[b] * cr[b]);
+    w[4][j] = pack_bf16x2(rr[a] * sr[a], rr[b] * sr[b]);
+  }
+#pragma unroll
+  for (int c = 0; c < 5; c++) F[c] = __builtin_bit_cast(bf16x8, w[c]);
+}
+
+// Phi(q) . z over this lane's 8 dims (features 16 c + 8h + i), z read from the wave's z vector;
+// per dim z0 + c z1 + s z2 + r (z3 + c z4 + s z5).
+__device__ __forceinline__ float dotz8(const float* zrow, const float (&cr)[8], const float (&sr)[8],
+                                       const float (&rr)[8]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i4 = 0; i4 < 2; i4++) {
+    float4 z[6];
+#pragma unroll
+    for (int c = 0; c < 6; c++) z[c] = *reinterpret_cast<const float4*>(zrow + 16 * c + 4 * i4);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int i = 4 * i4 + e;
+      float t = fmaf(cr[i], z[4][e], z[3][e]);
+      t = fmaf(sr[i], z[5][e], t);
+      acc += z[0][e];
+      acc = fmaf(rr[i], t, acc);
+      acc = fmaf(cr[i], z[1][e], acc);
+      acc = fmaf(sr[i], z[2][e], acc);
+    }
+  }
+  return acc;
+}
+
+template <int CH, bool STATE_ONLY>
+__global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs args) {
+  using G = GeomG<CH>;
+  constexpr int TB = G::TB, CT = G::CT, KP = G::KP, VP = G::VP, RP = G::RP;
+  // V pieces (16 bytes) per lane: pass 1 loads its private tile, pass 3 a quarter of the shared one
+  constexpr int NV = STATE_ONLY ? CT / 8 : CT / 32;
+  constexpr int VROW0 = STATE_ONLY ? 0 : CT / 4;  // pass 3: wave g writes rows g * CT/4 ..
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, grp = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
+  __bf16* KS = reinterpret_cast<__bf16*>(smem + grp * G::ks_bytes);
+  __bf16* Vbase = reinterpret_cast<__bf16*>(smem + G::vs_off);
+  float* red = reinterpret_cast<float*>(smem + G::red_off);
+  float* stage = reinterpret_cast<float*>(smem);
+  float* Zg = reinterpret_cast<float*>(smem + G::main_bytes(STATE_ONLY)) + grp * 96;
+  const int dbase = 16 * grp + 8 * h;
+  const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
+  const bf16x8 ONES = __builtin_bit_cast(bf16x8, ones4);
+  // the V tile of chunk number j of a piece (pass 3: shared double buffer; pass 1: private)
+  auto vtile = [&](int j) -> __bf16* {
+    return STATE_ONLY ? Vbase + grp * CT * VP : Vbase + (j & 1) * CT * VP;
+  };
+
+  const long long hi_c = range_lo(blockIdx.x + 1, args);
+  for (long long c = range_lo(blockIdx.x, args); c < hi_c;) {
+    const int bh = (int)(c / args.ncs);
+    const long long seq_c0 = (long long)bh * args.ncs;
+    const long long seq_end = seq_c0 + args.ncs;
+    const long long pend = hi_c < seq_end ? hi_c : seq_end;
+    const bool last_piece = (pend == seq_end);
+    const int t_begin = (int)(c - seq_c0) * CH;
+    const int t_end = min(args.T, (int)(pend - seq_c0) * CH);
+    c = pend;
+    if (STATE_ONLY && last_piece) continue;
+    const int hh = bh % args.H;
+    const __bf16* __restrict__ kp = static_cast<const __bf16*>(args.k) + (size_t)bh * args.T * kD;
+    const __bf16* __restrict__ qp = static_cast<const __bf16*>(args.q) + (size_t)bh * args.T * kD;
+    const __bf16* __restrict__ vp = static_cast<const __bf16*>(args.v) + (size_t)bh * args.T * kDV;
+    __bf16* __restrict__ op = static_cast<__bf16*>(args.out) + (size_t)bh * args.T * kDV;
+    float* slot = args.ws_state + (size_t)(bh + blockIdx.x) * kStateFloats;
+
+    float om4[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) om4[i] = anchor_rev(args.omega[(size_t)(hh % args.nph) * kD + dbase + i]);
+
+    // ---- initial state of the piece
+    f32x16 Sacc[3][2];
+#pragma unroll
+    for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++) zero16(Sacc[ft][vt]);
+    for (int m = l; m < 96; m += 64) Zg[m] = 0.0f;
+    if (!STATE_ONLY) {
+      auto add_slot = [&](const float* s, const float* zz) {
+        __syncthreads();
+        gstage_in(stage, s, zz);
+        __syncthreads();
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+          for (int vt = 0; vt < 2; vt++) {
+            const float* p = stage + ((grp * 3 + ft) * 2 + vt) * 16 * 64 + l;
+#pragma unroll
+            for (int i = 0; i < 16; i++) Sacc[ft][vt][i] += p[64 * i];
+          }
+        for (int m = l; m < 96; m += 64) Zg[m] += stage[kStageS + grp * 96 + m];
+      };
+      if (args.multi && args.scanned) {
+        add_slot(slot, slot + kF * kDV);
+      } else {
+        if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
+        if (args.multi) {
+          const int gf = range_of_chunk(seq_c0, args);
+          for (int gg = gf; gg < (int)blockIdx.x; gg++) {
+            const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
+            add_slot(sj, sj + kF * kDV);
+          }
+        }
+      }
+    }
+    __syncthreads();  // staging (aliasing the tiles) consumed; Zg initialised
+
+    // ---- raw inputs of one chunk: this lane's rows and phases, its pieces of V
+    bf16x8 uk[TB], uq[TB];
+    float4 rh[TB][2];
+    uint4 rv[NV];
+    float4 rh2[TB][2];  // pass 3: phases of the chunk after next, while rh still serves the queries
+    auto load_k = [&](int t0, float4 (&ph)[TB][2]) {
+      const int nv = min(CH, t_end - t0);
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        const int tc = t0 + min(32 * b + n32, nv - 1);
+        uk[b] = *reinterpret_cast<const bf16x8*>(kp + (size_t)tc * kD + dbase);
+        const float* pr = args.rho + (size_t)tc * kD + dbase;
+        ph[b][0] = *reinterpret_cast<const float4*>(pr);
+        ph[b][1] = *reinterpret_cast<const float4*>(pr + 4);
+      }
+    };
+    auto load_q = [&](int t0) {
+      const int nv = min(CH, t_end - t0);
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        const int tc = t0 + min(32 * b + n32, nv - 1);
+        uq[b] = *reinterpret_cast<const bf16x8*>(qp + (size_t)tc * kD + dbase);
+      }
+    };
+    auto load_v = [&](int t0) {
+      const int nv = min(CH, t_end - t0);
+#pragma unroll
+      for (int j = 0; j < NV; j++) {
+        const int e = l + 64 * j, row = grp * VROW0 + (e >> 3), col = 8 * (e & 7);
+        rv[j] = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + min(row, nv - 1)) * kDV + col);
+      }
+    };
+    auto load_raw = [&](int t0) {
+      load_k(t0, rh);
+      if (!STATE_ONLY) load_q(t0);
+      load_v(t0);
+    };
+    // this lane's pieces of V into a tile; rows past the chunk's end are zero
+    auto write_v = [&](__bf16* vt_, int nvalid) {
+#pragma unroll
+      for (int j = 0; j < NV; j++) {
+        const int e = l + 64 * j, row = grp * VROW0 + (e >> 3), col = 8 * (e & 7);
+        const unsigned m = 0u - (unsigned)(row < nvalid);
+        *reinterpret_cast<uint4*>(vt_ + row * VP + col) =
+            make_uint4(rv[j].x & m, rv[j].y & m, rv[j].z & m, rv[j].w & m);
+      }
+    };
+    bf16x8 KF[TB][5], QF[TB][5];
+    float dz[TB];
+    // Phi(K) rows to the wave's tile (channel 0 = ones); rows past the chunk's end (a ragged last chunk,
+    // or the upper half of the tile for chunk 16) are zeroed so that they reach neither z nor S.
+    auto write_k = [&](int nvalid) {
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        __bf16* row = KS + (32 * b + n32) * KP + 8 * h;
+        *reinterpret_cast<u32x4*>(row) = ones4;
+#pragma unroll
+        for (int cc = 1; cc < 6; cc++) *reinterpret_cast<bf16x8*>(row + 16 * cc) = KF[b][cc - 1];
+      }
+    };
+    auto zero_k_tail = [&](int nvalid) {
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        if (32 * b + n32 >= nvalid) {
+          __bf16* row = KS + (32 * b + n32) * KP + 8 * h;
+#pragma unroll
+          for (int cc = 0; cc < 6; cc++) *reinterpret_cast<u32x4*>(row + 16 * cc) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    auto feat_q = [&]() {  // queries of the loaded chunk + their readout part of the denominator (z as it is)
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        float cr[8], sr[8], rr[8];
+        feat8(uq[b], rh[b][0], rh[b][1], om4, args.kr, QF[b], cr, sr, rr);
+        const float d = dotz8(Zg + 8 * h, cr, sr, rr);
+        dz[b] = d + __shfl_xor(d, 32);
+      }
+    };
+    auto feat_k = [&]() {
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        float cr[8], sr[8], rr[8];
+        feat8(uk[b], rh[b][0], rh[b][1], om4, args.kr, KF[b], cr, sr, rr);
+      }
+    };
+
+    // ---- prologue: chunk 0 featurized, its Phi(K) and V in LDS; raw inputs of chunk 1 in registers
+    {
+      load_raw(t_begin);
+      const int nv0 = min(CH, t_end - t_begin);
+      feat_k();
+      write_k(nv0);
+      if (nv0 < CT) zero_k_tail(nv0);
+      if (!STATE_ONLY) feat_q();
+      write_v(vtile(0), nv0);
+      load_raw(t_begin + CH < t_end ? t_begin + CH : t_begin);
+    }
+
+    int j = 0;
+    for (int t0 = t_begin; t0 < t_end; t0 += CH, j++) {
+      const int nvalid = min(CH, t_end - t0);
+      const bool more = t0 + CH < t_end;
+      const int nvalid1 = more ? min(CH, t_end - t0 - CH) : CT;
+      const __bf16* Vs = vtile(j);
+      if (!STATE_ONLY) __syncthreads();  // V tile of this chunk complete; reduction buffer free
+
+      // keys of the next chunk (registers only; the tile is rewritten at the end of the iteration); the
+      // registers consumed here are refilled at once with the chunk after next
+      const int t2 = t0 + 2 * CH < t_end ? t0 + 2 * CH : t0;
+      feat_k();
+      if (!STATE_ONLY) {
+        write_v(vtile(j + 1), nvalid1);  // the other V buffer is no longer read by anyone
+        load_v(t2);
+        load_k(t2, rh2);
+      } else {
+        load_k(t2, rh);
+      }
+
+      if (!STATE_ONLY) {
+        // intra-chunk tiles A^T[s][t] = Phi(k_s) . Phi(q_t), masked to s <= t, rounded to bf16; Phi(k)
+        // from this lane's own rows of the LDS tile, Phi(q) from registers
+        bf16x8 P[TB][TB][2];
+        float rs[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; tb++) {
+          rs[tb] = 0.0f;
+#pragma unroll
+          for (int sb = 0; sb <= tb; sb++) {
+            f32x16 at;
+#pragma unroll
+            for (int i = 0; i < 16; i++) at[i] = 16.0f;  // channel 0: sixteen products 1 * 1
+            const __bf16* krow = KS + (32 * sb + n32) * KP + 8 * h;
+#pragma unroll
+            for (int cc = 0; cc < 5; cc++)
+              mma32(at, *reinterpret_cast<const bf16x8*>(krow + 16 * (cc + 1)), QF[tb][cc]);
+            float lo[8], hi8[8];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+              const int sl = 8 * (i >> 2) + 4 * h + (i & 3);
+              const float a = (sb == tb && sl > n32) ? 0.0f : at[i];
+              if (i < 8) lo[i] = a;
+              else hi8[i - 8] = a;
+            }
+            u32x4 w0, w1;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              w0[q] = pack_bf16x2(lo[2 * q], lo[2 * q + 1]);
+              w1[q] = pack_bf16x2(hi8[2 * q], hi8[2 * q + 1]);
+            }
+            P[tb][sb][0] = __builtin_bit_cast(bf16x8, w0);
+            P[tb][sb][1] = __builtin_bit_cast(bf16x8, w1);
+            rs[tb] = frag_sum(P[tb][sb][1], frag_sum(P[tb][sb][0], rs[tb]));
+          }
+        }
+        // numerators: V^T P (intra) + S^T Phi(q) (readout, S from before this chunk), written straight to
+        // the reduction buffer; each S^T operand is packed once and used for every token block
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          f32x16 num[TB];
+#pragma unroll
+          for (int tb = 0; tb < TB; tb++) {
+            zero16(num[tb]);
+#pragma unroll
+            for (int sb = 0; sb <= tb; sb++) {
+              mma32(num[tb], lds_tokfrag(Vs, VP, 32 * sb, 32 * vt, l), P[tb][sb][0]);
+              mma32(num[tb], lds_tokfrag(Vs, VP, 32 * sb + 16, 32 * vt, l), P[tb][sb][1]);
+            }
+          }
+#pragma unroll
+          for (int cc = 0; cc < 6; cc++) {
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+              w[q] = pack_bf16x2(Sacc[cc >> 1][vt][8 * (cc & 1) + 2 * q], Sacc[cc >> 1][vt][8 * (cc & 1) + 2 * q + 1]);
+            const bf16x8 sa = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int tb = 0; tb < TB; tb++) mma32(num[tb], sa, cc == 0 ? ONES : QF[tb][cc - 1]);
+          }
+#pragma unroll
+          for (int tb = 0; tb < TB; tb++) {
+            float* rrow = red + ((tb * 4 + grp) * 32 + n32) * RP;
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+              *reinterpret_cast<float4*>(rrow + 32 * vt + 8 * q + 4 * h) =
+                  make_float4(num[tb][4 * q], num[tb][4 * q + 1], num[tb][4 * q + 2], num[tb][4 * q + 3]);
+          }
+        }
+#pragma unroll
+        for (int tb = 0; tb < TB; tb++) {
+          const float rsf = rs[tb] + __shfl_xor(rs[tb], 32);
+          red[((tb * 4 + grp) * 32 + n32) * RP + 64] = rsf + dz[tb];  // both halves store the same value
+        }
+      }
+
+      // state update S += Phi(K)^T V, z += Phi(K)^T 1 for the wave's group
+      float zs[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 2 * TB; ks++) {
+        const bf16x8 B0 = lds_tokfrag(Vs, VP, 16 * ks, 0, l);
+        const bf16x8 B1 = lds_tokfrag(Vs, VP, 16 * ks, 32, l);
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) {
+          const bf16x8 A = lds_tokfrag_swz(KS, KP, 16 * ks, 32 * ft, l);
+          zs[ft] = frag_sum(A, zs[ft]);
+          mma32(Sacc[ft][0], A, B0);
+          mma32(Sacc[ft][1], A, B1);
+        }
+      }
+#pragma unroll
+      for (int ft = 0; ft < 3; ft++) {
+        const float zf = zs[ft] + __shfl_xor(zs[ft], 32);
+        float* zp = Zg + 32 * ft + 16 * (n32 >> 4) + swz16(n32 & 15);
+        const float znew = *zp + zf;
+        *zp = znew;  // both halves store the same value
+      }
+
+      // next chunk: queries (denominator part with the updated z), Phi(K) and V tiles, raw loads
+      if (!STATE_ONLY) {
+        feat_q();
+        load_q(t2);
+#pragma unroll
+        for (int b = 0; b < TB; b++) {
+          rh[b][0] = rh2[b][0];
+          rh[b][1] = rh2[b][1];
+        }
+      }
+      write_k(nvalid1);
+      if (STATE_ONLY) {
+        write_v(vtile(j + 1), nvalid1);
+        load_v(t2);
+        // interleave the next chunk's featurization with the update MFMAs and their LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 6 * TB; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+      }
+      if (nvalid1 < CT) zero_k_tail(nvalid1);
+
+      if (!STATE_ONLY) {
+        __syncthreads();  // all groups' partial numerators and denominators are in
+        constexpr int TPT = 256 / CT, NC = 64 / TPT;
+        const int t = tid / TPT, c0 = NC * (tid % TPT);
+        if (t < nvalid) {
+          const float* b0 = red + ((t >> 5) * 4 * 32 + (t & 31)) * RP;
+          constexpr int GS = 32 * RP;
+          const float den = ((b0[64] + b0[GS + 64]) + b0[2 * GS + 64]) + b0[3 * GS + 64];
+          const float inv = 1.0f / (den + args.ceps);
+#pragma unroll
+          for (int q4 = 0; q4 < NC / 8; q4++) {
+            u32x4 w;
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+              const int cb = c0 + 8 * q4 + 4 * half;
+              const float4 a0 = *reinterpret_cast<const float4*>(b0 + cb);
+              const float4 a1 = *reinterpret_cast<const float4*>(b0 + GS + cb);
+              const float4 a2 = *reinterpret_cast<const float4*>(b0 + 2 * GS + cb);
+              const float4 a3 = *reinterpret_cast<const float4*>(b0 + 3 * GS + cb);
+              w[2 * half] = pack_bf16x2((((a0.x + a1.x) + a2.x) + a3.x) * inv, (((a0.y + a1.y) + a2.y) + a3.y) * inv);
+              w[2 * half + 1] =
+                  pack_bf16x2((((a0.z + a1.z) + a2.z) + a3.z) * inv, (((a0.w + a1.w) + a2.w) + a3.w) * inv);
+            }
+            *reinterpret_cast<u32x4*>(op + (size_t)(t0 + t) * kDV + c0 + 8 * q4) = w;
+          }
+        }
+      }
+    }
+
+    float* dst_s = STATE_ONLY ? slot : (last_piece && args.S ? args.S + (size_t)bh * kF * kDV : nullptr);
+    float* dst_z = STATE_ONLY ? slot + kF * kDV : (last_piece && args.S ? args.z + (size_t)bh * kF : nullptr);
+    __syncthreads();  // tiles and reduction buffer are dead; the staging area may be reused
+    if (dst_s) {
+#pragma unroll
+      for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          float* p = stage + ((grp * 3 + ft) * 2 + vt) * 16 * 64 + l;
+#pragma unroll
+          for (int i = 0; i < 16; i++) p[64 * i] = Sacc[ft][vt][i];
+        }
+      for (int m = l; m < 96; m += 64) stage[kStageS + grp * 96 + m] = Zg[m];
+      __syncthreads();
+      gstage_out(stage, dst_s, dst_z);
+      __syncthreads();
+    }
+  }
+}
+
+template <int CH>
+hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
+  using G = GeomG<CH>;
+  static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::lds(true));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            G::lds(false));
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  if (a.multi) {
+    hipLaunchKernelGGL((prefill_grp_kernel<CH, true>), dim3(a.G), dim3(256), G::lds(true), stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.scanned) {
+      e = launch_prefill_scan(a, BH, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL((prefill_grp_kernel<CH, false>), dim3(a.G), dim3(256), G::lds(false), stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream) {
+  switch (chunk) {
+    case 16: return launch_grp_t<16>(a, BH, stream);
+    case 32: return launch_grp_t<32>(a, BH, stream);
+    case 64: return launch_grp_t<64>(a, BH, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sanatan

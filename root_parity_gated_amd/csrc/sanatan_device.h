@@ -34,11 +34,17 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Position phase in revolutions, frac(t * lambda_a / (2 pi)), lambda_a = base^(-a/d); fp64
-// so that large positions keep full fp32 accuracy of the reduced phase.
-__device__ __forceinline__ float phase_rev(int64_t t, int a, double log2_base) {
-  const double la = exp2(-(double)a * (1.0 / kD) * log2_base) * 0.15915494309189533576888376;
-  const double x = (double)t * la;
+// so that large positions keep full fp32 accuracy of the reduced phase.  phase_step gives
+// lambda_a / (2 pi) (one fp64 exp2, worth hoisting out of loops over t).
+__device__ __forceinline__ double phase_step(int a, double log2_base) {
+  return exp2(-(double)a * (1.0 / kD) * log2_base) * 0.15915494309189533576888376;
+}
+__device__ __forceinline__ float phase_at(int64_t t, double step) {
+  const double x = (double)t * step;
   return (float)(x - floor(x));
+}
+__device__ __forceinline__ float phase_rev(int64_t t, int a, double log2_base) {
+  return phase_at(t, phase_step(a, log2_base));
 }
 
 // Root anchor in revolutions, frac((omega + pi/4) / (2 pi)), in fp64.
