@@ -27,6 +27,15 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// x[l] + x[l ^ 32] in every lane, with the gfx950 half-swap instead of an LDS permute.  The swapped
+// words are read back through plain unsigned copies: a bit_cast applied directly to an element of
+// the returned pair was miscompiled into element 0.
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const unsigned a0 = r[0], a1 = r[1];
+  return __uint_as_float(a0) + __uint_as_float(a1);
+}
+
 __device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         float cr[8], sr[8], rr[8];
         feat8(uq[b], rh[b][0], rh[b][1], om4, args.kr, QF[b], cr, sr, rr);
         const float d = dotz8(Zg + 8 * h, cr, sr, rr);
-        dz[b] = d + __shfl_xor(d, 32);
+        dz[b] = xor32_sum(d);
       }
     };
     auto feat_k = [&]() {
@@ -330,19 +330,93 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       const bool more = t0 + CH < t_end;
       const int nvalid1 = more ? min(CH, t_end - t0 - CH) : CT;
       const __bf16* Vs = vtile(j);
-      if (!STATE_ONLY) __syncthreads();  // V tile of this chunk complete; reduction buffer free
+      const int t2 = t0 + 2 * CH < t_end ? t0 + 2 * CH : t0;
+      if constexpr (STATE_ONLY) {
+        // Pass 1: S += Phi(K)^T V for this chunk, with the next chunk's keys featurized in between the
+        // update MFMAs (scheduling fences keep the two streams interleaved), LDS fragments read one
+        // K-step ahead, and the raw inputs of the chunk after next loaded a full iteration ahead.
+        bf16x8 uk2[TB];
+        float4 rhn[TB][2];
+#pragma unroll
+        for (int b = 0; b < TB; b++) {
+          const int nv = min(CH, t_end - t2);
+          const int tc = t2 + min(32 * b + n32, nv - 1);
+          uk2[b] = *reinterpret_cast<const bf16x8*>(kp + (size_t)tc * kD + dbase);
+          const float* pr = args.rho + (size_t)tc * kD + dbase;
+          rhn[b][0] = *reinterpret_cast<const float4*>(pr);
+          rhn[b][1] = *reinterpret_cast<const float4*>(pr + 4);
+        }
+        float cr[TB][8], sr[TB][8], rr[TB][8];
+        auto fe = [&](int e) {
+          const int b = e >> 3, i = e & 7;
+          const float rho = i < 4 ? rh[b][0][i] : rh[b][1][i - 4];
+          featurize1((float)uk[b][i], rho, om4[i], args.kr, cr[b][i], sr[b][i], rr[b][i]);
+        };
+        bf16x8 Af[2][3], Bf[2][2];
+        auto ldf = [&](int ks, int buf) {
+          Bf[buf][0] = lds_tokfrag(Vs, VP, 16 * ks, 0, l);
+          Bf[buf][1] = lds_tokfrag(Vs, VP, 16 * ks, 32, l);
+#pragma unroll
+          for (int ft = 0; ft < 3; ft++) Af[buf][ft] = lds_tokfrag_swz(KS, KP, 16 * ks, 32 * ft, l);
+        };
+        constexpr int NE = 8 * TB;  // components to featurize, spread over the 2 TB K-steps
+        float zs[3] = {0.0f, 0.0f, 0.0f};
+        ldf(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 2 * TB; ks++) {
+          if (ks + 1 < 2 * TB) ldf(ks + 1, (ks + 1) & 1);
+#pragma unroll
+          for (int ft = 0; ft < 3; ft++) {
+            mma32(Sacc[ft][0], Af[ks & 1][ft], Bf[ks & 1][0]);
+            mma32(Sacc[ft][1], Af[ks & 1][ft], Bf[ks & 1][1]);
+            zs[ft] = frag_sum(Af[ks & 1][ft], zs[ft]);
+          }
+#pragma unroll
+          for (int e = ks * NE / (2 * TB); e < (ks + 1) * NE / (2 * TB); e++) fe(e);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int b = 0; b < TB; b++) {
+          u32x4 w[5];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int a = 2 * q, c = 2 * q + 1;
+            w[0][q] = pack_bf16x2(cr[b][a], cr[b][c]);
+            w[1][q] = pack_bf16x2(sr[b][a], sr[b][c]);
+            w[2][q] = pack_bf16x2(rr[b][a], rr[b][c]);
+            w[3][q] = pack_bf16x2(rr[b][a] * cr[b][a], rr[b][c] * cr[b][c]);
+            w[4][q] = pack_bf16x2(rr[b][a] * sr[b][a], rr[b][c] * sr[b][c]);
+          }
+#pragma unroll
+          for (int cc = 0; cc < 5; cc++) KF[b][cc] = __builtin_bit_cast(bf16x8, w[cc]);
+        }
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) {
+          const float zf = xor32_sum(zs[ft]);
+          float* zp = Zg + 32 * ft + 16 * (n32 >> 4) + swz16(n32 & 15);
+          const float znew = *zp + zf;
+          *zp = znew;  // both halves store the same value
+        }
+        write_k(nvalid1);
+        write_v(vtile(j + 1), nvalid1);
+        load_v(t2);
+#pragma unroll
+        for (int b = 0; b < TB; b++) {
+          uk[b] = uk2[b];
+          rh[b][0] = rhn[b][0];
+          rh[b][1] = rhn[b][1];
+        }
+        if (nvalid1 < CT) zero_k_tail(nvalid1);
+        continue;
+      }
+      __syncthreads();  // V tile of this chunk complete; reduction buffer free
 
       // keys of the next chunk (registers only; the tile is rewritten at the end of the iteration); the
       // registers consumed here are refilled at once with the chunk after next
-      const int t2 = t0 + 2 * CH < t_end ? t0 + 2 * CH : t0;
       feat_k();
-      if (!STATE_ONLY) {
-        write_v(vtile(j + 1), nvalid1);  // the other V buffer is no longer read by anyone
-        load_v(t2);
-        load_k(t2, rh2);
-      } else {
-        load_k(t2, rh);
-      }
+      write_v(vtile(j + 1), nvalid1);  // the other V buffer is no longer read by anyone
+      load_v(t2);
+      load_k(t2, rh2);
 
       if (!STATE_ONLY) {
         // intra-chunk tiles A^T[s][t] = Phi(k_s) . Phi(q_t), masked to s <= t, rounded to bf16; Phi(k)
@@ -415,7 +489,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         }
 #pragma unroll
         for (int tb = 0; tb < TB; tb++) {
-          const float rsf = rs[tb] + __shfl_xor(rs[tb], 32);
+          const float rsf = xor32_sum(rs[tb]);
           red[((tb * 4 + grp) * 32 + n32) * RP + 64] = rsf + dz[tb];  // both halves store the same value
         }
       }
@@ -436,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       }
 #pragma unroll
       for (int ft = 0; ft < 3; ft++) {
-        const float zf = zs[ft] + __shfl_xor(zs[ft], 32);
+        const float zf = xor32_sum(zs[ft]);
         float* zp = Zg + 32 * ft + 16 * (n32 >> 4) + swz16(n32 & 15);
         const float znew = *zp + zf;
         *zp = znew;  // both halves store the same value
@@ -453,18 +527,6 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         }
       }
       write_k(nvalid1);
-      if (STATE_ONLY) {
-        write_v(vtile(j + 1), nvalid1);
-        load_v(t2);
-        // interleave the next chunk's featurization with the update MFMAs and their LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int i = 0; i < 6 * TB; i++) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 28, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        }
-      }
       if (nvalid1 < CT) zero_k_tail(nvalid1);
 
       if (!STATE_ONLY) {
