@@ -4,25 +4,31 @@
 // o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c eps) -- the state is written before it is read.
 //
 // HBM-bound: 2 x 99,840 B of state move per head-state and token, against 0.5 flop/byte.
-// One 256-thread workgroup owns one head-state and streams its S once: each thread holds 24
-// float4 row pieces (rows rg + 16m, columns 4cg..4cg+3), so a wave reads 4 KB-contiguous
+// One 512-thread workgroup owns one head-state and streams its S once: each thread holds 12
+// float4 row pieces (rows rg + 32m, columns 4cg..4cg+3), so each wave touches 4 KB-contiguous
 // slabs; the rank-1 update and the readout share one pass, and the readout uses the updated S.
+// The state is touched once per token, so its loads and stores are marked non-temporal (they
+// would only evict other data from the caches).
 #include "launchers.h"
 #include "sanatan_device.h"
 
 namespace sanatan {
 
-__global__ __launch_bounds__(256) void decode_step_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                          const float* __restrict__ v, int64_t pos,
-                                                          const float* __restrict__ omega, int nph,
-                                                          double log2_base, float kr, float ceps,
-                                                          float* __restrict__ S, float* __restrict__ z,
-                                                          float* __restrict__ out) {
+namespace {
+constexpr int kDecThreads = 512;
+constexpr int kDecRows = kDecThreads / 16;  // row groups: 16 threads cover the 64 columns of a row
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+}  // namespace
+
+__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int64_t pos,
+    const float* __restrict__ omega, int nph, double log2_base, float kr, float ceps, float* __restrict__ S,
+    float* __restrict__ z, float* __restrict__ out) {
   __shared__ float fk[kF];
   __shared__ float fq[kF];
   __shared__ float vs[kDV];
-  __shared__ float red[16][kDV + 4];
-  __shared__ float dred[4];
+  __shared__ float red[kDecRows][kDV + 4];
+  __shared__ float dred[kDecThreads / 64];
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -31,13 +37,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const float* __restric
 
   // Issue the state loads first so their latency overlaps the feature computation.
   const int cg = tid & 15;  // column group: columns 4cg .. 4cg+3
-  const int rg = tid >> 4;  // row group: rows rg + 16m, m < 24
-  float4 rows[kF / 16];
+  const int rg = tid >> 4;  // row group: rows rg + kDecRows m
+  f32x4v rows[kF / kDecRows];
 #pragma unroll
-  for (int m = 0; m < kF / 16; m++) rows[m] = *reinterpret_cast<const float4*>(&Si[(rg + 16 * m) * kDV + 4 * cg]);
-  float zr[2];
-  zr[0] = zi[tid];
-  zr[1] = (tid + 256 < kF) ? zi[tid + 256] : 0.0f;
+  for (int m = 0; m < kF / kDecRows; m++)
+    rows[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(&Si[(rg + kDecRows * m) * kDV + 4 * cg]));
+  const float zr = tid < kF ? zi[tid] : 0.0f;
 
   if (tid < 2 * kD) {
     const int a = tid & (kD - 1);
@@ -58,39 +63,28 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const float* __restric
   }
   __syncthreads();
 
-  const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * cg]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const f32x4v vv = *reinterpret_cast<const f32x4v*>(&vs[4 * cg]);
+  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < kF / 16; m++) {
-    const int f = rg + 16 * m;
+  for (int m = 0; m < kF / kDecRows; m++) {
+    const int f = rg + kDecRows * m;
     const float a = fk[f], b = fq[f];
-    float4 s = rows[m];
-    s.x = fmaf(a, vv.x, s.x);
-    s.y = fmaf(a, vv.y, s.y);
-    s.z = fmaf(a, vv.z, s.z);
-    s.w = fmaf(a, vv.w, s.w);
-    *reinterpret_cast<float4*>(&Si[f * kDV + 4 * cg]) = s;
-    acc.x = fmaf(b, s.x, acc.x);
-    acc.y = fmaf(b, s.y, acc.y);
-    acc.z = fmaf(b, s.z, acc.z);
-    acc.w = fmaf(b, s.w, acc.w);
+    f32x4v s = rows[m];
+#pragma unroll
+    for (int e = 0; e < 4; e++) s[e] = fmaf(a, vv[e], s[e]);
+    __builtin_nontemporal_store(s, reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]));
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc[e] = fmaf(b, s[e], acc[e]);
   }
   // z update and the denominator partial
-  float dpart;
-  {
-    const float z0 = zr[0] + fk[tid];
+  float dpart = 0.0f;
+  if (tid < kF) {
+    const float z0 = zr + fk[tid];
     zi[tid] = z0;
     dpart = fq[tid] * z0;
-    if (tid + 256 < kF) {
-      const float z1 = zr[1] + fk[tid + 256];
-      zi[tid + 256] = z1;
-      dpart = fmaf(fq[tid + 256], z1, dpart);
-    }
   }
-  red[rg][4 * cg + 0] = acc.x;
-  red[rg][4 * cg + 1] = acc.y;
-  red[rg][4 * cg + 2] = acc.z;
-  red[rg][4 * cg + 3] = acc.w;
+#pragma unroll
+  for (int e = 0; e < 4; e++) red[rg][4 * cg + e] = acc[e];
   // wave-level reduction of the denominator partials (fixed order: deterministic)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) dpart += __shfl_xor(dpart, off);
@@ -99,15 +93,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const float* __restric
   if (tid < kDV) {
     float num = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 16; g++) num += red[g][tid];
-    const float den = ((dred[0] + dred[1]) + dred[2]) + dred[3];
+    for (int g = 0; g < kDecRows; g++) num += red[g][tid];
+    float den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecThreads / 64; w++) den += dred[w];
     out[(size_t)i * kDV + tid] = num / (den + ceps);
   }
 }
 
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
                               const MethodConsts& mc, float* S, float* z, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_step_kernel, dim3(N), dim3(256), 0, stream, q, k, v, pos, mc.omega, mc.nph,
+  hipLaunchKernelGGL(decode_step_kernel, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, mc.omega, mc.nph,
                      mc.log2_base, mc.kr, mc.ceps, S, z, out);
   return hipGetLastError();
 }
