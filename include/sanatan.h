@@ -122,7 +122,8 @@ size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, c
  * (training) form, no recurrence: w = (kappa/c)^p, o_t = sum_{s<=t} w v_s / (sum w + eps).
  * [N] §2.6; p = 2 is the sharpened kernel trained first in [N] §4.1, p = 1 the deployed one.
  *   q, k : [B][H][T][d], v, out : [B][H][T][d_v], element type t; p : 1 or 2 (else INVALID_ARG).
- *   ws   : at least sanatan_quadratic_workspace_bytes() bytes (holds Phi(K) in element type t).
+ *   ws   : at least sanatan_quadratic_workspace_bytes() bytes: the position phase table [T][d] fp32
+ *          (padded to 256 bytes), then Phi(K) [B][H][T][6d] in element type t.
  */
 sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
                                         int H, int T, int p, int64_t pos0, const sanatan_params* params,

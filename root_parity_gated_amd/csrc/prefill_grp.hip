@@ -257,10 +257,12 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         rv[j] = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + min(row, nv - 1)) * kDV + col);
       }
     };
+    // Same order as the loop's own batch (V, keys and phases, queries): the compiler's wait at the loop
+    // head must cover both paths, and a different order here would make it wait for everything.
     auto load_raw = [&](int t0) {
+      load_v(t0);
       load_k(t0, rh);
       if (!STATE_ONLY) load_q(t0);
-      load_v(t0);
     };
     // this lane's pieces of V into a tile; rows past the chunk's end are zero
     auto write_v = [&](__bf16* vt_, int nvalid) {
@@ -309,6 +311,34 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       for (int b = 0; b < TB; b++) {
         float cr[8], sr[8], rr[8];
         feat8(uk[b], rh[b][0], rh[b][1], om4, args.kr, KF[b], cr, sr, rr);
+      }
+    };
+
+    // o = num / (den + c eps) for one chunk from the four groups' partials in the reduction buffer
+    auto normalise = [&](int tc0, int nv) {
+      constexpr int TPT = 256 / CT, NC = 64 / TPT;
+      const int t = tid / TPT, c0 = NC * (tid % TPT);
+      if (t < nv) {
+        const float* b0 = red + ((t >> 5) * 4 * 32 + (t & 31)) * RP;
+        constexpr int GS = 32 * RP;
+        const float den = ((b0[64] + b0[GS + 64]) + b0[2 * GS + 64]) + b0[3 * GS + 64];
+        const float inv = 1.0f / (den + args.ceps);
+#pragma unroll
+        for (int q4 = 0; q4 < NC / 8; q4++) {
+          u32x4 w;
+#pragma unroll
+          for (int half = 0; half < 2; half++) {
+            const int cb = c0 + 8 * q4 + 4 * half;
+            const float4 a0 = *reinterpret_cast<const float4*>(b0 + cb);
+            const float4 a1 = *reinterpret_cast<const float4*>(b0 + GS + cb);
+            const float4 a2 = *reinterpret_cast<const float4*>(b0 + 2 * GS + cb);
+            const float4 a3 = *reinterpret_cast<const float4*>(b0 + 3 * GS + cb);
+            w[2 * half] = pack_bf16x2((((a0.x + a1.x) + a2.x) + a3.x) * inv, (((a0.y + a1.y) + a2.y) + a3.y) * inv);
+            w[2 * half + 1] =
+                pack_bf16x2((((a0.z + a1.z) + a2.z) + a3.z) * inv, (((a0.w + a1.w) + a2.w) + a3.w) * inv);
+          }
+          *reinterpret_cast<u32x4*>(op + (size_t)(tc0 + t) * kDV + c0 + 8 * q4) = w;
+        }
       }
     };
 
@@ -409,14 +439,33 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         if (nvalid1 < CT) zero_k_tail(nvalid1);
         continue;
       }
-      __syncthreads();  // V tile of this chunk complete; reduction buffer free
+      // the previous chunk's partial numerators and this chunk's V tile are complete; the previous chunk
+      // is normalised and stored here (its stores then have a whole iteration to drain), and the second
+      // barrier frees the reduction buffer for this chunk
+      __syncthreads();
+      if (t0 > t_begin) normalise(t0 - CH, CH);
+      __syncthreads();
 
       // keys of the next chunk (registers only; the tile is rewritten at the end of the iteration); the
       // registers consumed here are refilled at once with the chunk after next
       feat_k();
-      write_v(vtile(j + 1), nvalid1);  // the other V buffer is no longer read by anyone
-      load_v(t2);
+      // one batch of loads for the chunk after next, a full iteration before its use, into second
+      // register sets (V and the queries of the next chunk are consumed at the end of this iteration)
+      bf16x8 uq2[TB];
+      uint4 rvn[NV];
+#pragma unroll
+      for (int jj = 0; jj < NV; jj++) {
+        const int nv = min(CH, t_end - t2);
+        const int e = l + 64 * jj, row = grp * VROW0 + (e >> 3), col = 8 * (e & 7);
+        rvn[jj] = *reinterpret_cast<const uint4*>(vp + (size_t)(t2 + min(row, nv - 1)) * kDV + col);
+      }
       load_k(t2, rh2);
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        const int nv = min(CH, t_end - t2);
+        const int tc = t2 + min(32 * b + n32, nv - 1);
+        uq2[b] = *reinterpret_cast<const bf16x8*>(qp + (size_t)tc * kD + dbase);
+      }
 
       if (!STATE_ONLY) {
         // intra-chunk tiles A^T[s][t] = Phi(k_s) . Phi(q_t), masked to s <= t, rounded to bf16; Phi(k)
@@ -519,43 +568,23 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       // next chunk: queries (denominator part with the updated z), Phi(K) and V tiles, raw loads
       if (!STATE_ONLY) {
         feat_q();
-        load_q(t2);
+        write_v(vtile(j + 1), nvalid1);  // the other V buffer is no longer read by anyone
 #pragma unroll
         for (int b = 0; b < TB; b++) {
+          uq[b] = uq2[b];
           rh[b][0] = rh2[b][0];
           rh[b][1] = rh2[b][1];
         }
+#pragma unroll
+        for (int jj = 0; jj < NV; jj++) rv[jj] = rvn[jj];
       }
       write_k(nvalid1);
       if (nvalid1 < CT) zero_k_tail(nvalid1);
-
-      if (!STATE_ONLY) {
-        __syncthreads();  // all groups' partial numerators and denominators are in
-        constexpr int TPT = 256 / CT, NC = 64 / TPT;
-        const int t = tid / TPT, c0 = NC * (tid % TPT);
-        if (t < nvalid) {
-          const float* b0 = red + ((t >> 5) * 4 * 32 + (t & 31)) * RP;
-          constexpr int GS = 32 * RP;
-          const float den = ((b0[64] + b0[GS + 64]) + b0[2 * GS + 64]) + b0[3 * GS + 64];
-          const float inv = 1.0f / (den + args.ceps);
-#pragma unroll
-          for (int q4 = 0; q4 < NC / 8; q4++) {
-            u32x4 w;
-#pragma unroll
-            for (int half = 0; half < 2; half++) {
-              const int cb = c0 + 8 * q4 + 4 * half;
-              const float4 a0 = *reinterpret_cast<const float4*>(b0 + cb);
-              const float4 a1 = *reinterpret_cast<const float4*>(b0 + GS + cb);
-              const float4 a2 = *reinterpret_cast<const float4*>(b0 + 2 * GS + cb);
-              const float4 a3 = *reinterpret_cast<const float4*>(b0 + 3 * GS + cb);
-              w[2 * half] = pack_bf16x2((((a0.x + a1.x) + a2.x) + a3.x) * inv, (((a0.y + a1.y) + a2.y) + a3.y) * inv);
-              w[2 * half + 1] =
-                  pack_bf16x2((((a0.z + a1.z) + a2.z) + a3.z) * inv, (((a0.w + a1.w) + a2.w) + a3.w) * inv);
-            }
-            *reinterpret_cast<u32x4*>(op + (size_t)(t0 + t) * kDV + c0 + 8 * q4) = w;
-          }
-        }
-      }
+    }
+    if (!STATE_ONLY) {
+      __syncthreads();  // the last chunk's partial numerators and denominators are in
+      const int t_last = t_end - 1 - (t_end - 1 - t_begin) % CH;
+      normalise(t_last, t_end - t_last);
     }
 
     float* dst_s = STATE_ONLY ? slot : (last_piece && args.S ? args.S + (size_t)bh * kF * kDV : nullptr);

@@ -5,207 +5,247 @@
 // this is the training/parallel form.  Because 0 <= kappa <= 4d = c, every weight lies in [0, 1]
 // and no running maximum is needed (unlike softmax): partial sums over key blocks just add.
 //
-// Phi(K) is featurized once into the workspace (element type of the call); each workgroup
-// featurizes its own query rows straight into MFMA operand registers.  Per key block of 64
-// keys: Phi(K) and V^T are staged in LDS, every wave forms the score tile transposed
-// (rows = keys, cols = its query rows) so that the masked, powered tile is directly the A
-// operand of w.V' (V' = [V | 1]: the fifth 16-column tile accumulates the denominator).
-#include "launchers.h"
-#include "sanatan_device.h"
+// Phi(K) is featurized once into the workspace (element type of the call), after the position
+// phase table.  A workgroup is 4 waves (one per SIMD); each wave owns MQ tiles of 32 query rows
+// and featurizes them once into 32x32x16 MFMA operand registers (K-step j = 16 features).  Per
+// block of 32 keys, Phi(K) (channels 1..5: channel 0 is the constant 1 and contributes exactly
+// d = 64 to every score) and V are staged token-major in LDS, double-buffered, and every wave
+// forms its transposed score tiles A^T[s][t]; each Phi(K) fragment feeds MQ MFMAs.  The masked,
+// powered tile is the B operand of V^T P (V^T read with the transposing LDS load), and its row
+// sums (v_dot2) accumulate the denominator.
+#include "prefill_common.h"
 
 namespace sanatan {
+namespace {
 
 template <typename T>
-struct QuadGeom {
-  static constexpr int MT = sizeof(T) == 2 ? 2 : 1;   // 16-row query tiles per wave
-  static constexpr int QROWS = 4 * 16 * MT;           // query rows per workgroup
-  static constexpr int KB = 64;                        // keys per block
-  static constexpr int KPITCH = kF + 16 / (int)sizeof(T);
-  static constexpr int VPITCH = KB + 16 / (int)sizeof(T);
-  static constexpr size_t k_bytes = (size_t)KB * KPITCH * sizeof(T);
-  static constexpr size_t v_bytes = (size_t)kDV * VPITCH * sizeof(T);
-  static constexpr size_t lds = k_bytes + v_bytes;
+struct QGeom {
+  static constexpr int MQ = sizeof(T) == 2 ? 2 : 1;  // 32-row query tiles per wave
+  static constexpr int QROWS = 4 * 32 * MQ;          // query rows per workgroup
+  static constexpr int KB = 32;                       // keys per block
+  static constexpr int NF = kF - kD;                  // staged features: channels 1..5
+  static constexpr int NJ = NF / 16;                  // K-steps of the score product
+  static constexpr int KP = NF + 16 / (int)sizeof(T); // Phi(K) tile pitch (elements)
+  static constexpr int VP = kDV + 16 / (int)sizeof(T);
+  static constexpr int k_bytes = KB * KP * (int)sizeof(T);
+  static constexpr int v_bytes = KB * VP * (int)sizeof(T);
+  static constexpr int buf_bytes = k_bytes + v_bytes;
+  static constexpr int lds = 2 * buf_bytes;
+  static constexpr int EL = 16 / (int)sizeof(T);     // elements per 16-byte piece
+  static constexpr int KPIECES = KB * NF / EL;        // 16-byte pieces of one Phi(K) block
+  static constexpr int VPIECES = KB * kDV / EL;
+  static constexpr int PIECES = (KPIECES + VPIECES + 255) / 256;  // per thread
 };
+
+template <typename T> struct U4 { typedef uint4 type; };
 
 template <typename T, int P>
 __global__ __launch_bounds__(256, 1) void quadratic_kernel(const T* __restrict__ q, const T* __restrict__ phik,
                                                            const T* __restrict__ v, T* __restrict__ out,
-                                                           const float* __restrict__ omega, int nph, int H, int Tn,
-                                                           int BH, int nqb, int64_t pos0, double log2_base, float kr,
-                                                           float inv_c, float eps) {
-  using Gm = QuadGeom<T>;
-  using Frag = typename FragT<T>::type;
-  constexpr int MT = Gm::MT, KB = Gm::KB, KPITCH = Gm::KPITCH, VPITCH = Gm::VPITCH;
+                                                           const float* __restrict__ rho, const float* __restrict__ omega,
+                                                           int nph, int H, int Tn, int BH, int nqb, float kr, float inv_c,
+                                                           float eps) {
+  using G = QGeom<T>;
+  typedef typename FragT<T>::type Frag;
+  constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  T* Ks = reinterpret_cast<T*>(smem);                  // [KB][KPITCH]  Phi(K) block, token-major
-  T* Vt = reinterpret_cast<T*>(smem + Gm::k_bytes);    // [64][VPITCH]  V^T block
-
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, qd = l >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
   // heaviest (latest) query blocks first across all sequences
   const int qb = nqb - 1 - (int)(blockIdx.x / BH);
   const int bh = (int)(blockIdx.x % BH);
-  const int h = bh % H;
-  const int row0 = qb * Gm::QROWS + w * 16 * MT;  // this wave's first query row
+  const int hd = bh % H;
+  const int row0 = qb * G::QROWS + w * 32 * MQ;  // this wave's first query row
   const T* qp = q + (size_t)bh * Tn * kD;
-  const T* kp = phik + (size_t)bh * Tn * kF;
+  const T* kp = phik + (size_t)bh * Tn * kF + kD;  // skip channel 0
   const T* vp = v + (size_t)bh * Tn * kDV;
   T* op = out + (size_t)bh * Tn * kDV;
 
-  // Phi(Q) fragments, natural feature order: K-step j covers features 32j .. 32j+31 = channel j/2,
-  // dims 32(j%2) + 8qd + i; this lane featurizes dims {8qd .. 8qd+7, 32+8qd .. 32+8qd+7}.
-  Frag QF[MT][12];
+  // ---- Phi(q) operands: K-step j = channel 1 + j/4, dims 16 (j%4) + 8h + i (slot i)
+  Frag QF[MQ][NJ];
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) {
-    const int t = row0 + 16 * mt + r;
-    const bool valid = t < Tn;
+  for (int mq = 0; mq < MQ; mq++) {
+    const int t = min(row0 + 32 * mq + n32, Tn - 1);
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++) {
-      float ch[6][8];
+    for (int m = 0; m < 4; m++) {
+      float cr[8], sr[8], rr[8];
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const int a = 32 * hh + 8 * qd + i;
-        const float u = valid ? to_f32(qp[(size_t)t * kD + a]) : 0.0f;
-        const float om4 = anchor_rev(omega[(size_t)(h % nph) * kD + a]);
-        const float rho = phase_rev(pos0 + t, a, log2_base);
-        float cr, sr, rr;
-        featurize1(u, rho, om4, kr, cr, sr, rr);
-        ch[0][i] = 1.0f;
-        ch[1][i] = cr;
-        ch[2][i] = sr;
-        ch[3][i] = rr;
-        ch[4][i] = rr * cr;
-        ch[5][i] = rr * sr;
+        const int a = 16 * m + 8 * h + i;
+        const float om4 = anchor_rev(omega[(size_t)(hd % nph) * kD + a]);
+        featurize1(to_f32(qp[(size_t)t * kD + a]), rho[(size_t)t * kD + a], om4, kr, cr[i], sr[i], rr[i]);
+      }
+      float ch[5][8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        ch[0][i] = cr[i];
+        ch[1][i] = sr[i];
+        ch[2][i] = rr[i];
+        ch[3][i] = rr[i] * cr[i];
+        ch[4][i] = rr[i] * sr[i];
       }
 #pragma unroll
-      for (int c = 0; c < 6; c++) {
-        float lo[4] = {ch[c][0], ch[c][1], ch[c][2], ch[c][3]}, hi[4] = {ch[c][4], ch[c][5], ch[c][6], ch[c][7]};
-        QF[mt][2 * c + hh] = pack8<T>(lo, hi);
-      }
+      for (int c = 0; c < 5; c++) QF[mq][4 * c + m] = pack8f<T>(ch[c]);
     }
   }
 
-  Frag ONES;
-#pragma unroll
-  for (int i = 0; i < 8; i++) ONES[i] = (T)(r == 0 ? 1.0f : 0.0f);
-  f32x4 num[MT][5];
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-    for (int nt = 0; nt < 5; nt++) num[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int last_row = min(Tn - 1, qb * Gm::QROWS + Gm::QROWS - 1);
+  // ---- key blocks: staged Phi(K) (channels 1..5) and V, double-buffered
+  const int last_row = min(Tn - 1, qb * G::QROWS + G::QROWS - 1);
   const int nkb = last_row / KB + 1;
-  const int my_last = min(Tn - 1, row0 + 16 * MT - 1);
-  for (int kb = 0; kb < nkb; kb++) {
+  const int my_last = min(Tn - 1, row0 + 32 * MQ - 1);
+  uint4 pf[G::PIECES];
+  auto fetch = [&](int kb) {  // this thread's 16-byte pieces of key block kb -> registers
     const int s0 = kb * KB;
-    // stage Phi(K) rows s0 .. s0+63 (token-major) and V^T
-    {
-      constexpr int E = 16 / (int)sizeof(T);
-      constexpr int PER_ROW = kF / E;
-      for (int idx = tid; idx < KB * PER_ROW; idx += 256) {
-        const int s = idx / PER_ROW, cpos = (idx % PER_ROW) * E;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (s0 + s < Tn) raw = *reinterpret_cast<const uint4*>(kp + (size_t)(s0 + s) * kF + cpos);
-        *reinterpret_cast<uint4*>(Ks + s * KPITCH + cpos) = raw;
-      }
-      constexpr int TPT = kDV / E;
-      const int n0 = (tid % TPT) * E;
-      for (int s = tid / TPT; s < KB; s += 256 / TPT) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (s0 + s < Tn) raw = *reinterpret_cast<const uint4*>(vp + (size_t)(s0 + s) * kDV + n0);
-        const T* rv = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-        for (int j = 0; j < E; j++) Vt[(n0 + j) * VPITCH + s] = rv[j];
+    for (int p = 0; p < G::PIECES; p++) {
+      const int e = tid + 256 * p;
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      if (e < G::KPIECES) {
+        const int s = e / (NF / EL), c = (e % (NF / EL)) * EL;
+        if (s0 + s < Tn) raw = *reinterpret_cast<const uint4*>(kp + (size_t)(s0 + s) * kF + c);
+      } else if (e < G::KPIECES + G::VPIECES) {
+        const int e2 = e - G::KPIECES, s = e2 / (kDV / EL), c = (e2 % (kDV / EL)) * EL;
+        if (s0 + s < Tn) raw = *reinterpret_cast<const uint4*>(vp + (size_t)(s0 + s) * kDV + c);
+      }
+      pf[p] = raw;
+    }
+  };
+  auto stash = [&](int buf) {  // registers -> LDS buffer
+    T* Ks = reinterpret_cast<T*>(smem + buf * G::buf_bytes);
+    T* Vs = reinterpret_cast<T*>(smem + buf * G::buf_bytes + G::k_bytes);
+#pragma unroll
+    for (int p = 0; p < G::PIECES; p++) {
+      const int e = tid + 256 * p;
+      if (e < G::KPIECES) {
+        const int s = e / (NF / EL), c = (e % (NF / EL)) * EL;
+        *reinterpret_cast<uint4*>(Ks + s * KP + c) = pf[p];
+      } else if (e < G::KPIECES + G::VPIECES) {
+        const int e2 = e - G::KPIECES, s = e2 / (kDV / EL), c = (e2 % (kDV / EL)) * EL;
+        *reinterpret_cast<uint4*>(Vs + s * VP + c) = pf[p];
       }
     }
-    __syncthreads();
+  };
+
+  f32x16 num[MQ][2];
+  float rs[MQ];
+#pragma unroll
+  for (int mq = 0; mq < MQ; mq++) {
+    zero16(num[mq][0]);
+    zero16(num[mq][1]);
+    rs[mq] = 0.0f;
+  }
+  fetch(0);
+  stash(0);
+  if (nkb > 1) fetch(1);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb++) {
+    const int buf = kb & 1;
+    const T* Ks = reinterpret_cast<const T*>(smem + buf * G::buf_bytes);
+    const T* Vs = reinterpret_cast<const T*>(smem + buf * G::buf_bytes + G::k_bytes);
+    const int s0 = kb * KB;
     if (s0 <= my_last) {
+      // score tiles A^T[s][t] (rows = keys s0 + row, cols = queries), channel 0 folded in as + d
+      f32x16 at[MQ];
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) {
-        const int tq = row0 + 16 * mt;  // first row of this query tile
-        if (s0 > tq + 15) continue;
-        // score tiles transposed: D[sb] rows s = s0 + 16 sb + 4qd + i, cols t = tq + r
-        f32x4 d[4];
+      for (int mq = 0; mq < MQ; mq++)
 #pragma unroll
-        for (int sb = 0; sb < 4; sb++) {
-          d[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (s0 + 16 * sb > tq + 15) continue;
+        for (int i = 0; i < 16; i++) at[mq][i] = (float)kD;
+      const T* krow = Ks + n32 * KP + 8 * h;
 #pragma unroll
-          for (int j = 0; j < 12; j++) {
-            Frag A;
-            const T* pk = Ks + (16 * sb + r) * KPITCH + 32 * j + 8 * qd;
+      for (int j = 0; j < NJ; j++) {
+        Frag A;
+        if constexpr (sizeof(T) == 2) {
+          A = *reinterpret_cast<const Frag*>(krow + 16 * j);
+        } else {
 #pragma unroll
-            for (int i = 0; i < 8; i++) A[i] = pk[i];
-            mma(d[sb], A, QF[mt][j]);
-          }
-          // weight: (kappa / c)^p, masked s <= t
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int s = s0 + 16 * sb + 4 * qd + i;
-            float wv = d[sb][i] * inv_c;
-            if (P == 2) wv = wv * wv;
-            d[sb][i] = (s > tq + r) ? 0.0f : wv;
-          }
+          for (int i = 0; i < 8; i++) A[i] = krow[16 * j + i];
         }
 #pragma unroll
-        for (int m = 0; m < 2; m++) {
-          if (s0 + 32 * m > tq + 15) continue;
-          const Frag Pf = pack8v<T>(d[2 * m], d[2 * m + 1]);
+        for (int mq = 0; mq < MQ; mq++) mma32(at[mq], A, QF[mq][j]);
+      }
 #pragma unroll
-          for (int nt = 0; nt < 4; nt++) {
-            Frag B;
-            const T* pv = Vt + (16 * nt + r) * VPITCH + 32 * m + 4 * qd;
+      for (int mq = 0; mq < MQ; mq++) {
+        const int tq = row0 + 32 * mq + n32;  // this lane's query
+        float wv[16];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-              B[i] = pv[i];
-              B[4 + i] = pv[16 + i];
-            }
-            mma(num[mt][nt], Pf, B);
-          }
-          mma(num[mt][4], Pf, ONES);
+        for (int i = 0; i < 16; i++) {
+          const int s = s0 + 8 * (i >> 2) + 4 * h + (i & 3);
+          float x = at[mq][i] * inv_c;
+          if (P == 2) x = x * x;
+          wv[i] = (s > tq) ? 0.0f : x;
+        }
+        float lo[8], hi8[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          lo[i] = wv[i];
+          hi8[i] = wv[8 + i];
+        }
+        const Frag P0 = pack8f<T>(lo), P1 = pack8f<T>(hi8);
+        rs[mq] = frag_sum(P1, frag_sum(P0, rs[mq]));
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          mma32(num[mq][vt], lds_tokfrag(Vs, VP, 0, 32 * vt, l), P0);
+          mma32(num[mq][vt], lds_tokfrag(Vs, VP, 16, 32 * vt, l), P1);
         }
       }
+    }
+    if (kb + 1 < nkb) {
+      stash(buf ^ 1);  // the other buffer was last read before the previous barrier
+      if (kb + 2 < nkb) fetch(kb + 2);
     }
     __syncthreads();
   }
 
-  // o = num / (den + eps); the denominator sits in column 0 of tile 4 (lanes r == 0).
+  // ---- o = num / (den + eps): lane (query n32, half h) holds value rows 32 vt + 8 j + 4 h + i4
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) {
+  for (int mq = 0; mq < MQ; mq++) {
+    const int t = row0 + 32 * mq + n32;
+    const float den = xor32_sum(rs[mq]);
+    if (t < Tn) {
+      const float inv = 1.0f / (den + eps);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float den = __shfl(num[mt][4][i], l & 48);
-      const int t = row0 + 16 * mt + 4 * qd + i;
-      if (t < Tn) {
-        const float inv = 1.0f / (den + eps);
+      for (int vt = 0; vt < 2; vt++)
 #pragma unroll
-        for (int nt = 0; nt < 4; nt++) op[(size_t)t * kDV + 16 * nt + r] = from_f32<T>(num[mt][nt][i] * inv);
-      }
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; i4++)
+            op[(size_t)t * kDV + 32 * vt + 8 * j + 4 * h + i4] = from_f32<T>(num[mq][vt][4 * j + i4] * inv);
     }
   }
 }
+
+size_t rho_bytes(int T) { return (((size_t)T * kD * sizeof(float)) + 255) & ~(size_t)255; }
+
+template <typename T, int P>
+hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
+                         const MethodConsts& mc, void* out, void* ws, sanatan_dtype t, hipStream_t stream) {
+  float* rho = static_cast<float*>(ws);
+  void* phik = static_cast<char*>(ws) + rho_bytes(Tn);
+  hipError_t e = launch_phase_table(rho, Tn, pos0, mc.log2_base, stream);
+  if (e != hipSuccess) return e;
+  e = launch_featurize(k, t, B, H, Tn, pos0, mc, phik, t, stream);
+  if (e != hipSuccess) return e;
+  using G = QGeom<T>;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
+    e = hipFuncSetAttribute((const void*)quadratic_kernel<T, P>, hipFuncAttributeMaxDynamicSharedMemorySize, G::lds);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  const int nqb = (Tn + G::QROWS - 1) / G::QROWS;
+  const int BH = B * H;
+  hipLaunchKernelGGL((quadratic_kernel<T, P>), dim3(BH * nqb), dim3(256), G::lds, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(phik), static_cast<const T*>(v),
+                     static_cast<T*>(out), rho, mc.omega, mc.nph, H, Tn, BH, nqb, mc.kr, mc.inv_c, mc.eps);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t) {
   const size_t el = (t == SANATAN_BF16) ? 2 : 4;
-  return (size_t)B * H * T * kF * el;
-}
-
-template <typename T, int P>
-static hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
-                                const MethodConsts& mc, void* out, void* ws, sanatan_dtype t, hipStream_t stream) {
-  hipError_t e = launch_featurize(k, t, B, H, Tn, pos0, mc, ws, t, stream);
-  if (e != hipSuccess) return e;
-  using Gm = QuadGeom<T>;
-  const int nqb = (Tn + Gm::QROWS - 1) / Gm::QROWS;
-  const int BH = B * H;
-  e = hipFuncSetAttribute((const void*)quadratic_kernel<T, P>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)Gm::lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((quadratic_kernel<T, P>), dim3(BH * nqb), dim3(256), Gm::lds, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(ws), static_cast<const T*>(v),
-                     static_cast<T*>(out), mc.omega, mc.nph, H, Tn, BH, nqb, pos0, mc.log2_base, mc.kr, mc.inv_c,
-                     mc.eps);
-  return hipGetLastError();
+  return rho_bytes(T) + (size_t)B * H * T * kF * el;
 }
 
 hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,

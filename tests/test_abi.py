@@ -105,9 +105,11 @@ def test_workspace_sizes(L):
     assert L.sanatan_prefill_workspace_bytes(0, 1, 64, 64, ctypes.byref(p)) == 0
     assert L.sanatan_prefill_workspace_bytes(1, 1, 64, 0, ctypes.byref(p)) == 0
     assert L.sanatan_quadratic_workspace_bytes(1, 1, 0, 1, ctypes.byref(p)) == 0
-    # quadratic: Phi(K) in the element type, [B,H,T,384]
-    assert L.sanatan_quadratic_workspace_bytes(4, 12, 4096, rpg.SANATAN_BF16, ctypes.byref(p)) == 4 * 12 * 4096 * 384 * 2
-    assert L.sanatan_quadratic_workspace_bytes(1, 1, 256, rpg.SANATAN_F32, ctypes.byref(p)) == 256 * 384 * 4
+    # quadratic: phase table [T][64] fp32 (256-byte aligned), then Phi(K) in the element type, [B,H,T,384]
+    assert L.sanatan_quadratic_workspace_bytes(4, 12, 4096, rpg.SANATAN_BF16, ctypes.byref(p)) == \
+        4096 * 64 * 4 + 4 * 12 * 4096 * 384 * 2
+    assert L.sanatan_quadratic_workspace_bytes(1, 1, 255, rpg.SANATAN_F32, ctypes.byref(p)) == \
+        (255 * 64 * 4 + 255) // 256 * 256 + 255 * 384 * 4
     # prefill: phase table [T][64] fp32 (256-byte aligned) + one boundary state per (sequence + range - 1)
     ws = L.sanatan_prefill_workspace_bytes(8, 12, 2048, 64, ctypes.byref(p))
     state = L.sanatan_state_bytes(64, 64)
