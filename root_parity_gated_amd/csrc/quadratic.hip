@@ -6,13 +6,13 @@
 // and no running maximum is needed (unlike softmax): partial sums over key blocks just add.
 //
 // Phi(K) is featurized once into the workspace (element type of the call), after the position
-// phase table.  A workgroup is 4 waves (one per SIMD); each wave owns MQ tiles of 32 query rows
-// and featurizes them once into 32x32x16 MFMA operand registers (K-step j = 16 features).  Per
-// block of 32 keys, Phi(K) (channels 1..5: channel 0 is the constant 1 and contributes exactly
-// d = 64 to every score) and V are staged token-major in LDS, double-buffered, and every wave
-// forms its transposed score tiles A^T[s][t]; each Phi(K) fragment feeds MQ MFMAs.  The masked,
-// powered tile is the B operand of V^T P (V^T read with the transposing LDS load), and its row
-// sums (v_dot2) accumulate the denominator.
+// phase table.  A workgroup is 4 waves and two workgroups share a CU (two waves per SIMD hide each
+// other's latencies); each wave owns MQ tiles of 32 query rows and featurizes them once into
+// 32x32x16 MFMA operand registers (K-step j = 16 features).  Per block of 32 keys, Phi(K)
+// (channels 1..5: channel 0 is the constant 1 and contributes exactly d = 64 to every score) and
+// V are staged token-major in LDS, double-buffered, and every wave forms its transposed score
+// tiles A^T[s][t].  The masked, powered tile is the B operand of V^T P (V^T read with the
+// transposing LDS load), and its row sums (v_dot2) accumulate the denominator.
 #include "prefill_common.h"
 
 namespace sanatan {
@@ -20,7 +20,7 @@ namespace {
 
 template <typename T>
 struct QGeom {
-  static constexpr int MQ = sizeof(T) == 2 ? 2 : 1;  // 32-row query tiles per wave
+  static constexpr int MQ = 1;                        // 32-row query tiles per wave
   static constexpr int QROWS = 4 * 32 * MQ;          // query rows per workgroup
   static constexpr int KB = 32;                       // keys per block
   static constexpr int NF = kF - kD;                  // staged features: channels 1..5
@@ -37,10 +37,8 @@ struct QGeom {
   static constexpr int PIECES = (KPIECES + VPIECES + 255) / 256;  // per thread
 };
 
-template <typename T> struct U4 { typedef uint4 type; };
-
 template <typename T, int P>
-__global__ __launch_bounds__(256, 1) void quadratic_kernel(const T* __restrict__ q, const T* __restrict__ phik,
+__global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__ q, const T* __restrict__ phik,
                                                            const T* __restrict__ v, T* __restrict__ out,
                                                            const float* __restrict__ rho, const float* __restrict__ omega,
                                                            int nph, int H, int Tn, int BH, int nqb, float kr, float inv_c,
