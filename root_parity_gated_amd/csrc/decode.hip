@@ -7,8 +7,9 @@
 // One 512-thread workgroup owns one head-state and streams its S once: each thread holds 12
 // float4 row pieces (rows rg + 32m, columns 4cg..4cg+3), so each wave touches 4 KB-contiguous
 // slabs; the rank-1 update and the readout share one pass, and the readout uses the updated S.
-// The state is touched once per token, so its loads and stores are marked non-temporal (they
-// would only evict other data from the caches).
+// When the head-states together exceed what the last-level cache can keep between tokens, the
+// state is streamed with non-temporal loads and stores (caching it would only evict other data);
+// a smaller state (one sequence's 144 head-states: 14.4 MB) stays cache-resident between tokens.
 #include "launchers.h"
 #include "sanatan_device.h"
 
@@ -20,6 +21,7 @@ constexpr int kDecRows = kDecThreads / 16;  // row groups: 16 threads cover the 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 }  // namespace
 
+template <bool NT>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int64_t pos,
     const float* __restrict__ omega, int nph, double log2_base, float kr, float ceps, float* __restrict__ S,
@@ -41,7 +43,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   f32x4v rows[kF / kDecRows];
 #pragma unroll
   for (int m = 0; m < kF / kDecRows; m++)
-    rows[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(&Si[(rg + kDecRows * m) * kDV + 4 * cg]));
+    rows[m] = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(&Si[(rg + kDecRows * m) * kDV + 4 * cg]))
+                 : *reinterpret_cast<const f32x4v*>(&Si[(rg + kDecRows * m) * kDV + 4 * cg]);
   const float zr = tid < kF ? zi[tid] : 0.0f;
 
   if (tid < 2 * kD) {
@@ -72,7 +75,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     f32x4v s = rows[m];
 #pragma unroll
     for (int e = 0; e < 4; e++) s[e] = fmaf(a, vv[e], s[e]);
-    __builtin_nontemporal_store(s, reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]));
+    if (NT)
+      __builtin_nontemporal_store(s, reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]));
+    else
+      *reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]) = s;
 #pragma unroll
     for (int e = 0; e < 4; e++) acc[e] = fmaf(b, s[e], acc[e]);
   }
@@ -103,8 +109,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
                               const MethodConsts& mc, float* S, float* z, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_step_kernel, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, mc.omega, mc.nph,
-                     mc.log2_base, mc.kr, mc.ceps, S, z, out);
+  // states above 128 MB (half of the 256 MB last-level cache) are streamed
+  const bool stream_state = (size_t)N * kStateFloats * sizeof(float) > ((size_t)128 << 20);
+  if (stream_state)
+    hipLaunchKernelGGL(decode_step_kernel<true>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, mc.omega,
+                       mc.nph, mc.log2_base, mc.kr, mc.ceps, S, z, out);
+  else
+    hipLaunchKernelGGL(decode_step_kernel<false>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, mc.omega,
+                       mc.nph, mc.log2_base, mc.kr, mc.ceps, S, z, out);
   return hipGetLastError();
 }
 

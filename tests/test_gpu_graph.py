@@ -1,0 +1,100 @@
+"""Replays of captured HIP graphs give the eager results (bit for bit: the kernels are deterministic).
+
+The prefill (phase table, pass 1, pass 3) and a run of decode steps are captured once; each replay is
+separated by unrelated eager work and a synchronisation, and every replay is compared with the eager
+output of the same call.  bench.py times graph replays of the same calls.
+"""
+import numpy as np
+import pytest
+
+import sanatan_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import root_parity_gated_amd as rpg
+
+    rpg.lib()
+    return torch
+
+
+def test_prefill_graph_replays_match_eager(torch_dev):
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    B, H, T, C = 2, 4, 1000, 64  # 32 chunks over at most #CU workgroups: several pieces per sequence
+    q, k, v, om = si.attention_inputs(31, B, H, T, "bf16")
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
+    p = rpg.Params(omega=torch.from_numpy(om).cuda())
+    ws = torch.empty((rpg.sanatan_prefill_workspace_bytes(B, H, T, C, p),), dtype=torch.uint8, device="cuda")
+    S = torch.zeros((B, H, 384, 64), device="cuda")
+    z = torch.zeros((B, H, 384), device="cuda")
+    eager = torch.empty_like(vd)
+    rpg.sanatan_prefill_chunked(qd, kd, vd, C, p, out=eager, ws=ws, S=S, z=z)
+    S_eager, z_eager = S.clone(), z.clone()
+    torch.cuda.synchronize()
+
+    out = torch.empty_like(vd)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    S.zero_()
+    z.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        rpg.sanatan_prefill_chunked(qd, kd, vd, C, p, out=out, ws=ws, S=S, z=z)
+    other = torch.empty((B, H, T, 64), device="cuda", dtype=torch.bfloat16)
+    for rep in range(3):
+        S.zero_()
+        z.zero_()
+        out.fill_(float("nan"))
+        other.normal_()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        assert torch.equal(S, S_eager) and torch.equal(z, z_eager), rep
+
+
+def test_decode_graph_replays_match_eager(torch_dev):
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    nh, steps = 144, 4
+    om, (fq, fk, fv), (sq, sk, sv) = si.decode_inputs_numpy(57, nh, 8, steps)
+    dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    sq, sk, sv = map(dv, (sq, sk, sv))
+    p = rpg.Params(omega=dv(om))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    S0 = torch.randn((nh, 384, 64), device="cuda", generator=g) * 0.01
+    z0 = torch.rand((nh, 384), device="cuda", generator=g) + 1.0
+    S, z = S0.clone(), z0.clone()
+    eager = torch.empty((steps, nh, 64), device="cuda")
+    for i in range(steps):
+        rpg.sanatan_decode_step(sq[i], sk[i], sv[i], 4096 + i, p, S, z, eager[i])
+    S_eager, z_eager = S.clone(), z.clone()
+
+    out = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    S.copy_(S0)
+    z.copy_(z0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            rpg.sanatan_decode_step(sq[i], sk[i], sv[i], 4096 + i, p, S, z, out[i])
+    for rep in range(3):
+        S.copy_(S0)
+        z.copy_(z0)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        assert torch.equal(S, S_eager) and torch.equal(z, z_eager), rep
