@@ -40,46 +40,48 @@ struct GeomG {
   static constexpr int ks_bytes = CT * KP * 2;   // one wave's Phi(K) tile
   static constexpr int vs_bytes = CT * VP * 2;   // one V tile
   static constexpr int red_bytes = TB * 4 * 32 * RP * 4;
-  static constexpr int stage_bytes = kStateFloats * 4;
   // pass 3: [Phi(K) x 4 waves][V x 2 (shared, double-buffered)][reduction]; pass 1: [Phi(K) x 4][V x 4 (private)]
   static constexpr int vs_off = 4 * ks_bytes;
   static constexpr int red_off = vs_off + 2 * vs_bytes;
-  static constexpr int body(bool state_only) { return state_only ? vs_off + 4 * vs_bytes : red_off + red_bytes; }
-  static constexpr int main_bytes(bool state_only) {
-    return body(state_only) > stage_bytes ? body(state_only) : stage_bytes;
-  }
+  static constexpr int main_bytes(bool state_only) { return state_only ? vs_off + 4 * vs_bytes : red_off + red_bytes; }
   static constexpr int lds(bool state_only) { return main_bytes(state_only) + 4 * 96 * 4; }
 };
 
-// Staging layout of the state (floats): wave g's tile (ft, vt) occupies 16 x 64 consecutive floats in
-// accumulator order [register][lane]; z follows at kStageS, [g][16 c + dim].
-__device__ __forceinline__ int gstage_index(int row, int col) {
-  const int c = row >> 6, a = row & 63, g = a >> 4, d = a & 15;
-  const int r = 16 * (c & 1) + swz16(d), ft = c >> 1;
-  const int reg = 4 * (r >> 3) + (r & 3), hh = (r >> 2) & 1;
-  const int vt = col >> 5, n32 = col & 31;
-  return (((g * 3 + ft) * 2 + vt) * 16 + reg) * 64 + 32 * hh + n32;
+// The state slice of wave g lives in its accumulators: tile (ft, vt), register i = 8 m + j, lane (hh, n32)
+// holds S[128 ft + 64 m + 16 g + 8 hh + 4 (j / 4) + j % 4][32 vt + n32] (rows are channel-major features;
+// this is the accumulator layout with the dim bits 2 and 3 swapped).  For one register the 64 lanes
+// cover two 128-byte row segments, so the state moves between global memory and the accumulators with
+// plain coalesced loads and stores whose offsets are immediates.  z of the group is kept in LDS as
+// Zg[16 c + dim], dim = 0..15.
+__device__ __forceinline__ void gstate_add(f32x16 (&Sacc)[3][2], float* Zg, const float* __restrict__ s,
+                                           const float* __restrict__ zz, int g, int l) {
+  const float* base = s + (16 * g + 8 * (l >> 5)) * kDV + (l & 31);
+#pragma unroll
+  for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        const float* p = base + (128 * ft + 64 * m) * kDV + 32 * vt;
+#pragma unroll
+        for (int j = 0; j < 8; j++) Sacc[ft][vt][8 * m + j] += p[(4 * (j >> 2) + (j & 3)) * kDV];
+      }
+  for (int m = l; m < 96; m += 64) Zg[m] += zz[64 * (m >> 4) + 16 * g + (m & 15)];
 }
-__device__ __forceinline__ void gstage_in(float* st, const float* __restrict__ s, const float* __restrict__ zz) {
-  for (int e4 = threadIdx.x; e4 < kF * kDV / 4; e4 += 256) {
-    const float4 v = reinterpret_cast<const float4*>(s)[e4];
-    const int row = (4 * e4) / kDV, col = (4 * e4) % kDV;
-    *reinterpret_cast<float4*>(st + gstage_index(row, col)) = v;
-  }
-  for (int r = threadIdx.x; r < kF; r += 256) {
-    const int c = r >> 6, a = r & 63;
-    st[kStageS + (a >> 4) * 96 + 16 * c + (a & 15)] = zz[r];
-  }
-}
-__device__ __forceinline__ void gstage_out(const float* st, float* __restrict__ s, float* __restrict__ zz) {
-  for (int e4 = threadIdx.x; e4 < kF * kDV / 4; e4 += 256) {
-    const int row = (4 * e4) / kDV, col = (4 * e4) % kDV;
-    reinterpret_cast<float4*>(s)[e4] = *reinterpret_cast<const float4*>(st + gstage_index(row, col));
-  }
-  for (int r = threadIdx.x; r < kF; r += 256) {
-    const int c = r >> 6, a = r & 63;
-    zz[r] = st[kStageS + (a >> 4) * 96 + 16 * c + (a & 15)];
-  }
+__device__ __forceinline__ void gstate_store(const f32x16 (&Sacc)[3][2], const float* Zg, float* __restrict__ s,
+                                             float* __restrict__ zz, int g, int l) {
+  float* base = s + (16 * g + 8 * (l >> 5)) * kDV + (l & 31);
+#pragma unroll
+  for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        float* p = base + (128 * ft + 64 * m) * kDV + 32 * vt;
+#pragma unroll
+        for (int j = 0; j < 8; j++) p[(4 * (j >> 2) + (j & 3)) * kDV] = Sacc[ft][vt][8 * m + j];
+      }
+  for (int m = l; m < 96; m += 64) zz[64 * (m >> 4) + 16 * g + (m & 15)] = Zg[m];
 }
 
 // Transposed (token-consecutive) read of the Phi(K) tile for the state update: like lds_tokfrag, but
@@ -156,7 +158,6 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
   __bf16* KS = reinterpret_cast<__bf16*>(smem + grp * G::ks_bytes);
   __bf16* Vbase = reinterpret_cast<__bf16*>(smem + G::vs_off);
   float* red = reinterpret_cast<float*>(smem + G::red_off);
-  float* stage = reinterpret_cast<float*>(smem);
   float* Zg = reinterpret_cast<float*>(smem + G::main_bytes(STATE_ONLY)) + grp * 96;
   const int dbase = 16 * grp + 8 * h;
   const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
@@ -196,20 +197,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       for (int vt = 0; vt < 2; vt++) zero16(Sacc[ft][vt]);
     for (int m = l; m < 96; m += 64) Zg[m] = 0.0f;
     if (!STATE_ONLY) {
-      auto add_slot = [&](const float* s, const float* zz) {
-        __syncthreads();
-        gstage_in(stage, s, zz);
-        __syncthreads();
-#pragma unroll
-        for (int ft = 0; ft < 3; ft++)
-#pragma unroll
-          for (int vt = 0; vt < 2; vt++) {
-            const float* p = stage + ((grp * 3 + ft) * 2 + vt) * 16 * 64 + l;
-#pragma unroll
-            for (int i = 0; i < 16; i++) Sacc[ft][vt][i] += p[64 * i];
-          }
-        for (int m = l; m < 96; m += 64) Zg[m] += stage[kStageS + grp * 96 + m];
-      };
+      auto add_slot = [&](const float* s, const float* zz) { gstate_add(Sacc, Zg, s, zz, grp, l); };
       if (args.multi && args.scanned) {
         add_slot(slot, slot + kF * kDV);
       } else {
@@ -223,7 +211,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         }
       }
     }
-    __syncthreads();  // staging (aliasing the tiles) consumed; Zg initialised
+    __syncthreads();  // the previous piece's tiles are dead (Zg is private to the wave)
 
     // ---- raw inputs of one chunk: this lane's rows and phases, its pieces of V
     bf16x8 uk[TB], uq[TB];
@@ -589,21 +577,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
 
     float* dst_s = STATE_ONLY ? slot : (last_piece && args.S ? args.S + (size_t)bh * kF * kDV : nullptr);
     float* dst_z = STATE_ONLY ? slot + kF * kDV : (last_piece && args.S ? args.z + (size_t)bh * kF : nullptr);
-    __syncthreads();  // tiles and reduction buffer are dead; the staging area may be reused
-    if (dst_s) {
-#pragma unroll
-      for (int ft = 0; ft < 3; ft++)
-#pragma unroll
-        for (int vt = 0; vt < 2; vt++) {
-          float* p = stage + ((grp * 3 + ft) * 2 + vt) * 16 * 64 + l;
-#pragma unroll
-          for (int i = 0; i < 16; i++) p[64 * i] = Sacc[ft][vt][i];
-        }
-      for (int m = l; m < 96; m += 64) stage[kStageS + grp * 96 + m] = Zg[m];
-      __syncthreads();
-      gstage_out(stage, dst_s, dst_z);
-      __syncthreads();
-    }
+    if (dst_s) gstate_store(Sacc, Zg, dst_s, dst_z, grp, l);
   }
 }
 
