@@ -53,23 +53,26 @@ struct GeomG {
 // cover two 128-byte row segments, so the state moves between global memory and the accumulators with
 // plain coalesced loads and stores whose offsets are immediates.  z of the group is kept in LDS as
 // Zg[16 c + dim], dim = 0..15.
+// LOWREG keeps one tile's loads in flight at a time, for callers without registers to spare.
+template <bool LOWREG = false>
 __device__ __forceinline__ void gstate_add(f32x16 (&Sacc)[3][2], float* Zg, const float* __restrict__ s,
                                            const float* __restrict__ zz, int g, int l) {
   const float* base = s + (16 * g + 8 * (l >> 5)) * kDV + (l & 31);
 #pragma unroll
   for (int ft = 0; ft < 3; ft++)
 #pragma unroll
-    for (int vt = 0; vt < 2; vt++)
+    for (int vt = 0; vt < 2; vt++) {
 #pragma unroll
       for (int m = 0; m < 2; m++) {
         const float* p = base + (128 * ft + 64 * m) * kDV + 32 * vt;
 #pragma unroll
         for (int j = 0; j < 8; j++) Sacc[ft][vt][8 * m + j] += p[(4 * (j >> 2) + (j & 3)) * kDV];
       }
+      if (LOWREG) __builtin_amdgcn_sched_barrier(0);
+    }
   for (int m = l; m < 96; m += 64) Zg[m] += zz[64 * (m >> 4) + 16 * g + (m & 15)];
 }
-__device__ __forceinline__ void gstate_store(const f32x16 (&Sacc)[3][2], const float* Zg, float* __restrict__ s,
-                                             float* __restrict__ zz, int g, int l) {
+__device__ __forceinline__ void gstate_store_s(const f32x16 (&Sacc)[3][2], float* __restrict__ s, int g, int l) {
   float* base = s + (16 * g + 8 * (l >> 5)) * kDV + (l & 31);
 #pragma unroll
   for (int ft = 0; ft < 3; ft++)
@@ -81,6 +84,10 @@ __device__ __forceinline__ void gstate_store(const f32x16 (&Sacc)[3][2], const f
 #pragma unroll
         for (int j = 0; j < 8; j++) p[(4 * (j >> 2) + (j & 3)) * kDV] = Sacc[ft][vt][8 * m + j];
       }
+}
+__device__ __forceinline__ void gstate_store(const f32x16 (&Sacc)[3][2], const float* Zg, float* __restrict__ s,
+                                             float* __restrict__ zz, int g, int l) {
+  gstate_store_s(Sacc, s, g, l);
   for (int m = l; m < 96; m += 64) zz[64 * (m >> 4) + 16 * g + (m & 15)] = Zg[m];
 }
 
@@ -581,6 +588,242 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
   }
 }
 
+// Pass 1 for chunk 64 with the two 32-token halves of every chunk on different waves: wave 4 s + g
+// accumulates the feature-group-g increment of S and z over tokens 32 s .. 32 s + 31 of each chunk of
+// the piece, so that two waves share each SIMD.  Every wave's Phi(K) and V tiles are private, so the
+// chunk loop has no barrier; the two halves of a group meet at the end of the piece (the sum is over
+// tokens, so splitting it changes nothing but the rounding order).
+//
+// Per chunk j a wave reads all of its tile's MFMA operands into registers first, then overwrites the
+// tile with chunk j + 1 (featurized during the previous chunk), then runs the update MFMAs with the keys
+// of chunk j + 2 featurized in between.  A tile write and the next read of that tile are a whole chunk
+// apart, so neither waits on the other.
+struct GeomS8 {
+  static constexpr int CT = 32, KP = 104, VP = 72;
+  static constexpr int ks_bytes = CT * KP * 2;
+  static constexpr int vs_bytes = CT * VP * 2;
+  static constexpr int vs_off = 8 * ks_bytes;
+  // at the end of a piece the second-half waves pass their state slices to the first-half waves through
+  // a staging area that aliases the tiles: [group][register / 4][lane][4] floats, then z as [group][96]
+  static constexpr int stage_bytes = 4 * 96 * 64 * 4 + 4 * 96 * 4;
+  static constexpr int tiles_bytes = vs_off + 8 * vs_bytes;
+  static constexpr int lds = tiles_bytes > stage_bytes ? tiles_bytes : stage_bytes;
+};
+
+__global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArgs args) {
+  constexpr int CH = 64, KP = GeomS8::KP, VP = GeomS8::VP;
+  constexpr int NV = GeomS8::CT / 8;  // 16-byte pieces of the wave's V rows per lane
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, w = tid >> 6, grp = w & 3, half = w >> 2, l = tid & 63, h = l >> 5, n32 = l & 31;
+  __bf16* KS = reinterpret_cast<__bf16*>(smem + w * GeomS8::ks_bytes);
+  __bf16* Vs = reinterpret_cast<__bf16*>(smem + GeomS8::vs_off + w * GeomS8::vs_bytes);
+  const int dbase = 16 * grp + 8 * h;
+  const int toff = 32 * half;  // this wave's token offset inside a chunk
+  const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
+
+  const long long hi_c = range_lo(blockIdx.x + 1, args);
+  for (long long c = range_lo(blockIdx.x, args); c < hi_c;) {
+    const int bh = (int)(c / args.ncs);
+    const long long seq_c0 = (long long)bh * args.ncs;
+    const long long seq_end = seq_c0 + args.ncs;
+    const long long pend = hi_c < seq_end ? hi_c : seq_end;
+    const bool last_piece = (pend == seq_end);
+    const int t_begin = (int)(c - seq_c0) * CH;
+    const int t_end = min(args.T, (int)(pend - seq_c0) * CH);
+    c = pend;
+    if (last_piece) continue;  // the final piece's state comes out of pass 3
+    const int hh = bh % args.H;
+    const __bf16* __restrict__ kp = static_cast<const __bf16*>(args.k) + (size_t)bh * args.T * kD;
+    const __bf16* __restrict__ vp = static_cast<const __bf16*>(args.v) + (size_t)bh * args.T * kDV;
+    float* slot = args.ws_state + (size_t)(bh + blockIdx.x) * kStateFloats;
+
+    float om4[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) om4[i] = anchor_rev(args.omega[(size_t)(hh % args.nph) * kD + dbase + i]);
+
+    f32x16 Sacc[3][2];
+#pragma unroll
+    for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++) zero16(Sacc[ft][vt]);
+    // z of feature 32 ft + n32 of the group's tile order (both lane halves hold the same value)
+    float zacc[3] = {0.0f, 0.0f, 0.0f};
+
+    // raw inputs of one chunk (start t0; clamped to the sequence, so a chunk past the end re-reads the
+    // last one): this lane's key row and phases (token toff + n32), its pieces of the wave's V rows
+    auto next_t = [&](int t0) { return t0 + CH < t_end ? t0 + CH : t0; };
+    auto load_k = [&](int t0, bf16x8& u, float4 (&ph)[2]) {
+      const int tc = t0 + min(toff + n32, min(CH, t_end - t0) - 1);
+      u = *reinterpret_cast<const bf16x8*>(kp + (size_t)tc * kD + dbase);
+      const float* pr = args.rho + (size_t)tc * kD + dbase;
+      ph[0] = *reinterpret_cast<const float4*>(pr);
+      ph[1] = *reinterpret_cast<const float4*>(pr + 4);
+    };
+    auto load_v = [&](int t0, uint4 (&r)[NV]) {
+      const int nv = min(CH, t_end - t0);
+#pragma unroll
+      for (int j = 0; j < NV; j++) {
+        const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
+        r[j] = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + min(toff + row, nv - 1)) * kDV + col);
+      }
+    };
+    auto half_valid = [&](int t0) { return max(0, min(CH, t_end - t0) - toff); };
+    // the wave's rows of V and Phi(K) into its tiles; rows past the chunk's end are zero
+    // (a full half, the common case, takes the unmasked branch; nvh is the same on every lane)
+    auto write_v = [&](const uint4 (&r)[NV], int nvh) {
+      if (nvh >= 32) {
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+          const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
+          *reinterpret_cast<uint4*>(Vs + row * VP + col) = r[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+          const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
+          const unsigned m = 0u - (unsigned)(row < nvh);
+          *reinterpret_cast<uint4*>(Vs + row * VP + col) = make_uint4(r[j].x & m, r[j].y & m, r[j].z & m, r[j].w & m);
+        }
+      }
+    };
+    auto write_k = [&](const bf16x8 (&F)[5], int nvh) {
+      __bf16* row = KS + n32 * KP + 8 * h;
+      if (n32 < nvh) {
+        *reinterpret_cast<u32x4*>(row) = ones4;
+#pragma unroll
+        for (int cc = 1; cc < 6; cc++) *reinterpret_cast<bf16x8*>(row + 16 * cc) = F[cc - 1];
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < 6; cc++) *reinterpret_cast<u32x4*>(row + 16 * cc) = u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto pack = [&](const float (&cr)[8], const float (&sr)[8], const float (&rr)[8], bf16x8 (&F)[5]) {
+      u32x4 wv[5];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int a = 2 * q, b = 2 * q + 1;
+        wv[0][q] = pack_bf16x2(cr[a], cr[b]);
+        wv[1][q] = pack_bf16x2(sr[a], sr[b]);
+        wv[2][q] = pack_bf16x2(rr[a], rr[b]);
+        wv[3][q] = pack_bf16x2(rr[a] * cr[a], rr[b] * cr[b]);
+        wv[4][q] = pack_bf16x2(rr[a] * sr[a], rr[b] * sr[b]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 5; cc++) F[cc] = __builtin_bit_cast(bf16x8, wv[cc]);
+    };
+
+    // prologue: chunk 0 in the tiles, chunk 1 featurized (KF) with its V (rv) in registers, raw keys of
+    // chunk 2 (uk, rh) and V of chunk 2 (rvn) in flight
+    bf16x8 KF[5], uk;
+    float4 rh[2];
+    uint4 rv[NV];
+    const int t1 = next_t(t_begin);
+    {
+      load_v(t_begin, rv);
+      load_k(t_begin, uk, rh);
+      float cr[8], sr[8], rr[8];
+      feat8(uk, rh[0], rh[1], om4, args.kr, KF, cr, sr, rr);
+      const int nvh = half_valid(t_begin);
+      write_k(KF, nvh);
+      write_v(rv, nvh);
+      load_v(t1, rv);
+      load_k(t1, uk, rh);
+      feat8(uk, rh[0], rh[1], om4, args.kr, KF, cr, sr, rr);
+      load_k(next_t(t1), uk, rh);
+    }
+
+    for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+      const int ta = next_t(t0), tb = next_t(ta), tc = next_t(tb);  // chunks j + 1, j + 2, j + 3
+      // 1. every MFMA operand of chunk j out of the tiles
+      bf16x8 Af[2][3], Bf[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        Bf[ks][0] = lds_tokfrag(Vs, VP, 16 * ks, 0, l);
+        Bf[ks][1] = lds_tokfrag(Vs, VP, 16 * ks, 32, l);
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) Af[ks][ft] = lds_tokfrag_swz(KS, KP, 16 * ks, 32 * ft, l);
+      }
+      // 2. chunk j + 1 into the tiles (LDS serves the wave in order: the reads above see chunk j); past
+      //    the piece's end this rewrites chunk j, which nobody reads any more
+      {
+        const int nvh1 = ta != t0 ? half_valid(ta) : 0;
+        write_k(KF, nvh1);
+        write_v(rv, nvh1);
+      }
+      // 3. raw inputs further ahead: V of chunk j + 2, keys of chunk j + 3
+      uint4 rvn[NV];
+      load_v(tb, rvn);
+      bf16x8 uk2;
+      float4 rhn[2];
+      load_k(tc, uk2, rhn);
+      // 4. the update MFMAs of chunk j with the keys of chunk j + 2 featurized in between
+      float cr[8], sr[8], rr[8];
+      float zs[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) {
+          mma32(Sacc[ft][0], Af[ks][ft], Bf[ks][0]);
+          mma32(Sacc[ft][1], Af[ks][ft], Bf[ks][1]);
+          zs[ft] = frag_sum(Af[ks][ft], zs[ft]);
+        }
+#pragma unroll
+        for (int i = 4 * ks; i < 4 * ks + 4; i++) {
+          const float rho = i < 4 ? rh[0][i] : rh[1][i - 4];
+          featurize1((float)uk[i], rho, om4[i], args.kr, cr[i], sr[i], rr[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pack(cr, sr, rr, KF);
+#pragma unroll
+      for (int ft = 0; ft < 3; ft++) zacc[ft] += xor32_sum(zs[ft]);
+#pragma unroll
+      for (int j = 0; j < NV; j++) rv[j] = rvn[j];
+      uk = uk2;
+      rh[0] = rhn[0];
+      rh[1] = rhn[1];
+    }
+
+    // the two halves of each group meet: the second-half waves hand their slices over through LDS, the
+    // first-half waves add them to their own and store the sum in the slot
+    float4* stage = reinterpret_cast<float4*>(smem) + grp * 24 * 64 + l;
+    float* zstage = reinterpret_cast<float*>(smem + 4 * 96 * 64 * 4) + grp * 96;
+    __syncthreads();  // every wave is done with its tiles
+    if (half == 1) {
+#pragma unroll
+      for (int r4 = 0; r4 < 24; r4++) {
+        const int r = 4 * r4, ft = r >> 5, vt = (r >> 4) & 1, i = r & 15;
+        stage[64 * r4] = make_float4(Sacc[ft][vt][i], Sacc[ft][vt][i + 1], Sacc[ft][vt][i + 2], Sacc[ft][vt][i + 3]);
+      }
+      if (h == 0) {
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) zstage[32 * ft + n32] = zacc[ft];
+      }
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int r4 = 0; r4 < 24; r4++) {
+        const int r = 4 * r4, ft = r >> 5, vt = (r >> 4) & 1, i = r & 15;
+        const float4 o = stage[64 * r4];
+        Sacc[ft][vt][i] += o.x;
+        Sacc[ft][vt][i + 1] += o.y;
+        Sacc[ft][vt][i + 2] += o.z;
+        Sacc[ft][vt][i + 3] += o.w;
+      }
+      gstate_store_s(Sacc, slot, grp, l);
+      // feature 32 ft + n32 of the tile order is channel 2 ft + n32 / 16, dim 16 g + swz16(n32 % 16)
+      if (h == 0) {
+        float* zz = slot + kF * kDV;
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++)
+          zz[64 * (2 * ft + (n32 >> 4)) + 16 * grp + swz16(n32 & 15)] = zacc[ft] + zstage[32 * ft + n32];
+      }
+    }
+    __syncthreads();  // the staging area is free again before the next piece's tiles are written
+  }
+}
+
 template <int CH>
 hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   using G = GeomG<CH>;
@@ -595,10 +838,18 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
     e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             G::lds(false));
     if (e != hipSuccess) return e;
+    if constexpr (CH == 64) {
+      e = hipFuncSetAttribute((const void*)prefill_state8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GeomS8::lds);
+      if (e != hipSuccess) return e;
+    }
     attr_set[dev] = true;
   }
   if (a.multi) {
-    hipLaunchKernelGGL((prefill_grp_kernel<CH, true>), dim3(a.G), dim3(256), G::lds(true), stream, a);
+    if constexpr (CH == 64)
+      hipLaunchKernelGGL(prefill_state8_kernel, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_grp_kernel<CH, true>), dim3(a.G), dim3(256), G::lds(true), stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.scanned) {
