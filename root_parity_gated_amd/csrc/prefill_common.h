@@ -164,6 +164,14 @@ __device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
   return acc;
 }
+// acc + sum of the 8 products f[i] g[i] of two bf16 fragments (four v_dot2)
+__device__ __forceinline__ float frag_dot(const bf16x8& f, const bf16x8& g, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), __builtin_shufflevector(g, g, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), __builtin_shufflevector(g, g, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), __builtin_shufflevector(g, g, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), __builtin_shufflevector(g, g, 6, 7), acc, false);
+  return acc;
+}
 __device__ __forceinline__ float frag_sum(const f32x8& f, float acc) {
 #pragma unroll
   for (int i = 0; i < 8; i++) acc += f[i];

@@ -44,7 +44,8 @@ struct GeomG {
   static constexpr int vs_off = 4 * ks_bytes;
   static constexpr int red_off = vs_off + 2 * vs_bytes;
   static constexpr int main_bytes(bool state_only) { return state_only ? vs_off + 4 * vs_bytes : red_off + red_bytes; }
-  static constexpr int lds(bool state_only) { return main_bytes(state_only) + 4 * 96 * 4; }
+  // z per wave: fp32 [96], then (pass 3) a bf16 copy [96] for the readout's denominator
+  static constexpr int lds(bool state_only) { return main_bytes(state_only) + 4 * 96 * 4 + 4 * 96 * 2; }
 };
 
 // The state slice of wave g lives in its accumulators: tile (ft, vt), register i = 8 m + j, lane (hh, n32)
@@ -129,30 +130,6 @@ __device__ __forceinline__ void feat8(const bf16x8& u, const float4& rh0, const 
   for (int c = 0; c < 5; c++) F[c] = __builtin_bit_cast(bf16x8, w[c]);
 }
 
-// Phi(q) . z over this lane's 8 dims (features 16 c + 8h + i), z read from the wave's z vector;
-// per dim z0 + c z1 + s z2 + r (z3 + c z4 + s z5).
-__device__ __forceinline__ float dotz8(const float* zrow, const float (&cr)[8], const float (&sr)[8],
-                                       const float (&rr)[8]) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int i4 = 0; i4 < 2; i4++) {
-    float4 z[6];
-#pragma unroll
-    for (int c = 0; c < 6; c++) z[c] = *reinterpret_cast<const float4*>(zrow + 16 * c + 4 * i4);
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int i = 4 * i4 + e;
-      float t = fmaf(cr[i], z[4][e], z[3][e]);
-      t = fmaf(sr[i], z[5][e], t);
-      acc += z[0][e];
-      acc = fmaf(rr[i], t, acc);
-      acc = fmaf(cr[i], z[1][e], acc);
-      acc = fmaf(sr[i], z[2][e], acc);
-    }
-  }
-  return acc;
-}
-
 template <int CH, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs args) {
   using G = GeomG<CH>;
@@ -166,6 +143,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
   __bf16* Vbase = reinterpret_cast<__bf16*>(smem + G::vs_off);
   float* red = reinterpret_cast<float*>(smem + G::red_off);
   float* Zg = reinterpret_cast<float*>(smem + G::main_bytes(STATE_ONLY)) + grp * 96;
+  __bf16* Zb = reinterpret_cast<__bf16*>(smem + G::main_bytes(STATE_ONLY) + 4 * 96 * 4) + grp * 96;
   const int dbase = 16 * grp + 8 * h;
   const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
   const bf16x8 ONES = __builtin_bit_cast(bf16x8, ones4);
@@ -219,6 +197,8 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       }
     }
     __syncthreads();  // the previous piece's tiles are dead (Zg is private to the wave)
+    if (!STATE_ONLY)
+      for (int m = l; m < 96; m += 64) Zb[m] = (__bf16)Zg[m];
 
     // ---- raw inputs of one chunk: this lane's rows and phases, its pieces of V
     bf16x8 uk[TB], uq[TB];
@@ -297,7 +277,20 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
       for (int b = 0; b < TB; b++) {
         float cr[8], sr[8], rr[8];
         feat8(uq[b], rh[b][0], rh[b][1], om4, args.kr, QF[b], cr, sr, rr);
-        const float d = dotz8(Zg + 8 * h, cr, sr, rr);
+      }
+      // Phi(q) . z over the lane's 8 dims: channel 0 (the constant 1) in fp32, channels 1..5 as bf16
+      // products like the rest of the readout
+      const float4 z0a = *reinterpret_cast<const float4*>(Zg + 8 * h);
+      const float4 z0b = *reinterpret_cast<const float4*>(Zg + 8 * h + 4);
+      const float z0 = ((z0a.x + z0a.y) + (z0a.z + z0a.w)) + ((z0b.x + z0b.y) + (z0b.z + z0b.w));
+      bf16x8 zb[5];
+#pragma unroll
+      for (int cc = 0; cc < 5; cc++) zb[cc] = *reinterpret_cast<const bf16x8*>(Zb + 16 * (cc + 1) + 8 * h);
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        float d = z0;
+#pragma unroll
+        for (int cc = 0; cc < 5; cc++) d = frag_dot(QF[b][cc], zb[cc], d);
         dz[b] = xor32_sum(d);
       }
     };
@@ -472,9 +465,10 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
           rs[tb] = 0.0f;
 #pragma unroll
           for (int sb = 0; sb <= tb; sb++) {
+            // channel 0: sixteen products 1 * 1 in every entry, from one MFMA on the ones fragment
             f32x16 at;
-#pragma unroll
-            for (int i = 0; i < 16; i++) at[i] = 16.0f;  // channel 0: sixteen products 1 * 1
+            zero16(at);
+            mma32(at, ONES, ONES);
             const __bf16* krow = KS + (32 * sb + n32) * KP + 8 * h;
 #pragma unroll
             for (int cc = 0; cc < 5; cc++)
@@ -558,6 +552,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         float* zp = Zg + 32 * ft + 16 * (n32 >> 4) + swz16(n32 & 15);
         const float znew = *zp + zf;
         *zp = znew;  // both halves store the same value
+        if (!STATE_ONLY) Zb[zp - Zg] = (__bf16)znew;
       }
 
       // next chunk: queries (denominator part with the updated z), Phi(K) and V tiles, raw loads
