@@ -41,8 +41,8 @@ template <typename T, int P>
 __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__ q, const T* __restrict__ phik,
                                                            const T* __restrict__ v, T* __restrict__ out,
                                                            const float* __restrict__ rho, const float* __restrict__ omega,
-                                                           int nph, int H, int Tn, int BH, int nqb, float kr, float inv_c,
-                                                           float eps) {
+                                                           int nph, int H, int Tn, int BH, int nqb, float kr,
+                                                           float eps_cp) {
   using G = QGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
@@ -86,41 +86,45 @@ __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__
     }
   }
 
-  // ---- key blocks: staged Phi(K) (channels 1..5) and V, double-buffered
+  // ---- key blocks: staged Phi(K) (channels 1..5) and V, double-buffered.  A block is KB rows of NF
+  // features and KB rows of d_v values: exactly KPT + VPT 16-byte pieces per thread, whose offsets do
+  // not depend on the block.
+  constexpr int KPT = G::KPIECES / 256, VPT = G::VPIECES / 256;
+  static_assert(KPT * 256 == G::KPIECES && VPT * 256 == G::VPIECES, "pieces must divide evenly");
   const int last_row = min(Tn - 1, qb * G::QROWS + G::QROWS - 1);
   const int nkb = last_row / KB + 1;
   const int my_last = min(Tn - 1, row0 + 32 * MQ - 1);
-  uint4 pf[G::PIECES];
-  auto fetch = [&](int kb) {  // this thread's 16-byte pieces of key block kb -> registers
+  uint4 pf[KPT + VPT];
+  auto krow_of = [&](int p) { return (tid + 256 * p) / (NF / EL); };
+  auto kcol_of = [&](int p) { return ((tid + 256 * p) % (NF / EL)) * EL; };
+  auto vrow_of = [&](int p) { return (tid + 256 * p) / (kDV / EL); };
+  auto vcol_of = [&](int p) { return ((tid + 256 * p) % (kDV / EL)) * EL; };
+  auto fetch = [&](int kb) {  // this thread's pieces of key block kb -> registers (rows past Tn: zero)
     const int s0 = kb * KB;
+    const bool full = s0 + KB <= Tn;
 #pragma unroll
-    for (int p = 0; p < G::PIECES; p++) {
-      const int e = tid + 256 * p;
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (e < G::KPIECES) {
-        const int s = e / (NF / EL), c = (e % (NF / EL)) * EL;
-        if (s0 + s < Tn) raw = *reinterpret_cast<const uint4*>(kp + (size_t)(s0 + s) * kF + c);
-      } else if (e < G::KPIECES + G::VPIECES) {
-        const int e2 = e - G::KPIECES, s = e2 / (kDV / EL), c = (e2 % (kDV / EL)) * EL;
-        if (s0 + s < Tn) raw = *reinterpret_cast<const uint4*>(vp + (size_t)(s0 + s) * kDV + c);
-      }
-      pf[p] = raw;
+    for (int p = 0; p < KPT; p++) {
+      const int s = krow_of(p);
+      pf[p] = (full || s0 + s < Tn) ? *reinterpret_cast<const uint4*>(kp + (size_t)(s0 + s) * kF + kcol_of(p))
+                                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int p = 0; p < VPT; p++) {
+      const int s = vrow_of(p);
+      pf[KPT + p] = (full || s0 + s < Tn)
+                        ? *reinterpret_cast<const uint4*>(vp + (size_t)(s0 + s) * kDV + vcol_of(p))
+                        : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto stash = [&](int buf) {  // registers -> LDS buffer
     T* Ks = reinterpret_cast<T*>(smem + buf * G::buf_bytes);
     T* Vs = reinterpret_cast<T*>(smem + buf * G::buf_bytes + G::k_bytes);
 #pragma unroll
-    for (int p = 0; p < G::PIECES; p++) {
-      const int e = tid + 256 * p;
-      if (e < G::KPIECES) {
-        const int s = e / (NF / EL), c = (e % (NF / EL)) * EL;
-        *reinterpret_cast<uint4*>(Ks + s * KP + c) = pf[p];
-      } else if (e < G::KPIECES + G::VPIECES) {
-        const int e2 = e - G::KPIECES, s = e2 / (kDV / EL), c = (e2 % (kDV / EL)) * EL;
-        *reinterpret_cast<uint4*>(Vs + s * VP + c) = pf[p];
-      }
-    }
+    for (int p = 0; p < KPT; p++)
+      *reinterpret_cast<uint4*>(__builtin_assume_aligned(Ks + krow_of(p) * KP + kcol_of(p), 16)) = pf[p];
+#pragma unroll
+    for (int p = 0; p < VPT; p++)
+      *reinterpret_cast<uint4*>(__builtin_assume_aligned(Vs + vrow_of(p) * VP + vcol_of(p), 16)) = pf[KPT + p];
   };
 
   f32x16 num[MQ][2];
@@ -141,12 +145,24 @@ __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__
     const T* Vs = reinterpret_cast<const T*>(smem + buf * G::buf_bytes + G::k_bytes);
     const int s0 = kb * KB;
     if (s0 <= my_last) {
-      // score tiles A^T[s][t] (rows = keys s0 + row, cols = queries), channel 0 folded in as + d
+      // score tiles A^T[s][t] (rows = keys s0 + row, cols = queries); channel 0 (d products 1 * 1)
+      // comes in as 16 products 1 * 4 from one MFMA (bf16) or as the initial value (fp32)
       f32x16 at[MQ];
 #pragma unroll
-      for (int mq = 0; mq < MQ; mq++)
+      for (int mq = 0; mq < MQ; mq++) {
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                               (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+          const bf16x8 fours = {(__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f,
+                                (__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f};
+          static_assert(kD == 64, "channel 0 folded as 16 x 4");
+          zero16(at[mq]);
+          mma32(at[mq], ones, fours);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 16; i++) at[mq][i] = (float)kD;
+          for (int i = 0; i < 16; i++) at[mq][i] = (float)kD;
+        }
+      }
       const T* krow = Ks + n32 * KP + 8 * h;
 #pragma unroll
       for (int j = 0; j < NJ; j++) {
@@ -160,16 +176,21 @@ __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__
 #pragma unroll
         for (int mq = 0; mq < MQ; mq++) mma32(at[mq], A, QF[mq][j]);
       }
+      // the block reaches past a query of the wave only near the diagonal: mask there alone
+      const bool diag = s0 + KB - 1 > row0;
 #pragma unroll
       for (int mq = 0; mq < MQ; mq++) {
         const int tq = row0 + 32 * mq + n32;  // this lane's query
+        // weight kappa^p; the 1 / c^p of the pages' weights cancels against the scaled epsilon below
         float wv[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int s = s0 + 8 * (i >> 2) + 4 * h + (i & 3);
-          float x = at[mq][i] * inv_c;
-          if (P == 2) x = x * x;
-          wv[i] = (s > tq) ? 0.0f : x;
+        for (int i = 0; i < 16; i++) wv[i] = P == 2 ? at[mq][i] * at[mq][i] : at[mq][i];
+        if (diag) {
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const int s = s0 + 8 * (i >> 2) + 4 * h + (i & 3);
+            wv[i] = (s > tq) ? 0.0f : wv[i];
+          }
         }
         float lo[8], hi8[8];
 #pragma unroll
@@ -199,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__
     const int t = row0 + 32 * mq + n32;
     const float den = xor32_sum(rs[mq]);
     if (t < Tn) {
-      const float inv = 1.0f / (den + eps);
+      // weights are kappa^p here, so epsilon is scaled by c^p: o = sum w v / (sum w + eps c^p)
+      const float inv = 1.0f / (den + eps_cp);
 #pragma unroll
       for (int vt = 0; vt < 2; vt++)
 #pragma unroll
@@ -235,7 +257,8 @@ hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int
   const int BH = B * H;
   hipLaunchKernelGGL((quadratic_kernel<T, P>), dim3(BH * nqb), dim3(256), G::lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(phik), static_cast<const T*>(v),
-                     static_cast<T*>(out), rho, mc.omega, mc.nph, H, Tn, BH, nqb, mc.kr, mc.inv_c, mc.eps);
+                     static_cast<T*>(out), rho, mc.omega, mc.nph, H, Tn, BH, nqb, mc.kr,
+                     P == 2 ? (float)((double)mc.ceps / (double)mc.inv_c) : mc.ceps);
   return hipGetLastError();
 }
 
