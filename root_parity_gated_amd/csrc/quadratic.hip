@@ -164,8 +164,7 @@ __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__
         }
       }
       const T* krow = Ks + n32 * KP + 8 * h;
-#pragma unroll
-      for (int j = 0; j < NJ; j++) {
+      auto ldA = [&](int j) {
         Frag A;
         if constexpr (sizeof(T) == 2) {
           A = *reinterpret_cast<const Frag*>(krow + 16 * j);
@@ -173,8 +172,21 @@ __global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__
 #pragma unroll
           for (int i = 0; i < 8; i++) A[i] = krow[16 * j + i];
         }
+        return A;
+      };
+      // Phi(K) fragments are read PD K-steps ahead of their MFMA, so LDS latency stays hidden
+      constexpr int PD = 6;
+      Frag Ar[PD];
+#pragma unroll
+      for (int j = 0; j < PD; j++) Ar[j] = ldA(j);
+      __builtin_amdgcn_sched_barrier(0);  // (fences keep the compiler from shortening the distance)
+#pragma unroll
+      for (int j = 0; j < NJ; j++) {
+        const Frag A = Ar[j % PD];
 #pragma unroll
         for (int mq = 0; mq < MQ; mq++) mma32(at[mq], A, QF[mq][j]);
+        if (j + PD < NJ) Ar[j % PD] = ldA(j + PD);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // the block reaches past a query of the wave only near the diagonal: mask there alone
       const bool diag = s0 + KB - 1 > row0;
