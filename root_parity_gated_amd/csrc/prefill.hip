@@ -384,12 +384,17 @@ static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t st
   using G = Geom4<T, CH>;
   static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
   if (a.multi) {
-    const size_t lds1 = G::lds(true);
-    hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill4_kernel<T, CH, true>), dim3(a.G), dim3(256), lds1, stream, a);
-    e = hipGetLastError();
+    hipError_t e;
+    if constexpr (CH == 128 && sizeof(T) == 2) {
+      e = launch_prefill_state8_128(a, stream);  // two waves per SIMD, one per half of each 64 tokens
+    } else {
+      const size_t lds1 = G::lds(true);
+      e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((prefill4_kernel<T, CH, true>), dim3(a.G), dim3(256), lds1, stream, a);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     if (a.scanned) {
       hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);

@@ -605,8 +605,12 @@ struct GeomS8 {
   static constexpr int lds = tiles_bytes > stage_bytes ? tiles_bytes : stage_bytes;
 };
 
+// PCH is the chunk of the call (64 or 128), which fixes the pieces; the increment over a piece does
+// not depend on the chunking, so the loop always steps 64 tokens.
+template <int PCH>
 __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArgs args) {
   constexpr int CH = 64, KP = GeomS8::KP, VP = GeomS8::VP;
+  static_assert(PCH % CH == 0, "pieces are whole 64-token steps");
   constexpr int NV = GeomS8::CT / 8;  // 16-byte pieces of the wave's V rows per lane
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, w = tid >> 6, grp = w & 3, half = w >> 2, l = tid & 63, h = l >> 5, n32 = l & 31;
@@ -623,8 +627,8 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
     const long long seq_end = seq_c0 + args.ncs;
     const long long pend = hi_c < seq_end ? hi_c : seq_end;
     const bool last_piece = (pend == seq_end);
-    const int t_begin = (int)(c - seq_c0) * CH;
-    const int t_end = min(args.T, (int)(pend - seq_c0) * CH);
+    const int t_begin = (int)(c - seq_c0) * PCH;
+    const int t_end = min(args.T, (int)(pend - seq_c0) * PCH);
     c = pend;
     if (last_piece) continue;  // the final piece's state comes out of pass 3
     const int hh = bh % args.H;
@@ -834,7 +838,7 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
                             G::lds(false));
     if (e != hipSuccess) return e;
     if constexpr (CH == 64) {
-      e = hipFuncSetAttribute((const void*)prefill_state8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      e = hipFuncSetAttribute((const void*)prefill_state8_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               GeomS8::lds);
       if (e != hipSuccess) return e;
     }
@@ -842,7 +846,7 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   }
   if (a.multi) {
     if constexpr (CH == 64)
-      hipLaunchKernelGGL(prefill_state8_kernel, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
+      hipLaunchKernelGGL(prefill_state8_kernel<64>, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
     else
       hipLaunchKernelGGL((prefill_grp_kernel<CH, true>), dim3(a.G), dim3(256), G::lds(true), stream, a);
     hipError_t e = hipGetLastError();
@@ -857,6 +861,20 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_state8_128(const PrefillArgs& a, hipStream_t stream) {
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
+    const hipError_t e = hipFuncSetAttribute((const void*)prefill_state8_kernel<128>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, GeomS8::lds);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(prefill_state8_kernel<128>, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream) {
   switch (chunk) {
