@@ -1,0 +1,158 @@
+"""Edge cases of the HIP path against the fp64 oracle: sequences shorter than one chunk (down to a single
+token), the method's degenerate parameters (gamma = 0, hard roots, eps = 0 with constant values), inputs
+far outside N(0,1) (huge, tiny and zero components), one head-state in decode and one-token quadratic forms.
+
+Tolerances are the parity bars of the other GPU tests: row-wise max relative error <= 1e-4 for fp32 inputs,
+<= 2e-2 for bf16 inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sanatan_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import root_parity_gated_amd as rpg
+
+    rpg.lib()
+    return torch
+
+
+def dev(torch, x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def params(torch, omega, **kw):
+    import root_parity_gated_amd as rpg
+
+    return rpg.Params(omega=torch.from_numpy(np.ascontiguousarray(omega, dtype=np.float32)).cuda(), **kw)
+
+
+def row_rel_err(got, want):
+    got = np.asarray(got, np.float64).reshape(-1, want.shape[-1])
+    want = np.asarray(want, np.float64).reshape(-1, want.shape[-1])
+    return float((np.abs(got - want).max(1) / np.maximum(np.abs(want).max(1), 1e-12)).max())
+
+
+def oracle_heads(q, k, v, omega, pos0=0, **kw):
+    B, H, T, d = q.shape
+    out, S, z = oracle.recurrent_heads(q.reshape(B * H, T, d), k.reshape(B * H, T, d), v.reshape(B * H, T, -1),
+                                       np.tile(omega, (B, 1)), pos0=pos0, **kw)
+    return out.reshape(B, H, T, -1), S.reshape(B, H, *S.shape[1:]), z.reshape(B, H, -1)
+
+
+@pytest.mark.parametrize("dtype,chunk", [("f32", 16), ("f32", 64), ("bf16", 16), ("bf16", 32), ("bf16", 64),
+                                         ("bf16", 128)])
+@pytest.mark.parametrize("T", [1, 5, 63, 65])
+def test_prefill_short_sequences(torch_dev, dtype, chunk, T):
+    """Sequences of 1..65 tokens (a single ragged chunk, or a full chunk plus one token), with the final state."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    B, H = 2, 3
+    q, k, v, om = si.attention_inputs(300 + T, B, H, T, dtype)
+    S = torch.zeros((B, H, 384, 64), device="cuda")
+    z = torch.zeros((B, H, 384), device="cuda")
+    out = rpg.sanatan_prefill_chunked(dev(torch, q, dtype), dev(torch, k, dtype), dev(torch, v, dtype), chunk,
+                                      params(torch, om), pos0=7, S=S, z=z)
+    torch.cuda.synchronize()
+    want, Sw, zw = oracle_heads(q, k, v, om, pos0=7)
+    assert row_rel_err(host(out), want) <= TOL[dtype]
+    assert np.abs(host(S) - Sw).max() <= TOL[dtype] * np.abs(Sw).max()
+    assert np.abs(host(z) - zw).max() <= TOL[dtype] * np.abs(zw).max()
+
+
+@pytest.mark.parametrize("case", ["gamma0", "hard_roots", "eps0_constant_v"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_degenerate_parameters(torch_dev, case, dtype):
+    """gamma = 0 makes every root label 0 (three-channel kernel); a huge gamma saturates tanh to the sign
+    (hard roots, gate in {0, 2}); eps = 0 with constant values returns the values exactly up to rounding."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    B, H, T = 1, 2, 150
+    q, k, v, om = si.attention_inputs(410, B, H, T, dtype)
+    kw = {"gamma0": {"gamma": 0.0}, "hard_roots": {"gamma": 1000.0}, "eps0_constant_v": {"eps": 0.0}}[case]
+    if case == "eps0_constant_v":
+        v = np.broadcast_to(np.arange(64, dtype=np.float32) / 16 - 2, v.shape).copy()  # bf16-exact values
+    out = rpg.sanatan_prefill_chunked(dev(torch, q, dtype), dev(torch, k, dtype), dev(torch, v, dtype), 64,
+                                      params(torch, om, **kw))
+    torch.cuda.synchronize()
+    want, _, _ = oracle_heads(q, k, v, om, **kw)
+    assert row_rel_err(host(out), want) <= TOL[dtype]
+    if case == "eps0_constant_v":
+        # every output row is the constant value row (bf16 outputs round it)
+        assert np.abs(host(out) - v.astype(np.float64)).max() <= (1e-5 if dtype == "f32" else 1e-2)
+
+
+def test_prefill_extreme_inputs(torch_dev):
+    """Components far outside N(0,1): |u| up to 1e4 (theta near +-pi), 1e-30 and exact zeros (theta = 0)."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    B, H, T = 1, 2, 130
+    q, k, v, om = si.attention_inputs(420, B, H, T, "f32")
+    rng = np.random.default_rng(421)
+    scale = rng.choice(np.array([1e4, 1.0, 1e-30, 0.0], dtype=np.float32), size=q.shape)
+    q = (q * scale).astype(np.float32)
+    k = (k * rng.choice(np.array([1e4, 1.0, 1e-30, 0.0], dtype=np.float32), size=k.shape)).astype(np.float32)
+    out = rpg.sanatan_prefill_chunked(dev(torch, q, "f32"), dev(torch, k, "f32"), dev(torch, v, "f32"), 32,
+                                      params(torch, om))
+    torch.cuda.synchronize()
+    want, _, _ = oracle_heads(q, k, v, om)
+    assert row_rel_err(host(out), want) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("N", [1, 7])
+def test_decode_few_head_states(torch_dev, N):
+    """One and seven head-states (a single workgroup, and an odd count), eight steps from an empty state."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    steps = 8
+    om, _, (sq, sk, sv) = si.decode_inputs_numpy(430 + N, N, 1, steps)
+    p = params(torch, om)
+    S = torch.zeros((N, 384, 64), device="cuda")
+    z = torch.zeros((N, 384), device="cuda")
+    outs = [rpg.sanatan_decode_step(dev(torch, sq[i], "f32"), dev(torch, sk[i], "f32"), dev(torch, sv[i], "f32"),
+                                    5 + i, p, S, z).clone() for i in range(steps)]
+    torch.cuda.synchronize()
+    got = np.stack([host(o) for o in outs], 1)
+    want, Sw, zw = oracle.recurrent_heads(sq.transpose(1, 0, 2), sk.transpose(1, 0, 2), sv.transpose(1, 0, 2), om,
+                                          pos0=5)
+    assert row_rel_err(got, want) <= TOL["f32"]
+    assert np.abs(host(S) - Sw).max() <= 1e-4 * max(1.0, np.abs(Sw).max())
+
+
+@pytest.mark.parametrize("dtype,p", [("f32", 2), ("bf16", 2), ("bf16", 1)])
+@pytest.mark.parametrize("T", [1, 33])
+def test_quadratic_short_sequences(torch_dev, dtype, p, T):
+    """The masked quadratic form on one token (o_0 = v_0 w / (w + eps)) and on one key block plus one."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    B, H = 2, 2
+    q, k, v, om = si.attention_inputs(440 + T, B, H, T, dtype)
+    out = rpg.sanatan_quadratic_ref_p2(dev(torch, q, dtype), dev(torch, k, dtype), dev(torch, v, dtype), p,
+                                       params(torch, om))
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        for h in range(H):
+            want = oracle.attention_direct(q[b, h], k[b, h], v[b, h], om[h], p=p)
+            assert row_rel_err(got[b, h], want) <= TOL[dtype]
