@@ -244,6 +244,13 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup):
         print(f"# decode graph capture skipped: {ex}", file=sys.stderr)
     bytes_step = N * (2 * STATE_BYTES + 3 * D * 4 + DV * 4)
     best_ms = min(ms, g_ms) if g_ms else ms
+    # reference for what an in-place read-and-write-back stream of the same state bytes reaches on this
+    # device: torch's vectorized in-place add over the state tensor (one read and one write per element)
+    ref_tbs = None
+    if batch > 1:
+        flat = S.view(-1)
+        ref_ms = timed_loop(torch, lambda: flat.add_(0.0), 10, 2)
+        ref_tbs = 2 * flat.numel() * 4 / (ref_ms * 1e-3) / 1e12
     return {
         "batch": batch, "head_states": N, "steps": steps_timed,
         "us_per_step_eager": ms * 1e3, "us_per_step_graph": (g_ms * 1e3) if g_ms else None,
@@ -253,6 +260,7 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup):
                      "unit": "GB/s", "frac": bytes_step / (best_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "note": ("state (14.4 MB) is resident in the 256 MB Infinity Cache between steps" if batch == 1
                  else "state exceeds the Infinity Cache; HBM-bound"),
+        "rmw_stream_reference_TBps": ref_tbs,
     }
 
 
