@@ -156,3 +156,25 @@ def test_quadratic_short_sequences(torch_dev, dtype, p, T):
         for h in range(H):
             want = oracle.attention_direct(q[b, h], k[b, h], v[b, h], om[h], p=p)
             assert row_rel_err(got[b, h], want) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("wgs", [5, 13, 23, 30, 59])
+def test_prefill_many_partitions(torch_dev, monkeypatch, wgs):
+    """bf16 chunk 64 with the workgroup count forced: ranges of many lengths and 2..8 pieces per sequence,
+    so both the fused predecessor sums and the scan kernel run.  Output and final state against the
+    oracle."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    monkeypatch.setenv("SANATAN_PREFILL_WGS", str(wgs))
+    B, H, T = 2, 3, 2048 - 29
+    q, k, v, om = si.attention_inputs(450 + wgs, B, H, T, "bf16")
+    S = torch.zeros((B, H, 384, 64), device="cuda")
+    z = torch.zeros((B, H, 384), device="cuda")
+    out = rpg.sanatan_prefill_chunked(dev(torch, q, "bf16"), dev(torch, k, "bf16"), dev(torch, v, "bf16"), 64,
+                                      params(torch, om), S=S, z=z)
+    torch.cuda.synchronize()
+    want, Sw, zw = oracle_heads(q, k, v, om)
+    assert row_rel_err(host(out), want) <= TOL["bf16"]
+    assert np.abs(host(S) - Sw).max() <= TOL["bf16"] * np.abs(Sw).max()
+    assert np.abs(host(z) - zw).max() <= TOL["bf16"] * np.abs(zw).max()
