@@ -125,29 +125,54 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
       __syncthreads();  // the staging area is reused by the tiles
     }
 
+    // Raw K, Q and V rows of a chunk are loaded into registers one chunk ahead of their use (each set is
+    // refilled as soon as it is consumed), so the global-load latency is not exposed at the chunk start.
+    constexpr int EPL = 16 / G::ES, PER_TOK = kDV / EPL;
+    constexpr int NVP = (CT * PER_TOK + 255) / 256;  // 16-byte pieces of V per thread
+    Raw8<T> rk[TB], rq[TB];
+    uint4 rv[NVP];
+    auto fetch_kv = [&](int tc0) {
+      const int nv = min(CH, t_end - tc0);
+#pragma unroll
+      for (int j = 0; j < NVP; j++) {
+        const int idx = tid + 256 * j, s = idx / PER_TOK, col = (idx % PER_TOK) * EPL;
+        if (idx < CT * PER_TOK) rv[j] = *reinterpret_cast<const uint4*>(vp + (size_t)(tc0 + min(s, nv - 1)) * kDV + col);
+      }
+#pragma unroll
+      for (int sb = 0; sb < TB; sb++) load_raw8(kp + (size_t)(tc0 + min(32 * sb + n32, nv - 1)) * kD + dbase, rk[sb]);
+    };
+    auto fetch_q = [&](int tc0, int tb) {
+      const int nv = min(CH, t_end - tc0);
+      load_raw8(qp + (size_t)(tc0 + min(32 * tb + n32, nv - 1)) * kD + dbase, rq[tb]);
+    };
+    fetch_kv(t_begin);
+    if (!STATE_ONLY) {
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) fetch_q(t_begin, tb);
+    }
+
     for (int t0 = t_begin; t0 < t_end; t0 += CH) {
       const int nvalid = min(CH, t_end - t0);
+      const int tn = t0 + CH < t_end ? t0 + CH : t0;  // the next chunk (or this one again at the end)
 
       // (a) V tile -> LDS (token-major), zero beyond nvalid (loads clamped in bounds).
-      {
-        constexpr int EPL = 16 / G::ES;
-        constexpr int PER_TOK = kDV / EPL;
 #pragma unroll
-        for (int idx = tid; idx < CT * PER_TOK; idx += 256) {
-          const int s = idx / PER_TOK, col = (idx % PER_TOK) * EPL;
-          const int sc = min(s, nvalid - 1);
-          uint4 raw = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + sc) * kDV + col);
-          if (s >= nvalid) raw = make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(Vs + s * VP + col) = raw;
-        }
+      for (int j = 0; j < NVP; j++) {
+        const int idx = tid + 256 * j, s = idx / PER_TOK, col = (idx % PER_TOK) * EPL;
+        if (idx < CT * PER_TOK)
+          *reinterpret_cast<uint4*>(Vs + s * VP + col) = s < nvalid ? rv[j] : make_uint4(0u, 0u, 0u, 0u);
       }
       // (b) Phi(K) of the chunk -> this wave's token-major LDS tile (zero rows beyond nvalid)
+      float ku[TB][8];
+#pragma unroll
+      for (int sb = 0; sb < TB; sb++) unpack8(rk[sb], ku[sb]);
+      fetch_kv(tn);
 #pragma unroll
       for (int sb = 0; sb < TB; sb++) {
         const int sl = 32 * sb + n32;
         const int sc = t0 + min(sl, nvalid - 1);
-        float u[8], rh[8];
-        load8(kp + (size_t)sc * kD + dbase, u);
+        float rh[8];
+        const float (&u)[8] = ku[sb];
         load8(args.rho + (size_t)sc * kD + dbase, rh);
         float ch[6][8];
         featurize8(u, rh, om4, args.kr, ch);
@@ -182,7 +207,8 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
           const int tl = 32 * tb + n32;
           const int tc = t0 + min(tl, nvalid - 1);
           float u[8], rh[8];
-          load8(qp + (size_t)tc * kD + dbase, u);
+          unpack8(rq[tb], u);
+          fetch_q(tn, tb);
           load8(args.rho + (size_t)tc * kD + dbase, rh);
           float ch[6][8];
           featurize8(u, rh, om4, args.kr, ch);

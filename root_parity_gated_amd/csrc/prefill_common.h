@@ -8,6 +8,8 @@
 // dims {4h..4h+3, 8+4h..11+4h} of it.
 #pragma once
 
+#include <type_traits>
+
 #include "launchers.h"
 #include "sanatan_device.h"
 
@@ -132,6 +134,29 @@ __device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
 }
 __device__ __forceinline__ void load8(const __bf16* p, float (&o)[8]) {
   const bf16x4 a = *reinterpret_cast<const bf16x4*>(p), b = *reinterpret_cast<const bf16x4*>(p + 8);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    o[i] = (float)a[i];
+    o[4 + i] = (float)b[i];
+  }
+}
+
+// The same 8 values kept raw (two 4-element pieces) so that they can be loaded a chunk ahead.
+template <typename T> struct Raw8 {
+  typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type Half;
+  Half a, b;
+};
+template <typename T> __device__ __forceinline__ void load_raw8(const T* p, Raw8<T>& r) {
+  r.a = *reinterpret_cast<const typename Raw8<T>::Half*>(p);
+  r.b = *reinterpret_cast<const typename Raw8<T>::Half*>(p + 8);
+}
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&o)[8]) {
+  o[0] = __uint_as_float(r.a.x); o[1] = __uint_as_float(r.a.y); o[2] = __uint_as_float(r.a.z);
+  o[3] = __uint_as_float(r.a.w); o[4] = __uint_as_float(r.b.x); o[5] = __uint_as_float(r.b.y);
+  o[6] = __uint_as_float(r.b.z); o[7] = __uint_as_float(r.b.w);
+}
+__device__ __forceinline__ void unpack8(const Raw8<__bf16>& r, float (&o)[8]) {
+  const bf16x4 a = __builtin_bit_cast(bf16x4, r.a), b = __builtin_bit_cast(bf16x4, r.b);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     o[i] = (float)a[i];
