@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
   float* Zb = reinterpret_cast<float*>(smem + LDS - G::z_bytes);            // [4][96] z
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
-  const int g = blockIdx.x;
+  const int g = range_of_block(args);
   const int Tn = args.T;
   T* KSw = KS + w * CT * KP;
   float* Zw = Zb + w * 96;

@@ -70,6 +70,14 @@ struct PrefillArgs {
 };
 
 __device__ __forceinline__ long long range_lo(long long g, const PrefillArgs& a) { return g * a.total / a.G; }
+// Range (logical workgroup) of this workgroup.  Workgroups are dealt round-robin to the 8 XCDs, each
+// with its own L2; consecutive ranges -- the pieces of one sequence -- are given to workgroups on the
+// same XCD, so that pass 3 reads its predecessors' boundary states from the L2 that pass 1 wrote
+// them through.  A bijection on [0, G); the last G % 8 workgroups keep their own index.
+__device__ __forceinline__ int range_of_block(const PrefillArgs& a) {
+  const int b = (int)blockIdx.x, per = a.G / 8;
+  return b < 8 * per ? (b % 8) * per + b / 8 : b;
+}
 __device__ __forceinline__ int range_of_chunk(long long c, const PrefillArgs& a) {
   return (int)(((c + 1) * a.G - 1) / a.total);
 }

@@ -152,8 +152,9 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
     return STATE_ONLY ? Vbase + grp * CT * VP : Vbase + (j & 1) * CT * VP;
   };
 
-  const long long hi_c = range_lo(blockIdx.x + 1, args);
-  for (long long c = range_lo(blockIdx.x, args); c < hi_c;) {
+  const int g = range_of_block(args);
+  const long long hi_c = range_lo(g + 1, args);
+  for (long long c = range_lo(g, args); c < hi_c;) {
     const int bh = (int)(c / args.ncs);
     const long long seq_c0 = (long long)bh * args.ncs;
     const long long seq_end = seq_c0 + args.ncs;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
     const __bf16* __restrict__ qp = static_cast<const __bf16*>(args.q) + (size_t)bh * args.T * kD;
     const __bf16* __restrict__ vp = static_cast<const __bf16*>(args.v) + (size_t)bh * args.T * kDV;
     __bf16* __restrict__ op = static_cast<__bf16*>(args.out) + (size_t)bh * args.T * kDV;
-    float* slot = args.ws_state + (size_t)(bh + blockIdx.x) * kStateFloats;
+    float* slot = args.ws_state + (size_t)(bh + g) * kStateFloats;
 
     float om4[8];
 #pragma unroll
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
         if (args.multi) {
           const int gf = range_of_chunk(seq_c0, args);
-          for (int gg = gf; gg < (int)blockIdx.x; gg++) {
+          for (int gg = gf; gg < g; gg++) {
             const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
             add_slot(sj, sj + kF * kDV);
           }
@@ -620,8 +621,9 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
   const int toff = 32 * half;  // this wave's token offset inside a chunk
   const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
 
-  const long long hi_c = range_lo(blockIdx.x + 1, args);
-  for (long long c = range_lo(blockIdx.x, args); c < hi_c;) {
+  const int g = range_of_block(args);
+  const long long hi_c = range_lo(g + 1, args);
+  for (long long c = range_lo(g, args); c < hi_c;) {
     const int bh = (int)(c / args.ncs);
     const long long seq_c0 = (long long)bh * args.ncs;
     const long long seq_end = seq_c0 + args.ncs;
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
     const int hh = bh % args.H;
     const __bf16* __restrict__ kp = static_cast<const __bf16*>(args.k) + (size_t)bh * args.T * kD;
     const __bf16* __restrict__ vp = static_cast<const __bf16*>(args.v) + (size_t)bh * args.T * kDV;
-    float* slot = args.ws_state + (size_t)(bh + blockIdx.x) * kStateFloats;
+    float* slot = args.ws_state + (size_t)(bh + g) * kStateFloats;
 
     float om4[8];
 #pragma unroll
