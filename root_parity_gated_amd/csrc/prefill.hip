@@ -1,6 +1,6 @@
 // prefill.hip -- chunked causal p = 1 SANATAN attention on gfx950 MFMA: host plan, dispatch,
-// the boundary scan, and the 4-wave kernel (fp32 inputs, and 128-token chunks).  The bf16 kernel
-// for chunks up to 64 tokens (one wave per feature group) is in prefill_grp.hip.
+// the boundary scan, and the 4-wave kernel for fp32 inputs.  The bf16 kernels (one wave per feature
+// group) are in prefill_grp.hip.
 //
 // Exact regrouping of the recurrence of the SANATAN reading notes §2.7 (sum over s <= t of
 // kappa(t,s) v_s with kappa = <Phi(q_t), Phi(k_s)>, §2.3).  For a chunk with the state (S, z) of
@@ -410,17 +410,12 @@ static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t st
   using G = Geom4<T, CH>;
   static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
   if (a.multi) {
-    hipError_t e;
-    if constexpr (CH == 128 && sizeof(T) == 2) {
-      e = launch_prefill_state8_128(a, stream);  // two waves per SIMD, one per half of each 64 tokens
-    } else {
-      const size_t lds1 = G::lds(true);
-      e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds1);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((prefill4_kernel<T, CH, true>), dim3(a.G), dim3(256), lds1, stream, a);
-      e = hipGetLastError();
-    }
+    const size_t lds1 = G::lds(true);
+    hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill4_kernel<T, CH, true>), dim3(a.G), dim3(256), lds1, stream, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.scanned) {
       hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);
@@ -461,8 +456,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
     switch (plan.chunk) {
       case 16:
       case 32:
-      case 64: return launch_prefill_grp(a, plan.chunk, BH, stream);
-      case 128: return launch_prefill4_t<__bf16, 128>(a, BH, stream);
+      case 64:
+      case 128: return launch_prefill_grp(a, plan.chunk, BH, stream);
     }
   } else {
     switch (plan.chunk) {

@@ -83,8 +83,6 @@ __device__ __forceinline__ int range_of_chunk(long long c, const PrefillArgs& a)
 }
 
 hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream);
-// pass 1 (state increments of the non-final pieces) of a bf16 call with chunk 128
-hipError_t launch_prefill_state8_128(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream);
 
 template <typename T> __device__ __forceinline__ typename FragT<T>::type pack8f(const float (&x)[8]) {

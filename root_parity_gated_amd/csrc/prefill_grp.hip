@@ -825,6 +825,284 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
   }
 }
 
+// ------------------------------------------------------------------------------- chunk 128 (bf16)
+// Pass 3 for 128-token chunks with the layout of the kernel above (wave g = feature group g; lane
+// (n32, h) featurizes dims 16g + 8h + 0..7 of token n32 of a 32-token block straight into MFMA
+// K-slots), the four 32-row query blocks of a chunk taken one after another.  The chunk's Phi(K) (each
+// wave's 128 x 96 slice) and V stay in LDS for the whole chunk, the state is read out at the chunk's
+// start (one S^T packing per 128 tokens), and each query block's four partial numerators meet in one
+// reduction buffer.  Raw K, Q, V rows and phases are loaded a chunk (Q: a query block) ahead.
+struct Geom128 {
+  static constexpr int CH = 128, TB = 4, KP = 104, VP = 72, RP = 68;
+  static constexpr int ks_bytes = CH * KP * 2;  // one wave's Phi(K) tile
+  static constexpr int vs_off = 4 * ks_bytes;
+  static constexpr int vs_bytes = CH * VP * 2;
+  static constexpr int red_off = vs_off + vs_bytes;
+  static constexpr int red_bytes = 4 * 32 * RP * 4;  // one query block: [group][32][RP]
+  static constexpr int z_off = red_off + red_bytes;
+  static constexpr int lds = z_off + 4 * 96 * 4 + 4 * 96 * 2;  // z fp32 and its bf16 copy per wave
+};
+
+__global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArgs args) {
+  using G = Geom128;
+  constexpr int CH = G::CH, TB = G::TB, KP = G::KP, VP = G::VP, RP = G::RP;
+  constexpr int NV = CH * kDV / 8 / 256;  // 16-byte pieces of the V tile per thread
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, grp = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
+  __bf16* KS = reinterpret_cast<__bf16*>(smem + grp * G::ks_bytes);
+  __bf16* Vs = reinterpret_cast<__bf16*>(smem + G::vs_off);
+  float* red = reinterpret_cast<float*>(smem + G::red_off);
+  float* Zg = reinterpret_cast<float*>(smem + G::z_off) + grp * 96;
+  __bf16* Zb = reinterpret_cast<__bf16*>(smem + G::z_off + 4 * 96 * 4) + grp * 96;
+  const int dbase = 16 * grp + 8 * h;
+  const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
+  const bf16x8 ONES = __builtin_bit_cast(bf16x8, ones4);
+
+  const int g = range_of_block(args);
+  const long long hi_c = range_lo(g + 1, args);
+  for (long long c = range_lo(g, args); c < hi_c;) {
+    const int bh = (int)(c / args.ncs);
+    const long long seq_c0 = (long long)bh * args.ncs;
+    const long long seq_end = seq_c0 + args.ncs;
+    const long long pend = hi_c < seq_end ? hi_c : seq_end;
+    const bool last_piece = (pend == seq_end);
+    const int t_begin = (int)(c - seq_c0) * CH;
+    const int t_end = min(args.T, (int)(pend - seq_c0) * CH);
+    c = pend;
+    const int hh = bh % args.H;
+    const __bf16* __restrict__ kp = static_cast<const __bf16*>(args.k) + (size_t)bh * args.T * kD;
+    const __bf16* __restrict__ qp = static_cast<const __bf16*>(args.q) + (size_t)bh * args.T * kD;
+    const __bf16* __restrict__ vp = static_cast<const __bf16*>(args.v) + (size_t)bh * args.T * kDV;
+    __bf16* __restrict__ op = static_cast<__bf16*>(args.out) + (size_t)bh * args.T * kDV;
+    const float* slot = args.ws_state + (size_t)(bh + g) * kStateFloats;
+
+    float om4[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) om4[i] = anchor_rev(args.omega[(size_t)(hh % args.nph) * kD + dbase + i]);
+
+    // ---- state before the piece: the caller's state and the earlier pieces' increments (or their scan)
+    f32x16 Sacc[3][2];
+#pragma unroll
+    for (int ft = 0; ft < 3; ft++)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++) zero16(Sacc[ft][vt]);
+    for (int m = l; m < 96; m += 64) Zg[m] = 0.0f;
+    if (args.multi && args.scanned) {
+      gstate_add(Sacc, Zg, slot, slot + kF * kDV, grp, l);
+    } else {
+      if (args.S) gstate_add(Sacc, Zg, args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF, grp, l);
+      if (args.multi) {
+        const int gf = range_of_chunk(seq_c0, args);
+        for (int gg = gf; gg < g; gg++) {
+          const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
+          gstate_add(Sacc, Zg, sj, sj + kF * kDV, grp, l);
+        }
+      }
+    }
+    __syncthreads();  // the previous piece's tiles are dead
+    for (int m = l; m < 96; m += 64) Zb[m] = (__bf16)Zg[m];
+
+    // ---- raw rows a chunk ahead: this lane's key and query rows (token 32 b + n32, dims dbase..+7),
+    // their phases, and this thread's pieces of V; rows past the sequence's end re-read its last row
+    bf16x8 uk[TB], uq[TB];
+    float4 rh[TB][2];
+    uint4 rv[NV];
+    auto row_of = [&](int t0, int r) { return t0 + min(r, min(CH, t_end - t0) - 1); };
+    auto load_kv = [&](int t0) {
+#pragma unroll
+      for (int j = 0; j < NV; j++) {
+        const int e = tid + 256 * j;
+        rv[j] = *reinterpret_cast<const uint4*>(vp + (size_t)row_of(t0, e >> 3) * kDV + 8 * (e & 7));
+      }
+#pragma unroll
+      for (int b = 0; b < TB; b++) uk[b] = *reinterpret_cast<const bf16x8*>(kp + (size_t)row_of(t0, 32 * b + n32) * kD + dbase);
+    };
+    auto load_qr = [&](int t0, int b) {
+      const int tc = row_of(t0, 32 * b + n32);
+      uq[b] = *reinterpret_cast<const bf16x8*>(qp + (size_t)tc * kD + dbase);
+      const float* pr = args.rho + (size_t)tc * kD + dbase;
+      rh[b][0] = *reinterpret_cast<const float4*>(pr);
+      rh[b][1] = *reinterpret_cast<const float4*>(pr + 4);
+    };
+    load_kv(t_begin);
+#pragma unroll
+    for (int b = 0; b < TB; b++) load_qr(t_begin, b);
+
+    for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+      const int nvalid = min(CH, t_end - t0);
+      const int tn = t0 + CH < t_end ? t0 + CH : t0;
+      // 1. V tile (rows past the chunk's end zero) and this wave's Phi(K) rows (ones, then channels
+      //    1..5; zero rows past the end, so they reach neither S nor z)
+#pragma unroll
+      for (int j = 0; j < NV; j++) {
+        const int e = tid + 256 * j, row = e >> 3;
+        *reinterpret_cast<uint4*>(Vs + row * VP + 8 * (e & 7)) = row < nvalid ? rv[j] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int b = 0; b < TB; b++) {
+        __bf16* row = KS + (32 * b + n32) * KP + 8 * h;
+        if (32 * b + n32 < nvalid) {
+          bf16x8 F[5];
+          float cr[8], sr[8], rr[8];
+          feat8(uk[b], rh[b][0], rh[b][1], om4, args.kr, F, cr, sr, rr);
+          *reinterpret_cast<u32x4*>(row) = ones4;
+#pragma unroll
+          for (int cc = 1; cc < 6; cc++) *reinterpret_cast<bf16x8*>(row + 16 * cc) = F[cc - 1];
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < 6; cc++) *reinterpret_cast<u32x4*>(row + 16 * cc) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      load_kv(tn);  // the next chunk's V and keys, in flight through this chunk
+      __syncthreads();  // V tile complete
+
+      // 2. S^T operands of the readout, from the state before this chunk
+      bf16x8 SA[2][6];
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int cc = 0; cc < 6; cc++) {
+          u32x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            w[q] = pack_bf16x2(Sacc[cc >> 1][vt][8 * (cc & 1) + 2 * q], Sacc[cc >> 1][vt][8 * (cc & 1) + 2 * q + 1]);
+          SA[vt][cc] = __builtin_bit_cast(bf16x8, w);
+        }
+
+      // 3. query blocks one after another
+#pragma unroll
+      for (int tb = 0; tb < TB; tb++) {
+        bf16x8 QF[5];
+        float dz;
+        {
+          float cr[8], sr[8], rr[8];
+          feat8(uq[tb], rh[tb][0], rh[tb][1], om4, args.kr, QF, cr, sr, rr);
+          // Phi(q) . z: channel 0 in fp32, channels 1..5 as bf16 products like the rest of the readout
+          const float4 z0a = *reinterpret_cast<const float4*>(Zg + 8 * h);
+          const float4 z0b = *reinterpret_cast<const float4*>(Zg + 8 * h + 4);
+          float d = ((z0a.x + z0a.y) + (z0a.z + z0a.w)) + ((z0b.x + z0b.y) + (z0b.z + z0b.w));
+#pragma unroll
+          for (int cc = 0; cc < 5; cc++) d = frag_dot(QF[cc], *reinterpret_cast<const bf16x8*>(Zb + 16 * (cc + 1) + 8 * h), d);
+          dz = xor32_sum(d);
+        }
+        load_qr(tn, tb);  // this query block of the next chunk
+        // intra-chunk tiles A^T[s][t] for key blocks sb <= tb, masked on the diagonal, as bf16 B operands
+        bf16x8 P[TB][2];
+        float rs = 0.0f;
+#pragma unroll
+        for (int sb = 0; sb <= tb; sb++) {
+          f32x16 at;
+          zero16(at);
+          mma32(at, ONES, ONES);  // channel 0: sixteen products 1 * 1
+          const __bf16* krow = KS + (32 * sb + n32) * KP + 8 * h;
+#pragma unroll
+          for (int cc = 0; cc < 5; cc++) mma32(at, *reinterpret_cast<const bf16x8*>(krow + 16 * (cc + 1)), QF[cc]);
+          float lo[8], hi8[8];
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const int sl = 8 * (i >> 2) + 4 * h + (i & 3);
+            const float a = (sb == tb && sl > n32) ? 0.0f : at[i];
+            if (i < 8) lo[i] = a;
+            else hi8[i - 8] = a;
+          }
+          u32x4 w0, w1;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            w0[q] = pack_bf16x2(lo[2 * q], lo[2 * q + 1]);
+            w1[q] = pack_bf16x2(hi8[2 * q], hi8[2 * q + 1]);
+          }
+          P[sb][0] = __builtin_bit_cast(bf16x8, w0);
+          P[sb][1] = __builtin_bit_cast(bf16x8, w1);
+          rs = frag_sum(P[sb][1], frag_sum(P[sb][0], rs));
+        }
+        // numerators V^T P + S^T Phi(q) -> the reduction buffer (this group's 32 rows)
+        float* rrow = red + (grp * 32 + n32) * RP;
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          f32x16 num;
+          zero16(num);
+#pragma unroll
+          for (int sb = 0; sb <= tb; sb++) {
+            mma32(num, lds_tokfrag(Vs, VP, 32 * sb, 32 * vt, l), P[sb][0]);
+            mma32(num, lds_tokfrag(Vs, VP, 32 * sb + 16, 32 * vt, l), P[sb][1]);
+          }
+#pragma unroll
+          for (int cc = 0; cc < 6; cc++) mma32(num, SA[vt][cc], cc == 0 ? ONES : QF[cc - 1]);
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            *reinterpret_cast<float4*>(rrow + 32 * vt + 8 * q + 4 * h) =
+                make_float4(num[4 * q], num[4 * q + 1], num[4 * q + 2], num[4 * q + 3]);
+        }
+        rrow[64] = xor32_sum(rs) + dz;  // both halves store the same value
+        __syncthreads();
+        // o = num / (den + c eps) for the block's rows: thread -> row tid / 8, values 8 (tid % 8) .. + 7
+        {
+          const int t = tid >> 3, c0 = 8 * (tid & 7);
+          if (32 * tb + t < nvalid) {
+            const float* b0 = red + t * RP;
+            constexpr int GS = 32 * RP;
+            const float den = ((b0[64] + b0[GS + 64]) + b0[2 * GS + 64]) + b0[3 * GS + 64];
+            const float inv = 1.0f / (den + args.ceps);
+            u32x4 w;
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+              const int cb = c0 + 4 * half;
+              const float4 a0 = *reinterpret_cast<const float4*>(b0 + cb);
+              const float4 a1 = *reinterpret_cast<const float4*>(b0 + GS + cb);
+              const float4 a2 = *reinterpret_cast<const float4*>(b0 + 2 * GS + cb);
+              const float4 a3 = *reinterpret_cast<const float4*>(b0 + 3 * GS + cb);
+              w[2 * half] = pack_bf16x2((((a0.x + a1.x) + a2.x) + a3.x) * inv, (((a0.y + a1.y) + a2.y) + a3.y) * inv);
+              w[2 * half + 1] =
+                  pack_bf16x2((((a0.z + a1.z) + a2.z) + a3.z) * inv, (((a0.w + a1.w) + a2.w) + a3.w) * inv);
+            }
+            *reinterpret_cast<u32x4*>(op + (size_t)(t0 + 32 * tb + t) * kDV + c0) = w;
+          }
+        }
+        __syncthreads();  // the reduction buffer is free for the next block
+      }
+
+      // 4. state update S += Phi(K)^T V, z += Phi(K)^T 1 over the chunk's 128 tokens
+      float zs[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 2 * TB; ks++) {
+        const bf16x8 B0 = lds_tokfrag(Vs, VP, 16 * ks, 0, l);
+        const bf16x8 B1 = lds_tokfrag(Vs, VP, 16 * ks, 32, l);
+#pragma unroll
+        for (int ft = 0; ft < 3; ft++) {
+          const bf16x8 A = lds_tokfrag_swz(KS, KP, 16 * ks, 32 * ft, l);
+          zs[ft] = frag_sum(A, zs[ft]);
+          mma32(Sacc[ft][0], A, B0);
+          mma32(Sacc[ft][1], A, B1);
+        }
+      }
+#pragma unroll
+      for (int ft = 0; ft < 3; ft++) {
+        const int m = 32 * ft + 16 * (n32 >> 4) + swz16(n32 & 15);
+        const float znew = Zg[m] + xor32_sum(zs[ft]);
+        Zg[m] = znew;  // both halves store the same value
+        Zb[m] = (__bf16)znew;
+      }
+      __syncthreads();  // everyone is done with this chunk's tiles
+    }
+    if (last_piece && args.S) gstate_store(Sacc, Zg, args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF, grp, l);
+  }
+}
+
+hipError_t launch_prefill_grp128(const PrefillArgs& a, hipStream_t stream) {
+  static_assert(Geom128::lds <= 160 * 1024, "LDS budget");
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
+    const hipError_t e = hipFuncSetAttribute((const void*)prefill_grp128_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, Geom128::lds);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(prefill_grp128_kernel, dim3(a.G), dim3(256), Geom128::lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int CH>
 hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   using G = GeomG<CH>;
@@ -862,8 +1140,7 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
+// pass 1 for 128-token chunks: the 8-wave state kernel walks each chunk as two 64-token halves
 hipError_t launch_prefill_state8_128(const PrefillArgs& a, hipStream_t stream) {
   static bool attr_set[64] = {};
   int dev = 0;
@@ -878,11 +1155,24 @@ hipError_t launch_prefill_state8_128(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+}  // namespace
+
 hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream) {
   switch (chunk) {
     case 16: return launch_grp_t<16>(a, BH, stream);
     case 32: return launch_grp_t<32>(a, BH, stream);
     case 64: return launch_grp_t<64>(a, BH, stream);
+    case 128: {
+      if (a.multi) {
+        hipError_t e = launch_prefill_state8_128(a, stream);
+        if (e != hipSuccess) return e;
+        if (a.scanned) {
+          e = launch_prefill_scan(a, BH, stream);
+          if (e != hipSuccess) return e;
+        }
+      }
+      return launch_prefill_grp128(a, stream);
+    }
   }
   return hipErrorInvalidValue;
 }
