@@ -828,10 +828,13 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
 // ------------------------------------------------------------------------------- chunk 128 (bf16)
 // Pass 3 for 128-token chunks with the layout of the kernel above (wave g = feature group g; lane
 // (n32, h) featurizes dims 16g + 8h + 0..7 of token n32 of a 32-token block straight into MFMA
-// K-slots), the four 32-row query blocks of a chunk taken one after another.  The chunk's Phi(K) (each
-// wave's 128 x 96 slice) and V stay in LDS for the whole chunk, the state is read out at the chunk's
-// start (one S^T packing per 128 tokens), and each query block's four partial numerators meet in one
-// reduction buffer.  Raw K, Q, V rows and phases are loaded a chunk (Q: a query block) ahead.
+// K-slots).  A chunk runs as four 32-token blocks in order.  Block b featurizes its keys (kept in
+// registers for the diagonal score tile, and written to the wave's Phi(K) tile for the later blocks and
+// the state update) and its queries, then reads out against S as it was at the chunk's start (packed to
+// bf16 once per chunk) plus the masked scores of key blocks 0..b.  The four groups' partial numerators
+// of a block meet in one reduction buffer.  Raw key, query and phase rows are loaded one block ahead
+// and V rows two blocks ahead; the V rows of block b + 1 go to the shared tile while block b runs, so
+// block b's barriers publish them.
 struct Geom128 {
   static constexpr int CH = 128, TB = 4, KP = 104, VP = 72, RP = 68;
   static constexpr int ks_bytes = CH * KP * 2;  // one wave's Phi(K) tile
@@ -843,10 +846,15 @@ struct Geom128 {
   static constexpr int lds = z_off + 4 * 96 * 4 + 4 * 96 * 2;  // z fp32 and its bf16 copy per wave
 };
 
+// one lane's raw key, query and phase values of a token (8 dims)
+struct RawKQ {
+  bf16x8 k, q;
+  float4 r0, r1;
+};
+
 __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArgs args) {
   using G = Geom128;
   constexpr int CH = G::CH, TB = G::TB, KP = G::KP, VP = G::VP, RP = G::RP;
-  constexpr int NV = CH * kDV / 8 / 256;  // 16-byte pieces of the V tile per thread
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, grp = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
   __bf16* KS = reinterpret_cast<__bf16*>(smem + grp * G::ks_bytes);
@@ -855,6 +863,7 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
   float* Zg = reinterpret_cast<float*>(smem + G::z_off) + grp * 96;
   __bf16* Zb = reinterpret_cast<__bf16*>(smem + G::z_off + 4 * 96 * 4) + grp * 96;
   const int dbase = 16 * grp + 8 * h;
+  const int vrow = tid >> 3, vcol = 8 * (tid & 7);  // this thread's 16 bytes of a block's V rows
   const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
   const bf16x8 ONES = __builtin_bit_cast(bf16x8, ones4);
 
@@ -902,61 +911,39 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
     __syncthreads();  // the previous piece's tiles are dead
     for (int m = l; m < 96; m += 64) Zb[m] = (__bf16)Zg[m];
 
-    // ---- raw rows a chunk ahead: this lane's key and query rows (token 32 b + n32, dims dbase..+7),
-    // their phases, and this thread's pieces of V; rows past the sequence's end re-read its last row
-    bf16x8 uk[TB], uq[TB];
-    float4 rh[TB][2];
-    uint4 rv[NV];
-    auto row_of = [&](int t0, int r) { return t0 + min(r, min(CH, t_end - t0) - 1); };
-    auto load_kv = [&](int t0) {
-#pragma unroll
-      for (int j = 0; j < NV; j++) {
-        const int e = tid + 256 * j;
-        rv[j] = *reinterpret_cast<const uint4*>(vp + (size_t)row_of(t0, e >> 3) * kDV + 8 * (e & 7));
-      }
-#pragma unroll
-      for (int b = 0; b < TB; b++) uk[b] = *reinterpret_cast<const bf16x8*>(kp + (size_t)row_of(t0, 32 * b + n32) * kD + dbase);
+    // raw rows of block i of the piece (chunk t_begin + 128 (i / 4), tokens 32 (i % 4) ..); indexes past
+    // the piece's last block re-read that block, rows past a chunk's end re-read the chunk's last row
+    const int nblk = TB * ((t_end - t_begin + CH - 1) / CH);
+    auto src_row = [&](int i, int r) {
+      const int ib = min(i, nblk - 1);
+      const int t0 = t_begin + CH * (ib / TB);
+      return t0 + min(32 * (ib % TB) + r, min(CH, t_end - t0) - 1);
     };
-    auto load_qr = [&](int t0, int b) {
-      const int tc = row_of(t0, 32 * b + n32);
-      uq[b] = *reinterpret_cast<const bf16x8*>(qp + (size_t)tc * kD + dbase);
+    auto load_kq = [&](int i) {
+      RawKQ x;
+      const int tc = src_row(i, n32);
+      x.k = *reinterpret_cast<const bf16x8*>(kp + (size_t)tc * kD + dbase);
+      x.q = *reinterpret_cast<const bf16x8*>(qp + (size_t)tc * kD + dbase);
       const float* pr = args.rho + (size_t)tc * kD + dbase;
-      rh[b][0] = *reinterpret_cast<const float4*>(pr);
-      rh[b][1] = *reinterpret_cast<const float4*>(pr + 4);
+      x.r0 = *reinterpret_cast<const float4*>(pr);
+      x.r1 = *reinterpret_cast<const float4*>(pr + 4);
+      return x;
     };
-    load_kv(t_begin);
-#pragma unroll
-    for (int b = 0; b < TB; b++) load_qr(t_begin, b);
+    auto load_v = [&](int i) { return *reinterpret_cast<const uint4*>(vp + (size_t)src_row(i, vrow) * kDV + vcol); };
+    // this thread's piece of the V rows of block b of a chunk with nvalid tokens (rows past the end zero)
+    auto write_v = [&](int b, int nvalid, const uint4& x) {
+      const int row = 32 * b + vrow;
+      *reinterpret_cast<uint4*>(Vs + row * VP + vcol) = row < nvalid ? x : make_uint4(0u, 0u, 0u, 0u);
+    };
 
-    for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+    RawKQ kq = load_kq(0);
+    uint4 va = load_v(0), vb = load_v(1);  // V of the next block to publish, and of the one after
+    for (int t0 = t_begin, i0 = 0; t0 < t_end; t0 += CH, i0 += TB) {
       const int nvalid = min(CH, t_end - t0);
-      const int tn = t0 + CH < t_end ? t0 + CH : t0;
-      // 1. V tile (rows past the chunk's end zero) and this wave's Phi(K) rows (ones, then channels
-      //    1..5; zero rows past the end, so they reach neither S nor z)
-#pragma unroll
-      for (int j = 0; j < NV; j++) {
-        const int e = tid + 256 * j, row = e >> 3;
-        *reinterpret_cast<uint4*>(Vs + row * VP + 8 * (e & 7)) = row < nvalid ? rv[j] : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int b = 0; b < TB; b++) {
-        __bf16* row = KS + (32 * b + n32) * KP + 8 * h;
-        if (32 * b + n32 < nvalid) {
-          bf16x8 F[5];
-          float cr[8], sr[8], rr[8];
-          feat8(uk[b], rh[b][0], rh[b][1], om4, args.kr, F, cr, sr, rr);
-          *reinterpret_cast<u32x4*>(row) = ones4;
-#pragma unroll
-          for (int cc = 1; cc < 6; cc++) *reinterpret_cast<bf16x8*>(row + 16 * cc) = F[cc - 1];
-        } else {
-#pragma unroll
-          for (int cc = 0; cc < 6; cc++) *reinterpret_cast<u32x4*>(row + 16 * cc) = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      load_kv(tn);  // the next chunk's V and keys, in flight through this chunk
-      __syncthreads();  // V tile complete
+      write_v(0, nvalid, va);
+      __syncthreads();  // V rows of block 0 are in
 
-      // 2. S^T operands of the readout, from the state before this chunk
+      // S^T operands of the readout, from the state before this chunk
       bf16x8 SA[2][6];
 #pragma unroll
       for (int vt = 0; vt < 2; vt++)
@@ -969,14 +956,27 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
           SA[vt][cc] = __builtin_bit_cast(bf16x8, w);
         }
 
-      // 3. query blocks one after another
 #pragma unroll
       for (int tb = 0; tb < TB; tb++) {
-        bf16x8 QF[5];
+        const RawKQ kqn = load_kq(i0 + tb + 1);
+        const uint4 vn = load_v(i0 + tb + 2);
+        // keys of this block: features in registers, and rows of the wave's Phi(K) tile (ones, then
+        // channels 1..5; zero rows past the chunk's end, so they reach neither S nor z)
+        bf16x8 KF[5], QF[5];
         float dz;
         {
           float cr[8], sr[8], rr[8];
-          feat8(uq[tb], rh[tb][0], rh[tb][1], om4, args.kr, QF, cr, sr, rr);
+          feat8(kq.k, kq.r0, kq.r1, om4, args.kr, KF, cr, sr, rr);
+          __bf16* row = KS + (32 * tb + n32) * KP + 8 * h;
+          if (32 * tb + n32 < nvalid) {
+            *reinterpret_cast<u32x4*>(row) = ones4;
+#pragma unroll
+            for (int cc = 1; cc < 6; cc++) *reinterpret_cast<bf16x8*>(row + 16 * cc) = KF[cc - 1];
+          } else {
+#pragma unroll
+            for (int cc = 0; cc < 6; cc++) *reinterpret_cast<u32x4*>(row + 16 * cc) = u32x4{0u, 0u, 0u, 0u};
+          }
+          feat8(kq.q, kq.r0, kq.r1, om4, args.kr, QF, cr, sr, rr);
           // Phi(q) . z: channel 0 in fp32, channels 1..5 as bf16 products like the rest of the readout
           const float4 z0a = *reinterpret_cast<const float4*>(Zg + 8 * h);
           const float4 z0b = *reinterpret_cast<const float4*>(Zg + 8 * h + 4);
@@ -985,9 +985,17 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
           for (int cc = 0; cc < 5; cc++) d = frag_dot(QF[cc], *reinterpret_cast<const bf16x8*>(Zb + 16 * (cc + 1) + 8 * h), d);
           dz = xor32_sum(d);
         }
-        load_qr(tn, tb);  // this query block of the next chunk
-        // intra-chunk tiles A^T[s][t] for key blocks sb <= tb, masked on the diagonal, as bf16 B operands
-        bf16x8 P[TB][2];
+        if (tb + 1 < TB) write_v(tb + 1, nvalid, vb);  // published by this block's barriers
+
+        // numerators S^T Phi(q) (readout) + V^T P, P = the intra-chunk tiles A^T[s][t] of key blocks
+        // sb <= tb, masked on the diagonal, as bf16 B operands, each folded in as soon as it is packed
+        f32x16 num[2];
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          zero16(num[vt]);
+#pragma unroll
+          for (int cc = 0; cc < 6; cc++) mma32(num[vt], SA[vt][cc], cc == 0 ? ONES : QF[cc - 1]);
+        }
         float rs = 0.0f;
 #pragma unroll
         for (int sb = 0; sb <= tb; sb++) {
@@ -996,7 +1004,8 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
           mma32(at, ONES, ONES);  // channel 0: sixteen products 1 * 1
           const __bf16* krow = KS + (32 * sb + n32) * KP + 8 * h;
 #pragma unroll
-          for (int cc = 0; cc < 5; cc++) mma32(at, *reinterpret_cast<const bf16x8*>(krow + 16 * (cc + 1)), QF[cc]);
+          for (int cc = 0; cc < 5; cc++)
+            mma32(at, sb == tb ? KF[cc] : *reinterpret_cast<const bf16x8*>(krow + 16 * (cc + 1)), QF[cc]);
           float lo[8], hi8[8];
 #pragma unroll
           for (int i = 0; i < 16; i++) {
@@ -1011,29 +1020,26 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
             w0[q] = pack_bf16x2(lo[2 * q], lo[2 * q + 1]);
             w1[q] = pack_bf16x2(hi8[2 * q], hi8[2 * q + 1]);
           }
-          P[sb][0] = __builtin_bit_cast(bf16x8, w0);
-          P[sb][1] = __builtin_bit_cast(bf16x8, w1);
-          rs = frag_sum(P[sb][1], frag_sum(P[sb][0], rs));
+          const bf16x8 P0 = __builtin_bit_cast(bf16x8, w0), P1 = __builtin_bit_cast(bf16x8, w1);
+          rs = frag_sum(P1, frag_sum(P0, rs));
+#pragma unroll
+          for (int vt = 0; vt < 2; vt++) {
+            mma32(num[vt], lds_tokfrag(Vs, VP, 32 * sb, 32 * vt, l), P0);
+            mma32(num[vt], lds_tokfrag(Vs, VP, 32 * sb + 16, 32 * vt, l), P1);
+          }
         }
-        // numerators V^T P + S^T Phi(q) -> the reduction buffer (this group's 32 rows)
+        const float den = xor32_sum(rs) + dz;
+        // the previous block's normalisation (same scheduling region as this block's work, so the two
+        // overlap) must be done everywhere before the buffer is overwritten
+        if (tb > 0) __syncthreads();
         float* rrow = red + (grp * 32 + n32) * RP;
 #pragma unroll
-        for (int vt = 0; vt < 2; vt++) {
-          f32x16 num;
-          zero16(num);
-#pragma unroll
-          for (int sb = 0; sb <= tb; sb++) {
-            mma32(num, lds_tokfrag(Vs, VP, 32 * sb, 32 * vt, l), P[sb][0]);
-            mma32(num, lds_tokfrag(Vs, VP, 32 * sb + 16, 32 * vt, l), P[sb][1]);
-          }
-#pragma unroll
-          for (int cc = 0; cc < 6; cc++) mma32(num, SA[vt][cc], cc == 0 ? ONES : QF[cc - 1]);
+        for (int vt = 0; vt < 2; vt++)
 #pragma unroll
           for (int q = 0; q < 4; q++)
             *reinterpret_cast<float4*>(rrow + 32 * vt + 8 * q + 4 * h) =
-                make_float4(num[4 * q], num[4 * q + 1], num[4 * q + 2], num[4 * q + 3]);
-        }
-        rrow[64] = xor32_sum(rs) + dz;  // both halves store the same value
+                make_float4(num[vt][4 * q], num[vt][4 * q + 1], num[vt][4 * q + 2], num[vt][4 * q + 3]);
+        rrow[64] = den;  // both halves store the same value
         __syncthreads();
         // o = num / (den + c eps) for the block's rows: thread -> row tid / 8, values 8 (tid % 8) .. + 7
         {
@@ -1041,8 +1047,8 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
           if (32 * tb + t < nvalid) {
             const float* b0 = red + t * RP;
             constexpr int GS = 32 * RP;
-            const float den = ((b0[64] + b0[GS + 64]) + b0[2 * GS + 64]) + b0[3 * GS + 64];
-            const float inv = 1.0f / (den + args.ceps);
+            const float dsum = ((b0[64] + b0[GS + 64]) + b0[2 * GS + 64]) + b0[3 * GS + 64];
+            const float inv = 1.0f / (dsum + args.ceps);
             u32x4 w;
 #pragma unroll
             for (int half = 0; half < 2; half++) {
@@ -1058,10 +1064,12 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
             *reinterpret_cast<u32x4*>(op + (size_t)(t0 + 32 * tb + t) * kDV + c0) = w;
           }
         }
-        __syncthreads();  // the reduction buffer is free for the next block
+        kq = kqn;
+        va = vb;
+        vb = vn;
       }
 
-      // 4. state update S += Phi(K)^T V, z += Phi(K)^T 1 over the chunk's 128 tokens
+      // state update S += Phi(K)^T V, z += Phi(K)^T 1 over the chunk's 128 tokens
       float zs[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < 2 * TB; ks++) {
