@@ -55,7 +55,7 @@ def quadratic_flops(B, H, T):
 
 PREFILL_SOURCES = ("api.hip", "featurize.hip", "prefill.hip", "prefill_grp.hip", "prefill_common.h", "launchers.h",
                    "sanatan_device.h")
-PREFILL_KERNELS = ("phase_table_kernel", "prefill_grp_kernel", "prefill_state8_kernel", "prefill_scan_kernel",
+PREFILL_KERNELS = ("phase_table_kernel", "prefill_grp_kernel", "prefill_grp128_kernel", "prefill_state8_kernel", "prefill_scan_kernel",
                    "prefill4_kernel")
 CAL_BYTES = 256 << 20       # plain device copy used to calibrate the memory counters
 
