@@ -347,11 +347,23 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs arg
   const int gl = range_of_chunk(c1, args);
   float run = 0.0f;
   if (args.S) run = (e < kF * kDV) ? args.S[(size_t)bh * kF * kDV + e] : args.z[(size_t)bh * kF + (e - kF * kDV)];
-  for (int gg = gf; gg <= gl; gg++) {
-    float* p = args.ws_state + (size_t)(bh + gg) * kStateFloats + e;
-    const float d = (gg < gl) ? *p : 0.0f;
-    *p = run;
-    run += d;
+  // U slots' increments are loaded at once, then replaced by their prefixes in order
+  constexpr int U = 8;
+  for (int g0 = gf; g0 <= gl; g0 += U) {
+    float d[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int gg = g0 + u;
+      d[u] = (gg < gl) ? args.ws_state[(size_t)(bh + gg) * kStateFloats + e] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int gg = g0 + u;
+      if (gg <= gl) {
+        args.ws_state[(size_t)(bh + gg) * kStateFloats + e] = run;
+        run += d[u];
+      }
+    }
   }
 }
 
