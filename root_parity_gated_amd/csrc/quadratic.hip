@@ -37,12 +37,12 @@ struct QGeom {
   static constexpr int PIECES = (KPIECES + VPIECES + 255) / 256;  // per thread
 };
 
+// Two workgroups per CU for bf16; the fp32 operand fragments take the registers of one.
 template <typename T, int P>
-__global__ __launch_bounds__(256, 2) void quadratic_kernel(const T* __restrict__ q, const T* __restrict__ phik,
-                                                           const T* __restrict__ v, T* __restrict__ out,
-                                                           const float* __restrict__ rho, const float* __restrict__ omega,
-                                                           int nph, int H, int Tn, int BH, int nqb, float kr,
-                                                           float eps_cp) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
+    const T* __restrict__ q, const T* __restrict__ phik, const T* __restrict__ v, T* __restrict__ out,
+    const float* __restrict__ rho, const float* __restrict__ omega, int nph, int H, int Tn, int BH, int nqb, float kr,
+    float eps_cp) {
   using G = QGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
