@@ -288,6 +288,23 @@ def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False):
     return eager, graph
 
 
+def bench_featurize(torch, rpg, si, w, steps, warmup):
+    """Standalone feature map of one [B,H,T,64] operand (the keys of workload w) into [B,H,T,384], same dtype.
+    HBM-bound: the algorithmic bytes are the input read once and Phi written once."""
+    _, k, _, om = si.workload_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    kd = torch.from_numpy(k).cuda().to(dt)
+    del k
+    p = rpg.Params(omega=torch.from_numpy(om).cuda(), gamma=w.gamma, eps=w.eps, lambda_base=w.lambda_base)
+    phi = torch.empty((w.B, w.H, w.T, 6 * 64), dtype=dt, device="cuda")
+    fn = lambda: rpg.sanatan_featurize(kd, 0, p, out=phi)
+    eager = timed_loop(torch, fn, steps, warmup)
+    g = graph_of(torch, fn)
+    graph = timed_loop(torch, g.replay, steps, warmup) if g is not None else None
+    el = 2 if w.dtype == "bf16" else 4
+    return eager, graph, w.B * w.H * w.T * 64 * el * 7
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +414,14 @@ def main():
                                   "roofline": {"bound": "mfma", "achieved": qfl / (qms * 1e-3) / 1e12,
                                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                                "frac": qfl / (qms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+        log(f"featurize {w.name} keys")
+        fms_e, fms_g, fbytes = bench_featurize(torch, rpg, si, w, max(5, args.steps // 5), 3)
+        fms = min(fms_e, fms_g) if fms_g is not None else fms_e
+        extras["featurize"] = {"workload": f"featurize_keys_of_{w.name}", "ms": fms, "ms_eager": fms_e,
+                               "ms_graph": fms_g, "bytes_per_call": fbytes,
+                               "roofline": {"bound": "hbm", "achieved": fbytes / (fms * 1e-3) / 1e9,
+                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                            "frac": fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
         result["extras"] = extras
     print(json.dumps(result))
 
