@@ -158,23 +158,27 @@ def test_quadratic_short_sequences(torch_dev, dtype, p, T):
             assert row_rel_err(got[b, h], want) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("wgs", [5, 13, 23, 30, 59])
-def test_prefill_many_partitions(torch_dev, monkeypatch, wgs):
-    """bf16 chunk 64 with the workgroup count forced: ranges of many lengths and 2..8 pieces per sequence,
-    so both the fused predecessor sums and the scan kernel run.  Output and final state against the
-    oracle."""
+def test_prefill_many_partitions(torch_dev, monkeypatch, wgs, chunk):
+    """bf16 chunks of 64 and 128 tokens with the workgroup count forced: ranges of many lengths and
+    several pieces per sequence (up to 10 at chunk 64, 5 at chunk 128), so both the fused predecessor sums
+    and the scan kernel run, from a nonzero initial state.  Output and final state against the oracle."""
     import root_parity_gated_amd as rpg
 
     torch = torch_dev
     monkeypatch.setenv("SANATAN_PREFILL_WGS", str(wgs))
     B, H, T = 2, 3, 2048 - 29
     q, k, v, om = si.attention_inputs(450 + wgs, B, H, T, "bf16")
-    S = torch.zeros((B, H, 384, 64), device="cuda")
-    z = torch.zeros((B, H, 384), device="cuda")
-    out = rpg.sanatan_prefill_chunked(dev(torch, q, "bf16"), dev(torch, k, "bf16"), dev(torch, v, "bf16"), 64,
-                                      params(torch, om), S=S, z=z)
+    # initial state: the state after a seeded 300-token prefix, continued at position 300
+    pq, pk, pv, _ = si.attention_inputs(470 + wgs, B, H, 300, "bf16")
+    _, S0, z0 = oracle_heads(pq, pk, pv, om)
+    S = torch.from_numpy(S0.astype(np.float32)).cuda()
+    z = torch.from_numpy(z0.astype(np.float32)).cuda()
+    out = rpg.sanatan_prefill_chunked(dev(torch, q, "bf16"), dev(torch, k, "bf16"), dev(torch, v, "bf16"), chunk,
+                                      params(torch, om), pos0=300, S=S, z=z)
     torch.cuda.synchronize()
-    want, Sw, zw = oracle_heads(q, k, v, om)
-    assert row_rel_err(host(out), want) <= TOL["bf16"]
+    want, Sw, zw = oracle_heads(np.concatenate([pq, q], 2), np.concatenate([pk, k], 2), np.concatenate([pv, v], 2), om)
+    assert row_rel_err(host(out), want[:, :, 300:]) <= TOL["bf16"]
     assert np.abs(host(S) - Sw).max() <= TOL["bf16"] * np.abs(Sw).max()
     assert np.abs(host(z) - zw).max() <= TOL["bf16"] * np.abs(zw).max()
