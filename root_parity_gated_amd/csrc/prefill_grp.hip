@@ -20,7 +20,9 @@
 // uses the same swap, so readout K-slots and state rows line up.
 //
 // Channel 0 of Phi is the constant 1: in the intra-chunk product its 16 features contribute exactly
-// 16 to every entry, which initialises the accumulator instead of an MFMA.
+// 16 to every entry, which one MFMA on two fragments of ones supplies (it costs the VALU nothing, unlike
+// writing 16 accumulator registers).  The bf16 kernels for 16-, 32- and 64-token chunks and the one for
+// 128-token chunks (further below) share this layout.
 #include "prefill_common.h"
 
 namespace sanatan {
