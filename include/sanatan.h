@@ -80,7 +80,11 @@ sanatan_status sanatan_featurize(const void* u, sanatan_dtype in_t, int B, int H
                                  const sanatan_params* params, void* phi, sanatan_dtype out_t,
                                  hipStream_t stream);
 
-/* Workspace bytes sanatan_prefill_chunked needs for these sizes (0 on invalid sizes). */
+/* Workspace bytes sanatan_prefill_chunked needs for these sizes (0 on invalid sizes).
+ * The prefill splits the B*H*ceil(T/chunk) chunks over one workgroup per compute unit.  The environment
+ * variable SANATAN_PREFILL_WGS, when it holds a positive integer, replaces that count (capped at the number
+ * of chunks); it is a test hook that forces sequences into many pieces.  The workspace size follows the
+ * count, and a call whose workspace is smaller than its own plan needs returns SANATAN_ERR_WORKSPACE. */
 size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const sanatan_params* params);
 
 /*
