@@ -94,26 +94,24 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   const int last_row = min(Tn - 1, qb * G::QROWS + G::QROWS - 1);
   const int nkb = last_row / KB + 1;
   const int my_last = min(Tn - 1, row0 + 32 * MQ - 1);
-  uint4 pf[KPT + VPT];
+  u32x4 pf[KPT + VPT];
   auto krow_of = [&](int p) { return (tid + 256 * p) / (NF / EL); };
   auto kcol_of = [&](int p) { return ((tid + 256 * p) % (NF / EL)) * EL; };
   auto vrow_of = [&](int p) { return (tid + 256 * p) / (kDV / EL); };
   auto vcol_of = [&](int p) { return ((tid + 256 * p) % (kDV / EL)) * EL; };
-  auto fetch = [&](int kb) {  // this thread's pieces of key block kb -> registers (rows past Tn: zero)
+  // This thread's pieces of key block kb -> registers.  A row past the sequence re-reads its last row: such a
+  // key follows every query, so the causal mask zeroes its weight (and its finite V row then adds nothing).
+  auto fetch = [&](int kb) {
     const int s0 = kb * KB;
-    const bool full = s0 + KB <= Tn;
 #pragma unroll
     for (int p = 0; p < KPT; p++) {
-      const int s = krow_of(p);
-      pf[p] = (full || s0 + s < Tn) ? *reinterpret_cast<const uint4*>(kp + (size_t)(s0 + s) * kF + kcol_of(p))
-                                    : make_uint4(0u, 0u, 0u, 0u);
+      const int r = min(s0 + krow_of(p), Tn - 1);
+      pf[p] = *reinterpret_cast<const u32x4*>(kp + (size_t)r * kF + kcol_of(p));
     }
 #pragma unroll
     for (int p = 0; p < VPT; p++) {
-      const int s = vrow_of(p);
-      pf[KPT + p] = (full || s0 + s < Tn)
-                        ? *reinterpret_cast<const uint4*>(vp + (size_t)(s0 + s) * kDV + vcol_of(p))
-                        : make_uint4(0u, 0u, 0u, 0u);
+      const int r = min(s0 + vrow_of(p), Tn - 1);
+      pf[KPT + p] = *reinterpret_cast<const u32x4*>(vp + (size_t)r * kDV + vcol_of(p));
     }
   };
   auto stash = [&](int buf) {  // registers -> LDS buffer
@@ -121,10 +119,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     T* Vs = reinterpret_cast<T*>(smem + buf * G::buf_bytes + G::k_bytes);
 #pragma unroll
     for (int p = 0; p < KPT; p++)
-      *reinterpret_cast<uint4*>(__builtin_assume_aligned(Ks + krow_of(p) * KP + kcol_of(p), 16)) = pf[p];
+      *reinterpret_cast<u32x4*>(__builtin_assume_aligned(Ks + krow_of(p) * KP + kcol_of(p), 16)) = pf[p];
 #pragma unroll
     for (int p = 0; p < VPT; p++)
-      *reinterpret_cast<uint4*>(__builtin_assume_aligned(Vs + vrow_of(p) * VP + vcol_of(p), 16)) = pf[KPT + p];
+      *reinterpret_cast<u32x4*>(__builtin_assume_aligned(Vs + vrow_of(p) * VP + vcol_of(p), 16)) = pf[KPT + p];
   };
 
   f32x16 num[MQ][2];
