@@ -99,20 +99,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   auto kcol_of = [&](int p) { return ((tid + 256 * p) % (NF / EL)) * EL; };
   auto vrow_of = [&](int p) { return (tid + 256 * p) / (kDV / EL); };
   auto vcol_of = [&](int p) { return ((tid + 256 * p) % (kDV / EL)) * EL; };
-  // This thread's pieces of key block kb -> registers.  A row past the sequence re-reads its last row: such a
-  // key follows every query, so the causal mask zeroes its weight (and its finite V row then adds nothing).
+  // This thread's pieces of key block kb -> registers, through buffer loads: the block's descriptor starts
+  // at its first row and covers the rows up to the sequence's end, so the hardware's range check returns
+  // zeros for rows past the end, and each piece's offset from the descriptor's start is fixed per thread
+  // (no address arithmetic per block).  Descriptor word 3: the gfx9-family raw-buffer format.
+  unsigned koff[KPT], voff[VPT];
+#pragma unroll
+  for (int p = 0; p < KPT; p++) koff[p] = (unsigned)((krow_of(p) * kF + kcol_of(p)) * (int)sizeof(T));
+#pragma unroll
+  for (int p = 0; p < VPT; p++) voff[p] = (unsigned)((vrow_of(p) * kDV + vcol_of(p)) * (int)sizeof(T));
+  constexpr int kRawBufferWord3 = 0x00020000;
   auto fetch = [&](int kb) {
     const int s0 = kb * KB;
+    // Phi(K) rows start at channel 1 (kp skips channel 0), so the last row ends kD elements short of kF
+    const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kp + (size_t)s0 * kF), (short)0, (int)(((Tn - s0) * kF - kD) * (int)sizeof(T)), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vp + (size_t)s0 * kDV), (short)0, (int)((Tn - s0) * kDV * (int)sizeof(T)), kRawBufferWord3);
 #pragma unroll
-    for (int p = 0; p < KPT; p++) {
-      const int r = min(s0 + krow_of(p), Tn - 1);
-      pf[p] = *reinterpret_cast<const u32x4*>(kp + (size_t)r * kF + kcol_of(p));
-    }
+    for (int p = 0; p < KPT; p++) pf[p] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff[p], 0, 0);
 #pragma unroll
-    for (int p = 0; p < VPT; p++) {
-      const int r = min(s0 + vrow_of(p), Tn - 1);
-      pf[KPT + p] = *reinterpret_cast<const u32x4*>(vp + (size_t)r * kDV + vcol_of(p));
-    }
+    for (int p = 0; p < VPT; p++) pf[KPT + p] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff[p], 0, 0);
   };
   auto stash = [&](int buf) {  // registers -> LDS buffer
     T* Ks = reinterpret_cast<T*>(smem + buf * G::buf_bytes);
