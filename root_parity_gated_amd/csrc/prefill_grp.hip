@@ -652,22 +652,33 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
     // z of feature 32 ft + n32 of the group's tile order (both lane halves hold the same value)
     float zacc[3] = {0.0f, 0.0f, 0.0f};
 
-    // raw inputs of one chunk (start t0; clamped to the sequence, so a chunk past the end re-reads the
-    // last one): this lane's key row and phases (token toff + n32), its pieces of the wave's V rows
+    // Raw inputs of one 64-token step (start t0; a step past the piece's end re-reads the last one): this
+    // lane's key row and phases (token toff + n32), its pieces of the wave's V rows.  A piece handled here
+    // is not its sequence's last, so it starts and ends on chunk boundaries strictly inside the sequence:
+    // every step is whole.  The loads are buffer loads over the sequence (and the phase table), with the
+    // lane's offset inside a step fixed and the step's start as the scalar offset, so a step costs no
+    // address arithmetic; the descriptors' range check would return zeros past the sequence's end.
     auto next_t = [&](int t0) { return t0 + CH < t_end ? t0 + CH : t0; };
+    constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw-buffer format
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, args.T * kD * 2, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, args.T * kDV * 2, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)args.rho, (short)0, args.T * kD * 4, kRawBufferWord3);
+    const unsigned koff = (unsigned)(((toff + n32) * kD + dbase) * 2);
+    const unsigned poff = (unsigned)(((toff + n32) * kD + dbase) * 4);
     auto load_k = [&](int t0, bf16x8& u, float4 (&ph)[2]) {
-      const int tc = t0 + min(toff + n32, min(CH, t_end - t0) - 1);
-      u = *reinterpret_cast<const bf16x8*>(kp + (size_t)tc * kD + dbase);
-      const float* pr = args.rho + (size_t)tc * kD + dbase;
-      ph[0] = *reinterpret_cast<const float4*>(pr);
-      ph[1] = *reinterpret_cast<const float4*>(pr + 4);
+      u = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, koff, t0 * kD * 2, 0));
+      ph[0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prs, poff, t0 * kD * 4, 0));
+      ph[1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(prs, poff + 16, t0 * kD * 4, 0));
     };
     auto load_v = [&](int t0, uint4 (&r)[NV]) {
-      const int nv = min(CH, t_end - t0);
 #pragma unroll
       for (int j = 0; j < NV; j++) {
         const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
-        r[j] = *reinterpret_cast<const uint4*>(vp + (size_t)(t0 + min(toff + row, nv - 1)) * kDV + col);
+        r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             vrs, (unsigned)(((toff + row) * kDV + col) * 2), t0 * kDV * 2, 0));
       }
     };
     auto half_valid = [&](int t0) { return max(0, min(CH, t_end - t0) - toff); };
