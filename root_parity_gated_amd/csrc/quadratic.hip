@@ -58,34 +58,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   const T* vp = v + (size_t)bh * Tn * kDV;
   T* op = out + (size_t)bh * Tn * kDV;
 
-  // ---- Phi(q) operands: K-step j = channel 1 + j/4, dims 16 (j%4) + 8h + i (slot i)
-  Frag QF[MQ][NJ];
-#pragma unroll
-  for (int mq = 0; mq < MQ; mq++) {
-    const int t = min(row0 + 32 * mq + n32, Tn - 1);
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      float cr[8], sr[8], rr[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int a = 16 * m + 8 * h + i;
-        const float om4 = anchor_rev(omega[(size_t)(hd % nph) * kD + a]);
-        featurize1(to_f32(qp[(size_t)t * kD + a]), rho[(size_t)t * kD + a], om4, kr, cr[i], sr[i], rr[i]);
-      }
-      float ch[5][8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        ch[0][i] = cr[i];
-        ch[1][i] = sr[i];
-        ch[2][i] = rr[i];
-        ch[3][i] = rr[i] * cr[i];
-        ch[4][i] = rr[i] * sr[i];
-      }
-#pragma unroll
-      for (int c = 0; c < 5; c++) QF[mq][4 * c + m] = pack8f<T>(ch[c]);
-    }
-  }
-
   // ---- key blocks: staged Phi(K) (channels 1..5) and V, double-buffered.  A block is KB rows of NF
   // features and KB rows of d_v values: exactly KPT + VPT 16-byte pieces per thread, whose offsets do
   // not depend on the block.
@@ -140,7 +112,35 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     zero16(num[mq][1]);
     rs[mq] = 0.0f;
   }
-  fetch(0);
+  fetch(0);  // in flight while the queries are featurized
+  // ---- Phi(q) operands: K-step j = channel 1 + j/4, dims 16 (j%4) + 8h + i (slot i)
+  Frag QF[MQ][NJ];
+#pragma unroll
+  for (int mq = 0; mq < MQ; mq++) {
+    const int t = min(row0 + 32 * mq + n32, Tn - 1);
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      float cr[8], sr[8], rr[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int a = 16 * m + 8 * h + i;
+        const float om4 = anchor_rev(omega[(size_t)(hd % nph) * kD + a]);
+        featurize1(to_f32(qp[(size_t)t * kD + a]), rho[(size_t)t * kD + a], om4, kr, cr[i], sr[i], rr[i]);
+      }
+      float ch[5][8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        ch[0][i] = cr[i];
+        ch[1][i] = sr[i];
+        ch[2][i] = rr[i];
+        ch[3][i] = rr[i] * cr[i];
+        ch[4][i] = rr[i] * sr[i];
+      }
+#pragma unroll
+      for (int c = 0; c < 5; c++) QF[mq][4 * c + m] = pack8f<T>(ch[c]);
+    }
+  }
+
   stash(0);
   if (nkb > 1) fetch(1);
   __syncthreads();
