@@ -144,8 +144,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   stash(0);
   if (nkb > 1) fetch(1);
   __syncthreads();
-  for (int kb = 0; kb < nkb; kb++) {
-    const int buf = kb & 1;
+  // One key block.  The loop below alternates the two buffers explicitly, so each copy of this body names
+  // its buffer at compile time and its LDS accesses take immediate offsets.
+  auto step = [&](auto B, int kb) {
+    constexpr int buf = decltype(B)::value;
     const T* Ks = reinterpret_cast<const T*>(smem + buf * G::buf_bytes);
     const T* Vs = reinterpret_cast<const T*>(smem + buf * G::buf_bytes + G::k_bytes);
     const int s0 = kb * KB;
@@ -229,6 +231,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
       if (kb + 2 < nkb) fetch(kb + 2);
     }
     __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(std::integral_constant<int, 0>(), kb);
+    if (kb + 1 >= nkb) break;
+    step(std::integral_constant<int, 1>(), kb + 1);
   }
 
   // ---- o = num / (den + eps): lane (query n32, half h) holds value rows 32 vt + 8 j + 4 h + i4
