@@ -45,6 +45,15 @@ __device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& 
 #pragma unroll
   for (int i = 0; i < 8; i++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
 }
+// acc = a b + c (the accumulator starts from c instead of its own value)
+__device__ __forceinline__ void mma32c(f32x16& acc, const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32c(f32x16& acc, const f32x8& a, const f32x8& b, const f32x16& c) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+#pragma unroll
+  for (int i = 1; i < 8; i++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+}
 __device__ __forceinline__ void zero16(f32x16& a) {
 #pragma unroll
   for (int i = 0; i < 16; i++) a[i] = 0.0f;

@@ -26,7 +26,9 @@ struct QGeom {
   static constexpr int NF = kF - kD;                  // staged features: channels 1..5
   static constexpr int NJ = NF / 16;                  // K-steps of the score product
   static constexpr int KP = NF + 16 / (int)sizeof(T); // Phi(K) tile pitch (elements)
-  static constexpr int VP = kDV + 16 / (int)sizeof(T);
+  // V tile pitch: bf16 rows of 160 bytes (40 banks apart, 8 mod 32), so the four token rows that 16 lanes
+  // of a transposing read cover (eight banks each) fall on disjoint banks; fp32 rows 4 words apart
+  static constexpr int VP = kDV + (sizeof(T) == 2 ? 16 : 4);
   static constexpr int k_bytes = KB * KP * (int)sizeof(T);
   static constexpr int v_bytes = KB * VP * (int)sizeof(T);
   static constexpr int buf_bytes = k_bytes + v_bytes;
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   typedef typename FragT<T>::type Frag;
   constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n32 = l & 31;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
   // heaviest (latest) query blocks first across all sequences
   const int qb = nqb - 1 - (int)(blockIdx.x / BH);
   const int bh = (int)(blockIdx.x % BH);
@@ -66,7 +68,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   const int last_row = min(Tn - 1, qb * G::QROWS + G::QROWS - 1);
   const int nkb = last_row / KB + 1;
   const int my_last = min(Tn - 1, row0 + 32 * MQ - 1);
-  u32x4 pf[KPT + VPT];
+  // this wave's last key block: the only one that can reach past one of its queries
+  const int lastb = my_last / KB;
+  u32x4 pk[KPT], pv[VPT];
   auto krow_of = [&](int p) { return (tid + 256 * p) / (NF / EL); };
   auto kcol_of = [&](int p) { return ((tid + 256 * p) % (NF / EL)) * EL; };
   auto vrow_of = [&](int p) { return (tid + 256 * p) / (kDV / EL); };
@@ -74,34 +78,43 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   // This thread's pieces of key block kb -> registers, through buffer loads: the block's descriptor starts
   // at its first row and covers the rows up to the sequence's end, so the hardware's range check returns
   // zeros for rows past the end, and each piece's offset from the descriptor's start is fixed per thread
-  // (no address arithmetic per block).  Descriptor word 3: the gfx9-family raw-buffer format.
+  // (no address arithmetic per block).  Descriptor word 3: the gfx9-family raw-buffer format.  Callers
+  // fetch only blocks kb < nkb, whose first row lies inside the sequence.
   unsigned koff[KPT], voff[VPT];
 #pragma unroll
   for (int p = 0; p < KPT; p++) koff[p] = (unsigned)((krow_of(p) * kF + kcol_of(p)) * (int)sizeof(T));
 #pragma unroll
   for (int p = 0; p < VPT; p++) voff[p] = (unsigned)((vrow_of(p) * kDV + vcol_of(p)) * (int)sizeof(T));
   constexpr int kRawBufferWord3 = 0x00020000;
-  auto fetch = [&](int kb) {
+  auto fetch_k = [&](int kb, u32x4 (&dst)[KPT]) {
     const int s0 = kb * KB;
     // Phi(K) rows start at channel 1 (kp skips channel 0), so the last row ends kD elements short of kF
     const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kp + (size_t)s0 * kF), (short)0, (int)(((Tn - s0) * kF - kD) * (int)sizeof(T)), kRawBufferWord3);
+#pragma unroll
+    for (int p = 0; p < KPT; p++) dst[p] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff[p], 0, 0);
+  };
+  auto fetch_v = [&](int kb) {
+    const int s0 = kb * KB;
     const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vp + (size_t)s0 * kDV), (short)0, (int)((Tn - s0) * kDV * (int)sizeof(T)), kRawBufferWord3);
 #pragma unroll
-    for (int p = 0; p < KPT; p++) pf[p] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff[p], 0, 0);
-#pragma unroll
-    for (int p = 0; p < VPT; p++) pf[KPT + p] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff[p], 0, 0);
+    for (int p = 0; p < VPT; p++) pv[p] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff[p], 0, 0);
   };
-  auto stash = [&](int buf) {  // registers -> LDS buffer
-    T* Ks = reinterpret_cast<T*>(smem + buf * G::buf_bytes);
-    T* Vs = reinterpret_cast<T*>(smem + buf * G::buf_bytes + G::k_bytes);
+  // LDS: two Phi(K) slots, then two V slots.  Key block kb lives in K slot kb % 2 and V slot kb % 2.
+  auto kslot = [&](int s) { return reinterpret_cast<T*>(smem + s * G::k_bytes); };
+  auto vslot = [&](int s) { return reinterpret_cast<T*>(smem + 2 * G::k_bytes + s * G::v_bytes); };
+  auto stash_k = [&](int s, const u32x4 (&src)[KPT]) {
+    T* Ks = kslot(s);
 #pragma unroll
     for (int p = 0; p < KPT; p++)
-      *reinterpret_cast<u32x4*>(__builtin_assume_aligned(Ks + krow_of(p) * KP + kcol_of(p), 16)) = pf[p];
+      *reinterpret_cast<u32x4*>(__builtin_assume_aligned(Ks + krow_of(p) * KP + kcol_of(p), 16)) = src[p];
+  };
+  auto stash_v = [&](int s) {
+    T* Vs = vslot(s);
 #pragma unroll
     for (int p = 0; p < VPT; p++)
-      *reinterpret_cast<u32x4*>(__builtin_assume_aligned(Vs + vrow_of(p) * VP + vcol_of(p), 16)) = pf[KPT + p];
+      *reinterpret_cast<u32x4*>(__builtin_assume_aligned(Vs + vrow_of(p) * VP + vcol_of(p), 16)) = pv[p];
   };
 
   f32x16 num[MQ][2];
@@ -112,7 +125,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     zero16(num[mq][1]);
     rs[mq] = 0.0f;
   }
-  fetch(0);  // in flight while the queries are featurized
+  // in flight while the queries are featurized
+  u32x4 pk1[KPT];
+  fetch_k(0, pk);
+  fetch_v(0);
+  if (nkb > 1) fetch_k(1, pk1);
   // ---- Phi(q) operands: K-step j = channel 1 + j/4, dims 16 (j%4) + 8h + i (slot i)
   Frag QF[MQ][NJ];
 #pragma unroll
@@ -141,97 +158,156 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     }
   }
 
-  stash(0);
-  if (nkb > 1) fetch(1);
+  stash_k(0, pk);
+  stash_v(0);
+  if (nkb > 1) stash_k(1, pk1);
+  if (nkb > 2) fetch_k(2, pk);
+  if (nkb > 1) fetch_v(1);
   __syncthreads();
-  // One key block.  The loop below alternates the two buffers explicitly, so each copy of this body names
-  // its buffer at compile time and its LDS accesses take immediate offsets.
-  auto step = [&](auto B, int kb) {
-    constexpr int buf = decltype(B)::value;
-    const T* Ks = reinterpret_cast<const T*>(smem + buf * G::buf_bytes);
-    const T* Vs = reinterpret_cast<const T*>(smem + buf * G::buf_bytes + G::k_bytes);
+
+  // Score tiles of two consecutive key blocks, indexed by block parity: A^T[s][t] (rows = keys, cols =
+  // queries) in MFMA accumulator layout, lane (query n32, half h) holding keys 8(i/4) + 4h + i%4.
+  f32x16 at[2][MQ];
+  // Channel 0 (the constant 1 in both feature maps) adds exactly d to every score: the first MFMA of each
+  // tile starts from this splat instead of from zero.  (The empty asm keeps it in registers, so it is not
+  // rebuilt for every tile.)
+  f32x16 c0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) c0[i] = (float)kD;
+  asm volatile("" : "+v"(c0));
+  // weights of one score tile (kappa^p; the 1 / c^p of the pages' weights cancels against the scaled
+  // epsilon of the normalisation)
+  auto power = [&](float a) { return P == 2 ? a * a : a; };
+  // the weights of block kb (score tile sc, V slot vs) times V, masked where the block reaches past a query
+  auto weigh = [&](const f32x16 (&sc)[MQ], const T* Vs, int kb) {
     const int s0 = kb * KB;
-    if (s0 <= my_last) {
-      // score tiles A^T[s][t] (rows = keys s0 + row, cols = queries); channel 0 (d products 1 * 1)
-      // comes in as 16 products 1 * 4 from one MFMA (bf16) or as the initial value (fp32)
-      f32x16 at[MQ];
+    const bool diag = s0 + KB - 1 > row0;
 #pragma unroll
-      for (int mq = 0; mq < MQ; mq++) {
-        if constexpr (sizeof(T) == 2) {
-          const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                               (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-          const bf16x8 fours = {(__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f,
-                                (__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f, (__bf16)4.0f};
-          static_assert(kD == 64, "channel 0 folded as 16 x 4");
-          zero16(at[mq]);
-          mma32(at[mq], ones, fours);
-        } else {
+    for (int mq = 0; mq < MQ; mq++) {
+      const int tq = row0 + 32 * mq + n32;  // this lane's query
+      float wv[16];
 #pragma unroll
-          for (int i = 0; i < 16; i++) at[mq][i] = (float)kD;
+      for (int i = 0; i < 16; i++) {
+        // (an empty asm keeps the compiler from hoisting these powers above the branch that leads
+        // here, where the other path forms them again between its MFMAs)
+        float a = sc[mq][i];
+        asm volatile("" : "+v"(a));
+        wv[i] = power(a);
+      }
+      if (diag) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int s = s0 + 8 * (i >> 2) + 4 * h + (i & 3);
+          wv[i] = (s > tq) ? 0.0f : wv[i];
         }
       }
-      const T* krow = Ks + n32 * KP + 8 * h;
-      auto ldA = [&](int j) {
-        Frag A;
-        if constexpr (sizeof(T) == 2) {
-          A = *reinterpret_cast<const Frag*>(krow + 16 * j);
-        } else {
+      float lo[8], hi8[8];
 #pragma unroll
-          for (int i = 0; i < 8; i++) A[i] = krow[16 * j + i];
-        }
-        return A;
-      };
-      // Phi(K) fragments are read PD K-steps ahead of their MFMA, so LDS latency stays hidden
-      constexpr int PD = 6;
-      Frag Ar[PD];
-#pragma unroll
-      for (int j = 0; j < PD; j++) Ar[j] = ldA(j);
-      __builtin_amdgcn_sched_barrier(0);  // (fences keep the compiler from shortening the distance)
-#pragma unroll
-      for (int j = 0; j < NJ; j++) {
-        const Frag A = Ar[j % PD];
-#pragma unroll
-        for (int mq = 0; mq < MQ; mq++) mma32(at[mq], A, QF[mq][j]);
-        if (j + PD < NJ) Ar[j % PD] = ldA(j + PD);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 8; i++) {
+        lo[i] = wv[i];
+        hi8[i] = wv[8 + i];
       }
-      // the block reaches past a query of the wave only near the diagonal: mask there alone
-      const bool diag = s0 + KB - 1 > row0;
+      const Frag P0 = pack8f<T>(lo), P1 = pack8f<T>(hi8);
+      rs[mq] = frag_sum(P1, frag_sum(P0, rs[mq]));
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++) {
+        mma32(num[mq][vt], lds_tokfrag(Vs, VP, 0, 32 * vt, l), P0);
+        mma32(num[mq][vt], lds_tokfrag(Vs, VP, 16, 32 * vt, l), P1);
+      }
+    }
+  };
+  // Score tiles of key block kb (K slot kb % 2) into at[kb % 2].  With `prev`, the weights of block kb - 1
+  // (never a block that reaches past a query: only a wave's last block does) are formed in the same
+  // instruction stream: powered, packed and summed between the score MFMAs, then multiplied with their V
+  // (V slot (kb - 1) % 2), so the matrix cores have independent work while that VALU runs.
+  auto scores = [&](auto Par, auto Prev) {
+    constexpr int par = decltype(Par)::value;
+    constexpr bool prev = decltype(Prev)::value;
+    const T* Ks = kslot(par);
+    const T* Vs = vslot(par ^ 1);
+    f32x16(&cur)[MQ] = at[par];
+    const f32x16(&old)[MQ] = at[par ^ 1];
+    const T* krow = Ks + n32 * KP + 8 * h;
+    auto ldA = [&](int j) {
+      Frag A;
+      if constexpr (sizeof(T) == 2) {
+        A = *reinterpret_cast<const Frag*>(krow + 16 * j);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) A[i] = krow[16 * j + i];
+      }
+      return A;
+    };
+    // Phi(K) fragments are read PD K-steps ahead of their MFMA, so LDS latency stays hidden
+    constexpr int PD = 4;
+    static_assert(NJ >= 18, "the previous block's work is spread over the first 18 K-steps");
+    Frag Ar[PD];
+#pragma unroll
+    for (int j = 0; j < PD; j++) Ar[j] = ldA(j);
+    float wv[MQ][16];
+    Frag P0[MQ], P1[MQ], Vf[2][2];
+    __builtin_amdgcn_sched_barrier(0);  // (fences keep the compiler from shortening the distances)
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const Frag A = Ar[j % PD];
 #pragma unroll
       for (int mq = 0; mq < MQ; mq++) {
-        const int tq = row0 + 32 * mq + n32;  // this lane's query
-        // weight kappa^p; the 1 / c^p of the pages' weights cancels against the scaled epsilon below
-        float wv[16];
+        if (j == 0)
+          mma32c(cur[mq], A, QF[mq][0], c0);
+        else
+          mma32(cur[mq], A, QF[mq][j]);
+      }
+      if (j + PD < NJ) Ar[j % PD] = ldA(j + PD);
+      if constexpr (prev) {
+        // K-steps 0..7: powers; 8, 9: packing; 10: the V fragments; 11: row sums; 12..15: V^T P
+        if (j < 8) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) wv[i] = P == 2 ? at[mq][i] * at[mq][i] : at[mq][i];
-        if (diag) {
-#pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const int s = s0 + 8 * (i >> 2) + 4 * h + (i & 3);
-            wv[i] = (s > tq) ? 0.0f : wv[i];
+          for (int mq = 0; mq < MQ; mq++) {
+            wv[mq][2 * j] = power(old[mq][2 * j]);
+            wv[mq][2 * j + 1] = power(old[mq][2 * j + 1]);
           }
-        }
-        float lo[8], hi8[8];
+        } else if (j == 8 || j == 9) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-          lo[i] = wv[i];
-          hi8[i] = wv[8 + i];
-        }
-        const Frag P0 = pack8f<T>(lo), P1 = pack8f<T>(hi8);
-        rs[mq] = frag_sum(P1, frag_sum(P0, rs[mq]));
+          for (int mq = 0; mq < MQ; mq++) {
+            float x[8];
 #pragma unroll
-        for (int vt = 0; vt < 2; vt++) {
-          mma32(num[mq][vt], lds_tokfrag(Vs, VP, 0, 32 * vt, l), P0);
-          mma32(num[mq][vt], lds_tokfrag(Vs, VP, 16, 32 * vt, l), P1);
+            for (int i = 0; i < 8; i++) x[i] = wv[mq][8 * (j - 8) + i];
+            (j == 8 ? P0[mq] : P1[mq]) = pack8f<T>(x);
+          }
+        } else if (j == 10) {
+#pragma unroll
+          for (int vt = 0; vt < 2; vt++) {
+            Vf[vt][0] = lds_tokfrag(Vs, VP, 0, 32 * vt, l);
+            Vf[vt][1] = lds_tokfrag(Vs, VP, 16, 32 * vt, l);
+          }
+        } else if (j == 11) {
+#pragma unroll
+          for (int mq = 0; mq < MQ; mq++) rs[mq] = frag_sum(P1[mq], frag_sum(P0[mq], rs[mq]));
+        } else if (j >= 12 && j < 16) {
+          const int vt = (j - 12) >> 1, hf = (j - 12) & 1;
+#pragma unroll
+          for (int mq = 0; mq < MQ; mq++) mma32(num[mq][vt], Vf[vt][hf], hf ? P1[mq] : P0[mq]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kb + 1 < nkb) {
-      stash(buf ^ 1);  // the other buffer was last read before the previous barrier
-      if (kb + 2 < nkb) fetch(kb + 2);
-    }
+  };
+  // One step per key block kb: the scores of block kb + 1 together with the weights of block kb, or, on
+  // the wave's last block, its masked weights alone; then the staging of K(kb + 2) and V(kb + 1), whose
+  // slots were last read before the previous barrier.  The loop below alternates the parities
+  // explicitly, so each copy of this body names its slots and tiles at compile time.
+  auto step = [&](auto Par, int kb) {
+    constexpr int par = decltype(Par)::value;
+    if (kb < lastb) scores(std::integral_constant<int, par ^ 1>(), std::true_type());
+    if (kb == lastb) weigh(at[par], vslot(par), kb);
+    if (kb + 2 < nkb) stash_k(par, pk);
+    if (kb + 1 < nkb) stash_v(par ^ 1);
+    if (kb + 3 < nkb) fetch_k(kb + 3, pk);
+    if (kb + 2 < nkb) fetch_v(kb + 2);
     __syncthreads();
   };
+  scores(std::integral_constant<int, 0>(), std::false_type());  // every wave has key block 0
+  __syncthreads();  // K slot 0 is restaged in the first step
   for (int kb = 0; kb < nkb; kb += 2) {
     step(std::integral_constant<int, 0>(), kb);
     if (kb + 1 >= nkb) break;
