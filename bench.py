@@ -189,8 +189,10 @@ def cpu_baseline(w, budget_s=20.0):
                       f"({dt:.1f} s wall)"}
 
 
-def bench_decode(torch, rpg, si, batch, steps_timed, warmup):
-    """fp32 decode: 144 head-states per sequence, state filled by 4096 tokens, then sequential steps."""
+def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False):
+    """fp32 decode: 144 head-states per sequence, state filled by 4096 tokens, then sequential steps.
+    With `positions`, each sequence continues at its own position (4096 plus a seeded offset below 4096)
+    through the per-head-state entry point; the position arrays of every step are built before timing."""
     w = si.DECODE
     nh, fill = w.H, w.T
     N = batch * nh
@@ -212,12 +214,22 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup):
                                     rpg.Params(omega=p.omega), S=S[i:j].unsqueeze(0), z=z[i:j].unsqueeze(0))
     del fq, fk, fv
     out = torch.empty((N, DV), device="cuda")
+    posv = None
+    if positions:
+        seq_off = np.repeat(si.decode_positions(w.seed + 7 * batch, batch, 0, fill), nh)
+        posv = torch.from_numpy(fill + seq_off[None, :] + np.arange(steps_timed + warmup)[:, None]).cuda()
+
+    def dec(i, S_, z_):
+        if posv is None:
+            rpg.sanatan_decode_step(sq[i], sk[i], sv[i], fill + i, p, S_, z_, out)
+        else:
+            rpg.sanatan_decode_step_positions(sq[i], sk[i], sv[i], posv[i], p, S_, z_, out)
+
     torch.cuda.synchronize()
     step = [0]
 
     def one():
-        i = step[0]
-        rpg.sanatan_decode_step(sq[i], sk[i], sv[i], fill + i, p, S, z, out)
+        dec(step[0], S, z)
         step[0] += 1
 
     ms = timed_loop(torch, one, steps_timed, warmup)
@@ -230,7 +242,7 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup):
         n_cap = min(steps_timed, 256)
         with torch.cuda.graph(graph, stream=gstream):
             for i in range(n_cap):
-                rpg.sanatan_decode_step(sq[i], sk[i], sv[i], fill + i, p, S2, z2, out)
+                dec(i, S2, z2)
         graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -259,7 +271,8 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup):
         "roofline": {"bound": "hbm", "achieved": bytes_step / (best_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": bytes_step / (best_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "note": ("state (14.4 MB) is resident in the 256 MB Infinity Cache between steps" if batch == 1
-                 else "state exceeds the Infinity Cache; HBM-bound"),
+                 else "state exceeds the Infinity Cache; HBM-bound")
+                + ("; one position per sequence (sanatan_decode_step_positions)" if positions else ""),
         "rmw_stream_reference_TBps": ref_tbs,
     }
 
@@ -393,6 +406,11 @@ def main():
         for b in (1, 64):
             log(f"decode batch {b}")
             extras[f"decode_batch{b}"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16)
+            if b > 1:
+                log(f"decode batch {b}, one position per sequence")
+                extras[f"decode_batch{b}_positions"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16,
+                                                                    positions=True)
+                log(f"decode batch {b}, positions: {extras[f'decode_batch{b}_positions']['us_per_token']:.2f} us/token")
             log(f"decode batch {b}: {extras[f'decode_batch{b}']['us_per_token']:.2f} us/token")
         wl = si.LONG
         log(f"long prefill {wl.name}")

@@ -118,6 +118,20 @@ sanatan_status sanatan_decode_step(const float* q, const float* k, const float* 
                                    const sanatan_params* params, float* S, float* z, float* out,
                                    hipStream_t stream);
 
+/*
+ * sanatan_decode_step_positions -- sanatan_decode_step with one position per head-state, for a batch
+ * whose sequences have reached different lengths.  The position of a token sets the rotation
+ * theta + t lambda_a of both its feature maps ([N] §2.2), so each head-state's phase comes from its
+ * own entry.
+ *   pos  : device [N] int64, the position of head-state i's token (any value the single-position
+ *          call accepts); read only.
+ *   Everything else as sanatan_decode_step.  With every entry equal to one position the results are
+ *   bitwise those of sanatan_decode_step at that position.  A null pos is INVALID_ARG.
+ */
+sanatan_status sanatan_decode_step_positions(const float* q, const float* k, const float* v, int N,
+                                             const int64_t* pos, const sanatan_params* params, float* S,
+                                             float* z, float* out, hipStream_t stream);
+
 /* Workspace bytes sanatan_quadratic_ref_p2 needs (0 on invalid sizes). */
 size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params);
 

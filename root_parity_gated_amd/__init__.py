@@ -66,6 +66,8 @@ def lib():
         L.sanatan_prefill_chunked.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp, sz, vp]
         L.sanatan_decode_step.restype = i32
         L.sanatan_decode_step.argtypes = [vp, vp, vp, i32, i64, pp, vp, vp, vp, vp]
+        L.sanatan_decode_step_positions.restype = i32
+        L.sanatan_decode_step_positions.argtypes = [vp, vp, vp, i32, vp, pp, vp, vp, vp, vp]
         L.sanatan_quadratic_workspace_bytes.restype = sz
         L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_quadratic_ref_p2.restype = i32
@@ -76,7 +78,8 @@ def lib():
 
 EXPORTED = [
     "sanatan_state_bytes", "sanatan_status_string", "sanatan_featurize", "sanatan_prefill_workspace_bytes",
-    "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_quadratic_workspace_bytes",
+    "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_decode_step_positions",
+    "sanatan_quadratic_workspace_bytes",
     "sanatan_quadratic_ref_p2",
 ]
 
@@ -203,6 +206,25 @@ def sanatan_decode_step(q, k, v, pos: int, params: Params, S, z, out=None):
     p = params.struct()
     _check(lib().sanatan_decode_step(_ptr(q), _ptr(k), _ptr(v), N, int(pos), ctypes.byref(p), _ptr(S), _ptr(z),
                                      _ptr(out), _stream()), "sanatan_decode_step")
+    return out
+
+
+def sanatan_decode_step_positions(q, k, v, pos, params: Params, S, z, out=None):
+    """As sanatan_decode_step, with pos a device int64 tensor [N]: one position per head-state."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("S", S), ("z", z)):
+        _check_tensor(t, name, dtypes=("float32",))
+    _check_tensor(pos, "pos", dtypes=("int64",))
+    N = q.shape[0]
+    if pos.numel() != N:
+        raise ValueError(f"pos has {pos.numel()} entries for {N} head-states")
+    if out is None:
+        out = torch.empty((N, v.shape[-1]), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", dtypes=("float32",))
+    p = params.struct()
+    _check(lib().sanatan_decode_step_positions(_ptr(q), _ptr(k), _ptr(v), N, _ptr(pos), ctypes.byref(p), _ptr(S),
+                                               _ptr(z), _ptr(out), _stream()), "sanatan_decode_step_positions")
     return out
 
 

@@ -100,7 +100,16 @@ sanatan_status sanatan_decode_step(const float* q, const float* k, const float* 
   if (!q || !k || !v || !S || !z || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
-  return hip_status(launch_decode_step(q, k, v, N, pos, consts(params), S, z, out, stream));
+  return hip_status(launch_decode_step(q, k, v, N, pos, nullptr, consts(params), S, z, out, stream));
+}
+
+sanatan_status sanatan_decode_step_positions(const float* q, const float* k, const float* v, int N,
+                                             const int64_t* pos, const sanatan_params* params, float* S, float* z,
+                                             float* out, hipStream_t stream) {
+  if (!q || !k || !v || !pos || !S || !z || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  return hip_status(launch_decode_step(q, k, v, N, 0, pos, consts(params), S, z, out, stream));
 }
 
 size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params) {

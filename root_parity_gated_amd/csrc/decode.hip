@@ -2,6 +2,8 @@
 //
 // SANATAN reading notes §2.7: S_t = S_{t-1} + Phi(k_t) v_t^T, z_t = z_{t-1} + Phi(k_t),
 // o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c eps) -- the state is written before it is read.
+// The token's absolute position t sets the rotation of both feature maps (§2.2); it is one position for
+// all head-states, or one per head-state (sequences of a batch at different lengths).
 //
 // HBM-bound: 2 x 99,840 B of state move per head-state and token, against 0.5 flop/byte.
 // One 512-thread workgroup owns one head-state and streams its S once: each thread holds 12
@@ -24,7 +26,7 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 template <bool NT>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int64_t pos,
-    const float* __restrict__ omega, int nph, double log2_base, float kr, float ceps, float* __restrict__ S,
+    const int64_t* __restrict__ posv, const float* __restrict__ omega, int nph, double log2_base, float kr, float ceps, float* __restrict__ S,
     float* __restrict__ z, float* __restrict__ out) {
   __shared__ float fk[kF];
   __shared__ float fq[kF];
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const int a = tid & (kD - 1);
     const float u = (tid < kD) ? k[(size_t)i * kD + a] : q[(size_t)i * kD + a];
     const float om4 = anchor_rev(omega[(size_t)(i % nph) * kD + a]);
-    const float rho = phase_rev(pos, a, log2_base);
+    const float rho = phase_rev(posv ? posv[i] : pos, a, log2_base);
     float cr, sr, r;
     featurize1(u, rho, om4, kr, cr, sr, r);
     float* dst = (tid < kD) ? fk : fq;
@@ -108,14 +110,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 }
 
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
-                              const MethodConsts& mc, float* S, float* z, float* out, hipStream_t stream) {
+                              const int64_t* posv, const MethodConsts& mc, float* S, float* z, float* out, hipStream_t stream) {
   // states above 128 MB (half of the 256 MB last-level cache) are streamed
   const bool stream_state = (size_t)N * kStateFloats * sizeof(float) > ((size_t)128 << 20);
   if (stream_state)
-    hipLaunchKernelGGL(decode_step_kernel<true>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, mc.omega,
+    hipLaunchKernelGGL(decode_step_kernel<true>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega,
                        mc.nph, mc.log2_base, mc.kr, mc.ceps, S, z, out);
   else
-    hipLaunchKernelGGL(decode_step_kernel<false>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, mc.omega,
+    hipLaunchKernelGGL(decode_step_kernel<false>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega,
                        mc.nph, mc.log2_base, mc.kr, mc.ceps, S, z, out);
   return hipGetLastError();
 }

@@ -92,6 +92,11 @@ def decode_inputs_numpy(seed: int, n_heads: int, fill: int, steps: int, d: int =
     return omega, (fq, fk, fv), (sq, sk, sv)
 
 
+def decode_positions(seed: int, n: int, lo: int = 0, hi: int = 1 << 20) -> np.ndarray:
+    """Per head-state positions for a batch of sequences at different lengths: int64 [n], uniform in [lo, hi)."""
+    return np.random.default_rng(seed).integers(lo, hi, size=n, dtype=np.int64)
+
+
 def decode_inputs_torch(seed: int, batch: int, n_heads: int, fill: int, steps: int, device, d: int = D_HEAD,
                         dv: int = D_HEAD):
     """Large-batch decode inputs drawn on `device` with torch's seeded generator.

@@ -93,6 +93,12 @@ def test_featurize_decode_quadratic_validation(L):
     assert L.sanatan_decode_step(FAKE, FAKE, FAKE, 4, 0, ctypes.byref(p), None, FAKE, FAKE,
                                  None) == rpg.SANATAN_ERR_INVALID_ARG
     assert L.sanatan_decode_step(FAKE, FAKE, FAKE, 4, 0, None, FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    dp = L.sanatan_decode_step_positions
+    assert dp(FAKE, FAKE, FAKE, 4, None, ctypes.byref(p), FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert dp(FAKE, FAKE, FAKE, 0, FAKE, ctypes.byref(p), FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert dp(FAKE, FAKE, FAKE, 4, FAKE, ctypes.byref(p), FAKE, None, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert dp(FAKE, FAKE, FAKE, 4, FAKE, ctypes.byref(params(d=32)), FAKE, FAKE, FAKE,
+              None) == rpg.SANATAN_ERR_UNSUPPORTED
     for pe in (0, 3):
         assert L.sanatan_quadratic_ref_p2(FAKE, FAKE, FAKE, 1, 1, 1, 64, pe, 0, ctypes.byref(p), FAKE, FAKE, 1 << 40,
                                           None) == rpg.SANATAN_ERR_INVALID_ARG
