@@ -189,10 +189,12 @@ def cpu_baseline(w, budget_s=20.0):
                       f"({dt:.1f} s wall)"}
 
 
-def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False):
+def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False, compact=False):
     """fp32 decode: 144 head-states per sequence, state filled by 4096 tokens, then sequential steps.
     With `positions`, each sequence continues at its own position (4096 plus a seeded offset below 4096)
-    through the per-head-state entry point; the position arrays of every step are built before timing."""
+    through the per-head-state entry point; the position arrays of every step are built before timing.
+    With `compact`, the filled state is converted to the compact layout ((5d+1) rows: the d equal channel-0
+    rows kept once) and the compact decode is timed on its own bytes."""
     w = si.DECODE
     nh, fill = w.H, w.T
     N = batch * nh
@@ -213,6 +215,9 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False):
         rpg.sanatan_prefill_chunked(fq[i:j].unsqueeze(0), fk[i:j].unsqueeze(0), fv[i:j].unsqueeze(0), 64,
                                     rpg.Params(omega=p.omega), S=S[i:j].unsqueeze(0), z=z[i:j].unsqueeze(0))
     del fq, fk, fv
+    if compact:
+        S, z = rpg.sanatan_state_compact(S, z)
+        torch.cuda.synchronize()
     out = torch.empty((N, DV), device="cuda")
     posv = None
     if positions:
@@ -220,7 +225,10 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False):
         posv = torch.from_numpy(fill + seq_off[None, :] + np.arange(steps_timed + warmup)[:, None]).cuda()
 
     def dec(i, S_, z_):
-        if posv is None:
+        if compact:
+            rpg.sanatan_decode_step_compact(sq[i], sk[i], sv[i], fill + i if posv is None else posv[i], p, S_, z_,
+                                            out)
+        elif posv is None:
             rpg.sanatan_decode_step(sq[i], sk[i], sv[i], fill + i, p, S_, z_, out)
         else:
             rpg.sanatan_decode_step_positions(sq[i], sk[i], sv[i], posv[i], p, S_, z_, out)
@@ -254,7 +262,8 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False):
     except Exception as ex:  # graph capture is an optional view of the same kernel
         g_ms = None
         print(f"# decode graph capture skipped: {ex}", file=sys.stderr)
-    bytes_step = N * (2 * STATE_BYTES + 3 * D * 4 + DV * 4)
+    state_bytes = rpg.sanatan_compact_state_bytes(D, DV) if compact else STATE_BYTES
+    bytes_step = N * (2 * state_bytes + 3 * D * 4 + DV * 4)
     best_ms = min(ms, g_ms) if g_ms else ms
     # reference for what an in-place read-and-write-back stream of the same state bytes reaches on this
     # device: torch's vectorized in-place add over the state tensor (one read and one write per element)
@@ -272,7 +281,9 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False):
                      "unit": "GB/s", "frac": bytes_step / (best_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "note": ("state (14.4 MB) is resident in the 256 MB Infinity Cache between steps" if batch == 1
                  else "state exceeds the Infinity Cache; HBM-bound")
-                + ("; one position per sequence (sanatan_decode_step_positions)" if positions else ""),
+                + ("; one position per sequence (sanatan_decode_step_positions)" if positions else "")
+                + ("; compact state, (5d+1) x (d_v+1) floats per head-state: roofline on its own bytes, not on"
+                   " the 6d state's" if compact else ""),
         "rmw_stream_reference_TBps": ref_tbs,
     }
 
@@ -411,6 +422,10 @@ def main():
                 extras[f"decode_batch{b}_positions"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16,
                                                                     positions=True)
                 log(f"decode batch {b}, positions: {extras[f'decode_batch{b}_positions']['us_per_token']:.2f} us/token")
+                log(f"decode batch {b}, compact state")
+                extras[f"decode_batch{b}_compact"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16,
+                                                                  compact=True)
+                log(f"decode batch {b}, compact: {extras[f'decode_batch{b}_compact']['us_per_token']:.2f} us/token")
             log(f"decode batch {b}: {extras[f'decode_batch{b}']['us_per_token']:.2f} us/token")
         wl = si.LONG
         log(f"long prefill {wl.name}")

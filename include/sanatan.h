@@ -132,6 +132,43 @@ sanatan_status sanatan_decode_step_positions(const float* q, const float* k, con
                                              const int64_t* pos, const sanatan_params* params, float* S,
                                              float* z, float* out, hipStream_t stream);
 
+/*
+ * Compact recurrent state.  Channel 0 of both feature maps is the constant 1 ([N] §2.3), so the d rows of
+ * S that channel 0 owns all receive the same v_t in every update ([N] §2.7) and stay equal, as do their d
+ * entries of z.  The compact layout keeps them once:
+ *   Sc : [N][5d+1][d_v] fp32, row 0 = the shared channel-0 row, row 1 + (c-1) d + a = full row c d + a
+ *        (channels c = 1..5);
+ *   zc : [N][5d+1] fp32, the same rows.
+ * It holds the same information as a full state whose channel-0 rows are equal (every state the
+ * recurrence builds from a zero or compact start), in 17 % fewer bytes.
+ */
+/* Bytes of one head's compact state: (5d+1) x (d_v+1) floats. */
+size_t sanatan_compact_state_bytes(int d, int d_v);
+
+/*
+ * sanatan_state_compact -- full state (S [N][6d][d_v], z [N][6d]) -> compact (Sc, zc), taking row 0 of the
+ * channel-0 block.  sanatan_state_expand -- compact -> full, writing the shared row into all d channel-0
+ * rows.  Pure copies (bitwise); d = d_v = 64 layouts; source and destination must not overlap.
+ * INVALID_ARG for NULL pointers or N <= 0.
+ */
+sanatan_status sanatan_state_compact(const float* S, const float* z, int N, float* Sc, float* zc,
+                                     hipStream_t stream);
+sanatan_status sanatan_state_expand(const float* Sc, const float* zc, int N, float* S, float* z,
+                                    hipStream_t stream);
+
+/*
+ * sanatan_decode_step_compact -- sanatan_decode_step on the compact state.  A token adds 1 x v to the
+ * shared channel-0 row and 1 to its z entry; the readout weighs that row (and entry) by d, once for each
+ * of the d equal rows it stands for.  The results equal those of the full-state call up to the rounding
+ * of that sum.
+ *   pos, posv : posv NULL -> every head-state at position pos; else device [N] int64, one position per
+ *               head-state (as sanatan_decode_step_positions), and pos is ignored.
+ *   Sc, zc    : the compact state, updated in place.  Everything else as sanatan_decode_step.
+ */
+sanatan_status sanatan_decode_step_compact(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                           const int64_t* posv, const sanatan_params* params, float* Sc,
+                                           float* zc, float* out, hipStream_t stream);
+
 /* Workspace bytes sanatan_quadratic_ref_p2 needs (0 on invalid sizes). */
 size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params);
 

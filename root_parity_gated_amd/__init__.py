@@ -68,6 +68,14 @@ def lib():
         L.sanatan_decode_step.argtypes = [vp, vp, vp, i32, i64, pp, vp, vp, vp, vp]
         L.sanatan_decode_step_positions.restype = i32
         L.sanatan_decode_step_positions.argtypes = [vp, vp, vp, i32, vp, pp, vp, vp, vp, vp]
+        L.sanatan_compact_state_bytes.restype = sz
+        L.sanatan_compact_state_bytes.argtypes = [i32, i32]
+        L.sanatan_state_compact.restype = i32
+        L.sanatan_state_compact.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.sanatan_state_expand.restype = i32
+        L.sanatan_state_expand.argtypes = [vp, vp, i32, vp, vp, vp]
+        L.sanatan_decode_step_compact.restype = i32
+        L.sanatan_decode_step_compact.argtypes = [vp, vp, vp, i32, i64, vp, pp, vp, vp, vp, vp]
         L.sanatan_quadratic_workspace_bytes.restype = sz
         L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_quadratic_ref_p2.restype = i32
@@ -79,6 +87,7 @@ def lib():
 EXPORTED = [
     "sanatan_state_bytes", "sanatan_status_string", "sanatan_featurize", "sanatan_prefill_workspace_bytes",
     "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_decode_step_positions",
+    "sanatan_compact_state_bytes", "sanatan_state_compact", "sanatan_state_expand", "sanatan_decode_step_compact",
     "sanatan_quadratic_workspace_bytes",
     "sanatan_quadratic_ref_p2",
 ]
@@ -225,6 +234,70 @@ def sanatan_decode_step_positions(q, k, v, pos, params: Params, S, z, out=None):
     p = params.struct()
     _check(lib().sanatan_decode_step_positions(_ptr(q), _ptr(k), _ptr(v), N, _ptr(pos), ctypes.byref(p), _ptr(S),
                                                _ptr(z), _ptr(out), _stream()), "sanatan_decode_step_positions")
+    return out
+
+
+COMPACT_ROWS = 5 * 64 + 1  # compact state rows at d = 64: the d equal channel-0 rows kept once
+
+
+def sanatan_compact_state_bytes(d: int = 64, d_v: int = 64) -> int:
+    return int(lib().sanatan_compact_state_bytes(d, d_v))
+
+
+def sanatan_state_compact(S, z, Sc=None, zc=None):
+    """Full state S [...,384,64], z [...,384] -> compact Sc [...,321,64], zc [...,321] (pure copies)."""
+    import torch
+
+    for name, t in (("S", S), ("z", z)):
+        _check_tensor(t, name, dtypes=("float32",))
+    N = S.numel() // (S.shape[-2] * S.shape[-1])
+    if Sc is None:
+        Sc = torch.empty((*S.shape[:-2], COMPACT_ROWS, S.shape[-1]), dtype=torch.float32, device=S.device)
+    if zc is None:
+        zc = torch.empty((*z.shape[:-1], COMPACT_ROWS), dtype=torch.float32, device=z.device)
+    for name, t in (("Sc", Sc), ("zc", zc)):
+        _check_tensor(t, name, dtypes=("float32",))
+    _check(lib().sanatan_state_compact(_ptr(S), _ptr(z), N, _ptr(Sc), _ptr(zc), _stream()), "sanatan_state_compact")
+    return Sc, zc
+
+
+def sanatan_state_expand(Sc, zc, S=None, z=None):
+    """Compact Sc [...,321,64], zc [...,321] -> full S [...,384,64], z [...,384] (pure copies)."""
+    import torch
+
+    for name, t in (("Sc", Sc), ("zc", zc)):
+        _check_tensor(t, name, dtypes=("float32",))
+    N = Sc.numel() // (Sc.shape[-2] * Sc.shape[-1])
+    if S is None:
+        S = torch.empty((*Sc.shape[:-2], 6 * 64, Sc.shape[-1]), dtype=torch.float32, device=Sc.device)
+    if z is None:
+        z = torch.empty((*zc.shape[:-1], 6 * 64), dtype=torch.float32, device=zc.device)
+    for name, t in (("S", S), ("z", z)):
+        _check_tensor(t, name, dtypes=("float32",))
+    _check(lib().sanatan_state_expand(_ptr(Sc), _ptr(zc), N, _ptr(S), _ptr(z), _stream()), "sanatan_state_expand")
+    return S, z
+
+
+def sanatan_decode_step_compact(q, k, v, pos, params: Params, Sc, zc, out=None):
+    """sanatan_decode_step on the compact state; pos is an int (every head-state) or a device int64 tensor [N]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("Sc", Sc), ("zc", zc)):
+        _check_tensor(t, name, dtypes=("float32",))
+    N = q.shape[0]
+    posv = None
+    if isinstance(pos, torch.Tensor):
+        _check_tensor(pos, "pos", dtypes=("int64",))
+        if pos.numel() != N:
+            raise ValueError(f"pos has {pos.numel()} entries for {N} head-states")
+        posv, pos = pos, 0
+    if out is None:
+        out = torch.empty((N, v.shape[-1]), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", dtypes=("float32",))
+    p = params.struct()
+    _check(lib().sanatan_decode_step_compact(_ptr(q), _ptr(k), _ptr(v), N, int(pos),
+                                             _ptr(posv) if posv is not None else None, ctypes.byref(p), _ptr(Sc),
+                                             _ptr(zc), _ptr(out), _stream()), "sanatan_decode_step_compact")
     return out
 
 

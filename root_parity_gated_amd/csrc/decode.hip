@@ -12,6 +12,12 @@
 // When the head-states together exceed what the last-level cache can keep between tokens, the
 // state is streamed with non-temporal loads and stores (caching it would only evict other data);
 // a smaller state (one sequence's 144 head-states: 14.4 MB) stays cache-resident between tokens.
+//
+// Compact state.  Channel 0 of both feature maps is the constant 1 (§2.3), so the d rows of S that
+// channel 0 owns all receive the same v_t and stay equal, and so do their d entries of z.  The compact
+// layout keeps them once: row 0 is the shared channel-0 row, rows 1 .. 5d are channels 1..5 (full rows
+// d .. 6d-1).  A token adds 1 x v to row 0, and the readout weighs row 0 by d (the d equal rows, each read
+// with phi(q) = 1).  (5d+1) x (d_v+1) floats instead of 6d x (d_v+1): 17 % fewer bytes per token.
 #include "launchers.h"
 #include "sanatan_device.h"
 
@@ -23,11 +29,13 @@ constexpr int kDecRows = kDecThreads / 16;  // row groups: 16 threads cover the 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 }  // namespace
 
-template <bool NT>
+template <bool NT, bool Compact>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int64_t pos,
-    const int64_t* __restrict__ posv, const float* __restrict__ omega, int nph, double log2_base, float kr, float ceps, float* __restrict__ S,
-    float* __restrict__ z, float* __restrict__ out) {
+    const int64_t* __restrict__ posv, const float* __restrict__ omega, int nph, double log2_base, float kr,
+    float ceps, float* __restrict__ S, float* __restrict__ z, float* __restrict__ out) {
+  constexpr int R = Compact ? kCompactRows : kF;      // state rows
+  constexpr int MR = (R + kDecRows - 1) / kDecRows;   // row pieces per thread
   __shared__ float fk[kF];
   __shared__ float fq[kF];
   __shared__ float vs[kDV];
@@ -36,33 +44,43 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  float* __restrict__ Si = S + (size_t)i * kF * kDV;
-  float* __restrict__ zi = z + (size_t)i * kF;
+  float* __restrict__ Si = S + (size_t)i * R * kDV;
+  float* __restrict__ zi = z + (size_t)i * R;
 
   // Issue the state loads first so their latency overlaps the feature computation.
   const int cg = tid & 15;  // column group: columns 4cg .. 4cg+3
   const int rg = tid >> 4;  // row group: rows rg + kDecRows m
-  f32x4v rows[kF / kDecRows];
+  f32x4v rows[MR];
 #pragma unroll
-  for (int m = 0; m < kF / kDecRows; m++)
-    rows[m] = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(&Si[(rg + kDecRows * m) * kDV + 4 * cg]))
-                 : *reinterpret_cast<const f32x4v*>(&Si[(rg + kDecRows * m) * kDV + 4 * cg]);
-  const float zr = tid < kF ? zi[tid] : 0.0f;
+  for (int m = 0; m < MR; m++) {
+    const int f = rg + kDecRows * m;
+    const f32x4v* src = reinterpret_cast<const f32x4v*>(&Si[f * kDV + 4 * cg]);
+    if (f < R) rows[m] = NT ? __builtin_nontemporal_load(src) : *src;
+  }
+  const float zr = tid < R ? zi[tid] : 0.0f;
 
   if (tid < 2 * kD) {
     const int a = tid & (kD - 1);
-    const float u = (tid < kD) ? k[(size_t)i * kD + a] : q[(size_t)i * kD + a];
+    const bool is_k = tid < kD;
+    const float u = is_k ? k[(size_t)i * kD + a] : q[(size_t)i * kD + a];
     const float om4 = anchor_rev(omega[(size_t)(i % nph) * kD + a]);
     const float rho = phase_rev(posv ? posv[i] : pos, a, log2_base);
     float cr, sr, r;
     featurize1(u, rho, om4, kr, cr, sr, r);
-    float* dst = (tid < kD) ? fk : fq;
-    dst[0 * kD + a] = 1.0f;
-    dst[1 * kD + a] = cr;
-    dst[2 * kD + a] = sr;
-    dst[3 * kD + a] = r;
-    dst[4 * kD + a] = r * cr;
-    dst[5 * kD + a] = r * sr;
+    float* dst = is_k ? fk : fq;
+    // channel c >= 1 of dim a: row c d + a, or 1 + (c - 1) d + a in the compact layout
+    constexpr int sh = Compact ? 1 - kD : 0;
+    if constexpr (Compact) {
+      // the shared channel-0 row: a key adds 1 x v to it, a query reads it once for each of its d rows
+      if (a == 0) dst[0] = is_k ? 1.0f : (float)kD;
+    } else {
+      dst[a] = 1.0f;
+    }
+    dst[sh + 1 * kD + a] = cr;
+    dst[sh + 2 * kD + a] = sr;
+    dst[sh + 3 * kD + a] = r;
+    dst[sh + 4 * kD + a] = r * cr;
+    dst[sh + 5 * kD + a] = r * sr;
   } else if (tid < 2 * kD + kDV) {
     vs[tid - 2 * kD] = v[(size_t)i * kDV + (tid - 2 * kD)];
   }
@@ -71,22 +89,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   const f32x4v vv = *reinterpret_cast<const f32x4v*>(&vs[4 * cg]);
   f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < kF / kDecRows; m++) {
+  for (int m = 0; m < MR; m++) {
     const int f = rg + kDecRows * m;
-    const float a = fk[f], b = fq[f];
-    f32x4v s = rows[m];
+    if (f < R) {
+      const float a = fk[f], b = fq[f];
+      f32x4v s = rows[m];
 #pragma unroll
-    for (int e = 0; e < 4; e++) s[e] = fmaf(a, vv[e], s[e]);
-    if (NT)
-      __builtin_nontemporal_store(s, reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]));
-    else
-      *reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]) = s;
+      for (int e = 0; e < 4; e++) s[e] = fmaf(a, vv[e], s[e]);
+      if (NT)
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]));
+      else
+        *reinterpret_cast<f32x4v*>(&Si[f * kDV + 4 * cg]) = s;
 #pragma unroll
-    for (int e = 0; e < 4; e++) acc[e] = fmaf(b, s[e], acc[e]);
+      for (int e = 0; e < 4; e++) acc[e] = fmaf(b, s[e], acc[e]);
+    }
   }
   // z update and the denominator partial
   float dpart = 0.0f;
-  if (tid < kF) {
+  if (tid < R) {
     const float z0 = zr + fk[tid];
     zi[tid] = z0;
     dpart = fq[tid] * z0;
@@ -109,16 +129,53 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   }
 }
 
+// Full <-> compact state, one workgroup per head-state: row copies in float4 pieces.
+template <bool ToCompact>
+__global__ __launch_bounds__(256) void state_convert_kernel(const float* __restrict__ src_S,
+                                                            const float* __restrict__ src_z, float* __restrict__ dst_S,
+                                                            float* __restrict__ dst_z) {
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const size_t full = (size_t)i * kF, compact = (size_t)i * kCompactRows;
+  constexpr int P = kDV / 4;  // float4 pieces per row
+  // destination rows: compact 0 .. 5d (from full 0, d .. 6d-1), or full 0 .. 6d-1 (from compact 0 or f - d + 1)
+  constexpr int rows = ToCompact ? kCompactRows : kF;
+  for (int e = tid; e < rows * P; e += 256) {
+    const int row = e / P, c = e % P;
+    const int srow = ToCompact ? (row == 0 ? 0 : row + kD - 1) : (row < kD ? 0 : row - kD + 1);
+    const size_t sbase = ToCompact ? full : compact, dbase = ToCompact ? compact : full;
+    reinterpret_cast<f32x4v*>(dst_S + (dbase + row) * kDV)[c] =
+        reinterpret_cast<const f32x4v*>(src_S + (sbase + srow) * kDV)[c];
+  }
+  for (int row = tid; row < rows; row += 256) {
+    const int srow = ToCompact ? (row == 0 ? 0 : row + kD - 1) : (row < kD ? 0 : row - kD + 1);
+    dst_z[(ToCompact ? compact : full) + row] = src_z[(ToCompact ? full : compact) + srow];
+  }
+}
+
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
-                              const int64_t* posv, const MethodConsts& mc, float* S, float* z, float* out, hipStream_t stream) {
+                              const int64_t* posv, bool compact, const MethodConsts& mc, float* S, float* z,
+                              float* out, hipStream_t stream) {
   // states above 128 MB (half of the 256 MB last-level cache) are streamed
-  const bool stream_state = (size_t)N * kStateFloats * sizeof(float) > ((size_t)128 << 20);
-  if (stream_state)
-    hipLaunchKernelGGL(decode_step_kernel<true>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega,
-                       mc.nph, mc.log2_base, mc.kr, mc.ceps, S, z, out);
+  const size_t floats = compact ? (size_t)kCompactRows * (kDV + 1) : (size_t)kStateFloats;
+  const bool stream_state = (size_t)N * floats * sizeof(float) > ((size_t)128 << 20);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega, mc.nph,
+                       mc.log2_base, mc.kr, mc.ceps, S, z, out);
+  };
+  if (compact) {
+    if (stream_state) go(decode_step_kernel<true, true>); else go(decode_step_kernel<false, true>);
+  } else {
+    if (stream_state) go(decode_step_kernel<true, false>); else go(decode_step_kernel<false, false>);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_state_convert(const float* S, const float* z, int N, bool to_compact, float* dS, float* dz,
+                                hipStream_t stream) {
+  if (to_compact)
+    hipLaunchKernelGGL(state_convert_kernel<true>, dim3(N), dim3(256), 0, stream, S, z, dS, dz);
   else
-    hipLaunchKernelGGL(decode_step_kernel<false>, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega,
-                       mc.nph, mc.log2_base, mc.kr, mc.ceps, S, z, out);
+    hipLaunchKernelGGL(state_convert_kernel<false>, dim3(N), dim3(256), 0, stream, S, z, dS, dz);
   return hipGetLastError();
 }
 

@@ -27,10 +27,14 @@ hipError_t launch_phase_table(float* rho, int T, int64_t pos0, double log2_base,
 hipError_t launch_featurize(const void* u, sanatan_dtype in_t, int B, int H, int T, int64_t pos0,
                             const MethodConsts& mc, void* phi, sanatan_dtype out_t, hipStream_t stream);
 
-// posv: device [N] positions, one per head-state, or nullptr for the single position pos
+// posv: device [N] positions, one per head-state, or nullptr for the single position pos;
+// compact: S [N][5d+1][d_v], z [N][5d+1] (channel-0 rows kept once) instead of [N][6d][d_v], [N][6d]
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
-                              const int64_t* posv, const MethodConsts& mc, float* S, float* z, float* out,
-                              hipStream_t stream);
+                              const int64_t* posv, bool compact, const MethodConsts& mc, float* S, float* z,
+                              float* out, hipStream_t stream);
+// full state (S, z) -> compact (dS, dz), or compact -> full
+hipError_t launch_state_convert(const float* S, const float* z, int N, bool to_compact, float* dS, float* dz,
+                                hipStream_t stream);
 
 // Prefill plan: the flattened (sequence, chunk) list split into G equal ranges (one workgroup
 // each) and the workspace layout (phase table, then boundary-state slots).

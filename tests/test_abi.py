@@ -47,6 +47,13 @@ def test_state_bytes_matches_pages(L):
     assert L.sanatan_state_bytes(0, 64) == 0
 
 
+def test_compact_state_bytes(L):
+    """(5d+1)(d_v+1) floats: the d equal channel-0 rows of S and entries of z kept once."""
+    assert L.sanatan_compact_state_bytes(64, 64) == 321 * 65 * 4
+    assert L.sanatan_state_bytes(64, 64) - L.sanatan_compact_state_bytes(64, 64) == 63 * 65 * 4
+    assert L.sanatan_compact_state_bytes(64, 0) == 0
+
+
 def test_status_strings(L):
     for s in range(5):
         assert L.sanatan_status_string(s)
@@ -99,6 +106,16 @@ def test_featurize_decode_quadratic_validation(L):
     assert dp(FAKE, FAKE, FAKE, 4, FAKE, ctypes.byref(p), FAKE, None, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
     assert dp(FAKE, FAKE, FAKE, 4, FAKE, ctypes.byref(params(d=32)), FAKE, FAKE, FAKE,
               None) == rpg.SANATAN_ERR_UNSUPPORTED
+    dc = L.sanatan_decode_step_compact
+    assert dc(FAKE, FAKE, FAKE, 0, 0, None, ctypes.byref(p), FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert dc(FAKE, FAKE, FAKE, 4, 0, None, ctypes.byref(p), None, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert dc(FAKE, FAKE, FAKE, 4, 0, FAKE, None, FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert dc(FAKE, FAKE, FAKE, 4, 0, None, ctypes.byref(params(d_v=32)), FAKE, FAKE, FAKE,
+              None) == rpg.SANATAN_ERR_UNSUPPORTED
+    for conv in (L.sanatan_state_compact, L.sanatan_state_expand):
+        assert conv(FAKE, FAKE, 0, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+        assert conv(FAKE, None, 3, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+        assert conv(FAKE, FAKE, 3, FAKE, None, None) == rpg.SANATAN_ERR_INVALID_ARG
     for pe in (0, 3):
         assert L.sanatan_quadratic_ref_p2(FAKE, FAKE, FAKE, 1, 1, 1, 64, pe, 0, ctypes.byref(p), FAKE, FAKE, 1 << 40,
                                           None) == rpg.SANATAN_ERR_INVALID_ARG

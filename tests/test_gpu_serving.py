@@ -140,3 +140,93 @@ def test_prefill_decode_handoff_ragged_prompts(torch_dev, dtype):
         assert row_rel_err(got[b], want[:, T:]) <= tol, (b, T)
         assert np.abs(host(S[b]) - Sw).max() <= tol * np.abs(Sw).max()
         assert np.abs(host(z[b]) - zw).max() <= tol * np.abs(zw).max()
+
+
+# ---- compact state: the d equal channel-0 rows of S (and entries of z) kept once, (5d+1) rows
+
+
+def test_compact_expand_round_trip_is_bitwise(torch_dev):
+    """Compacting keeps row 0 and rows d..6d-1; expanding writes the shared row into all d channel-0 rows."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    N = 5
+    g = torch.Generator(device="cuda").manual_seed(600)
+    S = torch.randn((N, 384, 64), device="cuda", generator=g)
+    z = torch.rand((N, 384), device="cuda", generator=g)
+    S[:, 1:64] = S[:, :1]
+    z[:, 1:64] = z[:, :1]
+    Sc, zc = rpg.sanatan_state_compact(S, z)
+    assert Sc.shape == (N, 321, 64) and zc.shape == (N, 321)
+    assert torch.equal(Sc[:, 0], S[:, 0]) and torch.equal(Sc[:, 1:], S[:, 64:])
+    assert torch.equal(zc[:, 0], z[:, 0]) and torch.equal(zc[:, 1:], z[:, 64:])
+    S2, z2 = rpg.sanatan_state_expand(Sc, zc)
+    assert torch.equal(S2, S) and torch.equal(z2, z)
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_decode_compact_matches_recurrence(torch_dev, per_head):
+    """37 head-states continued from a 200-token fp32 prefill: the compact decode for six steps (one position
+    for all, or one per head-state) against the recurrence over the whole sequence; the expanded final
+    state against the recurrence's state."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    N, T, steps = 37, 200, 6
+    q, k, v, om = si.attention_inputs(610, 1, N, T, "f32")
+    p = params(torch, om)
+    S = torch.zeros((1, N, 384, 64), device="cuda")
+    z = torch.zeros((1, N, 384), device="cuda")
+    rpg.sanatan_prefill_chunked(dev(torch, q), dev(torch, k), dev(torch, v), 64, p, S=S, z=z)
+    Sc, zc = rpg.sanatan_state_compact(S[0], z[0])
+    _, _, (sq, sk, sv) = si.decode_inputs_numpy(611, N, 1, steps)
+    outs = []
+    for s in range(steps):
+        pos = torch.full((N,), T + s, dtype=torch.int64, device="cuda") if per_head else T + s
+        outs.append(rpg.sanatan_decode_step_compact(dev(torch, sq[s]), dev(torch, sk[s]), dev(torch, sv[s]), pos, p,
+                                                    Sc, zc).clone())
+    S2, z2 = rpg.sanatan_state_expand(Sc, zc)
+    torch.cuda.synchronize()
+    got = np.stack([host(o) for o in outs], 1)
+    want, Sw, zw = oracle.recurrent_heads(np.concatenate([q[0], sq.transpose(1, 0, 2)], 1),
+                                          np.concatenate([k[0], sk.transpose(1, 0, 2)], 1),
+                                          np.concatenate([v[0], sv.transpose(1, 0, 2)], 1), om)
+    assert row_rel_err(got, want[:, T:]) <= 1e-4
+    assert np.abs(host(S2) - Sw).max() <= 1e-4 * np.abs(Sw).max()
+    assert np.abs(host(z2) - zw).max() <= 1e-4 * np.abs(zw).max()
+
+
+def test_decode_compact_streamed_equals_full(torch_dev):
+    """1700 head-states (a 142 MB compact state, streamed with non-temporal accesses) at their own positions,
+    three steps from an empty state: the expanded compact state equals the full-state call's bit for bit (the
+    updates are the same operations), the outputs agree to the rounding of the channel-0 readout, and eight
+    sampled head-states match the recurrence."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    N, steps = 1700, 3
+    om, _, (sq, sk, sv) = si.decode_inputs_numpy(620, N, 1, steps)
+    om = om[:12]
+    p = params(torch, om)
+    pos = si.decode_positions(621, N, 0, 1 << 16)
+    S = torch.zeros((N, 384, 64), device="cuda")
+    z = torch.zeros((N, 384), device="cuda")
+    Sc = torch.zeros((N, 321, 64), device="cuda")
+    zc = torch.zeros((N, 321), device="cuda")
+    full, comp = [], []
+    for s in range(steps):
+        pd = torch.from_numpy(pos + s).cuda()
+        a = (dev(torch, sq[s]), dev(torch, sk[s]), dev(torch, sv[s]))
+        full.append(rpg.sanatan_decode_step_positions(*a, pd, p, S, z).clone())
+        comp.append(rpg.sanatan_decode_step_compact(*a, pd, p, Sc, zc).clone())
+    S2, z2 = rpg.sanatan_state_expand(Sc, zc)
+    torch.cuda.synchronize()
+    assert torch.equal(S2, S) and torch.equal(z2, z)
+    gf = np.stack([host(o) for o in full], 1)
+    gc = np.stack([host(o) for o in comp], 1)
+    assert row_rel_err(gc, gf) <= 1e-5
+    for i in np.random.default_rng(622).choice(N, 8, replace=False):
+        want, _, _ = oracle.recurrent_heads(sq[:, i:i + 1].transpose(1, 0, 2), sk[:, i:i + 1].transpose(1, 0, 2),
+                                            sv[:, i:i + 1].transpose(1, 0, 2), om[i % 12:i % 12 + 1],
+                                            pos0=int(pos[i]))
+        assert row_rel_err(gc[i], want[0]) <= 1e-4, int(i)
