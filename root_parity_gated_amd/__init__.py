@@ -11,6 +11,7 @@ Build the library with ``python -m root_parity_gated_amd.build``.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -110,6 +111,8 @@ class Params:
             ptr, nph = None, 1
         else:
             _check_tensor(om, "omega", dtypes=("float32",))
+            if om.dim() not in (1, 2) or om.shape[-1] != self.d:
+                raise ValueError(f"omega must be [n_param_heads, {self.d}] (got {tuple(om.shape)})")
             ptr, nph = om.data_ptr(), int(om.shape[0]) if om.dim() == 2 else 1
         c = float(4 * self.d) if self.c is None else float(self.c)
         return sanatan_params(int(self.d), int(self.d_v), float(self.gamma), c, float(self.eps),
@@ -142,6 +145,17 @@ def _check_tensor(t, name, dtypes=("float32", "bfloat16")):
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
 
 
+def _check_shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_same_dtype(ref, *named):
+    for name, t in named:
+        if t.dtype != ref.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {ref.dtype} (as q)")
+
+
 def _dtype_code(t) -> int:
     import torch
 
@@ -163,15 +177,44 @@ def sanatan_featurize(u, pos0: int, params: Params, out_dtype=None, out=None):
     import torch
 
     _check_tensor(u, "u")
+    if u.dim() != 4:
+        raise ValueError(f"u must be [B,H,T,d] (got {tuple(u.shape)})")
     B, H, T, d = u.shape
+    _check_shape(u, "u", (B, H, T, params.d))
     out_dtype = u.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, H, T, 6 * d), dtype=out_dtype, device=u.device)
     _check_tensor(out, "phi")
+    _check_shape(out, "phi", (B, H, T, 6 * d))
     p = params.struct()
     _check(lib().sanatan_featurize(_ptr(u), _dtype_code(u), B, H, T, int(pos0), ctypes.byref(p), _ptr(out),
                                    _dtype_code(out), _stream()), "sanatan_featurize")
     return out
+
+
+def _attention_shape(q, k, v, params):
+    """q, k [B,H,T,d] and v [B,H,T,d_v] (d, d_v of params) of one element type -> (B, H, T)."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,T,d] (got {tuple(q.shape)})")
+    B, H, T = q.shape[:3]
+    _check_shape(q, "q", (B, H, T, params.d))
+    _check_shape(k, "k", (B, H, T, params.d))
+    _check_shape(v, "v", (B, H, T, params.d_v))
+    _check_same_dtype(q, ("k", k), ("v", v))
+    return B, H, T
+
+
+def _decode_shapes(q, k, v, S, z, rows, params):
+    """q, k [N,d], v [N,d_v], S [N,rows,d_v], z [N,rows] (d, d_v of params) -> N."""
+    if q.dim() != 2:
+        raise ValueError(f"q must be [N,d] (got {tuple(q.shape)})")
+    N = q.shape[0]
+    _check_shape(q, "q", (N, params.d))
+    _check_shape(k, "k", (N, params.d))
+    _check_shape(v, "v", (N, params.d_v))
+    _check_shape(S, "S", (N, rows, params.d_v))
+    _check_shape(z, "z", (N, rows))
+    return N
 
 
 def sanatan_prefill_workspace_bytes(B: int, H: int, T: int, chunk: int, params: Params | None = None) -> int:
@@ -185,13 +228,17 @@ def sanatan_prefill_chunked(q, k, v, chunk: int, params: Params, pos0: int = 0, 
 
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(t, name)
-    B, H, T, d = q.shape
+    B, H, T = _attention_shape(q, k, v, params)
+    d, dv = params.d, params.d_v
     if out is None:
-        out = torch.empty((B, H, T, v.shape[-1]), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     _check_tensor(out, "out")
-    for name, t in (("S", S), ("z", z)):
+    _check_shape(out, "out", (B, H, T, dv))
+    _check_same_dtype(q, ("out", out))
+    for name, t, shape in (("S", S, (B, H, 6 * d, dv)), ("z", z, (B, H, 6 * d))):
         if t is not None:
             _check_tensor(t, name, dtypes=("float32",))
+            _check_shape(t, name, shape)
     p = params.struct()
     need = int(lib().sanatan_prefill_workspace_bytes(B, H, T, chunk, ctypes.byref(p)))
     if ws is None:
@@ -208,10 +255,11 @@ def sanatan_decode_step(q, k, v, pos: int, params: Params, S, z, out=None):
 
     for name, t in (("q", q), ("k", k), ("v", v), ("S", S), ("z", z)):
         _check_tensor(t, name, dtypes=("float32",))
-    N = q.shape[0]
+    N = _decode_shapes(q, k, v, S, z, 6 * params.d, params)
     if out is None:
         out = torch.empty((N, v.shape[-1]), dtype=torch.float32, device=q.device)
     _check_tensor(out, "out", dtypes=("float32",))
+    _check_shape(out, "out", (N, v.shape[-1]))
     p = params.struct()
     _check(lib().sanatan_decode_step(_ptr(q), _ptr(k), _ptr(v), N, int(pos), ctypes.byref(p), _ptr(S), _ptr(z),
                                      _ptr(out), _stream()), "sanatan_decode_step")
@@ -225,12 +273,13 @@ def sanatan_decode_step_positions(q, k, v, pos, params: Params, S, z, out=None):
     for name, t in (("q", q), ("k", k), ("v", v), ("S", S), ("z", z)):
         _check_tensor(t, name, dtypes=("float32",))
     _check_tensor(pos, "pos", dtypes=("int64",))
-    N = q.shape[0]
+    N = _decode_shapes(q, k, v, S, z, 6 * params.d, params)
     if pos.numel() != N:
         raise ValueError(f"pos has {pos.numel()} entries for {N} head-states")
     if out is None:
         out = torch.empty((N, v.shape[-1]), dtype=torch.float32, device=q.device)
     _check_tensor(out, "out", dtypes=("float32",))
+    _check_shape(out, "out", (N, v.shape[-1]))
     p = params.struct()
     _check(lib().sanatan_decode_step_positions(_ptr(q), _ptr(k), _ptr(v), N, _ptr(pos), ctypes.byref(p), _ptr(S),
                                                _ptr(z), _ptr(out), _stream()), "sanatan_decode_step_positions")
@@ -244,19 +293,33 @@ def sanatan_compact_state_bytes(d: int = 64, d_v: int = 64) -> int:
     return int(lib().sanatan_compact_state_bytes(d, d_v))
 
 
+def _state_lead(S, z, rows):
+    """S [...,rows,64] and z [...,rows] with the same leading shape (at least one head-state) -> that shape."""
+    if S.dim() < 3 or tuple(S.shape[-2:]) != (rows, 64):
+        raise ValueError(f"state has shape {tuple(S.shape)}, expected [..., {rows}, 64]")
+    lead = tuple(S.shape[:-2])
+    _check_shape(z, "z", (*lead, rows))
+    if math.prod(lead) == 0:
+        raise ValueError("state holds no head-states")
+    return lead
+
+
 def sanatan_state_compact(S, z, Sc=None, zc=None):
     """Full state S [...,384,64], z [...,384] -> compact Sc [...,321,64], zc [...,321] (pure copies)."""
     import torch
 
     for name, t in (("S", S), ("z", z)):
         _check_tensor(t, name, dtypes=("float32",))
-    N = S.numel() // (S.shape[-2] * S.shape[-1])
+    lead = _state_lead(S, z, 6 * 64)
+    N = math.prod(lead)
     if Sc is None:
-        Sc = torch.empty((*S.shape[:-2], COMPACT_ROWS, S.shape[-1]), dtype=torch.float32, device=S.device)
+        Sc = torch.empty((*lead, COMPACT_ROWS, 64), dtype=torch.float32, device=S.device)
     if zc is None:
-        zc = torch.empty((*z.shape[:-1], COMPACT_ROWS), dtype=torch.float32, device=z.device)
+        zc = torch.empty((*lead, COMPACT_ROWS), dtype=torch.float32, device=z.device)
     for name, t in (("Sc", Sc), ("zc", zc)):
         _check_tensor(t, name, dtypes=("float32",))
+    _check_shape(Sc, "Sc", (*lead, COMPACT_ROWS, 64))
+    _check_shape(zc, "zc", (*lead, COMPACT_ROWS))
     _check(lib().sanatan_state_compact(_ptr(S), _ptr(z), N, _ptr(Sc), _ptr(zc), _stream()), "sanatan_state_compact")
     return Sc, zc
 
@@ -267,13 +330,16 @@ def sanatan_state_expand(Sc, zc, S=None, z=None):
 
     for name, t in (("Sc", Sc), ("zc", zc)):
         _check_tensor(t, name, dtypes=("float32",))
-    N = Sc.numel() // (Sc.shape[-2] * Sc.shape[-1])
+    lead = _state_lead(Sc, zc, COMPACT_ROWS)
+    N = math.prod(lead)
     if S is None:
-        S = torch.empty((*Sc.shape[:-2], 6 * 64, Sc.shape[-1]), dtype=torch.float32, device=Sc.device)
+        S = torch.empty((*lead, 6 * 64, 64), dtype=torch.float32, device=Sc.device)
     if z is None:
-        z = torch.empty((*zc.shape[:-1], 6 * 64), dtype=torch.float32, device=zc.device)
+        z = torch.empty((*lead, 6 * 64), dtype=torch.float32, device=zc.device)
     for name, t in (("S", S), ("z", z)):
         _check_tensor(t, name, dtypes=("float32",))
+    _check_shape(S, "S", (*lead, 6 * 64, 64))
+    _check_shape(z, "z", (*lead, 6 * 64))
     _check(lib().sanatan_state_expand(_ptr(Sc), _ptr(zc), N, _ptr(S), _ptr(z), _stream()), "sanatan_state_expand")
     return S, z
 
@@ -284,7 +350,7 @@ def sanatan_decode_step_compact(q, k, v, pos, params: Params, Sc, zc, out=None):
 
     for name, t in (("q", q), ("k", k), ("v", v), ("Sc", Sc), ("zc", zc)):
         _check_tensor(t, name, dtypes=("float32",))
-    N = q.shape[0]
+    N = _decode_shapes(q, k, v, Sc, zc, 5 * params.d + 1, params)
     posv = None
     if isinstance(pos, torch.Tensor):
         _check_tensor(pos, "pos", dtypes=("int64",))
@@ -294,6 +360,7 @@ def sanatan_decode_step_compact(q, k, v, pos, params: Params, Sc, zc, out=None):
     if out is None:
         out = torch.empty((N, v.shape[-1]), dtype=torch.float32, device=q.device)
     _check_tensor(out, "out", dtypes=("float32",))
+    _check_shape(out, "out", (N, v.shape[-1]))
     p = params.struct()
     _check(lib().sanatan_decode_step_compact(_ptr(q), _ptr(k), _ptr(v), N, int(pos),
                                              _ptr(posv) if posv is not None else None, ctypes.byref(p), _ptr(Sc),
@@ -312,10 +379,12 @@ def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0,
 
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(t, name)
-    B, H, T, d = q.shape
+    B, H, T = _attention_shape(q, k, v, params)
     if out is None:
-        out = torch.empty((B, H, T, v.shape[-1]), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, T, params.d_v), dtype=q.dtype, device=q.device)
     _check_tensor(out, "out")
+    _check_shape(out, "out", (B, H, T, params.d_v))
+    _check_same_dtype(q, ("out", out))
     p = params.struct()
     need = int(lib().sanatan_quadratic_workspace_bytes(B, H, T, _dtype_code(q), ctypes.byref(p)))
     if ws is None:
