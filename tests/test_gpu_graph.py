@@ -98,3 +98,55 @@ def test_decode_graph_replays_match_eager(torch_dev):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
         assert torch.equal(S, S_eager) and torch.equal(z, z_eager), rep
+
+
+def test_serving_decode_graph_replays_match_eager(torch_dev):
+    """The per-head-state-position decode and the compact-state decode, four steps each, captured once and
+    replayed three times with unrelated eager work in between: every replay bitwise equal to the eager run."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    nh, steps = 144, 4
+    om, _, (sq, sk, sv) = si.decode_inputs_numpy(58, nh, 1, steps)
+    dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    sq, sk, sv = map(dv, (sq, sk, sv))
+    p = rpg.Params(omega=dv(om))
+    pos = dv(si.decode_positions(59, nh) + np.arange(steps)[:, None])  # [steps, nh]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    S0 = torch.randn((nh, 384, 64), device="cuda", generator=g) * 0.01
+    z0 = torch.rand((nh, 384), device="cuda", generator=g) + 1.0
+    S0[:, 1:64] = S0[:, :1]
+    z0[:, 1:64] = z0[:, :1]
+    Sc0, zc0 = rpg.sanatan_state_compact(S0, z0)
+
+    def run(S, z, Sc, zc, o1, o2):
+        for i in range(steps):
+            rpg.sanatan_decode_step_positions(sq[i], sk[i], sv[i], pos[i], p, S, z, o1[i])
+            rpg.sanatan_decode_step_compact(sq[i], sk[i], sv[i], pos[i], p, Sc, zc, o2[i])
+
+    S, z, Sc, zc = S0.clone(), z0.clone(), Sc0.clone(), zc0.clone()
+    e1, e2 = torch.empty((steps, nh, 64), device="cuda"), torch.empty((steps, nh, 64), device="cuda")
+    run(S, z, Sc, zc, e1, e2)
+    want = [t.clone() for t in (S, z, Sc, zc)]
+
+    o1, o2 = torch.empty_like(e1), torch.empty_like(e2)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    for t, t0 in zip((S, z, Sc, zc), (S0, z0, Sc0, zc0)):
+        t.copy_(t0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        run(S, z, Sc, zc, o1, o2)
+    for rep in range(3):
+        for t, t0 in zip((S, z, Sc, zc), (S0, z0, Sc0, zc0)):
+            t.copy_(t0)
+        o1.fill_(float("nan"))
+        o2.fill_(float("nan"))
+        torch.randn((1 << 20,), device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, e1) and torch.equal(o2, e2), rep
+        for got, w in zip((S, z, Sc, zc), want):
+            assert torch.equal(got, w), rep
