@@ -189,6 +189,47 @@ def cpu_baseline(w, budget_s=20.0):
                       f"({dt:.1f} s wall)"}
 
 
+def cpu_oracle_extras(si):
+    """The fp64 oracle timed beside the other workloads, each on a bounded sample (a few seconds at most):
+    the recurrent form for decode and the long prefill, the direct-kappa form for the p=2 quadratic."""
+    import oracle
+
+    nth = oracle.num_threads()
+    res = {}
+    # decode: 144 head-states, 128 tokens from an empty state (the per-token cost does not depend on the fill)
+    w = si.DECODE
+    steps = 128
+    om, _, (sq, sk, sv) = si.decode_inputs_numpy(w.seed, w.H, 1, steps)
+    t0 = time.perf_counter()
+    oracle.recurrent_heads(sq.transpose(1, 0, 2), sk.transpose(1, 0, 2), sv.transpose(1, 0, 2), om, pos0=w.T)
+    dt = time.perf_counter() - t0
+    res["decode"] = {"value": dt / steps * 1e6, "unit": "us/token", "cores": nth, "kind": "oracle",
+                     "sample": f"recurrent fp64 oracle, {w.H} head-states x {steps} tokens ({dt:.2f} s wall)"}
+    # long prefill: the recurrence over every head and the first 4096 tokens (cost per token is constant)
+    w = si.LONG
+    n_tok = min(w.T, 4096)
+    q, k, v, om = si.attention_inputs(w.seed, 1, w.H, n_tok, "bf16")
+    t0 = time.perf_counter()
+    oracle.recurrent_heads(q[0], k[0], v[0], om, want_out=True)
+    dt = time.perf_counter() - t0
+    res["long_prefill"] = {"value": n_tok / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+                           "sample": f"recurrent fp64 oracle, {w.H} heads x the first {n_tok} of {w.T} tokens "
+                                     f"({dt:.2f} s wall)"}
+    # quadratic p=2: direct kappa on 256 query rows spread over one head, extrapolated by causal pairs
+    w = si.QUAD_P2
+    q, k, v, om = si.attention_inputs(w.seed, 1, 1, w.T, "bf16")
+    rows = np.linspace(0, w.T - 1, 256).astype(np.int64)
+    pairs = float((rows + 1).sum())
+    t0 = time.perf_counter()
+    oracle.attention_direct(q[0, 0], k[0, 0], v[0, 0], om[0], p=w.p, rows=rows)
+    dt = time.perf_counter() - t0
+    full_s = dt / pairs * (w.B * w.H * w.T * (w.T + 1) / 2)
+    res["quadratic_p2"] = {"value": w.B * w.T / full_s, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+                           "sample": f"direct-kappa fp64 oracle, {rows.size} query rows of one head ({int(pairs)} pairs, "
+                                     f"{dt:.2f} s wall), extrapolated by causal pairs to the whole workload"}
+    return res
+
+
 def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False, compact=False):
     """fp32 decode: 144 head-states per sequence, state filled by 4096 tokens, then sequential steps.
     With `positions`, each sequence continues at its own position (4096 plus a seeded offset below 4096)
@@ -455,6 +496,10 @@ def main():
                                "roofline": {"bound": "hbm", "achieved": fbytes / (fms * 1e-3) / 1e9,
                                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                             "frac": fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+        if not args.no_cpu_baseline:
+            log("cpu oracle beside the other workloads")
+            for key, rec in cpu_oracle_extras(si).items():
+                extras.setdefault("cpu_oracle", {})[key] = rec
         result["extras"] = extras
     print(json.dumps(result))
 
