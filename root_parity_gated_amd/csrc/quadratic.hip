@@ -10,9 +10,11 @@
 // other's latencies); each wave owns MQ tiles of 32 query rows and featurizes them once into
 // 32x32x16 MFMA operand registers (K-step j = 16 features).  Per block of 32 keys, Phi(K)
 // (channels 1..5: channel 0 is the constant 1 and contributes exactly d = 64 to every score) and
-// V are staged token-major in LDS, double-buffered, and every wave forms its transposed score
-// tiles A^T[s][t].  The masked, powered tile is the B operand of V^T P (V^T read with the
-// transposing LDS load), and its row sums (v_dot2) accumulate the denominator.
+// V are staged token-major in LDS, two slots each, K one block ahead of V, and every wave forms its
+// transposed score tiles A^T[s][t].  The masked, powered tile is the B operand of V^T P (V^T read
+// with the transposing LDS load), and its row sums (v_dot2) accumulate the denominator.  A wave
+// issues the score MFMAs of block kb + 1 with the weight VALU and V^T P MFMAs of block kb between
+// them (software pipelining across key blocks).
 #include "prefill_common.h"
 
 namespace sanatan {
