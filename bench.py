@@ -320,7 +320,8 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False, co
         "bytes_per_step": bytes_step,
         "roofline": {"bound": "hbm", "achieved": bytes_step / (best_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": bytes_step / (best_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "note": ("state (14.4 MB) is resident in the 256 MB Infinity Cache between steps" if batch == 1
+        "note": ("state (14.4 MB, 12.0 MB compact) is resident in the 256 MB Infinity Cache between steps"
+                 if batch == 1
                  else "state exceeds the Infinity Cache; HBM-bound")
                 + ("; one position per sequence (sanatan_decode_step_positions)" if positions else "")
                 + ("; compact state, (5d+1) x (d_v+1) floats per head-state: roofline on its own bytes, not on"
@@ -463,10 +464,9 @@ def main():
                 extras[f"decode_batch{b}_positions"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16,
                                                                     positions=True)
                 log(f"decode batch {b}, positions: {extras[f'decode_batch{b}_positions']['us_per_token']:.2f} us/token")
-                log(f"decode batch {b}, compact state")
-                extras[f"decode_batch{b}_compact"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16,
-                                                                  compact=True)
-                log(f"decode batch {b}, compact: {extras[f'decode_batch{b}_compact']['us_per_token']:.2f} us/token")
+            log(f"decode batch {b}, compact state")
+            extras[f"decode_batch{b}_compact"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16, compact=True)
+            log(f"decode batch {b}, compact: {extras[f'decode_batch{b}_compact']['us_per_token']:.2f} us/token")
             log(f"decode batch {b}: {extras[f'decode_batch{b}']['us_per_token']:.2f} us/token")
         wl = si.LONG
         log(f"long prefill {wl.name}")
