@@ -61,6 +61,10 @@ def _load():
     lib.oracle_attention_direct.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, dp,
                                             ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                             ctypes.c_int, ip, ctypes.c_int, dp]
+    lib.oracle_attention_direct4.restype = None
+    lib.oracle_attention_direct4.argtypes = lib.oracle_attention_direct.argtypes
+    lib.oracle_kappa4.restype = ctypes.c_double
+    lib.oracle_kappa4.argtypes = lib.oracle_kappa.argtypes
     lib.oracle_recurrent.restype = None
     lib.oracle_recurrent.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, dp,
                                      ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
@@ -117,9 +121,20 @@ def kappa(q, k, t: int, s: int, omega, gamma: float = GAMMA, lambda_base: float 
                                       float(lambda_base)))
 
 
+def kappa4(q, k, t: int, s: int, omega, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE) -> float:
+    """The unclipped four-channel kernel of one (t, s) pair: sum_a 1 + r_q r_k (1 + cos dtheta)."""
+    q = _f64(q).ravel()
+    k = _f64(k).ravel()
+    om = _f64(omega).ravel()
+    return float(_load().oracle_kappa4(_ptr(q), _ptr(k), q.size, int(t), int(s), _ptr(om), float(gamma),
+                                       float(lambda_base)))
+
+
 def attention_direct(q, k, v, omega, pos0: int = 0, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE,
-                     c: float | None = None, eps: float = EPS, p: int = 1, rows=None) -> np.ndarray:
-    """Direct-kappa normalised causal attention for ONE head: q,k [T,d], v [T,dv]."""
+                     c: float | None = None, eps: float = EPS, p: int = 1, rows=None,
+                     four_channel: bool = False) -> np.ndarray:
+    """Direct-kappa normalised causal attention for ONE head: q,k [T,d], v [T,dv].  With four_channel, the
+    unclipped four-channel kernel (kappa4) replaces the six-channel one."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     T, d = q.shape
     dv = v.shape[1]
@@ -135,8 +150,9 @@ def attention_direct(q, k, v, omega, pos0: int = 0, gamma: float = GAMMA, lambda
             raise ValueError("row index out of range")
         out = np.empty((r.size, dv), dtype=np.float64)
         rp, nr = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), int(r.size)
-    _load().oracle_attention_direct(_ptr(q), _ptr(k), _ptr(v), T, d, dv, int(pos0), _ptr(om), float(gamma),
-                                    float(lambda_base), float(c), float(eps), int(p), rp, nr, _ptr(out))
+    fn = _load().oracle_attention_direct4 if four_channel else _load().oracle_attention_direct
+    fn(_ptr(q), _ptr(k), _ptr(v), T, d, dv, int(pos0), _ptr(om), float(gamma), float(lambda_base), float(c),
+       float(eps), int(p), rp, nr, _ptr(out))
     return out
 
 

@@ -98,6 +98,23 @@ double oracle_kappa(const double* q, const double* k, int d, int64_t t, int64_t 
 }
 
 /*
+ * The four-channel kernel, unclipped: Phi_4 = [1, r, r cos, r sin] per dim drops the independent
+ * cos and sin channels, so one dim contributes 1 + r_q r_k (1 + cos(dtheta)) -- [N] §2.5.  It can be
+ * negative (mismatched hard roots give -cos(dtheta)); no max(., 0) is applied here.
+ */
+double oracle_kappa4(const double* q, const double* k, int d, int64_t t, int64_t s, const double* omega,
+                     double gamma, double lambda_base) {
+  double acc = 0.0;
+  for (int a = 0; a < d; a++) {
+    const double thq = sanatan_angle(q[a]), thk = sanatan_angle(k[a]);
+    const double rq = sanatan_root(thq, omega[a], gamma), rk = sanatan_root(thk, omega[a], gamma);
+    const double dth = thq - thk + (double)(t - s) * sanatan_freq(a, d, lambda_base);
+    acc += 1.0 + rq * rk * (1.0 + cos(dth));
+  }
+  return acc;
+}
+
+/*
  * Normalised causal power attention, direct quadratic form, one head.
  *   q,k [T][d], v [T][dv], positions pos0+i.  Output rows: all T rows when rows == NULL
  *   (out [T][dv]), else only rows[0..n_rows) (out [n_rows][dv]).
@@ -106,10 +123,9 @@ double oracle_kappa(const double* q, const double* k, int d, int64_t t, int64_t 
  * The per-token angles and roots are tabulated first (they are per-token quantities of
  * the definition); kappa itself is summed with the cosine of a difference per pair.
  */
-void oracle_attention_direct(const double* q, const double* k, const double* v, int T, int d, int dv,
-                             int64_t pos0, const double* omega, double gamma, double lambda_base, double c,
-                             double eps, int p, const int* rows, int n_rows, double* out) {
-  (void)pos0; /* only t - s enters */
+static void attention_direct_impl(const double* q, const double* k, const double* v, int T, int d, int dv,
+                                  const double* omega, double gamma, double lambda_base, double c, double eps,
+                                  int p, const int* rows, int n_rows, int four, double* out) {
   double* thq = (double*)malloc(sizeof(double) * (size_t)T * d);
   double* thk = (double*)malloc(sizeof(double) * (size_t)T * d);
   double* rq = (double*)malloc(sizeof(double) * (size_t)T * d);
@@ -134,7 +150,8 @@ void oracle_attention_direct(const double* q, const double* k, const double* v, 
       double kap = 0.0;
       for (int a = 0; a < d; a++) {
         const double dth = thq[(size_t)t * d + a] - thk[(size_t)s * d + a] + (double)(t - s) * lam[a];
-        kap += (1.0 + rq[(size_t)t * d + a] * rk[(size_t)s * d + a]) * (1.0 + cos(dth));
+        const double gate = rq[(size_t)t * d + a] * rk[(size_t)s * d + a];
+        kap += four ? 1.0 + gate * (1.0 + cos(dth)) : (1.0 + gate) * (1.0 + cos(dth));
       }
       double w = kap / c;
       double wp = 1.0;
@@ -150,6 +167,21 @@ void oracle_attention_direct(const double* q, const double* k, const double* v, 
   free(rq);
   free(rk);
   free(lam);
+}
+
+void oracle_attention_direct(const double* q, const double* k, const double* v, int T, int d, int dv,
+                             int64_t pos0, const double* omega, double gamma, double lambda_base, double c,
+                             double eps, int p, const int* rows, int n_rows, double* out) {
+  (void)pos0; /* only t - s enters */
+  attention_direct_impl(q, k, v, T, d, dv, omega, gamma, lambda_base, c, eps, p, rows, n_rows, 0, out);
+}
+
+/* The same normalised power attention on the unclipped four-channel kernel (oracle_kappa4), [N] §2.5-§2.6. */
+void oracle_attention_direct4(const double* q, const double* k, const double* v, int T, int d, int dv,
+                              int64_t pos0, const double* omega, double gamma, double lambda_base, double c,
+                              double eps, int p, const int* rows, int n_rows, double* out) {
+  (void)pos0;
+  attention_direct_impl(q, k, v, T, d, dv, omega, gamma, lambda_base, c, eps, p, rows, n_rows, 1, out);
 }
 
 /*
