@@ -29,7 +29,8 @@ MUTS = [
   ("power off by one", "for (int e = 0; e < p; e++)", "for (int e = 0; e <= p; e++)"),
   ("channel 4 wrong", "row[4 * d + a] = r * c;", "row[4 * d + a] = r * s;"),
   ("gate dropped", "acc += (1.0 + rq * rk) * (1.0 + cos(dth));", "acc += (1.0 + cos(dth));"),
-  ("direct gate dropped", "kap += (1.0 + rq[(size_t)t * d + a] * rk[(size_t)s * d + a]) * (1.0 + cos(dth));", "kap += 2.0 * (1.0 + cos(dth));"),
+  ("direct gate dropped", ": (1.0 + gate) * (1.0 + cos(dth));", ": 2.0 * (1.0 + cos(dth));"),
+  ("four-channel gate applied to the constant", "four ? 1.0 + gate * (1.0 + cos(dth))", "four ? (1.0 + gate) * (1.0 + cos(dth))"),
   ("recurrent read before write", None, None),
   ("S transposed", "S[(size_t)f * dv + n] += fk[f]", "S[(size_t)n * 6 * d + f] += fk[f]"),
   ("direct weight not normalised by c", "double w = kap / c;", "double w = kap;"),
@@ -53,10 +54,11 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
                     ignore=shutil.ignore_patterns("*.so", "*.tmp*", "__pycache__"))
     (tmp_path / "tests" / "golden").mkdir(parents=True)
-    for f in ("conftest.py", "test_oracle_pins.py"):
+    for f in ("conftest.py", "test_oracle_pins.py", "test_oracle_four_channel.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
     shutil.copy(os.path.join(ROOT, "tests", "golden", "pages_values.json"), tmp_path / "tests" / "golden")
     (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py"],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py",
+                        "tests/test_oracle_four_channel.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "planted mistake '%s' passed every pin:\n%s" % (name, r.stdout[-2000:])
