@@ -48,9 +48,10 @@ def prefill_bytes(B, H, T, el=2):
     return B * H * T * (3 * D * el + DV * el)   # q, k, v in; out
 
 
-def quadratic_flops(B, H, T):
+def quadratic_flops(B, H, T, features=F):
+    """Causal pairs x (score over the features + weighted value sum); features = 4d for the four-channel kernel."""
     pairs = T * (T + 1) // 2
-    return B * H * pairs * 2 * (F + DV)
+    return B * H * pairs * 2 * (features + DV)
 
 
 PREFILL_SOURCES = ("api.hip", "featurize.hip", "prefill.hip", "prefill_grp.hip", "prefill_common.h", "launchers.h",
@@ -330,7 +331,7 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False, co
     }
 
 
-def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False):
+def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_channel=False):
     """ms per call: (eager, graph-replayed).  Each call is one complete library call on resident inputs;
     the graph variant replays that call captured once, which removes the host launch overhead."""
     q, k, v, om = si.workload_inputs(w)
@@ -343,7 +344,7 @@ def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False):
         code = rpg.SANATAN_BF16 if w.dtype == "bf16" else rpg.SANATAN_F32
         ws = torch.empty((rpg.sanatan_quadratic_workspace_bytes(w.B, w.H, w.T, code, p),), dtype=torch.uint8,
                          device="cuda")
-        fn = lambda: rpg.sanatan_quadratic_ref_p2(qd, kd, vd, w.p, p, out=out, ws=ws)
+        fn = lambda: rpg.sanatan_quadratic_ref_p2(qd, kd, vd, w.p, p, out=out, ws=ws, four_channel=four_channel)
     else:
         ws = torch.empty((rpg.sanatan_prefill_workspace_bytes(w.B, w.H, w.T, w.chunk, p),), dtype=torch.uint8,
                          device="cuda")
@@ -488,6 +489,17 @@ def main():
                                   "roofline": {"bound": "mfma", "achieved": qfl / (qms * 1e-3) / 1e12,
                                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                                "frac": qfl / (qms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+        log(f"quadratic {wq.name}, unclipped four-channel kernel")
+        q4_e, q4_g = bench_prefill_like(torch, rpg, si, wq, max(5, args.steps // 5), 3, quadratic=True,
+                                        four_channel=True)
+        q4 = min(q4_e, q4_g) if q4_g is not None else q4_e
+        q4fl = quadratic_flops(wq.B, wq.H, wq.T, features=4 * D)
+        extras["quadratic_p2_four_channel"] = {
+            "workload": wq.name + "_four_channel", "tokens_per_s": wq.B * wq.T / (q4 * 1e-3), "ms": q4,
+            "ms_eager": q4_e, "ms_graph": q4_g,
+            "roofline": {"bound": "mfma", "achieved": q4fl / (q4 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": q4fl / (q4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "note": "unclipped four-channel kernel: 2 (4d + d_v) flops per causal pair"}
         log(f"featurize {w.name} keys")
         fms_e, fms_g, fbytes = bench_featurize(torch, rpg, si, w, max(5, args.steps // 5), 3)
         fms = min(fms_e, fms_g) if fms_g is not None else fms_e

@@ -184,6 +184,21 @@ sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void
                                         int H, int T, int p, int64_t pos0, const sanatan_params* params,
                                         void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * sanatan_quadratic_four_channel -- the same masked quadratic form on the unclipped four-channel kernel
+ * of [N] §2.5: per dim the features are [1, r, r cos theta_rot, r sin theta_rot] (the independent cos and
+ * sin channels dropped), so
+ *   kappa4(t,s) = sum_a 1 + r_q r_k (1 + cos(theta_q - theta_k + (t - s) lambda_a)),
+ *   w = (kappa4/c)^p for s <= t, o_t = sum_{s<=t} w v_s / (sum w + eps).
+ * No max(kappa4, 0) is applied: a mismatched pair of hard roots contributes -cos(dtheta) to a dim, so with
+ * p = 1 a weight, and the denominator, can be negative or near zero.  c is the caller's (params->c).
+ * Arguments, workspace and errors exactly as sanatan_quadratic_ref_p2.
+ */
+sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, const void* v, sanatan_dtype t,
+                                              int B, int H, int T, int p, int64_t pos0,
+                                              const sanatan_params* params, void* out, void* ws,
+                                              size_t ws_bytes, hipStream_t stream);
+
 /* Static human-readable name of a status code. */
 const char* sanatan_status_string(sanatan_status status);
 

@@ -81,6 +81,8 @@ def lib():
         L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_quadratic_ref_p2.restype = i32
         L.sanatan_quadratic_ref_p2.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, sz, vp]
+        L.sanatan_quadratic_four_channel.restype = i32
+        L.sanatan_quadratic_four_channel.argtypes = L.sanatan_quadratic_ref_p2.argtypes
         _lib = L
     return _lib
 
@@ -90,7 +92,7 @@ EXPORTED = [
     "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_decode_step_positions",
     "sanatan_compact_state_bytes", "sanatan_state_compact", "sanatan_state_expand", "sanatan_decode_step_compact",
     "sanatan_quadratic_workspace_bytes",
-    "sanatan_quadratic_ref_p2",
+    "sanatan_quadratic_ref_p2", "sanatan_quadratic_four_channel",
 ]
 
 
@@ -373,8 +375,10 @@ def sanatan_quadratic_workspace_bytes(B: int, H: int, T: int, dtype_code: int, p
     return int(lib().sanatan_quadratic_workspace_bytes(B, H, T, dtype_code, ctypes.byref(p) if p is not None else None))
 
 
-def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, ws=None):
-    """Masked quadratic normalised power attention (p = 1 or 2).  Returns out [B,H,T,64]."""
+def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, ws=None,
+                             four_channel: bool = False):
+    """Masked quadratic normalised power attention (p = 1 or 2).  Returns out [B,H,T,64].  With four_channel,
+    the unclipped four-channel kernel (sanatan_quadratic_four_channel) replaces the six-channel one."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -389,7 +393,12 @@ def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0,
     need = int(lib().sanatan_quadratic_workspace_bytes(B, H, T, _dtype_code(q), ctypes.byref(p)))
     if ws is None:
         ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
-    _check(lib().sanatan_quadratic_ref_p2(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(p_exp), int(pos0),
-                                          ctypes.byref(p), _ptr(out), _ptr(ws), ws.numel(), _stream()),
-           "sanatan_quadratic_ref_p2")
+    name = "sanatan_quadratic_four_channel" if four_channel else "sanatan_quadratic_ref_p2"
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(p_exp), int(pos0),
+                                ctypes.byref(p), _ptr(out), _ptr(ws), ws.numel(), _stream()), name)
     return out
+
+
+def sanatan_quadratic_four_channel(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, ws=None):
+    """The masked quadratic form on the unclipped four-channel kernel.  Returns out [B,H,T,64]."""
+    return sanatan_quadratic_ref_p2(q, k, v, p_exp, params, pos0=pos0, out=out, ws=ws, four_channel=True)

@@ -152,7 +152,18 @@ sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   if (!ws || ws_bytes < quadratic_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
-  return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, pos0, consts(params), out, ws, stream));
+  return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, false, pos0, consts(params), out, ws, stream));
+}
+
+sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                              int H, int T, int p, int64_t pos0, const sanatan_params* params,
+                                              void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || (p != 1 && p != 2))
+    return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (!ws || ws_bytes < quadratic_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, true, pos0, consts(params), out, ws, stream));
 }
 
 }  // extern "C"

@@ -56,7 +56,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
                           const PrefillPlan& plan, hipStream_t stream);
 
 size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t);
+// four_channel: the unclipped four-channel kernel ([1, r, r cos, r sin] per dim) instead of the six-channel one
 hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
-                            int p, int64_t pos0, const MethodConsts& mc, void* out, void* ws, hipStream_t stream);
+                            int p, bool four_channel, int64_t pos0, const MethodConsts& mc, void* out, void* ws,
+                            hipStream_t stream);
 
 }  // namespace sanatan

@@ -20,12 +20,15 @@
 namespace sanatan {
 namespace {
 
-template <typename T>
+// C0: the first staged feature channel.  1 for the six-channel kernel (channels 1..5), 3 for the unclipped
+// four-channel kernel of the notes' §2.5, whose features per dim are [1, r, r cos, r sin] (channels 0, 3, 4, 5
+// of the six-channel layout): the score then sums 1 + r_q r_k (1 + cos dtheta) per dim.
+template <typename T, int C0 = 1>
 struct QGeom {
   static constexpr int MQ = 1;                        // 32-row query tiles per wave
   static constexpr int QROWS = 4 * 32 * MQ;          // query rows per workgroup
   static constexpr int KB = 32;                       // keys per block
-  static constexpr int NF = kF - kD;                  // staged features: channels 1..5
+  static constexpr int NF = kF - C0 * kD;             // staged features: channels C0..5
   static constexpr int NJ = NF / 16;                  // K-steps of the score product
   static constexpr int KP = NF + 16 / (int)sizeof(T); // Phi(K) tile pitch (elements)
   // V tile pitch: bf16 rows of 160 bytes (40 banks apart, 8 mod 32), so the four token rows that 16 lanes
@@ -42,12 +45,12 @@ struct QGeom {
 };
 
 // Two workgroups per CU for bf16; the fp32 operand fragments take the registers of one.
-template <typename T, int P>
+template <typename T, int P, int C0>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     const T* __restrict__ q, const T* __restrict__ phik, const T* __restrict__ v, T* __restrict__ out,
     const float* __restrict__ rho, const float* __restrict__ omega, int nph, int H, int Tn, int BH, int nqb, float kr,
     float eps_cp) {
-  using G = QGeom<T>;
+  using G = QGeom<T, C0>;
   typedef typename FragT<T>::type Frag;
   constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   const int hd = bh % H;
   const int row0 = qb * G::QROWS + w * 32 * MQ;  // this wave's first query row
   const T* qp = q + (size_t)bh * Tn * kD;
-  const T* kp = phik + (size_t)bh * Tn * kF + kD;  // skip channel 0
+  const T* kp = phik + (size_t)bh * Tn * kF + C0 * kD;  // skip the channels below C0
   const T* vp = v + (size_t)bh * Tn * kDV;
   T* op = out + (size_t)bh * Tn * kDV;
 
@@ -90,9 +93,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   constexpr int kRawBufferWord3 = 0x00020000;
   auto fetch_k = [&](int kb, u32x4 (&dst)[KPT]) {
     const int s0 = kb * KB;
-    // Phi(K) rows start at channel 1 (kp skips channel 0), so the last row ends kD elements short of kF
+    // Phi(K) rows start at channel C0 (kp skips the channels below), so the last row ends C0 kD elements
+    // short of kF
     const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kp + (size_t)s0 * kF), (short)0, (int)(((Tn - s0) * kF - kD) * (int)sizeof(T)), kRawBufferWord3);
+        (void*)(kp + (size_t)s0 * kF), (short)0, (int)(((Tn - s0) * kF - C0 * kD) * (int)sizeof(T)),
+        kRawBufferWord3);
 #pragma unroll
     for (int p = 0; p < KPT; p++) dst[p] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff[p], 0, 0);
   };
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   fetch_k(0, pk);
   fetch_v(0);
   if (nkb > 1) fetch_k(1, pk1);
-  // ---- Phi(q) operands: K-step j = channel 1 + j/4, dims 16 (j%4) + 8h + i (slot i)
+  // ---- Phi(q) operands: K-step j = channel C0 + j/4, dims 16 (j%4) + 8h + i (slot i)
   Frag QF[MQ][NJ];
 #pragma unroll
   for (int mq = 0; mq < MQ; mq++) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
         ch[4][i] = rr[i] * sr[i];
       }
 #pragma unroll
-      for (int c = 0; c < 5; c++) QF[mq][4 * c + m] = pack8f<T>(ch[c]);
+      for (int c = 0; c < 6 - C0; c++) QF[mq][4 * c + m] = pack8f<T>(ch[C0 - 1 + c]);
     }
   }
 
@@ -242,7 +247,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     };
     // Phi(K) fragments are read PD K-steps ahead of their MFMA, so LDS latency stays hidden
     constexpr int PD = 4;
-    static_assert(NJ >= 18, "the previous block's work is spread over the first 18 K-steps");
+    // the previous block's work, spread over the K-steps: powers over the first PW steps, then packing (2),
+    // the V fragments (1), the row sums (1) and the four V^T P MFMAs
+    constexpr int PW = NJ >= 16 ? 8 : 4;
+    static_assert(NJ >= PW + 8, "not enough K-steps to spread the previous block's work over");
     Frag Ar[PD];
 #pragma unroll
     for (int j = 0; j < PD; j++) Ar[j] = ldA(j);
@@ -261,32 +269,31 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
       }
       if (j + PD < NJ) Ar[j % PD] = ldA(j + PD);
       if constexpr (prev) {
-        // K-steps 0..7: powers; 8, 9: packing; 10: the V fragments; 11: row sums; 12..15: V^T P
-        if (j < 8) {
+        if (j < PW) {
+          constexpr int E = 16 / PW;
 #pragma unroll
-          for (int mq = 0; mq < MQ; mq++) {
-            wv[mq][2 * j] = power(old[mq][2 * j]);
-            wv[mq][2 * j + 1] = power(old[mq][2 * j + 1]);
-          }
-        } else if (j == 8 || j == 9) {
+          for (int mq = 0; mq < MQ; mq++)
+#pragma unroll
+            for (int e = 0; e < E; e++) wv[mq][E * j + e] = power(old[mq][E * j + e]);
+        } else if (j == PW || j == PW + 1) {
 #pragma unroll
           for (int mq = 0; mq < MQ; mq++) {
             float x[8];
 #pragma unroll
-            for (int i = 0; i < 8; i++) x[i] = wv[mq][8 * (j - 8) + i];
-            (j == 8 ? P0[mq] : P1[mq]) = pack8f<T>(x);
+            for (int i = 0; i < 8; i++) x[i] = wv[mq][8 * (j - PW) + i];
+            (j == PW ? P0[mq] : P1[mq]) = pack8f<T>(x);
           }
-        } else if (j == 10) {
+        } else if (j == PW + 2) {
 #pragma unroll
           for (int vt = 0; vt < 2; vt++) {
             Vf[vt][0] = lds_tokfrag(Vs, VP, 0, 32 * vt, l);
             Vf[vt][1] = lds_tokfrag(Vs, VP, 16, 32 * vt, l);
           }
-        } else if (j == 11) {
+        } else if (j == PW + 3) {
 #pragma unroll
           for (int mq = 0; mq < MQ; mq++) rs[mq] = frag_sum(P1[mq], frag_sum(P0[mq], rs[mq]));
-        } else if (j >= 12 && j < 16) {
-          const int vt = (j - 12) >> 1, hf = (j - 12) & 1;
+        } else if (j >= PW + 4 && j < PW + 8) {
+          const int vt = (j - PW - 4) >> 1, hf = (j - PW - 4) & 1;
 #pragma unroll
           for (int mq = 0; mq < MQ; mq++) mma32(num[mq][vt], Vf[vt][hf], hf ? P1[mq] : P0[mq]);
         }
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
 
 size_t rho_bytes(int T) { return (((size_t)T * kD * sizeof(float)) + 255) & ~(size_t)255; }
 
-template <typename T, int P>
+template <typename T, int P, int C0>
 hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
                          const MethodConsts& mc, void* out, void* ws, sanatan_dtype t, hipStream_t stream) {
   float* rho = static_cast<float*>(ws);
@@ -346,18 +353,19 @@ hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int
   if (e != hipSuccess) return e;
   e = launch_featurize(k, t, B, H, Tn, pos0, mc, phik, t, stream);
   if (e != hipSuccess) return e;
-  using G = QGeom<T>;
+  using G = QGeom<T, C0>;
   static bool attr_set[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!attr_set[dev]) {
-    e = hipFuncSetAttribute((const void*)quadratic_kernel<T, P>, hipFuncAttributeMaxDynamicSharedMemorySize, G::lds);
+    e = hipFuncSetAttribute((const void*)quadratic_kernel<T, P, C0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            G::lds);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
   const int nqb = (Tn + G::QROWS - 1) / G::QROWS;
   const int BH = B * H;
-  hipLaunchKernelGGL((quadratic_kernel<T, P>), dim3(BH * nqb), dim3(256), G::lds, stream,
+  hipLaunchKernelGGL((quadratic_kernel<T, P, C0>), dim3(BH * nqb), dim3(256), G::lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(phik), static_cast<const T*>(v),
                      static_cast<T*>(out), rho, mc.omega, mc.nph, H, Tn, BH, nqb, mc.kr,
                      P == 2 ? (float)((double)mc.ceps / (double)mc.inv_c) : mc.ceps);
@@ -371,13 +379,21 @@ size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t) {
   return rho_bytes(T) + (size_t)B * H * T * kF * el;
 }
 
-hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
-                            int p, int64_t pos0, const MethodConsts& mc, void* out, void* ws, hipStream_t stream) {
+template <int C0>
+static hipError_t launch_quad_c(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                                int p, int64_t pos0, const MethodConsts& mc, void* out, void* ws, hipStream_t stream) {
   if (t == SANATAN_BF16)
-    return p == 1 ? launch_quad_t<__bf16, 1>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream)
-                  : launch_quad_t<__bf16, 2>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream);
-  return p == 1 ? launch_quad_t<float, 1>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream)
-                : launch_quad_t<float, 2>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream);
+    return p == 1 ? launch_quad_t<__bf16, 1, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream)
+                  : launch_quad_t<__bf16, 2, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream);
+  return p == 1 ? launch_quad_t<float, 1, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream)
+                : launch_quad_t<float, 2, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream);
+}
+
+hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                            int p, bool four_channel, int64_t pos0, const MethodConsts& mc, void* out, void* ws,
+                            hipStream_t stream) {
+  return four_channel ? launch_quad_c<3>(q, k, v, t, B, H, T, p, pos0, mc, out, ws, stream)
+                      : launch_quad_c<1>(q, k, v, t, B, H, T, p, pos0, mc, out, ws, stream);
 }
 
 }  // namespace sanatan

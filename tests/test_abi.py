@@ -121,6 +121,13 @@ def test_featurize_decode_quadratic_validation(L):
                                           None) == rpg.SANATAN_ERR_INVALID_ARG
     assert L.sanatan_quadratic_ref_p2(FAKE, FAKE, FAKE, 1, 1, 1, 64, 2, 0, ctypes.byref(p), FAKE, FAKE, 10,
                                       None) == rpg.SANATAN_ERR_WORKSPACE
+    for pe in (0, 3):
+        assert L.sanatan_quadratic_four_channel(FAKE, FAKE, FAKE, 1, 1, 1, 64, pe, 0, ctypes.byref(p), FAKE, FAKE,
+                                                1 << 40, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_quadratic_four_channel(FAKE, FAKE, FAKE, 1, 1, 1, 64, 1, 0, ctypes.byref(p), FAKE, FAKE, 10,
+                                            None) == rpg.SANATAN_ERR_WORKSPACE
+    assert L.sanatan_quadratic_four_channel(None, FAKE, FAKE, 1, 1, 1, 64, 1, 0, ctypes.byref(p), FAKE, FAKE,
+                                            1 << 40, None) == rpg.SANATAN_ERR_INVALID_ARG
 
 
 def test_workspace_sizes(L):
