@@ -169,6 +169,23 @@ sanatan_status sanatan_decode_step_compact(const float* q, const float* k, const
                                            const int64_t* posv, const sanatan_params* params, float* Sc,
                                            float* zc, float* out, hipStream_t stream);
 
+/*
+ * The unclipped four-channel kernel of [N] §2.5 ([1, r, r cos theta_rot, r sin theta_rot] per dim) has the
+ * same exact p = 1 recurrence over its own features.  Its state is kept compact like the six-channel one:
+ *   S4 : [N][3d+1][d_v] fp32, row 0 = the shared channel-0 row, row 1 + (c-3) d + a = channel c of dim a
+ *        (c = 3, 4, 5: r, r cos, r sin);
+ *   z4 : [N][3d+1] fp32, the same rows.
+ * sanatan_four_channel_state_bytes: (3d+1) x (d_v+1) floats.
+ * sanatan_decode_step_four_channel: one token for N head-states on that state,
+ *   o = Phi4(q)^T S4 / (Phi4(q)^T z4 + c eps), with the updated state as in sanatan_decode_step; the weight
+ *   kappa4 is not clipped, so the denominator can be near zero or negative.  pos / posv as in
+ *   sanatan_decode_step_compact; everything else as sanatan_decode_step.
+ */
+size_t sanatan_four_channel_state_bytes(int d, int d_v);
+sanatan_status sanatan_decode_step_four_channel(const float* q, const float* k, const float* v, int N,
+                                                int64_t pos, const int64_t* posv, const sanatan_params* params,
+                                                float* S4, float* z4, float* out, hipStream_t stream);
+
 /* Workspace bytes sanatan_quadratic_ref_p2 needs (0 on invalid sizes). */
 size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params);
 

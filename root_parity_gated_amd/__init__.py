@@ -77,6 +77,10 @@ def lib():
         L.sanatan_state_expand.argtypes = [vp, vp, i32, vp, vp, vp]
         L.sanatan_decode_step_compact.restype = i32
         L.sanatan_decode_step_compact.argtypes = [vp, vp, vp, i32, i64, vp, pp, vp, vp, vp, vp]
+        L.sanatan_four_channel_state_bytes.restype = sz
+        L.sanatan_four_channel_state_bytes.argtypes = [i32, i32]
+        L.sanatan_decode_step_four_channel.restype = i32
+        L.sanatan_decode_step_four_channel.argtypes = L.sanatan_decode_step_compact.argtypes
         L.sanatan_quadratic_workspace_bytes.restype = sz
         L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_quadratic_ref_p2.restype = i32
@@ -91,6 +95,7 @@ EXPORTED = [
     "sanatan_state_bytes", "sanatan_status_string", "sanatan_featurize", "sanatan_prefill_workspace_bytes",
     "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_decode_step_positions",
     "sanatan_compact_state_bytes", "sanatan_state_compact", "sanatan_state_expand", "sanatan_decode_step_compact",
+    "sanatan_four_channel_state_bytes", "sanatan_decode_step_four_channel",
     "sanatan_quadratic_workspace_bytes",
     "sanatan_quadratic_ref_p2", "sanatan_quadratic_four_channel",
 ]
@@ -346,13 +351,14 @@ def sanatan_state_expand(Sc, zc, S=None, z=None):
     return S, z
 
 
-def sanatan_decode_step_compact(q, k, v, pos, params: Params, Sc, zc, out=None):
+def sanatan_decode_step_compact(q, k, v, pos, params: Params, Sc, zc, out=None, _entry="sanatan_decode_step_compact"):
     """sanatan_decode_step on the compact state; pos is an int (every head-state) or a device int64 tensor [N]."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("Sc", Sc), ("zc", zc)):
         _check_tensor(t, name, dtypes=("float32",))
-    N = _decode_shapes(q, k, v, Sc, zc, 5 * params.d + 1, params)
+    rows = 3 * params.d + 1 if _entry == "sanatan_decode_step_four_channel" else 5 * params.d + 1
+    N = _decode_shapes(q, k, v, Sc, zc, rows, params)
     posv = None
     if isinstance(pos, torch.Tensor):
         _check_tensor(pos, "pos", dtypes=("int64",))
@@ -364,10 +370,22 @@ def sanatan_decode_step_compact(q, k, v, pos, params: Params, Sc, zc, out=None):
     _check_tensor(out, "out", dtypes=("float32",))
     _check_shape(out, "out", (N, v.shape[-1]))
     p = params.struct()
-    _check(lib().sanatan_decode_step_compact(_ptr(q), _ptr(k), _ptr(v), N, int(pos),
-                                             _ptr(posv) if posv is not None else None, ctypes.byref(p), _ptr(Sc),
-                                             _ptr(zc), _ptr(out), _stream()), "sanatan_decode_step_compact")
+    _check(getattr(lib(), _entry)(_ptr(q), _ptr(k), _ptr(v), N, int(pos), _ptr(posv) if posv is not None else None,
+                                  ctypes.byref(p), _ptr(Sc), _ptr(zc), _ptr(out), _stream()), _entry)
     return out
+
+
+FOUR_ROWS = 3 * 64 + 1  # four-channel state rows at d = 64: shared channel 0, then r, r cos, r sin
+
+
+def sanatan_four_channel_state_bytes(d: int = 64, d_v: int = 64) -> int:
+    return int(lib().sanatan_four_channel_state_bytes(d, d_v))
+
+
+def sanatan_decode_step_four_channel(q, k, v, pos, params: Params, S4, z4, out=None):
+    """One token on the unclipped four-channel kernel's state S4 [N,193,64], z4 [N,193]; pos an int or [N] int64."""
+    return sanatan_decode_step_compact(q, k, v, pos, params, S4, z4, out=out,
+                                       _entry="sanatan_decode_step_four_channel")
 
 
 def sanatan_quadratic_workspace_bytes(B: int, H: int, T: int, dtype_code: int, params: Params | None = None) -> int:

@@ -100,7 +100,7 @@ sanatan_status sanatan_decode_step(const float* q, const float* k, const float* 
   if (!q || !k || !v || !S || !z || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
-  return hip_status(launch_decode_step(q, k, v, N, pos, nullptr, false, consts(params), S, z, out, stream));
+  return hip_status(launch_decode_step(q, k, v, N, pos, nullptr, 0, consts(params), S, z, out, stream));
 }
 
 sanatan_status sanatan_decode_step_positions(const float* q, const float* k, const float* v, int N,
@@ -109,7 +109,7 @@ sanatan_status sanatan_decode_step_positions(const float* q, const float* k, con
   if (!q || !k || !v || !pos || !S || !z || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
-  return hip_status(launch_decode_step(q, k, v, N, 0, pos, false, consts(params), S, z, out, stream));
+  return hip_status(launch_decode_step(q, k, v, N, 0, pos, 0, consts(params), S, z, out, stream));
 }
 
 size_t sanatan_compact_state_bytes(int d, int d_v) {
@@ -135,7 +135,21 @@ sanatan_status sanatan_decode_step_compact(const float* q, const float* k, const
   if (!q || !k || !v || !Sc || !zc || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
-  return hip_status(launch_decode_step(q, k, v, N, pos, posv, true, consts(params), Sc, zc, out, stream));
+  return hip_status(launch_decode_step(q, k, v, N, pos, posv, 1, consts(params), Sc, zc, out, stream));
+}
+
+size_t sanatan_four_channel_state_bytes(int d, int d_v) {
+  if (d <= 0 || d_v <= 0) return 0;
+  return ((size_t)3 * d + 1) * ((size_t)d_v + 1) * sizeof(float);
+}
+
+sanatan_status sanatan_decode_step_four_channel(const float* q, const float* k, const float* v, int N,
+                                                int64_t pos, const int64_t* posv, const sanatan_params* params,
+                                                float* S4, float* z4, float* out, hipStream_t stream) {
+  if (!q || !k || !v || !S4 || !z4 || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  return hip_status(launch_decode_step(q, k, v, N, pos, posv, 2, consts(params), S4, z4, out, stream));
 }
 
 size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params) {

@@ -29,12 +29,16 @@ constexpr int kDecRows = kDecThreads / 16;  // row groups: 16 threads cover the 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 }  // namespace
 
-template <bool NT, bool Compact>
+// Layout: 0 full six-channel state (6d rows), 1 compact six-channel (5d+1), 2 the unclipped four-channel kernel's
+// state ([N] §2.5: features [1, r, r cos, r sin]; kept compact too, 3d+1 rows: the shared channel-0 row, then
+// r, r cos, r sin).
+template <bool NT, int Layout>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int64_t pos,
     const int64_t* __restrict__ posv, const float* __restrict__ omega, int nph, double log2_base, float kr,
     float ceps, float* __restrict__ S, float* __restrict__ z, float* __restrict__ out) {
-  constexpr int R = Compact ? kCompactRows : kF;      // state rows
+  constexpr bool Compact = Layout != 0;
+  constexpr int R = Layout == 0 ? kF : Layout == 1 ? kCompactRows : kFourRows;  // state rows
   constexpr int MR = (R + kDecRows - 1) / kDecRows;   // row pieces per thread
   __shared__ float fk[kF];
   __shared__ float fq[kF];
@@ -68,16 +72,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     float cr, sr, r;
     featurize1(u, rho, om4, kr, cr, sr, r);
     float* dst = is_k ? fk : fq;
-    // channel c >= 1 of dim a: row c d + a, or 1 + (c - 1) d + a in the compact layout
-    constexpr int sh = Compact ? 1 - kD : 0;
+    // channel c >= 1 of dim a: row c d + a, or 1 + (c - 1) d + a in the compact layout, or 1 + (c - 3) d + a
+    // for the four-channel channels c = 3..5
+    constexpr int sh = Layout == 0 ? 0 : Layout == 1 ? 1 - kD : 1 - 3 * kD;
     if constexpr (Compact) {
       // the shared channel-0 row: a key adds 1 x v to it, a query reads it once for each of its d rows
       if (a == 0) dst[0] = is_k ? 1.0f : (float)kD;
     } else {
       dst[a] = 1.0f;
     }
-    dst[sh + 1 * kD + a] = cr;
-    dst[sh + 2 * kD + a] = sr;
+    if constexpr (Layout != 2) {
+      dst[sh + 1 * kD + a] = cr;
+      dst[sh + 2 * kD + a] = sr;
+    }
     dst[sh + 3 * kD + a] = r;
     dst[sh + 4 * kD + a] = r * cr;
     dst[sh + 5 * kD + a] = r * sr;
@@ -153,19 +160,22 @@ __global__ __launch_bounds__(256) void state_convert_kernel(const float* __restr
 }
 
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
-                              const int64_t* posv, bool compact, const MethodConsts& mc, float* S, float* z,
+                              const int64_t* posv, int layout, const MethodConsts& mc, float* S, float* z,
                               float* out, hipStream_t stream) {
   // states above 128 MB (half of the 256 MB last-level cache) are streamed
-  const size_t floats = compact ? (size_t)kCompactRows * (kDV + 1) : (size_t)kStateFloats;
+  const int rows = layout == 0 ? kF : layout == 1 ? kCompactRows : kFourRows;
+  const size_t floats = (size_t)rows * (kDV + 1);
   const bool stream_state = (size_t)N * floats * sizeof(float) > ((size_t)128 << 20);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega, mc.nph,
                        mc.log2_base, mc.kr, mc.ceps, S, z, out);
   };
-  if (compact) {
-    if (stream_state) go(decode_step_kernel<true, true>); else go(decode_step_kernel<false, true>);
+  if (layout == 2) {
+    if (stream_state) go(decode_step_kernel<true, 2>); else go(decode_step_kernel<false, 2>);
+  } else if (layout == 1) {
+    if (stream_state) go(decode_step_kernel<true, 1>); else go(decode_step_kernel<false, 1>);
   } else {
-    if (stream_state) go(decode_step_kernel<true, false>); else go(decode_step_kernel<false, false>);
+    if (stream_state) go(decode_step_kernel<true, 0>); else go(decode_step_kernel<false, 0>);
   }
   return hipGetLastError();
 }

@@ -28,9 +28,10 @@ hipError_t launch_featurize(const void* u, sanatan_dtype in_t, int B, int H, int
                             const MethodConsts& mc, void* phi, sanatan_dtype out_t, hipStream_t stream);
 
 // posv: device [N] positions, one per head-state, or nullptr for the single position pos;
-// compact: S [N][5d+1][d_v], z [N][5d+1] (channel-0 rows kept once) instead of [N][6d][d_v], [N][6d]
+// layout 0: S [N][6d][d_v], z [N][6d]; 1: compact, [N][5d+1] rows (channel-0 rows kept once); 2: the unclipped
+// four-channel kernel's state, [N][3d+1] rows (shared channel 0, then r, r cos, r sin)
 hipError_t launch_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
-                              const int64_t* posv, bool compact, const MethodConsts& mc, float* S, float* z,
+                              const int64_t* posv, int layout, const MethodConsts& mc, float* S, float* z,
                               float* out, hipStream_t stream);
 // full state (S, z) -> compact (dS, dz), or compact -> full
 hipError_t launch_state_convert(const float* S, const float* z, int N, bool to_compact, float* dS, float* dz,

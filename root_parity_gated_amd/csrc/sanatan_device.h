@@ -22,6 +22,7 @@ constexpr int kDV = 64;         // value dims per head
 constexpr int kF = 6 * kD;      // feature dims (6 channels)
 constexpr int kStateFloats = kF * kDV + kF;  // S [6d][d_v] then z [6d]
 constexpr int kCompactRows = 5 * kD + 1;     // compact state: the d equal channel-0 rows kept once
+constexpr int kFourRows = 3 * kD + 1;        // four-channel kernel's state: shared channel 0, then r, r cos, r sin
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -112,6 +112,12 @@ def test_featurize_decode_quadratic_validation(L):
     assert dc(FAKE, FAKE, FAKE, 4, 0, FAKE, None, FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
     assert dc(FAKE, FAKE, FAKE, 4, 0, None, ctypes.byref(params(d_v=32)), FAKE, FAKE, FAKE,
               None) == rpg.SANATAN_ERR_UNSUPPORTED
+    d4 = L.sanatan_decode_step_four_channel
+    assert d4(FAKE, FAKE, FAKE, 0, 0, None, ctypes.byref(p), FAKE, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert d4(FAKE, FAKE, FAKE, 4, 0, None, ctypes.byref(p), FAKE, None, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert d4(FAKE, FAKE, FAKE, 4, 0, None, ctypes.byref(params(d=32)), FAKE, FAKE, FAKE,
+              None) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert L.sanatan_four_channel_state_bytes(64, 64) == 193 * 65 * 4
     for conv in (L.sanatan_state_compact, L.sanatan_state_expand):
         assert conv(FAKE, FAKE, 0, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG
         assert conv(FAKE, None, 3, FAKE, FAKE, None) == rpg.SANATAN_ERR_INVALID_ARG

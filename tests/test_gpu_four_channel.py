@@ -90,3 +90,36 @@ def test_four_channel_differs_from_six_channel(torch_dev):
     b = rpg.sanatan_quadratic_ref_p2(dev(torch, q, "f32"), dev(torch, k, "f32"), dev(torch, v, "f32"), 2, par)
     torch.cuda.synchronize()
     assert row_rel_err(a.cpu().numpy(), b.cpu().numpy().astype(np.float64)) > 1e-2
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_four_channel_decode_matches_direct_form(torch_dev, per_head):
+    """37 head-states, eight tokens from an empty state on the four-channel kernel's state ((3d+1) rows).  The
+    outputs equal the direct p=1 form's rows (the recurrence is exact for the unclipped kernel); the state equals
+    the six-channel recurrence's rows of channels 0, 3, 4, 5 (the same features), channel 0 kept once."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    N, steps, nph = 37, 8, 12
+    om, _, (sq, sk, sv) = si.decode_inputs_numpy(750, N, 1, steps)
+    om = om[:nph]
+    par = rpg.Params(omega=torch.from_numpy(om).cuda())
+    pos0 = si.decode_positions(751, N, 0, 1 << 16) if per_head else np.full(N, 300, dtype=np.int64)
+    S4 = torch.zeros((N, 193, 64), device="cuda")
+    z4 = torch.zeros((N, 193), device="cuda")
+    outs = []
+    for s in range(steps):
+        pos = torch.from_numpy(pos0 + s).cuda() if per_head else 300 + s
+        outs.append(rpg.sanatan_decode_step_four_channel(dev(torch, sq[s], "f32"), dev(torch, sk[s], "f32"),
+                                                         dev(torch, sv[s], "f32"), pos, par, S4, z4).clone())
+    torch.cuda.synchronize()
+    got = np.stack([o.cpu().numpy() for o in outs], 1)
+    Sg, zg = S4.cpu().numpy().astype(np.float64), z4.cpu().numpy().astype(np.float64)
+    rows6 = np.concatenate([[0], np.arange(3 * 64, 6 * 64)])
+    for i in range(N):
+        q, k, v = sq[:, i], sk[:, i], sv[:, i]
+        want = oracle.attention_direct(q, k, v, om[i % nph], p=1, four_channel=True)
+        assert row_rel_err(got[i], want) <= 1e-4, i
+        _, S6, z6 = oracle.recurrent_heads(q[None], k[None], v[None], om[i % nph:i % nph + 1], pos0=int(pos0[i]))
+        assert np.abs(Sg[i] - S6[0][rows6]).max() <= 1e-4 * max(1.0, np.abs(S6).max()), i
+        assert np.abs(zg[i] - z6[0][rows6]).max() <= 1e-4 * max(1.0, np.abs(z6).max()), i
