@@ -71,7 +71,9 @@ size_t sanatan_state_bytes(int d, int d_v);
 /*
  * sanatan_featurize -- the feature map Phi of every vector of u.  [N] §2.2-§2.3.
  *   u    : [B][H][T][d], element type in_t (F32 or BF16).
- *   pos0 : position of u[..][..][0]; token i sits at pos0 + i (any int64 with |pos| < 2^53).
+ *   pos0 : position of u[..][..][0]; token i sits at pos0 + i.  Every position must satisfy |pos| < 2^53
+ *          (else INVALID_ARG); the phase t lambda_a / (2 pi) is reduced in fp64 with an exact two-product,
+ *          so it stays accurate to about 2^-53 revolutions over that whole range.
  *   phi  : [B][H][T][6d], element type out_t; row c*d + a as above.
  * Head h uses omega row h % n_param_heads.  Returns INVALID_ARG for NULL pointers or
  * B, H, T <= 0; UNSUPPORTED for d != 64.
@@ -80,11 +82,8 @@ sanatan_status sanatan_featurize(const void* u, sanatan_dtype in_t, int B, int H
                                  const sanatan_params* params, void* phi, sanatan_dtype out_t,
                                  hipStream_t stream);
 
-/* Workspace bytes sanatan_prefill_chunked needs for these sizes (0 on invalid sizes).
- * The prefill splits the B*H*ceil(T/chunk) chunks over one workgroup per compute unit.  The environment
- * variable SANATAN_PREFILL_WGS, when it holds a positive integer, replaces that count (capped at the number
- * of chunks); it is a test hook that forces sequences into many pieces.  The workspace size follows the
- * count, and a call whose workspace is smaller than its own plan needs returns SANATAN_ERR_WORKSPACE. */
+/* Workspace bytes sanatan_prefill_chunked needs for these sizes (0 on invalid sizes).  The prefill splits the
+ * B*H*ceil(T/chunk) chunks over one workgroup per compute unit of the current device. */
 size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const sanatan_params* params);
 
 /*
@@ -93,7 +92,9 @@ size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const san
  * mask(Phi(Q) Phi(K)^T) V, across chunks the readout Phi(Q) S; S += Phi(K)^T V after each chunk.
  *   q, k  : [B][H][T][d],  v : [B][H][T][d_v], element type t (F32 or BF16).
  *   chunk : chunk length in tokens; one of 16, 32, 64, 128 (128 with BF16 only).
- *   pos0  : position of token 0.
+ *   pos0  : position of token 0; pos0 and pos0 + T - 1 must satisfy |pos| < 2^53 (else INVALID_ARG).
+ *   T     : at most 2^22 (else UNSUPPORTED): the per-sequence byte ranges of the kernels' buffer loads must
+ *           fit a buffer descriptor's 31-bit range.
  *   S, z  : both NULL -> start from the zero state and do not return a final state;
  *           both non-NULL -> fp32 S [B][H][6d][d_v], z [B][H][6d] hold the initial state on entry
  *           and the state after the last token on exit (in place).  One NULL -> INVALID_ARG.
@@ -107,9 +108,24 @@ sanatan_status sanatan_prefill_chunked(const void* q, const void* k, const void*
                                        hipStream_t stream);
 
 /*
+ * Test hook: sanatan_prefill_chunked with the chunk list split over `workgroups` workgroups instead of one
+ * per compute unit (0 = one per compute unit; larger counts are capped at the number of chunks), so that
+ * tests can force a sequence into many pieces or one workgroup through many sequences.  The results equal
+ * those of the default split up to the rounding order of the pieces' state sums.  The workspace must hold
+ * sanatan_prefill_workspace_bytes_partitioned() bytes for the same count; a negative count is INVALID_ARG.
+ */
+size_t sanatan_prefill_workspace_bytes_partitioned(int B, int H, int T, int chunk, int workgroups,
+                                                  const sanatan_params* params);
+sanatan_status sanatan_prefill_chunked_partitioned(const void* q, const void* k, const void* v, sanatan_dtype t,
+                                                   int B, int H, int T, int chunk, int workgroups, int64_t pos0,
+                                                   const sanatan_params* params, float* S, float* z, void* out,
+                                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * sanatan_decode_step -- one token of the p=1 constant-state recurrence for N independent
  * head-states (e.g. batch x layers x heads).  [N] §2.7: write the token into the state, then read.
- *   q, k : [N][d] fp32;  v : [N][d_v] fp32;  pos : position of this token (shared by all N).
+ *   q, k : [N][d] fp32;  v : [N][d_v] fp32;  pos : position of this token (shared by all N), |pos| < 2^53
+ *          (else INVALID_ARG).
  *   S    : [N][6d][d_v] fp32, z : [N][6d] fp32, updated in place.
  *   out  : [N][d_v] fp32.
  * Head-state i uses omega row i % n_param_heads.  Streams each state once (read + write).
@@ -123,8 +139,8 @@ sanatan_status sanatan_decode_step(const float* q, const float* k, const float* 
  * whose sequences have reached different lengths.  The position of a token sets the rotation
  * theta + t lambda_a of both its feature maps ([N] §2.2), so each head-state's phase comes from its
  * own entry.
- *   pos  : device [N] int64, the position of head-state i's token (any value the single-position
- *          call accepts); read only.
+ *   pos  : device [N] int64, the position of head-state i's token, read only.  The library cannot check
+ *          device values: an entry with |pos| >= 2^53 gives a phase of reduced accuracy (never a fault).
  *   Everything else as sanatan_decode_step.  With every entry equal to one position the results are
  *   bitwise those of sanatan_decode_step at that position.  A null pos is INVALID_ARG.
  */
@@ -194,6 +210,8 @@ size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, c
  * (training) form, no recurrence: w = (kappa/c)^p, o_t = sum_{s<=t} w v_s / (sum w + eps).
  * [N] §2.6; p = 2 is the sharpened kernel trained first in [N] §4.1, p = 1 the deployed one.
  *   q, k : [B][H][T][d], v, out : [B][H][T][d_v], element type t; p : 1 or 2 (else INVALID_ARG).
+ *   T    : at most 2^20 (else UNSUPPORTED): one sequence's key features [T][6d] must fit a buffer
+ *          descriptor's 31-bit byte range.  pos0 as in sanatan_featurize.
  *   ws   : at least sanatan_quadratic_workspace_bytes() bytes: the position phase table [T][d] fp32
  *          (padded to 256 bytes), then Phi(K) [B][H][T][6d] in element type t.
  */

@@ -65,6 +65,11 @@ def lib():
         L.sanatan_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_prefill_chunked.restype = i32
         L.sanatan_prefill_chunked.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp, sz, vp]
+        L.sanatan_prefill_workspace_bytes_partitioned.restype = sz
+        L.sanatan_prefill_workspace_bytes_partitioned.argtypes = [i32, i32, i32, i32, i32, pp]
+        L.sanatan_prefill_chunked_partitioned.restype = i32
+        L.sanatan_prefill_chunked_partitioned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, pp, vp, vp,
+                                                          vp, vp, sz, vp]
         L.sanatan_decode_step.restype = i32
         L.sanatan_decode_step.argtypes = [vp, vp, vp, i32, i64, pp, vp, vp, vp, vp]
         L.sanatan_decode_step_positions.restype = i32
@@ -93,7 +98,8 @@ def lib():
 
 EXPORTED = [
     "sanatan_state_bytes", "sanatan_status_string", "sanatan_featurize", "sanatan_prefill_workspace_bytes",
-    "sanatan_prefill_chunked", "sanatan_decode_step", "sanatan_decode_step_positions",
+    "sanatan_prefill_chunked", "sanatan_prefill_workspace_bytes_partitioned", "sanatan_prefill_chunked_partitioned",
+    "sanatan_decode_step", "sanatan_decode_step_positions",
     "sanatan_compact_state_bytes", "sanatan_state_compact", "sanatan_state_expand", "sanatan_decode_step_compact",
     "sanatan_four_channel_state_bytes", "sanatan_decode_step_four_channel",
     "sanatan_quadratic_workspace_bytes",
@@ -229,8 +235,22 @@ def sanatan_prefill_workspace_bytes(B: int, H: int, T: int, chunk: int, params: 
     return int(lib().sanatan_prefill_workspace_bytes(B, H, T, chunk, ctypes.byref(p) if p is not None else None))
 
 
+def sanatan_prefill_workspace_bytes_partitioned(B: int, H: int, T: int, chunk: int, workgroups: int,
+                                                params: Params | None = None) -> int:
+    p = params.struct() if params is not None else None
+    return int(lib().sanatan_prefill_workspace_bytes_partitioned(B, H, T, chunk, int(workgroups),
+                                                                  ctypes.byref(p) if p is not None else None))
+
+
 def sanatan_prefill_chunked(q, k, v, chunk: int, params: Params, pos0: int = 0, S=None, z=None, out=None, ws=None):
     """Chunked causal p=1 attention; S, z (fp32, in/out) optional.  Returns out [B,H,T,64]."""
+    return sanatan_prefill_chunked_partitioned(q, k, v, chunk, 0, params, pos0=pos0, S=S, z=z, out=out, ws=ws,
+                                               _entry="sanatan_prefill_chunked")
+
+
+def sanatan_prefill_chunked_partitioned(q, k, v, chunk: int, workgroups: int, params: Params, pos0: int = 0, S=None,
+                                        z=None, out=None, ws=None, _entry="sanatan_prefill_chunked_partitioned"):
+    """Test hook: the prefill with the chunk list split over `workgroups` workgroups (0 = one per CU)."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -247,12 +267,18 @@ def sanatan_prefill_chunked(q, k, v, chunk: int, params: Params, pos0: int = 0, 
             _check_tensor(t, name, dtypes=("float32",))
             _check_shape(t, name, shape)
     p = params.struct()
-    need = int(lib().sanatan_prefill_workspace_bytes(B, H, T, chunk, ctypes.byref(p)))
+    need = int(lib().sanatan_prefill_workspace_bytes_partitioned(B, H, T, chunk, int(workgroups), ctypes.byref(p)))
     if ws is None:
         ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
-    _check(lib().sanatan_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(chunk), int(pos0),
-                                         ctypes.byref(p), _ptr(S), _ptr(z), _ptr(out), _ptr(ws), ws.numel(),
-                                         _stream()), "sanatan_prefill_chunked")
+    if _entry == "sanatan_prefill_chunked":
+        st = lib().sanatan_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(chunk), int(pos0),
+                                           ctypes.byref(p), _ptr(S), _ptr(z), _ptr(out), _ptr(ws), ws.numel(),
+                                           _stream())
+    else:
+        st = lib().sanatan_prefill_chunked_partitioned(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T,
+                                                       int(chunk), int(workgroups), int(pos0), ctypes.byref(p),
+                                                       _ptr(S), _ptr(z), _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _check(st, _entry)
     return out
 
 

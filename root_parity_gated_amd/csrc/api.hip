@@ -46,6 +46,16 @@ bool sizes_ok(int B, int H, int T) {
 
 sanatan_status hip_status(hipError_t e) { return e == hipSuccess ? SANATAN_OK : SANATAN_ERR_HIP; }
 
+// Positions are converted to fp64 exactly and reduced with an exact two-product, so any |pos| < 2^53 keeps the
+// phase accurate to about 2^-53 revolutions.
+bool pos_ok(int64_t p) { return p > -(int64_t(1) << 53) && p < (int64_t(1) << 53); }
+
+// Longest sequence a prefill call accepts: the per-sequence byte ranges of the buffer loads (position table
+// [T][d] fp32, key and value rows) must fit the 31-bit range of a buffer descriptor.
+constexpr int kMaxPrefillT = 1 << 22;
+// Longest sequence of the quadratic form: its key-feature rows [T][6d] fp32 must fit the same range.
+constexpr int kMaxQuadraticT = 1 << 20;
+
 }  // namespace
 
 extern "C" {
@@ -69,35 +79,53 @@ const char* sanatan_status_string(sanatan_status status) {
 sanatan_status sanatan_featurize(const void* u, sanatan_dtype in_t, int B, int H, int T, int64_t pos0,
                                  const sanatan_params* params, void* phi, sanatan_dtype out_t, hipStream_t stream) {
   if (!u || !phi || !dtype_ok(in_t) || !dtype_ok(out_t) || !sizes_ok(B, H, T)) return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   return hip_status(launch_featurize(u, in_t, B, H, T, pos0, consts(params), phi, out_t, stream));
 }
 
-size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const sanatan_params* params) {
+size_t sanatan_prefill_workspace_bytes_partitioned(int B, int H, int T, int chunk, int workgroups,
+                                                  const sanatan_params* params) {
   (void)params;
   PrefillPlan plan;
-  if (!sizes_ok(B, H, T) || chunk <= 0 || !prefill_plan(B, H, T, chunk, &plan)) return 0;
+  if (!sizes_ok(B, H, T) || T > kMaxPrefillT || chunk <= 0 || !prefill_plan(B, H, T, chunk, workgroups, false, &plan))
+    return 0;
   return plan.total_bytes;
+}
+
+size_t sanatan_prefill_workspace_bytes(int B, int H, int T, int chunk, const sanatan_params* params) {
+  return sanatan_prefill_workspace_bytes_partitioned(B, H, T, chunk, 0, params);
+}
+
+sanatan_status sanatan_prefill_chunked_partitioned(const void* q, const void* k, const void* v, sanatan_dtype t,
+                                                   int B, int H, int T, int chunk, int workgroups, int64_t pos0,
+                                                   const sanatan_params* params, float* S, float* z, void* out,
+                                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || chunk <= 0 || workgroups < 0)
+    return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxPrefillT) return SANATAN_ERR_UNSUPPORTED;
+  if ((S == nullptr) != (z == nullptr)) return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (chunk % 16 != 0 || !prefill_chunk_supported(chunk, t)) return SANATAN_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!prefill_plan(B, H, T, chunk, workgroups, S != nullptr, &plan)) return SANATAN_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < plan.total_bytes) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_prefill(q, k, v, t, B, H, T, pos0, consts(params), S, z, out, ws, plan, stream));
 }
 
 sanatan_status sanatan_prefill_chunked(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
                                        int T, int chunk, int64_t pos0, const sanatan_params* params, float* S,
                                        float* z, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || chunk <= 0) return SANATAN_ERR_INVALID_ARG;
-  if ((S == nullptr) != (z == nullptr)) return SANATAN_ERR_INVALID_ARG;
-  const sanatan_status ps = check_params(params);
-  if (ps != SANATAN_OK) return ps;
-  if (chunk % 16 != 0 || !prefill_chunk_supported(chunk, t)) return SANATAN_ERR_UNSUPPORTED;
-  PrefillPlan plan;
-  if (!prefill_plan(B, H, T, chunk, &plan)) return SANATAN_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < plan.total_bytes) return SANATAN_ERR_WORKSPACE;
-  return hip_status(launch_prefill(q, k, v, t, B, H, T, pos0, consts(params), S, z, out, ws, plan, stream));
+  return sanatan_prefill_chunked_partitioned(q, k, v, t, B, H, T, chunk, 0, pos0, params, S, z, out, ws, ws_bytes,
+                                             stream);
 }
 
 sanatan_status sanatan_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
                                    const sanatan_params* params, float* S, float* z, float* out, hipStream_t stream) {
-  if (!q || !k || !v || !S || !z || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !S || !z || !out || N <= 0 || !pos_ok(pos)) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   return hip_status(launch_decode_step(q, k, v, N, pos, nullptr, 0, consts(params), S, z, out, stream));
@@ -132,7 +160,7 @@ sanatan_status sanatan_state_expand(const float* Sc, const float* zc, int N, flo
 sanatan_status sanatan_decode_step_compact(const float* q, const float* k, const float* v, int N, int64_t pos,
                                            const int64_t* posv, const sanatan_params* params, float* Sc,
                                            float* zc, float* out, hipStream_t stream) {
-  if (!q || !k || !v || !Sc || !zc || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !Sc || !zc || !out || N <= 0 || (!posv && !pos_ok(pos))) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   return hip_status(launch_decode_step(q, k, v, N, pos, posv, 1, consts(params), Sc, zc, out, stream));
@@ -146,7 +174,7 @@ size_t sanatan_four_channel_state_bytes(int d, int d_v) {
 sanatan_status sanatan_decode_step_four_channel(const float* q, const float* k, const float* v, int N,
                                                 int64_t pos, const int64_t* posv, const sanatan_params* params,
                                                 float* S4, float* z4, float* out, hipStream_t stream) {
-  if (!q || !k || !v || !S4 || !z4 || !out || N <= 0) return SANATAN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !S4 || !z4 || !out || N <= 0 || (!posv && !pos_ok(pos))) return SANATAN_ERR_INVALID_ARG;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   return hip_status(launch_decode_step(q, k, v, N, pos, posv, 2, consts(params), S4, z4, out, stream));
@@ -154,7 +182,7 @@ sanatan_status sanatan_decode_step_four_channel(const float* q, const float* k, 
 
 size_t sanatan_quadratic_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params) {
   (void)params;
-  if (!sizes_ok(B, H, T) || !dtype_ok(t)) return 0;
+  if (!sizes_ok(B, H, T) || T > kMaxQuadraticT || !dtype_ok(t)) return 0;
   return quadratic_ws_bytes(B, H, T, t);
 }
 
@@ -163,6 +191,8 @@ sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void
                                         size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || (p != 1 && p != 2))
     return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxQuadraticT) return SANATAN_ERR_UNSUPPORTED;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   if (!ws || ws_bytes < quadratic_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
@@ -174,6 +204,8 @@ sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, cons
                                               void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || (p != 1 && p != 2))
     return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxQuadraticT) return SANATAN_ERR_UNSUPPORTED;
   const sanatan_status ps = check_params(params);
   if (ps != SANATAN_OK) return ps;
   if (!ws || ws_bytes < quadratic_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;

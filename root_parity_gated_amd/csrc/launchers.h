@@ -50,7 +50,9 @@ struct PrefillPlan {
   size_t state_bytes;   // (B*H + G - 1) boundary states of kStateFloats fp32
   size_t total_bytes;
 };
-bool prefill_plan(int B, int H, int T, int chunk, PrefillPlan* plan);
+// workgroups: 0 = one per compute unit, else that many (capped at the chunk count); with_state: the call
+// passes an initial state (S, z)
+bool prefill_plan(int B, int H, int T, int chunk, int workgroups, bool with_state, PrefillPlan* plan);
 bool prefill_chunk_supported(int chunk, sanatan_dtype t);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
                           int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,

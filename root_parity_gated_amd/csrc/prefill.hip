@@ -26,7 +26,7 @@
 //     Phi(q) . z), far cheaper than a 32-column MFMA tile for one column.
 //   * Partial (num, den) over feature groups are added through LDS in a fixed order (bitwise
 //     deterministic) before the division.
-#include <stdlib.h>
+#include <atomic>
 
 #include "prefill_common.h"
 
@@ -373,31 +373,30 @@ bool prefill_chunk_supported(int chunk, sanatan_dtype t) {
   return chunk == 128 && t == SANATAN_BF16;
 }
 
+// Compute units of the current device, cached per device (the cache is written once per device; a racing
+// first call on two threads stores the same value).
 static int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus;
+  return n;
 }
 
 // Pieces per sequence above which the separate scan kernel is cheaper than letting each pass-3
 // workgroup add up its predecessors' increments.
 static constexpr int kFusedScanMaxPieces = 4;
 
-bool prefill_plan(int B, int H, int T, int chunk, PrefillPlan* plan) {
-  if (B <= 0 || H <= 0 || T <= 0 || chunk <= 0) return false;
+bool prefill_plan(int B, int H, int T, int chunk, int workgroups, bool with_state, PrefillPlan* plan) {
+  if (B <= 0 || H <= 0 || T <= 0 || chunk <= 0 || workgroups < 0) return false;
   const long long BH = (long long)B * H;
   const long long ncs = (T + chunk - 1) / chunk;
   const long long total = BH * ncs;
-  long long G = device_cus();
-  const char* env = getenv("SANATAN_PREFILL_WGS");
-  if (env && atoll(env) > 0) G = atoll(env);
+  long long G = workgroups > 0 ? workgroups : device_cus();
   if (G > total) G = total;
   plan->chunk = chunk;
   plan->ncs = (int)ncs;
@@ -413,7 +412,10 @@ bool prefill_plan(int B, int H, int T, int chunk, PrefillPlan* plan) {
     if (np > max_pieces) max_pieces = np;
   }
   plan->multi = max_pieces > 1;
-  plan->scanned = max_pieces > kFusedScanMaxPieces;
+  // With a caller state and a sequence in several pieces, the state must be read before any piece's
+  // final state is written back.  Pass 3 cannot guarantee that (the final piece of a sequence may run
+  // on another workgroup before the head piece starts), so the scan kernel, an earlier launch, reads it.
+  plan->scanned = max_pieces > kFusedScanMaxPieces || (plan->multi && with_state);
   return true;
 }
 

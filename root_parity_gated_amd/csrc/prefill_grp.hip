@@ -23,6 +23,8 @@
 // 16 to every entry, which one MFMA on two fragments of ones supplies (it costs the VALU nothing, unlike
 // writing 16 accumulator registers).  The bf16 kernels for 16-, 32- and 64-token chunks and the one for
 // 128-token chunks (further below) share this layout.
+#include <atomic>
+
 #include "prefill_common.h"
 
 namespace sanatan {
@@ -1111,14 +1113,14 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
 
 hipError_t launch_prefill_grp128(const PrefillArgs& a, hipStream_t stream) {
   static_assert(Geom128::lds <= 160 * 1024, "LDS budget");
-  static bool attr_set[64] = {};
+  static std::atomic<bool> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute((const void*)prefill_grp128_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, Geom128::lds);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL(prefill_grp128_kernel, dim3(a.G), dim3(256), Geom128::lds, stream, a);
   return hipGetLastError();
@@ -1128,10 +1130,10 @@ template <int CH>
 hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   using G = GeomG<CH>;
   static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
-  static bool attr_set[64] = {};
+  static std::atomic<bool> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::lds(true));
     if (e != hipSuccess) return e;
@@ -1143,7 +1145,7 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
                               GeomS8::lds);
       if (e != hipSuccess) return e;
     }
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   if (a.multi) {
     if constexpr (CH == 64)
@@ -1163,14 +1165,14 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
 
 // pass 1 for 128-token chunks: the 8-wave state kernel walks each chunk as two 64-token halves
 hipError_t launch_prefill_state8_128(const PrefillArgs& a, hipStream_t stream) {
-  static bool attr_set[64] = {};
+  static std::atomic<bool> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute((const void*)prefill_state8_kernel<128>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, GeomS8::lds);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL(prefill_state8_kernel<128>, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
   return hipGetLastError();

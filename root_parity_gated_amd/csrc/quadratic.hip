@@ -15,6 +15,8 @@
 // with the transposing LDS load), and its row sums (v_dot2) accumulate the denominator.  A wave
 // issues the score MFMAs of block kb + 1 with the weight VALU and V^T P MFMAs of block kb between
 // them (software pipelining across key blocks).
+#include <atomic>
+
 #include "prefill_common.h"
 
 namespace sanatan {
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     // Phi(K) rows start at channel C0 (kp skips the channels below), so the last row ends C0 kD elements
     // short of kF
     const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kp + (size_t)s0 * kF), (short)0, (int)(((Tn - s0) * kF - C0 * kD) * (int)sizeof(T)),
+        (void*)(kp + (size_t)s0 * kF), (short)0, (int)(((long long)(Tn - s0) * kF - C0 * kD) * (long long)sizeof(T)),
         kRawBufferWord3);
 #pragma unroll
     for (int p = 0; p < KPT; p++) dst[p] = __builtin_amdgcn_raw_buffer_load_b128(kr_, koff[p], 0, 0);
@@ -104,7 +106,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   auto fetch_v = [&](int kb) {
     const int s0 = kb * KB;
     const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vp + (size_t)s0 * kDV), (short)0, (int)((Tn - s0) * kDV * (int)sizeof(T)), kRawBufferWord3);
+        (void*)(vp + (size_t)s0 * kDV), (short)0, (int)((long long)(Tn - s0) * kDV * (long long)sizeof(T)),
+        kRawBufferWord3);
 #pragma unroll
     for (int p = 0; p < VPT; p++) pv[p] = __builtin_amdgcn_raw_buffer_load_b128(vr_, voff[p], 0, 0);
   };
@@ -354,14 +357,14 @@ hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int
   e = launch_featurize(k, t, B, H, Tn, pos0, mc, phik, t, stream);
   if (e != hipSuccess) return e;
   using G = QGeom<T, C0>;
-  static bool attr_set[64] = {};
+  static std::atomic<bool> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute((const void*)quadratic_kernel<T, P, C0>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             G::lds);
     if (e != hipSuccess) return e;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   const int nqb = (Tn + G::QROWS - 1) / G::QROWS;
   const int BH = B * H;

@@ -41,8 +41,15 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 __device__ __forceinline__ double phase_step(int a, double log2_base) {
   return exp2(-(double)a * (1.0 / kD) * log2_base) * 0.15915494309189533576888376;
 }
+// The product t * step is split into its rounded value p and its exact rounding error e (an fma two-product;
+// t converts exactly for |t| < 2^53), and each part is reduced on its own, so the phase keeps about 2^-53
+// revolutions of accuracy at any such position instead of losing the product's high bits.
 __device__ __forceinline__ float phase_at(int64_t t, double step) {
-  const double x = (double)t * step;
+#pragma clang fp contract(off)  // p must be the rounded product, or e would count the error twice
+  const double tt = (double)t;
+  const double p = tt * step;
+  const double e = fma(tt, step, -p);
+  const double x = (p - floor(p)) + e;
   return (float)(x - floor(x));
 }
 __device__ __forceinline__ float phase_rev(int64_t t, int a, double log2_base) {

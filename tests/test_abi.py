@@ -152,3 +152,42 @@ def test_workspace_sizes(L):
     rho = 2048 * 64 * 4
     G = (ws - rho) // state - 96 + 1
     assert (ws - rho) % state == 0 and 1 <= G <= 3072
+
+
+def test_position_and_length_ranges(L):
+    """Positions must satisfy |pos| < 2^53 (the exact fp64 reduction's range); the prefill takes T <= 2^22 and
+    the quadratic form T <= 2^20 (buffer-descriptor byte ranges)."""
+    p = params()
+    big = 1 << 53
+    pf = lambda pos0, T=128: L.sanatan_prefill_chunked(FAKE, FAKE, FAKE, 1, 1, 1, T, 64, pos0, ctypes.byref(p), None,
+                                                       None, FAKE, FAKE, 1 << 40, None)
+    assert pf(big) == rpg.SANATAN_ERR_INVALID_ARG
+    assert pf(big - 127) == rpg.SANATAN_ERR_INVALID_ARG      # the last token reaches 2^53
+    assert pf(-big) == rpg.SANATAN_ERR_INVALID_ARG
+    assert pf(0, T=(1 << 22) + 1) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert L.sanatan_prefill_workspace_bytes(1, 1, (1 << 22) + 1, 64, ctypes.byref(p)) == 0
+    assert L.sanatan_featurize(FAKE, 0, 1, 1, 8, big - 4, ctypes.byref(p), FAKE, 0, None) == \
+        rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_decode_step(FAKE, FAKE, FAKE, 4, big, ctypes.byref(p), FAKE, FAKE, FAKE, None) == \
+        rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_decode_step_compact(FAKE, FAKE, FAKE, 4, -big, None, ctypes.byref(p), FAKE, FAKE, FAKE,
+                                         None) == rpg.SANATAN_ERR_INVALID_ARG
+    q2 = lambda T, pos0=0: L.sanatan_quadratic_ref_p2(FAKE, FAKE, FAKE, 1, 1, 1, T, 2, pos0, ctypes.byref(p), FAKE,
+                                                      FAKE, 1 << 62, None)
+    assert q2((1 << 20) + 1) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert q2(64, pos0=big) == rpg.SANATAN_ERR_INVALID_ARG
+    assert L.sanatan_quadratic_workspace_bytes(1, 1, (1 << 20) + 1, 1, ctypes.byref(p)) == 0
+
+
+def test_partitioned_prefill_validation(L):
+    """The partition test hook: a negative workgroup count is refused, and the workspace follows the count."""
+    p = params()
+    part = lambda wgs, ws_bytes=1 << 40: L.sanatan_prefill_chunked_partitioned(
+        FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, wgs, 0, ctypes.byref(p), None, None, FAKE, FAKE, ws_bytes, None)
+    assert part(-1) == rpg.SANATAN_ERR_INVALID_ARG
+    state = L.sanatan_state_bytes(64, 64)
+    w1 = L.sanatan_prefill_workspace_bytes_partitioned(2, 3, 1000, 64, 1, ctypes.byref(p))
+    w5 = L.sanatan_prefill_workspace_bytes_partitioned(2, 3, 1000, 64, 5, ctypes.byref(p))
+    assert w5 - w1 == 4 * state
+    assert part(2, ws_bytes=16) == rpg.SANATAN_ERR_WORKSPACE
+    assert L.sanatan_prefill_workspace_bytes_partitioned(2, 3, 1000, 64, -2, ctypes.byref(p)) == 0

@@ -160,14 +160,13 @@ def test_quadratic_short_sequences(torch_dev, dtype, p, T):
 
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("wgs", [5, 13, 23, 30, 59])
-def test_prefill_many_partitions(torch_dev, monkeypatch, wgs, chunk):
+def test_prefill_many_partitions(torch_dev, wgs, chunk):
     """bf16 chunks of 64 and 128 tokens with the workgroup count forced: ranges of many lengths and
     several pieces per sequence (up to 10 at chunk 64, 5 at chunk 128), so both the fused predecessor sums
     and the scan kernel run, from a nonzero initial state.  Output and final state against the oracle."""
     import root_parity_gated_amd as rpg
 
     torch = torch_dev
-    monkeypatch.setenv("SANATAN_PREFILL_WGS", str(wgs))
     B, H, T = 2, 3, 2048 - 29
     q, k, v, om = si.attention_inputs(450 + wgs, B, H, T, "bf16")
     # initial state: the state after a seeded 300-token prefix, continued at position 300
@@ -175,8 +174,8 @@ def test_prefill_many_partitions(torch_dev, monkeypatch, wgs, chunk):
     _, S0, z0 = oracle_heads(pq, pk, pv, om)
     S = torch.from_numpy(S0.astype(np.float32)).cuda()
     z = torch.from_numpy(z0.astype(np.float32)).cuda()
-    out = rpg.sanatan_prefill_chunked(dev(torch, q, "bf16"), dev(torch, k, "bf16"), dev(torch, v, "bf16"), chunk,
-                                      params(torch, om), pos0=300, S=S, z=z)
+    out = rpg.sanatan_prefill_chunked_partitioned(dev(torch, q, "bf16"), dev(torch, k, "bf16"), dev(torch, v, "bf16"),
+                                                  chunk, wgs, params(torch, om), pos0=300, S=S, z=z)
     torch.cuda.synchronize()
     want, Sw, zw = oracle_heads(np.concatenate([pq, q], 2), np.concatenate([pk, k], 2), np.concatenate([pv, v], 2), om)
     assert row_rel_err(host(out), want[:, :, 300:]) <= TOL["bf16"]

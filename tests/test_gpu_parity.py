@@ -156,8 +156,8 @@ def test_prefill_ragged_multi_piece_with_state(torch_dev, dtype, chunk, B, H, T)
     assert np.abs(host(zg) - zw).max() <= tol_s * np.abs(zw).max()
 
 
-def test_prefill_single_workgroup_and_determinism(torch_dev, monkeypatch):
-    """One workgroup walking every sequence (SANATAN_PREFILL_WGS=1) gives the same result up to
+def test_prefill_single_workgroup_and_determinism(torch_dev):
+    """One workgroup walking every sequence (the partition hook at 1) gives the same result up to
     rounding, and repeated runs are bitwise identical."""
     import root_parity_gated_amd as rpg
 
@@ -166,8 +166,7 @@ def test_prefill_single_workgroup_and_determinism(torch_dev, monkeypatch):
     args = [dev(torch, x, "bf16") for x in (q, k, v)]
     a = rpg.sanatan_prefill_chunked(*args, 32, params(torch, om)).clone()
     b = rpg.sanatan_prefill_chunked(*args, 32, params(torch, om)).clone()
-    monkeypatch.setenv("SANATAN_PREFILL_WGS", "1")
-    c = rpg.sanatan_prefill_chunked(*args, 32, params(torch, om)).clone()
+    c = rpg.sanatan_prefill_chunked_partitioned(*args, 32, 1, params(torch, om)).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     want, _, _ = oracle_heads(q, k, v, om)
