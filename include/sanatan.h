@@ -122,6 +122,21 @@ sanatan_status sanatan_prefill_chunked_partitioned(const void* q, const void* k,
                                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * sanatan_prefill_chunked_noalloc -- sanatan_prefill_chunked without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The workspace is a fixed 48 MiB device array inside the library (one per GPU, held until
+ * the process ends); the call allocates nothing.  Arguments, results and errors are those of
+ * sanatan_prefill_chunked without ws/ws_bytes, plus SANATAN_ERR_WORKSPACE when the sizes need more than
+ * 48 MiB of workspace (sanatan_prefill_workspace_bytes() > 48 MiB: e.g. B*H above about 240 sequences at
+ * T = 2048 on a 256-CU device), and SANATAN_ERR_HIP if the array's address cannot be found.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU race; order them on
+ * one stream.  The results are bitwise those of sanatan_prefill_chunked with the same arguments.
+ */
+sanatan_status sanatan_prefill_chunked_noalloc(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                               int H, int T, int chunk, int64_t pos0, const sanatan_params* params,
+                                               float* S, float* z, void* out, hipStream_t stream);
+
+/*
  * sanatan_decode_step -- one token of the p=1 constant-state recurrence for N independent
  * head-states (e.g. batch x layers x heads).  [N] §2.7: write the token into the state, then read.
  *   q, k : [N][d] fp32;  v : [N][d_v] fp32;  pos : position of this token (shared by all N), |pos| < 2^53

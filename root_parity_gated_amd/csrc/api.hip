@@ -123,6 +123,24 @@ sanatan_status sanatan_prefill_chunked(const void* q, const void* k, const void*
                                              stream);
 }
 
+sanatan_status sanatan_prefill_chunked_noalloc(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                               int H, int T, int chunk, int64_t pos0, const sanatan_params* params,
+                                               float* S, float* z, void* out, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T) || chunk <= 0) return SANATAN_ERR_INVALID_ARG;
+  if ((S == nullptr) != (z == nullptr)) return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxPrefillT) return SANATAN_ERR_UNSUPPORTED;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (chunk % 16 != 0 || !prefill_chunk_supported(chunk, t)) return SANATAN_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!prefill_plan(B, H, T, chunk, 0, S != nullptr, &plan)) return SANATAN_ERR_INVALID_ARG;
+  if (plan.total_bytes > noalloc_scratch_bytes()) return SANATAN_ERR_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return SANATAN_ERR_HIP;
+  return hip_status(launch_prefill(q, k, v, t, B, H, T, pos0, consts(params), S, z, out, ws, plan, stream));
+}
+
 sanatan_status sanatan_decode_step(const float* q, const float* k, const float* v, int N, int64_t pos,
                                    const sanatan_params* params, float* S, float* z, float* out, hipStream_t stream) {
   if (!q || !k || !v || !S || !z || !out || N <= 0 || !pos_ok(pos)) return SANATAN_ERR_INVALID_ARG;

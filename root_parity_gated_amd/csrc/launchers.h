@@ -58,6 +58,10 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
                           int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,
                           const PrefillPlan& plan, hipStream_t stream);
 
+// The no-allocation prefill's workspace: a fixed device array of the library (one per GPU)
+size_t noalloc_scratch_bytes();
+void* noalloc_scratch();  // this device's array (address looked up once per device); null on error
+
 size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t);
 // four_channel: the unclipped four-channel kernel ([1, r, r cos, r sin] per dim) instead of the six-channel one
 hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
