@@ -73,6 +73,10 @@ def _load():
     lib.oracle_recurrent_heads.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            i64, dp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double, ctypes.c_double, dp, dp, dp]
+    lib.oracle_attention_direct_grad.restype = None
+    lib.oracle_attention_direct_grad.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
+                                                 ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                                 ctypes.c_double, ctypes.c_int, dp, dp, dp, dp]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -193,3 +197,21 @@ def recurrent_heads(q, k, v, omega, pos0: int = 0, gamma: float = GAMMA, lambda_
                                    float(gamma), float(lambda_base), float(c), float(eps), _ptr(S), _ptr(z),
                                    _ptr(out) if want_out else None)
     return out, S, z
+
+
+def attention_direct_grad(q, k, v, dout, omega, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE,
+                          c: float | None = None, eps: float = EPS, p: int = 1):
+    """Gradient of sum_t <dout_t, o_t> of the direct form for ONE head: q,k [T,d], v,dout [T,dv], omega [d].
+    Returns (dq [T,d], dk [T,d], dv [T,dv], domega [d])."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    T, d = q.shape
+    dv = v.shape[1]
+    if c is None:
+        c = 4.0 * d
+    om = _f64(omega).reshape(d)
+    dq, dk = np.empty((T, d)), np.empty((T, d))
+    dvv, dom = np.empty((T, dv)), np.empty((d,))
+    _load().oracle_attention_direct_grad(_ptr(q), _ptr(k), _ptr(v), _ptr(g), T, d, dv, _ptr(om), float(gamma),
+                                         float(lambda_base), float(c), float(eps), int(p), _ptr(dq), _ptr(dk),
+                                         _ptr(dvv), _ptr(dom))
+    return dq, dk, dvv, dom

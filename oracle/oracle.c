@@ -234,6 +234,142 @@ void oracle_recurrent_heads(const double* q, const double* k, const double* v, i
   }
 }
 
+/*
+ * Gradient of the direct form, one head: the derivatives of L = sum_t <g_t, o_t> (g = dout [T][dv], the
+ * gradient arriving at the outputs) with respect to q, k [T][d], v [T][dv] and omega [d], for the weights
+ * w(t,s) = (kappa(t,s)/c)^p of oracle_attention_direct.  Needed because omega is learned ([N] §2.2) and the
+ * method is trained, p = 2 first, then adapted to p = 1 ([N] §4.1).  Plain chain rule through the definition:
+ *   D_t = sum_{s<=t} w_ts + eps,  o_t = sum_{s<=t} w_ts v_s / D_t
+ *   dL/dw_ts   = <g_t, v_s - o_t> / D_t                  dL/dv_s = sum_{t>=s} w_ts g_t / D_t
+ *   dw/dkappa  = p kappa^(p-1) / c^p
+ *   kappa_ts   = sum_a (1 + r_qa r_ka)(1 + cos x_a),  x_a = theta_qa - theta_ka + (t - s) lambda_a
+ *   dkappa/dtheta_qa = -(1 + r_qa r_ka) sin x_a + r_ka (1 + cos x_a) r'(theta_qa)
+ *   dkappa/dtheta_ka = +(1 + r_qa r_ka) sin x_a + r_qa (1 + cos x_a) r'(theta_ka)
+ *   dkappa/domega_a  = r_ka (1 + cos x_a) r'(theta_qa) + r_qa (1 + cos x_a) r'(theta_ka)
+ *   r'(theta)  = dr/dtheta = dr/domega = gamma (1 - r^2)(-sin(theta + omega) - cos(theta + omega))
+ *   dtheta/du  = pi / (1 + |u|)^2    (theta is C^1 at u = 0, with this value there)
+ * The query-side terms are summed over s <= t for each t, the key-side terms over t >= s for each s, in two
+ * separate loops (each recomputes kappa), so that every output is summed by one thread in a fixed order.
+ */
+static double sanatan_root_slope(double theta, double omega, double gamma, double r) {
+  return gamma * (1.0 - r * r) * (-sin(theta + omega) - cos(theta + omega));
+}
+
+void oracle_attention_direct_grad(const double* q, const double* k, const double* v, const double* g, int T, int d,
+                                  int dv, const double* omega, double gamma, double lambda_base, double c,
+                                  double eps, int p, double* dq, double* dk, double* dvv, double* domega) {
+  const size_t Td = (size_t)T * d;
+  double* thq = (double*)malloc(sizeof(double) * Td);
+  double* thk = (double*)malloc(sizeof(double) * Td);
+  double* rq = (double*)malloc(sizeof(double) * Td);
+  double* rk = (double*)malloc(sizeof(double) * Td);
+  double* sq = (double*)malloc(sizeof(double) * Td); /* r'(theta) of each query component */
+  double* sk = (double*)malloc(sizeof(double) * Td);
+  double* lam = (double*)malloc(sizeof(double) * (size_t)d);
+  double* o = (double*)malloc(sizeof(double) * (size_t)T * dv);
+  double* D = (double*)malloc(sizeof(double) * (size_t)T);
+  double* dom_q = (double*)calloc(Td, sizeof(double)); /* per-query-row omega terms, summed at the end */
+  double* dom_k = (double*)calloc(Td, sizeof(double));
+  for (int a = 0; a < d; a++) lam[a] = sanatan_freq(a, d, lambda_base);
+  for (size_t i = 0; i < Td; i++) {
+    const int a = (int)(i % (size_t)d);
+    thq[i] = sanatan_angle(q[i]);
+    thk[i] = sanatan_angle(k[i]);
+    rq[i] = sanatan_root(thq[i], omega[a], gamma);
+    rk[i] = sanatan_root(thk[i], omega[a], gamma);
+    sq[i] = sanatan_root_slope(thq[i], omega[a], gamma, rq[i]);
+    sk[i] = sanatan_root_slope(thk[i], omega[a], gamma, rk[i]);
+  }
+  const double cp = pow(c, (double)p);
+  /* kappa of one pair, from the tabulated angles and roots (the cosine of a difference, as in the forward) */
+#define KAPPA_OF(t, s, out_kap)                                                                          \
+  do {                                                                                                   \
+    double acc_ = 0.0;                                                                                   \
+    for (int a_ = 0; a_ < d; a_++) {                                                                     \
+      const double x_ = thq[(size_t)(t) * d + a_] - thk[(size_t)(s) * d + a_] + (double)((t) - (s)) * lam[a_]; \
+      acc_ += (1.0 + rq[(size_t)(t) * d + a_] * rk[(size_t)(s) * d + a_]) * (1.0 + cos(x_));            \
+    }                                                                                                    \
+    (out_kap) = acc_;                                                                                    \
+  } while (0)
+
+  /* forward rows: o_t and D_t */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < T; t++) {
+    double den = 0.0;
+    double* ot = o + (size_t)t * dv;
+    for (int n = 0; n < dv; n++) ot[n] = 0.0;
+    for (int s = 0; s <= t; s++) {
+      double kap;
+      KAPPA_OF(t, s, kap);
+      const double w = pow(kap, (double)p) / cp;
+      den += w;
+      for (int n = 0; n < dv; n++) ot[n] += w * v[(size_t)s * dv + n];
+    }
+    D[t] = den + eps;
+    for (int n = 0; n < dv; n++) ot[n] /= D[t];
+  }
+  /* query side: dq and the query-side omega terms, one row t per iteration */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < T; t++) {
+    double* dth = (double*)calloc((size_t)d, sizeof(double));
+    for (int s = 0; s <= t; s++) {
+      double kap;
+      KAPPA_OF(t, s, kap);
+      double gv = 0.0;
+      for (int n = 0; n < dv; n++) gv += g[(size_t)t * dv + n] * (v[(size_t)s * dv + n] - o[(size_t)t * dv + n]);
+      const double G = gv / D[t] * (double)p * pow(kap, (double)(p - 1)) / cp;
+      for (int a = 0; a < d; a++) {
+        const size_t ti = (size_t)t * d + a, si = (size_t)s * d + a;
+        const double x = thq[ti] - thk[si] + (double)(t - s) * lam[a];
+        dth[a] += G * (-(1.0 + rq[ti] * rk[si]) * sin(x) + rk[si] * (1.0 + cos(x)) * sq[ti]);
+        dom_q[ti] += G * rk[si] * (1.0 + cos(x)) * sq[ti];
+      }
+    }
+    for (int a = 0; a < d; a++) {
+      const double u = q[(size_t)t * d + a];
+      dq[(size_t)t * d + a] = dth[a] * ORACLE_PI / ((1.0 + fabs(u)) * (1.0 + fabs(u)));
+    }
+    free(dth);
+  }
+  /* key side: dk, dv and the key-side omega terms, one row s per iteration */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < T; s++) {
+    double* dth = (double*)calloc((size_t)d, sizeof(double));
+    double* dvs = dvv + (size_t)s * dv;
+    for (int n = 0; n < dv; n++) dvs[n] = 0.0;
+    for (int t = s; t < T; t++) {
+      double kap;
+      KAPPA_OF(t, s, kap);
+      const double w = pow(kap, (double)p) / cp;
+      double gv = 0.0;
+      for (int n = 0; n < dv; n++) {
+        gv += g[(size_t)t * dv + n] * (v[(size_t)s * dv + n] - o[(size_t)t * dv + n]);
+        dvs[n] += w * g[(size_t)t * dv + n] / D[t];
+      }
+      const double G = gv / D[t] * (double)p * pow(kap, (double)(p - 1)) / cp;
+      for (int a = 0; a < d; a++) {
+        const size_t ti = (size_t)t * d + a, si = (size_t)s * d + a;
+        const double x = thq[ti] - thk[si] + (double)(t - s) * lam[a];
+        dth[a] += G * ((1.0 + rq[ti] * rk[si]) * sin(x) + rq[ti] * (1.0 + cos(x)) * sk[si]);
+        dom_k[si] += G * rq[ti] * (1.0 + cos(x)) * sk[si];
+      }
+    }
+    for (int a = 0; a < d; a++) {
+      const double u = k[(size_t)s * d + a];
+      dk[(size_t)s * d + a] = dth[a] * ORACLE_PI / ((1.0 + fabs(u)) * (1.0 + fabs(u)));
+    }
+    free(dth);
+  }
+#undef KAPPA_OF
+  for (int a = 0; a < d; a++) {
+    double acc = 0.0;
+    for (int t = 0; t < T; t++) acc += dom_q[(size_t)t * d + a] + dom_k[(size_t)t * d + a];
+    domega[a] = acc;
+  }
+  free(thq); free(thk); free(rq); free(rk); free(sq); free(sk); free(lam); free(o); free(D); free(dom_q);
+  free(dom_k);
+}
+
 /* Number of threads OpenMP will use (reported next to oracle timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -34,6 +34,13 @@ MUTS = [
   ("recurrent read before write", None, None),
   ("S transposed", "S[(size_t)f * dv + n] += fk[f]", "S[(size_t)n * 6 * d + f] += fk[f]"),
   ("direct weight not normalised by c", "double w = kap / c;", "double w = kap;"),
+  ("grad query sin sign", "dth[a] += G * (-(1.0 + rq[ti] * rk[si]) * sin(x)", "dth[a] += G * ((1.0 + rq[ti] * rk[si]) * sin(x)"),
+  ("grad key root slope dropped", "+ rq[ti] * (1.0 + cos(x)) * sk[si]);", ");"),
+  ("grad output term dropped", "(v[(size_t)s * dv + n] - o[(size_t)t * dv + n])", "v[(size_t)s * dv + n]"),
+  ("grad angle slope not squared", "ORACLE_PI / ((1.0 + fabs(u)) * (1.0 + fabs(u)))", "ORACLE_PI / (1.0 + fabs(u))"),
+  ("grad root slope sign", "(-sin(theta + omega) - cos(theta + omega))", "(-sin(theta + omega) + cos(theta + omega))"),
+  ("grad power factor dropped", "(double)p * pow(kap, (double)(p - 1))", "pow(kap, (double)(p - 1))"),
+  ("grad value weight not normalised", "dvs[n] += w * g[(size_t)t * dv + n] / D[t];", "dvs[n] += w * g[(size_t)t * dv + n];"),
 ]
 
 READ_BEFORE_WRITE = (
@@ -54,11 +61,11 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
                     ignore=shutil.ignore_patterns("*.so", "*.tmp*", "__pycache__"))
     (tmp_path / "tests" / "golden").mkdir(parents=True)
-    for f in ("conftest.py", "test_oracle_pins.py", "test_oracle_four_channel.py"):
+    for f in ("conftest.py", "test_oracle_pins.py", "test_oracle_four_channel.py", "test_oracle_grad.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
     shutil.copy(os.path.join(ROOT, "tests", "golden", "pages_values.json"), tmp_path / "tests" / "golden")
     (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py",
-                        "tests/test_oracle_four_channel.py"],
+                        "tests/test_oracle_four_channel.py", "tests/test_oracle_grad.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "planted mistake '%s' passed every pin:\n%s" % (name, r.stdout[-2000:])
