@@ -355,6 +355,35 @@ def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_c
     return eager, graph
 
 
+def backward_flops(B, H, T):
+    """Algorithmic FLOPs of the attention backward: per causal pair the score kappa (2 x 6d), <g_t, v_s>
+    (2 d_v), and the three gradient products dPhi(q) (2 x 6d), dPhi(k) (2 x 6d) and dv (2 d_v)."""
+    pairs = T * (T + 1) // 2
+    return B * H * pairs * 2 * (3 * F + 2 * DV)
+
+
+def bench_backward(torch, rpg, si, w, p_exp, steps, warmup):
+    """ms per call (eager, graph-replayed) of sanatan_attention_backward on workload w's inputs with p = p_exp,
+    dout ~ N(0, 1) in the same dtype."""
+    q, k, v, om = si.workload_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(dt) for x in (q, k, v))
+    del q, k, v
+    g = torch.randn(vd.shape, generator=torch.Generator(device="cuda").manual_seed(w.seed), device="cuda").to(dt)
+    p = rpg.Params(omega=torch.from_numpy(om).cuda(), gamma=w.gamma, eps=w.eps, lambda_base=w.lambda_base)
+    code = rpg.SANATAN_BF16 if w.dtype == "bf16" else rpg.SANATAN_F32
+    ws = torch.empty((rpg.sanatan_attention_backward_workspace_bytes(w.B, w.H, w.T, code, p),), dtype=torch.uint8,
+                     device="cuda")
+    outs = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
+            torch.empty((om.shape[0], D), dtype=torch.float32, device="cuda"))
+    fn = lambda: rpg.sanatan_attention_backward(qd, kd, vd, g, p_exp, p, dq=outs[0], dk=outs[1], dv=outs[2],
+                                                domega=outs[3], ws=ws)
+    eager = timed_loop(torch, fn, steps, warmup)
+    gr = graph_of(torch, fn)
+    graph = timed_loop(torch, gr.replay, steps, warmup) if gr is not None else None
+    return eager, graph
+
+
 def bench_featurize(torch, rpg, si, w, steps, warmup):
     """Standalone feature map of one [B,H,T,64] operand (the keys of workload w) into [B,H,T,384], same dtype.
     HBM-bound: the algorithmic bytes are the input read once and Phi written once."""
@@ -500,6 +529,18 @@ def main():
             "roofline": {"bound": "mfma", "achieved": q4fl / (q4 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": q4fl / (q4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
             "note": "unclipped four-channel kernel: 2 (4d + d_v) flops per causal pair"}
+        for key, wb, pb in (("backward_p2", si.QUAD_P2, 2), ("backward_p1", w, 1)):
+            log(f"backward {wb.name}, p={pb}")
+            be, bg = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2)
+            bms = min(be, bg) if bg is not None else be
+            bfl = backward_flops(wb.B, wb.H, wb.T)
+            extras[key] = {"workload": f"{wb.name}_backward_p{pb}", "ms": bms, "ms_eager": be, "ms_graph": bg,
+                           "tokens_per_s": wb.B * wb.T / (bms * 1e-3), "flops_per_call": bfl,
+                           "roofline": {"bound": "mfma", "achieved": bfl / (bms * 1e-3) / 1e12,
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                           "note": "gradients of q, k, v, omega (sanatan_attention_backward, masked quadratic form); "
+                                   "flops: 2 (3 x 6d + 2 d_v) per causal pair"}
         log(f"featurize {w.name} keys")
         fms_e, fms_g, fbytes = bench_featurize(torch, rpg, si, w, max(5, args.steps // 5), 3)
         fms = min(fms_e, fms_g) if fms_g is not None else fms_e

@@ -249,6 +249,28 @@ sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, cons
                                               const sanatan_params* params, void* out, void* ws,
                                               size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Backward pass of normalised causal power attention: the gradients of L = sum_t <dout_t, o_t> with respect
+ * to q, k, v and the root anchors omega, where o is the output of sanatan_quadratic_ref_p2 with the same p
+ * (for p = 1 also of sanatan_prefill_chunked, which computes the same function).  omega is learned and the
+ * method is trained, p = 2 first and then p = 1 ([N] §2.2 root equation, §4.1), so both exponents are served.
+ *   q, k, dq, dk : [B][H][T][d];  v, dout, dv : [B][H][T][d_v]; element type t for all of them.
+ *   domega : DEVICE fp32 [n_param_heads][d]; row r receives the sum over every head h with h % n_param_heads
+ *            == r (overwritten, not accumulated).
+ *   p : 1 or 2 (else INVALID_ARG);  pos0 as in sanatan_featurize;  T at most 2^20 (else UNSUPPORTED).
+ *   ws : at least sanatan_attention_backward_workspace_bytes() bytes (else WORKSPACE): the position phase
+ *        table, Phi(Q) and Phi(K) in element type t, per-row statistics, fp32 feature gradients
+ *        [B][H][T][6d] for q and k, and per-block omega partials.
+ * The forward statistics (denominators and <dout_t, o_t>) are recomputed from q, k, v in fp32; the score
+ * products run on bf16 MFMA (fp32 MFMA for fp32 inputs) with fp32 accumulation.  Bitwise deterministic.
+ */
+size_t sanatan_attention_backward_workspace_bytes(int B, int H, int T, sanatan_dtype t,
+                                                  const sanatan_params* params);
+sanatan_status sanatan_attention_backward(const void* q, const void* k, const void* v, const void* dout,
+                                          sanatan_dtype t, int B, int H, int T, int p, int64_t pos0,
+                                          const sanatan_params* params, void* dq, void* dk, void* dv, float* domega,
+                                          void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static human-readable name of a status code. */
 const char* sanatan_status_string(sanatan_status status);
 

@@ -92,6 +92,11 @@ def lib():
         L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_quadratic_ref_p2.restype = i32
         L.sanatan_quadratic_ref_p2.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, sz, vp]
+        L.sanatan_attention_backward_workspace_bytes.restype = sz
+        L.sanatan_attention_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
+        L.sanatan_attention_backward.restype = i32
+        L.sanatan_attention_backward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp, vp,
+                                                 sz, vp]
         L.sanatan_quadratic_four_channel.restype = i32
         L.sanatan_quadratic_four_channel.argtypes = L.sanatan_quadratic_ref_p2.argtypes
         _lib = L
@@ -106,6 +111,7 @@ EXPORTED = [
     "sanatan_four_channel_state_bytes", "sanatan_decode_step_four_channel",
     "sanatan_quadratic_workspace_bytes",
     "sanatan_quadratic_ref_p2", "sanatan_quadratic_four_channel",
+    "sanatan_attention_backward_workspace_bytes", "sanatan_attention_backward",
 ]
 
 
@@ -473,3 +479,44 @@ def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0,
 def sanatan_quadratic_four_channel(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, ws=None):
     """The masked quadratic form on the unclipped four-channel kernel.  Returns out [B,H,T,64]."""
     return sanatan_quadratic_ref_p2(q, k, v, p_exp, params, pos0=pos0, out=out, ws=ws, four_channel=True)
+
+
+def sanatan_attention_backward_workspace_bytes(B: int, H: int, T: int, dtype_code: int,
+                                               params: Params | None = None) -> int:
+    p = params.struct() if params is not None else None
+    return int(lib().sanatan_attention_backward_workspace_bytes(B, H, T, dtype_code,
+                                                                ctypes.byref(p) if p is not None else None))
+
+
+def sanatan_attention_backward(q, k, v, dout, p_exp: int, params: Params, pos0: int = 0, dq=None, dk=None, dv=None,
+                               domega=None, ws=None):
+    """Gradient of sum(dout * o) for the normalised causal power attention o (p = 1: the chunked prefill's
+    output; p = 2: the quadratic form's).  Returns (dq, dk, dv [B,H,T,64] in the input dtype, domega fp32
+    [n_param_heads, 64])."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(t, name)
+    B, H, T = _attention_shape(q, k, v, params)
+    _check_shape(dout, "dout", (B, H, T, params.d_v))
+    _check_same_dtype(q, ("dout", dout))
+    pr = params.struct()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(t, name)
+        _check_shape(t, name, tuple(ref.shape))
+        _check_same_dtype(q, (name, t))
+    nph = pr.n_param_heads
+    if domega is None:
+        domega = torch.empty((nph, params.d), dtype=torch.float32, device=q.device)
+    _check_tensor(domega, "domega", dtypes=("float32",))
+    _check_shape(domega, "domega", (nph, params.d))
+    need = int(lib().sanatan_attention_backward_workspace_bytes(B, H, T, _dtype_code(q), ctypes.byref(pr)))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().sanatan_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _dtype_code(q), B, H, T, int(p_exp),
+                                            int(pos0), ctypes.byref(pr), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(domega),
+                                            _ptr(ws), ws.numel(), _stream()), "sanatan_attention_backward")
+    return dq, dk, dv, domega

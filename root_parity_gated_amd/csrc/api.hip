@@ -230,4 +230,26 @@ sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, cons
   return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, true, pos0, consts(params), out, ws, stream));
 }
 
+size_t sanatan_attention_backward_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params) {
+  (void)params;
+  if (!sizes_ok(B, H, T) || T > kMaxQuadraticT || !dtype_ok(t)) return 0;
+  return backward_ws_bytes(B, H, T, t);
+}
+
+sanatan_status sanatan_attention_backward(const void* q, const void* k, const void* v, const void* dout,
+                                          sanatan_dtype t, int B, int H, int T, int p, int64_t pos0,
+                                          const sanatan_params* params, void* dq, void* dk, void* dv, float* domega,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || !domega || !dtype_ok(t) || !sizes_ok(B, H, T) ||
+      (p != 1 && p != 2))
+    return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxQuadraticT) return SANATAN_ERR_UNSUPPORTED;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (!ws || ws_bytes < backward_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
+  return hip_status(
+      launch_backward(q, k, v, dout, t, B, H, T, p, pos0, consts(params), dq, dk, dv, domega, ws, stream));
+}
+
 }  // extern "C"

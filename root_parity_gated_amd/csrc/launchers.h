@@ -68,4 +68,11 @@ hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan
                             int p, bool four_channel, int64_t pos0, const MethodConsts& mc, void* out, void* ws,
                             hipStream_t stream);
 
+// Gradient of normalised causal power attention (p = 1 or 2) with respect to q, k, v and omega.  Workspace:
+// phase table, Phi(Q), Phi(K) (element type t), per-row statistics, fp32 feature gradients, omega partials.
+size_t backward_ws_bytes(int B, int H, int T, sanatan_dtype t);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* dout, sanatan_dtype t, int B,
+                           int H, int T, int p, int64_t pos0, const MethodConsts& mc, void* dq, void* dk, void* dv,
+                           float* domega, void* ws, hipStream_t stream);
+
 }  // namespace sanatan

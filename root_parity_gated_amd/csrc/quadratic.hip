@@ -47,11 +47,13 @@ struct QGeom {
 };
 
 // Two workgroups per CU for bf16; the fp32 operand fragments take the registers of one.
-template <typename T, int P, int C0>
+// STATS (the backward pass's forward statistics): instead of o, write per query row the denominator
+// Dn = sum_s kappa^p + eps c^p and delta = <g_t, o_t> with g = dout, as float2 stats[bh][t].
+template <typename T, int P, int C0, bool STATS = false>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     const T* __restrict__ q, const T* __restrict__ phik, const T* __restrict__ v, T* __restrict__ out,
     const float* __restrict__ rho, const float* __restrict__ omega, int nph, int H, int Tn, int BH, int nqb, float kr,
-    float eps_cp) {
+    float eps_cp, const T* __restrict__ gout = nullptr, float2* __restrict__ stats = nullptr) {
   using G = QGeom<T, C0>;
   typedef typename FragT<T>::type Frag;
   constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
@@ -331,6 +333,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   for (int mq = 0; mq < MQ; mq++) {
     const int t = row0 + 32 * mq + n32;
     const float den = xor32_sum(rs[mq]);
+    if constexpr (STATS) {
+      const int tc = min(t, Tn - 1);
+      const T* gp = gout + ((size_t)bh * Tn + tc) * kDV;
+      float dot = 0.0f;
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; i4++) dot = fmaf(to_f32(gp[32 * vt + 8 * j + 4 * h + i4]), num[mq][vt][4 * j + i4], dot);
+      dot = xor32_sum(dot);
+      const float dn = den + eps_cp;
+      if (t < Tn && h == 0) stats[(size_t)bh * Tn + t] = make_float2(dn, dot / dn);
+      continue;
+    }
     if (t < Tn) {
       // weights are kappa^p here, so epsilon is scaled by c^p: o = sum w v / (sum w + eps c^p)
       const float inv = 1.0f / (den + eps_cp);
@@ -345,13 +362,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
   }
 }
 
-size_t rho_bytes(int T) { return (((size_t)T * kD * sizeof(float)) + 255) & ~(size_t)255; }
+size_t rho_bytes_q(int T) { return (((size_t)T * kD * sizeof(float)) + 255) & ~(size_t)255; }
 
 template <typename T, int P, int C0>
 hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
                          const MethodConsts& mc, void* out, void* ws, sanatan_dtype t, hipStream_t stream) {
   float* rho = static_cast<float*>(ws);
-  void* phik = static_cast<char*>(ws) + rho_bytes(Tn);
+  void* phik = static_cast<char*>(ws) + rho_bytes_q(Tn);
   hipError_t e = launch_phase_table(rho, Tn, pos0, mc.log2_base, stream);
   if (e != hipSuccess) return e;
   e = launch_featurize(k, t, B, H, Tn, pos0, mc, phik, t, stream);
@@ -375,11 +392,43 @@ hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int
   return hipGetLastError();
 }
 
+template <typename T, int P>
+hipError_t launch_quad_stats_t(const void* q, const void* phik, const void* v, const void* g, int B, int H, int Tn,
+                               const float* rho, const MethodConsts& mc, float2* stats, hipStream_t stream) {
+  using G = QGeom<T, 1>;
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute((const void*)quadratic_kernel<T, P, 1, true>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, G::lds);
+    if (e != hipSuccess) return e;
+    attr_set[dev].store(true, std::memory_order_release);
+  }
+  const int nqb = (Tn + G::QROWS - 1) / G::QROWS;
+  const int BH = B * H;
+  hipLaunchKernelGGL((quadratic_kernel<T, P, 1, true>), dim3(BH * nqb), dim3(256), G::lds, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(phik), static_cast<const T*>(v), nullptr, rho,
+                     mc.omega, mc.nph, H, Tn, BH, nqb, mc.kr,
+                     P == 2 ? (float)((double)mc.ceps / (double)mc.inv_c) : mc.ceps, static_cast<const T*>(g), stats);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_quadratic_stats(const void* q, const void* phik, const void* v, const void* g, sanatan_dtype t,
+                                  int B, int H, int T, int p, const float* rho, const MethodConsts& mc, float2* stats,
+                                  hipStream_t stream) {
+  if (t == SANATAN_BF16)
+    return p == 1 ? launch_quad_stats_t<__bf16, 1>(q, phik, v, g, B, H, T, rho, mc, stats, stream)
+                  : launch_quad_stats_t<__bf16, 2>(q, phik, v, g, B, H, T, rho, mc, stats, stream);
+  return p == 1 ? launch_quad_stats_t<float, 1>(q, phik, v, g, B, H, T, rho, mc, stats, stream)
+                : launch_quad_stats_t<float, 2>(q, phik, v, g, B, H, T, rho, mc, stats, stream);
+}
 
 size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t) {
   const size_t el = (t == SANATAN_BF16) ? 2 : 4;
-  return rho_bytes(T) + (size_t)B * H * T * kF * el;
+  return rho_bytes_q(T) + (size_t)B * H * T * kF * el;
 }
 
 template <int C0>

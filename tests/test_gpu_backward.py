@@ -1,0 +1,145 @@
+"""The backward pass on the GPU against the oracle's fp64 gradient of the direct form.
+
+For L = sum(dout * o) with o the normalised causal power attention (p = 1 or 2), the GPU's dq, dk, dv and
+domega are compared with oracle.attention_direct_grad on the same seeded inputs (the oracle consumes the
+bf16-rounded values for bf16 cases).  Metric: per token row, max |error| / max |reference| over that row's
+components, maximised over rows (the forward's metric), with each row's scale floored at 1% of the largest
+row's in that tensor (a gradient row can vanish: dq of the first token is exactly 0 at eps = 0), and a tensor
+that vanishes as a whole (every gradient but dv of a single token) compared absolutely; domega per parameter
+row the same way.  Bars: the forward's, 1e-4 for fp32 inputs and 2e-2 for bf16 inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import sanatan_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import root_parity_gated_amd as rpg
+
+    rpg.lib()
+    return torch
+
+
+def dev(torch, x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rounded(x, dtype):
+    """The values the GPU sees: bf16 inputs are rounded to bf16 (round to nearest even)."""
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    import torch
+
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def row_rel_err(got, want, floor=1e-2):
+    """Per-row max |error| / max |reference|, the row's scale floored at `floor` times the largest row's.
+    Gradient rows can vanish: dq of the first token is exactly 0 at eps = 0 (o_0 = v_0), so without a floor
+    the metric would divide rounding noise by ~0."""
+    got = np.asarray(got, np.float64).reshape(-1, want.shape[-1])
+    want = np.asarray(want, np.float64).reshape(-1, want.shape[-1])
+    scale = np.abs(want).max(1)
+    if scale.max() < 1e-4:
+        # the whole tensor is an eps-sized signal (one token: o_0 = v_0 w / (w + eps), so dq, dk and domega are
+        # ~1e-6, below what fp32 resolves relative to <g, v> ~ 1): compare absolutely, against the unit scale of
+        # the N(0, 1) inputs
+        return float(np.abs(got - want).max())
+    scale = np.maximum(scale, floor * scale.max())
+    return float((np.abs(got - want).max(1) / scale).max())
+
+
+def run_case(torch, seed, B, H, T, dtype, p, nph=None, pos0=0, heads=None):
+    import root_parity_gated_amd as rpg
+
+    q, k, v, om = si.attention_inputs(seed, B, H, T, dtype)
+    rng = np.random.default_rng(seed + 17)
+    g = rounded(rng.standard_normal((B, H, T, 64)), dtype)
+    nph = H if nph is None else nph
+    om = om[:nph]
+    prm = rpg.Params(omega=torch.from_numpy(np.ascontiguousarray(om, dtype=np.float32)).cuda())
+    dq, dk, dv, dom = rpg.sanatan_attention_backward(dev(torch, q, dtype), dev(torch, k, dtype), dev(torch, v, dtype),
+                                                     dev(torch, g, dtype), p, prm, pos0=pos0)
+    torch.cuda.synchronize()
+    dq, dk, dv, dom = host(dq), host(dk), host(dv), host(dom)
+    want_dom = np.zeros_like(dom)
+    errs = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in range(B):
+        for h in range(H):
+            if heads is not None and (b, h) not in heads:
+                continue
+            wq, wk, wv, wo = oracle.attention_direct_grad(q[b, h], k[b, h], v[b, h], g[b, h], om[h % nph], p=p)
+            errs["dq"] = max(errs["dq"], row_rel_err(dq[b, h], wq))
+            errs["dk"] = max(errs["dk"], row_rel_err(dk[b, h], wk))
+            errs["dv"] = max(errs["dv"], row_rel_err(dv[b, h], wv))
+            want_dom[h % nph] += wo
+    if heads is None:
+        errs["domega"] = row_rel_err(dom, want_dom)
+    print(f"backward B{B} H{H} T{T} {dtype} p={p} nph={nph}: " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    return errs
+
+
+@pytest.mark.parametrize("p", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_small(torch_dev, dtype, p):
+    """Several key and query tiles, a ragged last tile, every head its own omega row."""
+    errs = run_case(torch_dev, 800 + p, 1, 3, 200, dtype, p)
+    for name, e in errs.items():
+        assert e <= TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 129])
+def test_backward_edge_lengths(torch_dev, T):
+    """One token, and lengths around the 32-token block and 128-token tile edges."""
+    for p in (1, 2):
+        errs = run_case(torch_dev, 810 + T, 1, 2, T, "f32", p)
+        for name, e in errs.items():
+            assert e <= TOL["f32"], (name, p, e)
+
+
+def test_backward_shared_omega_rows(torch_dev):
+    """Two batches and six heads over two omega rows: each row's gradient sums over every head using it."""
+    errs = run_case(torch_dev, 820, 2, 6, 96, "f32", 2, nph=2, pos0=12345)
+    for name, e in errs.items():
+        assert e <= TOL["f32"], (name, e)
+
+
+@pytest.mark.parametrize("p", [1, 2])
+def test_backward_long_bf16(torch_dev, p):
+    """1000 tokens in bf16: 8 query tiles, the heaviest first."""
+    errs = run_case(torch_dev, 830 + p, 1, 2, 1000, "bf16", p)
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+
+
+def test_backward_deterministic(torch_dev):
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    q, k, v, om = si.attention_inputs(840, 1, 2, 300, "bf16")
+    prm = rpg.Params(omega=torch.from_numpy(om).cuda())
+    g = dev(torch, np.random.default_rng(1).standard_normal((1, 2, 300, 64)), "bf16")
+    args = [dev(torch, x, "bf16") for x in (q, k, v)] + [g]
+    a = [x.clone() for x in rpg.sanatan_attention_backward(*args, 2, prm)]
+    b = [x.clone() for x in rpg.sanatan_attention_backward(*args, 2, prm)]
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
