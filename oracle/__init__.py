@@ -73,6 +73,18 @@ def _load():
     lib.oracle_recurrent_heads.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            i64, dp, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double, ctypes.c_double, dp, dp, dp]
+    lib.oracle_features_h.restype = None
+    lib.oracle_features_h.argtypes = [dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, dp, ctypes.c_double,
+                                      ctypes.c_double, dp]
+    lib.oracle_kappa_h.restype = ctypes.c_double
+    lib.oracle_kappa_h.argtypes = [dp, dp, ctypes.c_int, ctypes.c_int, i64, i64, dp, ctypes.c_double, ctypes.c_double]
+    lib.oracle_attention_direct_h.restype = None
+    lib.oracle_attention_direct_h.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
+                                              ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, ip,
+                                              ctypes.c_int, dp]
+    lib.oracle_recurrent_h.restype = None
+    lib.oracle_recurrent_h.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, dp,
+                                       ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, dp, dp, dp]
     lib.oracle_attention_direct_grad.restype = None
     lib.oracle_attention_direct_grad.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp,
                                                  ctypes.c_double, ctypes.c_double, ctypes.c_double,
@@ -215,3 +227,57 @@ def attention_direct_grad(q, k, v, dout, omega, gamma: float = GAMMA, lambda_bas
                                          float(lambda_base), float(c), float(eps), int(p), _ptr(dq), _ptr(dk),
                                          _ptr(dvv), _ptr(dom))
     return dq, dk, dvv, dom
+
+
+def features_h(u, pos0: int, omega, nh: int, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE) -> np.ndarray:
+    """Phi_h (spectral harmonics n = 1..nh) of rows u[T, d] at positions pos0.. -> [T, (2 + 4 nh) d]."""
+    u = _f64(u)
+    T, d = u.shape
+    out = np.empty((T, (2 + 4 * nh) * d), dtype=np.float64)
+    _load().oracle_features_h(_ptr(u), T, d, int(nh), int(pos0), _ptr(_f64(omega).reshape(d)), float(gamma),
+                              float(lambda_base), _ptr(out))
+    return out
+
+
+def kappa_h(q, k, t: int, s: int, omega, nh: int, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE) -> float:
+    q, k, om = _f64(q).ravel(), _f64(k).ravel(), _f64(omega).ravel()
+    return float(_load().oracle_kappa_h(_ptr(q), _ptr(k), q.size, int(nh), int(t), int(s), _ptr(om), float(gamma),
+                                        float(lambda_base)))
+
+
+def attention_direct_h(q, k, v, omega, nh: int, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE,
+                       c: float | None = None, eps: float = EPS, rows=None) -> np.ndarray:
+    """Direct-kappa_h normalised causal p = 1 attention for ONE head (spectral harmonics n = 1..nh)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, d = q.shape
+    dv = v.shape[1]
+    if c is None:
+        c = 4.0 * d
+    if rows is None:
+        out = np.empty((T, dv))
+        rp, nr = None, 0
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        out = np.empty((r.size, dv))
+        rp, nr = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), int(r.size)
+    _load().oracle_attention_direct_h(_ptr(q), _ptr(k), _ptr(v), T, d, dv, int(nh), _ptr(_f64(omega).reshape(d)),
+                                      float(gamma), float(lambda_base), float(c), float(eps), rp, nr, _ptr(out))
+    return out
+
+
+def recurrent_h(q, k, v, omega, nh: int, pos0: int = 0, gamma: float = GAMMA, lambda_base: float = LAMBDA_BASE,
+                c: float | None = None, eps: float = EPS, S=None, z=None, want_out: bool = True):
+    """p = 1 recurrence on Phi_h for ONE head.  Returns (out [T,dv] or None, S [(2+4nh)d, dv], z [(2+4nh)d])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, d = k.shape
+    dv = v.shape[1]
+    if c is None:
+        c = 4.0 * d
+    D = (2 + 4 * nh) * d
+    S = np.zeros((D, dv)) if S is None else _f64(S).copy()
+    z = np.zeros((D,)) if z is None else _f64(z).copy()
+    out = np.empty((T, dv)) if want_out else None
+    _load().oracle_recurrent_h(_ptr(q), _ptr(k), _ptr(v), T, d, dv, int(nh), int(pos0), _ptr(_f64(omega).reshape(d)),
+                               float(gamma), float(lambda_base), float(c), float(eps), _ptr(S), _ptr(z),
+                               _ptr(out) if want_out else None)
+    return out, S, z

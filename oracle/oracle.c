@@ -235,6 +235,108 @@ void oracle_recurrent_heads(const double* q, const double* k, const double* v, i
 }
 
 /*
+ * Spectral harmonics (the outlook of Appendix B as the notes present it): cos(n theta), sin(n theta) harmonics
+ * are added to each dim's angular part; at p = 1 the map stays explicit, but the features per dim, and so the
+ * recurrent state, grow with the number of harmonics.  The notes fix no feature set; the reading taken here:
+ * harmonics n = 1..nh of the ROTATED angle (so only t - s enters, as for the six-channel kernel), each gated
+ * by the same root label:
+ *   Phi_h per dim = [1, cos th_rot, sin th_rot, ..., cos nh th_rot, sin nh th_rot,
+ *                    r, r cos th_rot, r sin th_rot, ..., r cos nh th_rot, r sin nh th_rot]   (2 + 4 nh channels)
+ *   kappa_h(t,s) = sum_a (1 + r_q r_k)(1 + sum_{n=1..nh} cos(n x_a)),  x_a = theta_q - theta_k + (t - s) lambda_a
+ * nh = 1 is the six-channel kernel.  For nh >= 2 the angular factor 1 + sum cos(n x) takes negative values,
+ * so kappa_h can be negative: no clipping is applied (as for the unclipped four-channel kernel).
+ * Channel-major layout: channel 0 = 1; channel 2n-1 = cos n th_rot, 2n = sin n th_rot (n = 1..nh);
+ * channel 2nh+1 = r; channel 2nh+2n = r cos n th_rot, 2nh+2n+1 = r sin n th_rot.  Feature row c*d + a.
+ */
+void oracle_features_h(const double* u, int T, int d, int nh, int64_t pos0, const double* omega, double gamma,
+                       double lambda_base, double* phi) {
+  const int C = 2 + 4 * nh;
+  for (int i = 0; i < T; i++) {
+    const double t = (double)(pos0 + i);
+    double* row = phi + (size_t)i * C * d;
+    for (int a = 0; a < d; a++) {
+      const double th = sanatan_angle(u[(size_t)i * d + a]);
+      const double r = sanatan_root(th, omega[a], gamma);
+      const double th_rot = th + t * sanatan_freq(a, d, lambda_base);
+      row[0 * d + a] = 1.0;
+      row[(size_t)(2 * nh + 1) * d + a] = r;
+      for (int n = 1; n <= nh; n++) {
+        const double c = cos((double)n * th_rot), s = sin((double)n * th_rot);
+        row[(size_t)(2 * n - 1) * d + a] = c;
+        row[(size_t)(2 * n) * d + a] = s;
+        row[(size_t)(2 * nh + 2 * n) * d + a] = r * c;
+        row[(size_t)(2 * nh + 2 * n + 1) * d + a] = r * s;
+      }
+    }
+  }
+}
+
+/* kappa_h of one pair, as a sum over dims of gate times (1 + sum of cosines of multiples of the difference). */
+double oracle_kappa_h(const double* q, const double* k, int d, int nh, int64_t t, int64_t s, const double* omega,
+                      double gamma, double lambda_base) {
+  double acc = 0.0;
+  for (int a = 0; a < d; a++) {
+    const double thq = sanatan_angle(q[a]), thk = sanatan_angle(k[a]);
+    const double rq = sanatan_root(thq, omega[a], gamma), rk = sanatan_root(thk, omega[a], gamma);
+    const double x = thq - thk + (double)(t - s) * sanatan_freq(a, d, lambda_base);
+    double ang = 1.0;
+    for (int n = 1; n <= nh; n++) ang += cos((double)n * x);
+    acc += (1.0 + rq * rk) * ang;
+  }
+  return acc;
+}
+
+/* Normalised causal p = 1 attention on kappa_h, direct form, one head: o_t = sum_{s<=t} kappa_h v_s /
+ * (sum_{s<=t} kappa_h + c eps) -- the p = 1 weights of [N] §2.6 with kappa/c, written in raw units.  Rows as in
+ * oracle_attention_direct. */
+void oracle_attention_direct_h(const double* q, const double* k, const double* v, int T, int d, int dv, int nh,
+                               const double* omega, double gamma, double lambda_base, double c, double eps,
+                               const int* rows, int n_rows, double* out) {
+  const int n_out = rows ? n_rows : T;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int j = 0; j < n_out; j++) {
+    const int t = rows ? rows[j] : j;
+    double* o = out + (size_t)j * dv;
+    double* num = (double*)calloc((size_t)dv, sizeof(double));
+    double den = 0.0;
+    for (int s = 0; s <= t; s++) {
+      const double w = oracle_kappa_h(q + (size_t)t * d, k + (size_t)s * d, d, nh, t, s, omega, gamma, lambda_base) / c;
+      den += w;
+      for (int n = 0; n < dv; n++) num[n] += w * v[(size_t)s * dv + n];
+    }
+    for (int n = 0; n < dv; n++) o[n] = num[n] / (den + eps);
+    free(num);
+  }
+}
+
+/* The p = 1 recurrence on Phi_h, one head (state S [(2+4nh)d][dv], z [(2+4nh)d] in/out), as oracle_recurrent. */
+void oracle_recurrent_h(const double* q, const double* k, const double* v, int T, int d, int dv, int nh,
+                        int64_t pos0, const double* omega, double gamma, double lambda_base, double c, double eps,
+                        double* S, double* z, double* out) {
+  const int D = (2 + 4 * nh) * d;
+  double* fq = (double*)malloc(sizeof(double) * (size_t)D);
+  double* fk = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int i = 0; i < T; i++) {
+    oracle_features_h(k + (size_t)i * d, 1, d, nh, pos0 + i, omega, gamma, lambda_base, fk);
+    for (int f = 0; f < D; f++) {
+      z[f] += fk[f];
+      for (int n = 0; n < dv; n++) S[(size_t)f * dv + n] += fk[f] * v[(size_t)i * dv + n];
+    }
+    if (!out) continue;
+    oracle_features_h(q + (size_t)i * d, 1, d, nh, pos0 + i, omega, gamma, lambda_base, fq);
+    double den = 0.0;
+    for (int f = 0; f < D; f++) den += fq[f] * z[f];
+    for (int n = 0; n < dv; n++) {
+      double num = 0.0;
+      for (int f = 0; f < D; f++) num += fq[f] * S[(size_t)f * dv + n];
+      out[(size_t)i * dv + n] = num / (den + c * eps);
+    }
+  }
+  free(fq);
+  free(fk);
+}
+
+/*
  * Gradient of the direct form, one head: the derivatives of L = sum_t <g_t, o_t> (g = dout [T][dv], the
  * gradient arriving at the outputs) with respect to q, k [T][d], v [T][dv] and omega [d], for the weights
  * w(t,s) = (kappa(t,s)/c)^p of oracle_attention_direct.  Needed because omega is learned ([N] §2.2) and the

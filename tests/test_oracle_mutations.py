@@ -34,6 +34,10 @@ MUTS = [
   ("recurrent read before write", None, None),
   ("S transposed", "S[(size_t)f * dv + n] += fk[f]", "S[(size_t)n * 6 * d + f] += fk[f]"),
   ("direct weight not normalised by c", "double w = kap / c;", "double w = kap;"),
+  ("harmonic multiple dropped in kappa_h", "for (int n = 1; n <= nh; n++) ang += cos((double)n * x);", "for (int n = 1; n <= nh; n++) ang += cos(x);"),
+  ("harmonic multiple dropped in features", "const double c = cos((double)n * th_rot), s = sin((double)n * th_rot);", "const double c = cos(th_rot), s = sin(th_rot);"),
+  ("harmonic gated channel uses the wrong harmonic", "row[(size_t)(2 * nh + 2 * n + 1) * d + a] = r * s;", "row[(size_t)(2 * nh + 2 * n + 1) * d + a] = r * sin(th_rot);"),
+  ("harmonic root channel misplaced", "row[(size_t)(2 * nh + 1) * d + a] = r;", "row[(size_t)(2 * nh) * d + a] = r;"),
   ("grad query sin sign", "dth[a] += G * (-(1.0 + rq[ti] * rk[si]) * sin(x)", "dth[a] += G * ((1.0 + rq[ti] * rk[si]) * sin(x)"),
   ("grad key root slope dropped", "+ rq[ti] * (1.0 + cos(x)) * sk[si]);", ");"),
   ("grad output term dropped", "(v[(size_t)s * dv + n] - o[(size_t)t * dv + n])", "v[(size_t)s * dv + n]"),
@@ -61,11 +65,13 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
                     ignore=shutil.ignore_patterns("*.so", "*.tmp*", "__pycache__"))
     (tmp_path / "tests" / "golden").mkdir(parents=True)
-    for f in ("conftest.py", "test_oracle_pins.py", "test_oracle_four_channel.py", "test_oracle_grad.py"):
+    for f in ("conftest.py", "test_oracle_pins.py", "test_oracle_four_channel.py", "test_oracle_grad.py",
+              "test_oracle_harmonics.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
     shutil.copy(os.path.join(ROOT, "tests", "golden", "pages_values.json"), tmp_path / "tests" / "golden")
     (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "tests/test_oracle_pins.py",
-                        "tests/test_oracle_four_channel.py", "tests/test_oracle_grad.py"],
+                        "tests/test_oracle_four_channel.py", "tests/test_oracle_grad.py",
+                        "tests/test_oracle_harmonics.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "planted mistake '%s' passed every pin:\n%s" % (name, r.stdout[-2000:])
