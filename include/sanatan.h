@@ -250,6 +250,49 @@ sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, cons
                                               size_t ws_bytes, hipStream_t stream);
 
 /*
+ * sanatan_prefill_four_channel -- the chunked p = 1 prefill on the unclipped four-channel kernel of [N] §2.5
+ * (features [1, r, r cos theta_rot, r sin theta_rot] per dim), whose recurrence ([N] §2.7 applied to these
+ * features) is exact: o_t = Phi4(q_t)^T S4_t / (Phi4(q_t)^T z4_t + c eps).  The weights are not clipped, so a
+ * denominator can be near zero or negative.
+ *   S4, z4 : NULL (zero start, no final state) or the compact four-channel state of
+ *            sanatan_decode_step_four_channel, [B][H][3d+1][d_v] and [B][H][3d+1], in/out.
+ *   Everything else as sanatan_prefill_chunked without `chunk` (this path walks 32-token chunks, one workgroup
+ *   per sequence); ws: at least sanatan_prefill_four_channel_workspace_bytes() bytes, which hold Phi4(Q) and
+ *   Phi4(K) in element type t.  The final state continues exactly in sanatan_decode_step_four_channel.
+ */
+size_t sanatan_prefill_four_channel_workspace_bytes(int B, int H, int T, sanatan_dtype t,
+                                                    const sanatan_params* params);
+sanatan_status sanatan_prefill_four_channel(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                            int H, int T, int64_t pos0, const sanatan_params* params, float* S4,
+                                            float* z4, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Spectral harmonics (the notes' reading of the paper's Appendix B outlook: cos(n theta), sin(n theta) harmonics
+ * added per dim keep the p = 1 map explicit, at the cost of more features and a larger state).  Reading taken:
+ * harmonics n = 1..nh of the rotated angle theta_rot = theta + t lambda_a, each gated by the same root label,
+ *   Phi_h per dim = [1, cos n theta_rot, sin n theta_rot (n = 1..nh), r, r cos n theta_rot, r sin n theta_rot],
+ *   kappa_h(t,s)  = sum_a (1 + r_q r_k)(1 + sum_{n=1..nh} cos(n dtheta_a)),
+ * stored channel-major: channel 0 = 1, 2n-1 / 2n = cos / sin of n theta_rot, 2nh+1 = r, 2nh+2n / 2nh+2n+1 =
+ * r cos / r sin of n theta_rot; feature row c d + a.  nh = 1 is the six-channel map.  For nh >= 2 the factor
+ * 1 + sum cos(n x) takes negative values, so kappa_h and a denominator can be negative (no clipping).
+ * The state of one head is S [(2+4nh)d][d_v], z [(2+4nh)d] (sanatan_harmonics_state_bytes).  nh: 1 or 2
+ * (nh < 1 INVALID_ARG, nh > 2 UNSUPPORTED).
+ * sanatan_prefill_harmonics: the chunked p = 1 prefill on Phi_h; arguments as sanatan_prefill_four_channel, with
+ *   S, z of this layout; ws at least sanatan_prefill_harmonics_workspace_bytes().
+ * sanatan_decode_step_harmonics: one token of the recurrence on Phi_h for N head-states; pos / posv as in
+ *   sanatan_decode_step_compact; everything else as sanatan_decode_step.
+ */
+size_t sanatan_harmonics_state_bytes(int d, int d_v, int nh);
+size_t sanatan_prefill_harmonics_workspace_bytes(int B, int H, int T, sanatan_dtype t, int nh,
+                                                 const sanatan_params* params);
+sanatan_status sanatan_prefill_harmonics(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
+                                         int T, int nh, int64_t pos0, const sanatan_params* params, float* S, float* z,
+                                         void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+sanatan_status sanatan_decode_step_harmonics(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                             const int64_t* posv, int nh, const sanatan_params* params, float* S,
+                                             float* z, float* out, hipStream_t stream);
+
+/*
  * Backward pass of normalised causal power attention: the gradients of L = sum_t <dout_t, o_t> with respect
  * to q, k, v and the root anchors omega, where o is the output of sanatan_quadratic_ref_p2 with the same p
  * (for p = 1 also of sanatan_prefill_chunked, which computes the same function).  omega is learned and the

@@ -92,6 +92,18 @@ def lib():
         L.sanatan_quadratic_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_quadratic_ref_p2.restype = i32
         L.sanatan_quadratic_ref_p2.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, sz, vp]
+        L.sanatan_harmonics_state_bytes.restype = sz
+        L.sanatan_harmonics_state_bytes.argtypes = [i32, i32, i32]
+        L.sanatan_prefill_harmonics_workspace_bytes.restype = sz
+        L.sanatan_prefill_harmonics_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, pp]
+        L.sanatan_prefill_harmonics.restype = i32
+        L.sanatan_prefill_harmonics.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp, sz, vp]
+        L.sanatan_decode_step_harmonics.restype = i32
+        L.sanatan_decode_step_harmonics.argtypes = [vp, vp, vp, i32, i64, vp, i32, pp, vp, vp, vp, vp]
+        L.sanatan_prefill_four_channel_workspace_bytes.restype = sz
+        L.sanatan_prefill_four_channel_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
+        L.sanatan_prefill_four_channel.restype = i32
+        L.sanatan_prefill_four_channel.argtypes = [vp, vp, vp, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp, sz, vp]
         L.sanatan_attention_backward_workspace_bytes.restype = sz
         L.sanatan_attention_backward_workspace_bytes.argtypes = [i32, i32, i32, i32, pp]
         L.sanatan_attention_backward.restype = i32
@@ -112,6 +124,8 @@ EXPORTED = [
     "sanatan_quadratic_workspace_bytes",
     "sanatan_quadratic_ref_p2", "sanatan_quadratic_four_channel",
     "sanatan_attention_backward_workspace_bytes", "sanatan_attention_backward",
+    "sanatan_harmonics_state_bytes", "sanatan_prefill_harmonics_workspace_bytes", "sanatan_prefill_harmonics",
+    "sanatan_decode_step_harmonics", "sanatan_prefill_four_channel_workspace_bytes", "sanatan_prefill_four_channel",
 ]
 
 
@@ -520,3 +534,76 @@ def sanatan_attention_backward(q, k, v, dout, p_exp: int, params: Params, pos0: 
                                             int(pos0), ctypes.byref(pr), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(domega),
                                             _ptr(ws), ws.numel(), _stream()), "sanatan_attention_backward")
     return dq, dk, dv, domega
+
+
+def sanatan_harmonics_state_bytes(d: int = D, d_v: int = DV, nh: int = 2) -> int:
+    return int(lib().sanatan_harmonics_state_bytes(int(d), int(d_v), int(nh)))
+
+
+def _ext_prefill(entry, q, k, v, params: Params, pos0, S, z, out, ws, rows, ws_fn):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name)
+    B, H, T = _attention_shape(q, k, v, params)
+    if out is None:
+        out = torch.empty((B, H, T, params.d_v), dtype=q.dtype, device=q.device)
+    _check_tensor(out, "out")
+    _check_shape(out, "out", (B, H, T, params.d_v))
+    _check_same_dtype(q, ("out", out))
+    for name, t, shape in (("S", S, (B, H, rows, params.d_v)), ("z", z, (B, H, rows))):
+        if t is not None:
+            _check_tensor(t, name, dtypes=("float32",))
+            _check_shape(t, name, shape)
+    p = params.struct()
+    need = ws_fn(B, H, T, _dtype_code(q), p)
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    return B, H, T, p, out, ws
+
+
+def sanatan_prefill_harmonics(q, k, v, nh: int, params: Params, pos0: int = 0, S=None, z=None, out=None, ws=None):
+    """Chunked p = 1 prefill on the spectral-harmonic map with nh harmonics; S [B,H,(2+4nh)d,64], z optional."""
+    rows = (2 + 4 * nh) * params.d
+    ws_fn = lambda B, H, T, t, p: int(lib().sanatan_prefill_harmonics_workspace_bytes(B, H, T, t, int(nh),
+                                                                                        ctypes.byref(p)))
+    B, H, T, p, out, ws = _ext_prefill("harmonics", q, k, v, params, pos0, S, z, out, ws, rows, ws_fn)
+    _check(lib().sanatan_prefill_harmonics(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(nh), int(pos0),
+                                           ctypes.byref(p), _ptr(S), _ptr(z), _ptr(out), _ptr(ws), ws.numel(),
+                                           _stream()), "sanatan_prefill_harmonics")
+    return out
+
+
+def sanatan_prefill_four_channel(q, k, v, params: Params, pos0: int = 0, S4=None, z4=None, out=None, ws=None):
+    """Chunked p = 1 prefill on the unclipped four-channel kernel; S4 [B,H,3d+1,64], z4 [B,H,3d+1] optional."""
+    rows = 3 * params.d + 1
+    ws_fn = lambda B, H, T, t, p: int(lib().sanatan_prefill_four_channel_workspace_bytes(B, H, T, t, ctypes.byref(p)))
+    B, H, T, p, out, ws = _ext_prefill("four", q, k, v, params, pos0, S4, z4, out, ws, rows, ws_fn)
+    _check(lib().sanatan_prefill_four_channel(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(pos0),
+                                              ctypes.byref(p), _ptr(S4), _ptr(z4), _ptr(out), _ptr(ws), ws.numel(),
+                                              _stream()), "sanatan_prefill_four_channel")
+    return out
+
+
+def sanatan_decode_step_harmonics(q, k, v, pos, nh: int, params: Params, S, z, out=None):
+    """One token of the spectral-harmonic recurrence for N head-states: S [N,(2+4nh)d,64], z [N,(2+4nh)d]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("S", S), ("z", z)):
+        _check_tensor(t, name, dtypes=("float32",))
+    rows = (2 + 4 * nh) * params.d
+    N = _decode_shapes(q, k, v, S, z, rows, params)
+    if out is None:
+        out = torch.empty((N, params.d_v), dtype=torch.float32, device=q.device)
+    _check_tensor(out, "out", dtypes=("float32",))
+    _check_shape(out, "out", (N, params.d_v))
+    p = params.struct()
+    posv = None
+    if isinstance(pos, torch.Tensor):
+        _check_tensor(pos, "pos", dtypes=("int64",))
+        _check_shape(pos, "pos", (N,))
+        posv, pos = pos, 0
+    _check(lib().sanatan_decode_step_harmonics(_ptr(q), _ptr(k), _ptr(v), N, int(pos), _ptr(posv), int(nh),
+                                               ctypes.byref(p), _ptr(S), _ptr(z), _ptr(out), _stream()),
+           "sanatan_decode_step_harmonics")
+    return out

@@ -230,6 +230,63 @@ sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, cons
   return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, true, pos0, consts(params), out, ws, stream));
 }
 
+size_t sanatan_harmonics_state_bytes(int d, int d_v, int nh) {
+  if (d <= 0 || d_v <= 0 || nh <= 0) return 0;
+  return (size_t)(2 + 4 * nh) * d * ((size_t)d_v + 1) * sizeof(float);
+}
+
+size_t sanatan_prefill_harmonics_workspace_bytes(int B, int H, int T, sanatan_dtype t, int nh,
+                                                 const sanatan_params* params) {
+  (void)params;
+  if (!sizes_ok(B, H, T) || T > kMaxPrefillT || !dtype_ok(t) || nh < 1 || nh > 2) return 0;
+  return ext_prefill_ws_bytes(B, H, T, t, nh);
+}
+
+size_t sanatan_prefill_four_channel_workspace_bytes(int B, int H, int T, sanatan_dtype t,
+                                                    const sanatan_params* params) {
+  (void)params;
+  if (!sizes_ok(B, H, T) || T > kMaxPrefillT || !dtype_ok(t)) return 0;
+  return ext_prefill_ws_bytes(B, H, T, t, 0);
+}
+
+static sanatan_status ext_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                                  int nh_or_zero, int64_t pos0, const sanatan_params* params, float* S, float* z,
+                                  void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dtype_ok(t) || !sizes_ok(B, H, T)) return SANATAN_ERR_INVALID_ARG;
+  if ((S == nullptr) != (z == nullptr)) return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxPrefillT) return SANATAN_ERR_UNSUPPORTED;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (!ws || ws_bytes < ext_prefill_ws_bytes(B, H, T, t, nh_or_zero)) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_ext_prefill(q, k, v, t, B, H, T, nh_or_zero, pos0, consts(params), S, z, out, ws, stream));
+}
+
+sanatan_status sanatan_prefill_harmonics(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
+                                         int T, int nh, int64_t pos0, const sanatan_params* params, float* S, float* z,
+                                         void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (nh < 1) return SANATAN_ERR_INVALID_ARG;
+  if (nh > 2) return SANATAN_ERR_UNSUPPORTED;
+  return ext_prefill(q, k, v, t, B, H, T, nh, pos0, params, S, z, out, ws, ws_bytes, stream);
+}
+
+sanatan_status sanatan_prefill_four_channel(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                            int H, int T, int64_t pos0, const sanatan_params* params, float* S4,
+                                            float* z4, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ext_prefill(q, k, v, t, B, H, T, 0, pos0, params, S4, z4, out, ws, ws_bytes, stream);
+}
+
+sanatan_status sanatan_decode_step_harmonics(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                             const int64_t* posv, int nh, const sanatan_params* params, float* S,
+                                             float* z, float* out, hipStream_t stream) {
+  if (!q || !k || !v || !S || !z || !out || N <= 0 || nh < 1 || (!posv && !pos_ok(pos)))
+    return SANATAN_ERR_INVALID_ARG;
+  if (nh > 2) return SANATAN_ERR_UNSUPPORTED;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  return hip_status(launch_decode_step_harmonics(q, k, v, N, pos, posv, nh, consts(params), S, z, out, stream));
+}
+
 size_t sanatan_attention_backward_workspace_bytes(int B, int H, int T, sanatan_dtype t, const sanatan_params* params) {
   (void)params;
   if (!sizes_ok(B, H, T) || T > kMaxQuadraticT || !dtype_ok(t)) return 0;

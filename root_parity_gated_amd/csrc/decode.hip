@@ -32,16 +32,18 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // Layout: 0 full six-channel state (6d rows), 1 compact six-channel (5d+1), 2 the unclipped four-channel kernel's
 // state ([N] §2.5: features [1, r, r cos, r sin]; kept compact too, 3d+1 rows: the shared channel-0 row, then
 // r, r cos, r sin).
-template <bool NT, int Layout>
+// Layout 3: the spectral-harmonic map with NH harmonics, full state of (2 + 4 NH) d rows (channel 0 = 1; 2n-1, 2n =
+// cos, sin of n theta_rot; 2 NH + 1 = r; 2 NH + 2n, 2 NH + 2n + 1 = r cos, r sin of n theta_rot).
+template <bool NT, int Layout, int NH = 1>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int64_t pos,
     const int64_t* __restrict__ posv, const float* __restrict__ omega, int nph, double log2_base, float kr,
     float ceps, float* __restrict__ S, float* __restrict__ z, float* __restrict__ out) {
-  constexpr bool Compact = Layout != 0;
-  constexpr int R = Layout == 0 ? kF : Layout == 1 ? kCompactRows : kFourRows;  // state rows
+  constexpr bool Compact = Layout == 1 || Layout == 2;
+  constexpr int R = Layout == 0 ? kF : Layout == 1 ? kCompactRows : Layout == 2 ? kFourRows : (2 + 4 * NH) * kD;
   constexpr int MR = (R + kDecRows - 1) / kDecRows;   // row pieces per thread
-  __shared__ float fk[kF];
-  __shared__ float fq[kF];
+  __shared__ float fk[R];
+  __shared__ float fq[R];
   __shared__ float vs[kDV];
   __shared__ float red[kDecRows][kDV + 4];
   __shared__ float dred[kDecThreads / 64];
@@ -61,7 +63,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const f32x4v* src = reinterpret_cast<const f32x4v*>(&Si[f * kDV + 4 * cg]);
     if (f < R) rows[m] = NT ? __builtin_nontemporal_load(src) : *src;
   }
-  const float zr = tid < R ? zi[tid] : 0.0f;
+  constexpr int ZR = (R + kDecThreads - 1) / kDecThreads;  // z rows per thread (two for the 640-row state)
+  float zr[ZR];
+#pragma unroll
+  for (int m = 0; m < ZR; m++) zr[m] = tid + kDecThreads * m < R ? zi[tid + kDecThreads * m] : 0.0f;
 
   if (tid < 2 * kD) {
     const int a = tid & (kD - 1);
@@ -72,22 +77,37 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     float cr, sr, r;
     featurize1(u, rho, om4, kr, cr, sr, r);
     float* dst = is_k ? fk : fq;
+    if constexpr (Layout == 3) {
+      const float y = u * rcp_hw(fmaf(fabsf(u), 2.0f, 2.0f)) + rho;  // rotated angle in revolutions
+      dst[a] = 1.0f;
+      dst[(2 * NH + 1) * kD + a] = r;
+#pragma unroll
+      for (int n = 1; n <= NH; n++) {
+        const float c = n == 1 ? cr : cos_rev((float)n * y), s = n == 1 ? sr : sin_rev((float)n * y);
+        dst[(2 * n - 1) * kD + a] = c;
+        dst[(2 * n) * kD + a] = s;
+        dst[(2 * NH + 2 * n) * kD + a] = r * c;
+        dst[(2 * NH + 2 * n + 1) * kD + a] = r * s;
+      }
+    }
     // channel c >= 1 of dim a: row c d + a, or 1 + (c - 1) d + a in the compact layout, or 1 + (c - 3) d + a
     // for the four-channel channels c = 3..5
     constexpr int sh = Layout == 0 ? 0 : Layout == 1 ? 1 - kD : 1 - 3 * kD;
-    if constexpr (Compact) {
-      // the shared channel-0 row: a key adds 1 x v to it, a query reads it once for each of its d rows
-      if (a == 0) dst[0] = is_k ? 1.0f : (float)kD;
-    } else {
-      dst[a] = 1.0f;
+    if constexpr (Layout != 3) {
+      if constexpr (Compact) {
+        // the shared channel-0 row: a key adds 1 x v to it, a query reads it once for each of its d rows
+        if (a == 0) dst[0] = is_k ? 1.0f : (float)kD;
+      } else {
+        dst[a] = 1.0f;
+      }
+      if constexpr (Layout != 2) {
+        dst[sh + 1 * kD + a] = cr;
+        dst[sh + 2 * kD + a] = sr;
+      }
+      dst[sh + 3 * kD + a] = r;
+      dst[sh + 4 * kD + a] = r * cr;
+      dst[sh + 5 * kD + a] = r * sr;
     }
-    if constexpr (Layout != 2) {
-      dst[sh + 1 * kD + a] = cr;
-      dst[sh + 2 * kD + a] = sr;
-    }
-    dst[sh + 3 * kD + a] = r;
-    dst[sh + 4 * kD + a] = r * cr;
-    dst[sh + 5 * kD + a] = r * sr;
   } else if (tid < 2 * kD + kDV) {
     vs[tid - 2 * kD] = v[(size_t)i * kDV + (tid - 2 * kD)];
   }
@@ -113,10 +133,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   }
   // z update and the denominator partial
   float dpart = 0.0f;
-  if (tid < R) {
-    const float z0 = zr + fk[tid];
-    zi[tid] = z0;
-    dpart = fq[tid] * z0;
+#pragma unroll
+  for (int m = 0; m < ZR; m++) {
+    const int f = tid + kDecThreads * m;
+    if (f < R) {
+      const float z0 = zr[m] + fk[f];
+      zi[f] = z0;
+      dpart = fmaf(fq[f], z0, dpart);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 4; e++) red[rg][4 * cg + e] = acc[e];
@@ -176,6 +200,25 @@ hipError_t launch_decode_step(const float* q, const float* k, const float* v, in
     if (stream_state) go(decode_step_kernel<true, 1>); else go(decode_step_kernel<false, 1>);
   } else {
     if (stream_state) go(decode_step_kernel<true, 0>); else go(decode_step_kernel<false, 0>);
+  }
+  return hipGetLastError();
+}
+
+// the spectral-harmonic map with nh = 2 harmonics (nh = 1 is layout 0)
+hipError_t launch_decode_step_harmonics(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                        const int64_t* posv, int nh, const MethodConsts& mc, float* S, float* z,
+                                        float* out, hipStream_t stream) {
+  const size_t floats = (size_t)(2 + 4 * nh) * kD * (kDV + 1);
+  const bool stream_state = (size_t)N * floats * sizeof(float) > ((size_t)128 << 20);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(N), dim3(kDecThreads), 0, stream, q, k, v, pos, posv, mc.omega, mc.nph,
+                       mc.log2_base, mc.kr, mc.ceps, S, z, out);
+  };
+  if (nh == 1) return launch_decode_step(q, k, v, N, pos, posv, 0, mc, S, z, out, stream);
+  if (nh == 2) {
+    if (stream_state) go(decode_step_kernel<true, 3, 2>); else go(decode_step_kernel<false, 3, 2>);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

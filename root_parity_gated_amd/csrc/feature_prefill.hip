@@ -1,0 +1,344 @@
+// feature_prefill.hip -- chunked causal p = 1 attention over materialized feature maps: the spectral-harmonic
+// map and the unclipped four-channel map.
+//
+// SANATAN reading notes: the p = 1 recurrence S_t = S_{t-1} + Phi(k_t) v_t^T, z_t = z_{t-1} + Phi(k_t),
+// o_t = Phi(q_t)^T S_t / (Phi(q_t)^T z_t + c eps) holds for any explicit feature map (§2.7).  Two maps besides
+// the six-channel one are served here:
+//   * spectral harmonics (the Appendix B outlook): per dim [1, cos n th, sin n th (n = 1..nh), r,
+//     r cos n th, r sin n th (n = 1..nh)] of the rotated angle th, (2 + 4 nh) d features, state rows in that
+//     channel-major order (nh = 1 is the six-channel map);
+//   * the unclipped four-channel kernel (§2.5), per dim [1, r, r cos th, r sin th], kept compact like its decode
+//     state: row 0 is the shared channel-0 feature (1 for a key; d for a query, which stands for its d equal
+//     rows), then r, r cos th, r sin th: 3d + 1 features.
+// Phi(Q) and Phi(K) are featurized once into the workspace (element type of the call), padded to a multiple
+// of 128 features with zeros.  The prefill kernel then walks each sequence in 32-token chunks with one
+// workgroup of 4 waves per sequence: wave w owns feature tiles w, w + 4, ... (32 features each) and their
+// 32 x 64 slices of S in MFMA accumulators; per chunk it forms its partial masked scores Phi(K) Phi(Q)^T over
+// those features, the partial numerator V^T P + S^T Phi(Q)^T and denominator, and after the four partials
+// meet in LDS (fixed order) the chunk's outputs are normalised; then S += Phi(K)^T V and z += Phi(K)^T 1.
+// Operands: bf16 32x32x16 MFMA (fp32 32x32x2 for fp32 inputs), fp32 accumulation; S is rounded to the
+// operand type only as the readout's operand.  No sequence split: each sequence is one workgroup.
+#include <atomic>
+
+#include "prefill_common.h"
+
+namespace sanatan {
+namespace {
+
+constexpr int kFC = 32;  // chunk tokens
+
+// featurize one operand into the padded feature layout.  KIND 0: harmonics n = 1..NH; KIND 1: four-channel
+// compact (IS_Q: row 0 carries d instead of 1).  A thread owns 8 dims of one token.
+template <typename TIn, typename TOut, int KIND, int NH, bool IS_Q>
+__global__ __launch_bounds__(256) void featurize_ext_kernel(const TIn* __restrict__ u, TOut* __restrict__ phi, int H,
+                                                            int T, int Fp, int64_t pos0,
+                                                            const float* __restrict__ omega, int nph,
+                                                            double log2_base, float kr, int ntiles) {
+  const int bh = (int)(blockIdx.x / ntiles), tile = (int)(blockIdx.x % ntiles), j = threadIdx.x & 7, a0 = 8 * j;
+  const int t = tile * 32 + (threadIdx.x >> 3);
+  if (t >= T) return;
+  const int hd = bh % H;
+  const TIn* up = u + ((size_t)bh * T + t) * kD + a0;
+  TOut* o = phi + ((size_t)bh * T + t) * Fp;
+  float cr[8], sr[8], rr[8], y[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float om4 = anchor_rev(omega[(size_t)(hd % nph) * kD + a0 + i]);
+    const float rho = phase_at(pos0 + t, phase_step(a0 + i, log2_base));
+    const float x = to_f32(up[i]);
+    featurize1(x, rho, om4, kr, cr[i], sr[i], rr[i]);
+    y[i] = x * rcp_hw(fmaf(fabsf(x), 2.0f, 2.0f)) + rho;  // the rotated angle in revolutions, as featurize1
+  }
+  auto put = [&](int row0, const float (&val)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[row0 + a0 + i] = from_f32<TOut>(val[i]);
+  };
+  float tmp[8];
+  if constexpr (KIND == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = 1.0f;
+    put(0, tmp);
+    put((2 * NH + 1) * kD, rr);
+#pragma unroll
+    for (int n = 1; n <= NH; n++) {
+      float c[8], s[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        c[i] = n == 1 ? cr[i] : cos_rev((float)n * y[i]);
+        s[i] = n == 1 ? sr[i] : sin_rev((float)n * y[i]);
+      }
+      put((2 * n - 1) * kD, c);
+      put((2 * n) * kD, s);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        c[i] *= rr[i];
+        s[i] *= rr[i];
+      }
+      put((2 * NH + 2 * n) * kD, c);
+      put((2 * NH + 2 * n + 1) * kD, s);
+    }
+    // zero padding past (2 + 4 NH) d: written by the threads of dim block 0
+    const int Fr = (2 + 4 * NH) * kD;
+    for (int f = Fr + a0; f < Fp; f += 64)
+#pragma unroll
+      for (int i = 0; i < 8; i++) o[f + i] = from_f32<TOut>(0.0f);
+  } else {
+    if (j == 0) o[0] = from_f32<TOut>(IS_Q ? (float)kD : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      o[1 + a0 + i] = from_f32<TOut>(rr[i]);
+      o[1 + kD + a0 + i] = from_f32<TOut>(rr[i] * cr[i]);
+      o[1 + 2 * kD + a0 + i] = from_f32<TOut>(rr[i] * sr[i]);
+    }
+    for (int f = 3 * kD + 1 + threadIdx.x % 8; f < Fp; f += 8) o[f] = from_f32<TOut>(0.0f);
+  }
+}
+
+template <typename T, int NFT>
+struct FGeom {
+  static constexpr int Fp = 32 * NFT;
+  static constexpr int KP = Fp + 16 / (int)sizeof(T);  // Phi(K) tile pitch (elements)
+  static constexpr int VP = kDV + 16 / (int)sizeof(T);
+  static constexpr int RP = 68;
+  static constexpr int k_bytes = kFC * KP * (int)sizeof(T);
+  static constexpr int v_bytes = kFC * VP * (int)sizeof(T);
+  static constexpr int red_bytes = 4 * kFC * RP * 4;
+  static constexpr int lds = k_bytes + v_bytes + red_bytes + Fp * 4;
+};
+
+// 8 features of one row, slots (h, i) <-> feature base + 8 (i / 4) + 4 h + i % 4 (the accumulator row order)
+template <typename T>
+__device__ __forceinline__ typename FragT<T>::type slot_frag(const T* row, int base, int h) {
+  typename FragT<T>::type f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[i] = row[base + 4 * h + i];
+    f[4 + i] = row[base + 8 + 4 * h + i];
+  }
+  return f;
+}
+
+template <typename T, int NFT>
+__global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
+                                                              const T* __restrict__ v, T* __restrict__ out,
+                                                              float* __restrict__ S, float* __restrict__ z, int Tn,
+                                                              int Freal, float ceps) {
+  using G = FGeom<T, NFT>;
+  typedef typename FragT<T>::type Frag;
+  static_assert(NFT % 4 == 0, "feature tiles are dealt to four waves");
+  constexpr int NW = NFT / 4, Fp = G::Fp, KP = G::KP, VP = G::VP, RP = G::RP;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T* KT = reinterpret_cast<T*>(smem);
+  T* VT = reinterpret_cast<T*>(smem + G::k_bytes);
+  float* red = reinterpret_cast<float*>(smem + G::k_bytes + G::v_bytes);
+  float* zs = reinterpret_cast<float*>(smem + G::k_bytes + G::v_bytes + G::red_bytes);
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
+  const int bh = blockIdx.x;
+  const T* qp = phiq + (size_t)bh * Tn * Fp;
+  const T* kp = phik + (size_t)bh * Tn * Fp;
+  const T* vp = v + (size_t)bh * Tn * kDV;
+  T* op = out + (size_t)bh * Tn * kDV;
+  float* Sp = S ? S + (size_t)bh * Freal * kDV : nullptr;
+  float* zp = z ? z + (size_t)bh * Freal : nullptr;
+
+  // state slice: tile i of this wave is feature tile ft = w + 4 i; register 4 j + i4 of (i, vt) holds
+  // S[32 ft + 8 j + 4 h + i4][32 vt + n32]
+  f32x16 Sacc[NW][2];
+#pragma unroll
+  for (int i = 0; i < NW; i++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
+        Sacc[i][vt][r] = (Sp && f < Freal) ? Sp[(size_t)f * kDV + 32 * vt + n32] : 0.0f;
+      }
+    }
+  for (int f = tid; f < Fp; f += 256) zs[f] = (zp && f < Freal) ? zp[f] : 0.0f;
+
+  for (int t0 = 0; t0 < Tn; t0 += kFC) {
+    const int nv = min(kFC, Tn - t0);
+    // stage Phi(K) and V rows of the chunk, zero past its end
+    constexpr int EL = 16 / (int)sizeof(T);
+    for (int e = tid; e < kFC * (Fp / EL); e += 256) {
+      const int s = e / (Fp / EL), c = (e % (Fp / EL)) * EL;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (s < nv) val = *reinterpret_cast<const u32x4*>(kp + (size_t)(t0 + s) * Fp + c);
+      *reinterpret_cast<u32x4*>(KT + s * KP + c) = val;
+    }
+    for (int e = tid; e < kFC * (kDV / EL); e += 256) {
+      const int s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (s < nv) val = *reinterpret_cast<const u32x4*>(vp + (size_t)(t0 + s) * kDV + c);
+      *reinterpret_cast<u32x4*>(VT + s * VP + c) = val;
+    }
+    __syncthreads();
+
+    // this lane's query (column n32 of the transposed tiles), clamped into the chunk
+    const int tc = t0 + min(n32, nv - 1);
+    const T* qrow = qp + (size_t)tc * Fp;
+    // per feature tile: its two query fragments feed the partial scores A^T[s][t] and, right away, the readout
+    // against the state before this chunk (num^T += S^T Phi(Q)^T), so only two fragments are live at a time
+    f32x16 at, num[2];
+    zero16(at);
+    zero16(num[0]);
+    zero16(num[1]);
+    float dz = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) {
+        const int base = 32 * (w + 4 * i) + 16 * kk;
+        const Frag QF = slot_frag<T>(qrow, base, h);
+        mma32(at, slot_frag<T>(KT + n32 * KP, base, h), QF);
+#pragma unroll
+        for (int s = 0; s < 8; s++) dz = fmaf((float)QF[s], zs[base + 8 * (s >> 2) + 4 * h + (s & 3)], dz);
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          float x[8];
+#pragma unroll
+          for (int s = 0; s < 8; s++) x[s] = Sacc[i][vt][8 * kk + s];
+          mma32(num[vt], pack8f<T>(x), QF);
+        }
+      }
+    // masked partial scores (s <= t), their row sums, and V^T P
+    float lo[8], hi8[8];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int s = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float a = s > n32 ? 0.0f : at[r];
+      if (r < 8) lo[r] = a;
+      else hi8[r - 8] = a;
+    }
+    const Frag P0 = pack8f<T>(lo), P1 = pack8f<T>(hi8);
+    float den = frag_sum(P1, frag_sum(P0, dz));
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++) {
+      mma32(num[vt], lds_tokfrag(VT, VP, 0, 32 * vt, l), P0);
+      mma32(num[vt], lds_tokfrag(VT, VP, 16, 32 * vt, l), P1);
+    }
+    den = xor32_sum(den);
+    float* rw = red + (w * kFC + n32) * RP;
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *reinterpret_cast<float4*>(rw + 32 * vt + 8 * j + 4 * h) =
+            make_float4(num[vt][4 * j], num[vt][4 * j + 1], num[vt][4 * j + 2], num[vt][4 * j + 3]);
+    if (h == 0) rw[64] = den;
+    __syncthreads();
+    {
+      const int row = tid >> 3, c0 = 8 * (tid & 7);
+      if (row < nv) {
+        constexpr int WS = kFC * RP;
+        const float* b0 = red + row * RP;
+        const float dsum = ((b0[64] + b0[WS + 64]) + b0[2 * WS + 64]) + b0[3 * WS + 64];
+        const float inv = 1.0f / (dsum + ceps);
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          o[e] = (((b0[c0 + e] + b0[WS + c0 + e]) + b0[2 * WS + c0 + e]) + b0[3 * WS + c0 + e]) * inv;
+#pragma unroll
+        for (int e = 0; e < 8; e++) op[(size_t)(t0 + row) * kDV + c0 + e] = from_f32<T>(o[e]);
+      }
+    }
+    // state update S += Phi(K)^T V and z += Phi(K)^T 1 over this wave's feature tiles
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      const int ft = w + 4 * i;
+      float zsum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        const Frag A = lds_tokfrag(KT, KP, 16 * ks, 32 * ft, l);
+        zsum = frag_sum(A, zsum);
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) mma32(Sacc[i][vt], A, lds_tokfrag(VT, VP, 16 * ks, 32 * vt, l));
+      }
+      zsum = xor32_sum(zsum);
+      // every wave read zs for this chunk's readout before the reduction barrier; each wave updates its own tiles
+      if (h == 0) zs[32 * ft + n32] += zsum;
+    }
+    __syncthreads();  // tiles and the reduction buffer are reused by the next chunk
+  }
+  if (Sp) {
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (f < Freal) Sp[(size_t)f * kDV + 32 * vt + n32] = Sacc[i][vt][r];
+        }
+    for (int f = tid; f < Freal; f += 256) zp[f] = zs[f];
+  }
+}
+
+template <typename Kern>
+hipError_t set_lds_once(Kern k, int bytes, std::atomic<bool>& flag) {
+  if (flag.load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) flag.store(true, std::memory_order_release);
+  return e;
+}
+
+template <typename TIn, int KIND, int NH, int NFT>
+hipError_t launch_fp_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
+                       const MethodConsts& mc, float* S, float* z, void* out, void* ws, int Freal,
+                       hipStream_t stream) {
+  using G = FGeom<TIn, NFT>;
+  const int BH = B * H, ntiles = (Tn + 31) / 32;
+  TIn* phiq = static_cast<TIn*>(ws);
+  TIn* phik = phiq + (size_t)BH * Tn * G::Fp;
+  const dim3 fgrid((unsigned)((long long)BH * ntiles)), fblk(256);
+  hipLaunchKernelGGL((featurize_ext_kernel<TIn, TIn, KIND, NH, true>), fgrid, fblk, 0, stream,
+                     static_cast<const TIn*>(q), phiq, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
+                     ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((featurize_ext_kernel<TIn, TIn, KIND, NH, false>), fgrid, fblk, 0, stream,
+                     static_cast<const TIn*>(k), phik, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
+                     ntiles);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  static std::atomic<bool> attr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT>, G::lds, attr[dev])) != hipSuccess) return e;
+  hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT>), dim3(BH), dim3(256), G::lds, stream, phiq, phik,
+                     static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// padded feature count of a map: harmonics (2 + 4 nh) d, four-channel 3 d + 1, rounded up to 128
+int ext_features_padded(int nh_or_zero) {
+  const int f = nh_or_zero > 0 ? (2 + 4 * nh_or_zero) * kD : 3 * kD + 1;
+  return (f + 127) / 128 * 128;
+}
+
+size_t ext_prefill_ws_bytes(int B, int H, int T, sanatan_dtype t, int nh_or_zero) {
+  const size_t el = t == SANATAN_BF16 ? 2 : 4;
+  return 2 * (size_t)B * H * T * ext_features_padded(nh_or_zero) * el;
+}
+
+// nh_or_zero: 1 or 2 harmonics, or 0 for the four-channel compact map
+hipError_t launch_ext_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                              int nh_or_zero, int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out,
+                              void* ws, hipStream_t stream) {
+  const bool bf = t == SANATAN_BF16;
+  switch (nh_or_zero) {
+    case 0:
+      return bf ? launch_fp_t<__bf16, 1, 0, 8>(q, k, v, B, H, T, pos0, mc, S, z, out, ws, 3 * kD + 1, stream)
+                : launch_fp_t<float, 1, 0, 8>(q, k, v, B, H, T, pos0, mc, S, z, out, ws, 3 * kD + 1, stream);
+    case 1:
+      return bf ? launch_fp_t<__bf16, 0, 1, 12>(q, k, v, B, H, T, pos0, mc, S, z, out, ws, 6 * kD, stream)
+                : launch_fp_t<float, 0, 1, 12>(q, k, v, B, H, T, pos0, mc, S, z, out, ws, 6 * kD, stream);
+    case 2:
+      return bf ? launch_fp_t<__bf16, 0, 2, 20>(q, k, v, B, H, T, pos0, mc, S, z, out, ws, 10 * kD, stream)
+                : launch_fp_t<float, 0, 2, 20>(q, k, v, B, H, T, pos0, mc, S, z, out, ws, 10 * kD, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sanatan

@@ -68,6 +68,17 @@ hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan
                             int p, bool four_channel, int64_t pos0, const MethodConsts& mc, void* out, void* ws,
                             hipStream_t stream);
 
+// Materialized-feature chunked prefill: nh_or_zero = 1 or 2 spectral harmonics (state rows (2 + 4 nh) d), or 0 for the
+// unclipped four-channel compact map (3d + 1 rows).  Workspace: Phi(Q), Phi(K) padded to ext_features_padded.
+int ext_features_padded(int nh_or_zero);
+size_t ext_prefill_ws_bytes(int B, int H, int T, sanatan_dtype t, int nh_or_zero);
+hipError_t launch_ext_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
+                              int nh_or_zero, int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out,
+                              void* ws, hipStream_t stream);
+hipError_t launch_decode_step_harmonics(const float* q, const float* k, const float* v, int N, int64_t pos,
+                                        const int64_t* posv, int nh, const MethodConsts& mc, float* S, float* z,
+                                        float* out, hipStream_t stream);
+
 // Gradient of normalised causal power attention (p = 1 or 2) with respect to q, k, v and omega.  Workspace:
 // phase table, Phi(Q), Phi(K) (element type t), per-row statistics, fp32 feature gradients, omega partials.
 size_t backward_ws_bytes(int B, int H, int T, sanatan_dtype t);
