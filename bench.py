@@ -162,8 +162,19 @@ def graph_of(torch, fn):
         return None
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The fp64 oracle (recurrent form, all host threads) on a bounded sample of the prefill workload."""
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, budget_s=8.0):
+    """The fp64 oracle (recurrent form, all host threads) on a bounded sample of the prefill workload, timed
+    three times (the median is reported)."""
     import oracle
     import sanatan_inputs as si
 
@@ -181,13 +192,16 @@ def cpu_baseline(w, budget_s=20.0):
     ks = np.stack([k[b, h] for b, h in sel])
     vs = np.stack([v[b, h] for b, h in sel])
     oms = np.stack([om[h] for _, h in sel])
-    t0 = time.perf_counter()
-    oracle.recurrent_heads(qs, ks, vs, oms)
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.recurrent_heads(qs, ks, vs, oms)
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[1]
     tokens = n_heads * w.T / w.H  # a token carries H heads
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
-            "sample": f"recurrent fp64 oracle over {n_heads} of {len(heads)} (b,h) sequences x {w.T} tokens "
-                      f"({dt:.1f} s wall)"}
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle", "cpu_model": host_cpu_model(),
+            "sample": f"recurrent fp64 oracle over {n_heads} of {len(heads)} (b,h) sequences x {w.T} tokens, "
+                      f"median of 3 runs ({', '.join(f'{r:.1f}' for r in runs)} s wall)"}
 
 
 def cpu_oracle_extras(si):
@@ -216,6 +230,19 @@ def cpu_oracle_extras(si):
     res["long_prefill"] = {"value": n_tok / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
                            "sample": f"recurrent fp64 oracle, {w.H} heads x the first {n_tok} of {w.T} tokens "
                                      f"({dt:.2f} s wall)"}
+    # the headline prefill in its direct-kappa form: 128 query rows spread over one head, extrapolated by pairs
+    w = si.PREFILL
+    q, k, v, om = si.attention_inputs(w.seed, 1, 1, w.T, "bf16")
+    rows = np.linspace(0, w.T - 1, 128).astype(np.int64)
+    pairs = float((rows + 1).sum())
+    t0 = time.perf_counter()
+    oracle.attention_direct(q[0, 0], k[0, 0], v[0, 0], om[0], p=1, rows=rows)
+    dt = time.perf_counter() - t0
+    full_s = dt / pairs * (w.B * w.H * w.T * (w.T + 1) / 2)
+    res["prefill_direct_kappa"] = {
+        "value": w.B * w.T / full_s, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+        "sample": f"direct-kappa fp64 oracle, {rows.size} query rows of one head ({int(pairs)} pairs, {dt:.2f} s "
+                  f"wall), extrapolated by causal pairs to the whole headline workload"}
     # quadratic p=2: direct kappa on 256 query rows spread over one head, extrapolated by causal pairs
     w = si.QUAD_P2
     q, k, v, om = si.attention_inputs(w.seed, 1, 1, w.T, "bf16")
@@ -401,6 +428,50 @@ def bench_featurize(torch, rpg, si, w, steps, warmup):
     return eager, graph, w.B * w.H * w.T * 64 * el * 7
 
 
+def bench_feature_map(torch, rpg, si, w, nh, steps, warmup):
+    """ms per call (eager, graph-replayed) of the materialized-feature chunked prefill on workload w's inputs:
+    the spectral-harmonic map with nh harmonics, or (nh = 0) the unclipped four-channel map."""
+    q, k, v, om = si.workload_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(dt) for x in (q, k, v))
+    del q, k, v
+    p = rpg.Params(omega=torch.from_numpy(om).cuda(), gamma=w.gamma, eps=w.eps, lambda_base=w.lambda_base)
+    code = rpg.SANATAN_BF16 if w.dtype == "bf16" else rpg.SANATAN_F32
+    if nh > 0:
+        need = rpg.sanatan_prefill_harmonics_workspace_bytes(w.B, w.H, w.T, code, nh, p)
+    else:
+        need = rpg.sanatan_prefill_four_channel_workspace_bytes(w.B, w.H, w.T, code, p)
+    ws = torch.empty((int(need),), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(vd)
+    if nh > 0:
+        fn = lambda: rpg.sanatan_prefill_harmonics(qd, kd, vd, nh, p, out=out, ws=ws)
+    else:
+        fn = lambda: rpg.sanatan_prefill_four_channel(qd, kd, vd, p, out=out, ws=ws)
+    eager = timed_loop(torch, fn, steps, warmup)
+    g = graph_of(torch, fn)
+    graph = timed_loop(torch, g.replay, steps, warmup) if g is not None else None
+    return eager, graph
+
+
+def chunked_flops(B, H, T, C, F_, DV_=DV):
+    """Causal FLOPs of a chunked p = 1 prefill with F_ features per head (causal pairs inside chunks, readout
+    and update per token)."""
+    per_head = 0
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        per_head += 2 * (n * (n + 1) // 2) * (F_ + DV_) + 2 * n * F_ * DV_ * 2
+    return B * H * per_head
+
+
+def mfma_line(fl, ms):
+    return {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+ONLY = ("prefill", "decode1", "decode64", "long", "quad", "quad4", "backward_p2", "backward_p1", "featurize",
+        "harmonics", "four_channel")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,13 +480,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--only", choices=ONLY,
+                    help="time one workload and print its own JSON line (for profiling runs), not the headline line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain %d MiB device copy first (reference kernel for memory counters)" % (CAL_BYTES >> 20))
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json")
+    ap.add_argument("--traffic-key", default="prefill_b8h12_t2048")
     args = ap.parse_args()
     if args.traffic:
-        traffic_summary(args.traffic[0], args.traffic[1], "prefill_b8h12_t2048")
+        traffic_summary(args.traffic[0], args.traffic[1], args.traffic_key)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -439,6 +513,29 @@ def main():
         torch.cuda.synchronize()
         del src_buf, dst_buf
     w = si.PREFILL
+    small = max(5, args.steps // 5)
+    if args.only:
+        rec = {"only": args.only}
+        if args.only == "prefill":
+            rec["ms"] = bench_prefill_like(torch, rpg, si, w, args.steps, args.warmup)
+        elif args.only in ("decode1", "decode64"):
+            b = 1 if args.only == "decode1" else 64
+            rec.update(bench_decode(torch, rpg, si, b, args.decode_steps, 16))
+        elif args.only == "long":
+            rec["ms"] = bench_prefill_like(torch, rpg, si, si.LONG, small, 3)
+        elif args.only in ("quad", "quad4"):
+            rec["ms"] = bench_prefill_like(torch, rpg, si, si.QUAD_P2, small, 3, quadratic=True,
+                                           four_channel=args.only == "quad4")
+        elif args.only.startswith("backward"):
+            wb, pb = (si.QUAD_P2, 2) if args.only == "backward_p2" else (w, 1)
+            rec["ms"] = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2)
+        elif args.only == "featurize":
+            rec["ms"] = bench_featurize(torch, rpg, si, w, small, 3)[:2]
+        elif args.only in ("harmonics", "four_channel"):
+            rec["ms"] = bench_feature_map(torch, rpg, si, w, 2 if args.only == "harmonics" else 0, small, 3)
+        print(json.dumps(rec))
+        return
+
     log(f"prefill {w.name}: {args.warmup} warmup + {args.steps} timed steps")
     eager_ms, graph_ms = bench_prefill_like(torch, rpg, si, w, args.steps, args.warmup)
     use_graph = graph_ms is not None and graph_ms < eager_ms
@@ -449,7 +546,9 @@ def main():
     tokens = w.B * w.T
     fl = prefill_flops(w.B, w.H, w.T, w.chunk)
     fl_dense = prefill_flops(w.B, w.H, w.T, w.chunk, causal=False)
-    achieved = fl / (call_ms * 1e-3) / 1e12
+    nbytes = prefill_bytes(w.B, w.H, w.T)
+    achieved_tf = fl / (call_ms * 1e-3) / 1e12
+    achieved_gbs = nbytes / (call_ms * 1e-3) / 1e9
     src = source_hash(*PREFILL_SOURCES)
     result = {
         "metric": "prefill tokens/s (12h x d64, T=2K, p=1)",
@@ -466,17 +565,21 @@ def main():
         "data": "synthetic: q,k,v ~ N(0,1) rounded to bf16, omega ~ U(-pi,pi), seeded (sanatan_inputs)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": D, "d_v": DV, "chunk": w.chunk,
                    "p": 1, "gamma": w.gamma, "lambda_base": w.lambda_base},
+        # At about 249 flop per algorithmic byte the workload sits below the bf16 ridge (~315 flop/byte): the HBM
+        # roof (12.6 us) binds before the MFMA roof (10.0 us), so the line is priced against HBM, with the MFMA
+        # fraction beside it.
         "roofline": {
-            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
+            "bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved_gbs / PEAK_HBM_GBS,
             "traffic": traffic_from_profiles("prefill_b8h12_t2048", src),
             "kernel": "sanatan_prefill_chunked: phase table + pass 1 (state increments) + pass 3 (outputs), "
                       "timed as one launch sequence",
             "timing": "graph-replayed call" if use_graph else "eager call",
             "ms_per_call_eager": eager_ms, "ms_per_call_graph": graph_ms,
+            "hbm_bytes_algorithmic": nbytes,
+            "mfma_achieved_tflops": achieved_tf, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
+            "mfma_frac": achieved_tf / PEAK_BF16_TFLOPS,
             "flops_per_launch": fl, "flops_dense_tile": fl_dense,
-            "hbm_bytes_algorithmic": prefill_bytes(w.B, w.H, w.T),
-            "hbm_frac_algorithmic": prefill_bytes(w.B, w.H, w.T) / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "source_hash": src,
         },
     }
@@ -493,41 +596,30 @@ def main():
                 log(f"decode batch {b}, one position per sequence")
                 extras[f"decode_batch{b}_positions"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16,
                                                                     positions=True)
-                log(f"decode batch {b}, positions: {extras[f'decode_batch{b}_positions']['us_per_token']:.2f} us/token")
             log(f"decode batch {b}, compact state")
             extras[f"decode_batch{b}_compact"] = bench_decode(torch, rpg, si, b, args.decode_steps, 16, compact=True)
-            log(f"decode batch {b}, compact: {extras[f'decode_batch{b}_compact']['us_per_token']:.2f} us/token")
             log(f"decode batch {b}: {extras[f'decode_batch{b}']['us_per_token']:.2f} us/token")
         wl = si.LONG
         log(f"long prefill {wl.name}")
-        lms_e, lms_g = bench_prefill_like(torch, rpg, si, wl, max(5, args.steps // 5), 3)
+        lms_e, lms_g = bench_prefill_like(torch, rpg, si, wl, small, 3)
         lms = min(lms_e, lms_g) if lms_g is not None else lms_e
-        lfl = prefill_flops(wl.B, wl.H, wl.T, wl.chunk)
         extras["long_prefill"] = {"workload": wl.name, "tokens_per_s": wl.B * wl.T / (lms * 1e-3), "ms": lms,
                                   "ms_eager": lms_e, "ms_graph": lms_g,
-                                  "roofline": {"bound": "mfma", "achieved": lfl / (lms * 1e-3) / 1e12,
-                                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                               "frac": lfl / (lms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+                                  "roofline": mfma_line(prefill_flops(wl.B, wl.H, wl.T, wl.chunk), lms)}
         wq = si.QUAD_P2
         log(f"quadratic {wq.name}")
-        qms_e, qms_g = bench_prefill_like(torch, rpg, si, wq, max(5, args.steps // 5), 3, quadratic=True)
+        qms_e, qms_g = bench_prefill_like(torch, rpg, si, wq, small, 3, quadratic=True)
         qms = min(qms_e, qms_g) if qms_g is not None else qms_e
-        qfl = quadratic_flops(wq.B, wq.H, wq.T)
         extras["quadratic_p2"] = {"workload": wq.name, "tokens_per_s": wq.B * wq.T / (qms * 1e-3), "ms": qms,
                                   "ms_eager": qms_e, "ms_graph": qms_g,
-                                  "roofline": {"bound": "mfma", "achieved": qfl / (qms * 1e-3) / 1e12,
-                                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                               "frac": qfl / (qms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+                                  "roofline": mfma_line(quadratic_flops(wq.B, wq.H, wq.T), qms)}
         log(f"quadratic {wq.name}, unclipped four-channel kernel")
-        q4_e, q4_g = bench_prefill_like(torch, rpg, si, wq, max(5, args.steps // 5), 3, quadratic=True,
-                                        four_channel=True)
+        q4_e, q4_g = bench_prefill_like(torch, rpg, si, wq, small, 3, quadratic=True, four_channel=True)
         q4 = min(q4_e, q4_g) if q4_g is not None else q4_e
-        q4fl = quadratic_flops(wq.B, wq.H, wq.T, features=4 * D)
         extras["quadratic_p2_four_channel"] = {
             "workload": wq.name + "_four_channel", "tokens_per_s": wq.B * wq.T / (q4 * 1e-3), "ms": q4,
             "ms_eager": q4_e, "ms_graph": q4_g,
-            "roofline": {"bound": "mfma", "achieved": q4fl / (q4 * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": q4fl / (q4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "roofline": mfma_line(quadratic_flops(wq.B, wq.H, wq.T, features=4 * D), q4),
             "note": "unclipped four-channel kernel: 2 (4d + d_v) flops per causal pair"}
         for key, wb, pb in (("backward_p2", si.QUAD_P2, 2), ("backward_p1", w, 1)):
             log(f"backward {wb.name}, p={pb}")
@@ -536,13 +628,20 @@ def main():
             bfl = backward_flops(wb.B, wb.H, wb.T)
             extras[key] = {"workload": f"{wb.name}_backward_p{pb}", "ms": bms, "ms_eager": be, "ms_graph": bg,
                            "tokens_per_s": wb.B * wb.T / (bms * 1e-3), "flops_per_call": bfl,
-                           "roofline": {"bound": "mfma", "achieved": bfl / (bms * 1e-3) / 1e12,
-                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                        "frac": bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                           "roofline": mfma_line(bfl, bms),
                            "note": "gradients of q, k, v, omega (sanatan_attention_backward, masked quadratic form); "
                                    "flops: 2 (3 x 6d + 2 d_v) per causal pair"}
+        for key, nh, feats in (("harmonics_nh2_prefill", 2, 10 * D), ("four_channel_prefill", 0, 3 * D + 1)):
+            log(f"{key} {w.name}")
+            he, hg = bench_feature_map(torch, rpg, si, w, nh, small, 3)
+            hms = min(he, hg) if hg is not None else he
+            extras[key] = {"workload": f"{w.name}_{key}", "ms": hms, "ms_eager": he, "ms_graph": hg,
+                           "tokens_per_s": w.B * w.T / (hms * 1e-3),
+                           "roofline": mfma_line(chunked_flops(w.B, w.H, w.T, 32, feats), hms),
+                           "note": f"materialized-feature chunked prefill, {feats} features per head, chunk 32, "
+                                   "one workgroup per sequence"}
         log(f"featurize {w.name} keys")
-        fms_e, fms_g, fbytes = bench_featurize(torch, rpg, si, w, max(5, args.steps // 5), 3)
+        fms_e, fms_g, fbytes = bench_featurize(torch, rpg, si, w, small, 3)
         fms = min(fms_e, fms_g) if fms_g is not None else fms_e
         extras["featurize"] = {"workload": f"featurize_keys_of_{w.name}", "ms": fms, "ms_eager": fms_e,
                                "ms_graph": fms_g, "bytes_per_call": fbytes,

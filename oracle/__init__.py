@@ -27,10 +27,12 @@ EPS = 1e-6
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so (gcc, -O2, OpenMP, no fast-math, no FMA contraction)."""
+    """Compile oracle.c into liboracle.so (gcc -O3, OpenMP, no fast-math, no FMA contraction).  The target is
+    x86-64-v3 (AVX2), not -march=native: the library is built on one machine and run on another machine's host
+    CPU.  Without fast-math and with contraction off, the vector code gives the same results as scalar code."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+        cmd = ["gcc", "-std=c11", "-O3", "-march=x86-64-v3", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
                "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)

@@ -540,6 +540,20 @@ def sanatan_harmonics_state_bytes(d: int = D, d_v: int = DV, nh: int = 2) -> int
     return int(lib().sanatan_harmonics_state_bytes(int(d), int(d_v), int(nh)))
 
 
+def sanatan_prefill_harmonics_workspace_bytes(B: int, H: int, T: int, dtype_code: int, nh: int,
+                                              params: Params | None = None) -> int:
+    p = params.struct() if params is not None else None
+    return int(lib().sanatan_prefill_harmonics_workspace_bytes(B, H, T, dtype_code, int(nh),
+                                                               ctypes.byref(p) if p is not None else None))
+
+
+def sanatan_prefill_four_channel_workspace_bytes(B: int, H: int, T: int, dtype_code: int,
+                                                 params: Params | None = None) -> int:
+    p = params.struct() if params is not None else None
+    return int(lib().sanatan_prefill_four_channel_workspace_bytes(B, H, T, dtype_code,
+                                                                  ctypes.byref(p) if p is not None else None))
+
+
 def _ext_prefill(entry, q, k, v, params: Params, pos0, S, z, out, ws, rows, ws_fn):
     import torch
 

@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import sanatan_inputs as si
+from parity_log import record
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +95,9 @@ def run_case(torch, seed, B, H, T, dtype, p, nph=None, pos0=0, heads=None):
     if heads is None:
         errs["domega"] = row_rel_err(dom, want_dom)
     print(f"backward B{B} H{H} T{T} {dtype} p={p} nph={nph}: " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    if T > 1:
+        for name, e in errs.items():
+            record(f"backward {dtype} p={p}: {name}", e, TOL[dtype])
     return errs
 
 

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import sanatan_inputs as si
+from parity_log import record
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +85,7 @@ def test_harmonics_prefill(torch_dev, nh, dtype, T):
         assert np.abs(host(S)[0, h] - Sw).max() <= TOL[dtype] * np.abs(Sw).max()
         assert np.abs(host(z)[0, h] - zw).max() <= TOL[dtype] * np.abs(zw).max()
     print(f"harmonics nh={nh} {dtype} T={T}: max row error {err:.3e}")
-    assert err <= TOL[dtype]
+    assert record(f"harmonics prefill nh={nh} {dtype}", err, TOL[dtype]) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("nh", [1, 2])
@@ -116,7 +117,7 @@ def test_harmonics_decode_continues_prefill(torch_dev, nh):
         assert np.abs(host(S)[0, h] - Sw).max() <= 1e-4 * np.abs(Sw).max()
         assert np.abs(host(z)[0, h] - zw).max() <= 1e-4 * np.abs(zw).max()
     print(f"harmonics decode nh={nh}: max row error {err:.3e}")
-    assert err <= TOL["f32"]
+    assert record(f"harmonics decode nh={nh} f32", err, TOL["f32"]) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("dtype,T", [("f32", 97), ("bf16", 260)])
@@ -154,5 +155,5 @@ def test_four_channel_prefill(torch_dev, dtype, T):
         assert np.abs(S4_after[0, h] - Sw).max() <= TOL[dtype] * np.abs(Sw).max()
         assert np.abs(z4_after[0, h] - zw).max() <= TOL[dtype] * np.abs(zw).max()
     print(f"four-channel prefill {dtype} T={T}: max row error {err:.3e}, decode after it {errd:.3e}")
-    assert err <= TOL[dtype]
-    assert errd <= TOL[dtype]
+    assert record(f"four-channel chunked prefill {dtype}", err, TOL[dtype]) <= TOL[dtype]
+    assert record("four-channel decode after the prefill f32", errd, TOL[dtype]) <= TOL[dtype]

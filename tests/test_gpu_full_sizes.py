@@ -5,6 +5,7 @@ import pytest
 
 import oracle
 import sanatan_inputs as si
+from parity_log import record
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +51,8 @@ def test_prefill_b8h12_t2048(torch_dev):
     assert np.isfinite(got).all()
     for b, h in [(0, 0), (3, 7), (7, 11)]:
         want, _, _ = oracle.recurrent(q[b, h], k[b, h], v[b, h], om[h])
-        assert row_rel_err(got[b, h], want) <= TOL[w.dtype], (b, h)
+        err = record(f"prefill {w.name} (3 sequences)", row_rel_err(got[b, h], want), TOL[w.dtype])
+        assert err <= TOL[w.dtype], (b, h)
 
 
 def test_long_prefill_b1h12_t32768(torch_dev):
@@ -60,7 +62,8 @@ def test_long_prefill_b1h12_t32768(torch_dev):
     heads = [0, 11]
     want, _, _ = oracle.recurrent_heads(q[0, heads], k[0, heads], v[0, heads], om[heads])
     for j, h in enumerate(heads):
-        assert row_rel_err(got[0, h], want[j]) <= TOL[w.dtype], h
+        err = record(f"long prefill {w.name} (heads 0, 11)", row_rel_err(got[0, h], want[j]), TOL[w.dtype])
+        assert err <= TOL[w.dtype], h
     # explicitly the chunk-boundary rows, the first rows and the last row
     C = w.chunk
     rows = sorted(set([0, 1, w.T - 1] + [t for j in range(1, w.T // C) for t in (C * j - 1, C * j)]))
@@ -75,7 +78,8 @@ def test_quadratic_p2_b4h12_t4096(torch_dev):
     for b, h in [(0, 0), (2, 5), (3, 11)]:
         rows = sorted(set([0, 1, 63, 64, 127, 128, w.T - 1] + list(rng.integers(0, w.T, 12))))
         want = oracle.attention_direct(q[b, h], k[b, h], v[b, h], om[h], p=w.p, rows=rows)
-        assert row_rel_err(got[b, h, rows], want) <= TOL[w.dtype], (b, h)
+        err = record(f"quadratic {w.name} (sampled rows)", row_rel_err(got[b, h, rows], want), TOL[w.dtype])
+        assert err <= TOL[w.dtype], (b, h)
 
 
 @pytest.mark.parametrize("batch", [1, 64])
@@ -115,6 +119,35 @@ def test_decode_after_4096_token_fill(torch_dev, batch):
     Dv = (sv[:, sample].cpu().numpy() if hasattr(sv, "cpu") else sv[:, sample]).transpose(1, 0, 2)
     _, S0, z0 = oracle.recurrent_heads(Fq, Fk, Fv, om[hs], want_out=False)
     want, Sw, zw = oracle.recurrent_heads(Dq, Dk, Dv, om[hs], pos0=fill, S=S0, z=z0)
-    assert row_rel_err(got, want) <= TOL["f32"]
+    err = record(f"decode {w.name} batch {batch} (sampled head-states)", row_rel_err(got, want), TOL["f32"])
+    assert err <= TOL["f32"]
     Sg = S[idx].cpu().numpy()
     assert np.abs(Sg - Sw).max() <= 1e-4 * np.abs(Sw).max()
+
+
+def test_tiny_config_three_forms(torch_dev):
+    """The tiny workload's own seeded inputs (B1 H1 T256 fp32, seed 1000, positions from 0) through all three GPU
+    forms -- the chunked prefill at chunk 64, the masked quadratic form at p = 1 and 256 decode steps from an
+    empty state -- each against the oracle on the same inputs ([N] §2.7: the parallel and recurrent forms are the
+    same function)."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    w = si.TINY
+    q, k, v, om = si.workload_inputs(w)
+    want = oracle.attention_direct(q[0, 0], k[0, 0], v[0, 0], om[0])
+    want_rec, Sw, zw = oracle.recurrent(q[0, 0], k[0, 0], v[0, 0], om[0])
+    assert row_rel_err(want_rec, want) <= 1e-12  # the two oracle forms agree
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    p = rpg.Params(omega=d(om), gamma=w.gamma, eps=w.eps, lambda_base=w.lambda_base)
+    chunked = rpg.sanatan_prefill_chunked(d(q), d(k), d(v), w.chunk, p).cpu().numpy()[0, 0]
+    quad = rpg.sanatan_quadratic_ref_p2(d(q), d(k), d(v), 1, p).cpu().numpy()[0, 0]
+    S = torch.zeros((1, 384, 64), device="cuda")
+    z = torch.zeros((1, 384), device="cuda")
+    rec = np.stack([rpg.sanatan_decode_step(d(q[0, 0, t:t + 1]), d(k[0, 0, t:t + 1]), d(v[0, 0, t:t + 1]), t, p, S,
+                                            z).cpu().numpy()[0] for t in range(w.T)])
+    torch.cuda.synchronize()
+    for form, got in (("chunked C=64", chunked), ("quadratic p=1", quad), ("recurrent (256 decode steps)", rec)):
+        err = record(f"tiny {w.name}: {form}", row_rel_err(got, want), TOL["f32"])
+        assert err <= TOL["f32"], form
+    assert np.abs(S.cpu().numpy()[0] - Sw).max() <= 1e-4 * np.abs(Sw).max()
