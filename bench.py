@@ -97,7 +97,9 @@ def traffic_summary(fetch_dir, write_dir, key):
     out = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
-        cal = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        # the calibration copies are the run's first three copy dispatches (workloads may copy buffers later)
+        cal_rows = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+        cal = [float(r["Counter_Value"]) for r in cal_rows[:3]]
         if not cal:
             raise SystemExit(f"no calibration copy found in {d}")
         scale = CAL_BYTES / (max(cal) * 1024.0)
