@@ -241,7 +241,9 @@ sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void
  *   kappa4(t,s) = sum_a 1 + r_q r_k (1 + cos(theta_q - theta_k + (t - s) lambda_a)),
  *   w = (kappa4/c)^p for s <= t, o_t = sum_{s<=t} w v_s / (sum w + eps).
  * No max(kappa4, 0) is applied: a mismatched pair of hard roots contributes -cos(dtheta) to a dim, so with
- * p = 1 a weight, and the denominator, can be negative or near zero.  c is the caller's (params->c).
+ * p = 1 a weight, and the denominator, can be negative or near zero.  With p = 2 strongly mismatched pairs
+ * get large positive weights: this is not the clipped four-channel attention max(kappa4, 0)^p of the pages'
+ * own implementation, which this library does not provide.  c is the caller's (params->c).
  * Arguments, workspace and errors exactly as sanatan_quadratic_ref_p2.
  */
 sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, const void* v, sanatan_dtype t,

@@ -2,8 +2,12 @@
 //
 // SANATAN reading notes §2.6: w_ts = (kappa_ts / c)^p for s <= t, o_t = sum w v_s / (sum w + eps);
 // kappa_ts = <Phi(q_t), Phi(k_s)> (§2.3).  p = 2 has no small-state recurrence (§2.6, §4.1), so
-// this is the training/parallel form.  Because 0 <= kappa <= 4d = c, every weight lies in [0, 1]
-// and no running maximum is needed (unlike softmax): partial sums over key blocks just add.
+// this is the training/parallel form.  For the six-channel kernel 0 <= kappa <= 4d = c, so every
+// weight lies in [0, 1] and no running maximum is needed (unlike softmax): partial sums over key
+// blocks just add.  The unclipped four-channel instantiation (C0 = 3) has kappa4 in [-d, 3d]: its
+// p = 1 weights and denominators can be negative or near zero, and its p = 2 weights give
+// strongly mismatched pairs large positive weight; partial sums still just add (no maximum is
+// needed for bounded weights), but the p = 2 result is not the clipped four-channel attention.
 //
 // Phi(K) is featurized once into the workspace (element type of the call), after the position
 // phase table.  A workgroup is 4 waves and two workgroups share a CU (two waves per SIMD hide each
