@@ -122,6 +122,28 @@ sanatan_status sanatan_prefill_chunked_partitioned(const void* q, const void* k,
                                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * sanatan_prefill_chunked_ragged -- sanatan_prefill_chunked over a batch of sequences of different lengths in
+ * one call: the prompts of a serving batch, whose states then continue at their own positions in
+ * sanatan_decode_step_positions.  The recurrence of [N] §2.7 runs per sequence, so batch element b is the
+ * prefill of its first lengths[b] tokens alone.
+ *   q, k, v, out : [B][H][T][.] as for sanatan_prefill_chunked, right-padded: batch element b uses rows
+ *                  0 .. lengths[b] - 1 of each head; rows from lengths[b] on are neither read nor written.
+ *   lengths      : DEVICE int32 [B]; each value is clamped to [0, T] (the host cannot see them).  A length of
+ *                  0 leaves that element's output rows and state untouched.
+ *   pos0         : position of token 0 of every sequence; checked as for sanatan_prefill_chunked over T.
+ *   S, z         : as for sanatan_prefill_chunked; on exit element b's state is the one after its last token.
+ *   ws           : at least sanatan_prefill_workspace_bytes(B, H, T, chunk) bytes.
+ * The chunks of all sequences are split over one workgroup per compute unit as one flattened list, so one
+ * launch balances the whole batch.  Every call runs the state pass and the boundary scan (the pieces depend
+ * on the lengths), a few microseconds more than a uniform call with the same chunk count.
+ * Errors: those of sanatan_prefill_chunked, and INVALID_ARG for a NULL lengths pointer.
+ */
+sanatan_status sanatan_prefill_chunked_ragged(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                              int H, int T, int chunk, const int32_t* lengths, int64_t pos0,
+                                              const sanatan_params* params, float* S, float* z, void* out,
+                                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * sanatan_prefill_chunked_noalloc -- sanatan_prefill_chunked without a caller workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  The workspace is a fixed 48 MiB device array inside the library (one per GPU, held until

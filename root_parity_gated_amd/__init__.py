@@ -70,6 +70,9 @@ def lib():
         L.sanatan_prefill_chunked_partitioned.restype = i32
         L.sanatan_prefill_chunked_partitioned.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, pp, vp, vp,
                                                           vp, vp, sz, vp]
+        L.sanatan_prefill_chunked_ragged.restype = i32
+        L.sanatan_prefill_chunked_ragged.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i64, pp, vp, vp, vp,
+                                                     vp, sz, vp]
         L.sanatan_prefill_chunked_noalloc.restype = i32
         L.sanatan_prefill_chunked_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, vp]
         L.sanatan_decode_step.restype = i32
@@ -118,7 +121,7 @@ def lib():
 EXPORTED = [
     "sanatan_state_bytes", "sanatan_status_string", "sanatan_featurize", "sanatan_prefill_workspace_bytes",
     "sanatan_prefill_chunked", "sanatan_prefill_workspace_bytes_partitioned", "sanatan_prefill_chunked_partitioned",
-    "sanatan_prefill_chunked_noalloc", "sanatan_decode_step", "sanatan_decode_step_positions",
+    "sanatan_prefill_chunked_noalloc", "sanatan_prefill_chunked_ragged", "sanatan_decode_step", "sanatan_decode_step_positions",
     "sanatan_compact_state_bytes", "sanatan_state_compact", "sanatan_state_expand", "sanatan_decode_step_compact",
     "sanatan_four_channel_state_bytes", "sanatan_decode_step_four_channel",
     "sanatan_quadratic_workspace_bytes",
@@ -301,6 +304,39 @@ def sanatan_prefill_chunked_partitioned(q, k, v, chunk: int, workgroups: int, pa
                                                        int(chunk), int(workgroups), int(pos0), ctypes.byref(p),
                                                        _ptr(S), _ptr(z), _ptr(out), _ptr(ws), ws.numel(), _stream())
     _check(st, _entry)
+    return out
+
+
+def sanatan_prefill_chunked_ragged(q, k, v, lengths, chunk: int, params: Params, pos0: int = 0, S=None, z=None,
+                                   out=None, ws=None):
+    """One prefill call over sequences of different lengths: batch element b uses its first lengths[b] rows
+    (lengths: int32 device tensor [B], clamped to [0, T] by the kernels).  Output rows from lengths[b] on are
+    left as they are (zeros when `out` is allocated here); S, z (fp32, in/out) end at each element's length."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name)
+    B, H, T = _attention_shape(q, k, v, params)
+    d, dv = params.d, params.d_v
+    _check_tensor(lengths, "lengths", dtypes=("int32",))
+    _check_shape(lengths, "lengths", (B,))
+    if out is None:
+        out = torch.zeros((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check_tensor(out, "out")
+    _check_shape(out, "out", (B, H, T, dv))
+    _check_same_dtype(q, ("out", out))
+    for name, t, shape in (("S", S, (B, H, 6 * d, dv)), ("z", z, (B, H, 6 * d))):
+        if t is not None:
+            _check_tensor(t, name, dtypes=("float32",))
+            _check_shape(t, name, shape)
+    p = params.struct()
+    need = int(lib().sanatan_prefill_workspace_bytes(B, H, T, chunk, ctypes.byref(p)))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().sanatan_prefill_chunked_ragged(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(chunk),
+                                                _ptr(lengths), int(pos0), ctypes.byref(p), _ptr(S), _ptr(z),
+                                                _ptr(out), _ptr(ws), ws.numel(), _stream()),
+           "sanatan_prefill_chunked_ragged")
     return out
 
 

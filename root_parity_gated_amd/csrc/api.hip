@@ -123,6 +123,25 @@ sanatan_status sanatan_prefill_chunked(const void* q, const void* k, const void*
                                              stream);
 }
 
+sanatan_status sanatan_prefill_chunked_ragged(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
+                                              int H, int T, int chunk, const int32_t* lengths, int64_t pos0,
+                                              const sanatan_params* params, float* S, float* z, void* out, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !lengths || !dtype_ok(t) || !sizes_ok(B, H, T) || chunk <= 0)
+    return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxPrefillT) return SANATAN_ERR_UNSUPPORTED;
+  if ((S == nullptr) != (z == nullptr)) return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (chunk % 16 != 0 || !prefill_chunk_supported(chunk, t)) return SANATAN_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!prefill_plan(B, H, T, chunk, 0, S != nullptr, &plan)) return SANATAN_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < plan.total_bytes) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_prefill(q, k, v, t, B, H, T, pos0, consts(params), S, z, out, ws, plan, stream,
+                                   reinterpret_cast<const int*>(lengths)));
+}
+
 sanatan_status sanatan_prefill_chunked_noalloc(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
                                                int H, int T, int chunk, int64_t pos0, const sanatan_params* params,
                                                float* S, float* z, void* out, hipStream_t stream) {

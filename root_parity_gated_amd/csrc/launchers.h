@@ -56,7 +56,7 @@ bool prefill_plan(int B, int H, int T, int chunk, int workgroups, bool with_stat
 bool prefill_chunk_supported(int chunk, sanatan_dtype t);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
                           int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,
-                          const PrefillPlan& plan, hipStream_t stream);
+                          const PrefillPlan& plan, hipStream_t stream, const int* lens = nullptr);
 
 // The no-allocation prefill's workspace: a fixed device array of the library (one per GPU)
 size_t noalloc_scratch_bytes();

@@ -51,7 +51,7 @@ struct Geom4 {
   }
 };
 
-template <typename T, int CH, bool STATE_ONLY>
+template <typename T, int CH, bool STATE_ONLY, bool RAGGED>
 __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args) {
   using G = Geom4<T, CH>;
   using Frag = typename FragT<T>::type;
@@ -71,15 +71,18 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
   float* Zw = Zb + w * 96;
   const int dbase = 16 * w + 4 * h;  // this lane's dims: dbase + {0..3, 8..11}
 
-  const long long hi = range_lo(g + 1, args);
-  for (long long c = range_lo(g, args); c < hi;) {
-    const int bh = (int)(c / args.ncs);
-    const long long seq_c0 = (long long)bh * args.ncs;
-    const long long seq_end = seq_c0 + args.ncs;
+  const long long total = call_chunks<RAGGED>(args);
+  const long long hi = range_lo(g + 1, total, args.G);
+  for (long long c = range_lo(g, total, args.G); c < hi;) {
+    const SeqSpan sp = seq_span<RAGGED>(c, args);
+    if (RAGGED && sp.bh < 0) break;
+    const int bh = sp.bh;
+    const long long seq_c0 = sp.c0;
+    const long long seq_end = sp.c1;
     const long long pend = hi < seq_end ? hi : seq_end;
     const bool last_piece = (pend == seq_end);
     const int t_begin = (int)(c - seq_c0) * CH;
-    const int t_end = min(Tn, (int)(pend - seq_c0) * CH);
+    const int t_end = min(sp.len, (int)(pend - seq_c0) * CH);
     c = pend;
     if (STATE_ONLY && last_piece) continue;
     const int hh = bh % args.H;
@@ -114,8 +117,9 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
         add_slot(slot, slot + kF * kDV);
       } else {
         if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
-        if (args.multi) {  // few pieces per sequence: add the earlier pieces' increments here
-          const int gf = range_of_chunk(seq_c0, args);
+        if (!RAGGED && args.multi) {  // few pieces per sequence: add the earlier pieces' increments here
+          // (a uniform plan has no empty ranges: every slot gf..g-1 was written by pass 1)
+          const int gf = range_of_chunk(seq_c0, total, args.G);
           for (int gg = gf; gg < g; gg++) {
             const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
             add_slot(sj, sj + kF * kDV);
@@ -342,19 +346,24 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs arg
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
   if (e >= kStateFloats || bh >= BH) return;
-  const long long c0 = (long long)bh * args.ncs, c1 = c0 + args.ncs - 1;
-  const int gf = range_of_chunk(c0, args);
-  const int gl = range_of_chunk(c1, args);
+  const SeqSpan sp = seq_span_of(bh, args);
+  if (sp.c1 == sp.c0) return;  // a ragged length of 0: no piece, the caller's state stays as it is
+  const long long total = args.lens ? call_chunks<true>(args) : call_chunks<false>(args);
+  const int gf = range_of_chunk(sp.c0, total, args.G);
+  const int gl = range_of_chunk(sp.c1 - 1, total, args.G);
   float run = 0.0f;
   if (args.S) run = (e < kF * kDV) ? args.S[(size_t)bh * kF * kDV + e] : args.z[(size_t)bh * kF + (e - kF * kDV)];
-  // U slots' increments are loaded at once, then replaced by their prefixes in order
+  // U slots' increments are loaded at once, then replaced by their prefixes in order.  A ragged call may
+  // have more ranges than chunks: an empty range between gf and gl holds no piece, so pass 1 never wrote
+  // its slot and it adds nothing (a uniform call's plan has no empty ranges).
   constexpr int U = 8;
   for (int g0 = gf; g0 <= gl; g0 += U) {
     float d[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int gg = g0 + u;
-      d[u] = (gg < gl) ? args.ws_state[(size_t)(bh + gg) * kStateFloats + e] : 0.0f;
+      const bool piece = gg < gl && range_lo(gg + 1, total, args.G) > range_lo(gg, total, args.G);
+      d[u] = piece ? args.ws_state[(size_t)(bh + gg) * kStateFloats + e] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -419,16 +428,16 @@ bool prefill_plan(int B, int H, int T, int chunk, int workgroups, bool with_stat
   return true;
 }
 
-template <typename T, int CH>
-static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t stream) {
+template <typename T, int CH, bool RAGGED>
+static hipError_t launch_prefill4_r(const PrefillArgs& a, int BH, hipStream_t stream) {
   using G = Geom4<T, CH>;
   static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
   if (a.multi) {
     const size_t lds1 = G::lds(true);
-    hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, true, RAGGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill4_kernel<T, CH, true>), dim3(a.G), dim3(256), lds1, stream, a);
+    hipLaunchKernelGGL((prefill4_kernel<T, CH, true, RAGGED>), dim3(a.G), dim3(256), lds1, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.scanned) {
@@ -438,11 +447,16 @@ static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t st
     }
   }
   const size_t lds3 = G::lds(false);
-  hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, false>,
+  hipError_t e = hipFuncSetAttribute((const void*)prefill4_kernel<T, CH, false, RAGGED>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill4_kernel<T, CH, false>), dim3(a.G), dim3(256), lds3, stream, a);
+  hipLaunchKernelGGL((prefill4_kernel<T, CH, false, RAGGED>), dim3(a.G), dim3(256), lds3, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, int CH>
+static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t stream) {
+  return a.lens ? launch_prefill4_r<T, CH, true>(a, BH, stream) : launch_prefill4_r<T, CH, false>(a, BH, stream);
 }
 
 hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream) {
@@ -452,7 +466,7 @@ hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream)
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
                           int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,
-                          const PrefillPlan& plan, hipStream_t stream) {
+                          const PrefillPlan& plan, hipStream_t stream, const int* lens) {
   float* rho = static_cast<float*>(ws);
   hipError_t e = launch_phase_table(rho, T, pos0, mc.log2_base, stream);
   if (e != hipSuccess) return e;
@@ -462,8 +476,15 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
   a.ws_state = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.rho_bytes);
   a.rho = rho;
   a.total = plan.total;
-  a.G = plan.G; a.ncs = plan.ncs; a.nph = mc.nph; a.H = H; a.T = T;
+  a.lens = lens;
+  a.G = plan.G; a.ncs = plan.ncs; a.nph = mc.nph; a.B = B; a.H = H; a.T = T; a.chunk = plan.chunk;
   a.multi = plan.multi; a.scanned = plan.scanned;
+  if (lens && plan.G > 1) {
+    // the pieces depend on lengths the host does not see: any sequence may span several, and a caller
+    // state must be read by the scan kernel before any final piece writes it back
+    a.multi = 1;
+    a.scanned = 1;
+  }
   a.kr = mc.kr; a.ceps = mc.ceps;
   const int BH = B * H;
   if (t == SANATAN_BF16) {

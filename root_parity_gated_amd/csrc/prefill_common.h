@@ -61,6 +61,8 @@ __device__ __forceinline__ void zero16(f32x16& a) {
 
 // Work partition (see prefill_plan): the flattened (sequence, chunk) list split into G ranges, one per
 // workgroup.  Piece (bh, g) owns boundary-state slot bh + g (disjoint and increasing in (bh, g)).
+// A ragged call (lens != null) gives batch element b the length lens[b] (clamped to [0, T]); its H
+// sequences then hold ceil(len / chunk) chunks each, in the same flattened order.
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -71,14 +73,83 @@ struct PrefillArgs {
   float* z;          // user state [BH][6d] or null
   float* ws_state;   // [BH + G - 1][kStateFloats]
   const float* rho;  // [T][64] position phases in revolutions
-  long long total;   // BH * ncs chunks
+  long long total;   // BH * ncs chunks (uniform calls)
   int G, ncs, nph, H, T;
   int multi;         // some sequence spans several pieces: pass 1 ran
   int scanned;       // the scan kernel ran: each slot holds its piece's prefix (else pass 3 sums slots)
   float kr, ceps;
+  const int* lens;   // [B] per-batch-element lengths (device), or null: every sequence has T tokens
+  int B, chunk;
 };
 
-__device__ __forceinline__ long long range_lo(long long g, const PrefillArgs& a) { return g * a.total / a.G; }
+__device__ __forceinline__ int ragged_len(const PrefillArgs& a, int b) {
+  const int L = a.lens[b];
+  return L < 0 ? 0 : (L > a.T ? a.T : L);
+}
+// Chunks of the whole call.  A ragged call's count is summed from the lengths by every workgroup (B scalar
+// loads), so that the partition needs no host copy of them.  RAGGED is a template flag of the kernels, so
+// that the uniform kernels carry none of this code.
+template <bool RAGGED>
+__device__ __forceinline__ long long call_chunks(const PrefillArgs& a) {
+  if (!RAGGED) return a.total;
+  long long n = 0;
+  for (int b = 0; b < a.B; b++) n += (long long)a.H * ((ragged_len(a, b) + a.chunk - 1) / a.chunk);
+  return n;
+}
+// The sequence holding flattened chunk c: its index bh, its chunks [c0, c1) and its length in tokens.
+// bh = -1 if no sequence holds c (cannot happen for c < call_chunks(a) with unchanged lengths).
+struct SeqSpan {
+  long long c0, c1;
+  int bh, len;
+};
+template <bool RAGGED>
+__device__ __forceinline__ SeqSpan seq_span(long long c, const PrefillArgs& a) {
+  SeqSpan s;
+  if (!RAGGED) {
+    s.bh = (int)(c / a.ncs);
+    s.c0 = (long long)s.bh * a.ncs;
+    s.c1 = s.c0 + a.ncs;
+    s.len = a.T;
+    return s;
+  }
+  long long acc = 0;
+  for (int b = 0; b < a.B; b++) {
+    const int L = ragged_len(a, b);
+    const long long n = (L + a.chunk - 1) / a.chunk;
+    if (c < acc + a.H * n) {
+      const int h = (int)((c - acc) / n);
+      s.bh = b * a.H + h;
+      s.c0 = acc + h * n;
+      s.c1 = s.c0 + n;
+      s.len = L;
+      return s;
+    }
+    acc += a.H * n;
+  }
+  s.bh = -1; s.c0 = s.c1 = c; s.len = 0;
+  return s;
+}
+// The chunks [c0, c1) of sequence bh (empty for a ragged length of 0).
+__device__ __forceinline__ SeqSpan seq_span_of(int bh, const PrefillArgs& a) {
+  SeqSpan s;
+  s.bh = bh;
+  if (!a.lens) {
+    s.c0 = (long long)bh * a.ncs;
+    s.c1 = s.c0 + a.ncs;
+    s.len = a.T;
+    return s;
+  }
+  const int bb = bh / a.H, h = bh % a.H;
+  long long acc = 0;
+  for (int b = 0; b < bb; b++) acc += (long long)a.H * ((ragged_len(a, b) + a.chunk - 1) / a.chunk);
+  s.len = ragged_len(a, bb);
+  const long long n = (s.len + a.chunk - 1) / a.chunk;
+  s.c0 = acc + h * n;
+  s.c1 = s.c0 + n;
+  return s;
+}
+
+__device__ __forceinline__ long long range_lo(long long g, long long total, int G) { return g * total / G; }
 // Range (logical workgroup) of this workgroup.  Workgroups are dealt round-robin to the 8 XCDs, each
 // with its own L2; consecutive ranges -- the pieces of one sequence -- are given to workgroups on the
 // same XCD, so that pass 3 reads its predecessors' boundary states from the L2 that pass 1 wrote
@@ -87,8 +158,9 @@ __device__ __forceinline__ int range_of_block(const PrefillArgs& a) {
   const int b = (int)blockIdx.x, per = a.G / 8;
   return b < 8 * per ? (b % 8) * per + b / 8 : b;
 }
-__device__ __forceinline__ int range_of_chunk(long long c, const PrefillArgs& a) {
-  return (int)(((c + 1) * a.G - 1) / a.total);
+// The range holding chunk c (ranges may be empty when G exceeds the chunk count; c's range is still unique)
+__device__ __forceinline__ int range_of_chunk(long long c, long long total, int G) {
+  return (int)(((c + 1) * G - 1) / total);
 }
 
 hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream);

@@ -134,7 +134,7 @@ __device__ __forceinline__ void feat8(const bf16x8& u, const float4& rh0, const 
   for (int c = 0; c < 5; c++) F[c] = __builtin_bit_cast(bf16x8, w[c]);
 }
 
-template <int CH, bool STATE_ONLY>
+template <int CH, bool STATE_ONLY, bool RAGGED>
 __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs args) {
   using G = GeomG<CH>;
   constexpr int TB = G::TB, CT = G::CT, KP = G::KP, VP = G::VP, RP = G::RP;
@@ -156,16 +156,19 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
     return STATE_ONLY ? Vbase + grp * CT * VP : Vbase + (j & 1) * CT * VP;
   };
 
+  const long long total = call_chunks<RAGGED>(args);
   const int g = range_of_block(args);
-  const long long hi_c = range_lo(g + 1, args);
-  for (long long c = range_lo(g, args); c < hi_c;) {
-    const int bh = (int)(c / args.ncs);
-    const long long seq_c0 = (long long)bh * args.ncs;
-    const long long seq_end = seq_c0 + args.ncs;
+  const long long hi_c = range_lo(g + 1, total, args.G);
+  for (long long c = range_lo(g, total, args.G); c < hi_c;) {
+    const SeqSpan sp = seq_span<RAGGED>(c, args);
+    if (RAGGED && sp.bh < 0) break;
+    const int bh = sp.bh;
+    const long long seq_c0 = sp.c0;
+    const long long seq_end = sp.c1;
     const long long pend = hi_c < seq_end ? hi_c : seq_end;
     const bool last_piece = (pend == seq_end);
     const int t_begin = (int)(c - seq_c0) * CH;
-    const int t_end = min(args.T, (int)(pend - seq_c0) * CH);
+    const int t_end = min(sp.len, (int)(pend - seq_c0) * CH);
     c = pend;
     if (STATE_ONLY && last_piece) continue;
     const int hh = bh % args.H;
@@ -192,8 +195,8 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
         add_slot(slot, slot + kF * kDV);
       } else {
         if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
-        if (args.multi) {
-          const int gf = range_of_chunk(seq_c0, args);
+        if (!RAGGED && args.multi) {  // (a uniform plan has no empty ranges: every slot gf..g-1 was written)
+          const int gf = range_of_chunk(seq_c0, total, args.G);
           for (int gg = gf; gg < g; gg++) {
             const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
             add_slot(sj, sj + kF * kDV);
@@ -612,7 +615,7 @@ struct GeomS8 {
 
 // PCH is the chunk of the call (64 or 128), which fixes the pieces; the increment over a piece does
 // not depend on the chunking, so the loop always steps 64 tokens.
-template <int PCH>
+template <int PCH, bool RAGGED>
 __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArgs args) {
   constexpr int CH = 64, KP = GeomS8::KP, VP = GeomS8::VP;
   static_assert(PCH % CH == 0, "pieces are whole 64-token steps");
@@ -625,16 +628,19 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
   const int toff = 32 * half;  // this wave's token offset inside a chunk
   const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
 
+  const long long total = call_chunks<RAGGED>(args);
   const int g = range_of_block(args);
-  const long long hi_c = range_lo(g + 1, args);
-  for (long long c = range_lo(g, args); c < hi_c;) {
-    const int bh = (int)(c / args.ncs);
-    const long long seq_c0 = (long long)bh * args.ncs;
-    const long long seq_end = seq_c0 + args.ncs;
+  const long long hi_c = range_lo(g + 1, total, args.G);
+  for (long long c = range_lo(g, total, args.G); c < hi_c;) {
+    const SeqSpan sp = seq_span<RAGGED>(c, args);
+    if (RAGGED && sp.bh < 0) break;
+    const int bh = sp.bh;
+    const long long seq_c0 = sp.c0;
+    const long long seq_end = sp.c1;
     const long long pend = hi_c < seq_end ? hi_c : seq_end;
     const bool last_piece = (pend == seq_end);
     const int t_begin = (int)(c - seq_c0) * PCH;
-    const int t_end = min(args.T, (int)(pend - seq_c0) * PCH);
+    const int t_end = min(sp.len, (int)(pend - seq_c0) * PCH);
     c = pend;
     if (last_piece) continue;  // the final piece's state comes out of pass 3
     const int hh = bh % args.H;
@@ -867,6 +873,7 @@ struct RawKQ {
   float4 r0, r1;
 };
 
+template <bool RAGGED>
 __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArgs args) {
   using G = Geom128;
   constexpr int CH = G::CH, TB = G::TB, KP = G::KP, VP = G::VP, RP = G::RP;
@@ -882,16 +889,19 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
   const u32x4 ones4 = {kOnes2, kOnes2, kOnes2, kOnes2};
   const bf16x8 ONES = __builtin_bit_cast(bf16x8, ones4);
 
+  const long long total = call_chunks<RAGGED>(args);
   const int g = range_of_block(args);
-  const long long hi_c = range_lo(g + 1, args);
-  for (long long c = range_lo(g, args); c < hi_c;) {
-    const int bh = (int)(c / args.ncs);
-    const long long seq_c0 = (long long)bh * args.ncs;
-    const long long seq_end = seq_c0 + args.ncs;
+  const long long hi_c = range_lo(g + 1, total, args.G);
+  for (long long c = range_lo(g, total, args.G); c < hi_c;) {
+    const SeqSpan sp = seq_span<RAGGED>(c, args);
+    if (RAGGED && sp.bh < 0) break;
+    const int bh = sp.bh;
+    const long long seq_c0 = sp.c0;
+    const long long seq_end = sp.c1;
     const long long pend = hi_c < seq_end ? hi_c : seq_end;
     const bool last_piece = (pend == seq_end);
     const int t_begin = (int)(c - seq_c0) * CH;
-    const int t_end = min(args.T, (int)(pend - seq_c0) * CH);
+    const int t_end = min(sp.len, (int)(pend - seq_c0) * CH);
     c = pend;
     const int hh = bh % args.H;
     const __bf16* __restrict__ kp = static_cast<const __bf16*>(args.k) + (size_t)bh * args.T * kD;
@@ -915,8 +925,8 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
       gstate_add(Sacc, Zg, slot, slot + kF * kDV, grp, l);
     } else {
       if (args.S) gstate_add(Sacc, Zg, args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF, grp, l);
-      if (args.multi) {
-        const int gf = range_of_chunk(seq_c0, args);
+      if (!RAGGED && args.multi) {  // (a uniform plan has no empty ranges: every slot gf..g-1 was written)
+        const int gf = range_of_chunk(seq_c0, total, args.G);
         for (int gg = gf; gg < g; gg++) {
           const float* sj = args.ws_state + (size_t)(bh + gg) * kStateFloats;
           gstate_add(Sacc, Zg, sj, sj + kF * kDV, grp, l);
@@ -1111,22 +1121,23 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
   }
 }
 
+template <bool RAGGED>
 hipError_t launch_prefill_grp128(const PrefillArgs& a, hipStream_t stream) {
   static_assert(Geom128::lds <= 160 * 1024, "LDS budget");
   static std::atomic<bool> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)prefill_grp128_kernel,
+    const hipError_t e = hipFuncSetAttribute((const void*)prefill_grp128_kernel<RAGGED>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, Geom128::lds);
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(prefill_grp128_kernel, dim3(a.G), dim3(256), Geom128::lds, stream, a);
+  hipLaunchKernelGGL(prefill_grp128_kernel<RAGGED>, dim3(a.G), dim3(256), Geom128::lds, stream, a);
   return hipGetLastError();
 }
 
-template <int CH>
+template <int CH, bool RAGGED>
 hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   using G = GeomG<CH>;
   static_assert(G::lds(false) <= 160 * 1024, "LDS budget");
@@ -1134,24 +1145,24 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, true, RAGGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::lds(true));
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            G::lds(false));
+    e = hipFuncSetAttribute((const void*)prefill_grp_kernel<CH, false, RAGGED>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, G::lds(false));
     if (e != hipSuccess) return e;
     if constexpr (CH == 64) {
-      e = hipFuncSetAttribute((const void*)prefill_state8_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              GeomS8::lds);
+      e = hipFuncSetAttribute((const void*)prefill_state8_kernel<64, RAGGED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, GeomS8::lds);
       if (e != hipSuccess) return e;
     }
     attr_set[dev].store(true, std::memory_order_release);
   }
   if (a.multi) {
     if constexpr (CH == 64)
-      hipLaunchKernelGGL(prefill_state8_kernel<64>, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
+      hipLaunchKernelGGL((prefill_state8_kernel<64, RAGGED>), dim3(a.G), dim3(512), GeomS8::lds, stream, a);
     else
-      hipLaunchKernelGGL((prefill_grp_kernel<CH, true>), dim3(a.G), dim3(256), G::lds(true), stream, a);
+      hipLaunchKernelGGL((prefill_grp_kernel<CH, true, RAGGED>), dim3(a.G), dim3(256), G::lds(true), stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.scanned) {
@@ -1159,45 +1170,51 @@ hipError_t launch_grp_t(const PrefillArgs& a, int BH, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL((prefill_grp_kernel<CH, false>), dim3(a.G), dim3(256), G::lds(false), stream, a);
+  hipLaunchKernelGGL((prefill_grp_kernel<CH, false, RAGGED>), dim3(a.G), dim3(256), G::lds(false), stream, a);
   return hipGetLastError();
 }
 
 // pass 1 for 128-token chunks: the 8-wave state kernel walks each chunk as two 64-token halves
+template <bool RAGGED>
 hipError_t launch_prefill_state8_128(const PrefillArgs& a, hipStream_t stream) {
   static std::atomic<bool> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute((const void*)prefill_state8_kernel<128>,
+    const hipError_t e = hipFuncSetAttribute((const void*)prefill_state8_kernel<128, RAGGED>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, GeomS8::lds);
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(prefill_state8_kernel<128>, dim3(a.G), dim3(512), GeomS8::lds, stream, a);
+  hipLaunchKernelGGL((prefill_state8_kernel<128, RAGGED>), dim3(a.G), dim3(512), GeomS8::lds, stream, a);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream) {
+template <bool RAGGED>
+hipError_t launch_prefill_grp_r(const PrefillArgs& a, int chunk, int BH, hipStream_t stream) {
   switch (chunk) {
-    case 16: return launch_grp_t<16>(a, BH, stream);
-    case 32: return launch_grp_t<32>(a, BH, stream);
-    case 64: return launch_grp_t<64>(a, BH, stream);
+    case 16: return launch_grp_t<16, RAGGED>(a, BH, stream);
+    case 32: return launch_grp_t<32, RAGGED>(a, BH, stream);
+    case 64: return launch_grp_t<64, RAGGED>(a, BH, stream);
     case 128: {
       if (a.multi) {
-        hipError_t e = launch_prefill_state8_128(a, stream);
+        hipError_t e = launch_prefill_state8_128<RAGGED>(a, stream);
         if (e != hipSuccess) return e;
         if (a.scanned) {
           e = launch_prefill_scan(a, BH, stream);
           if (e != hipSuccess) return e;
         }
       }
-      return launch_prefill_grp128(a, stream);
+      return launch_prefill_grp128<RAGGED>(a, stream);
     }
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_grp(const PrefillArgs& a, int chunk, int BH, hipStream_t stream) {
+  return a.lens ? launch_prefill_grp_r<true>(a, chunk, BH, stream) : launch_prefill_grp_r<false>(a, chunk, BH, stream);
 }
 
 }  // namespace sanatan

@@ -82,6 +82,24 @@ def test_prefill_validation(L):
     assert _prefill(L, p, ws_bytes=16) == rpg.SANATAN_ERR_WORKSPACE
 
 
+def test_ragged_prefill_validation(L):
+    p = params()
+
+    def rg(q=FAKE, lengths=FAKE, T=128, chunk=64, S=None, z=None, ws=FAKE, ws_bytes=1 << 40, pos0=0):
+        return L.sanatan_prefill_chunked_ragged(q, FAKE, FAKE, rpg.SANATAN_BF16, 2, 1, T, chunk, lengths, pos0,
+                                                ctypes.byref(p), S, z, FAKE, ws, ws_bytes, None)
+
+    assert rg(lengths=None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert rg(q=None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert rg(T=0) == rpg.SANATAN_ERR_INVALID_ARG
+    assert rg(S=FAKE) == rpg.SANATAN_ERR_INVALID_ARG
+    assert rg(pos0=(1 << 53) - 10) == rpg.SANATAN_ERR_INVALID_ARG
+    assert rg(chunk=48) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert rg(T=(1 << 22) + 1) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert rg(ws=None) == rpg.SANATAN_ERR_WORKSPACE
+    assert rg(ws_bytes=16) == rpg.SANATAN_ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("bad", [dict(omega=0), dict(n_param_heads=0), dict(gamma=-1.0), dict(gamma=float("nan")),
                                  dict(c=0.0), dict(c=float("inf")), dict(eps=-1e-3), dict(lambda_base=0.0),
                                  dict(d=0)])
