@@ -11,6 +11,14 @@ if HERE not in sys.path:
 
 
 def pytest_configure(config):
+    # SANATAN_TEST_LIB: run the tests against another build of the library (the host-ASan build of
+    # test_abi_asan.py); the package itself always loads its in-tree libsanatan.so
+    alt = os.environ.get("SANATAN_TEST_LIB")
+    if alt:
+        import root_parity_gated_amd as rpg
+
+        rpg.LIB_PATH = alt
+
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; parity tests against the CPU oracle")
 
 
