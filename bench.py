@@ -455,6 +455,45 @@ def bench_feature_map(torch, rpg, si, w, nh, steps, warmup):
     return eager, graph
 
 
+def bench_ragged(torch, rpg, si, w, steps, warmup):
+    """The headline shape as a batch of prompts of seeded lengths in [T/8, T]: one ragged prefill call, and
+    for comparison one uniform call per prompt (what a caller without per-element lengths would run).
+    Returns (lengths, (eager, graph) of the ragged call, (eager, graph) of the per-prompt calls)."""
+    import numpy as np
+
+    q, k, v, om = si.workload_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(dt) for x in (q, k, v))
+    del q, k, v
+    p = rpg.Params(omega=torch.from_numpy(om).cuda(), gamma=w.gamma, eps=w.eps, lambda_base=w.lambda_base)
+    lens = np.random.default_rng(w.seed + 99).integers(w.T // 8, w.T + 1, w.B).astype(np.int32)
+    lens_d = torch.from_numpy(lens).cuda()
+    out = torch.zeros_like(vd)
+    ws = torch.empty((rpg.sanatan_prefill_workspace_bytes(w.B, w.H, w.T, w.chunk, p),), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: rpg.sanatan_prefill_chunked_ragged(qd, kd, vd, lens_d, w.chunk, p, out=out, ws=ws)
+    eager = timed_loop(torch, fn, steps, warmup)
+    g = graph_of(torch, fn)
+    graph = timed_loop(torch, g.replay, steps, warmup) if g is not None else None
+    # one uniform call per prompt, on contiguous copies of its rows
+    per = []
+    for b, L in enumerate(lens):
+        xs = [x[b:b + 1, :, :L].contiguous() for x in (qd, kd, vd)]
+        o = torch.empty_like(xs[2])
+        wsb = torch.empty((rpg.sanatan_prefill_workspace_bytes(1, w.H, int(L), w.chunk, p),), dtype=torch.uint8,
+                          device="cuda")
+        per.append((xs, o, wsb))
+
+    def fn_per():
+        for xs, o, wsb in per:
+            rpg.sanatan_prefill_chunked(xs[0], xs[1], xs[2], w.chunk, p, out=o, ws=wsb)
+
+    eager_p = timed_loop(torch, fn_per, steps, warmup)
+    gp = graph_of(torch, fn_per)
+    graph_p = timed_loop(torch, gp.replay, steps, warmup) if gp is not None else None
+    return lens, (eager, graph), (eager_p, graph_p)
+
+
 def chunked_flops(B, H, T, C, F_, DV_=DV):
     """Causal FLOPs of a chunked p = 1 prefill with F_ features per head (causal pairs inside chunks, readout
     and update per token)."""
@@ -471,7 +510,7 @@ def mfma_line(fl, ms):
 
 
 ONLY = ("prefill", "decode1", "decode64", "long", "quad", "quad4", "backward_p2", "backward_p1", "featurize",
-        "harmonics", "four_channel")
+        "harmonics", "four_channel", "ragged")
 
 
 def main():
@@ -533,6 +572,9 @@ def main():
             rec["ms"] = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2)
         elif args.only == "featurize":
             rec["ms"] = bench_featurize(torch, rpg, si, w, small, 3)[:2]
+        elif args.only == "ragged":
+            lens, r, pp = bench_ragged(torch, rpg, si, w, small, 3)
+            rec.update({"lengths": lens.tolist(), "ms": r, "ms_per_prompt_calls": pp})
         elif args.only in ("harmonics", "four_channel"):
             rec["ms"] = bench_feature_map(torch, rpg, si, w, 2 if args.only == "harmonics" else 0, small, 3)
         print(json.dumps(rec))
@@ -567,7 +609,7 @@ def main():
         "data": "synthetic: q,k,v ~ N(0,1) rounded to bf16, omega ~ U(-pi,pi), seeded (sanatan_inputs)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": D, "d_v": DV, "chunk": w.chunk,
                    "p": 1, "gamma": w.gamma, "lambda_base": w.lambda_base},
-        # At about 249 flop per algorithmic byte the workload sits below the bf16 ridge (~315 flop/byte): the HBM
+        # At about 249 flop per algorithmic byte the workload sits below the bf16 ridge (~312 flop/byte): the HBM
         # roof (12.6 us) binds before the MFMA roof (10.0 us), so the line is priced against HBM, with the MFMA
         # fraction beside it.
         "roofline": {
@@ -650,6 +692,20 @@ def main():
                                "roofline": {"bound": "hbm", "achieved": fbytes / (fms * 1e-3) / 1e9,
                                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                             "frac": fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+        log(f"ragged prefill {w.name}")
+        lens, (re_, rg_), (pe_, pg_) = bench_ragged(torch, rpg, si, w, small, 3)
+        rms = min(re_, rg_) if rg_ is not None else re_
+        pms = min(pe_, pg_) if pg_ is not None else pe_
+        rtok = int(lens.sum())
+        rbytes = prefill_bytes(1, w.H, rtok)
+        extras["ragged_prefill"] = {
+            "workload": f"{w.name}_ragged", "lengths": lens.tolist(), "tokens_per_s": rtok / (rms * 1e-3),
+            "ms": rms, "ms_eager": re_, "ms_graph": rg_,
+            "ms_one_call_per_prompt": pms, "ms_one_call_per_prompt_eager": pe_, "ms_one_call_per_prompt_graph": pg_,
+            "roofline": {"bound": "hbm", "achieved": rbytes / (rms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": rbytes / (rms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "note": "one sanatan_prefill_chunked_ragged call over prompts of seeded lengths in [T/8, T]; "
+                    "algorithmic bytes: q, k, v read and out written for the valid rows only"}
         if not args.no_cpu_baseline:
             log("cpu oracle beside the other workloads")
             for key, rec in cpu_oracle_extras(si).items():

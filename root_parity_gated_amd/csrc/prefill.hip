@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
         for (int m = l; m < 96; m += 64) Zw[m] += stage[kStageS + w * 96 + m];
       };
       if (args.multi && args.scanned) {
-        add_slot(slot, slot + kF * kDV);
+        // (a ragged call's scan leaves the head piece's slot unwritten when there is no caller state)
+        if (!RAGGED || args.S || g != range_of_chunk(seq_c0, total, args.G)) add_slot(slot, slot + kF * kDV);
       } else {
         if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
         if (!RAGGED && args.multi) {  // few pieces per sequence: add the earlier pieces' increments here
@@ -341,39 +342,62 @@ __global__ __launch_bounds__(256, 1) void prefill4_kernel(const PrefillArgs args
 }
 
 // Exclusive prefix over the pieces of each sequence, in place: slot(bh, g) <- S0 + increments of the
-// earlier pieces of sequence bh.  One thread per (sequence, state element).
+// earlier pieces of sequence bh.  Block (x, bh) covers every gridDim.x-th group of 256 state elements of
+// sequence bh (gridDim.x = scan_slices()); the sequence's piece range is worked out once per block, not once
+// per element (its 64-bit divisions would otherwise dominate the kernel).
+constexpr int kScanMaxFlags = 4096;  // ragged calls: ranges of one sequence whose emptiness is looked up in LDS
 __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs args, int BH) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
-  if (e >= kStateFloats || bh >= BH) return;
+  if (bh >= BH) return;
   const SeqSpan sp = seq_span_of(bh, args);
   if (sp.c1 == sp.c0) return;  // a ragged length of 0: no piece, the caller's state stays as it is
   const long long total = args.lens ? call_chunks<true>(args) : call_chunks<false>(args);
   const int gf = range_of_chunk(sp.c0, total, args.G);
   const int gl = range_of_chunk(sp.c1 - 1, total, args.G);
-  float run = 0.0f;
-  if (args.S) run = (e < kF * kDV) ? args.S[(size_t)bh * kF * kDV + e] : args.z[(size_t)bh * kF + (e - kF * kDV)];
-  // U slots' increments are loaded at once, then replaced by their prefixes in order.  A ragged call may
-  // have more ranges than chunks: an empty range between gf and gl holds no piece, so pass 1 never wrote
-  // its slot and it adds nothing (a uniform call's plan has no empty ranges).
-  constexpr int U = 8;
-  for (int g0 = gf; g0 <= gl; g0 += U) {
-    float d[U];
+  // A ragged call may have more ranges than chunks: an empty range between gf and gl holds no piece, so pass 1
+  // never wrote its slot and it adds nothing.  A uniform call's plan has no empty ranges.
+  __shared__ unsigned char piece[kScanMaxFlags];
+  const bool ragged = args.lens != nullptr;
+  if (ragged) {
+    for (int i = threadIdx.x; i <= gl - gf && i < kScanMaxFlags; i += 256)
+      piece[i] = range_lo(gf + i + 1, total, args.G) > range_lo(gf + i, total, args.G);
+    __syncthreads();
+  }
+  auto has_piece = [&](int gg) {
+    if (!ragged) return true;
+    const int i = gg - gf;
+    return i < kScanMaxFlags ? piece[i] != 0 : range_lo(gg + 1, total, args.G) > range_lo(gg, total, args.G);
+  };
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < kStateFloats; e += gridDim.x * 256) {
+    float run = 0.0f;
+    if (args.S) run = (e < kF * kDV) ? args.S[(size_t)bh * kF * kDV + e] : args.z[(size_t)bh * kF + (e - kF * kDV)];
+    // U slots' increments are loaded at once, then replaced by their prefixes in order
+    constexpr int U = 8;
+    for (int g0 = gf; g0 <= gl; g0 += U) {
+      float d[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int gg = g0 + u;
-      const bool piece = gg < gl && range_lo(gg + 1, total, args.G) > range_lo(gg, total, args.G);
-      d[u] = piece ? args.ws_state[(size_t)(bh + gg) * kStateFloats + e] : 0.0f;
-    }
+      for (int u = 0; u < U; u++) {
+        const int gg = g0 + u;
+        d[u] = (gg < gl && has_piece(gg)) ? args.ws_state[(size_t)(bh + gg) * kStateFloats + e] : 0.0f;
+      }
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int gg = g0 + u;
-      if (gg <= gl) {
-        args.ws_state[(size_t)(bh + gg) * kStateFloats + e] = run;
-        run += d[u];
+      for (int u = 0; u < U; u++) {
+        const int gg = g0 + u;
+        if (gg <= gl) {
+          // a ragged call's pass 3 starts a head piece without a caller state from zero, not from its slot
+          if (!ragged || args.S || gg != gf) args.ws_state[(size_t)(bh + gg) * kStateFloats + e] = run;
+          run += d[u];
+        }
       }
     }
   }
+}
+
+// Blocks per sequence of the scan: about four per workgroup of the call in all, 8 to one per 256 elements.
+static int scan_slices(const PrefillArgs& a, int BH) {
+  const int want = (4 * a.G + BH - 1) / BH;
+  const int most = (kStateFloats + 255) / 256;
+  return want < 8 ? 8 : (want > most ? most : want);
 }
 
 // ------------------------------------------------------------------------------- host side
@@ -441,7 +465,7 @@ static hipError_t launch_prefill4_r(const PrefillArgs& a, int BH, hipStream_t st
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.scanned) {
-      hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);
+      hipLaunchKernelGGL(prefill_scan_kernel, dim3(scan_slices(a, BH), BH), dim3(256), 0, stream, a, BH);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -460,7 +484,7 @@ static hipError_t launch_prefill4_t(const PrefillArgs& a, int BH, hipStream_t st
 }
 
 hipError_t launch_prefill_scan(const PrefillArgs& a, int BH, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3((kStateFloats + 255) / 256, BH), dim3(256), 0, stream, a, BH);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(scan_slices(a, BH), BH), dim3(256), 0, stream, a, BH);
   return hipGetLastError();
 }
 

@@ -192,7 +192,8 @@ __global__ __launch_bounds__(256, 1) void prefill_grp_kernel(const PrefillArgs a
     if (!STATE_ONLY) {
       auto add_slot = [&](const float* s, const float* zz) { gstate_add(Sacc, Zg, s, zz, grp, l); };
       if (args.multi && args.scanned) {
-        add_slot(slot, slot + kF * kDV);
+        // (a ragged call's scan leaves the head piece's slot unwritten when there is no caller state)
+        if (!RAGGED || args.S || g != range_of_chunk(seq_c0, total, args.G)) add_slot(slot, slot + kF * kDV);
       } else {
         if (args.S) add_slot(args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF);
         if (!RAGGED && args.multi) {  // (a uniform plan has no empty ranges: every slot gf..g-1 was written)
@@ -693,19 +694,11 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
     // the wave's rows of V and Phi(K) into its tiles; rows past the chunk's end are zero
     // (a full half, the common case, takes the unmasked branch; nvh is the same on every lane)
     auto write_v = [&](const uint4 (&r)[NV], int nvh) {
-      if (nvh >= 32) {
 #pragma unroll
-        for (int j = 0; j < NV; j++) {
-          const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
-          *reinterpret_cast<uint4*>(Vs + row * VP + col) = r[j];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NV; j++) {
-          const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
-          const unsigned m = 0u - (unsigned)(row < nvh);
-          *reinterpret_cast<uint4*>(Vs + row * VP + col) = make_uint4(r[j].x & m, r[j].y & m, r[j].z & m, r[j].w & m);
-        }
+      for (int j = 0; j < NV; j++) {
+        const int e = l + 64 * j, row = e >> 3, col = 8 * (e & 7);
+        const unsigned m = 0u - (unsigned)(row < nvh);
+        *reinterpret_cast<uint4*>(Vs + row * VP + col) = make_uint4(r[j].x & m, r[j].y & m, r[j].z & m, r[j].w & m);
       }
     };
     auto write_k = [&](const bf16x8 (&F)[5], int nvh) {
@@ -734,28 +727,35 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
       for (int cc = 0; cc < 5; cc++) F[cc] = __builtin_bit_cast(bf16x8, wv[cc]);
     };
 
-    // prologue: chunk 0 in the tiles, chunk 1 featurized (KF) with its V (rv) in registers, raw keys of
-    // chunk 2 (uk, rh) and V of chunk 2 (rvn) in flight
-    bf16x8 KF[5], uk;
+    // prologue: chunk 0 in the tiles; V rows and raw keys of chunk 1 in flight (set A)
+    bf16x8 uk;
     float4 rh[2];
     uint4 rv[NV];
-    const int t1 = next_t(t_begin);
     {
       load_v(t_begin, rv);
       load_k(t_begin, uk, rh);
+      bf16x8 F[5];
       float cr[8], sr[8], rr[8];
-      feat8(uk, rh[0], rh[1], om4, args.kr, KF, cr, sr, rr);
+      feat8(uk, rh[0], rh[1], om4, args.kr, F, cr, sr, rr);
       const int nvh = half_valid(t_begin);
-      write_k(KF, nvh);
+      write_k(F, nvh);
       write_v(rv, nvh);
+      // V before keys, as in the loop, so that the loop's first wait for V does not also wait for the keys
+      const int t1 = next_t(t_begin);
       load_v(t1, rv);
+      __builtin_amdgcn_sched_barrier(0);
       load_k(t1, uk, rh);
-      feat8(uk, rh[0], rh[1], om4, args.kr, KF, cr, sr, rr);
-      load_k(next_t(t1), uk, rh);
     }
 
+    // The loop over chunks j: rv and (uk, rh) hold chunk j + 1's V rows and raw keys, loaded during chunk
+    // j - 1.  After the MFMA operands of chunk j are read out of the tiles, chunk j + 1's V rows overwrite the
+    // V tile and its keys, featurized between the update MFMAs, overwrite the Phi(K) tile (LDS serves the
+    // wave in order, so the reads see chunk j).  Each register set is reloaded with chunk j + 2 as soon as it
+    // has been consumed, so no copy closes the loop (a copy would wait for loads issued in the same chunk),
+    // and the V rows are waited for only in the next chunk's step 2, the keys in its step 4.
     for (int t0 = t_begin; t0 < t_end; t0 += CH) {
-      const int ta = next_t(t0), tb = next_t(ta), tc = next_t(tb);  // chunks j + 1, j + 2, j + 3
+      const int ta = next_t(t0), tb = next_t(ta);  // chunks j + 1, j + 2
+      const int nvh1 = ta != t0 ? half_valid(ta) : 0;  // past the piece's end the tiles get zero rows
       // 1. every MFMA operand of chunk j out of the tiles
       bf16x8 Af[2][3], Bf[2][2];
 #pragma unroll
@@ -765,20 +765,10 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
 #pragma unroll
         for (int ft = 0; ft < 3; ft++) Af[ks][ft] = lds_tokfrag_swz(KS, KP, 16 * ks, 32 * ft, l);
       }
-      // 2. chunk j + 1 into the tiles (LDS serves the wave in order: the reads above see chunk j); past
-      //    the piece's end this rewrites chunk j, which nobody reads any more
-      {
-        const int nvh1 = ta != t0 ? half_valid(ta) : 0;
-        write_k(KF, nvh1);
-        write_v(rv, nvh1);
-      }
-      // 3. raw inputs further ahead: V of chunk j + 2, keys of chunk j + 3
-      uint4 rvn[NV];
-      load_v(tb, rvn);
-      bf16x8 uk2;
-      float4 rhn[2];
-      load_k(tc, uk2, rhn);
-      // 4. the update MFMAs of chunk j with the keys of chunk j + 2 featurized in between
+      // 2. chunk j + 1's V rows into the V tile, 3. and chunk j + 2's into their registers
+      write_v(rv, nvh1);
+      load_v(tb, rv);
+      // 4. the update MFMAs of chunk j with the keys of chunk j + 1 featurized in between, then into the tile
       float cr[8], sr[8], rr[8];
       float zs[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -796,14 +786,14 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      pack(cr, sr, rr, KF);
+      bf16x8 F[5];
+      pack(cr, sr, rr, F);
+      write_k(F, nvh1);
 #pragma unroll
       for (int ft = 0; ft < 3; ft++) zacc[ft] += xor32_sum(zs[ft]);
-#pragma unroll
-      for (int j = 0; j < NV; j++) rv[j] = rvn[j];
-      uk = uk2;
-      rh[0] = rhn[0];
-      rh[1] = rhn[1];
+      // 5. chunk j + 2's keys into the registers just read
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(tb, uk, rh);
     }
 
     // the two halves of each group meet: the second-half waves hand their slices over through LDS, the
@@ -922,7 +912,9 @@ __global__ __launch_bounds__(256, 1) void prefill_grp128_kernel(const PrefillArg
       for (int vt = 0; vt < 2; vt++) zero16(Sacc[ft][vt]);
     for (int m = l; m < 96; m += 64) Zg[m] = 0.0f;
     if (args.multi && args.scanned) {
-      gstate_add(Sacc, Zg, slot, slot + kF * kDV, grp, l);
+      // (a ragged call's scan leaves the head piece's slot unwritten when there is no caller state)
+      if (!RAGGED || args.S || g != range_of_chunk(seq_c0, total, args.G))
+        gstate_add(Sacc, Zg, slot, slot + kF * kDV, grp, l);
     } else {
       if (args.S) gstate_add(Sacc, Zg, args.S + (size_t)bh * kF * kDV, args.z + (size_t)bh * kF, grp, l);
       if (!RAGGED && args.multi) {  // (a uniform plan has no empty ranges: every slot gf..g-1 was written)
