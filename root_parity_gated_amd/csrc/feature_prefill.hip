@@ -17,7 +17,12 @@
 // those features, the partial numerator V^T P + S^T Phi(Q)^T and denominator, and after the four partials
 // meet in LDS (fixed order) the chunk's outputs are normalised; then S += Phi(K)^T V and z += Phi(K)^T 1.
 // Operands: bf16 32x32x16 MFMA (fp32 32x32x2 for fp32 inputs), fp32 accumulation; S is rounded to the
-// operand type only as the readout's operand.  No sequence split: each sequence is one workgroup.
+// operand type only as the readout's operand.
+// Sequence split: with fewer sequences than compute units, each sequence is cut into P pieces of whole chunks,
+// one workgroup each.  Pass 1 (STATE_ONLY) runs pieces 0..P-2 and writes each piece's state increment to its
+// slot (piece 0's includes the caller's start state, which it also copies to the spare slot P - 1); pass 3 then
+// starts piece p from the sum of slots 0..p-1 (piece 0 from slot P - 1), so that no piece of pass 3 reads the
+// caller's state while the final piece writes it back.
 #include <atomic>
 
 #include "prefill_common.h"
@@ -118,11 +123,11 @@ __device__ __forceinline__ typename FragT<T>::type slot_frag(const T* row, int b
   return f;
 }
 
-template <typename T, int NFT>
+template <typename T, int NFT, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                               const T* __restrict__ v, T* __restrict__ out,
                                                               float* __restrict__ S, float* __restrict__ z, int Tn,
-                                                              int Freal, float ceps) {
+                                                              int Freal, float ceps, int P, float* __restrict__ slots) {
   using G = FGeom<T, NFT>;
   typedef typename FragT<T>::type Frag;
   static_assert(NFT % 4 == 0, "feature tiles are dealt to four waves");
@@ -133,7 +138,13 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
   float* red = reinterpret_cast<float*>(smem + G::k_bytes + G::v_bytes);
   float* zs = reinterpret_cast<float*>(smem + G::k_bytes + G::v_bytes + G::red_bytes);
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / P, p = blockIdx.x % P;
+  if (STATE_ONLY && p == P - 1) return;  // the final piece's state comes out of pass 3
+  const int nch = (Tn + kFC - 1) / kFC;
+  const int t_lo = (int)((long long)p * nch / P) * kFC;
+  const int t_hi = min(Tn, (int)((long long)(p + 1) * nch / P) * kFC);
+  constexpr size_t SLOT = (size_t)Fp * (kDV + 1);  // S [Fp][d_v], then z [Fp]
+  auto slot = [&](int q) { return slots + ((size_t)bh * P + q) * SLOT; };
   const T* qp = phiq + (size_t)bh * Tn * Fp;
   const T* kp = phik + (size_t)bh * Tn * Fp;
   const T* vp = v + (size_t)bh * Tn * kDV;
@@ -147,17 +158,39 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
 #pragma unroll
   for (int i = 0; i < NW; i++)
 #pragma unroll
-    for (int vt = 0; vt < 2; vt++) {
+    for (int vt = 0; vt < 2; vt++) zero16(Sacc[i][vt]);
+  for (int f = tid; f < Fp; f += 256) zs[f] = 0.0f;
+  // add a state of `rows` rows ([rows][d_v] then [rows]) to the wave's tiles and to zs (each zs entry is
+  // touched by the same thread here as in the zeroing above)
+  auto add_state = [&](const float* s_, const float* z_, int rows) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
-        Sacc[i][vt][r] = (Sp && f < Freal) ? Sp[(size_t)f * kDV + 32 * vt + n32] : 0.0f;
-      }
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (f < rows) Sacc[i][vt][r] += s_[(size_t)f * kDV + 32 * vt + n32];
+        }
+    for (int f = tid; f < rows; f += 256) zs[f] += z_[f];
+  };
+  if (P == 1) {
+    if (Sp) add_state(Sp, zp, Freal);
+  } else if (STATE_ONLY) {
+    if (p == 0 && Sp) {
+      add_state(Sp, zp, Freal);
+      float* sp1 = slot(P - 1);  // the start state of pass 3's piece 0, padded with zero rows
+      for (int e = tid; e < Fp * kDV; e += 256) sp1[e] = e < Freal * kDV ? Sp[e] : 0.0f;
+      for (int f = tid; f < Fp; f += 256) sp1[Fp * kDV + f] = f < Freal ? zp[f] : 0.0f;
     }
-  for (int f = tid; f < Fp; f += 256) zs[f] = (zp && f < Freal) ? zp[f] : 0.0f;
+  } else if (p == 0) {
+    if (Sp) add_state(slot(P - 1), slot(P - 1) + Fp * kDV, Fp);
+  } else {
+    for (int q = 0; q < p; q++) add_state(slot(q), slot(q) + Fp * kDV, Fp);
+  }
 
-  for (int t0 = 0; t0 < Tn; t0 += kFC) {
-    const int nv = min(kFC, Tn - t0);
+  for (int t0 = t_lo; t0 < t_hi; t0 += kFC) {
+    const int nv = min(kFC, t_hi - t0);
     // stage Phi(K) and V rows of the chunk, zero past its end
     constexpr int EL = 16 / (int)sizeof(T);
     for (int e = tid; e < kFC * (Fp / EL); e += 256) {
@@ -174,6 +207,7 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
     }
     __syncthreads();
 
+    if constexpr (!STATE_ONLY) {
     // this lane's query (column n32 of the transposed tiles), clamped into the chunk
     const int tc = t0 + min(n32, nv - 1);
     const T* qrow = qp + (size_t)tc * Fp;
@@ -242,6 +276,7 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
         for (int e = 0; e < 8; e++) op[(size_t)(t0 + row) * kDV + c0 + e] = from_f32<T>(o[e]);
       }
     }
+    }  // !STATE_ONLY
     // state update S += Phi(K)^T V and z += Phi(K)^T 1 over this wave's feature tiles
 #pragma unroll
     for (int i = 0; i < NW; i++) {
@@ -260,7 +295,7 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
     }
     __syncthreads();  // tiles and the reduction buffer are reused by the next chunk
   }
-  if (Sp) {
+  auto store_state = [&](float* s_, float* z_, int rows) {
 #pragma unroll
     for (int i = 0; i < NW; i++)
 #pragma unroll
@@ -268,10 +303,22 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (f < Freal) Sp[(size_t)f * kDV + 32 * vt + n32] = Sacc[i][vt][r];
+          if (f < rows) s_[(size_t)f * kDV + 32 * vt + n32] = Sacc[i][vt][r];
         }
-    for (int f = tid; f < Freal; f += 256) zp[f] = zs[f];
-  }
+    for (int f = tid; f < rows; f += 256) z_[f] = zs[f];
+  };
+  if (STATE_ONLY) store_state(slot(p), slot(p) + Fp * kDV, Fp);
+  else if (Sp && p == P - 1) store_state(Sp, zp, Freal);
+}
+
+// Pieces per sequence: as many as keep every sequence's pieces on distinct compute units (at most 8, at most
+// one per chunk); 1 (no split) when there are at least as many sequences as compute units.
+int ext_pieces(int B, int H, int Tn) {
+  const long long BH = (long long)B * H, nch = (Tn + kFC - 1) / kFC;
+  long long P = device_cus() / BH;
+  if (P > 8) P = 8;
+  if (P > nch) P = nch;
+  return P < 1 ? 1 : (int)P;
 }
 
 template <typename Kern>
@@ -300,12 +347,20 @@ hipError_t launch_fp_t(const void* q, const void* k, const void* v, int B, int H
                      static_cast<const TIn*>(k), phik, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
                      ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  static std::atomic<bool> attr[64];
+  static std::atomic<bool> attr[64], attr1[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT>, G::lds, attr[dev])) != hipSuccess) return e;
-  hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT>), dim3(BH), dim3(256), G::lds, stream, phiq, phik,
-                     static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps);
+  if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, false>, G::lds, attr[dev])) != hipSuccess) return e;
+  const int P = ext_pieces(B, H, Tn);
+  float* slots = reinterpret_cast<float*>(phik + (size_t)BH * Tn * G::Fp);
+  if (P > 1) {
+    if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, true>, G::lds, attr1[dev])) != hipSuccess) return e;
+    hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, true>), dim3(BH * P), dim3(256), G::lds, stream, phiq, phik,
+                       static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, false>), dim3(BH * P), dim3(256), G::lds, stream, phiq, phik,
+                     static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots);
   return hipGetLastError();
 }
 
@@ -319,7 +374,11 @@ int ext_features_padded(int nh_or_zero) {
 
 size_t ext_prefill_ws_bytes(int B, int H, int T, sanatan_dtype t, int nh_or_zero) {
   const size_t el = t == SANATAN_BF16 ? 2 : 4;
-  return 2 * (size_t)B * H * T * ext_features_padded(nh_or_zero) * el;
+  const size_t Fp = ext_features_padded(nh_or_zero);
+  const int P = ext_pieces(B, H, T);
+  const size_t slots = P > 1 ? (size_t)B * H * P * Fp * (kDV + 1) * sizeof(float) : 0;
+  // Phi(Q), Phi(K), then the piece slots (Phi's bytes are a multiple of 4: Fp is a multiple of 128)
+  return 2 * (size_t)B * H * T * Fp * el + slots;
 }
 
 // nh_or_zero: 1 or 2 harmonics, or 0 for the four-channel compact map

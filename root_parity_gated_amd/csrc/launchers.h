@@ -53,6 +53,7 @@ struct PrefillPlan {
 // workgroups: 0 = one per compute unit, else that many (capped at the chunk count); with_state: the call
 // passes an initial state (S, z)
 bool prefill_plan(int B, int H, int T, int chunk, int workgroups, bool with_state, PrefillPlan* plan);
+int device_cus();  // compute units of the current device (256 if it cannot be queried)
 bool prefill_chunk_supported(int chunk, sanatan_dtype t);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
                           int64_t pos0, const MethodConsts& mc, float* S, float* z, void* out, void* ws,

@@ -408,7 +408,7 @@ bool prefill_chunk_supported(int chunk, sanatan_dtype t) {
 
 // Compute units of the current device, cached per device (the cache is written once per device; a racing
 // first call on two threads stores the same value).
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -157,3 +157,47 @@ def test_four_channel_prefill(torch_dev, dtype, T):
     print(f"four-channel prefill {dtype} T={T}: max row error {err:.3e}, decode after it {errd:.3e}")
     assert record(f"four-channel chunked prefill {dtype}", err, TOL[dtype]) <= TOL[dtype]
     assert record("four-channel decode after the prefill f32", errd, TOL[dtype]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("kind", ["nh1", "nh2", "four"])
+def test_feature_prefill_split_and_unsplit(torch_dev, kind):
+    """The sequence split (pieces of whole chunks over several workgroups, a state pass and a start state
+    summed from the pieces' slots) and the unsplit form (at least as many sequences as compute units), both
+    with a caller state, against the oracle; every sequence's outputs and final state are checked."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, H, T in ((1, 2, 333), (2, (n_cu + 1) // 2, 70)):  # split into up to 8 pieces, then unsplit
+        q, k, v, om = si.attention_inputs(950 + T, B, H, T + 20, "bf16")
+        p = params(torch, om)
+        nh = {"nh1": 1, "nh2": 2, "four": 0}[kind]
+        rows = (2 + 4 * nh) * D if nh else 3 * D + 1
+        # caller state: the prefill of 20 earlier tokens (positions 0..19), checked through the outputs below
+        S = torch.zeros((B, H, rows, 64), device="cuda")
+        z = torch.zeros((B, H, rows), device="cuda")
+        pre, main = slice(0, 20), slice(20, 20 + T)
+        run = (lambda a, b, c, **kw: rpg.sanatan_prefill_harmonics(a, b, c, nh, p, **kw)) if nh else (
+            lambda a, b, c, **kw: rpg.sanatan_prefill_four_channel(a, b, c, p, S4=kw.pop("S"), z4=kw.pop("z"), **kw))
+        run(dev(torch, q[:, :, pre], "bf16"), dev(torch, k[:, :, pre], "bf16"), dev(torch, v[:, :, pre], "bf16"),
+            S=S, z=z)
+        out = run(dev(torch, q[:, :, main], "bf16"), dev(torch, k[:, :, main], "bf16"),
+                  dev(torch, v[:, :, main], "bf16"), pos0=20, S=S, z=z)
+        torch.cuda.synchronize()
+        got, Sg, zg = host(out), host(S), host(z)
+        err = serr = 0.0
+        for b in range(B):
+            for h in range(H):
+                if nh:
+                    want = oracle.attention_direct_h(q[b, h], k[b, h], v[b, h], om[h], nh)[20:]
+                    _, Sw, zw = oracle.recurrent_h(q[b, h], k[b, h], v[b, h], om[h], nh, want_out=False)
+                else:
+                    want = oracle.attention_direct(q[b, h], k[b, h], v[b, h], om[h], four_channel=True)[20:]
+                    _, S6, z6 = oracle.recurrent(q[b, h], k[b, h], v[b, h], om[h], want_out=False)
+                    rows6 = [0] + list(range(3 * D, 6 * D))
+                    Sw, zw = S6[rows6], z6[rows6]
+                err = max(err, row_rel_err(got[b, h], want))
+                serr = max(serr, np.abs(Sg[b, h] - Sw).max() / np.abs(Sw).max(), np.abs(zg[b, h] - zw).max() / np.abs(zw).max())
+        print(f"feature prefill {kind} B{B} H{H} T{T}: output {err:.3e}, state {serr:.3e}")
+        assert record(f"feature-map prefill {kind} bf16 (split and unsplit)", err, TOL["bf16"]) <= TOL["bf16"]
+        assert serr <= TOL["bf16"]
