@@ -393,9 +393,9 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(const PrefillArgs arg
   }
 }
 
-// Blocks per sequence of the scan: about four per workgroup of the call in all, 8 to one per 256 elements.
+// Blocks per sequence of the scan: about eight per workgroup of the call in all, 8 to one per 256 elements.
 static int scan_slices(const PrefillArgs& a, int BH) {
-  const int want = (4 * a.G + BH - 1) / BH;
+  const int want = (8 * a.G + BH - 1) / BH;
   const int most = (kStateFloats + 255) / 256;
   return want < 8 ? 8 : (want > most ? most : want);
 }
