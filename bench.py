@@ -533,7 +533,7 @@ def main():
         traffic_summary(args.traffic[0], args.traffic[1], args.traffic_key)
         return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(pass --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
