@@ -502,6 +502,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, sanatan_d
   a.total = plan.total;
   a.lens = lens;
   a.G = plan.G; a.ncs = plan.ncs; a.nph = mc.nph; a.B = B; a.H = H; a.T = T; a.chunk = plan.chunk;
+  a.chunk_log2 = 0;
+  while ((1 << a.chunk_log2) < plan.chunk) a.chunk_log2++;
   a.multi = plan.multi; a.scanned = plan.scanned;
   if (lens && plan.G > 1) {
     // the pieces depend on lengths the host does not see: any sequence may span several, and a caller

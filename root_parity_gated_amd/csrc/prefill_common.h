@@ -80,20 +80,25 @@ struct PrefillArgs {
   float kr, ceps;
   const int* lens;   // [B] per-batch-element lengths (device), or null: every sequence has T tokens
   int B, chunk;
+  int chunk_log2;    // chunk = 1 << chunk_log2 (16, 32, 64 or 128)
 };
 
 __device__ __forceinline__ int ragged_len(const PrefillArgs& a, int b) {
   const int L = a.lens[b];
   return L < 0 ? 0 : (L > a.T ? a.T : L);
 }
+// chunks of a sequence of L tokens (the chunk is a power of two: a shift, not a division)
+__device__ __forceinline__ long long ragged_chunks(const PrefillArgs& a, int L) {
+  return (long long)((L + a.chunk - 1) >> a.chunk_log2);
+}
 // Chunks of the whole call.  A ragged call's count is summed from the lengths by every workgroup (B scalar
-// loads), so that the partition needs no host copy of them.  RAGGED is a template flag of the kernels, so
+// loads and a few scalar operations each), so that the partition needs no host copy of them.  RAGGED is a template flag of the kernels, so
 // that the uniform kernels carry none of this code.
 template <bool RAGGED>
 __device__ __forceinline__ long long call_chunks(const PrefillArgs& a) {
   if (!RAGGED) return a.total;
   long long n = 0;
-  for (int b = 0; b < a.B; b++) n += (long long)a.H * ((ragged_len(a, b) + a.chunk - 1) / a.chunk);
+  for (int b = 0; b < a.B; b++) n += (long long)a.H * ragged_chunks(a, ragged_len(a, b));
   return n;
 }
 // The sequence holding flattened chunk c: its index bh, its chunks [c0, c1) and its length in tokens.
@@ -115,7 +120,7 @@ __device__ __forceinline__ SeqSpan seq_span(long long c, const PrefillArgs& a) {
   long long acc = 0;
   for (int b = 0; b < a.B; b++) {
     const int L = ragged_len(a, b);
-    const long long n = (L + a.chunk - 1) / a.chunk;
+    const long long n = ragged_chunks(a, L);
     if (c < acc + a.H * n) {
       const int h = (int)((c - acc) / n);
       s.bh = b * a.H + h;
@@ -141,9 +146,9 @@ __device__ __forceinline__ SeqSpan seq_span_of(int bh, const PrefillArgs& a) {
   }
   const int bb = bh / a.H, h = bh % a.H;
   long long acc = 0;
-  for (int b = 0; b < bb; b++) acc += (long long)a.H * ((ragged_len(a, b) + a.chunk - 1) / a.chunk);
+  for (int b = 0; b < bb; b++) acc += (long long)a.H * ragged_chunks(a, ragged_len(a, b));
   s.len = ragged_len(a, bb);
-  const long long n = (s.len + a.chunk - 1) / a.chunk;
+  const long long n = ragged_chunks(a, s.len);
   s.c0 = acc + h * n;
   s.c1 = s.c0 + n;
   return s;

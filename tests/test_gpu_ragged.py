@@ -148,3 +148,16 @@ def test_ragged_equals_uniform_when_lengths_are_full(torch_dev):
     b = rpg.sanatan_prefill_chunked(*args, 64, prm)
     torch.cuda.synchronize()
     assert row_rel_err(host(a), host(b)) <= TOL["bf16"]
+
+
+def test_ragged_many_short_prompts(torch_dev):
+    """256 prompts of seeded lengths 0..100 (many sequences per workgroup, many of them empty or one chunk long),
+    fp32 with a caller state."""
+    rng = np.random.default_rng(1350)
+    B, H, T = 256, 2, 100
+    lengths = rng.integers(0, T + 1, B)
+    lengths[::17] = 0
+    err, serr = run_ragged(torch_dev, 1351, "f32", 32, B, H, T, lengths, pos0=3, with_state=True)
+    print(f"ragged many short prompts: output {err:.3e}, state {serr:.3e}")
+    assert record("ragged prefill f32: output", err, TOL["f32"]) <= TOL["f32"]
+    assert record("ragged prefill f32: state", serr, TOL["f32"]) <= TOL["f32"]
