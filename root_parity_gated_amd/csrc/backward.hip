@@ -19,7 +19,9 @@
 // for each 32-key tile (dPhi(K) and dv); both recompute the score and <g, v> tiles on 32x32x16 bf16 MFMA
 // (32x32x2 fp32 for fp32 inputs).  A wave keeps a 32 x 192 fp32 slice of its gradient in accumulators (32 x 128
 // for fp32 inputs, whose operand fragments need twice the registers), so the feature gradients take two (three)
-// passes, each recomputing the score tiles.  The feature gradients go to an fp32 workspace; the Jacobian kernel turns them into
+// passes, each recomputing the score tiles.  With bf16 operands, G enters the dPhi products as its bf16 rounding
+// plus the bf16 rounding of the residual: a row of G nearly cancels (its weighted sum is ~0), so one rounding
+// would leave an error of the order of the result.  The feature gradients go to an fp32 workspace; the Jacobian kernel turns them into
 // du and per-block omega partials, which two small kernels sum in a fixed order (bitwise deterministic).
 #include <atomic>
 
@@ -121,6 +123,15 @@ __device__ __forceinline__ typename FragT<T>::type row_frag(const T* base, int p
   }
 }
 
+// x - (float)rounded, packed: the part of 8 fp32 values that their bf16 rounding dropped
+template <typename T>
+__device__ __forceinline__ typename FragT<T>::type residual8(const float (&x)[8], const typename FragT<T>::type& rounded) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) r[i] = x[i] - (float)rounded[i];
+  return pack8f<T>(r);
+}
+
 // dPhi(Q) for one 32-query tile per wave (four per workgroup), feature tiles FT0 .. FT0 + NFT - 1 (32 features
 // each).  Tile layout: accumulator [s][t] (rows keys, columns queries), so a lane (query n32, half h) owns
 // one query and its scalars (Dn_t, delta_t).
@@ -192,11 +203,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const T* __restrict__ ph
       hi8[i] = gl[8 + i];
     }
     const Frag G0 = pack8f<T>(lo), G1 = pack8f<T>(hi8);
-    // dPhi(q)^T[f][t] += Phi(K)^T[f][s] G^T[s][t]
+    // dPhi(q)^T[f][t] += Phi(K)^T[f][s] G^T[s][t].  With bf16 operands G also enters as its rounding residual
+    // (a second bf16 term): a row of G nearly cancels, so its rounding error would weigh on the sum.
+    Frag R0 = G0, R1 = G1;
+    if constexpr (sizeof(T) == 2) R0 = residual8<T>(lo, G0), R1 = residual8<T>(hi8, G1);
 #pragma unroll
     for (int f = 0; f < NFT; f++) {
-      mma32(acc[f], lds_tokfrag(F, G::FP, 0, 32 * (FT0 + f), l), G0);
-      mma32(acc[f], lds_tokfrag(F, G::FP, 16, 32 * (FT0 + f), l), G1);
+      const Frag A0 = lds_tokfrag(F, G::FP, 0, 32 * (FT0 + f), l), A1 = lds_tokfrag(F, G::FP, 16, 32 * (FT0 + f), l);
+      mma32(acc[f], A0, G0);
+      mma32(acc[f], A1, G1);
+      if constexpr (sizeof(T) == 2) {
+        mma32(acc[f], A0, R0);
+        mma32(acc[f], A1, R1);
+      }
     }
   }
   if (t >= Tn) return;
@@ -280,10 +299,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const T* __restrict__ p
       hi8[i] = gl[8 + i];
     }
     const Frag G0 = pack8f<T>(lo), G1 = pack8f<T>(hi8);
+    Frag R0 = G0, R1 = G1;  // bf16: G's rounding residual as a second term, as in the dPhi(q) kernel
+    if constexpr (sizeof(T) == 2) R0 = residual8<T>(lo, G0), R1 = residual8<T>(hi8, G1);
 #pragma unroll
     for (int f = 0; f < NFT; f++) {
-      mma32(acc[f], lds_tokfrag(F, G::FP, 0, 32 * (FT0 + f), l), G0);
-      mma32(acc[f], lds_tokfrag(F, G::FP, 16, 32 * (FT0 + f), l), G1);
+      const Frag A0 = lds_tokfrag(F, G::FP, 0, 32 * (FT0 + f), l), A1 = lds_tokfrag(F, G::FP, 16, 32 * (FT0 + f), l);
+      mma32(acc[f], A0, G0);
+      mma32(acc[f], A1, G1);
+      if constexpr (sizeof(T) == 2) {
+        mma32(acc[f], A0, R0);
+        mma32(acc[f], A1, R1);
+      }
     }
     if constexpr (WITH_V) {
 #pragma unroll
