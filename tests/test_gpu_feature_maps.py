@@ -156,7 +156,7 @@ def test_four_channel_prefill(torch_dev, dtype, T):
         assert np.abs(z4_after[0, h] - zw).max() <= TOL[dtype] * np.abs(zw).max()
     print(f"four-channel prefill {dtype} T={T}: max row error {err:.3e}, decode after it {errd:.3e}")
     assert record(f"four-channel chunked prefill {dtype}", err, TOL[dtype]) <= TOL[dtype]
-    assert record("four-channel decode after the prefill f32", errd, TOL[dtype]) <= TOL[dtype]
+    assert record(f"four-channel decode (fp32) after a {dtype} prefill", errd, TOL[dtype]) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("kind", ["nh1", "nh2", "four"])
