@@ -128,3 +128,97 @@ def test_quadratic_random_shape(torch_dev, case):
             err = max(err, float(d.max()))
     print(f"case {case}: {err:.3e}")
     assert record(f"random quadratic shapes {dtype}", err, TOL[dtype]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_backward_random_shape(torch_dev, case):
+    """The backward pass (p = 1 or 2) at seeded random shapes, heads sharing omega rows at random."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    rng = np.random.default_rng(4700 + case)
+    dtype = ["f32", "bf16"][rng.integers(2)]
+    p = int(rng.integers(1, 3))
+    B, H, T = int(rng.integers(1, 3)), int(rng.integers(1, 5)), int(rng.integers(2, 260))
+    nph = int(rng.integers(1, H + 1))
+    print(f"case {case}: {dtype} p={p} B={B} H={H} T={T} nph={nph}", flush=True)
+    q, k, v, om = si.attention_inputs(4800 + case, B, H, T, dtype)
+    g = np.random.default_rng(4900 + case).standard_normal((B, H, T, 64)).astype(np.float32)
+    if dtype == "bf16":
+        g = si.bf16_round(g)
+    om = om[:nph]
+    dev = lambda x: (lambda t: t.to(torch.bfloat16) if dtype == "bf16" else t)(
+        torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda())
+    prm = rpg.Params(omega=torch.from_numpy(np.ascontiguousarray(om, dtype=np.float32)).cuda())
+    dq, dk, dv, dom = rpg.sanatan_attention_backward(dev(q), dev(k), dev(v), dev(g), p, prm)
+    torch.cuda.synchronize()
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)
+    dq, dk, dv, dom = host(dq), host(dk), host(dv), host(dom)
+
+    def rel(got, want):  # the backward tests' metric: rows floored at 1 % of the largest row
+        got, want = got.reshape(-1, want.shape[-1]), want.reshape(-1, want.shape[-1])
+        sc = np.abs(want).max(1)
+        sc = np.maximum(sc, 1e-2 * sc.max())
+        return float((np.abs(got - want).max(1) / sc).max())
+
+    want_dom = np.zeros_like(dom)
+    errs = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in range(B):
+        for h in range(H):
+            wq, wk, wv, wo = oracle.attention_direct_grad(q[b, h], k[b, h], v[b, h], g[b, h], om[h % nph], p=p)
+            errs["dq"] = max(errs["dq"], rel(dq[b, h], wq))
+            errs["dk"] = max(errs["dk"], rel(dk[b, h], wk))
+            errs["dv"] = max(errs["dv"], rel(dv[b, h], wv))
+            want_dom[h % nph] += wo
+    errs["domega"] = rel(dom, want_dom)
+    err = max(errs.values())
+    print(f"case {case}: " + ", ".join(f"{n} {e:.3e}" for n, e in errs.items()))
+    assert record(f"random backward shapes {dtype}", err, TOL[dtype]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_decode_random_shape(torch_dev, case):
+    """Decode steps from a prefilled state at seeded random sizes: one position for all head-states or one each,
+    on the full or the compact state."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    rng = np.random.default_rng(5000 + case)
+    N, steps, fill = int(rng.integers(1, 300)), int(rng.integers(1, 9)), int(rng.integers(1, 200))
+    per_state, compact = bool(rng.integers(2)), bool(rng.integers(2))
+    print(f"case {case}: N={N} steps={steps} fill={fill} per_state={per_state} compact={compact}", flush=True)
+    q, k, v, om = si.attention_inputs(5100 + case, 1, N, fill + steps, "f32")
+    q, k, v = q[0], k[0], v[0]
+    base = rng.integers(0, 1 << 20, N) if per_state else np.full(N, int(rng.integers(0, 1 << 20)))
+    prm = rpg.Params(omega=torch.from_numpy(np.ascontiguousarray(om, dtype=np.float32)).cuda())
+    # the starting state: the oracle's recurrence over the fill tokens of each head-state, from its own position
+    S0 = np.zeros((N, 384, 64), np.float32)
+    z0 = np.zeros((N, 384), np.float32)
+    for i in range(N):
+        _, s_, z_ = oracle.recurrent(q[i, :fill], k[i, :fill], v[i, :fill], om[i], pos0=int(base[i]), want_out=False)
+        S0[i], z0[i] = s_, z_
+    S, z = torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda()
+    if compact:
+        Sc = torch.empty((N, 5 * 64 + 1, 64), device="cuda")
+        zc = torch.empty((N, 5 * 64 + 1), device="cuda")
+        rpg.sanatan_state_compact(S, z, Sc, zc)
+    outs = []
+    for j in range(steps):
+        pos = torch.from_numpy((base + fill + j).astype(np.int64)).cuda() if per_state else int(base[0] + fill + j)
+        args = [torch.from_numpy(np.ascontiguousarray(x[:, fill + j], dtype=np.float32)).cuda() for x in (q, k, v)]
+        if compact:
+            outs.append(rpg.sanatan_decode_step_compact(*args, pos, prm, Sc, zc).clone())
+        elif per_state:
+            outs.append(rpg.sanatan_decode_step_positions(*args, pos, prm, S, z).clone())
+        else:
+            outs.append(rpg.sanatan_decode_step(*args, pos, prm, S, z).clone())
+    torch.cuda.synchronize()
+    err = 0.0
+    for i in range(N):
+        want, _, _ = oracle.recurrent(q[i, fill:], k[i, fill:], v[i, fill:], om[i], pos0=int(base[i] + fill),
+                                      S=S0[i], z=z0[i])
+        got = np.stack([o[i].cpu().numpy() for o in outs]).astype(np.float64)
+        d = np.abs(got - want).max(1) / np.maximum(np.abs(want).max(1), 1e-12)
+        err = max(err, float(d.max()))
+    print(f"case {case}: {err:.3e}")
+    assert record("random decode shapes f32", err, TOL["f32"]) <= TOL["f32"]
