@@ -150,6 +150,21 @@ def timed_loop(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def per_call_ms(torch, fn, steps):
+    """Each of `steps` calls timed on its own (an event pair around every call, on the current stream);
+    returns (median, mean) in ms.  Used beside timed_loop's whole-loop figure."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2]), sum(ms) / len(ms)
+
+
 def graph_of(torch, fn):
     """One call of fn captured as a HIP graph (replayed on the current stream); None if capture fails."""
     try:
@@ -360,7 +375,7 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False, co
     }
 
 
-def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_channel=False):
+def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_channel=False, per_call=None):
     """ms per call: (eager, graph-replayed).  Each call is one complete library call on resident inputs;
     the graph variant replays that call captured once, which removes the host launch overhead."""
     q, k, v, om = si.workload_inputs(w)
@@ -379,6 +394,8 @@ def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_c
                          device="cuda")
         fn = lambda: rpg.sanatan_prefill_chunked(qd, kd, vd, w.chunk, p, out=out, ws=ws)
     eager = timed_loop(torch, fn, steps, warmup)
+    if per_call is not None:  # each call timed on its own as well: median and mean
+        per_call["median"], per_call["mean"] = per_call_ms(torch, fn, steps)
     g = graph_of(torch, fn)
     graph = timed_loop(torch, g.replay, steps, warmup) if g is not None else None
     return eager, graph
@@ -581,7 +598,8 @@ def main():
         return
 
     log(f"prefill {w.name}: {args.warmup} warmup + {args.steps} timed steps")
-    eager_ms, graph_ms = bench_prefill_like(torch, rpg, si, w, args.steps, args.warmup)
+    per_call = {}
+    eager_ms, graph_ms = bench_prefill_like(torch, rpg, si, w, args.steps, args.warmup, per_call=per_call)
     use_graph = graph_ms is not None and graph_ms < eager_ms
     ms = graph_ms if use_graph else eager_ms
     log(f"prefill: {eager_ms * 1e3:.1f} us/step eager, "
@@ -620,6 +638,7 @@ def main():
                       "timed as one launch sequence",
             "timing": "graph-replayed call" if use_graph else "eager call",
             "ms_per_call_eager": eager_ms, "ms_per_call_graph": graph_ms,
+            "ms_per_call_eager_median": per_call.get("median"), "ms_per_call_eager_mean_single": per_call.get("mean"),
             "hbm_bytes_algorithmic": nbytes,
             "mfma_achieved_tflops": achieved_tf, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
             "mfma_frac": achieved_tf / PEAK_BF16_TFLOPS,
