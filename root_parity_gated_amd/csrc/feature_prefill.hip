@@ -8,8 +8,9 @@
 //     r cos n th, r sin n th (n = 1..nh)] of the rotated angle th, (2 + 4 nh) d features, state rows in that
 //     channel-major order (nh = 1 is the six-channel map);
 //   * the unclipped four-channel kernel (§2.5), per dim [1, r, r cos th, r sin th], kept compact like its decode
-//     state: row 0 is the shared channel-0 feature (1 for a key; d for a query, which stands for its d equal
-//     rows), then r, r cos th, r sin th: 3d + 1 features.
+//     state: one shared channel-0 feature (1 for a key; d for a query, which stands for its d equal rows) and
+//     r, r cos th, r sin th: 3d + 1 features.  The caller's state holds the shared row first; the workspace
+//     holds it last (feature 3d), so that every thread's 8 dims of a channel are one aligned vector store.
 // Phi(Q) and Phi(K) are featurized once into the workspace (element type of the call), padded to a multiple
 // of 128 features with zeros.  The prefill kernel then walks each sequence in 32-token chunks with one
 // workgroup of 4 waves per sequence: wave w owns feature tiles w, w + 4, ... (32 features each) and their
@@ -33,7 +34,7 @@ namespace {
 constexpr int kFC = 32;  // chunk tokens
 
 // featurize one operand into the padded feature layout.  KIND 0: harmonics n = 1..NH; KIND 1: four-channel
-// compact (IS_Q: row 0 carries d instead of 1).  A thread owns 8 dims of one token.
+// compact, shared feature at 3d (IS_Q: it carries d instead of 1).  A thread owns 8 dims of one token.
 template <typename TIn, typename TOut, int KIND, int NH, bool IS_Q>
 __global__ __launch_bounds__(256) void featurize_ext_kernel(const TIn* __restrict__ u, TOut* __restrict__ phi, int H,
                                                             int T, int Fp, int64_t pos0,
@@ -54,9 +55,17 @@ __global__ __launch_bounds__(256) void featurize_ext_kernel(const TIn* __restric
     featurize1(x, rho, om4, kr, cr[i], sr[i], rr[i]);
     y[i] = x * rcp_hw(fmaf(fabsf(x), 2.0f, 2.0f)) + rho;  // the rotated angle in revolutions, as featurize1
   }
-  auto put = [&](int row0, const float (&val)[8]) {
+  auto put = [&](int row0, const float (&val)[8]) {  // 8 consecutive features, one vector store
+    if constexpr (sizeof(TOut) == 2) {
+      bf16x8 w;
 #pragma unroll
-    for (int i = 0; i < 8; i++) o[row0 + a0 + i] = from_f32<TOut>(val[i]);
+      for (int i = 0; i < 8; i++) w[i] = (__bf16)val[i];
+      *reinterpret_cast<bf16x8*>(o + row0 + a0) = w;
+    } else {
+      float* d = reinterpret_cast<float*>(o + row0 + a0);
+      *reinterpret_cast<float4*>(d) = make_float4(val[0], val[1], val[2], val[3]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(val[4], val[5], val[6], val[7]);
+    }
   };
   float tmp[8];
   if constexpr (KIND == 0) {
@@ -82,20 +91,29 @@ __global__ __launch_bounds__(256) void featurize_ext_kernel(const TIn* __restric
       put((2 * NH + 2 * n) * kD, c);
       put((2 * NH + 2 * n + 1) * kD, s);
     }
-    // zero padding past (2 + 4 NH) d: written by the threads of dim block 0
+    // zero padding past (2 + 4 NH) d
     const int Fr = (2 + 4 * NH) * kD;
-    for (int f = Fr + a0; f < Fp; f += 64)
 #pragma unroll
-      for (int i = 0; i < 8; i++) o[f + i] = from_f32<TOut>(0.0f);
+    for (int i = 0; i < 8; i++) tmp[i] = 0.0f;
+    for (int f = Fr; f < Fp; f += 64) put(f, tmp);
   } else {
-    if (j == 0) o[0] = from_f32<TOut>(IS_Q ? (float)kD : 1.0f);
+    // internal order r, r cos, r sin (d each), then the shared feature (d for a query, 1 for a key) and zero
+    // padding; the caller's compact state keeps the shared row first, and the prefill maps rows between the two
+    float rc[8], rs[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      o[1 + a0 + i] = from_f32<TOut>(rr[i]);
-      o[1 + kD + a0 + i] = from_f32<TOut>(rr[i] * cr[i]);
-      o[1 + 2 * kD + a0 + i] = from_f32<TOut>(rr[i] * sr[i]);
+      rc[i] = rr[i] * cr[i];
+      rs[i] = rr[i] * sr[i];
     }
-    for (int f = 3 * kD + 1 + threadIdx.x % 8; f < Fp; f += 8) o[f] = from_f32<TOut>(0.0f);
+    put(0, rr);
+    put(kD, rc);
+    put(2 * kD, rs);
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = (j == 0 && i == 0) ? (IS_Q ? (float)kD : 1.0f) : 0.0f;
+    put(3 * kD, tmp);  // the shared feature, then zeros up to 3 d + 64
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = 0.0f;
+    for (int f = 4 * kD; f < Fp; f += 64) put(f, tmp);
   }
 }
 
@@ -108,17 +126,31 @@ struct FGeom {
   static constexpr int k_bytes = kFC * KP * (int)sizeof(T);
   static constexpr int v_bytes = kFC * VP * (int)sizeof(T);
   static constexpr int red_bytes = 4 * kFC * RP * 4;
-  static constexpr int lds = k_bytes + v_bytes + red_bytes + Fp * 4;
+  // bf16: the chunk's Phi(Q) rows are staged in LDS like Phi(K) (fp32 rows would not fit beside them; they are
+  // read from global memory)
+  static constexpr bool QLDS = sizeof(T) == 2;
+  static constexpr int q_bytes = QLDS ? k_bytes : 0;
+  static constexpr int lds = k_bytes + q_bytes + v_bytes + red_bytes + Fp * 4;
+  static constexpr int EL = 16 / (int)sizeof(T);            // elements per 16-byte piece
+  static constexpr int FPIECES = kFC * (Fp / EL) / 256;     // 16-byte pieces of a feature chunk per thread
+  static constexpr int VPIECES = (kFC * (kDV / EL) + 255) / 256;
+  static_assert(kFC * (Fp / EL) % 256 == 0, "a feature chunk is a whole number of pieces per thread");
 };
 
-// 8 features of one row, slots (h, i) <-> feature base + 8 (i / 4) + 4 h + i % 4 (the accumulator row order)
+// 8 features of one row, slots (h, i) <-> feature base + 8 (i / 4) + 4 h + i % 4 (the accumulator row order):
+// two 4-element vector loads
 template <typename T>
 __device__ __forceinline__ typename FragT<T>::type slot_frag(const T* row, int base, int h) {
   typename FragT<T>::type f;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    f[i] = row[base + 4 * h + i];
-    f[4 + i] = row[base + 8 + 4 * h + i];
+  if constexpr (sizeof(T) == 2) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(row + base + 4 * h);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(row + base + 8 + 4 * h);
+    const u32x4 w = {a[0], a[1], b[0], b[1]};
+    f = __builtin_bit_cast(typename FragT<T>::type, w);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(row + base + 4 * h);
+    const float4 b = *reinterpret_cast<const float4*>(row + base + 8 + 4 * h);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
   }
   return f;
 }
@@ -127,16 +159,18 @@ template <typename T, int NFT, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                               const T* __restrict__ v, T* __restrict__ out,
                                                               float* __restrict__ S, float* __restrict__ z, int Tn,
-                                                              int Freal, float ceps, int P, float* __restrict__ slots) {
+                                                              int Freal, float ceps, int P, float* __restrict__ slots,
+                                                              int shared_last) {
   using G = FGeom<T, NFT>;
   typedef typename FragT<T>::type Frag;
   static_assert(NFT % 4 == 0, "feature tiles are dealt to four waves");
   constexpr int NW = NFT / 4, Fp = G::Fp, KP = G::KP, VP = G::VP, RP = G::RP;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   T* KT = reinterpret_cast<T*>(smem);
-  T* VT = reinterpret_cast<T*>(smem + G::k_bytes);
-  float* red = reinterpret_cast<float*>(smem + G::k_bytes + G::v_bytes);
-  float* zs = reinterpret_cast<float*>(smem + G::k_bytes + G::v_bytes + G::red_bytes);
+  T* QT = reinterpret_cast<T*>(smem + G::k_bytes);  // (bf16 only)
+  T* VT = reinterpret_cast<T*>(smem + G::k_bytes + G::q_bytes);
+  float* red = reinterpret_cast<float*>(smem + G::k_bytes + G::q_bytes + G::v_bytes);
+  float* zs = reinterpret_cast<float*>(smem + G::k_bytes + G::q_bytes + G::v_bytes + G::red_bytes);
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
   const int bh = blockIdx.x / P, p = blockIdx.x % P;
   if (STATE_ONLY && p == P - 1) return;  // the final piece's state comes out of pass 3
@@ -162,7 +196,10 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
   for (int f = tid; f < Fp; f += 256) zs[f] = 0.0f;
   // add a state of `rows` rows ([rows][d_v] then [rows]) to the wave's tiles and to zs (each zs entry is
   // touched by the same thread here as in the zeroing above)
-  auto add_state = [&](const float* s_, const float* z_, int rows) {
+  // The caller's row of internal feature f: the four-channel map keeps its shared feature last internally
+  // (feature 3 d) but first in the caller's compact state
+  auto user_row = [&](int f) { return shared_last ? (f == Freal - 1 ? 0 : f + 1) : f; };
+  auto add_state = [&](const float* s_, const float* z_, int rows, bool user) {
 #pragma unroll
     for (int i = 0; i < NW; i++)
 #pragma unroll
@@ -170,47 +207,75 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (f < rows) Sacc[i][vt][r] += s_[(size_t)f * kDV + 32 * vt + n32];
+          if (f < rows) Sacc[i][vt][r] += s_[(size_t)(user ? user_row(f) : f) * kDV + 32 * vt + n32];
         }
-    for (int f = tid; f < rows; f += 256) zs[f] += z_[f];
+    for (int f = tid; f < rows; f += 256) zs[f] += z_[user ? user_row(f) : f];
   };
   if (P == 1) {
-    if (Sp) add_state(Sp, zp, Freal);
+    if (Sp) add_state(Sp, zp, Freal, true);
   } else if (STATE_ONLY) {
     if (p == 0 && Sp) {
-      add_state(Sp, zp, Freal);
-      float* sp1 = slot(P - 1);  // the start state of pass 3's piece 0, padded with zero rows
-      for (int e = tid; e < Fp * kDV; e += 256) sp1[e] = e < Freal * kDV ? Sp[e] : 0.0f;
-      for (int f = tid; f < Fp; f += 256) sp1[Fp * kDV + f] = f < Freal ? zp[f] : 0.0f;
+      add_state(Sp, zp, Freal, true);
+      float* sp1 = slot(P - 1);  // the start state of pass 3's piece 0, internal rows, padded with zeros
+      for (int e = tid; e < Fp * kDV; e += 256) {
+        const int f = e / kDV;
+        sp1[e] = f < Freal ? Sp[(size_t)user_row(f) * kDV + e % kDV] : 0.0f;
+      }
+      for (int f = tid; f < Fp; f += 256) sp1[Fp * kDV + f] = f < Freal ? zp[user_row(f)] : 0.0f;
     }
   } else if (p == 0) {
-    if (Sp) add_state(slot(P - 1), slot(P - 1) + Fp * kDV, Fp);
+    if (Sp) add_state(slot(P - 1), slot(P - 1) + Fp * kDV, Fp, false);
   } else {
-    for (int q = 0; q < p; q++) add_state(slot(q), slot(q) + Fp * kDV, Fp);
+    for (int q = 0; q < p; q++) add_state(slot(q), slot(q) + Fp * kDV, Fp, false);
   }
 
   for (int t0 = t_lo; t0 < t_hi; t0 += kFC) {
     const int nv = min(kFC, t_hi - t0);
-    // stage Phi(K) and V rows of the chunk, zero past its end
-    constexpr int EL = 16 / (int)sizeof(T);
-    for (int e = tid; e < kFC * (Fp / EL); e += 256) {
-      const int s = e / (Fp / EL), c = (e % (Fp / EL)) * EL;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (s < nv) val = *reinterpret_cast<const u32x4*>(kp + (size_t)(t0 + s) * Fp + c);
-      *reinterpret_cast<u32x4*>(KT + s * KP + c) = val;
+    // stage Phi(K) (and, bf16, Phi(Q)) and V rows of the chunk, zero past its end: the loads are issued in
+    // groups of GS pieces per operand before the group's LDS writes, so the staging waits for memory once per
+    // group instead of once per piece
+    constexpr int EL = G::EL, FPC = Fp / EL;
+    constexpr int GS = G::FPIECES < 4 ? G::FPIECES : 4;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g0 = 0; g0 < G::FPIECES; g0 += GS) {
+      u32x4 kr[GS], qr[GS];
+#pragma unroll
+      for (int i = 0; i < GS; i++) {
+        if (g0 + i < G::FPIECES) {
+          const int e = tid + 256 * (g0 + i), s = e / FPC, c = (e % FPC) * EL, sc = t0 + min(s, nv - 1);
+          kr[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)sc * Fp + c);
+          if constexpr (G::QLDS) qr[i] = *reinterpret_cast<const u32x4*>(qp + (size_t)sc * Fp + c);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < GS; i++) {
+        if (g0 + i < G::FPIECES) {
+          const int e = tid + 256 * (g0 + i), s = e / FPC, c = (e % FPC) * EL;
+          *reinterpret_cast<u32x4*>(KT + s * KP + c) = s < nv ? kr[i] : zero4;
+          if constexpr (G::QLDS) *reinterpret_cast<u32x4*>(QT + s * KP + c) = qr[i];
+        }
+      }
     }
-    for (int e = tid; e < kFC * (kDV / EL); e += 256) {
-      const int s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (s < nv) val = *reinterpret_cast<const u32x4*>(vp + (size_t)(t0 + s) * kDV + c);
-      *reinterpret_cast<u32x4*>(VT + s * VP + c) = val;
+    {
+      u32x4 vr[G::VPIECES];
+#pragma unroll
+      for (int i = 0; i < G::VPIECES; i++) {
+        const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+        if (e < kFC * (kDV / EL)) vr[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)(t0 + min(s, nv - 1)) * kDV + c);
+      }
+#pragma unroll
+      for (int i = 0; i < G::VPIECES; i++) {
+        const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+        if (e < kFC * (kDV / EL)) *reinterpret_cast<u32x4*>(VT + s * VP + c) = s < nv ? vr[i] : zero4;
+      }
     }
     __syncthreads();
 
     if constexpr (!STATE_ONLY) {
     // this lane's query (column n32 of the transposed tiles), clamped into the chunk
     const int tc = t0 + min(n32, nv - 1);
-    const T* qrow = qp + (size_t)tc * Fp;
+    const T* qrow = G::QLDS ? QT + n32 * KP : qp + (size_t)tc * Fp;
     // per feature tile: its two query fragments feed the partial scores A^T[s][t] and, right away, the readout
     // against the state before this chunk (num^T += S^T Phi(Q)^T), so only two fragments are live at a time
     f32x16 at, num[2];
@@ -272,8 +337,16 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
 #pragma unroll
         for (int e = 0; e < 8; e++)
           o[e] = (((b0[c0 + e] + b0[WS + c0 + e]) + b0[2 * WS + c0 + e]) + b0[3 * WS + c0 + e]) * inv;
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 ov;
 #pragma unroll
-        for (int e = 0; e < 8; e++) op[(size_t)(t0 + row) * kDV + c0 + e] = from_f32<T>(o[e]);
+          for (int e = 0; e < 8; e++) ov[e] = (__bf16)o[e];
+          *reinterpret_cast<bf16x8*>(op + (size_t)(t0 + row) * kDV + c0) = ov;
+        } else {
+          float* dst = reinterpret_cast<float*>(op + (size_t)(t0 + row) * kDV + c0);
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
       }
     }
     }  // !STATE_ONLY
@@ -295,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
     }
     __syncthreads();  // tiles and the reduction buffer are reused by the next chunk
   }
-  auto store_state = [&](float* s_, float* z_, int rows) {
+  auto store_state = [&](float* s_, float* z_, int rows, bool user) {
 #pragma unroll
     for (int i = 0; i < NW; i++)
 #pragma unroll
@@ -303,12 +376,12 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int f = 32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (f < rows) s_[(size_t)f * kDV + 32 * vt + n32] = Sacc[i][vt][r];
+          if (f < rows) s_[(size_t)(user ? user_row(f) : f) * kDV + 32 * vt + n32] = Sacc[i][vt][r];
         }
-    for (int f = tid; f < rows; f += 256) z_[f] = zs[f];
+    for (int f = tid; f < rows; f += 256) z_[user ? user_row(f) : f] = zs[f];
   };
-  if (STATE_ONLY) store_state(slot(p), slot(p) + Fp * kDV, Fp);
-  else if (Sp && p == P - 1) store_state(Sp, zp, Freal);
+  if (STATE_ONLY) store_state(slot(p), slot(p) + Fp * kDV, Fp, false);
+  else if (Sp && p == P - 1) store_state(Sp, zp, Freal, true);
 }
 
 // Pieces per sequence: as many as keep every sequence's pieces on distinct compute units (at most 8, at most
@@ -356,11 +429,13 @@ hipError_t launch_fp_t(const void* q, const void* k, const void* v, int B, int H
   if (P > 1) {
     if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, true>, G::lds, attr1[dev])) != hipSuccess) return e;
     hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, true>), dim3(BH * P), dim3(256), G::lds, stream, phiq, phik,
-                       static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots);
+                       static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots,
+                       KIND == 1 ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, false>), dim3(BH * P), dim3(256), G::lds, stream, phiq, phik,
-                     static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots);
+                     static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots,
+                     KIND == 1 ? 1 : 0);
   return hipGetLastError();
 }
 
