@@ -14,7 +14,8 @@
 //   du = dtheta pi / (1 + |u|)^2,  domega_a = sum over tokens of r' (g_r + g_rc cos y + g_rs sin y).
 //
 // Work split.  Phi(Q) and Phi(K) are featurized once into the workspace (element type of the call).  A
-// statistics pass (the forward kernel in its STATS mode) writes (Dn_t, delta_t).  Then, flash-attention
+// statistics pass (the forward kernel in its STATS mode) writes (Dn_t, delta_t).  At p = 1 the feature
+// gradients and dv then come from the chunked recurrences of backward_chunked.hip.  At p = 2, flash-attention
 // style, one kernel walks key blocks for each 32-query tile of a wave (dPhi(Q)), and one walks query blocks
 // for each 32-key tile (dPhi(K) and dv); both recompute the score and <g, v> tiles on 32x32x16 bf16 MFMA
 // (32x32x2 fp32 for fp32 inputs).  A wave keeps a 32 x 192 fp32 slice of its gradient in accumulators (32 x 128
@@ -25,13 +26,18 @@
 // du and per-block omega partials, which two small kernels sum in a fixed order (bitwise deterministic).
 #include <atomic>
 
-#include "prefill_common.h"
+#include "feature_tiles.h"
 
 namespace sanatan {
 
 hipError_t launch_quadratic_stats(const void* q, const void* phik, const void* v, const void* g, sanatan_dtype t,
                                   int B, int H, int T, int p, const float* rho, const MethodConsts& mc, float2* stats,
                                   hipStream_t stream);
+// backward_chunked.hip: the p = 1 feature gradients and dv as chunked recurrences, and their slot bytes
+size_t bwd_chunked_slot_bytes(int B, int H, int T);
+hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats,
+                              sanatan_dtype t, int B, int H, int T, float* dphiq, float* dphik, void* dv,
+                              float* slots, hipStream_t stream);
 
 namespace {
 
@@ -121,15 +127,6 @@ __device__ __forceinline__ typename FragT<T>::type row_frag(const T* base, int p
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     return f;
   }
-}
-
-// x - (float)rounded, packed: the part of 8 fp32 values that their bf16 rounding dropped
-template <typename T>
-__device__ __forceinline__ typename FragT<T>::type residual8(const float (&x)[8], const typename FragT<T>::type& rounded) {
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) r[i] = x[i] - (float)rounded[i];
-  return pack8f<T>(r);
 }
 
 // dPhi(Q) for one 32-query tile per wave (four per workgroup), feature tiles FT0 .. FT0 + NFT - 1 (32 features
@@ -441,7 +438,7 @@ hipError_t set_lds(Kern k, int bytes, std::atomic<bool>& flag) {
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t rho, phiq, phik, stats, dphiq, dphik, dom, total;
+  size_t rho, phiq, phik, stats, dphiq, dphik, dom, slots, total;
 };
 BwdLayout bwd_layout(int B, int H, int T, sanatan_dtype t) {
   const size_t el = t == SANATAN_BF16 ? 2 : 4;
@@ -455,7 +452,8 @@ BwdLayout bwd_layout(int B, int H, int T, sanatan_dtype t) {
   L.dphiq = L.stats + al256(BHT * 8);
   L.dphik = L.dphiq + al256(BHT * kF * 4);
   L.dom = L.dphik + al256(BHT * kF * 4);
-  L.total = L.dom + al256(2 * nblk * kD * 4) + al256((size_t)2 * B * H * kD * 4);
+  L.slots = L.dom + al256(2 * nblk * kD * 4) + al256((size_t)2 * B * H * kD * 4);
+  L.total = L.slots + al256(bwd_chunked_slot_bytes(B, H, T));
   return L;
 }
 
@@ -478,11 +476,17 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   if ((e = launch_featurize(q, dt, B, H, Tn, pos0, mc, phiq, dt, stream)) != hipSuccess) return e;
   if ((e = launch_featurize(k, dt, B, H, Tn, pos0, mc, phik, dt, stream)) != hipSuccess) return e;
   if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) return e;
+  if constexpr (P == 1) {
+    // p = 1: the feature gradients and dv as chunked recurrences, linear in T
+    if ((e = launch_bwd_chunked(phiq, phik, v, g, stats, dt, B, H, Tn, dphiq, dphik, dv,
+                                reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
+      return e;
+  } else {
 
   // feature-gradient passes: NFT feature tiles of 32 each per pass (the 32 x 32 NFT fp32 slice of a wave in
   // accumulators, next to its 20 operand fragments); dv comes with the first dK pass
   constexpr int NFT = sizeof(T) == 4 ? 4 : 6;
-  const int BH = B * H, nqb = (Tn + 127) / 128, nkb_all = (Tn + kBlk - 1) / kBlk;
+  const int nqb = (Tn + 127) / 128, nkb_all = (Tn + kBlk - 1) / kBlk, BH = B * H;
   static std::atomic<bool> attr[8][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
@@ -509,7 +513,8 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   if constexpr (3 * NFT == 12) {
     if ((e = pass(std::integral_constant<int, 2 * NFT>(), std::false_type(), 2)) != hipSuccess) return e;
   }
-  const int ntiles = (Tn + 31) / 32, nblk = BH * ntiles;
+  }
+  const int BH = B * H, ntiles = (Tn + 31) / 32, nblk = BH * ntiles;
   hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(q), dphiq,
                      rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dq), dom);
   if ((e = hipGetLastError()) != hipSuccess) return e;

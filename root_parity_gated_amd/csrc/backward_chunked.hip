@@ -1,0 +1,681 @@
+// backward_chunked.hip -- the p = 1 backward pass as chunked linear recurrences: the feature gradients dPhi(q),
+// dPhi(k) and dv in time linear in T.
+//
+// SANATAN reading notes, §2.7: at p = 1 the attention is the recurrence of an explicit feature map, and so is
+// each of its gradients.  With the forward statistics Dn_t (denominator, epsilon included) and
+// delta_t = <g_t, o_t> (g = dout), the gradient of kappa_ts is (<g_t, v_s> - delta_t) / Dn_t for s <= t, so
+//   dPhi(q_t) = (S_t g_t - delta_t z_t) / Dn_t,   S_t = sum_{s<=t} Phi(k_s) v_s^T,  z_t = sum_{s<=t} Phi(k_s),
+//   dPhi(k_s) = R_s v_s - r_s,  dv_s = R_s^T Phi(k_s),
+//   R_s = sum_{t>=s} Phi(q_t) g_t^T / Dn_t,  r_s = sum_{t>=s} Phi(q_t) delta_t / Dn_t.
+// Per 32-token chunk, with A[t][s] = <g_t, v_s> - delta_t and the masked scores P[t][s] = <Phi(q_t), Phi(k_s)>:
+//   dPhi(q_t) = (S g_t - delta_t z + sum_{s<=t} A[t][s] Phi(k_s)) / Dn_t        (S, z: the keys before the chunk)
+//   dPhi(k_s) = R v_s - r + sum_{t>=s} Phi(q_t) A[t][s] / Dn_t                  (R, r: the queries after it)
+//   dv_s      = R^T Phi(k_s) + sum_{t>=s} P[t][s] g_t / Dn_t.
+// Phi(Q) and Phi(K) are materialized (6d = 384 features, the call's element type); the statistics come in as
+// float2 (Dn_t, delta_t) per token.
+//
+// Work split.  Each sequence is cut into NP pieces of whole chunks.  One launch runs two workgroups per piece:
+// the forward one walks its chunks in order carrying S^T (as 32 x 32 accumulator tiles [value][feature]) and z,
+// the reverse one walks them backwards carrying R^T and r.  Four waves share a workgroup, wave w owning feature
+// tiles w, w + 4, w + 8 (32 features each).  The dPhi products need no exchange between waves; dv sums over all
+// features, so its four partials meet in LDS in a fixed order.  R^T Phi(k) contracts over features, the other
+// way round from R v, so each R^T tile also passes through a wave-private LDS tile read back transposed.  With
+// NP > 1 an increments pass first writes every piece's own S and z (pieces 0 .. NP-2) and R and r (pieces
+// 1 .. NP-1) to slots; a piece starts from the sum of its predecessors' (forward) or successors' (reverse)
+// slots, in a fixed order.
+// Operands: bf16 32x32x16 MFMA (fp32 32x32x2 for fp32 inputs), fp32 accumulation.  With bf16 operands, A, the
+// states S and R, and g / Dn in the update of R enter the products as their rounding plus the rounding of their
+// residual: S g and delta z (R v and r) nearly cancel, so a single rounding would leave an error near the
+// result's own size.  dv takes R once rounded (its terms do not cancel).
+#include <atomic>
+
+#include "feature_tiles.h"
+
+namespace sanatan {
+namespace {
+
+constexpr int kBC = 32;  // chunk tokens
+
+template <typename T>
+struct CGeom {
+  static constexpr int Fp = kF;                      // 384 features
+  static constexpr int NFT = Fp / 32, NW = NFT / 4;  // feature tiles, per wave
+  static constexpr int EL = 16 / (int)sizeof(T);      // elements per 16-byte piece
+  static constexpr int KP = Fp + EL, VP = kDV + EL, RLP = kDV + EL, RP = 68;
+  // bf16: Phi(Q) rows staged in LDS like Phi(K); fp32 reads them from global memory (the rows would not fit)
+  static constexpr bool QLDS = sizeof(T) == 2;
+  static constexpr int kt_b = kBC * KP * (int)sizeof(T);
+  static constexpr int qt_b = QLDS ? kt_b : 0;
+  static constexpr int v_b = kBC * VP * (int)sizeof(T);
+  static constexpr int o_kt = 0, o_qt = o_kt + kt_b, o_vt = o_qt + qt_b, o_gt = o_vt + v_b, o_ht = o_gt + v_b;
+  // bf16: g / Dn is staged as its rounding (o_ht) and the rounding of its residual (o_hl)
+  static constexpr int hl_b = sizeof(T) == 2 ? v_b : 0;
+  static constexpr int o_hl = o_ht + v_b;
+  static constexpr int o_st = o_hl + hl_b;         // 1 / Dn, delta, delta / Dn of the chunk's tokens
+  static constexpr int o_zs = o_st + 3 * kBC * 4;  // z (forward) or r (reverse) [Fp]
+  static constexpr int o_rs = o_zs + Fp * 4;       // r in the increments pass [Fp]
+  static constexpr int o_rl = o_rs + Fp * 4;       // per wave: one packed R^T tile as [32 features][RLP]
+  static constexpr int rl_b = 4 * 32 * RLP * (int)sizeof(T);
+  static constexpr int o_red = o_rl + rl_b;        // dv partials [4 waves][32 keys][RP]
+  static constexpr int lds = o_red + 4 * kBC * RP * 4;
+  static constexpr size_t SLOT = (size_t)Fp * kDV + Fp;  // one state: the tiles, then the vector
+  static_assert(kBC * (Fp / EL) % 256 == 0 && kBC * (kDV / EL) % 256 == 0, "whole pieces per thread");
+  static_assert(o_st % 16 == 0 && o_rl % 16 == 0 && o_red % 16 == 0, "aligned LDS regions");
+};
+
+// Pieces per sequence: with two workgroups per piece, as many as keep every workgroup on a compute unit of its
+// own (at most 8, at most one per chunk).
+int bwd_pieces(int B, int H, int Tn) {
+  const long long BH = (long long)B * H, nch = (Tn + kBC - 1) / kBC;
+  long long P = device_cus() / (2 * BH);
+  if (P > 8) P = 8;
+  if (P > nch) P = nch;
+  return P < 1 ? 1 : (int)P;
+}
+
+// 16 bytes of T scaled by s (hi), and for bf16 the rounding of what that rounding dropped (lo)
+template <typename T>
+__device__ __forceinline__ void scale16(const u32x4& x, float s, u32x4& hi, u32x4& lo) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, x);
+    bf16x8 b, c;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float y = (float)a[i] * s;
+      b[i] = (__bf16)y;
+      c[i] = (__bf16)(y - (float)b[i]);
+    }
+    hi = __builtin_bit_cast(u32x4, b);
+    lo = __builtin_bit_cast(u32x4, c);
+  } else {
+    const f32x4 a = __builtin_bit_cast(f32x4, x);
+    const f32x4 b = {a[0] * s, a[1] * s, a[2] * s, a[3] * s};
+    hi = __builtin_bit_cast(u32x4, b);
+    lo = hi;
+  }
+}
+
+// One chunk's staged operands (tokens t0 .. t0 + nv - 1 of a sequence) held in registers between their global
+// loads and their LDS stores, so that the next chunk's loads are in flight while the current one computes.
+// Flags: Phi(K), Phi(Q) (staged for bf16 only), V, g, and g / Dn; the statistics of the chunk's tokens (1 / Dn,
+// delta and delta / Dn) always.  Rows past nv are stored as zeros (statistics too); rows are clamped into the
+// sequence before they are read.  A workgroup-uniform mask can skip the feature rows (kq: Phi(K) and V; qq:
+// Phi(Q) and g / Dn).
+template <typename T, bool SK, bool SQ, bool SV, bool SG, bool SH>
+struct ChunkRegs {
+  using G = CGeom<T>;
+  static constexpr int EL = G::EL, FPC = G::Fp / EL, VPC = kDV / EL;
+  static constexpr int NF = kBC * FPC / 256, NV = kBC * VPC / 256;
+  static constexpr bool LQ = SQ && G::QLDS, LG = SG || SH;
+  u32x4 k[SK ? NF : 1], q[LQ ? NF : 1], vv[SV ? NV : 1], gg[LG ? NV : 1];
+  float dn_row[SH ? NV : 1];
+  float2 st;
+  int t0, nv;
+
+  __device__ __forceinline__ void load(const T* kp, const T* qp, const T* vp, const T* gp, const float2* sp, int t0_,
+                                       int nv_, int tid, bool kq = true, bool qq = true) {
+    t0 = t0_;
+    nv = nv_;
+    if (tid < kBC) st = sp[t0 + min(tid, nv - 1)];
+#pragma unroll
+    for (int i = 0; i < NF; i++) {
+      const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
+      const size_t off = (size_t)(t0 + min(s, nv - 1)) * G::Fp + c;
+      if (SK && kq) k[i] = *reinterpret_cast<const u32x4*>(kp + off);
+      if (LQ && qq) q[i] = *reinterpret_cast<const u32x4*>(qp + off);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int e = tid + 256 * i, s = e / VPC, c = (e % VPC) * EL;
+      const int row = t0 + min(s, nv - 1);
+      const size_t off = (size_t)row * kDV + c;
+      if (SV && kq) vv[i] = *reinterpret_cast<const u32x4*>(vp + off);
+      if (LG && (SG || qq)) gg[i] = *reinterpret_cast<const u32x4*>(gp + off);
+      if (SH && qq) dn_row[i] = sp[row].x;
+    }
+  }
+
+  __device__ __forceinline__ void store(char* smem, int tid, bool kq = true, bool qq = true) const {
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    if (tid < kBC) {
+      float* sl = reinterpret_cast<float*>(smem + G::o_st);
+      const bool ok = tid < nv;
+      const float inv = ok ? 1.0f / st.x : 0.0f, dl = ok ? st.y : 0.0f;
+      sl[tid] = inv;
+      sl[kBC + tid] = dl;
+      sl[2 * kBC + tid] = dl * inv;
+    }
+    T* KT = reinterpret_cast<T*>(smem + G::o_kt);
+    T* QT = reinterpret_cast<T*>(smem + G::o_qt);
+#pragma unroll
+    for (int i = 0; i < NF; i++) {
+      const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
+      if (SK && kq) *reinterpret_cast<u32x4*>(KT + s * G::KP + c) = s < nv ? k[i] : zero4;
+      if (LQ && qq) *reinterpret_cast<u32x4*>(QT + s * G::KP + c) = s < nv ? q[i] : zero4;
+    }
+    T* VT = reinterpret_cast<T*>(smem + G::o_vt);
+    T* GT = reinterpret_cast<T*>(smem + G::o_gt);
+    T* HT = reinterpret_cast<T*>(smem + G::o_ht);
+    T* HL = reinterpret_cast<T*>(smem + G::o_hl);
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int e = tid + 256 * i, s = e / VPC, c = (e % VPC) * EL;
+      const bool ok = s < nv;
+      if (SV && kq) *reinterpret_cast<u32x4*>(VT + s * G::VP + c) = ok ? vv[i] : zero4;
+      if (SG) *reinterpret_cast<u32x4*>(GT + s * G::VP + c) = ok ? gg[i] : zero4;
+      if (SH && qq) {
+        u32x4 hi, lo;
+        scale16<T>(gg[i], 1.0f / dn_row[i], hi, lo);
+        *reinterpret_cast<u32x4*>(HT + s * G::VP + c) = ok ? hi : zero4;
+        if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x4*>(HL + s * G::VP + c) = ok ? lo : zero4;
+      }
+    }
+  }
+};
+
+// A state slot in the accumulator's own order: tile (w, i, vt), register r, lane l at
+// (((w NW + i) 2 + vt) 16 + r) 64 + l, then the feature vector [Fp].
+template <typename T>
+__device__ __forceinline__ void slot_add(const float* sl, f32x16 (&A)[CGeom<T>::NW][2], float* vec, int w, int l,
+                                         int tid) {
+  constexpr int NW = CGeom<T>::NW;
+#pragma unroll
+  for (int i = 0; i < NW; i++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) A[i][vt][r] += sl[((size_t)((w * NW + i) * 2 + vt) * 16 + r) * 64 + l];
+  for (int f = tid; f < kF; f += 256) vec[f] += sl[(size_t)kF * kDV + f];
+}
+template <typename T>
+__device__ __forceinline__ void slot_put(float* sl, const f32x16 (&A)[CGeom<T>::NW][2], const float* vec, int w,
+                                         int l, int tid) {
+  constexpr int NW = CGeom<T>::NW;
+#pragma unroll
+  for (int i = 0; i < NW; i++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) sl[((size_t)((w * NW + i) * 2 + vt) * 16 + r) * 64 + l] = A[i][vt][r];
+  for (int f = tid; f < kF; f += 256) sl[(size_t)kF * kDV + f] = vec[f];
+}
+
+// Tokens [t_lo, t_hi) of piece p of NP (whole chunks).
+__device__ __forceinline__ void piece_bounds(int p, int NP, int Tn, int& t_lo, int& t_hi) {
+  const int nch = (Tn + kBC - 1) / kBC;
+  t_lo = (int)((long long)p * nch / NP) * kBC;
+  t_hi = min(Tn, (int)((long long)(p + 1) * nch / NP) * kBC);
+}
+
+// Feature fragment of Phi(Q) with tokens along K (lane row = feature col0 + l % 32): from the LDS tile (bf16)
+// or from global memory (fp32)
+template <typename T>
+__device__ __forceinline__ typename FragT<T>::type q_tokfrag(const char* smem, const T* qp, int t0, int tok0,
+                                                             int col0, int l, int tmax) {
+  using G = CGeom<T>;
+  if constexpr (G::QLDS) {
+    return lds_tokfrag(reinterpret_cast<const T*>(smem + G::o_qt), G::KP, tok0, col0, l);
+  } else {
+    return gtok_frag(qp, G::Fp, t0 + tok0, col0, l, tmax);
+  }
+}
+
+// The increments pass: piece p's own S^T and z (p < NP - 1) and R^T and r (p > 0), to its slots.
+template <typename T>
+__global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
+                                                          const T* __restrict__ v, const T* __restrict__ g,
+                                                          const float2* __restrict__ stats, int Tn, int NP,
+                                                          float* __restrict__ sslots, float* __restrict__ rslots) {
+  using G = CGeom<T>;
+  typedef typename FragT<T>::type Frag;
+  constexpr int NW = G::NW, Fp = G::Fp;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
+  const int bh = blockIdx.x / NP, p = blockIdx.x % NP;
+  const bool doS = p < NP - 1, doR = p > 0;
+  int t_lo, t_hi;
+  piece_bounds(p, NP, Tn, t_lo, t_hi);
+  const size_t so = (size_t)bh * Tn;
+  const T* qp = phiq + so * Fp;
+  const T* kp = phik + so * Fp;
+  const T* vp = v + so * kDV;
+  const T* gp = g + so * kDV;
+  const float2* sp = stats + so;
+  const T* KT = reinterpret_cast<const T*>(smem + G::o_kt);
+  const T* VT = reinterpret_cast<const T*>(smem + G::o_vt);
+  const T* HT = reinterpret_cast<const T*>(smem + G::o_ht);
+  const T* HL = reinterpret_cast<const T*>(smem + G::o_hl);
+  const float* dh = reinterpret_cast<const float*>(smem + G::o_st) + 2 * kBC;
+  float* zs = reinterpret_cast<float*>(smem + G::o_zs);
+  float* rs = reinterpret_cast<float*>(smem + G::o_rs);
+  f32x16 ST[NW][2], RT[NW][2];
+#pragma unroll
+  for (int i = 0; i < NW; i++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++) {
+      zero16(ST[i][vt]);
+      zero16(RT[i][vt]);
+    }
+  for (int f = tid; f < Fp; f += 256) zs[f] = rs[f] = 0.0f;
+  ChunkRegs<T, true, true, true, false, true> R;
+  R.load(kp, qp, vp, gp, sp, t_lo, min(kBC, t_hi - t_lo), tid, doS, doR);
+  for (int t0 = t_lo; t0 < t_hi; t0 += kBC) {
+    R.store(smem, tid, doS, doR);
+    __syncthreads();
+    if (t0 + kBC < t_hi) R.load(kp, qp, vp, gp, sp, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid, doS, doR);
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      const int ft = w + 4 * i;
+      float zsum = 0.0f, rsum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        if (doS) {
+          const Frag KF = lds_tokfrag(KT, G::KP, 16 * ks, 32 * ft, l);
+          zsum = frag_sum(KF, zsum);
+#pragma unroll
+          for (int vt = 0; vt < 2; vt++) mma32(ST[i][vt], lds_tokfrag(VT, G::VP, 16 * ks, 32 * vt, l), KF);
+        }
+        if (doR) {
+          const Frag QF = q_tokfrag<T>(smem, qp, t0, 16 * ks, 32 * ft, l, Tn - 1);
+#pragma unroll
+          for (int e = 0; e < 8; e++) rsum = fmaf((float)QF[e], dh[16 * ks + 8 * (e >> 2) + 4 * h + (e & 3)], rsum);
+#pragma unroll
+          for (int vt = 0; vt < 2; vt++) {
+            mma32(RT[i][vt], lds_tokfrag(HT, G::VP, 16 * ks, 32 * vt, l), QF);
+            if constexpr (sizeof(T) == 2) mma32(RT[i][vt], lds_tokfrag(HL, G::VP, 16 * ks, 32 * vt, l), QF);
+          }
+        }
+      }
+      zsum = xor32_sum(zsum);
+      rsum = xor32_sum(rsum);
+      if (h == 0) {
+        if (doS) zs[32 * ft + n32] += zsum;
+        if (doR) rs[32 * ft + n32] += rsum;
+      }
+    }
+    __syncthreads();
+  }
+  if (doS) slot_put<T>(sslots + ((size_t)bh * NP + p) * G::SLOT, ST, zs, w, l, tid);
+  if (doR) slot_put<T>(rslots + ((size_t)bh * NP + p) * G::SLOT, RT, rs, w, l, tid);
+}
+
+// Forward direction: dPhi(q) of one piece.
+template <typename T>
+__device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, const T* __restrict__ v,
+                                         const T* __restrict__ g, const float2* __restrict__ stats, int Tn, int NP,
+                                         const float* __restrict__ sslots, float* __restrict__ dphiq, char* smem) {
+  using G = CGeom<T>;
+  typedef typename FragT<T>::type Frag;
+  constexpr int NW = G::NW, Fp = G::Fp;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
+  const int bh = blk / NP, p = blk % NP;
+  int t_lo, t_hi;
+  piece_bounds(p, NP, Tn, t_lo, t_hi);
+  const size_t so = (size_t)bh * Tn;
+  const T* kp = phik + so * Fp;
+  const T* vp = v + so * kDV;
+  const T* gp = g + so * kDV;
+  const float2* sp = stats + so;
+  float* dq = dphiq + so * Fp;
+  const T* KT = reinterpret_cast<const T*>(smem + G::o_kt);
+  const T* VT = reinterpret_cast<const T*>(smem + G::o_vt);
+  const T* GT = reinterpret_cast<const T*>(smem + G::o_gt);
+  const float* st = reinterpret_cast<const float*>(smem + G::o_st);
+  float* zs = reinterpret_cast<float*>(smem + G::o_zs);
+  // S^T tiles: tile (i, vt) holds S[32 ft + n32][32 vt + 8 j + 4 h + i4] in register 4 j + i4, ft = w + 4 i
+  f32x16 ST[NW][2];
+#pragma unroll
+  for (int i = 0; i < NW; i++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++) zero16(ST[i][vt]);
+  for (int f = tid; f < Fp; f += 256) zs[f] = 0.0f;
+  for (int q = 0; q < p; q++) slot_add<T>(sslots + ((size_t)bh * NP + q) * G::SLOT, ST, zs, w, l, tid);
+  ChunkRegs<T, true, false, true, true, false> R;
+  R.load(kp, nullptr, vp, gp, sp, t_lo, min(kBC, t_hi - t_lo), tid);
+  for (int t0 = t_lo; t0 < t_hi; t0 += kBC) {
+    const int nv = R.nv;
+    R.store(smem, tid);
+    __syncthreads();
+    if (t0 + kBC < t_hi) R.load(kp, nullptr, vp, gp, sp, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid);
+    // this lane's query t = n32: A[t][s] = <g_t, v_s> - delta_t over s <= t, as accumulator [s][t]
+    const float inv = st[n32], dlt = st[kBC + n32];
+    f32x16 acc;
+    zero16(acc);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++)
+      mma32(acc, slot_frag<T>(VT + n32 * G::VP, 16 * kk, h), slot_frag<T>(GT + n32 * G::VP, 16 * kk, h));
+    float a0[8], a1[8];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int s = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float x = s <= n32 ? acc[r] - dlt : 0.0f;
+      if (r < 8) a0[r] = x;
+      else a1[r - 8] = x;
+    }
+    const Frag A0 = pack8f<T>(a0), A1 = pack8f<T>(a1);
+    Frag R0 = A0, R1 = A1;
+    if constexpr (sizeof(T) == 2) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      const int ft = w + 4 * i;
+      f32x16 d;  // dPhi(q) before the scaling, as [feature][query]
+      zero16(d);
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+          float x[8];
+#pragma unroll
+          for (int s = 0; s < 8; s++) x[s] = ST[i][vt][8 * kk + s];
+          const Frag SF = pack8f<T>(x), GF = slot_frag<T>(GT + n32 * G::VP, 32 * vt + 16 * kk, h);
+          mma32(d, SF, GF);
+          if constexpr (sizeof(T) == 2) mma32(d, residual8<T>(x, SF), GF);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        const Frag KF = lds_tokfrag(KT, G::KP, 16 * ks, 32 * ft, l);
+        mma32(d, KF, ks ? A1 : A0);
+        if constexpr (sizeof(T) == 2) mma32(d, KF, ks ? R1 : R0);
+      }
+      if (n32 < nv) {
+        float* o = dq + (size_t)(t0 + n32) * Fp;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int f0 = 32 * ft + 8 * j + 4 * h;
+          const float4 z4 = *reinterpret_cast<const float4*>(zs + f0);
+          *reinterpret_cast<float4*>(o + f0) =
+              make_float4((d[4 * j] - dlt * z4.x) * inv, (d[4 * j + 1] - dlt * z4.y) * inv,
+                          (d[4 * j + 2] - dlt * z4.z) * inv, (d[4 * j + 3] - dlt * z4.w) * inv);
+        }
+      }
+    }
+    // S += Phi(K)^T V and z += Phi(K)^T 1 over this wave's tiles (each wave reads and updates its own z entries)
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      const int ft = w + 4 * i;
+      float zsum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        const Frag KF = lds_tokfrag(KT, G::KP, 16 * ks, 32 * ft, l);
+        zsum = frag_sum(KF, zsum);
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) mma32(ST[i][vt], lds_tokfrag(VT, G::VP, 16 * ks, 32 * vt, l), KF);
+      }
+      zsum = xor32_sum(zsum);
+      if (h == 0) zs[32 * ft + n32] += zsum;
+    }
+    __syncthreads();  // the next chunk's staging overwrites the tiles
+  }
+}
+
+// Reverse direction: dPhi(k) and dv of one piece.
+template <typename T>
+__device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
+                                          const T* __restrict__ v, const T* __restrict__ g,
+                                          const float2* __restrict__ stats, int Tn, int NP,
+                                          const float* __restrict__ rslots, float* __restrict__ dphik,
+                                          T* __restrict__ dv, char* smem) {
+  using G = CGeom<T>;
+  typedef typename FragT<T>::type Frag;
+  constexpr int NW = G::NW, Fp = G::Fp;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
+  const int bh = blk / NP, p = blk % NP;
+  int t_lo, t_hi;
+  piece_bounds(p, NP, Tn, t_lo, t_hi);
+  const size_t so = (size_t)bh * Tn;
+  const T* qp = phiq + so * Fp;
+  const T* kp = phik + so * Fp;
+  const T* vp = v + so * kDV;
+  const T* gp = g + so * kDV;
+  const float2* sp = stats + so;
+  float* dk = dphik + so * Fp;
+  T* dvp = dv + so * kDV;
+  const T* KT = reinterpret_cast<const T*>(smem + G::o_kt);
+  const T* QT = reinterpret_cast<const T*>(smem + G::o_qt);
+  const T* VT = reinterpret_cast<const T*>(smem + G::o_vt);
+  const T* GT = reinterpret_cast<const T*>(smem + G::o_gt);
+  const T* HT = reinterpret_cast<const T*>(smem + G::o_ht);
+  const T* HL = reinterpret_cast<const T*>(smem + G::o_hl);
+  const float* st = reinterpret_cast<const float*>(smem + G::o_st);
+  float* rs = reinterpret_cast<float*>(smem + G::o_zs);
+  T* RL = reinterpret_cast<T*>(smem + G::o_rl) + w * 32 * G::RLP;
+  float* red = reinterpret_cast<float*>(smem + G::o_red);
+  // R^T tiles: tile (i, vt) holds R[32 ft + n32][32 vt + 8 j + 4 h + i4] in register 4 j + i4, ft = w + 4 i
+  f32x16 RT[NW][2];
+#pragma unroll
+  for (int i = 0; i < NW; i++)
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++) zero16(RT[i][vt]);
+  for (int f = tid; f < Fp; f += 256) rs[f] = 0.0f;
+  for (int q = NP - 1; q > p; q--) slot_add<T>(rslots + ((size_t)bh * NP + q) * G::SLOT, RT, rs, w, l, tid);
+  const int c_lo = t_lo / kBC, c_hi = (t_hi + kBC - 1) / kBC;
+  ChunkRegs<T, true, true, true, true, true> R;
+  R.load(kp, qp, vp, gp, sp, (c_hi - 1) * kBC, min(kBC, t_hi - (c_hi - 1) * kBC), tid);
+  for (int c = c_hi - 1; c >= c_lo; c--) {
+    const int t0 = c * kBC, nv = R.nv;
+    R.store(smem, tid);
+    __syncthreads();
+    if (c > c_lo) R.load(kp, qp, vp, gp, sp, t0 - kBC, kBC, tid);
+    // this lane's key s = n32.  <g_t, v_s> and this wave's part of the scores, as accumulators [t][s]
+    f32x16 gv, sc;
+    zero16(gv);
+    zero16(sc);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++)
+      mma32(gv, slot_frag<T>(GT + n32 * G::VP, 16 * kk, h), slot_frag<T>(VT + n32 * G::VP, 16 * kk, h));
+    const T* qrow = G::QLDS ? QT + n32 * G::KP : qp + (size_t)min(t0 + n32, Tn - 1) * Fp;
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) {
+        const int base = 32 * (w + 4 * i) + 16 * kk;
+        mma32(sc, slot_frag<T>(qrow, base, h), slot_frag<T>(KT + n32 * G::KP, base, h));
+      }
+    // A[t][s] / Dn_t and P[t][s] / Dn_t over t >= s (1 / Dn is zero past the chunk's end)
+    float a0[8], a1[8], p0[8], p1[8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int tb = 8 * j + 4 * h;
+      const float4 inv4 = *reinterpret_cast<const float4*>(st + tb);
+      const float4 dl4 = *reinterpret_cast<const float4*>(st + kBC + tb);
+      const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w}, dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int r = 4 * j + e;
+        const bool keep = tb + e >= n32;
+        const float x = keep ? (gv[r] - dl[e]) * inv[e] : 0.0f;
+        const float y = keep ? sc[r] * inv[e] : 0.0f;
+        if (r < 8) a0[r] = x, p0[r] = y;
+        else a1[r - 8] = x, p1[r - 8] = y;
+      }
+    }
+    const Frag A0 = pack8f<T>(a0), A1 = pack8f<T>(a1), P0 = pack8f<T>(p0), P1 = pack8f<T>(p1);
+    Frag R0 = A0, R1 = A1;
+    if constexpr (sizeof(T) == 2) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
+    // dv^T [value][key]: the chunk's queries, then R^T Phi(k) tile by tile below
+    f32x16 dvt[2];
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++) {
+      zero16(dvt[vt]);
+      mma32(dvt[vt], lds_tokfrag(GT, G::VP, 0, 32 * vt, l), P0);
+      mma32(dvt[vt], lds_tokfrag(GT, G::VP, 16, 32 * vt, l), P1);
+    }
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      const int ft = w + 4 * i;
+      Frag RF[2][2];
+      f32x16 d;  // dPhi(k) + r, as [feature][key]
+      zero16(d);
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+          float x[8];
+#pragma unroll
+          for (int s = 0; s < 8; s++) x[s] = RT[i][vt][8 * kk + s];
+          RF[vt][kk] = pack8f<T>(x);
+          const Frag VF = slot_frag<T>(VT + n32 * G::VP, 32 * vt + 16 * kk, h);
+          mma32(d, RF[vt][kk], VF);
+          if constexpr (sizeof(T) == 2) mma32(d, residual8<T>(x, RF[vt][kk]), VF);
+        }
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++) {
+        const Frag QF = q_tokfrag<T>(smem, qp, t0, 16 * kt, 32 * ft, l, Tn - 1);
+        mma32(d, QF, kt ? A1 : A0);
+        if constexpr (sizeof(T) == 2) mma32(d, QF, kt ? R1 : R0);
+      }
+      if (n32 < nv) {
+        float* o = dk + (size_t)(t0 + n32) * Fp;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int f0 = 32 * ft + 8 * j + 4 * h;
+          const float4 r4 = *reinterpret_cast<const float4*>(rs + f0);
+          *reinterpret_cast<float4*>(o + f0) =
+              make_float4(d[4 * j] - r4.x, d[4 * j + 1] - r4.y, d[4 * j + 2] - r4.z, d[4 * j + 3] - r4.w);
+        }
+      }
+      // the packed tile as R[feature][value] in this wave's LDS tile, read back with values along the rows
+      // (the wave's LDS accesses complete in order, so no barrier is needed between the stores and the reads)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+          T* dst = RL + n32 * G::RLP + 32 * vt + 16 * kk + 4 * h;
+          if constexpr (sizeof(T) == 2) {
+            const u32x4 wd = __builtin_bit_cast(u32x4, RF[vt][kk]);
+            *reinterpret_cast<u32x2*>(dst) = (u32x2){wd[0], wd[1]};
+            *reinterpret_cast<u32x2*>(dst + 8) = (u32x2){wd[2], wd[3]};
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(RF[vt][kk][0], RF[vt][kk][1], RF[vt][kk][2], RF[vt][kk][3]);
+            *reinterpret_cast<float4*>(dst + 8) =
+                make_float4(RF[vt][kk][4], RF[vt][kk][5], RF[vt][kk][6], RF[vt][kk][7]);
+          }
+        }
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+          mma32(dvt[vt], lds_tokfrag(RL, G::RLP, 16 * kk, 32 * vt, l),
+                slot_frag<T>(KT + n32 * G::KP, 32 * ft + 16 * kk, h));
+    }
+    // the four waves' dv partials meet in LDS; summed in a fixed order
+#pragma unroll
+    for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *reinterpret_cast<float4*>(red + (w * kBC + n32) * G::RP + 32 * vt + 8 * j + 4 * h) =
+            make_float4(dvt[vt][4 * j], dvt[vt][4 * j + 1], dvt[vt][4 * j + 2], dvt[vt][4 * j + 3]);
+    __syncthreads();
+    {
+      const int row = tid >> 3, c0 = 8 * (tid & 7);
+      if (row < nv) {
+        constexpr int WS = kBC * G::RP;
+        const float* b0 = red + row * G::RP + c0;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[e] = ((b0[e] + b0[WS + e]) + b0[2 * WS + e]) + b0[3 * WS + e];
+        T* dst = dvp + (size_t)(t0 + row) * kDV + c0;
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 ov;
+#pragma unroll
+          for (int e = 0; e < 8; e++) ov[e] = (__bf16)o[e];
+          *reinterpret_cast<bf16x8*>(dst) = ov;
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+      }
+    }
+    // R += Phi(Q)^T (G / Dn) and r += Phi(Q)^T (delta / Dn) with the chunk's queries (each wave reads and updates
+    // its own r entries)
+    const float* dh = st + 2 * kBC;
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      const int ft = w + 4 * i;
+      float rsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++) {
+        const Frag QF = q_tokfrag<T>(smem, qp, t0, 16 * kt, 32 * ft, l, Tn - 1);
+#pragma unroll
+        for (int e = 0; e < 8; e++) rsum = fmaf((float)QF[e], dh[16 * kt + 8 * (e >> 2) + 4 * h + (e & 3)], rsum);
+#pragma unroll
+        for (int vt = 0; vt < 2; vt++) {
+          mma32(RT[i][vt], lds_tokfrag(HT, G::VP, 16 * kt, 32 * vt, l), QF);
+          if constexpr (sizeof(T) == 2) mma32(RT[i][vt], lds_tokfrag(HL, G::VP, 16 * kt, 32 * vt, l), QF);
+        }
+      }
+      rsum = xor32_sum(rsum);
+      if (h == 0) rs[32 * ft + n32] += rsum;
+    }
+    __syncthreads();  // the next chunk's staging overwrites the tiles and the reduction buffer
+  }
+}
+
+// Workgroups [0, BH NP) run the forward direction, [BH NP, 2 BH NP) the reverse one.
+template <typename T>
+__global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
+                                                           const T* __restrict__ v, const T* __restrict__ g,
+                                                           const float2* __restrict__ stats, int Tn, int NP,
+                                                           const float* __restrict__ sslots,
+                                                           const float* __restrict__ rslots,
+                                                           float* __restrict__ dphiq, float* __restrict__ dphik,
+                                                           T* __restrict__ dv) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nb = (int)gridDim.x / 2;
+  if ((int)blockIdx.x < nb)
+    dq_piece<T>(blockIdx.x, phik, v, g, stats, Tn, NP, sslots, dphiq, smem);
+  else
+    dkv_piece<T>(blockIdx.x - nb, phiq, phik, v, g, stats, Tn, NP, rslots, dphik, dv, smem);
+}
+
+template <typename Kern>
+hipError_t set_lds_attr(Kern k, int bytes, std::atomic<bool>& flag) {
+  if (flag.load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) flag.store(true, std::memory_order_release);
+  return e;
+}
+
+template <typename T>
+hipError_t launch_t(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats, int B,
+                    int H, int Tn, float* dphiq, float* dphik, void* dv, float* slots, hipStream_t stream) {
+  using G = CGeom<T>;
+  static std::atomic<bool> attr[2][64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const int BH = B * H, NP = bwd_pieces(B, H, Tn);
+  float* sslots = slots;
+  float* rslots = NP > 1 ? slots + (size_t)BH * NP * G::SLOT : slots;
+  const T* q = static_cast<const T*>(phiq);
+  const T* k = static_cast<const T*>(phik);
+  const T* vv = static_cast<const T*>(v);
+  const T* gg = static_cast<const T*>(g);
+  hipError_t e;
+  if (NP > 1) {
+    if ((e = set_lds_attr(bwd_incr_kernel<T>, G::lds, attr[0][dev])) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_incr_kernel<T>, dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
+                       sslots, rslots);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = set_lds_attr(bwd_chunk_kernel<T>, G::lds, attr[1][dev])) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_chunk_kernel<T>, dim3(2 * BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
+                     sslots, rslots, dphiq, dphik, static_cast<T*>(dv));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_chunked_slot_bytes(int B, int H, int T) {
+  const int NP = bwd_pieces(B, H, T);
+  return NP > 1 ? 2 * (size_t)B * H * NP * CGeom<float>::SLOT * sizeof(float) : 0;
+}
+
+hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats,
+                              sanatan_dtype t, int B, int H, int T, float* dphiq, float* dphik, void* dv,
+                              float* slots, hipStream_t stream) {
+  return t == SANATAN_BF16
+             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, dphiq, dphik, dv, slots, stream)
+             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, dphiq, dphik, dv, slots, stream);
+}
+
+}  // namespace sanatan

@@ -26,7 +26,7 @@
 // caller's state while the final piece writes it back.
 #include <atomic>
 
-#include "prefill_common.h"
+#include "feature_tiles.h"
 
 namespace sanatan {
 namespace {
@@ -136,24 +136,6 @@ struct FGeom {
   static constexpr int VPIECES = (kFC * (kDV / EL) + 255) / 256;
   static_assert(kFC * (Fp / EL) % 256 == 0, "a feature chunk is a whole number of pieces per thread");
 };
-
-// 8 features of one row, slots (h, i) <-> feature base + 8 (i / 4) + 4 h + i % 4 (the accumulator row order):
-// two 4-element vector loads
-template <typename T>
-__device__ __forceinline__ typename FragT<T>::type slot_frag(const T* row, int base, int h) {
-  typename FragT<T>::type f;
-  if constexpr (sizeof(T) == 2) {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(row + base + 4 * h);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(row + base + 8 + 4 * h);
-    const u32x4 w = {a[0], a[1], b[0], b[1]};
-    f = __builtin_bit_cast(typename FragT<T>::type, w);
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(row + base + 4 * h);
-    const float4 b = *reinterpret_cast<const float4*>(row + base + 8 + 4 * h);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-  return f;
-}
 
 template <typename T, int NFT, bool STATE_ONLY>
 __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,

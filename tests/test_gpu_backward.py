@@ -119,9 +119,18 @@ def test_backward_edge_lengths(torch_dev, T):
             assert e <= TOL["f32"], (name, p, e)
 
 
-def test_backward_shared_omega_rows(torch_dev):
+@pytest.mark.parametrize("p", [1, 2])
+def test_backward_shared_omega_rows(torch_dev, p):
     """Two batches and six heads over two omega rows: each row's gradient sums over every head using it."""
-    errs = run_case(torch_dev, 820, 2, 6, 96, "f32", 2, nph=2, pos0=12345)
+    errs = run_case(torch_dev, 820, 2, 6, 96, "f32", p, nph=2, pos0=12345)
+    for name, e in errs.items():
+        assert e <= TOL["f32"], (name, e)
+
+
+def test_backward_p1_one_piece_per_sequence(torch_dev):
+    """p = 1 with enough sequences (128) that each runs its recurrences whole, in one piece per direction (the
+    smaller cases above split every sequence into pieces that start from their neighbours' states)."""
+    errs = run_case(torch_dev, 825, 2, 64, 70, "f32", 1)
     for name, e in errs.items():
         assert e <= TOL["f32"], (name, e)
 
@@ -134,7 +143,8 @@ def test_backward_long_bf16(torch_dev, p):
         assert e <= TOL["bf16"], (name, e)
 
 
-def test_backward_deterministic(torch_dev):
+@pytest.mark.parametrize("p", [1, 2])
+def test_backward_deterministic(torch_dev, p):
     import root_parity_gated_amd as rpg
 
     torch = torch_dev
@@ -142,8 +152,8 @@ def test_backward_deterministic(torch_dev):
     prm = rpg.Params(omega=torch.from_numpy(om).cuda())
     g = dev(torch, np.random.default_rng(1).standard_normal((1, 2, 300, 64)), "bf16")
     args = [dev(torch, x, "bf16") for x in (q, k, v)] + [g]
-    a = [x.clone() for x in rpg.sanatan_attention_backward(*args, 2, prm)]
-    b = [x.clone() for x in rpg.sanatan_attention_backward(*args, 2, prm)]
+    a = [x.clone() for x in rpg.sanatan_attention_backward(*args, p, prm)]
+    b = [x.clone() for x in rpg.sanatan_attention_backward(*args, p, prm)]
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
