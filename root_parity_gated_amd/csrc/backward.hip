@@ -35,8 +35,10 @@ hipError_t launch_quadratic_stats(const void* q, const void* phik, const void* v
                                   hipStream_t stream);
 // backward_chunked.hip: the p = 1 feature gradients and dv as chunked recurrences, and their slot bytes
 size_t bwd_chunked_slot_bytes(int B, int H, int T);
+int bwd_chunked_pieces(int B, int H, int T);
 hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats,
-                              sanatan_dtype t, int B, int H, int T, float* dphiq, float* dphik, void* dv,
+                              sanatan_dtype t, int B, int H, int T, const void* q, const void* k, const float* rho,
+                              const float* omega, int nph, float kr, void* dq, void* dk, void* dv, float* dom_part,
                               float* slots, hipStream_t stream);
 
 namespace {
@@ -376,20 +378,7 @@ __global__ __launch_bounds__(256) void bwd_jacobian_kernel(const T* __restrict__
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float om4 = anchor_rev(omega[(size_t)(hd % nph) * kD + a0 + i]);
-      const float ui = x[i];
-      const float xr = ui * rcp_hw(fmaf(fabsf(ui), 2.0f, 2.0f));  // theta / (2 pi), as featurize1
-      const float y = xr + rh[i];
-      const float cy = cos_rev(y), sy = sin_rev(y);
-      const float gg = cos_rev(xr + om4);
-      const float e = exp2_hw(kr * gg);
-      const float r = fmaf(-2.0f, rcp_hw(e + 1.0f), 1.0f);
-      // r = tanh(gamma sqrt2 cos(theta + omega + pi/4)); kr = 2 sqrt2 gamma log2(e), so gamma sqrt2 = kr ln2 / 2
-      const float rp = -(kr * 0.34657359027997264f) * (1.0f - r * r) * sin_rev(xr + om4);
-      const float gr = gch[3][i] + gch[4][i] * cy + gch[5][i] * sy;
-      const float dth = rp * gr - sy * (gch[1][i] + r * gch[4][i]) + cy * (gch[2][i] + r * gch[5][i]);
-      const float den = 1.0f + fabsf(ui);
-      o[i] = dth * (3.14159265358979f / (den * den));
-      dom[i] = rp * gr;
+      feature_vjp(x[i], rh[i], om4, kr, gch[1][i], gch[2][i], gch[3][i], gch[4][i], gch[5][i], o[i], dom[i]);
     }
     st8c(du + base * kD + a0, o);
   }
@@ -478,8 +467,8 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) return e;
   if constexpr (P == 1) {
     // p = 1: the feature gradients and dv as chunked recurrences, linear in T
-    if ((e = launch_bwd_chunked(phiq, phik, v, g, stats, dt, B, H, Tn, dphiq, dphik, dv,
-                                reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
+    if ((e = launch_bwd_chunked(phiq, phik, v, g, stats, dt, B, H, Tn, q, k, rho, mc.omega, mc.nph, mc.kr, dq, dk, dv,
+                                dom, reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
       return e;
   } else {
 
@@ -515,14 +504,20 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   }
   }
   const int BH = B * H, ntiles = (Tn + 31) / 32, nblk = BH * ntiles;
-  hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(q), dphiq,
-                     rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dq), dom);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(k), dphik,
-                     rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dk), dom + (size_t)nblk * kD);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int nparts = ntiles;  // omega partial rows per (side, sequence)
+  if constexpr (P == 1) {
+    nparts = bwd_chunked_pieces(B, H, Tn);  // the chunk kernels applied the Jacobian themselves
+  } else {
+    hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(q), dphiq,
+                       rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dq), dom);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(k), dphik,
+                       rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dk),
+                       dom + (size_t)nparts * BH * kD);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   float* seq_sum = dom + (size_t)2 * nblk * kD;
-  hipLaunchKernelGGL(bwd_domega_seq_kernel, dim3(2 * BH), dim3(64), 0, stream, dom, ntiles, seq_sum);
+  hipLaunchKernelGGL(bwd_domega_seq_kernel, dim3(2 * BH), dim3(64), 0, stream, dom, nparts, seq_sum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_domega_kernel, dim3(mc.nph), dim3(64), 0, stream, seq_sum, BH, H, mc.nph, domega);
   return hipGetLastError();

@@ -12,7 +12,9 @@
 //   dPhi(k_s) = R v_s - r + sum_{t>=s} Phi(q_t) A[t][s] / Dn_t                  (R, r: the queries after it)
 //   dv_s      = R^T Phi(k_s) + sum_{t>=s} P[t][s] g_t / Dn_t.
 // Phi(Q) and Phi(K) are materialized (6d = 384 features, the call's element type); the statistics come in as
-// float2 (Dn_t, delta_t) per token.
+// float2 (Dn_t, delta_t) per token.  The feature map's Jacobian is applied in the chunk kernels themselves:
+// each wave owns 16 dims of every channel, so after a chunk a lane holds all channels' gradients of its token's
+// 8 dims and writes du (and accumulates the omega gradient) without a dPhi array.
 //
 // Work split.  Each sequence is cut into NP pieces of whole chunks.  One launch runs two workgroups per piece:
 // the forward one walks its chunks in order carrying S^T (as 32 x 32 accumulator tiles [value][feature]) and z,
@@ -95,6 +97,19 @@ __device__ __forceinline__ void scale16(const u32x4& x, float s, u32x4& hi, u32x
   }
 }
 
+// Internal feature order (LDS tiles, states, slots): dims in blocks of 16, each block's 6 channels together, so
+// that wave w owns dims 16 w .. 16 w + 15 of every channel as its tiles 3 w, 3 w + 1, 3 w + 2 (tile j: channels
+// 2 j and 2 j + 1).  Internal feature 96 m + 32 j + 16 c' + a' is channel 2 j + c', dim 16 m + a'; the
+// materialized features are channel-major (64 c + a).
+__device__ __forceinline__ int fint(int fg) {
+  const int c = fg >> 6, a = fg & 63;
+  return 96 * (a >> 4) + 32 * (c >> 1) + 16 * (c & 1) + (a & 15);
+}
+__device__ __forceinline__ int fglob(int fi) {
+  const int m = fi / 96, rem = fi % 96;
+  return 64 * (2 * (rem >> 5) + ((rem >> 4) & 1)) + 16 * m + (fi & 15);
+}
+
 // One chunk's staged operands (tokens t0 .. t0 + nv - 1 of a sequence) held in registers between their global
 // loads and their LDS stores, so that the next chunk's loads are in flight while the current one computes.
 // Flags: Phi(K), Phi(Q) (staged for bf16 only), V, g, and g / Dn; the statistics of the chunk's tokens (1 / Dn,
@@ -150,8 +165,9 @@ struct ChunkRegs {
 #pragma unroll
     for (int i = 0; i < NF; i++) {
       const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
-      if (SK && kq) *reinterpret_cast<u32x4*>(KT + s * G::KP + c) = s < nv ? k[i] : zero4;
-      if (LQ && qq) *reinterpret_cast<u32x4*>(QT + s * G::KP + c) = s < nv ? q[i] : zero4;
+      const int ci = fint(c);
+      if (SK && kq) *reinterpret_cast<u32x4*>(KT + s * G::KP + ci) = s < nv ? k[i] : zero4;
+      if (LQ && qq) *reinterpret_cast<u32x4*>(QT + s * G::KP + ci) = s < nv ? q[i] : zero4;
     }
     T* VT = reinterpret_cast<T*>(smem + G::o_vt);
     T* GT = reinterpret_cast<T*>(smem + G::o_gt);
@@ -207,8 +223,8 @@ __device__ __forceinline__ void piece_bounds(int p, int NP, int Tn, int& t_lo, i
   t_hi = min(Tn, (int)((long long)(p + 1) * nch / NP) * kBC);
 }
 
-// Feature fragment of Phi(Q) with tokens along K (lane row = feature col0 + l % 32): from the LDS tile (bf16)
-// or from global memory (fp32)
+// Feature fragment of Phi(Q) with tokens along K (lane row = internal feature col0 + l % 32): from the LDS tile
+// (bf16) or from global memory (fp32)
 template <typename T>
 __device__ __forceinline__ typename FragT<T>::type q_tokfrag(const char* smem, const T* qp, int t0, int tok0,
                                                              int col0, int l, int tmax) {
@@ -216,8 +232,62 @@ __device__ __forceinline__ typename FragT<T>::type q_tokfrag(const char* smem, c
   if constexpr (G::QLDS) {
     return lds_tokfrag(reinterpret_cast<const T*>(smem + G::o_qt), G::KP, tok0, col0, l);
   } else {
-    return gtok_frag(qp, G::Fp, t0 + tok0, col0, l, tmax);
+    return gtok_frag(qp, G::Fp, t0 + tok0, fglob(col0 + (l & 31)), l, tmax);
   }
+}
+
+// The feature map's Jacobian for this lane's token and its 8 dims 16 w + 8 hb + 4 h + e: gch[k - 1][hb][e] holds
+// the gradient of feature channel k (1 .. 5).  Writes du (element type T) and adds the omega gradients to dom.
+template <typename T>
+__device__ __forceinline__ void lane_vjp(const float (&gch)[5][2][4], const float (&u)[2][4], const float (&rh)[2][4],
+                                         const float (&om4)[2][4], float kr, T* du_row, float (&dom)[2][4]) {
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      float dm;
+      feature_vjp(u[hb][e], rh[hb][e], om4[hb][e], kr, gch[0][hb][e], gch[1][hb][e], gch[2][hb][e], gch[3][hb][e],
+                  gch[4][hb][e], o[e], dm);
+      dom[hb][e] += dm;
+    }
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; e++) ov[e] = (__bf16)o[e];
+      *reinterpret_cast<bf16x4*>(du_row + 8 * hb) = ov;
+    } else {
+      *reinterpret_cast<float4*>(du_row + 8 * hb) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// This lane's raw components (8 dims, as lane_vjp) and their phases, for token row t of the sequence
+template <typename T>
+__device__ __forceinline__ void lane_inputs(const T* up, const float* rho, int t, int a0, float (&u)[2][4],
+                                            float (&rh)[2][4]) {
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++) {
+    float x[4];
+    load4(up + (size_t)t * kD + a0 + 8 * hb, x);
+    const float4 r4 = *reinterpret_cast<const float4*>(rho + (size_t)t * kD + a0 + 8 * hb);
+#pragma unroll
+    for (int e = 0; e < 4; e++) u[hb][e] = x[e];
+    rh[hb][0] = r4.x; rh[hb][1] = r4.y; rh[hb][2] = r4.z; rh[hb][3] = r4.w;
+  }
+}
+
+// This lane's 8 omega partials summed over the 32 lanes of its half (fixed order), stored by lane 0 of the half
+__device__ __forceinline__ void store_dom(float (&dom)[2][4], float* part, int a0, int n32) {
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      float x = dom[hb][e];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off);
+      if (n32 == 0) part[a0 + 8 * hb + e] = x;
+    }
 }
 
 // The increments pass: piece p's own S^T and z (p < NP - 1) and R^T and r (p > 0), to its slots.
@@ -265,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ 
     if (t0 + kBC < t_hi) R.load(kp, qp, vp, gp, sp, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid, doS, doR);
 #pragma unroll
     for (int i = 0; i < NW; i++) {
-      const int ft = w + 4 * i;
+      const int ft = 3 * w + i;
       float zsum = 0.0f, rsum = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
@@ -299,11 +369,22 @@ __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ 
   if (doR) slot_put<T>(rslots + ((size_t)bh * NP + p) * G::SLOT, RT, rs, w, l, tid);
 }
 
-// Forward direction: dPhi(q) of one piece.
+// Method inputs of the fused Jacobian: the raw q and k, the phase table, the root anchors and kr.
+struct JacArgs {
+  const void* uq;
+  const void* uk;
+  const float* rho;
+  const float* omega;
+  int nph, H;
+  float kr;
+};
+
+// Forward direction: dq of one piece, and its omega partials (row (bh NP + p) of dom).
 template <typename T>
 __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, const T* __restrict__ v,
                                          const T* __restrict__ g, const float2* __restrict__ stats, int Tn, int NP,
-                                         const float* __restrict__ sslots, float* __restrict__ dphiq, char* smem) {
+                                         const float* __restrict__ sslots, const JacArgs& ja, T* __restrict__ dq,
+                                         float* __restrict__ dom_part, char* smem) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
@@ -316,7 +397,17 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
   const T* vp = v + so * kDV;
   const T* gp = g + so * kDV;
   const float2* sp = stats + so;
-  float* dq = dphiq + so * Fp;
+  const T* uq = static_cast<const T*>(ja.uq) + so * kD;
+  T* dqp = dq + so * kD;
+  const int da = 16 * w + 4 * h;  // this lane's dims da + 8 hb + e
+  float om4[2][4], dom[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      om4[hb][e] = anchor_rev(ja.omega[(size_t)((bh % ja.H) % ja.nph) * kD + da + 8 * hb + e]);
+      dom[hb][e] = 0.0f;
+    }
   const T* KT = reinterpret_cast<const T*>(smem + G::o_kt);
   const T* VT = reinterpret_cast<const T*>(smem + G::o_vt);
   const T* GT = reinterpret_cast<const T*>(smem + G::o_gt);
@@ -339,6 +430,8 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
     if (t0 + kBC < t_hi) R.load(kp, nullptr, vp, gp, sp, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid);
     // this lane's query t = n32: A[t][s] = <g_t, v_s> - delta_t over s <= t, as accumulator [s][t]
     const float inv = st[n32], dlt = st[kBC + n32];
+    float u[2][4], rh[2][4], gch[5][2][4];
+    lane_inputs<T>(uq, ja.rho, t0 + min(n32, nv - 1), da, u, rh);
     f32x16 acc;
     zero16(acc);
 #pragma unroll
@@ -357,7 +450,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
     if constexpr (sizeof(T) == 2) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
 #pragma unroll
     for (int i = 0; i < NW; i++) {
-      const int ft = w + 4 * i;
+      const int ft = 3 * w + i;
       f32x16 d;  // dPhi(q) before the scaling, as [feature][query]
       zero16(d);
 #pragma unroll
@@ -377,22 +470,22 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
         mma32(d, KF, ks ? A1 : A0);
         if constexpr (sizeof(T) == 2) mma32(d, KF, ks ? R1 : R0);
       }
-      if (n32 < nv) {
-        float* o = dq + (size_t)(t0 + n32) * Fp;
+      // dPhi(q): internal row 8 j + 4 h + e of tile i is channel 2 i + (j >> 1), dim da + 8 (j & 1) + e
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int f0 = 32 * ft + 8 * j + 4 * h;
-          const float4 z4 = *reinterpret_cast<const float4*>(zs + f0);
-          *reinterpret_cast<float4*>(o + f0) =
-              make_float4((d[4 * j] - dlt * z4.x) * inv, (d[4 * j + 1] - dlt * z4.y) * inv,
-                          (d[4 * j + 2] - dlt * z4.z) * inv, (d[4 * j + 3] - dlt * z4.w) * inv);
-        }
+      for (int j = 0; j < 4; j++) {
+        const int c = 2 * i + (j >> 1);
+        if (c == 0) continue;  // the constant feature has no Jacobian
+        const float4 z4 = *reinterpret_cast<const float4*>(zs + 32 * ft + 8 * j + 4 * h);
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) gch[c - 1][j & 1][e] = (d[4 * j + e] - dlt * zz[e]) * inv;
       }
     }
+    if (n32 < nv) lane_vjp<T>(gch, u, rh, om4, ja.kr, dqp + (size_t)(t0 + n32) * kD + da, dom);
     // S += Phi(K)^T V and z += Phi(K)^T 1 over this wave's tiles (each wave reads and updates its own z entries)
 #pragma unroll
     for (int i = 0; i < NW; i++) {
-      const int ft = w + 4 * i;
+      const int ft = 3 * w + i;
       float zsum = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
@@ -406,15 +499,16 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
     }
     __syncthreads();  // the next chunk's staging overwrites the tiles
   }
+  store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
 }
 
-// Reverse direction: dPhi(k) and dv of one piece.
+// Reverse direction: dk and dv of one piece, and its omega partials (row (bh NP + p) of dom).
 template <typename T>
 __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
                                           const T* __restrict__ v, const T* __restrict__ g,
                                           const float2* __restrict__ stats, int Tn, int NP,
-                                          const float* __restrict__ rslots, float* __restrict__ dphik,
-                                          T* __restrict__ dv, char* smem) {
+                                          const float* __restrict__ rslots, const JacArgs& ja, T* __restrict__ dk,
+                                          T* __restrict__ dv, float* __restrict__ dom_part, char* smem) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
@@ -428,8 +522,18 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
   const T* vp = v + so * kDV;
   const T* gp = g + so * kDV;
   const float2* sp = stats + so;
-  float* dk = dphik + so * Fp;
+  const T* uk = static_cast<const T*>(ja.uk) + so * kD;
+  T* dkp = dk + so * kD;
   T* dvp = dv + so * kDV;
+  const int da = 16 * w + 4 * h;  // this lane's dims da + 8 hb + e
+  float om4[2][4], dom[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      om4[hb][e] = anchor_rev(ja.omega[(size_t)((bh % ja.H) % ja.nph) * kD + da + 8 * hb + e]);
+      dom[hb][e] = 0.0f;
+    }
   const T* KT = reinterpret_cast<const T*>(smem + G::o_kt);
   const T* QT = reinterpret_cast<const T*>(smem + G::o_qt);
   const T* VT = reinterpret_cast<const T*>(smem + G::o_vt);
@@ -457,6 +561,8 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     __syncthreads();
     if (c > c_lo) R.load(kp, qp, vp, gp, sp, t0 - kBC, kBC, tid);
     // this lane's key s = n32.  <g_t, v_s> and this wave's part of the scores, as accumulators [t][s]
+    float u[2][4], rh[2][4], gch[5][2][4];
+    lane_inputs<T>(uk, ja.rho, t0 + min(n32, nv - 1), da, u, rh);
     f32x16 gv, sc;
     zero16(gv);
     zero16(sc);
@@ -468,8 +574,8 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     for (int i = 0; i < NW; i++)
 #pragma unroll
       for (int kk = 0; kk < 2; kk++) {
-        const int base = 32 * (w + 4 * i) + 16 * kk;
-        mma32(sc, slot_frag<T>(qrow, base, h), slot_frag<T>(KT + n32 * G::KP, base, h));
+        const int base = 32 * (3 * w + i) + 16 * kk;
+        mma32(sc, slot_frag<T>(qrow, G::QLDS ? base : fglob(base), h), slot_frag<T>(KT + n32 * G::KP, base, h));
       }
     // A[t][s] / Dn_t and P[t][s] / Dn_t over t >= s (1 / Dn is zero past the chunk's end)
     float a0[8], a1[8], p0[8], p1[8];
@@ -502,7 +608,7 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     }
 #pragma unroll
     for (int i = 0; i < NW; i++) {
-      const int ft = w + 4 * i;
+      const int ft = 3 * w + i;
       Frag RF[2][2];
       f32x16 d;  // dPhi(k) + r, as [feature][key]
       zero16(d);
@@ -524,15 +630,15 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
         mma32(d, QF, kt ? A1 : A0);
         if constexpr (sizeof(T) == 2) mma32(d, QF, kt ? R1 : R0);
       }
-      if (n32 < nv) {
-        float* o = dk + (size_t)(t0 + n32) * Fp;
+      // dPhi(k): internal row 8 j + 4 h + e of tile i is channel 2 i + (j >> 1), dim da + 8 (j & 1) + e
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int f0 = 32 * ft + 8 * j + 4 * h;
-          const float4 r4 = *reinterpret_cast<const float4*>(rs + f0);
-          *reinterpret_cast<float4*>(o + f0) =
-              make_float4(d[4 * j] - r4.x, d[4 * j + 1] - r4.y, d[4 * j + 2] - r4.z, d[4 * j + 3] - r4.w);
-        }
+      for (int j = 0; j < 4; j++) {
+        const int c = 2 * i + (j >> 1);
+        if (c == 0) continue;  // the constant feature has no Jacobian
+        const float4 r4 = *reinterpret_cast<const float4*>(rs + 32 * ft + 8 * j + 4 * h);
+        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) gch[c - 1][j & 1][e] = d[4 * j + e] - rr[e];
       }
       // the packed tile as R[feature][value] in this wave's LDS tile, read back with values along the rows
       // (the wave's LDS accesses complete in order, so no barrier is needed between the stores and the reads)
@@ -558,6 +664,7 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
           mma32(dvt[vt], lds_tokfrag(RL, G::RLP, 16 * kk, 32 * vt, l),
                 slot_frag<T>(KT + n32 * G::KP, 32 * ft + 16 * kk, h));
     }
+    if (n32 < nv) lane_vjp<T>(gch, u, rh, om4, ja.kr, dkp + (size_t)(t0 + n32) * kD + da, dom);
     // the four waves' dv partials meet in LDS; summed in a fixed order
 #pragma unroll
     for (int vt = 0; vt < 2; vt++)
@@ -591,7 +698,7 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     const float* dh = st + 2 * kBC;
 #pragma unroll
     for (int i = 0; i < NW; i++) {
-      const int ft = w + 4 * i;
+      const int ft = 3 * w + i;
       float rsum = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 2; kt++) {
@@ -609,6 +716,7 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     }
     __syncthreads();  // the next chunk's staging overwrites the tiles and the reduction buffer
   }
+  store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
 }
 
 // Workgroups [0, BH NP) run the forward direction, [BH NP, 2 BH NP) the reverse one.
@@ -617,15 +725,16 @@ __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(const T* __restrict__
                                                            const T* __restrict__ v, const T* __restrict__ g,
                                                            const float2* __restrict__ stats, int Tn, int NP,
                                                            const float* __restrict__ sslots,
-                                                           const float* __restrict__ rslots,
-                                                           float* __restrict__ dphiq, float* __restrict__ dphik,
-                                                           T* __restrict__ dv) {
+                                                           const float* __restrict__ rslots, const JacArgs ja,
+                                                           T* __restrict__ dq, T* __restrict__ dk,
+                                                           T* __restrict__ dv, float* __restrict__ dom_part) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int nb = (int)gridDim.x / 2;
   if ((int)blockIdx.x < nb)
-    dq_piece<T>(blockIdx.x, phik, v, g, stats, Tn, NP, sslots, dphiq, smem);
+    dq_piece<T>(blockIdx.x, phik, v, g, stats, Tn, NP, sslots, ja, dq, dom_part, smem);
   else
-    dkv_piece<T>(blockIdx.x - nb, phiq, phik, v, g, stats, Tn, NP, rslots, dphik, dv, smem);
+    dkv_piece<T>(blockIdx.x - nb, phiq, phik, v, g, stats, Tn, NP, rslots, ja, dk, dv, dom_part + (size_t)nb * kD,
+                 smem);
 }
 
 template <typename Kern>
@@ -638,7 +747,8 @@ hipError_t set_lds_attr(Kern k, int bytes, std::atomic<bool>& flag) {
 
 template <typename T>
 hipError_t launch_t(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats, int B,
-                    int H, int Tn, float* dphiq, float* dphik, void* dv, float* slots, hipStream_t stream) {
+                    int H, int Tn, const JacArgs& ja, void* dq, void* dk, void* dv, float* dom_part, float* slots,
+                    hipStream_t stream) {
   using G = CGeom<T>;
   static std::atomic<bool> attr[2][64];
   int dev = 0;
@@ -659,7 +769,7 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
   }
   if ((e = set_lds_attr(bwd_chunk_kernel<T>, G::lds, attr[1][dev])) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_chunk_kernel<T>, dim3(2 * BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
-                     sslots, rslots, dphiq, dphik, static_cast<T*>(dv));
+                     sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk), static_cast<T*>(dv), dom_part);
   return hipGetLastError();
 }
 
@@ -670,12 +780,16 @@ size_t bwd_chunked_slot_bytes(int B, int H, int T) {
   return NP > 1 ? 2 * (size_t)B * H * NP * CGeom<float>::SLOT * sizeof(float) : 0;
 }
 
+int bwd_chunked_pieces(int B, int H, int T) { return bwd_pieces(B, H, T); }
+
 hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats,
-                              sanatan_dtype t, int B, int H, int T, float* dphiq, float* dphik, void* dv,
+                              sanatan_dtype t, int B, int H, int T, const void* q, const void* k, const float* rho,
+                              const float* omega, int nph, float kr, void* dq, void* dk, void* dv, float* dom_part,
                               float* slots, hipStream_t stream) {
+  const JacArgs ja{q, k, rho, omega, nph, H, kr};
   return t == SANATAN_BF16
-             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, dphiq, dphik, dv, slots, stream)
-             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, dphiq, dphik, dv, slots, stream);
+             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, ja, dq, dk, dv, dom_part, slots, stream)
+             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, ja, dq, dk, dv, dom_part, slots, stream);
 }
 
 }  // namespace sanatan

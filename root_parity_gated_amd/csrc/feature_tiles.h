@@ -25,9 +25,9 @@ __device__ __forceinline__ typename FragT<T>::type slot_frag(const T* row, int b
 }
 
 // The fp32 counterpart of lds_tokfrag read from a token-major array in global memory: lane (row = l % 32, h)
-// gets column col0 + (l % 32) at tokens tok0 + 8 (i / 4) + 4 h + i % 4, each token clamped to tmax.
-__device__ __forceinline__ f32x8 gtok_frag(const float* base, int pitch, int tok0, int col0, int l, int tmax) {
-  const int col = col0 + (l & 31), tb = tok0 + 4 * (l >> 5);
+// gets its column col at tokens tok0 + 8 (i / 4) + 4 h + i % 4, each token clamped to tmax.
+__device__ __forceinline__ f32x8 gtok_frag(const float* base, int pitch, int tok0, int col, int l, int tmax) {
+  const int tb = tok0 + 4 * (l >> 5);
   f32x8 f;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -44,6 +44,29 @@ __device__ __forceinline__ typename FragT<T>::type residual8(const float (&x)[8]
 #pragma unroll
   for (int i = 0; i < 8; i++) r[i] = x[i] - (float)rounded[i];
   return pack8f<T>(r);
+}
+
+// The feature map's vector-Jacobian product for one component u (one token, one dim): from the gradients
+// g1 .. g5 of its features cos y, sin y, r, r cos y, r sin y (y the rotated angle; the constant feature has none),
+// du = dtheta pi / (1 + |u|)^2 with
+//   dtheta = r' (g3 + g4 cos y + g5 sin y) - sin y (g1 + r g4) + cos y (g2 + r g5),   r' = dr/dtheta = dr/domega,
+// and the omega gradient r' (g3 + g4 cos y + g5 sin y).  The angle, root and rotation are recomputed with the
+// same hardware operations and reduced phase as the feature map.
+__device__ __forceinline__ void feature_vjp(float u, float rho, float om4, float kr, float g1, float g2, float g3,
+                                            float g4, float g5, float& du, float& dom) {
+  const float xr = u * rcp_hw(fmaf(fabsf(u), 2.0f, 2.0f));  // theta / (2 pi)
+  const float y = xr + rho;
+  const float cy = cos_rev(y), sy = sin_rev(y);
+  const float gg = cos_rev(xr + om4);
+  const float e = exp2_hw(kr * gg);
+  const float r = fmaf(-2.0f, rcp_hw(e + 1.0f), 1.0f);
+  // r = tanh(gamma sqrt2 cos(theta + omega + pi/4)); kr = 2 sqrt2 gamma log2(e), so gamma sqrt2 = kr ln2 / 2
+  const float rp = -(kr * 0.34657359027997264f) * (1.0f - r * r) * sin_rev(xr + om4);
+  const float gr = g3 + g4 * cy + g5 * sy;
+  const float dth = rp * gr - sy * (g1 + r * g4) + cy * (g2 + r * g5);
+  const float den = 1.0f + fabsf(u);
+  du = dth * (3.14159265358979f / (den * den));
+  dom = rp * gr;
 }
 
 }  // namespace sanatan
