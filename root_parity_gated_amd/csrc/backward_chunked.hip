@@ -37,6 +37,9 @@ namespace sanatan {
 namespace {
 
 constexpr int kBC = 32;  // chunk tokens
+// bf16 operands that also enter as the rounding of their residual: the state R in dPhi(k) = R v - r, and the
+// masked A tiles
+constexpr bool kResidR = true, kResidA = true;
 
 template <typename T>
 struct CGeom {
@@ -155,7 +158,7 @@ struct ChunkRegs {
     if (tid < kBC) {
       float* sl = reinterpret_cast<float*>(smem + G::o_st);
       const bool ok = tid < nv;
-      const float inv = ok ? 1.0f / st.x : 0.0f, dl = ok ? st.y : 0.0f;
+      const float inv = ok ? rcp_hw(st.x) : 0.0f, dl = ok ? st.y : 0.0f;
       sl[tid] = inv;
       sl[kBC + tid] = dl;
       sl[2 * kBC + tid] = dl * inv;
@@ -181,7 +184,7 @@ struct ChunkRegs {
       if (SG) *reinterpret_cast<u32x4*>(GT + s * G::VP + c) = ok ? gg[i] : zero4;
       if (SH && qq) {
         u32x4 hi, lo;
-        scale16<T>(gg[i], 1.0f / dn_row[i], hi, lo);
+        scale16<T>(gg[i], rcp_hw(dn_row[i]), hi, lo);
         *reinterpret_cast<u32x4*>(HT + s * G::VP + c) = ok ? hi : zero4;
         if constexpr (sizeof(T) == 2) *reinterpret_cast<u32x4*>(HL + s * G::VP + c) = ok ? lo : zero4;
       }
@@ -447,7 +450,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
     }
     const Frag A0 = pack8f<T>(a0), A1 = pack8f<T>(a1);
     Frag R0 = A0, R1 = A1;
-    if constexpr (sizeof(T) == 2) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
+    if constexpr (sizeof(T) == 2 && kResidA) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
 #pragma unroll
     for (int i = 0; i < NW; i++) {
       const int ft = 3 * w + i;
@@ -468,7 +471,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
       for (int ks = 0; ks < 2; ks++) {
         const Frag KF = lds_tokfrag(KT, G::KP, 16 * ks, 32 * ft, l);
         mma32(d, KF, ks ? A1 : A0);
-        if constexpr (sizeof(T) == 2) mma32(d, KF, ks ? R1 : R0);
+        if constexpr (sizeof(T) == 2 && kResidA) mma32(d, KF, ks ? R1 : R0);
       }
       // dPhi(q): internal row 8 j + 4 h + e of tile i is channel 2 i + (j >> 1), dim da + 8 (j & 1) + e
 #pragma unroll
@@ -597,7 +600,7 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     }
     const Frag A0 = pack8f<T>(a0), A1 = pack8f<T>(a1), P0 = pack8f<T>(p0), P1 = pack8f<T>(p1);
     Frag R0 = A0, R1 = A1;
-    if constexpr (sizeof(T) == 2) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
+    if constexpr (sizeof(T) == 2 && kResidA) R0 = residual8<T>(a0, A0), R1 = residual8<T>(a1, A1);
     // dv^T [value][key]: the chunk's queries, then R^T Phi(k) tile by tile below
     f32x16 dvt[2];
 #pragma unroll
@@ -622,13 +625,13 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
           RF[vt][kk] = pack8f<T>(x);
           const Frag VF = slot_frag<T>(VT + n32 * G::VP, 32 * vt + 16 * kk, h);
           mma32(d, RF[vt][kk], VF);
-          if constexpr (sizeof(T) == 2) mma32(d, residual8<T>(x, RF[vt][kk]), VF);
+          if constexpr (sizeof(T) == 2 && kResidR) mma32(d, residual8<T>(x, RF[vt][kk]), VF);
         }
 #pragma unroll
       for (int kt = 0; kt < 2; kt++) {
         const Frag QF = q_tokfrag<T>(smem, qp, t0, 16 * kt, 32 * ft, l, Tn - 1);
         mma32(d, QF, kt ? A1 : A0);
-        if constexpr (sizeof(T) == 2) mma32(d, QF, kt ? R1 : R0);
+        if constexpr (sizeof(T) == 2 && kResidA) mma32(d, QF, kt ? R1 : R0);
       }
       // dPhi(k): internal row 8 j + 4 h + e of tile i is channel 2 i + (j >> 1), dim da + 8 (j & 1) + e
 #pragma unroll

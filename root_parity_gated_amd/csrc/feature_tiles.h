@@ -65,7 +65,7 @@ __device__ __forceinline__ void feature_vjp(float u, float rho, float om4, float
   const float gr = g3 + g4 * cy + g5 * sy;
   const float dth = rp * gr - sy * (g1 + r * g4) + cy * (g2 + r * g5);
   const float den = 1.0f + fabsf(u);
-  du = dth * (3.14159265358979f / (den * den));
+  du = dth * 3.14159265358979f * rcp_hw(den * den);
   dom = rp * gr;
 }
 
