@@ -409,17 +409,15 @@ def backward_flops(B, H, T):
 
 
 def backward_p1_flops(B, H, T, C=32):
-    """Algorithmic FLOPs of the p = 1 backward as the library computes it: the statistics (Dn_t, delta_t) by the
-    masked quadratic form (per causal pair the score, 2 x 6d, and the numerator, 2 d_v), then the chunked
-    recurrences in 32-token chunks.  Per token the state products S g, Phi(K)^T V (forward), R v, R^T Phi(k) and
-    Phi(Q)^T (G / Dn) (reverse), 2 x 6d x d_v each; per causal pair inside a chunk <g_t, v_s> twice (2 d_v each),
-    A Phi(K), the scores and Phi(Q) A (2 x 6d each) and the chunk's part of dv (2 d_v)."""
-    pairs = T * (T + 1) // 2
+    """Algorithmic FLOPs of the p = 1 backward as the library computes it, as chunked recurrences in 32-token chunks
+    (statistics included).  Per token the state products S g, Phi(K)^T V (forward), R v, R^T Phi(k) and
+    Phi(Q)^T (G / Dn) (reverse), 2 x 6d x d_v each, and the statistics' dot products Phi(q) . S g and Phi(q) . z
+    (2 x 6d each); per causal pair inside a chunk <g_t, v_s> twice (2 d_v each), the scores twice, A Phi(K) and
+    Phi(Q) A (2 x 6d each), and the chunk's part of dv (2 d_v)."""
     chunk_pairs = (T // C) * C * (C + 1) // 2 + (T % C) * (T % C + 1) // 2
-    stats = pairs * 2 * (F + DV)
-    linear = T * 5 * 2 * F * DV
-    intra = chunk_pairs * 2 * (3 * DV + 3 * F)
-    return B * H * (stats + linear + intra)
+    linear = T * (5 * 2 * F * DV + 2 * 2 * F)
+    intra = chunk_pairs * 2 * (3 * DV + 4 * F)
+    return B * H * (linear + intra)
 
 
 def bench_backward(torch, rpg, si, w, p_exp, steps, warmup):
@@ -705,8 +703,8 @@ def main():
             bfl = backward_flops(wb.B, wb.H, wb.T) if pb == 2 else backward_p1_flops(wb.B, wb.H, wb.T)
             note = ("gradients of q, k, v, omega (sanatan_attention_backward, masked quadratic form); "
                     "flops: 2 (3 x 6d + 2 d_v) per causal pair") if pb == 2 else (
-                    "gradients of q, k, v, omega (sanatan_attention_backward: statistics by the masked quadratic "
-                    "form, feature gradients and dv as chunked recurrences); flops as backward_p1_flops states")
+                    "gradients of q, k, v, omega (sanatan_attention_backward: statistics, feature gradients and dv "
+                    "as chunked recurrences, linear in T); flops as backward_p1_flops states")
             extras[key] = {"workload": f"{wb.name}_backward_p{pb}", "ms": bms, "ms_eager": be, "ms_graph": bg,
                            "tokens_per_s": wb.B * wb.T / (bms * 1e-3), "flops_per_call": bfl,
                            "roofline": mfma_line(bfl, bms), "note": note}

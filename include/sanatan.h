@@ -329,8 +329,8 @@ sanatan_status sanatan_decode_step_harmonics(const float* q, const float* k, con
  *        table, Phi(Q) and Phi(K) in element type t, per-row statistics, fp32 feature gradients
  *        [B][H][T][6d] for q and k (used at p = 2), per-block omega partials, and (p = 1, sequences split into
  *        pieces) the pieces' recurrence states.  The size depends on the device's compute-unit count.
- * The forward statistics (denominators and <dout_t, o_t>) are recomputed from q, k, v in fp32.  At p = 1 the
- * gradients follow the recurrence form (reading notes §2.7: each gradient is a prefix or suffix sum of feature
+ * The forward statistics (denominators and <dout_t, o_t>) are recomputed from q, k, v in fp32.  At p = 1 they
+ * and the gradients follow the recurrence form (reading notes §2.7: each is a prefix or suffix sum of feature
  * outer products), in time linear in T; at p = 2 they sum over score tiles.  Products run on bf16 MFMA (fp32
  * MFMA for fp32 inputs) with fp32 accumulation.  Bitwise deterministic.
  */

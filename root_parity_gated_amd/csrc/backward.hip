@@ -13,9 +13,9 @@
 //   dtheta = r' (g_r + g_rc cos y + g_rs sin y) - sin y (g_c + r g_rc) + cos y (g_s + r g_rs),
 //   du = dtheta pi / (1 + |u|)^2,  domega_a = sum over tokens of r' (g_r + g_rc cos y + g_rs sin y).
 //
-// Work split.  Phi(Q) and Phi(K) are featurized once into the workspace (element type of the call).  A
-// statistics pass (the forward kernel in its STATS mode) writes (Dn_t, delta_t).  At p = 1 the feature
-// gradients and dv then come from the chunked recurrences of backward_chunked.hip.  At p = 2, flash-attention
+// Work split.  Phi(Q) and Phi(K) are featurized once into the workspace (element type of the call).  At p = 1
+// the statistics, the feature gradients and dv come from the chunked recurrences of backward_chunked.hip.  At
+// p = 2 a statistics pass (the forward kernel in its STATS mode) writes (Dn_t, delta_t); then, flash-attention
 // style, one kernel walks key blocks for each 32-query tile of a wave (dPhi(Q)), and one walks query blocks
 // for each 32-key tile (dPhi(K) and dv); both recompute the score and <g, v> tiles on 32x32x16 bf16 MFMA
 // (32x32x2 fp32 for fp32 inputs).  A wave keeps a 32 x 192 fp32 slice of its gradient in accumulators (32 x 128
@@ -36,10 +36,10 @@ hipError_t launch_quadratic_stats(const void* q, const void* phik, const void* v
 // backward_chunked.hip: the p = 1 feature gradients and dv as chunked recurrences, and their slot bytes
 size_t bwd_chunked_slot_bytes(int B, int H, int T);
 int bwd_chunked_pieces(int B, int H, int T);
-hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats,
-                              sanatan_dtype t, int B, int H, int T, const void* q, const void* k, const float* rho,
-                              const float* omega, int nph, float kr, void* dq, void* dk, void* dv, float* dom_part,
-                              float* slots, hipStream_t stream);
+hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, float2* stats,
+                              sanatan_dtype t, int B, int H, int T, float ceps, const void* q, const void* k,
+                              const float* rho, const float* omega, int nph, float kr, void* dq, void* dk, void* dv,
+                              float* dom_part, float* slots, hipStream_t stream);
 
 namespace {
 
@@ -464,13 +464,13 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   if (e != hipSuccess) return e;
   if ((e = launch_featurize(q, dt, B, H, Tn, pos0, mc, phiq, dt, stream)) != hipSuccess) return e;
   if ((e = launch_featurize(k, dt, B, H, Tn, pos0, mc, phik, dt, stream)) != hipSuccess) return e;
-  if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) return e;
   if constexpr (P == 1) {
-    // p = 1: the feature gradients and dv as chunked recurrences, linear in T
-    if ((e = launch_bwd_chunked(phiq, phik, v, g, stats, dt, B, H, Tn, q, k, rho, mc.omega, mc.nph, mc.kr, dq, dk, dv,
-                                dom, reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
+    // p = 1: the statistics, the feature gradients and dv as chunked recurrences, linear in T
+    if ((e = launch_bwd_chunked(phiq, phik, v, g, stats, dt, B, H, Tn, mc.ceps, q, k, rho, mc.omega, mc.nph, mc.kr,
+                                dq, dk, dv, dom, reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
       return e;
   } else {
+    if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) return e;
 
   // feature-gradient passes: NFT feature tiles of 32 each per pass (the 32 x 32 NFT fp32 slice of a wave in
   // accumulators, next to its 20 operand fragments); dv comes with the first dK pass

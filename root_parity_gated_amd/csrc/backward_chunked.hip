@@ -1,5 +1,5 @@
-// backward_chunked.hip -- the p = 1 backward pass as chunked linear recurrences: the feature gradients dPhi(q),
-// dPhi(k) and dv in time linear in T.
+// backward_chunked.hip -- the p = 1 backward pass as chunked linear recurrences: the forward statistics, the
+// feature gradients and dv, all in time linear in T.
 //
 // SANATAN reading notes, §2.7: at p = 1 the attention is the recurrence of an explicit feature map, and so is
 // each of its gradients.  With the forward statistics Dn_t (denominator, epsilon included) and
@@ -11,20 +11,23 @@
 //   dPhi(q_t) = (S g_t - delta_t z + sum_{s<=t} A[t][s] Phi(k_s)) / Dn_t        (S, z: the keys before the chunk)
 //   dPhi(k_s) = R v_s - r + sum_{t>=s} Phi(q_t) A[t][s] / Dn_t                  (R, r: the queries after it)
 //   dv_s      = R^T Phi(k_s) + sum_{t>=s} P[t][s] g_t / Dn_t.
-// Phi(Q) and Phi(K) are materialized (6d = 384 features, the call's element type); the statistics come in as
-// float2 (Dn_t, delta_t) per token.  The feature map's Jacobian is applied in the chunk kernels themselves:
-// each wave owns 16 dims of every channel, so after a chunk a lane holds all channels' gradients of its token's
-// 8 dims and writes du (and accumulates the omega gradient) without a dPhi array.
+// The statistics come from the forward pass over the same chunks: Dn_t = Phi(q_t) . z + sum_{s<=t} P[t][s] + c eps
+// and delta_t Dn_t = Phi(q_t) . (S g_t) + sum_{s<=t} P[t][s] <g_t, v_s>, where S g_t is the product dPhi(q_t)
+// needs anyway.  Phi(Q) and Phi(K) are materialized (6d = 384 features, the call's element type).  The feature
+// map's Jacobian is applied in the chunk kernels themselves: each wave owns 16 dims of every channel, so after a
+// chunk a lane holds all channels' gradients of its token's 8 dims and writes du (and accumulates the omega
+// gradient) without a dPhi array.
 //
-// Work split.  Each sequence is cut into NP pieces of whole chunks.  One launch runs two workgroups per piece:
-// the forward one walks its chunks in order carrying S^T (as 32 x 32 accumulator tiles [value][feature]) and z,
-// the reverse one walks them backwards carrying R^T and r.  Four waves share a workgroup, wave w owning feature
-// tiles w, w + 4, w + 8 (32 features each).  The dPhi products need no exchange between waves; dv sums over all
-// features, so its four partials meet in LDS in a fixed order.  R^T Phi(k) contracts over features, the other
-// way round from R v, so each R^T tile also passes through a wave-private LDS tile read back transposed.  With
-// NP > 1 an increments pass first writes every piece's own S and z (pieces 0 .. NP-2) and R and r (pieces
-// 1 .. NP-1) to slots; a piece starts from the sum of its predecessors' (forward) or successors' (reverse)
-// slots, in a fixed order.
+// Work split.  Each sequence is cut into NP pieces of whole chunks, one workgroup per piece and direction.  The
+// forward direction walks its chunks in order carrying S^T (as 32 x 32 accumulator tiles [value][feature]) and
+// z, and writes the statistics; the reverse direction, launched after it, walks them backwards carrying R^T and
+// r.  Four waves share a workgroup, wave w owning dims 16 w .. 16 w + 15 of every channel (three 32-feature
+// tiles).  The dPhi products need no exchange between waves; the statistics and dv sum over all features, so
+// their four partials meet in LDS in a fixed order.  R^T Phi(k) contracts over features, the other way round
+// from R v, so each R^T tile also passes through a wave-private LDS tile read back transposed.  With NP > 1 an
+// increments pass writes pieces 0 .. NP-2's own S and z to slots before the forward direction, and another
+// pieces 1 .. NP-1's own R and r (which need the statistics) before the reverse one; a piece starts from the sum
+// of its predecessors' (forward) or successors' (reverse) slots, in a fixed order.
 // Operands: bf16 32x32x16 MFMA (fp32 32x32x2 for fp32 inputs), fp32 accumulation.  With bf16 operands, A, the
 // states S and R, and g / Dn in the update of R enter the products as their rounding plus the rounding of their
 // residual: S g and delta z (R v and r) nearly cancel, so a single rounding would leave an error near the
@@ -68,11 +71,11 @@ struct CGeom {
   static_assert(o_st % 16 == 0 && o_rl % 16 == 0 && o_red % 16 == 0, "aligned LDS regions");
 };
 
-// Pieces per sequence: with two workgroups per piece, as many as keep every workgroup on a compute unit of its
-// own (at most 8, at most one per chunk).
+// Pieces per sequence: as many as keep every workgroup of a launch on a compute unit of its own (at most 8, at
+// most one per chunk).
 int bwd_pieces(int B, int H, int Tn) {
   const long long BH = (long long)B * H, nch = (Tn + kBC - 1) / kBC;
-  long long P = device_cus() / (2 * BH);
+  long long P = device_cus() / BH;
   if (P > 8) P = 8;
   if (P > nch) P = nch;
   return P < 1 ? 1 : (int)P;
@@ -115,11 +118,11 @@ __device__ __forceinline__ int fglob(int fi) {
 
 // One chunk's staged operands (tokens t0 .. t0 + nv - 1 of a sequence) held in registers between their global
 // loads and their LDS stores, so that the next chunk's loads are in flight while the current one computes.
-// Flags: Phi(K), Phi(Q) (staged for bf16 only), V, g, and g / Dn; the statistics of the chunk's tokens (1 / Dn,
-// delta and delta / Dn) always.  Rows past nv are stored as zeros (statistics too); rows are clamped into the
+// Flags: Phi(K), Phi(Q) (staged for bf16 only), V, g, g / Dn, and the statistics of the chunk's tokens (1 / Dn,
+// delta and delta / Dn).  Rows past nv are stored as zeros (statistics too); rows are clamped into the
 // sequence before they are read.  A workgroup-uniform mask can skip the feature rows (kq: Phi(K) and V; qq:
 // Phi(Q) and g / Dn).
-template <typename T, bool SK, bool SQ, bool SV, bool SG, bool SH>
+template <typename T, bool SK, bool SQ, bool SV, bool SG, bool SH, bool SS = true>
 struct ChunkRegs {
   using G = CGeom<T>;
   static constexpr int EL = G::EL, FPC = G::Fp / EL, VPC = kDV / EL;
@@ -134,7 +137,7 @@ struct ChunkRegs {
                                        int nv_, int tid, bool kq = true, bool qq = true) {
     t0 = t0_;
     nv = nv_;
-    if (tid < kBC) st = sp[t0 + min(tid, nv - 1)];
+    if (SS && tid < kBC) st = sp[t0 + min(tid, nv - 1)];
 #pragma unroll
     for (int i = 0; i < NF; i++) {
       const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
@@ -155,7 +158,7 @@ struct ChunkRegs {
 
   __device__ __forceinline__ void store(char* smem, int tid, bool kq = true, bool qq = true) const {
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    if (tid < kBC) {
+    if (SS && tid < kBC) {
       float* sl = reinterpret_cast<float*>(smem + G::o_st);
       const bool ok = tid < nv;
       const float inv = ok ? rcp_hw(st.x) : 0.0f, dl = ok ? st.y : 0.0f;
@@ -293,19 +296,22 @@ __device__ __forceinline__ void store_dom(float (&dom)[2][4], float* part, int a
     }
 }
 
-// The increments pass: piece p's own S^T and z (p < NP - 1) and R^T and r (p > 0), to its slots.
+// The increments pass: piece p's own S^T and z (mode 1; pieces p < NP - 1, before the forward direction) or R^T
+// and r (mode 2; pieces p > 0, after it: they need the statistics the forward direction writes), to its slots.
 template <typename T>
 __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                           const T* __restrict__ v, const T* __restrict__ g,
                                                           const float2* __restrict__ stats, int Tn, int NP,
-                                                          float* __restrict__ sslots, float* __restrict__ rslots) {
+                                                          int mode, float* __restrict__ sslots,
+                                                          float* __restrict__ rslots) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
   const int bh = blockIdx.x / NP, p = blockIdx.x % NP;
-  const bool doS = p < NP - 1, doR = p > 0;
+  const bool doS = mode == 1 && p < NP - 1, doR = mode == 2 && p > 0;
+  if (!doS && !doR) return;
   int t_lo, t_hi;
   piece_bounds(p, NP, Tn, t_lo, t_hi);
   const size_t so = (size_t)bh * Tn;
@@ -382,10 +388,16 @@ struct JacArgs {
   float kr;
 };
 
-// Forward direction: dq of one piece, and its omega partials (row (bh NP + p) of dom).
+// Forward direction: the statistics and dq of one piece, and its omega partials (row (bh NP + p) of dom).  The
+// statistics come out of the same pass: with W_t = S g_t (S before the chunk, the product that dPhi(q) needs
+// anyway) and the chunk's scores P,
+//   Dn_t = Phi(q_t) . z + sum_{s<=t} P[t][s] + c eps,   delta_t Dn_t = Phi(q_t) . W_t + sum_{s<=t} P[t][s] <g_t, v_s>,
+// each wave summing over its features and the four partials meeting in LDS in a fixed order.  They are written
+// to stats for the reverse direction.
 template <typename T>
-__device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, const T* __restrict__ v,
-                                         const T* __restrict__ g, const float2* __restrict__ stats, int Tn, int NP,
+__device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
+                                         const T* __restrict__ v, const T* __restrict__ g,
+                                         float2* __restrict__ stats, int Tn, int NP, float ceps,
                                          const float* __restrict__ sslots, const JacArgs& ja, T* __restrict__ dq,
                                          float* __restrict__ dom_part, char* smem) {
   using G = CGeom<T>;
@@ -396,10 +408,11 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
   int t_lo, t_hi;
   piece_bounds(p, NP, Tn, t_lo, t_hi);
   const size_t so = (size_t)bh * Tn;
+  const T* qp = phiq + so * Fp;
   const T* kp = phik + so * Fp;
   const T* vp = v + so * kDV;
   const T* gp = g + so * kDV;
-  const float2* sp = stats + so;
+  float2* sp = stats + so;
   const T* uq = static_cast<const T*>(ja.uq) + so * kD;
   T* dqp = dq + so * kD;
   const int da = 16 * w + 4 * h;  // this lane's dims da + 8 hb + e
@@ -412,11 +425,12 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
       dom[hb][e] = 0.0f;
     }
   const T* KT = reinterpret_cast<const T*>(smem + G::o_kt);
+  const T* QT = reinterpret_cast<const T*>(smem + G::o_qt);
   const T* VT = reinterpret_cast<const T*>(smem + G::o_vt);
   const T* GT = reinterpret_cast<const T*>(smem + G::o_gt);
-  const float* st = reinterpret_cast<const float*>(smem + G::o_st);
   float* zs = reinterpret_cast<float*>(smem + G::o_zs);
-  // S^T tiles: tile (i, vt) holds S[32 ft + n32][32 vt + 8 j + 4 h + i4] in register 4 j + i4, ft = w + 4 i
+  float4* part = reinterpret_cast<float4*>(smem + G::o_red);  // [4 waves][32 queries] statistics partials
+  // S^T tiles: tile (i, vt) holds S[32 ft + n32][32 vt + 8 j + 4 h + i4] in register 4 j + i4, ft = 3 w + i
   f32x16 ST[NW][2];
 #pragma unroll
   for (int i = 0; i < NW; i++)
@@ -424,22 +438,88 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
     for (int vt = 0; vt < 2; vt++) zero16(ST[i][vt]);
   for (int f = tid; f < Fp; f += 256) zs[f] = 0.0f;
   for (int q = 0; q < p; q++) slot_add<T>(sslots + ((size_t)bh * NP + q) * G::SLOT, ST, zs, w, l, tid);
-  ChunkRegs<T, true, false, true, true, false> R;
-  R.load(kp, nullptr, vp, gp, sp, t_lo, min(kBC, t_hi - t_lo), tid);
+  ChunkRegs<T, true, true, true, true, false, false> R;
+  R.load(kp, qp, vp, gp, nullptr, t_lo, min(kBC, t_hi - t_lo), tid);
   for (int t0 = t_lo; t0 < t_hi; t0 += kBC) {
     const int nv = R.nv;
     R.store(smem, tid);
     __syncthreads();
-    if (t0 + kBC < t_hi) R.load(kp, nullptr, vp, gp, sp, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid);
-    // this lane's query t = n32: A[t][s] = <g_t, v_s> - delta_t over s <= t, as accumulator [s][t]
-    const float inv = st[n32], dlt = st[kBC + n32];
+    if (t0 + kBC < t_hi) R.load(kp, qp, vp, gp, nullptr, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid);
+    // this lane's query t = n32
     float u[2][4], rh[2][4], gch[5][2][4];
     lane_inputs<T>(uq, ja.rho, t0 + min(n32, nv - 1), da, u, rh);
-    f32x16 acc;
+    const T* qrow = G::QLDS ? QT + n32 * G::KP : qp + (size_t)min(t0 + n32, Tn - 1) * Fp;
+    // <g_t, v_s> and this wave's part of the scores, as accumulators [s][t]
+    f32x16 acc, sc;
     zero16(acc);
+    zero16(sc);
 #pragma unroll
     for (int kk = 0; kk < 4; kk++)
       mma32(acc, slot_frag<T>(VT + n32 * G::VP, 16 * kk, h), slot_frag<T>(GT + n32 * G::VP, 16 * kk, h));
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) {
+        const int base = 32 * (3 * w + i) + 16 * kk;
+        mma32(sc, slot_frag<T>(KT + n32 * G::KP, base, h), slot_frag<T>(qrow, G::QLDS ? base : fglob(base), h));
+      }
+    // W = S g over this wave's tiles, as [feature][query]
+    f32x16 d[NW];
+#pragma unroll
+    for (int i = 0; i < NW; i++) {
+      zero16(d[i]);
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+          float x[8];
+#pragma unroll
+          for (int s = 0; s < 8; s++) x[s] = ST[i][vt][8 * kk + s];
+          const Frag SF = pack8f<T>(x), GF = slot_frag<T>(GT + n32 * G::VP, 32 * vt + 16 * kk, h);
+          mma32(d[i], SF, GF);
+          if constexpr (sizeof(T) == 2) mma32(d[i], residual8<T>(x, SF), GF);
+        }
+    }
+    // this wave's parts of Phi(q) . W, Phi(q) . z, sum_s P and sum_s P <g, v>
+    float pw = 0.0f, pz = 0.0f, ps = 0.0f, pg = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int f0 = 32 * (3 * w + i) + 8 * j + 4 * h;
+        float qv[4];
+        load4(qrow + (G::QLDS ? f0 : fglob(f0)), qv);
+        const float4 z4 = *reinterpret_cast<const float4*>(zs + f0);
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          pw = fmaf(qv[e], d[i][4 * j + e], pw);
+          pz = fmaf(qv[e], zz[e], pz);
+        }
+      }
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int s = 8 * (r >> 2) + 4 * h + (r & 3);
+      if (s <= n32) {
+        ps += sc[r];
+        pg = fmaf(sc[r], acc[r], pg);
+      }
+    }
+    pw = xor32_sum(pw);
+    pz = xor32_sum(pz);
+    ps = xor32_sum(ps);
+    pg = xor32_sum(pg);
+    if (h == 0) part[w * kBC + n32] = make_float4(pw, pz, ps, pg);
+    __syncthreads();
+    float4 tot = part[n32];
+#pragma unroll
+    for (int ww = 1; ww < 4; ww++) {
+      const float4 x = part[ww * kBC + n32];
+      tot = make_float4(tot.x + x.x, tot.y + x.y, tot.z + x.z, tot.w + x.w);
+    }
+    const float dn = (tot.y + tot.z) + ceps, inv = rcp_hw(dn), dlt = (tot.x + tot.w) * inv;
+    if (w == 0 && h == 0 && n32 < nv) sp[t0 + n32] = make_float2(dn, dlt);
+    // A[t][s] = <g_t, v_s> - delta_t over s <= t, as accumulator [s][t]
     float a0[8], a1[8];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
@@ -454,24 +534,11 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
 #pragma unroll
     for (int i = 0; i < NW; i++) {
       const int ft = 3 * w + i;
-      f32x16 d;  // dPhi(q) before the scaling, as [feature][query]
-      zero16(d);
-#pragma unroll
-      for (int vt = 0; vt < 2; vt++)
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-          float x[8];
-#pragma unroll
-          for (int s = 0; s < 8; s++) x[s] = ST[i][vt][8 * kk + s];
-          const Frag SF = pack8f<T>(x), GF = slot_frag<T>(GT + n32 * G::VP, 32 * vt + 16 * kk, h);
-          mma32(d, SF, GF);
-          if constexpr (sizeof(T) == 2) mma32(d, residual8<T>(x, SF), GF);
-        }
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
         const Frag KF = lds_tokfrag(KT, G::KP, 16 * ks, 32 * ft, l);
-        mma32(d, KF, ks ? A1 : A0);
-        if constexpr (sizeof(T) == 2 && kResidA) mma32(d, KF, ks ? R1 : R0);
+        mma32(d[i], KF, ks ? A1 : A0);
+        if constexpr (sizeof(T) == 2 && kResidA) mma32(d[i], KF, ks ? R1 : R0);
       }
       // dPhi(q): internal row 8 j + 4 h + e of tile i is channel 2 i + (j >> 1), dim da + 8 (j & 1) + e
 #pragma unroll
@@ -481,7 +548,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
         const float4 z4 = *reinterpret_cast<const float4*>(zs + 32 * ft + 8 * j + 4 * h);
         const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-        for (int e = 0; e < 4; e++) gch[c - 1][j & 1][e] = (d[4 * j + e] - dlt * zz[e]) * inv;
+        for (int e = 0; e < 4; e++) gch[c - 1][j & 1][e] = (d[i][4 * j + e] - dlt * zz[e]) * inv;
       }
     }
     if (n32 < nv) lane_vjp<T>(gch, u, rh, om4, ja.kr, dqp + (size_t)(t0 + n32) * kD + da, dom);
@@ -500,7 +567,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phik, co
       zsum = xor32_sum(zsum);
       if (h == 0) zs[32 * ft + n32] += zsum;
     }
-    __syncthreads();  // the next chunk's staging overwrites the tiles
+    __syncthreads();  // the next chunk's staging overwrites the tiles and the statistics partials
   }
   store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
 }
@@ -722,22 +789,22 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
   store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
 }
 
-// Workgroups [0, BH NP) run the forward direction, [BH NP, 2 BH NP) the reverse one.
+// dir 0: the forward direction (statistics, dq), written to rows [0, BH NP) of dom; dir 1: the reverse one
+// (dk, dv), rows [BH NP, 2 BH NP).  One workgroup per piece.
 template <typename T>
 __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                            const T* __restrict__ v, const T* __restrict__ g,
-                                                           const float2* __restrict__ stats, int Tn, int NP,
-                                                           const float* __restrict__ sslots,
+                                                           float2* __restrict__ stats, int Tn, int NP, float ceps,
+                                                           int dir, const float* __restrict__ sslots,
                                                            const float* __restrict__ rslots, const JacArgs ja,
                                                            T* __restrict__ dq, T* __restrict__ dk,
                                                            T* __restrict__ dv, float* __restrict__ dom_part) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int nb = (int)gridDim.x / 2;
-  if ((int)blockIdx.x < nb)
-    dq_piece<T>(blockIdx.x, phik, v, g, stats, Tn, NP, sslots, ja, dq, dom_part, smem);
+  if (dir == 0)
+    dq_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, ceps, sslots, ja, dq, dom_part, smem);
   else
-    dkv_piece<T>(blockIdx.x - nb, phiq, phik, v, g, stats, Tn, NP, rslots, ja, dk, dv, dom_part + (size_t)nb * kD,
-                 smem);
+    dkv_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, rslots, ja, dk, dv,
+                 dom_part + (size_t)gridDim.x * kD, smem);
 }
 
 template <typename Kern>
@@ -749,9 +816,9 @@ hipError_t set_lds_attr(Kern k, int bytes, std::atomic<bool>& flag) {
 }
 
 template <typename T>
-hipError_t launch_t(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats, int B,
-                    int H, int Tn, const JacArgs& ja, void* dq, void* dk, void* dv, float* dom_part, float* slots,
-                    hipStream_t stream) {
+hipError_t launch_t(const void* phiq, const void* phik, const void* v, const void* g, float2* stats, int B, int H,
+                    int Tn, float ceps, const JacArgs& ja, void* dq, void* dk, void* dv, float* dom_part,
+                    float* slots, hipStream_t stream) {
   using G = CGeom<T>;
   static std::atomic<bool> attr[2][64];
   int dev = 0;
@@ -764,16 +831,24 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
   const T* vv = static_cast<const T*>(v);
   const T* gg = static_cast<const T*>(g);
   hipError_t e;
-  if (NP > 1) {
-    if ((e = set_lds_attr(bwd_incr_kernel<T>, G::lds, attr[0][dev])) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_incr_kernel<T>, dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
-                       sslots, rslots);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   if ((e = set_lds_attr(bwd_chunk_kernel<T>, G::lds, attr[1][dev])) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_chunk_kernel<T>, dim3(2 * BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
-                     sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk), static_cast<T*>(dv), dom_part);
-  return hipGetLastError();
+  if (NP > 1 && (e = set_lds_attr(bwd_incr_kernel<T>, G::lds, attr[0][dev])) != hipSuccess) return e;
+  auto incr = [&](int mode) {
+    hipLaunchKernelGGL(bwd_incr_kernel<T>, dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
+                       mode, sslots, rslots);
+    return hipGetLastError();
+  };
+  auto chunks = [&](int dir) {
+    hipLaunchKernelGGL(bwd_chunk_kernel<T>, dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
+                       ceps, dir, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk), static_cast<T*>(dv),
+                       dom_part);
+    return hipGetLastError();
+  };
+  // S increments, the forward direction (which writes the statistics), R increments, the reverse direction
+  if (NP > 1 && (e = incr(1)) != hipSuccess) return e;
+  if ((e = chunks(0)) != hipSuccess) return e;
+  if (NP > 1 && (e = incr(2)) != hipSuccess) return e;
+  return chunks(1);
 }
 
 }  // namespace
@@ -785,14 +860,14 @@ size_t bwd_chunked_slot_bytes(int B, int H, int T) {
 
 int bwd_chunked_pieces(int B, int H, int T) { return bwd_pieces(B, H, T); }
 
-hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, const float2* stats,
-                              sanatan_dtype t, int B, int H, int T, const void* q, const void* k, const float* rho,
-                              const float* omega, int nph, float kr, void* dq, void* dk, void* dv, float* dom_part,
-                              float* slots, hipStream_t stream) {
+hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, float2* stats,
+                              sanatan_dtype t, int B, int H, int T, float ceps, const void* q, const void* k,
+                              const float* rho, const float* omega, int nph, float kr, void* dq, void* dk, void* dv,
+                              float* dom_part, float* slots, hipStream_t stream) {
   const JacArgs ja{q, k, rho, omega, nph, H, kr};
   return t == SANATAN_BF16
-             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, ja, dq, dk, dv, dom_part, slots, stream)
-             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, ja, dq, dk, dv, dom_part, slots, stream);
+             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, ceps, ja, dq, dk, dv, dom_part, slots, stream)
+             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, ceps, ja, dq, dk, dv, dom_part, slots, stream);
 }
 
 }  // namespace sanatan
