@@ -71,12 +71,12 @@ struct CGeom {
   static_assert(o_st % 16 == 0 && o_rl % 16 == 0 && o_red % 16 == 0, "aligned LDS regions");
 };
 
-// Pieces per sequence: as many as keep every workgroup of a launch on a compute unit of its own (at most 8, at
+// Pieces per sequence: as many as keep every workgroup of a launch on a compute unit of its own (at most 32, at
 // most one per chunk).
 int bwd_pieces(int B, int H, int Tn) {
   const long long BH = (long long)B * H, nch = (Tn + kBC - 1) / kBC;
   long long P = device_cus() / BH;
-  if (P > 8) P = 8;
+  if (P > 32) P = 32;
   if (P > nch) P = nch;
   return P < 1 ? 1 : (int)P;
 }

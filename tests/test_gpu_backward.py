@@ -143,6 +143,14 @@ def test_backward_long_bf16(torch_dev, p):
         assert e <= TOL["bf16"], (name, e)
 
 
+def test_backward_p1_long_many_pieces(torch_dev):
+    """p = 1 at 4096 tokens in bf16: each sequence runs as 32 pieces of four chunks, so the reverse direction's
+    start states sum up to 31 successors' slots."""
+    errs = run_case(torch_dev, 835, 1, 2, 4096, "bf16", 1)
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+
+
 @pytest.mark.parametrize("p", [1, 2])
 def test_backward_deterministic(torch_dev, p):
     import root_parity_gated_amd as rpg
