@@ -61,8 +61,7 @@ struct CGeom {
   static constexpr int o_hl = o_ht + v_b;
   static constexpr int o_st = o_hl + hl_b;         // 1 / Dn, delta, delta / Dn of the chunk's tokens
   static constexpr int o_zs = o_st + 3 * kBC * 4;  // z (forward) or r (reverse) [Fp]
-  static constexpr int o_rs = o_zs + Fp * 4;       // r in the increments pass [Fp]
-  static constexpr int o_rl = o_rs + Fp * 4;       // per wave: one packed R^T tile as [32 features][RLP]
+  static constexpr int o_rl = o_zs + Fp * 4;       // per wave: one packed R^T tile as [32 features][RLP]
   static constexpr int rl_b = 4 * 32 * RLP * (int)sizeof(T);
   static constexpr int o_red = o_rl + rl_b;        // dv partials [4 waves][32 keys][RP]
   static constexpr int lds = o_red + 4 * kBC * RP * 4;
@@ -296,22 +295,23 @@ __device__ __forceinline__ void store_dom(float (&dom)[2][4], float* part, int a
     }
 }
 
-// The increments pass: piece p's own S^T and z (mode 1; pieces p < NP - 1, before the forward direction) or R^T
-// and r (mode 2; pieces p > 0, after it: they need the statistics the forward direction writes), to its slots.
-template <typename T>
+// The increments pass: piece p's own S^T and z (MODE 1; pieces p < NP - 1, before the forward direction) or R^T
+// and r (MODE 2; pieces p > 0, after it: they need the statistics the forward direction writes), to its slots.
+// Two register sets alternate, so each chunk's rows are loaded two chunks ahead of their use: the per-chunk work
+// here is short, and one chunk of lead does not cover the loads' latency.
+template <typename T, int MODE>
 __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                           const T* __restrict__ v, const T* __restrict__ g,
                                                           const float2* __restrict__ stats, int Tn, int NP,
-                                                          int mode, float* __restrict__ sslots,
-                                                          float* __restrict__ rslots) {
+                                                          float* __restrict__ slots) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
+  constexpr bool DS = MODE == 1, DR = MODE == 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
   const int bh = blockIdx.x / NP, p = blockIdx.x % NP;
-  const bool doS = mode == 1 && p < NP - 1, doR = mode == 2 && p > 0;
-  if (!doS && !doR) return;
+  if (DS ? p == NP - 1 : p == 0) return;
   int t_lo, t_hi;
   piece_bounds(p, NP, Tn, t_lo, t_hi);
   const size_t so = (size_t)bh * Tn;
@@ -325,57 +325,61 @@ __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ 
   const T* HT = reinterpret_cast<const T*>(smem + G::o_ht);
   const T* HL = reinterpret_cast<const T*>(smem + G::o_hl);
   const float* dh = reinterpret_cast<const float*>(smem + G::o_st) + 2 * kBC;
-  float* zs = reinterpret_cast<float*>(smem + G::o_zs);
-  float* rs = reinterpret_cast<float*>(smem + G::o_rs);
-  f32x16 ST[NW][2], RT[NW][2];
+  float* vs = reinterpret_cast<float*>(smem + G::o_zs);  // z (MODE 1) or r (MODE 2)
+  f32x16 A[NW][2];  // S^T or R^T tiles
 #pragma unroll
   for (int i = 0; i < NW; i++)
 #pragma unroll
-    for (int vt = 0; vt < 2; vt++) {
-      zero16(ST[i][vt]);
-      zero16(RT[i][vt]);
-    }
-  for (int f = tid; f < Fp; f += 256) zs[f] = rs[f] = 0.0f;
-  ChunkRegs<T, true, true, true, false, true> R;
-  R.load(kp, qp, vp, gp, sp, t_lo, min(kBC, t_hi - t_lo), tid, doS, doR);
-  for (int t0 = t_lo; t0 < t_hi; t0 += kBC) {
-    R.store(smem, tid, doS, doR);
-    __syncthreads();
-    if (t0 + kBC < t_hi) R.load(kp, qp, vp, gp, sp, t0 + kBC, min(kBC, t_hi - t0 - kBC), tid, doS, doR);
+    for (int vt = 0; vt < 2; vt++) zero16(A[i][vt]);
+  for (int f = tid; f < Fp; f += 256) vs[f] = 0.0f;
+  auto compute = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < NW; i++) {
       const int ft = 3 * w + i;
-      float zsum = 0.0f, rsum = 0.0f;
+      float sum = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
-        if (doS) {
+        if constexpr (DS) {
           const Frag KF = lds_tokfrag(KT, G::KP, 16 * ks, 32 * ft, l);
-          zsum = frag_sum(KF, zsum);
+          sum = frag_sum(KF, sum);
 #pragma unroll
-          for (int vt = 0; vt < 2; vt++) mma32(ST[i][vt], lds_tokfrag(VT, G::VP, 16 * ks, 32 * vt, l), KF);
-        }
-        if (doR) {
+          for (int vt = 0; vt < 2; vt++) mma32(A[i][vt], lds_tokfrag(VT, G::VP, 16 * ks, 32 * vt, l), KF);
+        } else {
           const Frag QF = q_tokfrag<T>(smem, qp, t0, 16 * ks, 32 * ft, l, Tn - 1);
 #pragma unroll
-          for (int e = 0; e < 8; e++) rsum = fmaf((float)QF[e], dh[16 * ks + 8 * (e >> 2) + 4 * h + (e & 3)], rsum);
+          for (int e = 0; e < 8; e++) sum = fmaf((float)QF[e], dh[16 * ks + 8 * (e >> 2) + 4 * h + (e & 3)], sum);
 #pragma unroll
           for (int vt = 0; vt < 2; vt++) {
-            mma32(RT[i][vt], lds_tokfrag(HT, G::VP, 16 * ks, 32 * vt, l), QF);
-            if constexpr (sizeof(T) == 2) mma32(RT[i][vt], lds_tokfrag(HL, G::VP, 16 * ks, 32 * vt, l), QF);
+            mma32(A[i][vt], lds_tokfrag(HT, G::VP, 16 * ks, 32 * vt, l), QF);
+            if constexpr (sizeof(T) == 2) mma32(A[i][vt], lds_tokfrag(HL, G::VP, 16 * ks, 32 * vt, l), QF);
           }
         }
       }
-      zsum = xor32_sum(zsum);
-      rsum = xor32_sum(rsum);
-      if (h == 0) {
-        if (doS) zs[32 * ft + n32] += zsum;
-        if (doR) rs[32 * ft + n32] += rsum;
-      }
+      sum = xor32_sum(sum);
+      if (h == 0) vs[32 * ft + n32] += sum;
     }
+  };
+  // MODE 1 stages Phi(K) and V; MODE 2 Phi(Q) (bf16), g / Dn and the statistics
+  ChunkRegs<T, DS, DR, DS, false, DR, DR> R0, R1;
+  const int nch = (t_hi - t_lo + kBC - 1) / kBC;
+  auto nvof = [&](int c) { return min(kBC, t_hi - t_lo - c * kBC); };
+  R0.load(kp, qp, vp, gp, sp, t_lo, nvof(0), tid);
+  if (nch > 1) R1.load(kp, qp, vp, gp, sp, t_lo + kBC, nvof(1), tid);
+  for (int c = 0; c < nch; c += 2) {
+    R0.store(smem, tid);
     __syncthreads();
+    if (c + 2 < nch) R0.load(kp, qp, vp, gp, sp, t_lo + (c + 2) * kBC, nvof(c + 2), tid);
+    compute(t_lo + c * kBC);
+    __syncthreads();
+    if (c + 1 < nch) {
+      R1.store(smem, tid);
+      __syncthreads();
+      if (c + 3 < nch) R1.load(kp, qp, vp, gp, sp, t_lo + (c + 3) * kBC, nvof(c + 3), tid);
+      compute(t_lo + (c + 1) * kBC);
+      __syncthreads();
+    }
   }
-  if (doS) slot_put<T>(sslots + ((size_t)bh * NP + p) * G::SLOT, ST, zs, w, l, tid);
-  if (doR) slot_put<T>(rslots + ((size_t)bh * NP + p) * G::SLOT, RT, rs, w, l, tid);
+  slot_put<T>(slots + ((size_t)bh * NP + p) * G::SLOT, A, vs, w, l, tid);
 }
 
 // Method inputs of the fused Jacobian: the raw q and k, the phase table, the root anchors and kr.
@@ -820,7 +824,7 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
                     int Tn, float ceps, const JacArgs& ja, void* dq, void* dk, void* dv, float* dom_part,
                     float* slots, hipStream_t stream) {
   using G = CGeom<T>;
-  static std::atomic<bool> attr[2][64];
+  static std::atomic<bool> attr[3][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   const int BH = B * H, NP = bwd_pieces(B, H, Tn);
@@ -832,10 +836,16 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
   const T* gg = static_cast<const T*>(g);
   hipError_t e;
   if ((e = set_lds_attr(bwd_chunk_kernel<T>, G::lds, attr[1][dev])) != hipSuccess) return e;
-  if (NP > 1 && (e = set_lds_attr(bwd_incr_kernel<T>, G::lds, attr[0][dev])) != hipSuccess) return e;
+  if (NP > 1 && ((e = set_lds_attr(bwd_incr_kernel<T, 1>, G::lds, attr[0][dev])) != hipSuccess ||
+                 (e = set_lds_attr(bwd_incr_kernel<T, 2>, G::lds, attr[2][dev])) != hipSuccess))
+    return e;
   auto incr = [&](int mode) {
-    hipLaunchKernelGGL(bwd_incr_kernel<T>, dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
-                       mode, sslots, rslots);
+    if (mode == 1)
+      hipLaunchKernelGGL((bwd_incr_kernel<T, 1>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
+                         NP, sslots);
+    else
+      hipLaunchKernelGGL((bwd_incr_kernel<T, 2>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
+                         NP, rslots);
     return hipGetLastError();
   };
   auto chunks = [&](int dir) {
