@@ -793,18 +793,18 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
   store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
 }
 
-// dir 0: the forward direction (statistics, dq), written to rows [0, BH NP) of dom; dir 1: the reverse one
+// DIR 0: the forward direction (statistics, dq), written to rows [0, BH NP) of dom; DIR 1: the reverse one
 // (dk, dv), rows [BH NP, 2 BH NP).  One workgroup per piece.
-template <typename T>
+template <typename T, int DIR>
 __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                            const T* __restrict__ v, const T* __restrict__ g,
                                                            float2* __restrict__ stats, int Tn, int NP, float ceps,
-                                                           int dir, const float* __restrict__ sslots,
+                                                           const float* __restrict__ sslots,
                                                            const float* __restrict__ rslots, const JacArgs ja,
                                                            T* __restrict__ dq, T* __restrict__ dk,
                                                            T* __restrict__ dv, float* __restrict__ dom_part) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if (dir == 0)
+  if constexpr (DIR == 0)
     dq_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, ceps, sslots, ja, dq, dom_part, smem);
   else
     dkv_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, rslots, ja, dk, dv,
@@ -824,7 +824,7 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
                     int Tn, float ceps, const JacArgs& ja, void* dq, void* dk, void* dv, float* dom_part,
                     float* slots, hipStream_t stream) {
   using G = CGeom<T>;
-  static std::atomic<bool> attr[3][64];
+  static std::atomic<bool> attr[4][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   const int BH = B * H, NP = bwd_pieces(B, H, Tn);
@@ -835,7 +835,9 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
   const T* vv = static_cast<const T*>(v);
   const T* gg = static_cast<const T*>(g);
   hipError_t e;
-  if ((e = set_lds_attr(bwd_chunk_kernel<T>, G::lds, attr[1][dev])) != hipSuccess) return e;
+  if ((e = set_lds_attr(bwd_chunk_kernel<T, 0>, G::lds, attr[1][dev])) != hipSuccess ||
+      (e = set_lds_attr(bwd_chunk_kernel<T, 1>, G::lds, attr[3][dev])) != hipSuccess)
+    return e;
   if (NP > 1 && ((e = set_lds_attr(bwd_incr_kernel<T, 1>, G::lds, attr[0][dev])) != hipSuccess ||
                  (e = set_lds_attr(bwd_incr_kernel<T, 2>, G::lds, attr[2][dev])) != hipSuccess))
     return e;
@@ -849,9 +851,14 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
     return hipGetLastError();
   };
   auto chunks = [&](int dir) {
-    hipLaunchKernelGGL(bwd_chunk_kernel<T>, dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, NP,
-                       ceps, dir, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk), static_cast<T*>(dv),
-                       dom_part);
+    if (dir == 0)
+      hipLaunchKernelGGL((bwd_chunk_kernel<T, 0>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
+                         NP, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
+                         static_cast<T*>(dv), dom_part);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<T, 1>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
+                         NP, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
+                         static_cast<T*>(dv), dom_part);
     return hipGetLastError();
   };
   // S increments, the forward direction (which writes the statistics), R increments, the reverse direction
