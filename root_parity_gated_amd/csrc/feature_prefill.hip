@@ -211,48 +211,89 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
     for (int q = 0; q < p; q++) add_state(slot(q), slot(q) + Fp * kDV, Fp, false);
   }
 
+  // Staging of a chunk's Phi(K) (and, bf16 output pass, Phi(Q)) and V rows, zero past its end.  With few pieces
+  // per thread (PF) the next chunk's rows are loaded into registers while the current chunk computes; otherwise
+  // the loads are issued in groups of GS pieces per operand before the group's LDS writes, so the staging waits
+  // for memory once per group instead of once per piece.
+  constexpr int EL = G::EL, FPC = Fp / EL;
+  constexpr bool LQ = G::QLDS && !STATE_ONLY;
+  constexpr int NPIECE = G::FPIECES * (LQ ? 2 : 1) + G::VPIECES;
+  constexpr bool PF = NPIECE <= 12;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 pk[PF ? G::FPIECES : 1], pq[PF && LQ ? G::FPIECES : 1], pv[PF ? G::VPIECES : 1];
+  auto pf_load = [&](int c0, int cnv) {
+#pragma unroll
+    for (int i = 0; i < G::FPIECES; i++) {
+      const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
+      const size_t off = (size_t)(c0 + min(s, cnv - 1)) * Fp + c;
+      pk[PF ? i : 0] = *reinterpret_cast<const u32x4*>(kp + off);
+      if constexpr (LQ) pq[PF ? i : 0] = *reinterpret_cast<const u32x4*>(qp + off);
+    }
+#pragma unroll
+    for (int i = 0; i < G::VPIECES; i++) {
+      const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+      if (e < kFC * (kDV / EL)) pv[PF ? i : 0] = *reinterpret_cast<const u32x4*>(vp + (size_t)(c0 + min(s, cnv - 1)) * kDV + c);
+    }
+  };
+  auto pf_store = [&](int cnv) {
+#pragma unroll
+    for (int i = 0; i < G::FPIECES; i++) {
+      const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
+      *reinterpret_cast<u32x4*>(KT + s * KP + c) = s < cnv ? pk[PF ? i : 0] : zero4;
+      if constexpr (LQ) *reinterpret_cast<u32x4*>(QT + s * KP + c) = pq[PF ? i : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < G::VPIECES; i++) {
+      const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+      if (e < kFC * (kDV / EL)) *reinterpret_cast<u32x4*>(VT + s * VP + c) = s < cnv ? pv[PF ? i : 0] : zero4;
+    }
+  };
+  if constexpr (PF) {
+    if (t_lo < t_hi) pf_load(t_lo, min(kFC, t_hi - t_lo));
+  }
   for (int t0 = t_lo; t0 < t_hi; t0 += kFC) {
     const int nv = min(kFC, t_hi - t0);
-    // stage Phi(K) (and, bf16, Phi(Q)) and V rows of the chunk, zero past its end: the loads are issued in
-    // groups of GS pieces per operand before the group's LDS writes, so the staging waits for memory once per
-    // group instead of once per piece
-    constexpr int EL = G::EL, FPC = Fp / EL;
-    constexpr int GS = G::FPIECES < 4 ? G::FPIECES : 4;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    if constexpr (PF) {
+      pf_store(nv);
+      __syncthreads();
+      if (t0 + kFC < t_hi) pf_load(t0 + kFC, min(kFC, t_hi - t0 - kFC));
+    } else {
+      constexpr int GS = G::FPIECES < 4 ? G::FPIECES : 4;
 #pragma unroll
-    for (int g0 = 0; g0 < G::FPIECES; g0 += GS) {
-      u32x4 kr[GS], qr[GS];
+      for (int g0 = 0; g0 < G::FPIECES; g0 += GS) {
+        u32x4 kr[GS], qr[GS];
 #pragma unroll
-      for (int i = 0; i < GS; i++) {
-        if (g0 + i < G::FPIECES) {
-          const int e = tid + 256 * (g0 + i), s = e / FPC, c = (e % FPC) * EL, sc = t0 + min(s, nv - 1);
-          kr[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)sc * Fp + c);
-          if constexpr (G::QLDS) qr[i] = *reinterpret_cast<const u32x4*>(qp + (size_t)sc * Fp + c);
+        for (int i = 0; i < GS; i++) {
+          if (g0 + i < G::FPIECES) {
+            const int e = tid + 256 * (g0 + i), s = e / FPC, c = (e % FPC) * EL, sc = t0 + min(s, nv - 1);
+            kr[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)sc * Fp + c);
+            if constexpr (LQ) qr[i] = *reinterpret_cast<const u32x4*>(qp + (size_t)sc * Fp + c);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < GS; i++) {
+          if (g0 + i < G::FPIECES) {
+            const int e = tid + 256 * (g0 + i), s = e / FPC, c = (e % FPC) * EL;
+            *reinterpret_cast<u32x4*>(KT + s * KP + c) = s < nv ? kr[i] : zero4;
+            if constexpr (LQ) *reinterpret_cast<u32x4*>(QT + s * KP + c) = qr[i];
+          }
         }
       }
+      {
+        u32x4 vr[G::VPIECES];
 #pragma unroll
-      for (int i = 0; i < GS; i++) {
-        if (g0 + i < G::FPIECES) {
-          const int e = tid + 256 * (g0 + i), s = e / FPC, c = (e % FPC) * EL;
-          *reinterpret_cast<u32x4*>(KT + s * KP + c) = s < nv ? kr[i] : zero4;
-          if constexpr (G::QLDS) *reinterpret_cast<u32x4*>(QT + s * KP + c) = qr[i];
+        for (int i = 0; i < G::VPIECES; i++) {
+          const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+          if (e < kFC * (kDV / EL)) vr[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)(t0 + min(s, nv - 1)) * kDV + c);
+        }
+#pragma unroll
+        for (int i = 0; i < G::VPIECES; i++) {
+          const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
+          if (e < kFC * (kDV / EL)) *reinterpret_cast<u32x4*>(VT + s * VP + c) = s < nv ? vr[i] : zero4;
         }
       }
+      __syncthreads();
     }
-    {
-      u32x4 vr[G::VPIECES];
-#pragma unroll
-      for (int i = 0; i < G::VPIECES; i++) {
-        const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
-        if (e < kFC * (kDV / EL)) vr[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)(t0 + min(s, nv - 1)) * kDV + c);
-      }
-#pragma unroll
-      for (int i = 0; i < G::VPIECES; i++) {
-        const int e = tid + 256 * i, s = e / (kDV / EL), c = (e % (kDV / EL)) * EL;
-        if (e < kFC * (kDV / EL)) *reinterpret_cast<u32x4*>(VT + s * VP + c) = s < nv ? vr[i] : zero4;
-      }
-    }
-    __syncthreads();
 
     if constexpr (!STATE_ONLY) {
     // this lane's query (column n32 of the transposed tiles), clamped into the chunk
