@@ -1,7 +1,7 @@
 """Replays of captured HIP graphs give the eager results (bit for bit: the kernels are deterministic).
 
-The prefill (phase table, pass 1, pass 3) and a run of decode steps are captured once; each replay is
-separated by unrelated eager work and a synchronisation, and every replay is compared with the eager
+The prefill (phase table, pass 1, pass 3), a run of decode steps and the backward pass are captured once; each
+replay is separated by unrelated eager work and a synchronisation, and every replay is compared with the eager
 output of the same call.  bench.py times graph replays of the same calls.
 """
 import numpy as np
@@ -150,3 +150,41 @@ def test_serving_decode_graph_replays_match_eager(torch_dev):
         assert torch.equal(o1, e1) and torch.equal(o2, e2), rep
         for got, w in zip((S, z, Sc, zc), want):
             assert torch.equal(got, w), rep
+
+
+@pytest.mark.parametrize("p", [1, 2])
+def test_backward_graph_replays_match_eager(torch_dev, p):
+    """The backward pass captured once (at p = 1 several pieces per sequence: increments, forward direction,
+    increments, reverse direction), replayed three times between unrelated eager work."""
+    import root_parity_gated_amd as rpg
+
+    torch = torch_dev
+    B, H, T = 1, 3, 700
+    q, k, v, om = si.attention_inputs(41 + p, B, H, T, "bf16")
+    qd, kd, vd = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
+    g = torch.from_numpy(np.random.default_rng(43).standard_normal((B, H, T, 64)).astype(np.float32)).cuda()
+    g = g.to(torch.bfloat16)
+    prm = rpg.Params(omega=torch.from_numpy(om).cuda())
+    ws = torch.empty((rpg.sanatan_attention_backward_workspace_bytes(B, H, T, rpg.SANATAN_BF16, prm),),
+                     dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
+            torch.empty((H, 64), dtype=torch.float32, device="cuda")]
+    call = lambda: rpg.sanatan_attention_backward(qd, kd, vd, g, p, prm, dq=outs[0], dk=outs[1], dv=outs[2],
+                                                  domega=outs[3], ws=ws)
+    call()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in outs]
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call()
+    other = torch.empty((B, H, T, 64), device="cuda")
+    for rep in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        other.normal_()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dq", "dk", "dv", "domega"), outs, eager):
+            assert torch.equal(x, y), (rep, name)
