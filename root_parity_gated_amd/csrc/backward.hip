@@ -41,6 +41,11 @@ hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v,
                               const float* rho, const float* omega, int nph, float kr, void* dq, void* dk, void* dv,
                               float* dom_part, float* slots, hipStream_t stream);
 
+// backward_quadratic.hip: the bf16 feature gradients and dv at p = 2, software-pipelined
+hipError_t launch_bwd_quadratic_bf16(const void* phiq, const void* phik, const void* v, const void* g,
+                                     const float2* stats, int B, int H, int T, float* dphiq, float* dphik, void* dv,
+                                     hipStream_t stream);
+
 namespace {
 
 constexpr int kBlk = 32;  // tokens per staged block (and per wave tile)
@@ -363,12 +368,12 @@ __global__ __launch_bounds__(256) void bwd_jacobian_kernel(const T* __restrict__
   for (int i = 0; i < 8; i++) dom[i] = 0.0f;
   if (t < Tn) {
     const size_t base = (size_t)bh * Tn + t;
-    float x[8], rh[8], gch[6][8];
+    float x[8], rh[8], gch[6][8];  // gch[0] unused
     ld8c(u + base * kD + a0, x);
 #pragma unroll
     for (int i = 0; i < 8; i++) rh[i] = rho[(size_t)t * kD + a0 + i];
 #pragma unroll
-    for (int c = 0; c < 6; c++) {
+    for (int c = 1; c < 6; c++) {  // channel 0 (the constant feature) has no derivative
       const float4 p0 = *reinterpret_cast<const float4*>(dphi + base * kF + c * kD + a0);
       const float4 p1 = *reinterpret_cast<const float4*>(dphi + base * kF + c * kD + a0 + 4);
       gch[c][0] = p0.x; gch[c][1] = p0.y; gch[c][2] = p0.z; gch[c][3] = p0.w;
@@ -472,9 +477,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   } else {
     if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) return e;
 
-  // feature-gradient passes: NFT feature tiles of 32 each per pass (the 32 x 32 NFT fp32 slice of a wave in
-  // accumulators, next to its 20 operand fragments); dv comes with the first dK pass
-  constexpr int NFT = sizeof(T) == 4 ? 4 : 6;
+  // feature gradients over the feature tiles of channels 1..5 (tiles 2..11: channel 0 is the constant 1, whose
+  // gradient the Jacobian does not use).  bf16 runs the pipelined one-pass kernels of backward_quadratic.hip;
+  // fp32, whose operand fragments need twice the registers, takes 4 + 4 + 2 tiles in three passes here, dv
+  // with the first dK pass.
   const int nqb = (Tn + 127) / 128, nkb_all = (Tn + kBlk - 1) / kBlk, BH = B * H;
   static std::atomic<bool> attr[8][64];
   int dev = 0;
@@ -484,8 +490,8 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   const T* ck = phik;
   const T* cv = static_cast<const T*>(v);
   const T* cg = static_cast<const T*>(g);
-  auto pass = [&](auto Ft0, auto WithV, int slot) -> hipError_t {
-    constexpr int FT0 = decltype(Ft0)::value;
+  auto pass = [&](auto Ft0, auto Nft, auto WithV, int slot) -> hipError_t {
+    constexpr int FT0 = decltype(Ft0)::value, NFT = decltype(Nft)::value;
     constexpr bool WV = decltype(WithV)::value;
     hipError_t err = set_lds(bwd_dq_kernel<T, P, FT0, NFT>, G::lds, attr[2 * slot][dev]);
     if (err != hipSuccess) return err;
@@ -497,10 +503,19 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                        static_cast<T*>(dv), Tn, BH, nkb_all);
     return hipGetLastError();
   };
-  if ((e = pass(std::integral_constant<int, 0>(), std::true_type(), 0)) != hipSuccess) return e;
-  if ((e = pass(std::integral_constant<int, NFT>(), std::false_type(), 1)) != hipSuccess) return e;
-  if constexpr (3 * NFT == 12) {
-    if ((e = pass(std::integral_constant<int, 2 * NFT>(), std::false_type(), 2)) != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2) {
+    if ((e = launch_bwd_quadratic_bf16(phiq, phik, v, g, stats, B, H, Tn, dphiq, dphik, dv, stream)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = pass(std::integral_constant<int, 2>(), std::integral_constant<int, 4>(), std::true_type(), 0)) !=
+        hipSuccess)
+      return e;
+    if ((e = pass(std::integral_constant<int, 6>(), std::integral_constant<int, 4>(), std::false_type(), 1)) !=
+        hipSuccess)
+      return e;
+    if ((e = pass(std::integral_constant<int, 10>(), std::integral_constant<int, 2>(), std::false_type(), 2)) !=
+        hipSuccess)
+      return e;
   }
   }
   const int BH = B * H, ntiles = (Tn + 31) / 32, nblk = BH * ntiles;
