@@ -192,9 +192,56 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
 #pragma unroll
   for (int i = 0; i < 16; i++) cz[i] = 0.0f;
 
-  // Phase A: the score tiles of block bn (buffer Bn) into parity par ^ 1 (with NXT), the weights of block bc
-  // (parity par; with CUR) formed between their MFMAs.  Phase B: the gradient products of block bc.
+  // Weights of the current block.  Register i of a tile is row r = 8 (i / 4) + 4 h + i % 4 of the block, column
+  // n32 (the owned token).  SIDE 1 reads the per-row scalars of registers 2 jj and 2 jj + 1 (rows 8 (jj / 2) +
+  // 4 h + 2 (jj % 2) + 0..1) a little ahead of their use.
   bf16x8 G0, G1, R0, R1, W0, W1;
+  float gw[16], ww[16];
+  float2 qa[8], qn[8], qc[8];
+  auto ldq = [&](const char* Bc, int jj) {
+    const float* S = reinterpret_cast<const float*>(Bc + G::f_bytes + G::v_bytes);
+    const int r = 8 * (jj >> 1) + 4 * h + 2 * (jj & 1);
+    qa[jj] = *reinterpret_cast<const float2*>(S + r);
+    qn[jj] = *reinterpret_cast<const float2*>(S + kQB + r);
+    qc[jj] = *reinterpret_cast<const float2*>(S + 2 * kQB + r);
+  };
+  auto weight = [&](const f32x16& sct, const f32x16& gvt, int i, bool diag) {
+    const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+    const float kap = sct[i] + (float)kD;  // channel 0 adds exactly d
+    const float kp1 = P == 2 ? kap : 1.0f;
+    float a, nb;
+    if constexpr (SIDE == 0) {
+      a = la;
+      nb = lnb;
+    } else {
+      a = (i & 1) ? qa[i >> 1].y : qa[i >> 1].x;
+      nb = (i & 1) ? qn[i >> 1].y : qn[i >> 1].x;
+    }
+    float gg = kp1 * fmaf(a, gvt[i], nb);
+    // the diagonal block: SIDE 0 drops keys after the query, SIDE 1 queries before the key
+    const bool drop = SIDE == 0 ? r > n32 : r < n32;
+    gw[i] = diag && drop ? 0.0f : gg;
+    if constexpr (SIDE == 1) {
+      const float wt = (P == 2 ? kap * kap : kap) * ((i & 1) ? qc[i >> 1].y : qc[i >> 1].x);
+      ww[i] = diag && drop ? 0.0f : wt;
+    }
+  };
+  // pack registers o .. o + 7 of the weights: G (and its residual) and W
+  auto pack_half = [&](int o, bf16x8& Gh, bf16x8& Rh, bf16x8& Wh) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) x[i] = gw[o + i];
+    Gh = pack8f<__bf16>(x);
+    Rh = residual8<__bf16>(x, Gh);
+    if constexpr (SIDE == 1) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = ww[o + i];
+      Wh = pack8f<__bf16>(x);
+    }
+  };
+
+  // Phase A: the score tiles of block bn (buffer Bn) into parity par ^ 1 (with NXT), and (with CUR) registers
+  // 0..7 of block bc's weights (parity par) formed between their MFMAs, one register per K-step.
   auto phase_a = [&](auto Par, auto Nxt, auto Cur, const char* Bn, const char* Bc, bool diag) {
     constexpr int par = decltype(Par)::value;
     constexpr bool nxt = decltype(Nxt)::value, cur = decltype(Cur)::value;
@@ -207,44 +254,10 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
 #pragma unroll
       for (int j = 0; j < PD; j++) Ar[j] = *(lds_bf16x8*)(frow + 32 * j);
     }
-    // SIDE 1: the per-row scalars of block bc for registers 2 jj and 2 jj + 1 (rows 8 (jj / 2) + 4 h + 2 (jj % 2)
-    // + 0..1), read two K-steps before their use
-    const float* S = reinterpret_cast<const float*>(Bc + G::f_bytes + G::v_bytes);
-    float2 qa[8], qn[8], qc[8];
-    auto ldq = [&](int jj) {
-      const int r = 8 * (jj >> 1) + 4 * h + 2 * (jj & 1);
-      qa[jj] = *reinterpret_cast<const float2*>(S + r);
-      qn[jj] = *reinterpret_cast<const float2*>(S + kQB + r);
-      qc[jj] = *reinterpret_cast<const float2*>(S + 2 * kQB + r);
-    };
     if constexpr (cur && SIDE == 1) {
-      ldq(0);
-      ldq(1);
+      ldq(Bc, 0);
+      ldq(Bc, 1);
     }
-    float gw[16], ww[16];
-    // weights of register i (row r = 8 (i / 4) + 4 h + i % 4 of the tile, column n32)
-    auto weight = [&](int i) {
-      const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-      const float kap = sc[par][i] + (float)kD;  // channel 0 adds exactly d
-      const float kp1 = P == 2 ? kap : 1.0f;
-      float a, nb;
-      if constexpr (SIDE == 0) {
-        a = la;
-        nb = lnb;
-      } else {
-        a = (i & 1) ? qa[i >> 1].y : qa[i >> 1].x;
-        nb = (i & 1) ? qn[i >> 1].y : qn[i >> 1].x;
-      }
-      float gg = kp1 * fmaf(a, gv[par][i], nb);
-      // the diagonal block: SIDE 0 drops keys after the query, SIDE 1 queries before the key
-      const bool drop = SIDE == 0 ? r > n32 : r < n32;
-      gg = diag && drop ? 0.0f : gg;
-      gw[i] = gg;
-      if constexpr (SIDE == 1) {
-        const float wt = (P == 2 ? kap * kap : kap) * ((i & 1) ? qc[i >> 1].y : qc[i >> 1].x);
-        ww[i] = diag && drop ? 0.0f : wt;
-      }
-    };
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NJ + 4; j++) {
@@ -265,55 +278,53 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
         }
       }
       if constexpr (cur) {
-        // registers 0..7 over steps 0..3, packed at step 4; registers 8..15 over steps 5..8, packed at step 9
-        if (j < 9 && j != 4) {
-          const int jj = j < 4 ? j : j - 1;
-          if (SIDE == 1 && jj + 2 < 8) ldq(jj + 2);
-          weight(2 * jj);
-          weight(2 * jj + 1);
-        } else if (j == 4 || j == 9) {
-          const int o = j == 4 ? 0 : 8;
-          float x[8];
-#pragma unroll
-          for (int i = 0; i < 8; i++) x[i] = gw[o + i];
-          const bf16x8 Gr = pack8f<__bf16>(x);
-          const bf16x8 Rr = residual8<__bf16>(x, Gr);
-          if (j == 4) G0 = Gr, R0 = Rr;
-          else G1 = Gr, R1 = Rr;
-          if constexpr (SIDE == 1) {
-#pragma unroll
-            for (int i = 0; i < 8; i++) x[i] = ww[o + i];
-            (j == 4 ? W0 : W1) = pack8f<__bf16>(x);
-          }
+        if (j < 8) {
+          if (SIDE == 1 && (j & 1) && (j >> 1) + 2 < 4) ldq(Bc, (j >> 1) + 2);
+          weight(sc[par], gv[par], j, diag);
+        } else if (j == 8) {
+          pack_half(0, G0, R0, W0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   const int tf_lane = tok_lane_bytes(FP, l), tv_lane = tok_lane_bytes(VP, l);
-  auto phase_b = [&](const char* Bc) {
+  // Phase B: the gradient products of block bc, first over its keys 0..15 (G0, R0) for all ten tiles, with
+  // registers 8..15 of the weights formed between them, then over keys 16..31 (G1, R1).
+  auto phase_b = [&](auto Par, const char* Bc, bool diag) {
+    constexpr int par = decltype(Par)::value;
     // (opaque to the optimiser, so that every read adds its constant in the instruction's offset field
     // instead of the loop keeping one hoisted address register per read)
     lds_cchar* F = (lds_cchar*)Bc + tf_lane;
     lds_cchar* V = (lds_cchar*)Bc + G::f_bytes + tv_lane;
     asm volatile("" : "+v"(F), "+v"(V));
-    // Phi^T fragments (tokens of the block as K-slots, feature column n32 of tile f), two tiles ahead
-    bf16x8 A0[3], A1[3];
+    // Phi^T fragments (tokens tok0.. of the block as K-slots, feature column n32 of tile f), two tiles ahead
+    bf16x8 A[3];
 #pragma unroll
-    for (int f = 0; f < 2; f++) {
-      A0[f] = tokfrag_at(F, FP, 0, 32 * f);
-      A1[f] = tokfrag_at(F, FP, 16, 32 * f);
-    }
+    for (int hf = 0; hf < 2; hf++) {
+      const int tok0 = 16 * hf;
 #pragma unroll
-    for (int f = 0; f < NT; f++) {
-      if (f + 2 < NT) {
-        A0[(f + 2) % 3] = tokfrag_at(F, FP, 0, 32 * (f + 2));
-        A1[(f + 2) % 3] = tokfrag_at(F, FP, 16, 32 * (f + 2));
+      for (int f = 0; f < 2; f++) A[f] = tokfrag_at(F, FP, tok0, 32 * f);
+      if (hf == 0 && SIDE == 1) {
+        ldq(Bc, 4);
+        ldq(Bc, 5);
       }
-      mma32(acc[f], A0[f % 3], G0);
-      mma32(acc[f], A1[f % 3], G1);
-      mma32(acc[f], A0[f % 3], R0);
-      mma32(acc[f], A1[f % 3], R1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < NT; f++) {
+        if (f + 2 < NT) A[(f + 2) % 3] = tokfrag_at(F, FP, tok0, 32 * (f + 2));
+        mma32(acc[f], A[f % 3], hf ? G1 : G0);
+        mma32(acc[f], A[f % 3], hf ? R1 : R0);
+        if (hf == 0) {
+          if (f < 8) {
+            if (SIDE == 1 && (f & 1) && (f >> 1) + 6 < 8) ldq(Bc, (f >> 1) + 6);
+            weight(sc[par], gv[par], 8 + f, diag);
+          } else if (f == 8) {
+            pack_half(8, G1, R1, W1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if constexpr (SIDE == 1) {
 #pragma unroll
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
       phase_a(Par, std::true_type(), std::false_type(), Bn, Bc, diag);
     else if (cur)
       phase_a(Par, std::false_type(), std::true_type(), Bn, Bc, diag);
-    if (cur) phase_b(Bc);
+    if (cur) phase_b(Par, Bc, diag);
     __syncthreads();
   };
   // the first block's scores (parity 0)
