@@ -15,7 +15,7 @@
 //
 // Work split.  Phi(Q) and Phi(K) are featurized once into the workspace (element type of the call).  At p = 1
 // the statistics, the feature gradients and dv come from the chunked recurrences of backward_chunked.hip.  At
-// p = 2 a statistics pass (the forward kernel in its STATS mode) writes (Dn_t, delta_t); then, flash-attention
+// p = 2 a statistics pass (the forward kernel in its STATS mode) writes (1 / Dn_t, delta_t); then, flash-attention
 // style, one kernel walks key blocks for each 32-query tile of a wave (dPhi(Q)), and one walks query blocks
 // for each 32-key tile (dPhi(K) and dv); both recompute the score and <g, v> tiles on 32x32x16 bf16 MFMA
 // (32x32x2 fp32 for fp32 inputs).  A wave keeps a 32 x 192 fp32 slice of its gradient in accumulators (32 x 128
@@ -41,10 +41,11 @@ hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v,
                               const float* rho, const float* omega, int nph, float kr, void* dq, void* dk, void* dv,
                               float* dom_part, float* slots, hipStream_t stream);
 
-// backward_quadratic.hip: the bf16 feature gradients and dv at p = 2, software-pipelined
+// backward_quadratic.hip: the bf16 gradients at p = 2 (feature gradients, Jacobian and omega partials fused)
 hipError_t launch_bwd_quadratic_bf16(const void* phiq, const void* phik, const void* v, const void* g,
-                                     const float2* stats, int B, int H, int T, float* dphiq, float* dphik, void* dv,
-                                     hipStream_t stream);
+                                     const float2* stats, int B, int H, int T, const void* q, const void* k,
+                                     const float* rho, const float* omega, int nph, float kr, void* dq, void* dk,
+                                     void* dv, float* dom_q, float* dom_k, hipStream_t stream);
 
 namespace {
 
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const T* __restrict__ ph
 #pragma unroll
   for (int j = 0; j < 4; j++) GF[j] = row_frag<T>(g + sq * kDV, kDV, tc, 16 * j + 8 * h);
   const float2 stt = stats[sq + tc];
-  const float inv_dn = 1.0f / stt.x, delta = stt.y;
+  const float inv_dn = stt.x, delta = stt.y;
 
   f32x16 acc[NFT];
 #pragma unroll
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(const T* __restrict__ p
     for (int i = 0; i < 16; i++) {
       const int r = 8 * (i >> 2) + 4 * h + (i & 3), t = t0 + r;
       const float2 st = St[r];
-      const float inv_dn = 1.0f / st.x;
+      const float inv_dn = st.x;
       const float kap = at[i];
       const bool keep = s <= t && t < Tn;
       gl[i] = keep ? (P == 2 ? 2.0f * kap : 1.0f) * (gv[i] - st.y) * inv_dn : 0.0f;
@@ -504,7 +505,9 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     return hipGetLastError();
   };
   if constexpr (sizeof(T) == 2) {
-    if ((e = launch_bwd_quadratic_bf16(phiq, phik, v, g, stats, B, H, Tn, dphiq, dphik, dv, stream)) != hipSuccess)
+    const size_t side = (size_t)BH * nkb_all * kD;  // omega partial rows of one side
+    if ((e = launch_bwd_quadratic_bf16(phiq, phik, v, g, stats, B, H, Tn, q, k, rho, mc.omega, mc.nph, mc.kr, dq, dk,
+                                       dv, dom, dom + side, stream)) != hipSuccess)
       return e;
   } else {
     if ((e = pass(std::integral_constant<int, 2>(), std::integral_constant<int, 4>(), std::true_type(), 0)) !=
@@ -522,7 +525,7 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   int nparts = ntiles;  // omega partial rows per (side, sequence)
   if constexpr (P == 1) {
     nparts = bwd_chunked_pieces(B, H, Tn);  // the chunk kernels applied the Jacobian themselves
-  } else {
+  } else if constexpr (sizeof(T) == 4) {  // (bf16: the gradient kernels applied it)
     hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(q), dphiq,
                        rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dq), dom);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -48,7 +48,22 @@ struct Q2Geom {
   static_assert(buf_bytes % 16 == 0, "buffers must stay 16-byte aligned");
 };
 
-constexpr int kRawBufferWord3 = 0x00020000;  // descriptor word 3: the gfx9-family raw-buffer format
+// LDS read distances: score fragments kPD K-steps ahead of their MFMA; gradient-side fragments kRB - 1 tiles
+// (two MFMAs each) ahead
+constexpr int kPD = 4, kRB = 3;
+constexpr int RB = kRB;
+
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Inputs of the fused Jacobian: the owned side's raw rows u [BH][T][d], the phase table [T][d] (revolutions),
+// the anchors omega [nph][d] and the gate constant.
+struct JacIn {
+  const __bf16* u;
+  const float* rho;
+  const float* omega;
+  int nph, H;
+  float kr;
+};  // descriptor word 3: the gfx9-family raw-buffer format
 
 // Transposing reads of a token-major bf16 tile (the operand of lds_tokfrag): the lane's part of the byte
 // address, fixed per lane, so that a read at (tok0, col0) only adds a constant to it.
@@ -73,9 +88,9 @@ template <int P, int SIDE>
 __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restrict__ phiq,
                                                           const __bf16* __restrict__ phik,
                                                           const __bf16* __restrict__ v, const __bf16* __restrict__ g,
-                                                          const float2* __restrict__ stats,
-                                                          float* __restrict__ dphi, __bf16* __restrict__ dv, int Tn,
-                                                          int BH, int nqb) {
+                                                          const float2* __restrict__ stats, JacIn jin,
+                                                          __bf16* __restrict__ du, float* __restrict__ dom_part,
+                                                          __bf16* __restrict__ dv, int Tn, int BH, int nqb) {
   using G = Q2Geom;
   constexpr int NJ = G::NJ, NT = G::NT, FP = G::FP, VP = G::VP;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -149,12 +164,12 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
     }
     if constexpr (SIDE == 1) {
       if (tid < kQB) {
-        // rows past the end carry Dn = 0: their weights are zero
+        // rows past the end carry 1 / Dn = 0: their weights are zero
         float* S = reinterpret_cast<float*>(B_ + G::f_bytes + G::v_bytes);
-        const float a = rs.x > 0.0f ? (float)P / rs.x : 0.0f;
+        const float a = (float)P * rs.x;
         S[tid] = a;
         S[kQB + tid] = -a * rs.y;
-        S[2 * kQB + tid] = rs.x > 0.0f ? 1.0f / rs.x : 0.0f;
+        S[2 * kQB + tid] = rs.x;
       }
     }
   };
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
   float la = 0.0f, lnb = 0.0f;  // SIDE 0: the owned query's p / Dn and -(p / Dn) delta
   if constexpr (SIDE == 0) {
     const float2 st = stats[sq + oc];
-    la = (float)P / st.x;
+    la = (float)P * st.x;
     lnb = -la * st.y;
   }
   stash(bbeg);
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
     lds_cchar* frow = (lds_cchar*)Bn + (n32 * FP + 8 * h) * 2;
     lds_cchar* vrow = (lds_cchar*)Bn + G::f_bytes + (n32 * VP + 8 * h) * 2;
     asm volatile("" : "+v"(frow), "+v"(vrow));
-    constexpr int PD = 4;  // feature fragments are read PD K-steps ahead of their MFMA
+    constexpr int PD = kPD;  // feature fragments are read PD K-steps ahead of their MFMA
     bf16x8 Ar[PD];
     if constexpr (nxt) {
 #pragma unroll
@@ -298,13 +313,13 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
     lds_cchar* F = (lds_cchar*)Bc + tf_lane;
     lds_cchar* V = (lds_cchar*)Bc + G::f_bytes + tv_lane;
     asm volatile("" : "+v"(F), "+v"(V));
-    // Phi^T fragments (tokens tok0.. of the block as K-slots, feature column n32 of tile f), two tiles ahead
-    bf16x8 A[3];
+    // Phi^T fragments (tokens tok0.. of the block as K-slots, feature column n32 of tile f), RB - 1 tiles ahead
+    bf16x8 A[RB];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
       const int tok0 = 16 * hf;
 #pragma unroll
-      for (int f = 0; f < 2; f++) A[f] = tokfrag_at(F, FP, tok0, 32 * f);
+      for (int f = 0; f < RB - 1; f++) A[f] = tokfrag_at(F, FP, tok0, 32 * f);
       if (hf == 0 && SIDE == 1) {
         ldq(Bc, 4);
         ldq(Bc, 5);
@@ -312,9 +327,9 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < NT; f++) {
-        if (f + 2 < NT) A[(f + 2) % 3] = tokfrag_at(F, FP, tok0, 32 * (f + 2));
-        mma32(acc[f], A[f % 3], hf ? G1 : G0);
-        mma32(acc[f], A[f % 3], hf ? R1 : R0);
+        if (f + RB - 1 < NT) A[(f + RB - 1) % RB] = tokfrag_at(F, FP, tok0, 32 * (f + RB - 1));
+        mma32(acc[f], A[f % RB], hf ? G1 : G0);
+        mma32(acc[f], A[f % RB], hf ? R1 : R0);
         if (hf == 0) {
           if (f < 8) {
             if (SIDE == 1 && (f & 1) && (f >> 1) + 6 < 8) ldq(Bc, (f >> 1) + 6);
@@ -362,14 +377,49 @@ __global__ __launch_bounds__(256, 1) void bwd_quad_kernel(const __bf16* __restri
     step(std::integral_constant<int, 1>(), b + 1);
   }
 
-  if (own >= Tn) return;
-  float* dst = dphi + (sq + own) * kF + kD;
+  // ---- the feature map's Jacobian, fused: lane (n32, h) holds, for its owned token, the gradient of channel c
+  // (1..5) at dim 32 e + 8 (i / 4) + 4 h + i % 4 in register i of tile 2 (c - 1) + e.  It writes du for those dims
+  // and the wave sums the omega gradients of its 32 tokens per dim in a fixed order (through a wave-private LDS
+  // tile), one partial row per 32-token tile of the sequence.
+  const bool valid = own < Tn;
+  float* red = reinterpret_cast<float*>(smem) + w * (kQB * (kD + 1));
+  const int hd = bh % jin.H;
+  const float* omrow = jin.omega + (size_t)(hd % jin.nph) * kD;
+  const __bf16* urow = jin.u + (sq + oc) * kD;
+  const float* rrow = jin.rho + (size_t)oc * kD;
+  __syncthreads();  // the streamed-block buffers are free
 #pragma unroll
-  for (int f = 0; f < NT; f++)
+  for (int e = 0; e < 2; e++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      *reinterpret_cast<float4*>(dst + 32 * f + 8 * j + 4 * h) =
-          make_float4(acc[f][4 * j], acc[f][4 * j + 1], acc[f][4 * j + 2], acc[f][4 * j + 3]);
+    for (int m = 0; m < 4; m++) {
+      const int a0 = 32 * e + 8 * m + 4 * h;
+      const u32x2 uw = *reinterpret_cast<const u32x2*>(urow + a0);
+      const bf16x4 ub = __builtin_bit_cast(bf16x4, uw);
+      const float4 rh = *reinterpret_cast<const float4*>(rrow + a0);
+      const float4 om = *reinterpret_cast<const float4*>(omrow + a0);
+      const float rha[4] = {rh.x, rh.y, rh.z, rh.w}, oma[4] = {om.x, om.y, om.z, om.w};
+      float dus[4];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; i4++) {
+        const int i = 4 * m + i4;
+        float dom;
+        feature_vjp((float)ub[i4], rha[i4], anchor_rev(oma[i4]), jin.kr, acc[e][i], acc[2 + e][i], acc[4 + e][i],
+                    acc[6 + e][i], acc[8 + e][i], dus[i4], dom);
+        red[n32 * (kD + 1) + a0 + i4] = valid ? dom : 0.0f;
+      }
+      if (valid) {
+        const u32x2 o = {pack_bf16x2(dus[0], dus[1]), pack_bf16x2(dus[2], dus[3])};
+        *reinterpret_cast<u32x2*>(du + (sq + own) * kD + a0) = o;
+      }
+    }
+  }
+  __syncthreads();
+  if (row0 < Tn) {
+    float sum = 0.0f;
+    for (int r = 0; r < kQB; r++) sum += red[r * (kD + 1) + l];
+    dom_part[((size_t)bh * nblk + row0 / kQB) * kD + l] = sum;
+  }
+  if (!valid) return;
   if constexpr (SIDE == 1) {
     __bf16* dvp = dv + (sq + own) * kDV;
 #pragma unroll
@@ -393,7 +443,9 @@ hipError_t set_lds_attr(Kern k, int bytes, std::atomic<bool>& flag) {
 
 template <int P>
 hipError_t launch_t(const __bf16* phiq, const __bf16* phik, const __bf16* v, const __bf16* g, const float2* stats,
-                    int B, int H, int Tn, float* dphiq, float* dphik, __bf16* dv, hipStream_t stream) {
+                    int B, int H, int Tn, const __bf16* q, const __bf16* k, const float* rho, const float* omega,
+                    int nph, float kr, __bf16* dq, __bf16* dk, __bf16* dv, float* dom_q, float* dom_k,
+                    hipStream_t stream) {
   static std::atomic<bool> attr[2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
@@ -401,24 +453,28 @@ hipError_t launch_t(const __bf16* phiq, const __bf16* phik, const __bf16* v, con
   hipError_t e = set_lds_attr(bwd_quad_kernel<P, 0>, Q2Geom::lds, attr[0][dev]);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_quad_kernel<P, 0>), dim3(BH * nqb), dim3(256), Q2Geom::lds, stream, phiq, phik, v, g,
-                     stats, dphiq, (__bf16*)nullptr, Tn, BH, nqb);
+                     stats, JacIn{q, rho, omega, nph, H, kr}, dq, dom_q, (__bf16*)nullptr, Tn, BH, nqb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = set_lds_attr(bwd_quad_kernel<P, 1>, Q2Geom::lds, attr[1][dev])) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_quad_kernel<P, 1>), dim3(BH * nqb), dim3(256), Q2Geom::lds, stream, phiq, phik, v, g,
-                     stats, dphik, dv, Tn, BH, nqb);
+                     stats, JacIn{k, rho, omega, nph, H, kr}, dk, dom_k, dv, Tn, BH, nqb);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// dPhi(q) and dPhi(k) (fp32 [BH][T][6d], channels 1..5 written) and dv (bf16 [BH][T][d_v]) from the featurized
-// operands and the statistics (Dn_t, delta_t) of the forward pass, p = 2.
+// dq, dk (through the feature map's Jacobian), dv (bf16 [BH][T][d]) and the omega partials (fp32, one row of d per
+// (side, sequence, 32-token tile): dom_q and dom_k each [BH][ceil(T / 32)][d]) from the featurized operands and
+// the statistics (1 / Dn_t, delta_t) of the forward pass, p = 2.  rho is the position phase table [T][d].
 hipError_t launch_bwd_quadratic_bf16(const void* phiq, const void* phik, const void* v, const void* g,
-                                     const float2* stats, int B, int H, int T, float* dphiq, float* dphik, void* dv,
-                                     hipStream_t stream) {
+                                     const float2* stats, int B, int H, int T, const void* q, const void* k,
+                                     const float* rho, const float* omega, int nph, float kr, void* dq, void* dk,
+                                     void* dv, float* dom_q, float* dom_k, hipStream_t stream) {
   return launch_t<2>(static_cast<const __bf16*>(phiq), static_cast<const __bf16*>(phik),
-                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(g), stats, B, H, T, dphiq, dphik,
-                     static_cast<__bf16*>(dv), stream);
+                     static_cast<const __bf16*>(v), static_cast<const __bf16*>(g), stats, B, H, T,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), rho, omega, nph, kr,
+                     static_cast<__bf16*>(dq), static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), dom_q, dom_k,
+                     stream);
 }
 
 }  // namespace sanatan

@@ -52,7 +52,7 @@ struct QGeom {
 
 // Two workgroups per CU for bf16; the fp32 operand fragments take the registers of one.
 // STATS (the backward pass's forward statistics): instead of o, write per query row the denominator
-// Dn = sum_s kappa^p + eps c^p and delta = <g_t, o_t> with g = dout, as float2 stats[bh][t].
+// 1 / Dn (Dn = sum_s kappa^p + eps c^p) and delta = <g_t, o_t> with g = dout, as float2 stats[bh][t].
 template <typename T, int P, int C0, bool STATS = false>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     const T* __restrict__ q, const T* __restrict__ phik, const T* __restrict__ v, T* __restrict__ out,
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
           for (int i4 = 0; i4 < 4; i4++) dot = fmaf(to_f32(gp[32 * vt + 8 * j + 4 * h + i4]), num[mq][vt][4 * j + i4], dot);
       dot = xor32_sum(dot);
       const float dn = den + eps_cp;
-      if (t < Tn && h == 0) stats[(size_t)bh * Tn + t] = make_float2(dn, dot / dn);
+      if (t < Tn && h == 0) stats[(size_t)bh * Tn + t] = make_float2(1.0f / dn, dot / dn);
       continue;
     }
     if (t < Tn) {
