@@ -281,8 +281,10 @@ sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, cons
  *   S4, z4 : NULL (zero start, no final state) or the compact four-channel state of
  *            sanatan_decode_step_four_channel, [B][H][3d+1][d_v] and [B][H][3d+1], in/out.
  *   Everything else as sanatan_prefill_chunked without `chunk` (this path walks 32-token chunks, one workgroup
- *   per sequence); ws: at least sanatan_prefill_four_channel_workspace_bytes() bytes, which hold Phi4(Q) and
- *   Phi4(K) in element type t.  The final state continues exactly in sanatan_decode_step_four_channel.
+ *   per sequence); ws: at least sanatan_prefill_four_channel_workspace_bytes() bytes: for bf16 the position
+ *   phase table (the features are formed while each chunk is staged), for fp32 Phi4(Q) and Phi4(K); then, when
+ *   sequences are split across compute units, the pieces' state increments.  The final state continues exactly
+ *   in sanatan_decode_step_four_channel.
  */
 size_t sanatan_prefill_four_channel_workspace_bytes(int B, int H, int T, sanatan_dtype t,
                                                     const sanatan_params* params);

@@ -33,8 +33,83 @@ namespace {
 
 constexpr int kFC = 32;  // chunk tokens
 
-// featurize one operand into the padded feature layout.  KIND 0: harmonics n = 1..NH; KIND 1: four-channel
-// compact, shared feature at 3d (IS_Q: it carries d instead of 1).  A thread owns 8 dims of one token.
+// The map's features of 8 consecutive dims a0 = 8 j .. 8 j + 7 of one token, in the padded feature layout:
+// emit(row0, val) receives features row0 + a0 .. row0 + a0 + 7 of each channel (and zeros for the padding rows up
+// to Fp).  KIND 0: harmonics n = 1..NH; KIND 1: four-channel compact, shared feature at 3d (IS_Q: it carries d
+// instead of 1).  x: the raw components, rho: their phases (revolutions), om4: their anchors (anchor_rev).
+template <int KIND, int NH, bool IS_Q, typename Emit>
+__device__ __forceinline__ void ext_features8(const float (&x)[8], const float (&rho)[8], const float (&om4)[8],
+                                              float kr, int j, int Fp, Emit&& emit) {
+  float cr[8], sr[8], rr[8], y[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    featurize1(x[i], rho[i], om4[i], kr, cr[i], sr[i], rr[i]);
+    y[i] = x[i] * rcp_hw(fmaf(fabsf(x[i]), 2.0f, 2.0f)) + rho[i];  // the rotated angle in revolutions, as featurize1
+  }
+  float tmp[8];
+  if constexpr (KIND == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = 1.0f;
+    emit(0, tmp);
+    emit((2 * NH + 1) * kD, rr);
+#pragma unroll
+    for (int n = 1; n <= NH; n++) {
+      float c[8], sn[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        c[i] = n == 1 ? cr[i] : cos_rev((float)n * y[i]);
+        sn[i] = n == 1 ? sr[i] : sin_rev((float)n * y[i]);
+      }
+      emit((2 * n - 1) * kD, c);
+      emit((2 * n) * kD, sn);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        c[i] *= rr[i];
+        sn[i] *= rr[i];
+      }
+      emit((2 * NH + 2 * n) * kD, c);
+      emit((2 * NH + 2 * n + 1) * kD, sn);
+    }
+    // zero padding past (2 + 4 NH) d
+    constexpr int Fr = (2 + 4 * NH) * kD;
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = 0.0f;
+    for (int f = Fr; f < Fp; f += kD) emit(f, tmp);
+  } else {
+    // internal order r, r cos, r sin (d each), then the shared feature (d for a query, 1 for a key) and zero
+    // padding; the caller's compact state keeps the shared row first, and the prefill maps rows between the two
+    float rc[8], rs[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      rc[i] = rr[i] * cr[i];
+      rs[i] = rr[i] * sr[i];
+    }
+    emit(0, rr);
+    emit(kD, rc);
+    emit(2 * kD, rs);
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = (j == 0 && i == 0) ? (IS_Q ? (float)kD : 1.0f) : 0.0f;
+    emit(3 * kD, tmp);  // the shared feature, then zeros up to 3 d + 64
+#pragma unroll
+    for (int i = 0; i < 8; i++) tmp[i] = 0.0f;
+    for (int f = 4 * kD; f < Fp; f += kD) emit(f, tmp);
+  }
+}
+
+// 8 features as one 16-byte (bf16) or two 16-byte (fp32) stores
+__device__ __forceinline__ void put8(__bf16* o, const float (&val)[8]) {
+  bf16x8 w;
+#pragma unroll
+  for (int i = 0; i < 8; i++) w[i] = (__bf16)val[i];
+  *reinterpret_cast<bf16x8*>(o) = w;
+}
+__device__ __forceinline__ void put8(float* o, const float (&val)[8]) {
+  *reinterpret_cast<float4*>(o) = make_float4(val[0], val[1], val[2], val[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(val[4], val[5], val[6], val[7]);
+}
+
+// featurize one operand into the padded feature layout in global memory (the fp32 prefill's operands).  A thread
+// owns 8 dims of one token.
 template <typename TIn, typename TOut, int KIND, int NH, bool IS_Q>
 __global__ __launch_bounds__(256) void featurize_ext_kernel(const TIn* __restrict__ u, TOut* __restrict__ phi, int H,
                                                             int T, int Fp, int64_t pos0,
@@ -46,75 +121,14 @@ __global__ __launch_bounds__(256) void featurize_ext_kernel(const TIn* __restric
   const int hd = bh % H;
   const TIn* up = u + ((size_t)bh * T + t) * kD + a0;
   TOut* o = phi + ((size_t)bh * T + t) * Fp;
-  float cr[8], sr[8], rr[8], y[8];
+  float x[8], rho[8], om4[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const float om4 = anchor_rev(omega[(size_t)(hd % nph) * kD + a0 + i]);
-    const float rho = phase_at(pos0 + t, phase_step(a0 + i, log2_base));
-    const float x = to_f32(up[i]);
-    featurize1(x, rho, om4, kr, cr[i], sr[i], rr[i]);
-    y[i] = x * rcp_hw(fmaf(fabsf(x), 2.0f, 2.0f)) + rho;  // the rotated angle in revolutions, as featurize1
+    om4[i] = anchor_rev(omega[(size_t)(hd % nph) * kD + a0 + i]);
+    rho[i] = phase_at(pos0 + t, phase_step(a0 + i, log2_base));
+    x[i] = to_f32(up[i]);
   }
-  auto put = [&](int row0, const float (&val)[8]) {  // 8 consecutive features, one vector store
-    if constexpr (sizeof(TOut) == 2) {
-      bf16x8 w;
-#pragma unroll
-      for (int i = 0; i < 8; i++) w[i] = (__bf16)val[i];
-      *reinterpret_cast<bf16x8*>(o + row0 + a0) = w;
-    } else {
-      float* d = reinterpret_cast<float*>(o + row0 + a0);
-      *reinterpret_cast<float4*>(d) = make_float4(val[0], val[1], val[2], val[3]);
-      *reinterpret_cast<float4*>(d + 4) = make_float4(val[4], val[5], val[6], val[7]);
-    }
-  };
-  float tmp[8];
-  if constexpr (KIND == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) tmp[i] = 1.0f;
-    put(0, tmp);
-    put((2 * NH + 1) * kD, rr);
-#pragma unroll
-    for (int n = 1; n <= NH; n++) {
-      float c[8], s[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        c[i] = n == 1 ? cr[i] : cos_rev((float)n * y[i]);
-        s[i] = n == 1 ? sr[i] : sin_rev((float)n * y[i]);
-      }
-      put((2 * n - 1) * kD, c);
-      put((2 * n) * kD, s);
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        c[i] *= rr[i];
-        s[i] *= rr[i];
-      }
-      put((2 * NH + 2 * n) * kD, c);
-      put((2 * NH + 2 * n + 1) * kD, s);
-    }
-    // zero padding past (2 + 4 NH) d
-    const int Fr = (2 + 4 * NH) * kD;
-#pragma unroll
-    for (int i = 0; i < 8; i++) tmp[i] = 0.0f;
-    for (int f = Fr; f < Fp; f += 64) put(f, tmp);
-  } else {
-    // internal order r, r cos, r sin (d each), then the shared feature (d for a query, 1 for a key) and zero
-    // padding; the caller's compact state keeps the shared row first, and the prefill maps rows between the two
-    float rc[8], rs[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      rc[i] = rr[i] * cr[i];
-      rs[i] = rr[i] * sr[i];
-    }
-    put(0, rr);
-    put(kD, rc);
-    put(2 * kD, rs);
-#pragma unroll
-    for (int i = 0; i < 8; i++) tmp[i] = (j == 0 && i == 0) ? (IS_Q ? (float)kD : 1.0f) : 0.0f;
-    put(3 * kD, tmp);  // the shared feature, then zeros up to 3 d + 64
-#pragma unroll
-    for (int i = 0; i < 8; i++) tmp[i] = 0.0f;
-    for (int f = 4 * kD; f < Fp; f += 64) put(f, tmp);
-  }
+  ext_features8<KIND, NH, IS_Q>(x, rho, om4, kr, j, Fp, [&](int row0, const float (&val)[8]) { put8(o + row0 + a0, val); });
 }
 
 template <typename T, int NFT>
@@ -137,12 +151,25 @@ struct FGeom {
   static_assert(kFC * (Fp / EL) % 256 == 0, "a feature chunk is a whole number of pieces per thread");
 };
 
-template <typename T, int NFT, bool STATE_ONLY>
+// Raw operands of the fused staging: q and k rows [BH][T][d], the phase table [T][d] (revolutions), the anchors
+// omega [nph][d] and the gate constant.
+struct FuseIn {
+  const __bf16* uq;
+  const __bf16* uk;
+  const float* rho;
+  const float* omega;
+  int nph, H;
+  float kr;
+};
+
+// FUSED (bf16): Phi(Q) and Phi(K) are not read from the workspace; each thread featurizes 8 dims of one token of
+// the chunk (map KIND, NH) straight into the LDS tiles while staging it.
+template <typename T, int NFT, bool STATE_ONLY, bool FUSED = false, int KIND = 0, int NH = 0>
 __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                               const T* __restrict__ v, T* __restrict__ out,
                                                               float* __restrict__ S, float* __restrict__ z, int Tn,
                                                               int Freal, float ceps, int P, float* __restrict__ slots,
-                                                              int shared_last) {
+                                                              int shared_last, FuseIn fu) {
   using G = FGeom<T, NFT>;
   typedef typename FragT<T>::type Frag;
   static_assert(NFT % 4 == 0, "feature tiles are dealt to four waves");
@@ -218,12 +245,30 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
   constexpr int EL = G::EL, FPC = Fp / EL;
   constexpr bool LQ = G::QLDS && !STATE_ONLY;
   constexpr int NPIECE = G::FPIECES * (LQ ? 2 : 1) + G::VPIECES;
-  constexpr bool PF = NPIECE <= 12;
+  constexpr bool PF = FUSED || NPIECE <= 12;
+  static_assert(!FUSED || sizeof(T) == 2, "the fused staging is for bf16 operands");
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 pk[PF ? G::FPIECES : 1], pq[PF && LQ ? G::FPIECES : 1], pv[PF ? G::VPIECES : 1];
-  auto pf_load = [&](int c0, int cnv) {
+  u32x4 pk[PF && !FUSED ? G::FPIECES : 1], pq[PF && LQ && !FUSED ? G::FPIECES : 1], pv[PF ? G::VPIECES : 1];
+  // (FUSED) this thread's token s = fs of a chunk and dims fa0 .. fa0 + 7: raw q and k pieces, their phases and
+  // anchors
+  const int fs = tid >> 3, fj = tid & 7, fa0 = 8 * fj;
+  u32x4 fk = zero4, fq = zero4;
+  float4 fr0 = make_float4(0.f, 0.f, 0.f, 0.f), fr1 = fr0;
+  float fom[8];
+  if constexpr (FUSED) {
 #pragma unroll
-    for (int i = 0; i < G::FPIECES; i++) {
+    for (int i = 0; i < 8; i++) fom[i] = anchor_rev(fu.omega[(size_t)((bh % fu.H) % fu.nph) * kD + fa0 + i]);
+  }
+  auto pf_load = [&](int c0, int cnv) {
+    if constexpr (FUSED) {
+      const size_t row = (size_t)(c0 + min(fs, cnv - 1));
+      fk = *reinterpret_cast<const u32x4*>(fu.uk + ((size_t)bh * Tn + row) * kD + fa0);
+      if constexpr (LQ) fq = *reinterpret_cast<const u32x4*>(fu.uq + ((size_t)bh * Tn + row) * kD + fa0);
+      fr0 = *reinterpret_cast<const float4*>(fu.rho + row * kD + fa0);
+      fr1 = *reinterpret_cast<const float4*>(fu.rho + row * kD + fa0 + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < (FUSED ? 0 : G::FPIECES); i++) {
       const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
       const size_t off = (size_t)(c0 + min(s, cnv - 1)) * Fp + c;
       pk[PF ? i : 0] = *reinterpret_cast<const u32x4*>(kp + off);
@@ -236,8 +281,30 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
     }
   };
   auto pf_store = [&](int cnv) {
+    if constexpr (FUSED) {
+      const float rh[8] = {fr0.x, fr0.y, fr0.z, fr0.w, fr1.x, fr1.y, fr1.z, fr1.w};
+      float x[8];
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, fk);
 #pragma unroll
-    for (int i = 0; i < G::FPIECES; i++) {
+      for (int i = 0; i < 8; i++) x[i] = (float)kb[i];
+      T* krow = KT + fs * KP + fa0;
+      if (fs < cnv) {
+        ext_features8<KIND, NH, false>(x, rh, fom, fu.kr, fj, Fp,
+                                       [&](int row0, const float (&val)[8]) { put8(krow + row0, val); });
+      } else {
+        for (int f = 0; f < Fp; f += kD) *reinterpret_cast<u32x4*>(krow + f) = zero4;  // keys past the end
+      }
+      if constexpr (LQ) {
+        const bf16x8 qb = __builtin_bit_cast(bf16x8, fq);
+#pragma unroll
+        for (int i = 0; i < 8; i++) x[i] = (float)qb[i];
+        T* qrow_ = QT + fs * KP + fa0;
+        ext_features8<KIND, NH, true>(x, rh, fom, fu.kr, fj, Fp,
+                                      [&](int row0, const float (&val)[8]) { put8(qrow_ + row0, val); });
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (FUSED ? 0 : G::FPIECES); i++) {
       const int e = tid + 256 * i, s = e / FPC, c = (e % FPC) * EL;
       *reinterpret_cast<u32x4*>(KT + s * KP + c) = s < cnv ? pk[PF ? i : 0] : zero4;
       if constexpr (LQ) *reinterpret_cast<u32x4*>(QT + s * KP + c) = pq[PF ? i : 0];
@@ -425,40 +492,60 @@ hipError_t set_lds_once(Kern k, int bytes, std::atomic<bool>& flag) {
   return e;
 }
 
+// bytes of the position phase table [T][d] fp32 at the front of a bf16 call's workspace (256-byte aligned)
+size_t ext_rho_bytes(int T) { return ((size_t)T * kD * sizeof(float) + 255) & ~(size_t)255; }
+
 template <typename TIn, int KIND, int NH, int NFT>
 hipError_t launch_fp_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
                        const MethodConsts& mc, float* S, float* z, void* out, void* ws, int Freal,
                        hipStream_t stream) {
   using G = FGeom<TIn, NFT>;
+  // bf16 featurizes while staging (FUSED); fp32 materializes Phi(Q) and Phi(K) first (its tiles would not fit
+  // in LDS side by side)
+  constexpr bool FUSED = sizeof(TIn) == 2;
   const int BH = B * H, ntiles = (Tn + 31) / 32;
-  TIn* phiq = static_cast<TIn*>(ws);
-  TIn* phik = phiq + (size_t)BH * Tn * G::Fp;
-  const dim3 fgrid((unsigned)((long long)BH * ntiles)), fblk(256);
-  hipLaunchKernelGGL((featurize_ext_kernel<TIn, TIn, KIND, NH, true>), fgrid, fblk, 0, stream,
-                     static_cast<const TIn*>(q), phiq, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
-                     ntiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((featurize_ext_kernel<TIn, TIn, KIND, NH, false>), fgrid, fblk, 0, stream,
-                     static_cast<const TIn*>(k), phik, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
-                     ntiles);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  TIn* phiq = nullptr;
+  TIn* phik = nullptr;
+  float* rho = nullptr;
+  float* slots = nullptr;
+  hipError_t e = hipSuccess;
+  if constexpr (FUSED) {
+    rho = static_cast<float*>(ws);
+    slots = reinterpret_cast<float*>(static_cast<char*>(ws) + ext_rho_bytes(Tn));
+    if ((e = launch_phase_table(rho, Tn, pos0, mc.log2_base, stream)) != hipSuccess) return e;
+  } else {
+    phiq = static_cast<TIn*>(ws);
+    phik = phiq + (size_t)BH * Tn * G::Fp;
+    slots = reinterpret_cast<float*>(phik + (size_t)BH * Tn * G::Fp);
+    const dim3 fgrid((unsigned)((long long)BH * ntiles)), fblk(256);
+    hipLaunchKernelGGL((featurize_ext_kernel<TIn, TIn, KIND, NH, true>), fgrid, fblk, 0, stream,
+                       static_cast<const TIn*>(q), phiq, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
+                       ntiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((featurize_ext_kernel<TIn, TIn, KIND, NH, false>), fgrid, fblk, 0, stream,
+                       static_cast<const TIn*>(k), phik, H, Tn, G::Fp, pos0, mc.omega, mc.nph, mc.log2_base, mc.kr,
+                       ntiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const FuseIn fu{reinterpret_cast<const __bf16*>(q), reinterpret_cast<const __bf16*>(k), rho, mc.omega, mc.nph, H,
+                  mc.kr};
   static std::atomic<bool> attr[64], attr1[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, false>, G::lds, attr[dev])) != hipSuccess) return e;
+  if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, false, FUSED, KIND, NH>, G::lds, attr[dev])) != hipSuccess)
+    return e;
   const int P = ext_pieces(B, H, Tn);
-  float* slots = reinterpret_cast<float*>(phik + (size_t)BH * Tn * G::Fp);
   if (P > 1) {
-    if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, true>, G::lds, attr1[dev])) != hipSuccess) return e;
-    hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, true>), dim3(BH * P), dim3(256), G::lds, stream, phiq, phik,
-                       static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots,
-                       KIND == 1 ? 1 : 0);
+    if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, true, FUSED, KIND, NH>, G::lds, attr1[dev])) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, true, FUSED, KIND, NH>), dim3(BH * P), dim3(256), G::lds,
+                       stream, phiq, phik, static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal,
+                       mc.ceps, P, slots, KIND == 1 ? 1 : 0, fu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, false>), dim3(BH * P), dim3(256), G::lds, stream, phiq, phik,
-                     static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps, P, slots,
-                     KIND == 1 ? 1 : 0);
+  hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, false, FUSED, KIND, NH>), dim3(BH * P), dim3(256), G::lds,
+                     stream, phiq, phik, static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps,
+                     P, slots, KIND == 1 ? 1 : 0, fu);
   return hipGetLastError();
 }
 
@@ -471,12 +558,13 @@ int ext_features_padded(int nh_or_zero) {
 }
 
 size_t ext_prefill_ws_bytes(int B, int H, int T, sanatan_dtype t, int nh_or_zero) {
-  const size_t el = t == SANATAN_BF16 ? 2 : 4;
   const size_t Fp = ext_features_padded(nh_or_zero);
   const int P = ext_pieces(B, H, T);
   const size_t slots = P > 1 ? (size_t)B * H * P * Fp * (kDV + 1) * sizeof(float) : 0;
-  // Phi(Q), Phi(K), then the piece slots (Phi's bytes are a multiple of 4: Fp is a multiple of 128)
-  return 2 * (size_t)B * H * T * Fp * el + slots;
+  // bf16: the phase table, then the piece slots; fp32: Phi(Q), Phi(K), then the piece slots (Phi's bytes are a
+  // multiple of 4: Fp is a multiple of 128)
+  if (t == SANATAN_BF16) return ext_rho_bytes(T) + slots;
+  return 2 * (size_t)B * H * T * Fp * sizeof(float) + slots;
 }
 
 // nh_or_zero: 1 or 2 harmonics, or 0 for the four-channel compact map
