@@ -375,7 +375,8 @@ def bench_decode(torch, rpg, si, batch, steps_timed, warmup, positions=False, co
     }
 
 
-def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_channel=False, per_call=None):
+def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_channel=False, per_call=None,
+                       train=False):
     """ms per call: (eager, graph-replayed).  Each call is one complete library call on resident inputs;
     the graph variant replays that call captured once, which removes the host launch overhead."""
     q, k, v, om = si.workload_inputs(w)
@@ -388,7 +389,12 @@ def bench_prefill_like(torch, rpg, si, w, steps, warmup, quadratic=False, four_c
         code = rpg.SANATAN_BF16 if w.dtype == "bf16" else rpg.SANATAN_F32
         ws = torch.empty((rpg.sanatan_quadratic_workspace_bytes(w.B, w.H, w.T, code, p),), dtype=torch.uint8,
                          device="cuda")
-        fn = lambda: rpg.sanatan_quadratic_ref_p2(qd, kd, vd, w.p, p, out=out, ws=ws, four_channel=four_channel)
+        if train:  # the training forward: also saves the backward pass's statistics
+            saved = torch.empty((rpg.lib().sanatan_quadratic_saved_bytes(w.B, w.H, w.T, None) // 4,),
+                                dtype=torch.float32, device="cuda")
+            fn = lambda: rpg.sanatan_quadratic_train(qd, kd, vd, w.p, p, out=out, saved=saved, ws=ws)
+        else:
+            fn = lambda: rpg.sanatan_quadratic_ref_p2(qd, kd, vd, w.p, p, out=out, ws=ws, four_channel=four_channel)
     else:
         ws = torch.empty((rpg.sanatan_prefill_workspace_bytes(w.B, w.H, w.T, w.chunk, p),), dtype=torch.uint8,
                          device="cuda")
@@ -420,9 +426,11 @@ def backward_p1_flops(B, H, T, C=32):
     return B * H * (linear + intra)
 
 
-def bench_backward(torch, rpg, si, w, p_exp, steps, warmup):
+def bench_backward(torch, rpg, si, w, p_exp, steps, warmup, saved=False):
     """ms per call (eager, graph-replayed) of sanatan_attention_backward on workload w's inputs with p = p_exp,
-    dout ~ N(0, 1) in the same dtype."""
+    dout ~ N(0, 1) in the same dtype.  saved: sanatan_attention_backward_saved instead, given the statistics one
+    sanatan_quadratic_train call saved before the timed region (a training step's forward pass; the forward itself
+    is timed as the quadratic workload)."""
     q, k, v, om = si.workload_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(x).cuda().to(dt) for x in (q, k, v))
@@ -434,8 +442,13 @@ def bench_backward(torch, rpg, si, w, p_exp, steps, warmup):
                      device="cuda")
     outs = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
             torch.empty((om.shape[0], D), dtype=torch.float32, device="cuda"))
-    fn = lambda: rpg.sanatan_attention_backward(qd, kd, vd, g, p_exp, p, dq=outs[0], dk=outs[1], dv=outs[2],
-                                                domega=outs[3], ws=ws)
+    if saved:
+        _, saved_stats = rpg.sanatan_quadratic_train(qd, kd, vd, p_exp, p)
+        fn = lambda: rpg.sanatan_attention_backward_saved(qd, kd, vd, g, saved_stats, p_exp, p, dq=outs[0],
+                                                          dk=outs[1], dv=outs[2], domega=outs[3], ws=ws)
+    else:
+        fn = lambda: rpg.sanatan_attention_backward(qd, kd, vd, g, p_exp, p, dq=outs[0], dk=outs[1], dv=outs[2],
+                                                    domega=outs[3], ws=ws)
     eager = timed_loop(torch, fn, steps, warmup)
     gr = graph_of(torch, fn)
     graph = timed_loop(torch, gr.replay, steps, warmup) if gr is not None else None
@@ -538,8 +551,8 @@ def mfma_line(fl, ms):
             "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-ONLY = ("prefill", "decode1", "decode64", "long", "quad", "quad4", "backward_p2", "backward_p1", "featurize",
-        "harmonics", "four_channel", "ragged")
+ONLY = ("prefill", "decode1", "decode64", "long", "quad", "quad4", "backward_p2", "backward_p2_saved", "backward_p1",
+        "featurize", "harmonics", "four_channel", "ragged")
 
 
 def main():
@@ -597,8 +610,9 @@ def main():
             rec["ms"] = bench_prefill_like(torch, rpg, si, si.QUAD_P2, small, 3, quadratic=True,
                                            four_channel=args.only == "quad4")
         elif args.only.startswith("backward"):
-            wb, pb = (si.QUAD_P2, 2) if args.only == "backward_p2" else (w, 1)
-            rec["ms"] = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2)
+            wb, pb = (w, 1) if args.only == "backward_p1" else (si.QUAD_P2, 2)
+            rec["ms"] = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2,
+                                       saved=args.only == "backward_p2_saved")
         elif args.only == "featurize":
             rec["ms"] = bench_featurize(torch, rpg, si, w, small, 3)[:2]
         elif args.only == "ragged":
@@ -688,6 +702,14 @@ def main():
         extras["quadratic_p2"] = {"workload": wq.name, "tokens_per_s": wq.B * wq.T / (qms * 1e-3), "ms": qms,
                                   "ms_eager": qms_e, "ms_graph": qms_g,
                                   "roofline": mfma_line(quadratic_flops(wq.B, wq.H, wq.T), qms)}
+        log(f"quadratic {wq.name}, training forward (saves the backward pass's statistics)")
+        qt_e, qt_g = bench_prefill_like(torch, rpg, si, wq, small, 3, quadratic=True, train=True)
+        qt = min(qt_e, qt_g) if qt_g is not None else qt_e
+        extras["quadratic_p2_train"] = {
+            "workload": wq.name + "_train", "tokens_per_s": wq.B * wq.T / (qt * 1e-3), "ms": qt, "ms_eager": qt_e,
+            "ms_graph": qt_g, "roofline": mfma_line(quadratic_flops(wq.B, wq.H, wq.T), qt),
+            "note": "sanatan_quadratic_train: the p=2 forward plus its saved fp32 output rows and 1/Dn, the input "
+                    "of backward_p2_saved"}
         log(f"quadratic {wq.name}, unclipped four-channel kernel")
         q4_e, q4_g = bench_prefill_like(torch, rpg, si, wq, small, 3, quadratic=True, four_channel=True)
         q4 = min(q4_e, q4_g) if q4_g is not None else q4_e
@@ -696,16 +718,20 @@ def main():
             "ms_eager": q4_e, "ms_graph": q4_g,
             "roofline": mfma_line(quadratic_flops(wq.B, wq.H, wq.T, features=4 * D), q4),
             "note": "unclipped four-channel kernel: 2 (4d + d_v) flops per causal pair"}
-        for key, wb, pb in (("backward_p2", si.QUAD_P2, 2), ("backward_p1", w, 1)):
-            log(f"backward {wb.name}, p={pb}")
-            be, bg = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2)
+        for key, wb, pb, sv in (("backward_p2", si.QUAD_P2, 2, False), ("backward_p2_saved", si.QUAD_P2, 2, True),
+                                ("backward_p1", w, 1, False)):
+            log(f"backward {wb.name}, p={pb}" + (", saved statistics" if sv else ""))
+            be, bg = bench_backward(torch, rpg, si, wb, pb, max(3, args.steps // 10), 2, saved=sv)
             bms = min(be, bg) if bg is not None else be
             bfl = backward_flops(wb.B, wb.H, wb.T) if pb == 2 else backward_p1_flops(wb.B, wb.H, wb.T)
             note = ("gradients of q, k, v, omega (sanatan_attention_backward, masked quadratic form); "
-                    "flops: 2 (3 x 6d + 2 d_v) per causal pair") if pb == 2 else (
+                    "flops: 2 (3 x 6d + 2 d_v) per causal pair") if pb == 2 and not sv else (
+                    "sanatan_attention_backward_saved: the same gradients given the fp32 output rows and 1/Dn "
+                    "saved by sanatan_quadratic_train (no statistics pass); flops as backward_p2") if pb == 2 else (
                     "gradients of q, k, v, omega (sanatan_attention_backward: statistics, feature gradients and dv "
                     "as chunked recurrences, linear in T); flops as backward_p1_flops states")
-            extras[key] = {"workload": f"{wb.name}_backward_p{pb}", "ms": bms, "ms_eager": be, "ms_graph": bg,
+            extras[key] = {"workload": f"{wb.name}_backward_p{pb}" + ("_saved" if sv else ""), "ms": bms,
+                           "ms_eager": be, "ms_graph": bg,
                            "tokens_per_s": wb.B * wb.T / (bms * 1e-3), "flops_per_call": bfl,
                            "roofline": mfma_line(bfl, bms), "note": note}
         for key, nh, feats in (("harmonics_nh2_prefill", 2, 10 * D), ("four_channel_prefill", 0, 3 * D + 1)):

@@ -257,6 +257,18 @@ sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void
                                         void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * sanatan_quadratic_train -- sanatan_quadratic_ref_p2 that also saves what its backward pass needs, so that a
+ * training step's backward (sanatan_attention_backward_saved) skips its statistics pass.  saved: DEVICE fp32,
+ * 16-byte aligned, sanatan_quadratic_saved_bytes() bytes, written: the output rows in fp32 [B][H][T][d_v], then per
+ * query row the reciprocal of its normaliser in the kernels' scaled units, 1 / (sum_{s<=t} kappa_ts^p + eps c^p),
+ * [B][H][T].  saved NULL is INVALID_ARG; everything else as sanatan_quadratic_ref_p2 (out is bitwise the same).
+ */
+size_t sanatan_quadratic_saved_bytes(int B, int H, int T, const sanatan_params* params);
+sanatan_status sanatan_quadratic_train(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
+                                       int T, int p, int64_t pos0, const sanatan_params* params, void* out,
+                                       float* saved, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * sanatan_quadratic_four_channel -- the same masked quadratic form on the unclipped four-channel kernel
  * of [N] §2.5: per dim the features are [1, r, r cos theta_rot, r sin theta_rot] (the independent cos and
  * sin channels dropped), so
@@ -342,6 +354,20 @@ sanatan_status sanatan_attention_backward(const void* q, const void* k, const vo
                                           sanatan_dtype t, int B, int H, int T, int p, int64_t pos0,
                                           const sanatan_params* params, void* dq, void* dk, void* dv, float* domega,
                                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * sanatan_attention_backward_saved -- sanatan_attention_backward given the statistics that sanatan_quadratic_train
+ * saved for the same q, k, v, p, pos0 and params.  At p = 2 they replace the statistics pass (a second
+ * forward-sized pass over the score tiles): delta_t = <dout_t, o_t> is summed in fp32 from the saved fp32 output
+ * rows (the bf16 output would leave delta too coarse for G's cancelling rows).  At p = 1 the chunked recurrences
+ * form the statistics on the way and the saved values are not read.  saved NULL is INVALID_ARG; workspace,
+ * outputs and everything else as sanatan_attention_backward.
+ */
+sanatan_status sanatan_attention_backward_saved(const void* q, const void* k, const void* v, const void* dout,
+                                                const float* saved, sanatan_dtype t, int B, int H, int T, int p,
+                                                int64_t pos0, const sanatan_params* params, void* dq, void* dk,
+                                                void* dv, float* domega, void* ws, size_t ws_bytes,
+                                                hipStream_t stream);
 
 /* Static human-readable name of a status code. */
 const char* sanatan_status_string(sanatan_status status);

@@ -114,6 +114,13 @@ def lib():
                                                  sz, vp]
         L.sanatan_quadratic_four_channel.restype = i32
         L.sanatan_quadratic_four_channel.argtypes = L.sanatan_quadratic_ref_p2.argtypes
+        L.sanatan_quadratic_saved_bytes.restype = sz
+        L.sanatan_quadratic_saved_bytes.argtypes = [i32, i32, i32, pp]
+        L.sanatan_quadratic_train.restype = i32
+        L.sanatan_quadratic_train.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp, vp, sz, vp]
+        L.sanatan_attention_backward_saved.restype = i32
+        L.sanatan_attention_backward_saved.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, pp, vp, vp,
+                                                       vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -125,8 +132,9 @@ EXPORTED = [
     "sanatan_compact_state_bytes", "sanatan_state_compact", "sanatan_state_expand", "sanatan_decode_step_compact",
     "sanatan_four_channel_state_bytes", "sanatan_decode_step_four_channel",
     "sanatan_quadratic_workspace_bytes",
-    "sanatan_quadratic_ref_p2", "sanatan_quadratic_four_channel",
-    "sanatan_attention_backward_workspace_bytes", "sanatan_attention_backward",
+    "sanatan_quadratic_ref_p2", "sanatan_quadratic_four_channel", "sanatan_quadratic_saved_bytes",
+    "sanatan_quadratic_train",
+    "sanatan_attention_backward_workspace_bytes", "sanatan_attention_backward", "sanatan_attention_backward_saved",
     "sanatan_harmonics_state_bytes", "sanatan_prefill_harmonics_workspace_bytes", "sanatan_prefill_harmonics",
     "sanatan_decode_step_harmonics", "sanatan_prefill_four_channel_workspace_bytes", "sanatan_prefill_four_channel",
 ]
@@ -526,6 +534,34 @@ def sanatan_quadratic_ref_p2(q, k, v, p_exp: int, params: Params, pos0: int = 0,
     return out
 
 
+def sanatan_quadratic_train(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, saved=None, ws=None):
+    """sanatan_quadratic_ref_p2 that also saves what sanatan_attention_backward_saved needs (fp32 output rows, then
+    1 / Dn per row).  Returns (out [B,H,T,64] in the input dtype, saved: fp32 1-D tensor)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name)
+    B, H, T = _attention_shape(q, k, v, params)
+    if out is None:
+        out = torch.empty((B, H, T, params.d_v), dtype=q.dtype, device=q.device)
+    _check_tensor(out, "out")
+    _check_shape(out, "out", (B, H, T, params.d_v))
+    _check_same_dtype(q, ("out", out))
+    p = params.struct()
+    nsaved = int(lib().sanatan_quadratic_saved_bytes(B, H, T, ctypes.byref(p))) // 4
+    if saved is None:
+        saved = torch.empty((nsaved,), dtype=torch.float32, device=q.device)
+    _check_tensor(saved, "saved", dtypes=("float32",))
+    _check_shape(saved, "saved", (nsaved,))
+    need = int(lib().sanatan_quadratic_workspace_bytes(B, H, T, _dtype_code(q), ctypes.byref(p)))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().sanatan_quadratic_train(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, int(p_exp), int(pos0),
+                                         ctypes.byref(p), _ptr(out), _ptr(saved), _ptr(ws), ws.numel(), _stream()),
+           "sanatan_quadratic_train")
+    return out, saved
+
+
 def sanatan_quadratic_four_channel(q, k, v, p_exp: int, params: Params, pos0: int = 0, out=None, ws=None):
     """The masked quadratic form on the unclipped four-channel kernel.  Returns out [B,H,T,64]."""
     return sanatan_quadratic_ref_p2(q, k, v, p_exp, params, pos0=pos0, out=out, ws=ws, four_channel=True)
@@ -569,6 +605,42 @@ def sanatan_attention_backward(q, k, v, dout, p_exp: int, params: Params, pos0: 
     _check(lib().sanatan_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _dtype_code(q), B, H, T, int(p_exp),
                                             int(pos0), ctypes.byref(pr), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(domega),
                                             _ptr(ws), ws.numel(), _stream()), "sanatan_attention_backward")
+    return dq, dk, dv, domega
+
+
+def sanatan_attention_backward_saved(q, k, v, dout, saved, p_exp: int, params: Params, pos0: int = 0,
+                                     dq=None, dk=None, dv=None, domega=None, ws=None):
+    """sanatan_attention_backward given the statistics sanatan_quadratic_train saved (same q, k, v, p, pos0,
+    params).  Returns (dq, dk, dv, domega) as sanatan_attention_backward."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(t, name)
+    B, H, T = _attention_shape(q, k, v, params)
+    _check_shape(dout, "dout", (B, H, T, params.d_v))
+    _check_same_dtype(q, ("dout", dout))
+    pr = params.struct()
+    _check_tensor(saved, "saved", dtypes=("float32",))
+    _check_shape(saved, "saved", (int(lib().sanatan_quadratic_saved_bytes(B, H, T, ctypes.byref(pr))) // 4,))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(t, name)
+        _check_shape(t, name, tuple(ref.shape))
+        _check_same_dtype(q, (name, t))
+    nph = pr.n_param_heads
+    if domega is None:
+        domega = torch.empty((nph, params.d), dtype=torch.float32, device=q.device)
+    _check_tensor(domega, "domega", dtypes=("float32",))
+    _check_shape(domega, "domega", (nph, params.d))
+    need = int(lib().sanatan_attention_backward_workspace_bytes(B, H, T, _dtype_code(q), ctypes.byref(pr)))
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().sanatan_attention_backward_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(saved),
+                                                  _dtype_code(q), B, H, T, int(p_exp), int(pos0), ctypes.byref(pr),
+                                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(domega), _ptr(ws), ws.numel(),
+                                                  _stream()), "sanatan_attention_backward_saved")
     return dq, dk, dv, domega
 
 

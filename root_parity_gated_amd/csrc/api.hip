@@ -236,6 +236,25 @@ sanatan_status sanatan_quadratic_ref_p2(const void* q, const void* k, const void
   return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, false, pos0, consts(params), out, ws, stream));
 }
 
+size_t sanatan_quadratic_saved_bytes(int B, int H, int T, const sanatan_params* params) {
+  (void)params;
+  if (!sizes_ok(B, H, T) || T > kMaxQuadraticT) return 0;
+  return (size_t)B * H * T * (kDV + 1) * sizeof(float);
+}
+
+sanatan_status sanatan_quadratic_train(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H,
+                                       int T, int p, int64_t pos0, const sanatan_params* params, void* out,
+                                       float* saved, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out || !saved || !dtype_ok(t) || !sizes_ok(B, H, T) || (p != 1 && p != 2))
+    return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxQuadraticT) return SANATAN_ERR_UNSUPPORTED;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (!ws || ws_bytes < quadratic_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
+  return hip_status(launch_quadratic(q, k, v, t, B, H, T, p, false, pos0, consts(params), out, ws, stream, saved));
+}
+
 sanatan_status sanatan_quadratic_four_channel(const void* q, const void* k, const void* v, sanatan_dtype t, int B,
                                               int H, int T, int p, int64_t pos0, const sanatan_params* params,
                                               void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -326,6 +345,23 @@ sanatan_status sanatan_attention_backward(const void* q, const void* k, const vo
   if (!ws || ws_bytes < backward_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
   return hip_status(
       launch_backward(q, k, v, dout, t, B, H, T, p, pos0, consts(params), dq, dk, dv, domega, ws, stream));
+}
+
+sanatan_status sanatan_attention_backward_saved(const void* q, const void* k, const void* v, const void* dout,
+                                                const float* saved, sanatan_dtype t, int B, int H, int T, int p,
+                                                int64_t pos0, const sanatan_params* params, void* dq, void* dk,
+                                                void* dv, float* domega, void* ws, size_t ws_bytes,
+                                                hipStream_t stream) {
+  if (!q || !k || !v || !dout || !saved || !dq || !dk || !dv || !domega || !dtype_ok(t) || !sizes_ok(B, H, T) ||
+      (p != 1 && p != 2))
+    return SANATAN_ERR_INVALID_ARG;
+  if (!pos_ok(pos0) || !pos_ok(pos0 + (int64_t)T - 1)) return SANATAN_ERR_INVALID_ARG;
+  if (T > kMaxQuadraticT) return SANATAN_ERR_UNSUPPORTED;
+  const sanatan_status ps = check_params(params);
+  if (ps != SANATAN_OK) return ps;
+  if (!ws || ws_bytes < backward_ws_bytes(B, H, T, t)) return SANATAN_ERR_WORKSPACE;
+  return hip_status(
+      launch_backward(q, k, v, dout, t, B, H, T, p, pos0, consts(params), dq, dk, dv, domega, ws, stream, saved));
 }
 
 }  // extern "C"

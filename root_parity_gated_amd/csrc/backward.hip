@@ -422,6 +422,26 @@ __global__ __launch_bounds__(64) void bwd_domega_kernel(const float* __restrict_
   domega[(size_t)prow * kD + a] = acc;
 }
 
+// The statistics from a saved forward pass (fp32 output rows o [rows][d_v], then 1 / Dn [rows]):
+// stats[r] = (1 / Dn_r, delta_r = <dout_r, o_r>), one row per thread, the dot product in fp32 in dimension order.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_saved_stats_kernel(const T* __restrict__ g, const float* __restrict__ saved,
+                                                              size_t rows, float2* __restrict__ stats) {
+  const size_t r = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const float* o = saved;
+  const float* inv = saved + rows * kDV;
+  float gv[8], ov[8], acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kDV / 8; j++) {
+    ld8c(g + r * kDV + 8 * j, gv);
+    ld8c(o + r * kDV + 8 * j, ov);
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc = fmaf(gv[i], ov[i], acc);
+  }
+  stats[r] = make_float2(inv[r], acc);
+}
+
 template <typename Kern>
 hipError_t set_lds(Kern k, int bytes, std::atomic<bool>& flag) {
   if (flag.load(std::memory_order_acquire)) return hipSuccess;
@@ -455,7 +475,7 @@ BwdLayout bwd_layout(int B, int H, int T, sanatan_dtype t) {
 template <typename T, int P>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* g, int B, int H, int Tn,
                         int64_t pos0, const MethodConsts& mc, void* dq, void* dk, void* dv, float* domega, void* ws,
-                        sanatan_dtype dt, hipStream_t stream) {
+                        sanatan_dtype dt, hipStream_t stream, const float* saved) {
   using G = BGeom<T>;
   char* base = static_cast<char*>(ws);
   const BwdLayout L = bwd_layout(B, H, Tn, dt);
@@ -476,7 +496,14 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                                 dq, dk, dv, dom, reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
       return e;
   } else {
-    if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) return e;
+    if (saved) {  // the forward pass's saved output rows and normalisers replace the statistics pass
+      const size_t rows = (size_t)B * H * Tn;
+      hipLaunchKernelGGL((bwd_saved_stats_kernel<T>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                         static_cast<const T*>(g), saved, rows, stats);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if ((e = launch_quadratic_stats(q, phik, v, g, dt, B, H, Tn, P, rho, mc, stats, stream)) != hipSuccess) {
+      return e;
+    }
 
   // feature gradients over the feature tiles of channels 1..5 (tiles 2..11: channel 0 is the constant 1, whose
   // gradient the Jacobian does not use).  bf16 runs the pipelined one-pass kernels of backward_quadratic.hip;
@@ -547,12 +574,12 @@ size_t backward_ws_bytes(int B, int H, int T, sanatan_dtype t) { return bwd_layo
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* dout, sanatan_dtype t, int B,
                            int H, int T, int p, int64_t pos0, const MethodConsts& mc, void* dq, void* dk, void* dv,
-                           float* domega, void* ws, hipStream_t stream) {
+                           float* domega, void* ws, hipStream_t stream, const float* si) {
   if (t == SANATAN_BF16)
-    return p == 1 ? launch_bwd_t<__bf16, 1>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream)
-                  : launch_bwd_t<__bf16, 2>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream);
-  return p == 1 ? launch_bwd_t<float, 1>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream)
-                : launch_bwd_t<float, 2>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream);
+    return p == 1 ? launch_bwd_t<__bf16, 1>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream, si)
+                  : launch_bwd_t<__bf16, 2>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream, si);
+  return p == 1 ? launch_bwd_t<float, 1>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream, si)
+                : launch_bwd_t<float, 2>(q, k, v, dout, B, H, T, pos0, mc, dq, dk, dv, domega, ws, t, stream, si);
 }
 
 }  // namespace sanatan

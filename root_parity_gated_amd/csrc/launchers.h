@@ -65,9 +65,11 @@ void* noalloc_scratch();  // this device's array (address looked up once per dev
 
 size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t);
 // four_channel: the unclipped four-channel kernel ([1, r, r cos, r sin] per dim) instead of the six-channel one
+// inv_out (nullable): the saved statistics of a training step, fp32: the output rows [B][H][T][d_v], then 1 / Dn
+// per query row [B][H][T] (the normaliser in the kernel's scaled units)
 hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
                             int p, bool four_channel, int64_t pos0, const MethodConsts& mc, void* out, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, float* inv_out = nullptr);
 
 // Materialized-feature chunked prefill: nh_or_zero = 1 or 2 spectral harmonics (state rows (2 + 4 nh) d), or 0 for the
 // unclipped four-channel compact map (3d + 1 rows).  Workspace: Phi(Q), Phi(K) padded to ext_features_padded.
@@ -83,8 +85,10 @@ hipError_t launch_decode_step_harmonics(const float* q, const float* k, const fl
 // Gradient of normalised causal power attention (p = 1 or 2) with respect to q, k, v and omega.  Workspace:
 // phase table, Phi(Q), Phi(K) (element type t), per-row statistics, fp32 feature gradients, omega partials.
 size_t backward_ws_bytes(int B, int H, int T, sanatan_dtype t);
+// saved (nullable): the statistics saved by the forward (fp32 output rows, then 1 / Dn per row); at p = 2 they
+// replace the statistics pass
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* dout, sanatan_dtype t, int B,
                            int H, int T, int p, int64_t pos0, const MethodConsts& mc, void* dq, void* dk, void* dv,
-                           float* domega, void* ws, hipStream_t stream);
+                           float* domega, void* ws, hipStream_t stream, const float* saved = nullptr);
 
 }  // namespace sanatan

@@ -57,7 +57,8 @@ template <typename T, int P, int C0, bool STATS = false>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     const T* __restrict__ q, const T* __restrict__ phik, const T* __restrict__ v, T* __restrict__ out,
     const float* __restrict__ rho, const float* __restrict__ omega, int nph, int H, int Tn, int BH, int nqb, float kr,
-    float eps_cp, const T* __restrict__ gout = nullptr, float2* __restrict__ stats = nullptr) {
+    float eps_cp, const T* __restrict__ gout = nullptr, float2* __restrict__ stats = nullptr,
+    float* __restrict__ inv_out = nullptr) {
   using G = QGeom<T, C0>;
   typedef typename FragT<T>::type Frag;
   constexpr int MQ = G::MQ, KB = G::KB, NF = G::NF, NJ = G::NJ, KP = G::KP, VP = G::VP, EL = G::EL;
@@ -355,13 +356,21 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void quadratic_kernel(
     if (t < Tn) {
       // weights are kappa^p here, so epsilon is scaled by c^p: o = sum w v / (sum w + eps c^p)
       const float inv = 1.0f / (den + eps_cp);
+      // saved for the backward pass: the fp32 output row ([BH][T][d_v]) then 1 / Dn ([BH][T])
+      float* sv = inv_out ? inv_out + ((size_t)bh * Tn + t) * kDV : nullptr;
+      if (inv_out && h == 0) inv_out[(size_t)BH * Tn * kDV + (size_t)bh * Tn + t] = inv;
 #pragma unroll
       for (int vt = 0; vt < 2; vt++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 4; j++) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; i4++)
             op[(size_t)t * kDV + 32 * vt + 8 * j + 4 * h + i4] = from_f32<T>(num[mq][vt][4 * j + i4] * inv);
+          if (sv)
+            *reinterpret_cast<float4*>(sv + 32 * vt + 8 * j + 4 * h) =
+                make_float4(num[mq][vt][4 * j] * inv, num[mq][vt][4 * j + 1] * inv, num[mq][vt][4 * j + 2] * inv,
+                            num[mq][vt][4 * j + 3] * inv);
+        }
     }
   }
 }
@@ -370,7 +379,8 @@ size_t rho_bytes_q(int T) { return (((size_t)T * kD * sizeof(float)) + 255) & ~(
 
 template <typename T, int P, int C0>
 hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int H, int Tn, int64_t pos0,
-                         const MethodConsts& mc, void* out, void* ws, sanatan_dtype t, hipStream_t stream) {
+                         const MethodConsts& mc, void* out, void* ws, sanatan_dtype t, float* inv_out,
+                         hipStream_t stream) {
   float* rho = static_cast<float*>(ws);
   void* phik = static_cast<char*>(ws) + rho_bytes_q(Tn);
   hipError_t e = launch_phase_table(rho, Tn, pos0, mc.log2_base, stream);
@@ -392,7 +402,7 @@ hipError_t launch_quad_t(const void* q, const void* k, const void* v, int B, int
   hipLaunchKernelGGL((quadratic_kernel<T, P, C0>), dim3(BH * nqb), dim3(256), G::lds, stream,
                      static_cast<const T*>(q), static_cast<const T*>(phik), static_cast<const T*>(v),
                      static_cast<T*>(out), rho, mc.omega, mc.nph, H, Tn, BH, nqb, mc.kr,
-                     P == 2 ? (float)((double)mc.ceps / (double)mc.inv_c) : mc.ceps);
+                     P == 2 ? (float)((double)mc.ceps / (double)mc.inv_c) : mc.ceps, nullptr, nullptr, inv_out);
   return hipGetLastError();
 }
 
@@ -437,19 +447,20 @@ size_t quadratic_ws_bytes(int B, int H, int T, sanatan_dtype t) {
 
 template <int C0>
 static hipError_t launch_quad_c(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
-                                int p, int64_t pos0, const MethodConsts& mc, void* out, void* ws, hipStream_t stream) {
+                                int p, int64_t pos0, const MethodConsts& mc, void* out, void* ws, float* inv_out,
+                                hipStream_t stream) {
   if (t == SANATAN_BF16)
-    return p == 1 ? launch_quad_t<__bf16, 1, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream)
-                  : launch_quad_t<__bf16, 2, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream);
-  return p == 1 ? launch_quad_t<float, 1, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream)
-                : launch_quad_t<float, 2, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, stream);
+    return p == 1 ? launch_quad_t<__bf16, 1, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, inv_out, stream)
+                  : launch_quad_t<__bf16, 2, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, inv_out, stream);
+  return p == 1 ? launch_quad_t<float, 1, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, inv_out, stream)
+                : launch_quad_t<float, 2, C0>(q, k, v, B, H, T, pos0, mc, out, ws, t, inv_out, stream);
 }
 
 hipError_t launch_quadratic(const void* q, const void* k, const void* v, sanatan_dtype t, int B, int H, int T,
                             int p, bool four_channel, int64_t pos0, const MethodConsts& mc, void* out, void* ws,
-                            hipStream_t stream) {
-  return four_channel ? launch_quad_c<3>(q, k, v, t, B, H, T, p, pos0, mc, out, ws, stream)
-                      : launch_quad_c<1>(q, k, v, t, B, H, T, p, pos0, mc, out, ws, stream);
+                            hipStream_t stream, float* inv_out) {
+  return four_channel ? launch_quad_c<3>(q, k, v, t, B, H, T, p, pos0, mc, out, ws, inv_out, stream)
+                      : launch_quad_c<1>(q, k, v, t, B, H, T, p, pos0, mc, out, ws, inv_out, stream);
 }
 
 }  // namespace sanatan

@@ -152,6 +152,30 @@ def test_featurize_decode_quadratic_validation(L):
                                             None) == rpg.SANATAN_ERR_WORKSPACE
     assert L.sanatan_quadratic_four_channel(None, FAKE, FAKE, 1, 1, 1, 64, 1, 0, ctypes.byref(p), FAKE, FAKE,
                                             1 << 40, None) == rpg.SANATAN_ERR_INVALID_ARG
+    # the training forward: the quadratic form's checks, and its saved-statistics output is required
+    qt = lambda pe, sv, ws_bytes=1 << 40: L.sanatan_quadratic_train(FAKE, FAKE, FAKE, 1, 1, 1, 64, pe, 0,
+                                                                    ctypes.byref(p), FAKE, sv, FAKE, ws_bytes, None)
+    assert qt(2, None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert qt(3, FAKE) == rpg.SANATAN_ERR_INVALID_ARG
+    assert qt(2, FAKE, ws_bytes=10) == rpg.SANATAN_ERR_WORKSPACE
+    # saved statistics: the fp32 output row and 1 / Dn per query row
+    assert L.sanatan_quadratic_saved_bytes(2, 3, 100, ctypes.byref(p)) == 2 * 3 * 100 * 65 * 4
+    assert L.sanatan_quadratic_saved_bytes(2, 3, 0, ctypes.byref(p)) == 0
+
+
+def test_backward_saved_validation(L):
+    """The backward pass from saved statistics: the saved buffer is required, and the rest is checked as in
+    sanatan_attention_backward."""
+    p = params()
+    def bs(saved=FAKE, pe=2, T=64, ws_bytes=1 << 40, dq=FAKE):
+        return L.sanatan_attention_backward_saved(FAKE, FAKE, FAKE, FAKE, saved, 1, 1, 1, T, pe, 0, ctypes.byref(p),
+                                                  dq, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert bs(saved=None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert bs(dq=None) == rpg.SANATAN_ERR_INVALID_ARG
+    assert bs(pe=3) == rpg.SANATAN_ERR_INVALID_ARG
+    assert bs(T=0) == rpg.SANATAN_ERR_INVALID_ARG
+    assert bs(T=(1 << 20) + 1) == rpg.SANATAN_ERR_UNSUPPORTED
+    assert bs(ws_bytes=10) == rpg.SANATAN_ERR_WORKSPACE
 
 
 def test_workspace_sizes(L):
