@@ -80,6 +80,19 @@ int bwd_pieces(int B, int H, int Tn) {
   return P < 1 ? 1 : (int)P;
 }
 
+// Workgroups per piece in the increments passes: only NP - 1 of a sequence's NP pieces have an increment, so each
+// such piece's chunks are split over this many workgroups (each writes a slot of its own, and the consumers sum
+// them) to keep the compute units busy: at most 8, and never more than the chunks of the smallest piece.
+int bwd_split(int B, int H, int Tn) {
+  const int NP = bwd_pieces(B, H, Tn);
+  if (NP < 2) return 1;
+  const long long BH = (long long)B * H, nch = (Tn + kBC - 1) / kBC;
+  long long S = device_cus() / (BH * (NP - 1));
+  if (S > 8) S = 8;
+  if (S > nch / NP) S = nch / NP;
+  return S < 1 ? 1 : (int)S;
+}
+
 // 16 bytes of T scaled by s (hi), and for bf16 the rounding of what that rounding dropped (lo)
 template <typename T>
 __device__ __forceinline__ void scale16(const u32x4& x, float s, u32x4& hi, u32x4& lo) {
@@ -303,17 +316,24 @@ template <typename T, int MODE>
 __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                           const T* __restrict__ v, const T* __restrict__ g,
                                                           const float2* __restrict__ stats, int Tn, int NP,
-                                                          float* __restrict__ slots) {
+                                                          int SPL, float* __restrict__ slots) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
   constexpr bool DS = MODE == 1, DR = MODE == 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
-  const int bh = blockIdx.x / NP, p = blockIdx.x % NP;
-  if (DS ? p == NP - 1 : p == 0) return;
+  // one workgroup per part of a piece that has an increment (all but the last for S, all but the first for R), so
+  // consecutive workgroups, which go to different XCDs, all have work
+  const int bh = blockIdx.x / ((NP - 1) * SPL), p = (blockIdx.x / SPL) % (NP - 1) + (DS ? 0 : 1),
+            sp_ = blockIdx.x % SPL;
   int t_lo, t_hi;
   piece_bounds(p, NP, Tn, t_lo, t_hi);
+  {  // part sp_ of the piece's chunks (never empty: every piece has at least SPL chunks)
+    const int pc = (t_hi - t_lo + kBC - 1) / kBC, base = t_lo;
+    t_lo = base + (sp_ * pc / SPL) * kBC;
+    t_hi = min(t_hi, base + ((sp_ + 1) * pc / SPL) * kBC);
+  }
   const size_t so = (size_t)bh * Tn;
   const T* qp = phiq + so * Fp;
   const T* kp = phik + so * Fp;
@@ -379,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ 
       __syncthreads();
     }
   }
-  slot_put<T>(slots + ((size_t)bh * NP + p) * G::SLOT, A, vs, w, l, tid);
+  slot_put<T>(slots + (((size_t)bh * NP + p) * SPL + sp_) * G::SLOT, A, vs, w, l, tid);
 }
 
 // Method inputs of the fused Jacobian: the raw q and k, the phase table, the root anchors and kr.
@@ -401,7 +421,7 @@ struct JacArgs {
 template <typename T>
 __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
                                          const T* __restrict__ v, const T* __restrict__ g,
-                                         float2* __restrict__ stats, int Tn, int NP, float ceps,
+                                         float2* __restrict__ stats, int Tn, int NP, int SPL, float ceps,
                                          const float* __restrict__ sslots, const JacArgs& ja, T* __restrict__ dq,
                                          float* __restrict__ dom_part, char* smem) {
   using G = CGeom<T>;
@@ -441,7 +461,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, co
 #pragma unroll
     for (int vt = 0; vt < 2; vt++) zero16(ST[i][vt]);
   for (int f = tid; f < Fp; f += 256) zs[f] = 0.0f;
-  for (int q = 0; q < p; q++) slot_add<T>(sslots + ((size_t)bh * NP + q) * G::SLOT, ST, zs, w, l, tid);
+  for (int q = 0; q < p * SPL; q++) slot_add<T>(sslots + ((size_t)bh * NP * SPL + q) * G::SLOT, ST, zs, w, l, tid);
   ChunkRegs<T, true, true, true, true, false, false> R;
   R.load(kp, qp, vp, gp, nullptr, t_lo, min(kBC, t_hi - t_lo), tid);
   for (int t0 = t_lo; t0 < t_hi; t0 += kBC) {
@@ -580,7 +600,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, co
 template <typename T>
 __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
                                           const T* __restrict__ v, const T* __restrict__ g,
-                                          const float2* __restrict__ stats, int Tn, int NP,
+                                          const float2* __restrict__ stats, int Tn, int NP, int SPL,
                                           const float* __restrict__ rslots, const JacArgs& ja, T* __restrict__ dk,
                                           T* __restrict__ dv, float* __restrict__ dom_part, char* smem) {
   using G = CGeom<T>;
@@ -625,7 +645,8 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
 #pragma unroll
     for (int vt = 0; vt < 2; vt++) zero16(RT[i][vt]);
   for (int f = tid; f < Fp; f += 256) rs[f] = 0.0f;
-  for (int q = NP - 1; q > p; q--) slot_add<T>(rslots + ((size_t)bh * NP + q) * G::SLOT, RT, rs, w, l, tid);
+  for (int q = NP * SPL - 1; q >= (p + 1) * SPL; q--)
+    slot_add<T>(rslots + ((size_t)bh * NP * SPL + q) * G::SLOT, RT, rs, w, l, tid);
   const int c_lo = t_lo / kBC, c_hi = (t_hi + kBC - 1) / kBC;
   ChunkRegs<T, true, true, true, true, true> R;
   R.load(kp, qp, vp, gp, sp, (c_hi - 1) * kBC, min(kBC, t_hi - (c_hi - 1) * kBC), tid);
@@ -798,16 +819,17 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
 template <typename T, int DIR>
 __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                            const T* __restrict__ v, const T* __restrict__ g,
-                                                           float2* __restrict__ stats, int Tn, int NP, float ceps,
+                                                           float2* __restrict__ stats, int Tn, int NP, int SPL,
+                                                           float ceps,
                                                            const float* __restrict__ sslots,
                                                            const float* __restrict__ rslots, const JacArgs ja,
                                                            T* __restrict__ dq, T* __restrict__ dk,
                                                            T* __restrict__ dv, float* __restrict__ dom_part) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if constexpr (DIR == 0)
-    dq_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, ceps, sslots, ja, dq, dom_part, smem);
+    dq_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, SPL, ceps, sslots, ja, dq, dom_part, smem);
   else
-    dkv_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, rslots, ja, dk, dv,
+    dkv_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, SPL, rslots, ja, dk, dv,
                  dom_part + (size_t)gridDim.x * kD, smem);
 }
 
@@ -827,9 +849,9 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
   static std::atomic<bool> attr[4][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const int BH = B * H, NP = bwd_pieces(B, H, Tn);
+  const int BH = B * H, NP = bwd_pieces(B, H, Tn), SPL = bwd_split(B, H, Tn);
   float* sslots = slots;
-  float* rslots = NP > 1 ? slots + (size_t)BH * NP * G::SLOT : slots;
+  float* rslots = NP > 1 ? slots + (size_t)BH * NP * SPL * G::SLOT : slots;
   const T* q = static_cast<const T*>(phiq);
   const T* k = static_cast<const T*>(phik);
   const T* vv = static_cast<const T*>(v);
@@ -843,21 +865,21 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
     return e;
   auto incr = [&](int mode) {
     if (mode == 1)
-      hipLaunchKernelGGL((bwd_incr_kernel<T, 1>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
-                         NP, sslots);
+      hipLaunchKernelGGL((bwd_incr_kernel<T, 1>), dim3(BH * (NP - 1) * SPL), dim3(256), G::lds, stream, q, k, vv, gg, stats,
+                         Tn, NP, SPL, sslots);
     else
-      hipLaunchKernelGGL((bwd_incr_kernel<T, 2>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
-                         NP, rslots);
+      hipLaunchKernelGGL((bwd_incr_kernel<T, 2>), dim3(BH * (NP - 1) * SPL), dim3(256), G::lds, stream, q, k, vv, gg, stats,
+                         Tn, NP, SPL, rslots);
     return hipGetLastError();
   };
   auto chunks = [&](int dir) {
     if (dir == 0)
       hipLaunchKernelGGL((bwd_chunk_kernel<T, 0>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
-                         NP, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
+                         NP, SPL, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
                          static_cast<T*>(dv), dom_part);
     else
       hipLaunchKernelGGL((bwd_chunk_kernel<T, 1>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
-                         NP, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
+                         NP, SPL, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
                          static_cast<T*>(dv), dom_part);
     return hipGetLastError();
   };
@@ -872,7 +894,7 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
 
 size_t bwd_chunked_slot_bytes(int B, int H, int T) {
   const int NP = bwd_pieces(B, H, T);
-  return NP > 1 ? 2 * (size_t)B * H * NP * CGeom<float>::SLOT * sizeof(float) : 0;
+  return NP > 1 ? 2 * (size_t)B * H * NP * bwd_split(B, H, T) * CGeom<float>::SLOT * sizeof(float) : 0;
 }
 
 int bwd_chunked_pieces(int B, int H, int T) { return bwd_pieces(B, H, T); }
