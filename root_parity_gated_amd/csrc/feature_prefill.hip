@@ -20,10 +20,11 @@
 // Operands: bf16 32x32x16 MFMA (fp32 32x32x2 for fp32 inputs), fp32 accumulation; S is rounded to the
 // operand type only as the readout's operand.
 // Sequence split: with fewer sequences than compute units, each sequence is cut into P pieces of whole chunks,
-// one workgroup each.  Pass 1 (STATE_ONLY) runs pieces 0..P-2 and writes each piece's state increment to its
-// slot (piece 0's includes the caller's start state, which it also copies to the spare slot P - 1); pass 3 then
-// starts piece p from the sum of slots 0..p-1 (piece 0 from slot P - 1), so that no piece of pass 3 reads the
-// caller's state while the final piece writes it back.
+// one workgroup each.  Pass 1 (STATE_ONLY) runs pieces 0..P-2, each split into SPL parts of whole chunks, and
+// writes each part's state increment to its slot (part 0 of piece 0 includes the caller's start state, which it
+// also copies to the spare slot of piece P - 1); pass 3 then starts piece p from the sum of the slots of pieces
+// 0..p-1 (piece 0 from that spare slot), so that no piece of pass 3 reads the caller's state while the final
+// piece writes it back.
 #include <atomic>
 
 #include "feature_tiles.h"
@@ -168,8 +169,8 @@ template <typename T, int NFT, bool STATE_ONLY, bool FUSED = false, int KIND = 0
 __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                               const T* __restrict__ v, T* __restrict__ out,
                                                               float* __restrict__ S, float* __restrict__ z, int Tn,
-                                                              int Freal, float ceps, int P, float* __restrict__ slots,
-                                                              int shared_last, FuseIn fu) {
+                                                              int Freal, float ceps, int P, int SPL,
+                                                              float* __restrict__ slots, int shared_last, FuseIn fu) {
   using G = FGeom<T, NFT>;
   typedef typename FragT<T>::type Frag;
   static_assert(NFT % 4 == 0, "feature tiles are dealt to four waves");
@@ -181,13 +182,21 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
   float* red = reinterpret_cast<float*>(smem + G::k_bytes + G::q_bytes + G::v_bytes);
   float* zs = reinterpret_cast<float*>(smem + G::k_bytes + G::q_bytes + G::v_bytes + G::red_bytes);
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
-  const int bh = blockIdx.x / P, p = blockIdx.x % P;
-  if (STATE_ONLY && p == P - 1) return;  // the final piece's state comes out of pass 3
+  // pass 1 (STATE_ONLY) runs part sp_ of SPL of every piece but the last (the final piece's state comes out of
+  // pass 3), so consecutive workgroups, which go to different XCDs, all have work; pass 3 runs whole pieces
+  const int bh = STATE_ONLY ? blockIdx.x / ((P - 1) * SPL) : blockIdx.x / P;
+  const int p = STATE_ONLY ? (blockIdx.x / SPL) % (P - 1) : blockIdx.x % P;
+  const int sp_ = STATE_ONLY ? blockIdx.x % SPL : 0;
   const int nch = (Tn + kFC - 1) / kFC;
-  const int t_lo = (int)((long long)p * nch / P) * kFC;
-  const int t_hi = min(Tn, (int)((long long)(p + 1) * nch / P) * kFC);
+  int t_lo = (int)((long long)p * nch / P) * kFC;
+  int t_hi = min(Tn, (int)((long long)(p + 1) * nch / P) * kFC);
+  if (STATE_ONLY) {  // never empty: every piece has at least SPL chunks
+    const int pc = (t_hi - t_lo + kFC - 1) / kFC, base = t_lo;
+    t_lo = base + (sp_ * pc / SPL) * kFC;
+    t_hi = min(t_hi, base + ((sp_ + 1) * pc / SPL) * kFC);
+  }
   constexpr size_t SLOT = (size_t)Fp * (kDV + 1);  // S [Fp][d_v], then z [Fp]
-  auto slot = [&](int q) { return slots + ((size_t)bh * P + q) * SLOT; };
+  auto slot = [&](int q, int part) { return slots + (((size_t)bh * P + q) * SPL + part) * SLOT; };
   const T* qp = phiq + (size_t)bh * Tn * Fp;
   const T* kp = phik + (size_t)bh * Tn * Fp;
   const T* vp = v + (size_t)bh * Tn * kDV;
@@ -220,12 +229,24 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
         }
     for (int f = tid; f < rows; f += 256) zs[f] += z_[user ? user_row(f) : f];
   };
+  // the same for a slot (all Fp rows, internal order): without the per-element guard the loads need not wait
+  // for one another
+  auto add_slot = [&](const float* s_) {
+#pragma unroll
+    for (int i = 0; i < NW; i++)
+#pragma unroll
+      for (int vt = 0; vt < 2; vt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          Sacc[i][vt][r] += s_[(size_t)(32 * (w + 4 * i) + 8 * (r >> 2) + 4 * h + (r & 3)) * kDV + 32 * vt + n32];
+    for (int f = tid; f < Fp; f += 256) zs[f] += s_[(size_t)Fp * kDV + f];
+  };
   if (P == 1) {
     if (Sp) add_state(Sp, zp, Freal, true);
   } else if (STATE_ONLY) {
-    if (p == 0 && Sp) {
+    if (p == 0 && sp_ == 0 && Sp) {
       add_state(Sp, zp, Freal, true);
-      float* sp1 = slot(P - 1);  // the start state of pass 3's piece 0, internal rows, padded with zeros
+      float* sp1 = slot(P - 1, 0);  // the start state of pass 3's piece 0, internal rows, padded with zeros
       for (int e = tid; e < Fp * kDV; e += 256) {
         const int f = e / kDV;
         sp1[e] = f < Freal ? Sp[(size_t)user_row(f) * kDV + e % kDV] : 0.0f;
@@ -233,9 +254,10 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
       for (int f = tid; f < Fp; f += 256) sp1[Fp * kDV + f] = f < Freal ? zp[user_row(f)] : 0.0f;
     }
   } else if (p == 0) {
-    if (Sp) add_state(slot(P - 1), slot(P - 1) + Fp * kDV, Fp, false);
+    if (Sp) add_slot(slot(P - 1, 0));
   } else {
-    for (int q = 0; q < p; q++) add_state(slot(q), slot(q) + Fp * kDV, Fp, false);
+    for (int q = 0; q < p; q++)
+      for (int part = 0; part < SPL; part++) add_slot(slot(q, part));
   }
 
   // Staging of a chunk's Phi(K) (and, bf16 output pass, Phi(Q)) and V rows, zero past its end.  With few pieces
@@ -470,7 +492,7 @@ __global__ __launch_bounds__(256, 1) void feat_prefill_kernel(const T* __restric
         }
     for (int f = tid; f < rows; f += 256) z_[user ? user_row(f) : f] = zs[f];
   };
-  if (STATE_ONLY) store_state(slot(p), slot(p) + Fp * kDV, Fp, false);
+  if (STATE_ONLY) store_state(slot(p, sp_), slot(p, sp_) + Fp * kDV, Fp, false);
   else if (Sp && p == P - 1) store_state(Sp, zp, Freal, true);
 }
 
@@ -482,6 +504,19 @@ int ext_pieces(int B, int H, int Tn) {
   if (P > 8) P = 8;
   if (P > nch) P = nch;
   return P < 1 ? 1 : (int)P;
+}
+
+// Workgroups per piece in pass 1: only P - 1 pieces of a sequence have a state to hand on, so each one's chunks
+// are split over this many workgroups (each writes a slot of its own, and pass 3 sums them) to keep the compute
+// units busy: at most 8, and never more than the chunks of the smallest piece.
+int ext_split(int B, int H, int Tn) {
+  const int P = ext_pieces(B, H, Tn);
+  if (P < 2) return 1;
+  const long long BH = (long long)B * H, nch = (Tn + kFC - 1) / kFC;
+  long long S = device_cus() / (BH * (P - 1));
+  if (S > 8) S = 8;
+  if (S > nch / P) S = nch / P;
+  return S < 1 ? 1 : (int)S;
 }
 
 template <typename Kern>
@@ -534,18 +569,18 @@ hipError_t launch_fp_t(const void* q, const void* k, const void* v, int B, int H
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, false, FUSED, KIND, NH>, G::lds, attr[dev])) != hipSuccess)
     return e;
-  const int P = ext_pieces(B, H, Tn);
+  const int P = ext_pieces(B, H, Tn), SPL = ext_split(B, H, Tn);
   if (P > 1) {
     if ((e = set_lds_once(feat_prefill_kernel<TIn, NFT, true, FUSED, KIND, NH>, G::lds, attr1[dev])) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, true, FUSED, KIND, NH>), dim3(BH * P), dim3(256), G::lds,
-                       stream, phiq, phik, static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal,
-                       mc.ceps, P, slots, KIND == 1 ? 1 : 0, fu);
+    hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, true, FUSED, KIND, NH>), dim3(BH * (P - 1) * SPL), dim3(256),
+                       G::lds, stream, phiq, phik, static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn,
+                       Freal, mc.ceps, P, SPL, slots, KIND == 1 ? 1 : 0, fu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((feat_prefill_kernel<TIn, NFT, false, FUSED, KIND, NH>), dim3(BH * P), dim3(256), G::lds,
                      stream, phiq, phik, static_cast<const TIn*>(v), static_cast<TIn*>(out), S, z, Tn, Freal, mc.ceps,
-                     P, slots, KIND == 1 ? 1 : 0, fu);
+                     P, SPL, slots, KIND == 1 ? 1 : 0, fu);
   return hipGetLastError();
 }
 
@@ -560,7 +595,7 @@ int ext_features_padded(int nh_or_zero) {
 size_t ext_prefill_ws_bytes(int B, int H, int T, sanatan_dtype t, int nh_or_zero) {
   const size_t Fp = ext_features_padded(nh_or_zero);
   const int P = ext_pieces(B, H, T);
-  const size_t slots = P > 1 ? (size_t)B * H * P * Fp * (kDV + 1) * sizeof(float) : 0;
+  const size_t slots = P > 1 ? (size_t)B * H * P * ext_split(B, H, T) * Fp * (kDV + 1) * sizeof(float) : 0;
   // bf16: the phase table, then the piece slots; fp32: Phi(Q), Phi(K), then the piece slots (Phi's bytes are a
   // multiple of 4: Fp is a multiple of 128)
   if (t == SANATAN_BF16) return ext_rho_bytes(T) + slots;
