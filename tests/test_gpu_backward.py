@@ -152,11 +152,21 @@ def test_backward_long_bf16(torch_dev, p):
 
 
 def test_backward_p1_long_many_pieces(torch_dev):
-    """p = 1 at 4096 tokens in bf16: each sequence runs as 32 pieces of four chunks, so the reverse direction's
-    start states sum up to 31 successors' slots."""
+    """p = 1 at 4096 tokens in bf16: each sequence runs as 32 pieces of four chunks, and on 256 compute units
+    each piece's increments as four one-chunk parts, so the reverse direction's start states sum up to 124
+    slots of 31 successors."""
     errs = run_case(torch_dev, 835, 1, 2, 4096, "bf16", 1)
     for name, e in errs.items():
         assert e <= TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_p1_split_increments_ragged(torch_dev, dtype):
+    """p = 1 at 2100 tokens (a ragged last chunk) over three heads: on 256 compute units 32 pieces of two or
+    three chunks, each piece's increments computed as two parts with a slot each."""
+    errs = run_case(torch_dev, 837, 1, 3, 2100, dtype, 1)
+    for name, e in errs.items():
+        assert e <= TOL[dtype], (name, e)
 
 
 @pytest.mark.parametrize("p", [1, 2])

@@ -161,14 +161,16 @@ def test_four_channel_prefill(torch_dev, dtype, T):
 
 @pytest.mark.parametrize("kind", ["nh1", "nh2", "four"])
 def test_feature_prefill_split_and_unsplit(torch_dev, kind):
-    """The sequence split (pieces of whole chunks over several workgroups, a state pass and a start state
-    summed from the pieces' slots) and the unsplit form (at least as many sequences as compute units), both
+    """The sequence split (pieces of whole chunks over several workgroups, a state pass that may cut each piece
+    into parts, and a start state summed from the parts' slots) and the unsplit form (at least as many sequences as compute units), both
     with a caller state, against the oracle; every sequence's outputs and final state are checked."""
     import root_parity_gated_amd as rpg
 
     torch = torch_dev
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    for B, H, T in ((1, 2, 333), (2, (n_cu + 1) // 2, 70)):  # split into up to 8 pieces, then unsplit
+    # split into up to 8 pieces; at T = 1000 (8 pieces of 4 chunks, the last ragged) the state pass runs each
+    # piece as 4 one-chunk parts with a slot each; then unsplit
+    for B, H, T in ((1, 2, 333), (1, 2, 1000), (2, (n_cu + 1) // 2, 70)):
         q, k, v, om = si.attention_inputs(950 + T, B, H, T + 20, "bf16")
         p = params(torch, om)
         nh = {"nh1": 1, "nh2": 2, "four": 0}[kind]
