@@ -33,13 +33,13 @@ namespace sanatan {
 hipError_t launch_quadratic_stats(const void* q, const void* phik, const void* v, const void* g, sanatan_dtype t,
                                   int B, int H, int T, int p, const float* rho, const MethodConsts& mc, float2* stats,
                                   hipStream_t stream);
-// backward_chunked.hip: the p = 1 feature gradients and dv as chunked recurrences, and their slot bytes
+// backward_chunked.hip: the p = 1 feature gradients and dv as chunked recurrences (writing the per-sequence omega
+// sums [2 sides][BH][d] to seq_sum), and the bytes of their slots and omega partials
 size_t bwd_chunked_slot_bytes(int B, int H, int T);
-int bwd_chunked_pieces(int B, int H, int T);
 hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, float2* stats,
                               sanatan_dtype t, int B, int H, int T, float ceps, const void* q, const void* k,
                               const float* rho, const float* omega, int nph, float kr, void* dq, void* dk, void* dv,
-                              float* dom_part, float* slots, hipStream_t stream);
+                              float* seq_sum, float* slots, hipStream_t stream);
 
 // backward_quadratic.hip: the bf16 gradients at p = 2 (feature gradients, Jacobian and omega partials fused)
 hipError_t launch_bwd_quadratic_bf16(const void* phiq, const void* phik, const void* v, const void* g,
@@ -492,8 +492,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   if ((e = launch_featurize(k, dt, B, H, Tn, pos0, mc, phik, dt, stream)) != hipSuccess) return e;
   if constexpr (P == 1) {
     // p = 1: the statistics, the feature gradients and dv as chunked recurrences, linear in T
+    // (the per-sequence omega sums go where the p = 2 path's stage 1 writes them)
+    float* seq_sum = dom + (size_t)2 * B * H * ((Tn + 31) / 32) * kD;
     if ((e = launch_bwd_chunked(phiq, phik, v, g, stats, dt, B, H, Tn, mc.ceps, q, k, rho, mc.omega, mc.nph, mc.kr,
-                                dq, dk, dv, dom, reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
+                                dq, dk, dv, seq_sum, reinterpret_cast<float*>(base + L.slots), stream)) != hipSuccess)
       return e;
   } else {
     if (saved) {  // the forward pass's saved output rows and normalisers replace the statistics pass
@@ -549,10 +551,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   }
   }
   const int BH = B * H, ntiles = (Tn + 31) / 32, nblk = BH * ntiles;
-  int nparts = ntiles;  // omega partial rows per (side, sequence)
-  if constexpr (P == 1) {
-    nparts = bwd_chunked_pieces(B, H, Tn);  // the chunk kernels applied the Jacobian themselves
-  } else if constexpr (sizeof(T) == 4) {  // (bf16: the gradient kernels applied it)
+  const int nparts = ntiles;  // omega partial rows per (side, sequence)
+  float* seq_sum = dom + (size_t)2 * nblk * kD;
+  if constexpr (sizeof(T) == 4 && P != 1) {  // (bf16: the gradient kernels applied the Jacobian; p = 1: the chunk
+                                            // kernels did, and wrote the per-sequence sums)
     hipLaunchKernelGGL((bwd_jacobian_kernel<T>), dim3(nblk), dim3(256), 0, stream, static_cast<const T*>(q), dphiq,
                        rho, mc.omega, mc.nph, H, Tn, mc.kr, ntiles, static_cast<T*>(dq), dom);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -561,9 +563,10 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                        dom + (size_t)nparts * BH * kD);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  float* seq_sum = dom + (size_t)2 * nblk * kD;
-  hipLaunchKernelGGL(bwd_domega_seq_kernel, dim3(2 * BH), dim3(64), 0, stream, dom, nparts, seq_sum);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (P != 1) {
+    hipLaunchKernelGGL(bwd_domega_seq_kernel, dim3(2 * BH), dim3(64), 0, stream, dom, nparts, seq_sum);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(bwd_domega_kernel, dim3(mc.nph), dim3(64), 0, stream, seq_sum, BH, H, mc.nph, domega);
   return hipGetLastError();
 }

@@ -18,16 +18,20 @@
 // chunk a lane holds all channels' gradients of its token's 8 dims and writes du (and accumulates the omega
 // gradient) without a dPhi array.
 //
-// Work split.  Each sequence is cut into NP pieces of whole chunks, one workgroup per piece and direction.  The
-// forward direction walks its chunks in order carrying S^T (as 32 x 32 accumulator tiles [value][feature]) and
-// z, and writes the statistics; the reverse direction, launched after it, walks them backwards carrying R^T and
-// r.  Four waves share a workgroup, wave w owning dims 16 w .. 16 w + 15 of every channel (three 32-feature
+// Work split.  The chunks of all sequences form one list (sequence-major), cut into G ranges of equal length, one
+// workgroup per range and direction; with fewer sequences than compute units G = min(CUs, chunks), so a range
+// covers the tail of one sequence and the head of the next at most (two segments), otherwise G is the number of
+// sequences and each range is one whole sequence.  For each of its segments the forward direction walks the
+// chunks in order carrying S^T (as 32 x 32 accumulator tiles [value][feature]) and z, and writes the statistics;
+// the reverse direction, launched after it, walks them backwards carrying R^T and r.  Four waves share a workgroup, wave w owning dims 16 w .. 16 w + 15 of every channel (three 32-feature
 // tiles).  The dPhi products need no exchange between waves; the statistics and dv sum over all features, so
 // their four partials meet in LDS in a fixed order.  R^T Phi(k) contracts over features, the other way round
-// from R v, so each R^T tile also passes through a wave-private LDS tile read back transposed.  With NP > 1 an
-// increments pass writes pieces 0 .. NP-2's own S and z to slots before the forward direction, and another
-// pieces 1 .. NP-1's own R and r (which need the statistics) before the reverse one; a piece starts from the sum
-// of its predecessors' (forward) or successors' (reverse) slots, in a fixed order.
+// from R v, so each R^T tile also passes through a wave-private LDS tile read back transposed.  When ranges split
+// sequences, an increments pass writes the own S and z of each range's last segment that does not end its
+// sequence to the range's slot before the forward direction, and another the own R and r (which need the
+// statistics) of each range's first segment that does not start its sequence before the reverse one; a segment
+// starts from the sum of the slots of the ranges before it (forward) or after it (reverse) in its sequence, in a
+// fixed order.
 // Operands: bf16 32x32x16 MFMA (fp32 32x32x2 for fp32 inputs), fp32 accumulation.  With bf16 operands, A, the
 // states S and R, and g / Dn in the update of R enter the products as their rounding plus the rounding of their
 // residual: S g and delta z (R v and r) nearly cancel, so a single rounding would leave an error near the
@@ -70,27 +74,20 @@ struct CGeom {
   static_assert(o_st % 16 == 0 && o_rl % 16 == 0 && o_red % 16 == 0, "aligned LDS regions");
 };
 
-// Pieces per sequence: as many as keep every workgroup of a launch on a compute unit of its own (at most 32, at
-// most one per chunk).
-int bwd_pieces(int B, int H, int Tn) {
-  const long long BH = (long long)B * H, nch = (Tn + kBC - 1) / kBC;
-  long long P = device_cus() / BH;
-  if (P > 32) P = 32;
-  if (P > nch) P = nch;
-  return P < 1 ? 1 : (int)P;
+// Ranges (workgroups per launch): with at least as many sequences as compute units one per sequence, otherwise
+// one per compute unit (at most one per chunk).  G >= BH, so a range never spans more than two sequences.
+int bwd_ranges(int B, int H, int Tn) {
+  const long long BH = (long long)B * H, total = BH * ((Tn + kBC - 1) / kBC);
+  long long G = device_cus();
+  if (G <= BH) return (int)BH;
+  return (int)(G < total ? G : total);
 }
 
-// Workgroups per piece in the increments passes: only NP - 1 of a sequence's NP pieces have an increment, so each
-// such piece's chunks are split over this many workgroups (each writes a slot of its own, and the consumers sum
-// them) to keep the compute units busy: at most 8, and never more than the chunks of the smallest piece.
-int bwd_split(int B, int H, int Tn) {
-  const int NP = bwd_pieces(B, H, Tn);
-  if (NP < 2) return 1;
-  const long long BH = (long long)B * H, nch = (Tn + kBC - 1) / kBC;
-  long long S = device_cus() / (BH * (NP - 1));
-  if (S > 8) S = 8;
-  if (S > nch / NP) S = nch / NP;
-  return S < 1 ? 1 : (int)S;
+// The range a workgroup runs: workgroups are dealt round-robin to the 8 XCDs, so consecutive ranges (the segments
+// of one sequence, which read each other's slots) go to workgroups on one XCD.  A bijection on [0, NR).
+__device__ __forceinline__ int bwd_range_of_block(int NR) {
+  const int b = (int)blockIdx.x, per = NR / 8;
+  return b < 8 * per ? (b % 8) * per + b / 8 : b;
 }
 
 // 16 bytes of T scaled by s (hi), and for bf16 the rounding of what that rounding dropped (lo)
@@ -234,13 +231,6 @@ __device__ __forceinline__ void slot_put(float* sl, const f32x16 (&A)[CGeom<T>::
   for (int f = tid; f < kF; f += 256) sl[(size_t)kF * kDV + f] = vec[f];
 }
 
-// Tokens [t_lo, t_hi) of piece p of NP (whole chunks).
-__device__ __forceinline__ void piece_bounds(int p, int NP, int Tn, int& t_lo, int& t_hi) {
-  const int nch = (Tn + kBC - 1) / kBC;
-  t_lo = (int)((long long)p * nch / NP) * kBC;
-  t_hi = min(Tn, (int)((long long)(p + 1) * nch / NP) * kBC);
-}
-
 // Feature fragment of Phi(Q) with tokens along K (lane row = internal feature col0 + l % 32): from the LDS tile
 // (bf16) or from global memory (fp32)
 template <typename T>
@@ -308,31 +298,37 @@ __device__ __forceinline__ void store_dom(float (&dom)[2][4], float* part, int a
     }
 }
 
-// The increments pass: piece p's own S^T and z (MODE 1; pieces p < NP - 1, before the forward direction) or R^T
-// and r (MODE 2; pieces p > 0, after it: they need the statistics the forward direction writes), to its slots.
+// The increments pass: the own S^T and z of the range's last segment if it does not end its sequence (MODE 1,
+// before the forward direction), or the own R^T and r of its first segment if it does not start its sequence
+// (MODE 2, after it: they need the statistics the forward direction writes), to the range's slot.
 // Two register sets alternate, so each chunk's rows are loaded two chunks ahead of their use: the per-chunk work
 // here is short, and one chunk of lead does not cover the loads' latency.
 template <typename T, int MODE>
 __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                           const T* __restrict__ v, const T* __restrict__ g,
-                                                          const float2* __restrict__ stats, int Tn, int NP,
-                                                          int SPL, float* __restrict__ slots) {
+                                                          const float2* __restrict__ stats, int Tn, int nch,
+                                                          int BH, int NR, float* __restrict__ slots) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
   constexpr bool DS = MODE == 1, DR = MODE == 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
-  // one workgroup per part of a piece that has an increment (all but the last for S, all but the first for R), so
-  // consecutive workgroups, which go to different XCDs, all have work
-  const int bh = blockIdx.x / ((NP - 1) * SPL), p = (blockIdx.x / SPL) % (NP - 1) + (DS ? 0 : 1),
-            sp_ = blockIdx.x % SPL;
-  int t_lo, t_hi;
-  piece_bounds(p, NP, Tn, t_lo, t_hi);
-  {  // part sp_ of the piece's chunks (never empty: every piece has at least SPL chunks)
-    const int pc = (t_hi - t_lo + kBC - 1) / kBC, base = t_lo;
-    t_lo = base + (sp_ * pc / SPL) * kBC;
-    t_hi = min(t_hi, base + ((sp_ + 1) * pc / SPL) * kBC);
+  const int rg = bwd_range_of_block(NR);
+  const long long total = (long long)BH * nch, lo = range_lo(rg, total, NR), hi = range_lo(rg + 1, total, NR);
+  int bh, t_lo, t_hi;
+  if constexpr (DS) {  // the last segment, unless it ends its sequence
+    bh = (int)((hi - 1) / nch);
+    const long long seq0 = (long long)bh * nch;
+    if (hi == seq0 + nch) return;
+    t_lo = (int)((lo > seq0 ? lo : seq0) - seq0) * kBC;
+    t_hi = (int)(hi - seq0) * kBC;
+  } else {  // the first segment, unless it starts its sequence
+    bh = (int)(lo / nch);
+    const long long seq0 = (long long)bh * nch;
+    if (lo == seq0) return;
+    t_lo = (int)(lo - seq0) * kBC;
+    t_hi = min(Tn, (int)((hi < seq0 + nch ? hi : seq0 + nch) - seq0) * kBC);
   }
   const size_t so = (size_t)bh * Tn;
   const T* qp = phiq + so * Fp;
@@ -381,25 +377,25 @@ __global__ __launch_bounds__(256, 1) void bwd_incr_kernel(const T* __restrict__ 
   };
   // MODE 1 stages Phi(K) and V; MODE 2 Phi(Q) (bf16), g / Dn and the statistics
   ChunkRegs<T, DS, DR, DS, false, DR, DR> R0, R1;
-  const int nch = (t_hi - t_lo + kBC - 1) / kBC;
+  const int sc = (t_hi - t_lo + kBC - 1) / kBC;
   auto nvof = [&](int c) { return min(kBC, t_hi - t_lo - c * kBC); };
   R0.load(kp, qp, vp, gp, sp, t_lo, nvof(0), tid);
-  if (nch > 1) R1.load(kp, qp, vp, gp, sp, t_lo + kBC, nvof(1), tid);
-  for (int c = 0; c < nch; c += 2) {
+  if (sc > 1) R1.load(kp, qp, vp, gp, sp, t_lo + kBC, nvof(1), tid);
+  for (int c = 0; c < sc; c += 2) {
     R0.store(smem, tid);
     __syncthreads();
-    if (c + 2 < nch) R0.load(kp, qp, vp, gp, sp, t_lo + (c + 2) * kBC, nvof(c + 2), tid);
+    if (c + 2 < sc) R0.load(kp, qp, vp, gp, sp, t_lo + (c + 2) * kBC, nvof(c + 2), tid);
     compute(t_lo + c * kBC);
     __syncthreads();
-    if (c + 1 < nch) {
+    if (c + 1 < sc) {
       R1.store(smem, tid);
       __syncthreads();
-      if (c + 3 < nch) R1.load(kp, qp, vp, gp, sp, t_lo + (c + 3) * kBC, nvof(c + 3), tid);
+      if (c + 3 < sc) R1.load(kp, qp, vp, gp, sp, t_lo + (c + 3) * kBC, nvof(c + 3), tid);
       compute(t_lo + (c + 1) * kBC);
       __syncthreads();
     }
   }
-  slot_put<T>(slots + (((size_t)bh * NP + p) * SPL + sp_) * G::SLOT, A, vs, w, l, tid);
+  slot_put<T>(slots + (size_t)rg * G::SLOT, A, vs, w, l, tid);
 }
 
 // Method inputs of the fused Jacobian: the raw q and k, the phase table, the root anchors and kr.
@@ -412,25 +408,23 @@ struct JacArgs {
   float kr;
 };
 
-// Forward direction: the statistics and dq of one piece, and its omega partials (row (bh NP + p) of dom).  The
+// Forward direction: the statistics and dq of one segment (tokens [t_lo, t_hi) of sequence bh, starting from the
+// sum of the S slots of ranges [g0, g1)), and its omega partials (dom_row).  The
 // statistics come out of the same pass: with W_t = S g_t (S before the chunk, the product that dPhi(q) needs
 // anyway) and the chunk's scores P,
 //   Dn_t = Phi(q_t) . z + sum_{s<=t} P[t][s] + c eps,   delta_t Dn_t = Phi(q_t) . W_t + sum_{s<=t} P[t][s] <g_t, v_s>,
 // each wave summing over its features and the four partials meeting in LDS in a fixed order.  They are written
 // to stats for the reverse direction.
 template <typename T>
-__device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
-                                         const T* __restrict__ v, const T* __restrict__ g,
-                                         float2* __restrict__ stats, int Tn, int NP, int SPL, float ceps,
+__device__ __forceinline__ void dq_piece(int bh, int t_lo, int t_hi, int g0, int g1, const T* __restrict__ phiq,
+                                         const T* __restrict__ phik, const T* __restrict__ v,
+                                         const T* __restrict__ g, float2* __restrict__ stats, int Tn, float ceps,
                                          const float* __restrict__ sslots, const JacArgs& ja, T* __restrict__ dq,
-                                         float* __restrict__ dom_part, char* smem) {
+                                         float* __restrict__ dom_row, char* smem) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
-  const int bh = blk / NP, p = blk % NP;
-  int t_lo, t_hi;
-  piece_bounds(p, NP, Tn, t_lo, t_hi);
   const size_t so = (size_t)bh * Tn;
   const T* qp = phiq + so * Fp;
   const T* kp = phik + so * Fp;
@@ -461,7 +455,7 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, co
 #pragma unroll
     for (int vt = 0; vt < 2; vt++) zero16(ST[i][vt]);
   for (int f = tid; f < Fp; f += 256) zs[f] = 0.0f;
-  for (int q = 0; q < p * SPL; q++) slot_add<T>(sslots + ((size_t)bh * NP * SPL + q) * G::SLOT, ST, zs, w, l, tid);
+  for (int q = g0; q < g1; q++) slot_add<T>(sslots + (size_t)q * G::SLOT, ST, zs, w, l, tid);
   ChunkRegs<T, true, true, true, true, false, false> R;
   R.load(kp, qp, vp, gp, nullptr, t_lo, min(kBC, t_hi - t_lo), tid);
   for (int t0 = t_lo; t0 < t_hi; t0 += kBC) {
@@ -593,23 +587,21 @@ __device__ __forceinline__ void dq_piece(int blk, const T* __restrict__ phiq, co
     }
     __syncthreads();  // the next chunk's staging overwrites the tiles and the statistics partials
   }
-  store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
+  store_dom(dom, dom_row, da, n32);
 }
 
-// Reverse direction: dk and dv of one piece, and its omega partials (row (bh NP + p) of dom).
+// Reverse direction: dk and dv of one segment (tokens [t_lo, t_hi) of sequence bh, starting from the sum of the R
+// slots of ranges [g0, g1), the farthest first), and its omega partials (dom_row).
 template <typename T>
-__device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, const T* __restrict__ phik,
-                                          const T* __restrict__ v, const T* __restrict__ g,
-                                          const float2* __restrict__ stats, int Tn, int NP, int SPL,
+__device__ __forceinline__ void dkv_piece(int bh, int t_lo, int t_hi, int g0, int g1, const T* __restrict__ phiq,
+                                          const T* __restrict__ phik, const T* __restrict__ v,
+                                          const T* __restrict__ g, const float2* __restrict__ stats, int Tn,
                                           const float* __restrict__ rslots, const JacArgs& ja, T* __restrict__ dk,
-                                          T* __restrict__ dv, float* __restrict__ dom_part, char* smem) {
+                                          T* __restrict__ dv, float* __restrict__ dom_row, char* smem) {
   using G = CGeom<T>;
   typedef typename FragT<T>::type Frag;
   constexpr int NW = G::NW, Fp = G::Fp;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, n32 = l & 31;
-  const int bh = blk / NP, p = blk % NP;
-  int t_lo, t_hi;
-  piece_bounds(p, NP, Tn, t_lo, t_hi);
   const size_t so = (size_t)bh * Tn;
   const T* qp = phiq + so * Fp;
   const T* kp = phik + so * Fp;
@@ -645,8 +637,7 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
 #pragma unroll
     for (int vt = 0; vt < 2; vt++) zero16(RT[i][vt]);
   for (int f = tid; f < Fp; f += 256) rs[f] = 0.0f;
-  for (int q = NP * SPL - 1; q >= (p + 1) * SPL; q--)
-    slot_add<T>(rslots + ((size_t)bh * NP * SPL + q) * G::SLOT, RT, rs, w, l, tid);
+  for (int q = g1 - 1; q >= g0; q--) slot_add<T>(rslots + (size_t)q * G::SLOT, RT, rs, w, l, tid);
   const int c_lo = t_lo / kBC, c_hi = (t_hi + kBC - 1) / kBC;
   ChunkRegs<T, true, true, true, true, true> R;
   R.load(kp, qp, vp, gp, sp, (c_hi - 1) * kBC, min(kBC, t_hi - (c_hi - 1) * kBC), tid);
@@ -811,26 +802,70 @@ __device__ __forceinline__ void dkv_piece(int blk, const T* __restrict__ phiq, c
     }
     __syncthreads();  // the next chunk's staging overwrites the tiles and the reduction buffer
   }
-  store_dom(dom, dom_part + (size_t)blk * kD, da, n32);
+  store_dom(dom, dom_row, da, n32);
 }
 
-// DIR 0: the forward direction (statistics, dq), written to rows [0, BH NP) of dom; DIR 1: the reverse one
-// (dk, dv), rows [BH NP, 2 BH NP).  One workgroup per piece.
+// DIR 0: the forward direction (statistics, dq); DIR 1: the reverse one (dk, dv).  One workgroup per range, which
+// runs its one or two segments in order; segment j of range r writes its omega partials to row (DIR NR + r) 2 + j
+// of dom_part.
 template <typename T, int DIR>
 __global__ __launch_bounds__(256, 1) void bwd_chunk_kernel(const T* __restrict__ phiq, const T* __restrict__ phik,
                                                            const T* __restrict__ v, const T* __restrict__ g,
-                                                           float2* __restrict__ stats, int Tn, int NP, int SPL,
-                                                           float ceps,
-                                                           const float* __restrict__ sslots,
+                                                           float2* __restrict__ stats, int Tn, int nch, int BH,
+                                                           int NR, float ceps, const float* __restrict__ sslots,
                                                            const float* __restrict__ rslots, const JacArgs ja,
                                                            T* __restrict__ dq, T* __restrict__ dk,
                                                            T* __restrict__ dv, float* __restrict__ dom_part) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  // the range's one or two segments, as workgroup-uniform 32-bit values (kept in scalar registers, out of the way
+  // of the chunk loop's vector registers): sequence bh0 chunks [a0, a1), then, if nseg = 2, sequence bh0 + 1
+  // chunks [0, b1)
+  const int rg = bwd_range_of_block(NR);
+  const long long total = (long long)BH * nch, lo = range_lo(rg, total, NR), hi = range_lo(rg + 1, total, NR);
+  const long long s0 = lo / nch * nch;
+  const int bh0 = __builtin_amdgcn_readfirstlane((int)(lo / nch));
+  const int a0 = __builtin_amdgcn_readfirstlane((int)(lo - s0));
+  const int a1 = __builtin_amdgcn_readfirstlane((int)((hi < s0 + nch ? hi : s0 + nch) - s0));
+  const int nseg = hi > s0 + nch ? 2 : 1;
+  const int b1 = __builtin_amdgcn_readfirstlane((int)(hi - s0 - nch));
+  // forward: the ranges before the first segment in its sequence (the second starts its sequence); reverse: the
+  // ranges after the last segment in its sequence (the first ends its sequence when there is a second)
+  const int pre = __builtin_amdgcn_readfirstlane(a0 > 0 ? range_of_chunk(s0, total, NR) : rg);
+  const long long sl = nseg == 2 ? s0 + nch : s0;  // the last segment's sequence start
+  const int c_last = nseg == 2 ? b1 : a1;
+  const int post = __builtin_amdgcn_readfirstlane(c_last < nch ? range_of_chunk(sl + nch - 1, total, NR) + 1 : rg + 1);
+  // (two inlined calls rather than a loop: each copy then keeps the registers of a single segment)
+  float* drow = dom_part + (size_t)(DIR * NR + rg) * 2 * kD;
   if constexpr (DIR == 0)
-    dq_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, SPL, ceps, sslots, ja, dq, dom_part, smem);
+    dq_piece<T>(bh0, a0 * kBC, min(Tn, a1 * kBC), pre, rg, phiq, phik, v, g, stats, Tn, ceps, sslots, ja, dq, drow,
+                smem);
   else
-    dkv_piece<T>(blockIdx.x, phiq, phik, v, g, stats, Tn, NP, SPL, rslots, ja, dk, dv,
-                 dom_part + (size_t)gridDim.x * kD, smem);
+    dkv_piece<T>(bh0, a0 * kBC, min(Tn, a1 * kBC), rg + 1, nseg == 2 ? rg + 1 : post, phiq, phik, v, g, stats, Tn,
+                 rslots, ja, dk, dv, drow, smem);
+  if (nseg == 2) {
+    __syncthreads();  // the first segment's LDS tiles and vectors are dead
+    if constexpr (DIR == 0)
+      dq_piece<T>(bh0 + 1, 0, min(Tn, b1 * kBC), rg, rg, phiq, phik, v, g, stats, Tn, ceps, sslots, ja, dq,
+                  drow + kD, smem);
+    else
+      dkv_piece<T>(bh0 + 1, 0, min(Tn, b1 * kBC), rg + 1, post, phiq, phik, v, g, stats, Tn, rslots, ja, dk, dv,
+                   drow + kD, smem);
+  }
+}
+
+// Per (side, sequence): the omega partials of the sequence's segments summed in range order (side 0: the dq
+// rows, side 1: the dk rows), to seq_sum[side BH + bh].
+__global__ __launch_bounds__(64) void bwd_domega_seg_kernel(const float* __restrict__ part, int nch, int BH, int NR,
+                                                            float* __restrict__ seq_sum) {
+  const int sb = blockIdx.x, side = sb / BH, bh = sb % BH, a = threadIdx.x;
+  const long long total = (long long)BH * nch, seq0 = (long long)bh * nch;
+  const int gf = range_of_chunk(seq0, total, NR), gl = range_of_chunk(seq0 + nch - 1, total, NR);
+  float acc = 0.0f;
+  for (int r = gf; r <= gl; r++) {
+    const int j = (r == gf && range_lo(r, total, NR) < seq0) ? 1 : 0;  // the sequence is the range's second segment
+    acc += part[((size_t)(side * NR + r) * 2 + j) * kD + a];
+  }
+  seq_sum[(size_t)sb * kD + a] = acc;
 }
 
 template <typename Kern>
@@ -843,15 +878,17 @@ hipError_t set_lds_attr(Kern k, int bytes, std::atomic<bool>& flag) {
 
 template <typename T>
 hipError_t launch_t(const void* phiq, const void* phik, const void* v, const void* g, float2* stats, int B, int H,
-                    int Tn, float ceps, const JacArgs& ja, void* dq, void* dk, void* dv, float* dom_part,
+                    int Tn, float ceps, const JacArgs& ja, void* dq, void* dk, void* dv, float* seq_sum,
                     float* slots, hipStream_t stream) {
   using G = CGeom<T>;
   static std::atomic<bool> attr[4][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const int BH = B * H, NP = bwd_pieces(B, H, Tn), SPL = bwd_split(B, H, Tn);
+  const int BH = B * H, nch = (Tn + kBC - 1) / kBC, NR = bwd_ranges(B, H, Tn);
+  const bool split = NR > BH;  // ranges cut sequences: increments and slots
   float* sslots = slots;
-  float* rslots = NP > 1 ? slots + (size_t)BH * NP * SPL * G::SLOT : slots;
+  float* rslots = slots + (size_t)NR * G::SLOT;
+  float* dom_part = slots + (split ? 2 * (size_t)NR * G::SLOT : 0);  // [2 sides][NR ranges][2 segments][d]
   const T* q = static_cast<const T*>(phiq);
   const T* k = static_cast<const T*>(phik);
   const T* vv = static_cast<const T*>(v);
@@ -860,53 +897,56 @@ hipError_t launch_t(const void* phiq, const void* phik, const void* v, const voi
   if ((e = set_lds_attr(bwd_chunk_kernel<T, 0>, G::lds, attr[1][dev])) != hipSuccess ||
       (e = set_lds_attr(bwd_chunk_kernel<T, 1>, G::lds, attr[3][dev])) != hipSuccess)
     return e;
-  if (NP > 1 && ((e = set_lds_attr(bwd_incr_kernel<T, 1>, G::lds, attr[0][dev])) != hipSuccess ||
-                 (e = set_lds_attr(bwd_incr_kernel<T, 2>, G::lds, attr[2][dev])) != hipSuccess))
+  if (split && ((e = set_lds_attr(bwd_incr_kernel<T, 1>, G::lds, attr[0][dev])) != hipSuccess ||
+                (e = set_lds_attr(bwd_incr_kernel<T, 2>, G::lds, attr[2][dev])) != hipSuccess))
     return e;
   auto incr = [&](int mode) {
     if (mode == 1)
-      hipLaunchKernelGGL((bwd_incr_kernel<T, 1>), dim3(BH * (NP - 1) * SPL), dim3(256), G::lds, stream, q, k, vv, gg, stats,
-                         Tn, NP, SPL, sslots);
+      hipLaunchKernelGGL((bwd_incr_kernel<T, 1>), dim3(NR), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, nch,
+                         BH, NR, sslots);
     else
-      hipLaunchKernelGGL((bwd_incr_kernel<T, 2>), dim3(BH * (NP - 1) * SPL), dim3(256), G::lds, stream, q, k, vv, gg, stats,
-                         Tn, NP, SPL, rslots);
+      hipLaunchKernelGGL((bwd_incr_kernel<T, 2>), dim3(NR), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, nch,
+                         BH, NR, rslots);
     return hipGetLastError();
   };
   auto chunks = [&](int dir) {
     if (dir == 0)
-      hipLaunchKernelGGL((bwd_chunk_kernel<T, 0>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
-                         NP, SPL, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
+      hipLaunchKernelGGL((bwd_chunk_kernel<T, 0>), dim3(NR), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, nch,
+                         BH, NR, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
                          static_cast<T*>(dv), dom_part);
     else
-      hipLaunchKernelGGL((bwd_chunk_kernel<T, 1>), dim3(BH * NP), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn,
-                         NP, SPL, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
+      hipLaunchKernelGGL((bwd_chunk_kernel<T, 1>), dim3(NR), dim3(256), G::lds, stream, q, k, vv, gg, stats, Tn, nch,
+                         BH, NR, ceps, sslots, rslots, ja, static_cast<T*>(dq), static_cast<T*>(dk),
                          static_cast<T*>(dv), dom_part);
     return hipGetLastError();
   };
-  // S increments, the forward direction (which writes the statistics), R increments, the reverse direction
-  if (NP > 1 && (e = incr(1)) != hipSuccess) return e;
+  // S increments, the forward direction (which writes the statistics), R increments, the reverse direction, and
+  // the per-sequence omega sums
+  if (split && (e = incr(1)) != hipSuccess) return e;
   if ((e = chunks(0)) != hipSuccess) return e;
-  if (NP > 1 && (e = incr(2)) != hipSuccess) return e;
-  return chunks(1);
+  if (split && (e = incr(2)) != hipSuccess) return e;
+  if ((e = chunks(1)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_domega_seg_kernel, dim3(2 * BH), dim3(64), 0, stream, dom_part, nch, BH, NR, seq_sum);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Slots (two states per range when ranges cut sequences), then the omega partial rows (two sides, two per range)
 size_t bwd_chunked_slot_bytes(int B, int H, int T) {
-  const int NP = bwd_pieces(B, H, T);
-  return NP > 1 ? 2 * (size_t)B * H * NP * bwd_split(B, H, T) * CGeom<float>::SLOT * sizeof(float) : 0;
+  const size_t NR = bwd_ranges(B, H, T);
+  const bool split = NR > (size_t)B * H;
+  return ((split ? 2 * NR * CGeom<float>::SLOT : 0) + 4 * NR * kD) * sizeof(float);
 }
-
-int bwd_chunked_pieces(int B, int H, int T) { return bwd_pieces(B, H, T); }
 
 hipError_t launch_bwd_chunked(const void* phiq, const void* phik, const void* v, const void* g, float2* stats,
                               sanatan_dtype t, int B, int H, int T, float ceps, const void* q, const void* k,
                               const float* rho, const float* omega, int nph, float kr, void* dq, void* dk, void* dv,
-                              float* dom_part, float* slots, hipStream_t stream) {
+                              float* seq_sum, float* slots, hipStream_t stream) {
   const JacArgs ja{q, k, rho, omega, nph, H, kr};
   return t == SANATAN_BF16
-             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, ceps, ja, dq, dk, dv, dom_part, slots, stream)
-             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, ceps, ja, dq, dk, dv, dom_part, slots, stream);
+             ? launch_t<__bf16>(phiq, phik, v, g, stats, B, H, T, ceps, ja, dq, dk, dv, seq_sum, slots, stream)
+             : launch_t<float>(phiq, phik, v, g, stats, B, H, T, ceps, ja, dq, dk, dv, seq_sum, slots, stream);
 }
 
 }  // namespace sanatan

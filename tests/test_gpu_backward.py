@@ -152,19 +152,20 @@ def test_backward_long_bf16(torch_dev, p):
 
 
 def test_backward_p1_long_many_pieces(torch_dev):
-    """p = 1 at 4096 tokens in bf16: each sequence runs as 32 pieces of four chunks, and on 256 compute units
-    each piece's increments as four one-chunk parts, so the reverse direction's start states sum up to 124
-    slots of 31 successors."""
+    """p = 1 at 4096 tokens in bf16: on 256 compute units the 256 chunks of the two sequences run as 256
+    one-chunk ranges, so a range's start state sums up to 127 slots of the ranges before (forward) or after
+    (reverse) it."""
     errs = run_case(torch_dev, 835, 1, 2, 4096, "bf16", 1)
     for name, e in errs.items():
         assert e <= TOL["bf16"], (name, e)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_p1_split_increments_ragged(torch_dev, dtype):
-    """p = 1 at 2100 tokens (a ragged last chunk) over three heads: on 256 compute units 32 pieces of two or
-    three chunks, each piece's increments computed as two parts with a slot each."""
-    errs = run_case(torch_dev, 837, 1, 3, 2100, dtype, 1)
+def test_backward_p1_range_across_sequences(torch_dev, dtype):
+    """p = 1 at 2020 tokens (a 4-token last chunk) over five heads: on 256 compute units the 320 chunks run as
+    ranges of one or two chunks, one of which holds the last chunk of one sequence and the first of the next, so
+    a workgroup runs two segments of different sequences in turn."""
+    errs = run_case(torch_dev, 837, 1, 5, 2020, dtype, 1)
     for name, e in errs.items():
         assert e <= TOL[dtype], (name, e)
 
