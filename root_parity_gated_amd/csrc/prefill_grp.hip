@@ -701,10 +701,12 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
         *reinterpret_cast<uint4*>(Vs + row * VP + col) = make_uint4(r[j].x & m, r[j].y & m, r[j].z & m, r[j].w & m);
       }
     };
-    auto write_k = [&](const bf16x8 (&F)[5], int nvh) {
+    // (channel 0, the constant 1, is written with the piece's first chunk only: the loop writes whole
+    // chunks, so nothing overwrites it before the staging at the piece's end)
+    auto write_k = [&](const bf16x8 (&F)[5], int nvh, bool ones) {
       __bf16* row = KS + n32 * KP + 8 * h;
       if (n32 < nvh) {
-        *reinterpret_cast<u32x4*>(row) = ones4;
+        if (ones) *reinterpret_cast<u32x4*>(row) = ones4;
 #pragma unroll
         for (int cc = 1; cc < 6; cc++) *reinterpret_cast<bf16x8*>(row + 16 * cc) = F[cc - 1];
       } else {
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
       float cr[8], sr[8], rr[8];
       feat8(uk, rh[0], rh[1], om4, args.kr, F, cr, sr, rr);
       const int nvh = half_valid(t_begin);
-      write_k(F, nvh);
+      write_k(F, nvh, true);
       write_v(rv, nvh);
       // V before keys, as in the loop, so that the loop's first wait for V does not also wait for the keys
       const int t1 = next_t(t_begin);
@@ -755,7 +757,7 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
     // and the V rows are waited for only in the next chunk's step 2, the keys in its step 4.
     for (int t0 = t_begin; t0 < t_end; t0 += CH) {
       const int ta = next_t(t0), tb = next_t(ta);  // chunks j + 1, j + 2
-      const int nvh1 = ta != t0 ? half_valid(ta) : 0;  // past the piece's end the tiles get zero rows
+      const int nvh1 = ta != t0 ? half_valid(ta) : 0;  // 0: no next chunk, the tiles are not written again
       // 1. every MFMA operand of chunk j out of the tiles
       bf16x8 Af[2][3], Bf[2][2];
 #pragma unroll
@@ -766,7 +768,7 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
         for (int ft = 0; ft < 3; ft++) Af[ks][ft] = lds_tokfrag_swz(KS, KP, 16 * ks, 32 * ft, l);
       }
       // 2. chunk j + 1's V rows into the V tile, 3. and chunk j + 2's into their registers
-      write_v(rv, nvh1);
+      if (nvh1 > 0) write_v(rv, nvh1);
       load_v(tb, rv);
       // 4. the update MFMAs of chunk j with the keys of chunk j + 1 featurized in between, then into the tile
       float cr[8], sr[8], rr[8];
@@ -788,7 +790,7 @@ __global__ __launch_bounds__(512, 1) void prefill_state8_kernel(const PrefillArg
       }
       bf16x8 F[5];
       pack(cr, sr, rr, F);
-      write_k(F, nvh1);
+      if (nvh1 > 0) write_k(F, nvh1, false);
 #pragma unroll
       for (int ft = 0; ft < 3; ft++) zacc[ft] += xor32_sum(zs[ft]);
       // 5. chunk j + 2's keys into the registers just read
